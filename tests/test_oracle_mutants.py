@@ -1,0 +1,174 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case monkeypatches one plausible mistake into a copy of an oracle
+function — a dropped guard, a wrong rounding rule, a swapped operand or
+index — and checks that at least one of the pin tests then fails. This shows
+the pins constrain every step, not only the happy path.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as oatt
+import oracle.pages as opages
+import oracle.quant as oquant
+from tests.conftest import read_golden
+from tests import test_oracle_attention as TA
+from tests import test_oracle_pages as TP
+from tests import test_oracle_quant as TQ
+
+
+def _quantizer(scale_fn=None, round_fn=np.rint, divide=True, zero_guard=True, lo=-127):
+    def q(x):
+        x = oquant.as_f32(x)
+        a = np.max(np.abs(x), axis=-1)
+        s32 = np.divide(a, np.float32(127.0), dtype=np.float32)
+        s16 = scale_fn(s32) if scale_fn else oquant.ru16(s32)
+        if zero_guard:
+            s16 = np.where(a == 0, np.float16(1.0), s16).astype(np.float16)
+        sf = s16.astype(np.float32)[..., None]
+        with np.errstate(all="ignore"):
+            qq = np.divide(x, sf, dtype=np.float32) if divide else x * (np.float32(1) / sf)
+            codes = np.clip(round_fn(qq), lo, 127)
+        return np.nan_to_num(codes).astype(np.int8), s16
+    return q
+
+
+QUANT_MUTANTS = {
+    "scale floored at 1.0": _quantizer(
+        scale_fn=lambda s: np.maximum(oquant.ru16(s), np.float16(1.0))),
+    "round half away from zero": _quantizer(
+        round_fn=lambda v: np.sign(v) * np.floor(np.abs(v) + 0.5)),
+    "reciprocal multiply": _quantizer(divide=False),
+    "scale rounded to nearest": _quantizer(scale_fn=lambda s: s.astype(np.float16)),
+    "no zero-token guard": _quantizer(zero_guard=False),
+    "absmax/128 with -128 allowed": _quantizer(
+        scale_fn=lambda s: oquant.ru16(s * np.float32(127.0 / 128.0)), lo=-128),
+}
+
+QUANT_PINS = [
+    lambda: TQ.test_worked_examples(read_golden),
+    lambda: TQ.test_page_invariants("outlier"),
+    lambda: TQ.test_scale_exhaustive_over_fp16_absmax(),
+    lambda: TQ.test_zero_token_gets_scale_one(),
+    lambda: TQ.test_no_floor_at_one_for_small_rows(),
+    lambda: TQ.test_max_coordinate_maps_to_127("f16"),
+    lambda: TQ.test_exact_ties_round_to_even(),
+]
+
+
+def _caught(pins):
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("name", sorted(QUANT_MUTANTS))
+def test_quantizer_mutant_is_caught(name, monkeypatch):
+    monkeypatch.setattr(oracle, "quantize_rows", QUANT_MUTANTS[name])
+    assert _caught(QUANT_PINS), name
+
+
+def test_unmutated_oracle_passes_the_same_pins():
+    assert not _caught(QUANT_PINS)
+
+
+def _v_index_token_major(pos, d, head_dim):
+    return pos * head_dim + d
+
+
+def _offsets_scales_swapped(block_size, head_dim):
+    bs, d = block_size, head_dim
+    return {"k_codes": 0, "v_codes": bs * d, "k_scales": 2 * bs * d + 2 * bs,
+            "v_scales": 2 * bs * d, "head_bytes": 2 * bs * d + 4 * bs}
+
+
+PAGE_MUTANTS = {
+    "V stored token-major": ("_v_index", _v_index_token_major),
+    "K and V scale slots swapped": ("int8_head_offsets", _offsets_scales_swapped),
+}
+
+PAGE_PINS = [
+    lambda: TP.test_int8_byte_offsets_by_hand(),
+    lambda: TP.test_16bit_byte_offsets_by_hand(),
+]
+
+
+@pytest.mark.parametrize("name", sorted(PAGE_MUTANTS))
+def test_page_layout_mutant_is_caught(name, monkeypatch):
+    attr, fn = PAGE_MUTANTS[name]
+    monkeypatch.setattr(opages, attr, fn)
+    assert _caught(PAGE_PINS), name
+
+
+def _attend(scale_mul=1.0, swap_kv=False, drop_last=False, no_norm=False,
+            ignore_sm_scale=False):
+    def f(q, k, v, sm_scale):
+        q = np.asarray(q, np.float64)
+        k = np.asarray(k, np.float64)
+        v = np.asarray(v, np.float64)
+        if swap_kv:
+            k, v = v, k
+        if drop_last and k.shape[0] > 1:
+            k, v = k[:-1], v[:-1]
+        hq, d = q.shape
+        hkv = k.shape[1]
+        g = hq // hkv
+        out = np.zeros((hq, d))
+        if k.shape[0] == 0:
+            return out
+        for h in range(hq):
+            lg = (1.0 if ignore_sm_scale else sm_scale) * scale_mul * (k[:, h // g] @ q[h])
+            w = np.exp(lg - lg.max())
+            out[h] = (w @ v[:, h // g]) / (1.0 if no_norm else w.sum())
+        return out
+    return f
+
+
+def _decode_head_map_modulo(pool, block_tables, context_lens, q, sm_scale, block_size,
+                            num_kv_heads, head_dim, pairs=None):
+    """decode_int8_from_pool with query head h reading KV head h % Hkv."""
+    qf = oquant.as_f32(q)
+    B, hq, d = qf.shape
+    out = np.zeros((B, hq, d))
+    for b in range(B):
+        kc, ks, vc, vs = opages.gather_int8_sequence(pool, block_tables[b], int(context_lens[b]),
+                                                     block_size, num_kv_heads, head_dim)
+        k, v = oquant.dequantize_rows(kc, ks), oquant.dequantize_rows(vc, vs)
+        for h in range(hq):
+            g = h % num_kv_heads
+            out[b, h] = oatt.attend_one_sequence(qf[b, h][None], k[:, g:g + 1], v[:, g:g + 1],
+                                                 sm_scale)[0]
+    return out
+
+
+ATT_MUTANTS = {
+    "sm_scale ignored": ("attend_one_sequence", _attend(ignore_sm_scale=True)),
+    "K and V swapped": ("attend_one_sequence", _attend(swap_kv=True)),
+    "last token dropped": ("attend_one_sequence", _attend(drop_last=True)),
+    "softmax not normalised": ("attend_one_sequence", _attend(no_norm=True)),
+    "GQA head map h % Hkv": ("decode_int8_from_pool", _decode_head_map_modulo),
+}
+
+ATT_PINS = [
+    lambda: TA.test_int8_decode_matches_pure_python_brute_force(17, 8, 2, 128),
+    lambda: TA.test_single_token_returns_its_value(),
+    lambda: TA.test_zero_query_gives_mean_of_values(),
+]
+
+
+@pytest.mark.parametrize("name", sorted(ATT_MUTANTS))
+def test_attention_mutant_is_caught(name, monkeypatch):
+    attr, fn = ATT_MUTANTS[name]
+    monkeypatch.setattr(oatt, attr, fn)
+    if attr == "decode_int8_from_pool":
+        monkeypatch.setattr(oracle, attr, fn)
+    assert _caught(ATT_PINS), name
+
+
+def test_unmutated_attention_passes_the_same_pins():
+    assert not _caught(ATT_PINS)
