@@ -1,0 +1,219 @@
+/*
+ * pdakv.h — paged INT8-KV decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpdakv.so. Plain pointers and sizes only; no framework types.
+ *
+ * What the library computes
+ * -------------------------
+ * 1. kv_quant_int8_sym_write — per-token symmetric INT8 quantization of K and
+ *    V into a paged cache (MoE-Infinity PR #183 "feat: opt-in INT8 KV-cache
+ *    quantization", section "What landed", format-contract bullet, and section
+ *    "Precision & memory"; mlxcel PR #717 "fix(cuda/kv): correct Int8 KV
+ *    per-token scale ...", section "The Int8 bug and fix"). For every written
+ *    token, KV head, and each of K and V separately:
+ *        a     = max_d |x_d|
+ *        scale = 1.0                                  if a == 0
+ *              = smallest FP16 >= fl32(a / 127)        otherwise
+ *        code  = clamp(round_half_even(fl32(x_d / scale)), -127, 127)
+ *    so codes never take -128, exact zeros stay zero and every element obeys
+ *    |x - code * scale| <= scale / 2 (+1e-6).
+ * 2. paged_attn_decode_int8 — one decode query per sequence attending over
+ *    that sequence's INT8 pages, reading the codes and FP16 scales directly,
+ *    dequantizing in registers and accumulating with an FP32 online softmax;
+ *    MHA and GQA (MoE-Infinity PR #183, "What landed", native-kernel bullet;
+ *    "Scope & fallback").
+ * 3. paged_attn_decode_fp16 — the same decode over 16-bit (fp16 or bf16) K/V
+ *    pages with the same block-table layout, as a control.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Ownership: the caller allocates and owns every buffer (device memory for
+ *   all data pointers) and the stream. The library allocates nothing, keeps no
+ *   global state and never synchronizes; every call is asynchronous on
+ *   `stream` (a hipStream_t passed as void*; NULL = the default stream).
+ * - Errors: every int-returning call returns PDAKV_OK (0) or a negative
+ *   PDAKV_ERR_* code; nothing is launched when a call fails. Host-side checks
+ *   look only at scalar arguments and pointer values, never at device memory.
+ *   There is no silent fallback: an unsupported shape or dtype is an error.
+ * - Data-dependent problems (a slot, block id or context length out of range,
+ *   a scale beyond FP16) are found in the kernels: the offending token, page
+ *   or row is skipped and, when `err_flag` (device int32, may be NULL) is
+ *   given, the matching PDAKV_EFLAG_* bit is OR-ed into it. The caller clears
+ *   it.
+ * - Supported: head_dim 64 or 128; block_size 16; num_q_heads a multiple of
+ *   num_kv_heads with at most 16 query heads per KV head; q/K/V dtype fp16 or
+ *   bf16; FP16 scales always.
+ * - Strides are in elements and must be >= 0; the innermost (head_dim)
+ *   stride of q and out is 1.
+ *
+ * Page layout (the contract between writer, reader and any other user)
+ * --------------------------------------------------------------------
+ * One pool per layer: uint8 pool[num_blocks][page_bytes], 16-byte aligned.
+ * A token at position t of a sequence lives in page block_table[t / 16] at
+ * slot t % 16; writers address it as slot_id = page * 16 + t % 16.
+ *
+ * INT8 page (kv_format PDAKV_KV_INT8_SYM), for each KV head h in order, a head
+ * block of 2*16*D + 4*16 bytes:
+ *     +0          K codes  int8 [16][D]        token-major
+ *     +16*D       V codes  int8 [4][D][4]      byte (p/4)*4*D + 4*d + p%4
+ *     +32*D       K scales fp16 [16]
+ *     +32*D+32    V scales fp16 [16]
+ *   page_bytes = Hkv * (32*D + 64): 33,280 for (16, 8, 128), 4,224 for
+ *   (16, 2, 64). The V codes are grouped four tokens at a time so that one
+ *   32-bit word holds one dimension of four consecutive tokens, which is the
+ *   operand shape of the matrix instructions the reader uses.
+ * 16-bit page (kv_format PDAKV_KV_16BIT), for each KV head h, 4*16*D bytes:
+ *     +0          K  [16][D]                    token-major
+ *     +32*D       V  [4][D][4]                  element (p/4)*4*D + 4*d + p%4
+ *   page_bytes = Hkv * 64 * D: 65,536 for (16, 8, 128).
+ */
+#ifndef PDAKV_H
+#define PDAKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes --------------------------------------------------- */
+#define PDAKV_OK               0
+#define PDAKV_ERR_INVALID_ARG (-1) /* null pointer, negative size/stride, misalignment */
+#define PDAKV_ERR_UNSUPPORTED (-2) /* shape outside the supported set */
+#define PDAKV_ERR_DTYPE       (-3) /* dtype code not accepted by this call */
+#define PDAKV_ERR_WORKSPACE   (-4) /* workspace missing or too small */
+#define PDAKV_ERR_HIP         (-5) /* a HIP runtime call or kernel launch failed */
+#define PDAKV_ERR_NO_DEVICE   (-6) /* no usable HIP device */
+
+/* ---- dtype codes ------------------------------------------------------ */
+#define PDAKV_DTYPE_F32  0
+#define PDAKV_DTYPE_F16  1
+#define PDAKV_DTYPE_BF16 2
+
+/* ---- KV page formats -------------------------------------------------- */
+#define PDAKV_KV_INT8_SYM 1
+#define PDAKV_KV_16BIT    2
+
+/* ---- bits OR-ed into the optional device error flag ------------------- */
+#define PDAKV_EFLAG_SLOT_RANGE    1 /* slot_id >= num_blocks * block_size   */
+#define PDAKV_EFLAG_BLOCK_RANGE   2 /* block table entry outside the pool   */
+#define PDAKV_EFLAG_CONTEXT_RANGE 4 /* context_lens[b] < 0 or > max_context */
+#define PDAKV_EFLAG_SCALE_RANGE   8 /* absmax / 127 beyond the FP16 range   */
+
+/* ---- capability bits -------------------------------------------------- */
+#define PDAKV_CAP_GFX950      1u  /* current device is gfx950             */
+#define PDAKV_CAP_HEAD_DIM_64 2u
+#define PDAKV_CAP_HEAD_DIM_128 4u
+#define PDAKV_CAP_BLOCK_16    8u
+#define PDAKV_CAP_F16         16u
+#define PDAKV_CAP_BF16        32u
+
+/* Library version, major*10000 + minor*100 + patch. */
+int pdakv_version(void);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* pdakv_status_string(int status);
+
+/* Bytes of one page of the given format (MoE-Infinity PR #183, "Precision &
+ * memory": 33,280 INT8 vs 65,536 FP16 bytes for block 16, 8 KV heads,
+ * head_dim 128). Returns 0 for an unsupported combination. Pure host
+ * arithmetic; needs no device. */
+size_t pdakv_page_bytes(int kv_format, int block_size, int num_kv_heads, int head_dim);
+
+/* Capability probe of the current HIP device (the native-binding check of
+ * MoE-Infinity PR #183, "What landed", runtime-integration bullet). Writes the
+ * PDAKV_CAP_* bits to *flags_out. Returns PDAKV_ERR_NO_DEVICE without a
+ * device, PDAKV_ERR_INVALID_ARG for a NULL flags_out. */
+int pdakv_capabilities(uint32_t* flags_out);
+
+/* Split plan the decode calls use for these sizes: the context of every
+ * sequence is cut into chunks of *pages_per_split pages that run in separate
+ * workgroups and are merged afterwards; *max_splits chunks cover
+ * max_context_len. Either output pointer may be NULL. Returns
+ * PDAKV_ERR_INVALID_ARG for negative sizes. Host arithmetic only. */
+int pdakv_decode_plan(int num_seqs, int num_kv_heads, int max_context_len,
+                      int* pages_per_split, int* max_splits);
+
+/* Device workspace the decode calls need for these sizes (0 when no split
+ * merge is needed). The same value serves the INT8 and the 16-bit decode. */
+size_t pdakv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                    int head_dim, int max_context_len);
+
+/* Quantize-on-write (MoE-Infinity PR #183, "What landed": write_chunk into
+ * the paged store; the quantizer of the format-contract bullet).
+ *   k_src, v_src   device, [num_tokens][num_kv_heads][head_dim] of src_dtype
+ *                  (PDAKV_DTYPE_F16 or _BF16) addressed through the given
+ *                  element strides, so views of a fused QKV buffer can be
+ *                  passed without a copy (K/V are read in model precision
+ *                  before quantization, as InfiniLM PR #553 "Summary" asks).
+ *   slot_mapping   device int32 [num_tokens]; slot_id = page * block_size +
+ *                  offset; a negative entry marks a padding token, which is
+ *                  skipped; an entry >= num_blocks * block_size is skipped
+ *                  and flagged PDAKV_EFLAG_SLOT_RANGE.
+ *   kv_pool        device, num_blocks pages of the INT8 format.
+ * Two tokens of one call must not name the same slot. Rows whose scale would
+ * exceed 65504 are left unwritten and flagged PDAKV_EFLAG_SCALE_RANGE. */
+int kv_quant_int8_sym_write(const void* k_src, const void* v_src, int src_dtype,
+                            int64_t num_tokens, int num_kv_heads, int head_dim,
+                            int64_t k_stride_tok, int64_t k_stride_head, int64_t k_stride_dim,
+                            int64_t v_stride_tok, int64_t v_stride_head, int64_t v_stride_dim,
+                            const int32_t* slot_mapping, void* kv_pool, int64_t num_blocks,
+                            int block_size, int32_t* err_flag, void* stream);
+
+/* Plain 16-bit write into a PDAKV_KV_16BIT pool (fills the control cache);
+ * same arguments and conventions as kv_quant_int8_sym_write, values copied
+ * unchanged. */
+int kv_write_16bit(const void* k_src, const void* v_src, int src_dtype,
+                   int64_t num_tokens, int num_kv_heads, int head_dim,
+                   int64_t k_stride_tok, int64_t k_stride_head, int64_t k_stride_dim,
+                   int64_t v_stride_tok, int64_t v_stride_head, int64_t v_stride_dim,
+                   const int32_t* slot_mapping, void* kv_pool, int64_t num_blocks,
+                   int block_size, int32_t* err_flag, void* stream);
+
+/* Paged decode over INT8 pages (MoE-Infinity PR #183, "What landed",
+ * native-kernel bullet: INT8 + FP16-scale paged decode with FP32
+ * accumulation, MHA/GQA).
+ *   out            device [num_seqs][num_q_heads][head_dim] of out_dtype
+ *                  (F32, F16 or BF16), strides out_stride_seq/_head.
+ *   q              device [num_seqs][num_q_heads][head_dim], q_dtype F16/BF16.
+ *   kv_pool        INT8 pool of num_blocks pages (layout above).
+ *   block_tables   device int32 [num_seqs][block_table_stride]; row b lists the
+ *                  pages of sequence b; only the first ceil(context_lens[b]/16)
+ *                  entries are read.
+ *   context_lens   device int32 [num_seqs]; 0 gives a zero output row; values
+ *                  above max_context_len are clamped and flagged.
+ *   max_context_len host upper bound of context_lens (sizes the launch).
+ *   sm_scale       logit scale (usually 1/sqrt(head_dim)).
+ *   workspace      device scratch of at least pdakv_decode_workspace_bytes();
+ *                  may be NULL when that is 0. Its contents need no
+ *                  initialization and are garbage afterwards.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads). The output
+ * must not alias any input. */
+int paged_attn_decode_int8(void* out, int out_dtype, int64_t out_stride_seq,
+                           int64_t out_stride_head, const void* q, int q_dtype,
+                           int64_t q_stride_seq, int64_t q_stride_head, const void* kv_pool,
+                           int64_t num_blocks, int block_size, const int32_t* block_tables,
+                           int64_t block_table_stride, const int32_t* context_lens,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int max_context_len, float sm_scale, void* workspace,
+                           size_t workspace_bytes, int32_t* err_flag, void* stream);
+
+/* Paged decode over 16-bit pages (the FP16-KV control; MoE-Infinity PR #183,
+ * "What landed": the pre-existing FP16 paged-attention kernel). Same
+ * arguments as paged_attn_decode_int8; kv_pool is a PDAKV_KV_16BIT pool whose
+ * values have the dtype q_dtype. */
+int paged_attn_decode_fp16(void* out, int out_dtype, int64_t out_stride_seq,
+                           int64_t out_stride_head, const void* q, int q_dtype,
+                           int64_t q_stride_seq, int64_t q_stride_head, const void* kv_pool,
+                           int64_t num_blocks, int block_size, const int32_t* block_tables,
+                           int64_t block_table_stride, const int32_t* context_lens,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int max_context_len, float sm_scale, void* workspace,
+                           size_t workspace_bytes, int32_t* err_flag, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PDAKV_H */

@@ -1,0 +1,187 @@
+"""ctypes binding of libpdakv.so — argument marshalling only.
+
+Every function here has the name of the C entry point it calls, takes torch
+tensors (device memory) and passes their pointers, dtype codes and element
+strides. No computation happens in Python: if the shared library is missing,
+importing this module fails.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpdakv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m paged_decode_attention_kv_amd.build` "
+        "(the HIP library is required; there is no fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# status / dtype / format codes (mirrors include/pdakv.h)
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED = -2
+ERR_DTYPE = -3
+ERR_WORKSPACE = -4
+ERR_HIP = -5
+ERR_NO_DEVICE = -6
+DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
+KV_INT8_SYM, KV_16BIT = 1, 2
+EFLAG_SLOT_RANGE, EFLAG_BLOCK_RANGE, EFLAG_CONTEXT_RANGE, EFLAG_SCALE_RANGE = 1, 2, 4, 8
+CAP_GFX950 = 1
+
+_c_i64, _c_int, _c_vp, _c_f = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float
+
+_SIGS = {
+    "pdakv_version": (_c_int, []),
+    "pdakv_status_string": (ctypes.c_char_p, [_c_int]),
+    "pdakv_page_bytes": (ctypes.c_size_t, [_c_int, _c_int, _c_int, _c_int]),
+    "pdakv_capabilities": (_c_int, [ctypes.POINTER(ctypes.c_uint32)]),
+    "pdakv_decode_plan": (_c_int, [_c_int, _c_int, _c_int, ctypes.POINTER(_c_int),
+                                   ctypes.POINTER(_c_int)]),
+    "pdakv_decode_workspace_bytes": (ctypes.c_size_t, [_c_int] * 5),
+    "kv_quant_int8_sym_write": (_c_int, [_c_vp, _c_vp, _c_int, _c_i64, _c_int, _c_int] +
+                                [_c_i64] * 6 + [_c_vp, _c_vp, _c_i64, _c_int, _c_vp, _c_vp]),
+    "kv_write_16bit": (_c_int, [_c_vp, _c_vp, _c_int, _c_i64, _c_int, _c_int] +
+                       [_c_i64] * 6 + [_c_vp, _c_vp, _c_i64, _c_int, _c_vp, _c_vp]),
+    "paged_attn_decode_int8": (_c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_int, _c_i64,
+                                        _c_i64, _c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_vp,
+                                        _c_int, _c_int, _c_int, _c_int, _c_int, _c_f, _c_vp,
+                                        ctypes.c_size_t, _c_vp, _c_vp]),
+}
+_SIGS["paged_attn_decode_fp16"] = _SIGS["paged_attn_decode_int8"]
+
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class PdakvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {pdakv_status_string(status)} (status {status})")
+
+
+def _check(fn: str, status: int) -> None:
+    if status != OK:
+        raise PdakvError(fn, status)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    return {torch.float32: DTYPE_F32, torch.float16: DTYPE_F16,
+            torch.bfloat16: DTYPE_BF16}.get(t, -99)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+# ---- host-only queries ----------------------------------------------------
+
+def pdakv_version() -> int:
+    return _lib.pdakv_version()
+
+
+def pdakv_status_string(status: int) -> str:
+    return _lib.pdakv_status_string(status).decode()
+
+
+def pdakv_page_bytes(kv_format: int, block_size: int, num_kv_heads: int, head_dim: int) -> int:
+    return int(_lib.pdakv_page_bytes(kv_format, block_size, num_kv_heads, head_dim))
+
+
+def pdakv_capabilities() -> int:
+    flags = ctypes.c_uint32(0)
+    _check("pdakv_capabilities", _lib.pdakv_capabilities(ctypes.byref(flags)))
+    return int(flags.value)
+
+
+def pdakv_decode_plan(num_seqs: int, num_kv_heads: int, max_context_len: int):
+    pps, n = _c_int(0), _c_int(0)
+    _check("pdakv_decode_plan", _lib.pdakv_decode_plan(num_seqs, num_kv_heads, max_context_len,
+                                                       ctypes.byref(pps), ctypes.byref(n)))
+    return pps.value, n.value
+
+
+def pdakv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                                 head_dim: int, max_context_len: int) -> int:
+    return int(_lib.pdakv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                 max_context_len))
+
+
+# ---- device entry points --------------------------------------------------
+
+def _write(fn_name, k, v, slot_mapping, kv_pool, num_blocks, block_size, err_flag, stream):
+    T, hkv, d = k.shape
+    if tuple(v.shape) != (T, hkv, d) or v.dtype != k.dtype:
+        raise ValueError("k and v must have the same shape and dtype")
+    st = getattr(_lib, fn_name)(
+        _ptr(k), _ptr(v), _dtype_code(k.dtype), T, hkv, d,
+        k.stride(0), k.stride(1), k.stride(2), v.stride(0), v.stride(1), v.stride(2),
+        _ptr(slot_mapping), _ptr(kv_pool), num_blocks, block_size, _ptr(err_flag),
+        _stream(stream))
+    _check(fn_name, st)
+
+
+def kv_quant_int8_sym_write(k, v, slot_mapping, kv_pool, num_blocks: int, block_size: int = 16,
+                            err_flag=None, stream=None) -> None:
+    """Quantize k, v [T, Hkv, D] (fp16/bf16, any strides) into the INT8 pool."""
+    _write("kv_quant_int8_sym_write", k, v, slot_mapping, kv_pool, num_blocks, block_size,
+           err_flag, stream)
+
+
+def kv_write_16bit(k, v, slot_mapping, kv_pool, num_blocks: int, block_size: int = 16,
+                   err_flag=None, stream=None) -> None:
+    """Copy k, v [T, Hkv, D] into a 16-bit pool of the same dtype."""
+    _write("kv_write_16bit", k, v, slot_mapping, kv_pool, num_blocks, block_size, err_flag,
+           stream)
+
+
+def _decode(fn_name, out, q, kv_pool, num_blocks, block_tables, context_lens, num_kv_heads,
+            max_context_len, sm_scale, workspace, block_size, err_flag, stream):
+    B, hq, d = q.shape
+    if q.stride(2) != 1 or out.stride(2) != 1:
+        raise ValueError("the head_dim stride of q and out must be 1")
+    if tuple(out.shape) != (B, hq, d):
+        raise ValueError("out must have the shape of q")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = getattr(_lib, fn_name)(
+        _ptr(out), _dtype_code(out.dtype), out.stride(0), out.stride(1),
+        _ptr(q), _dtype_code(q.dtype), q.stride(0), q.stride(1),
+        _ptr(kv_pool), num_blocks, block_size, _ptr(block_tables), block_tables.stride(0),
+        _ptr(context_lens), B, hq, num_kv_heads, d, max_context_len, float(sm_scale),
+        _ptr(workspace), ws_bytes, _ptr(err_flag), _stream(stream))
+    _check(fn_name, st)
+
+
+def paged_attn_decode_int8(out, q, kv_pool, num_blocks: int, block_tables, context_lens,
+                           num_kv_heads: int, max_context_len: int, sm_scale: float,
+                           workspace=None, block_size: int = 16, err_flag=None,
+                           stream=None) -> None:
+    """Decode over INT8 pages; writes out [B, Hq, D] (f32/f16/bf16)."""
+    _decode("paged_attn_decode_int8", out, q, kv_pool, num_blocks, block_tables, context_lens,
+            num_kv_heads, max_context_len, sm_scale, workspace, block_size, err_flag, stream)
+
+
+def paged_attn_decode_fp16(out, q, kv_pool, num_blocks: int, block_tables, context_lens,
+                           num_kv_heads: int, max_context_len: int, sm_scale: float,
+                           workspace=None, block_size: int = 16, err_flag=None,
+                           stream=None) -> None:
+    """Decode over 16-bit (q's dtype) pages; writes out [B, Hq, D]."""
+    _decode("paged_attn_decode_fp16", out, q, kv_pool, num_blocks, block_tables, context_lens,
+            num_kv_heads, max_context_len, sm_scale, workspace, block_size, err_flag, stream)

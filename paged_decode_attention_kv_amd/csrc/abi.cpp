@@ -1,0 +1,285 @@
+// C-ABI entry points of libpdakv.so: argument validation, split planning,
+// and dispatch to the gfx950 kernels. See include/pdakv.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/pdakv.h"
+#include "launch.h"
+
+namespace {
+
+using pdakv::DecodeArgs;
+using pdakv::WriteArgs;
+
+constexpr int kTargetWorkgroups = 2048;  // about 8 per CU on 256 CUs
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Pages per workgroup and number of splits for a launch. Aim for about
+// kTargetWorkgroups workgroups; each split holds 16..64 pages (a multiple of
+// the four waves) so no workgroup is too small to amortize its start-up and
+// none is large enough to leave the chip idle at the tail.
+void plan(int num_seqs, int num_kv_heads, int max_context_len, int* pps, int* nsplit) {
+  const int64_t max_pages = ceil_div(max_context_len, pdakv::kBlockSize);
+  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  int64_t p = ceil_div(units * max_pages, kTargetWorkgroups);
+  p = ceil_div(p, pdakv::kWaves) * pdakv::kWaves;
+  if (p < 16) p = 16;
+  if (p > pdakv::kMaxPagesPerSplit) p = pdakv::kMaxPagesPerSplit;
+  *pps = static_cast<int>(p);
+  const int64_t n = ceil_div(max_pages, p);
+  *nsplit = static_cast<int>(n < 1 ? 1 : n);
+}
+
+int check_write(const void* k_src, const void* v_src, int src_dtype, int64_t num_tokens,
+                int num_kv_heads, int head_dim, int64_t kst, int64_t ksh, int64_t ksd,
+                int64_t vst, int64_t vsh, int64_t vsd, const int32_t* slot_mapping,
+                void* kv_pool, int64_t num_blocks, int block_size) {
+  if (src_dtype != PDAKV_DTYPE_F16 && src_dtype != PDAKV_DTYPE_BF16) return PDAKV_ERR_DTYPE;
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return PDAKV_ERR_INVALID_ARG;
+  if (kst < 0 || ksh < 0 || ksd < 0 || vst < 0 || vsh < 0 || vsd < 0)
+    return PDAKV_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim) || block_size != pdakv::kBlockSize)
+    return PDAKV_ERR_UNSUPPORTED;
+  if (num_blocks * block_size > INT32_MAX) return PDAKV_ERR_UNSUPPORTED;  // int32 slots
+  if (num_tokens == 0) return PDAKV_OK;
+  if (!k_src || !v_src || !slot_mapping || !kv_pool) return PDAKV_ERR_INVALID_ARG;
+  if (!aligned16(kv_pool)) return PDAKV_ERR_INVALID_ARG;
+  return PDAKV_OK;
+}
+
+int check_decode(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, const void* q,
+                 int q_dtype, int64_t q_ss, int64_t q_sh, const void* kv_pool,
+                 int64_t num_blocks, int block_size, const int32_t* block_tables,
+                 int64_t bt_stride, const int32_t* context_lens, int num_seqs, int num_q_heads,
+                 int num_kv_heads, int head_dim, int max_context_len, float sm_scale,
+                 const void* workspace, size_t workspace_bytes) {
+  if (q_dtype != PDAKV_DTYPE_F16 && q_dtype != PDAKV_DTYPE_BF16) return PDAKV_ERR_DTYPE;
+  if (out_dtype != PDAKV_DTYPE_F32 && out_dtype != PDAKV_DTYPE_F16 &&
+      out_dtype != PDAKV_DTYPE_BF16)
+    return PDAKV_ERR_DTYPE;
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
+      num_blocks < 0 || bt_stride < 0 || out_ss < 0 || out_sh < 0 || q_ss < 0 || q_sh < 0)
+    return PDAKV_ERR_INVALID_ARG;
+  if (!std::isfinite(sm_scale)) return PDAKV_ERR_INVALID_ARG;
+  if (num_q_heads % num_kv_heads != 0) return PDAKV_ERR_UNSUPPORTED;
+  if (num_q_heads / num_kv_heads > pdakv::kMaxGroup) return PDAKV_ERR_UNSUPPORTED;
+  if (!supported_head_dim(head_dim) || block_size != pdakv::kBlockSize)
+    return PDAKV_ERR_UNSUPPORTED;
+  if (bt_stride < ceil_div(max_context_len, block_size)) return PDAKV_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PDAKV_OK;
+  if (!out || !q || !block_tables || !context_lens) return PDAKV_ERR_INVALID_ARG;
+  if (max_context_len > 0 && !kv_pool) return PDAKV_ERR_INVALID_ARG;
+  if (kv_pool && !aligned16(kv_pool)) return PDAKV_ERR_INVALID_ARG;
+  const size_t need = pdakv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
+                                                   head_dim, max_context_len);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PDAKV_ERR_WORKSPACE;
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 3u)) return PDAKV_ERR_INVALID_ARG;
+  // grid limits: sequences on grid z, (sequence, head) pairs on grid x
+  if (num_seqs > 65535 || num_kv_heads > 65535) return PDAKV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(num_seqs) * num_q_heads > INT32_MAX) return PDAKV_ERR_UNSUPPORTED;
+  return PDAKV_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PDAKV_OK : PDAKV_ERR_HIP; }
+
+template <bool Int8>
+int decode_common(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, const void* q,
+                  int q_dtype, int64_t q_ss, int64_t q_sh, const void* kv_pool,
+                  int64_t num_blocks, int block_size, const int32_t* block_tables,
+                  int64_t bt_stride, const int32_t* context_lens, int num_seqs,
+                  int num_q_heads, int num_kv_heads, int head_dim, int max_context_len,
+                  float sm_scale, void* workspace, size_t workspace_bytes, int32_t* err_flag,
+                  void* stream) {
+  int st = check_decode(out, out_dtype, out_ss, out_sh, q, q_dtype, q_ss, q_sh, kv_pool,
+                        num_blocks, block_size, block_tables, bt_stride, context_lens,
+                        num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                        sm_scale, workspace, workspace_bytes);
+  if (st != PDAKV_OK || num_seqs == 0) return st;
+  DecodeArgs a{};
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.out_ss = out_ss;
+  a.out_sh = out_sh;
+  a.q = q;
+  a.q_ss = q_ss;
+  a.q_sh = q_sh;
+  a.pool = static_cast<const uint8_t*>(kv_pool);
+  a.num_blocks = num_blocks;
+  a.page_bytes = static_cast<int64_t>(pdakv_page_bytes(
+      Int8 ? PDAKV_KV_INT8_SYM : PDAKV_KV_16BIT, block_size, num_kv_heads, head_dim));
+  a.bt = block_tables;
+  a.bt_stride = bt_stride;
+  a.ctx = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.max_ctx = max_context_len;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.ws = static_cast<float*>(workspace);
+  plan(num_seqs, num_kv_heads, max_context_len, &a.pages_per_split, &a.max_splits);
+  a.err = err_flag;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = q_dtype == PDAKV_DTYPE_BF16;
+  return hip_status(Int8 ? pdakv::launch_decode_int8(a, head_dim, bf16, s)
+                         : pdakv::launch_decode_16bit(a, head_dim, bf16, s));
+}
+
+template <bool Int8>
+int write_common(const void* k_src, const void* v_src, int src_dtype, int64_t num_tokens,
+                 int num_kv_heads, int head_dim, int64_t kst, int64_t ksh, int64_t ksd,
+                 int64_t vst, int64_t vsh, int64_t vsd, const int32_t* slot_mapping,
+                 void* kv_pool, int64_t num_blocks, int block_size, int32_t* err_flag,
+                 void* stream) {
+  int st = check_write(k_src, v_src, src_dtype, num_tokens, num_kv_heads, head_dim, kst, ksh,
+                       ksd, vst, vsh, vsd, slot_mapping, kv_pool, num_blocks, block_size);
+  if (st != PDAKV_OK || num_tokens == 0) return st;
+  if (num_tokens * num_kv_heads / 4 >= INT32_MAX) return PDAKV_ERR_UNSUPPORTED;
+  WriteArgs a{};
+  a.k = k_src;
+  a.v = v_src;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.k_st = kst;
+  a.k_sh = ksh;
+  a.k_sd = ksd;
+  a.v_st = vst;
+  a.v_sh = vsh;
+  a.v_sd = vsd;
+  a.slots = slot_mapping;
+  a.pool = static_cast<uint8_t*>(kv_pool);
+  a.num_blocks = num_blocks;
+  a.page_bytes = static_cast<int64_t>(pdakv_page_bytes(
+      Int8 ? PDAKV_KV_INT8_SYM : PDAKV_KV_16BIT, block_size, num_kv_heads, head_dim));
+  a.err = err_flag;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(Int8 ? pdakv::launch_quant_write_int8(a, head_dim,
+                                                          src_dtype == PDAKV_DTYPE_BF16, s)
+                         : pdakv::launch_write_16bit(a, head_dim, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pdakv_version(void) { return 100; /* 0.1.0 */ }
+
+const char* pdakv_status_string(int status) {
+  switch (status) {
+    case PDAKV_OK: return "ok";
+    case PDAKV_ERR_INVALID_ARG: return "invalid argument";
+    case PDAKV_ERR_UNSUPPORTED: return "unsupported shape";
+    case PDAKV_ERR_DTYPE: return "unsupported dtype";
+    case PDAKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PDAKV_ERR_HIP: return "HIP runtime or launch error";
+    case PDAKV_ERR_NO_DEVICE: return "no usable HIP device";
+    default: return "unknown status";
+  }
+}
+
+size_t pdakv_page_bytes(int kv_format, int block_size, int num_kv_heads, int head_dim) {
+  if (block_size <= 0 || block_size % 4 != 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+  const size_t bs = static_cast<size_t>(block_size), d = static_cast<size_t>(head_dim);
+  const size_t h = static_cast<size_t>(num_kv_heads);
+  if (kv_format == PDAKV_KV_INT8_SYM) return h * (2 * bs * d + 4 * bs);
+  if (kv_format == PDAKV_KV_16BIT) return h * 4 * bs * d;
+  return 0;
+}
+
+int pdakv_capabilities(uint32_t* flags_out) {
+  if (!flags_out) return PDAKV_ERR_INVALID_ARG;
+  *flags_out = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PDAKV_ERR_NO_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return PDAKV_ERR_NO_DEVICE;
+  uint32_t f = PDAKV_CAP_HEAD_DIM_64 | PDAKV_CAP_HEAD_DIM_128 | PDAKV_CAP_BLOCK_16 |
+               PDAKV_CAP_F16 | PDAKV_CAP_BF16;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) f |= PDAKV_CAP_GFX950;
+  *flags_out = f;
+  return PDAKV_OK;
+}
+
+int pdakv_decode_plan(int num_seqs, int num_kv_heads, int max_context_len, int* pages_per_split,
+                      int* max_splits) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0) return PDAKV_ERR_INVALID_ARG;
+  int p = 0, n = 0;
+  plan(num_seqs, num_kv_heads, max_context_len, &p, &n);
+  if (pages_per_split) *pages_per_split = p;
+  if (max_splits) *max_splits = n;
+  return PDAKV_OK;
+}
+
+size_t pdakv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
+                                    int head_dim, int max_context_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len < 0)
+    return 0;
+  int p = 0, n = 0;
+  plan(num_seqs, num_kv_heads, max_context_len, &p, &n);
+  if (n <= 1) return 0;
+  return static_cast<size_t>(num_seqs) * num_q_heads * n * (head_dim + 2) * sizeof(float);
+}
+
+int kv_quant_int8_sym_write(const void* k_src, const void* v_src, int src_dtype,
+                            int64_t num_tokens, int num_kv_heads, int head_dim,
+                            int64_t k_stride_tok, int64_t k_stride_head, int64_t k_stride_dim,
+                            int64_t v_stride_tok, int64_t v_stride_head, int64_t v_stride_dim,
+                            const int32_t* slot_mapping, void* kv_pool, int64_t num_blocks,
+                            int block_size, int32_t* err_flag, void* stream) {
+  return write_common<true>(k_src, v_src, src_dtype, num_tokens, num_kv_heads, head_dim,
+                            k_stride_tok, k_stride_head, k_stride_dim, v_stride_tok,
+                            v_stride_head, v_stride_dim, slot_mapping, kv_pool, num_blocks,
+                            block_size, err_flag, stream);
+}
+
+int kv_write_16bit(const void* k_src, const void* v_src, int src_dtype, int64_t num_tokens,
+                   int num_kv_heads, int head_dim, int64_t k_stride_tok, int64_t k_stride_head,
+                   int64_t k_stride_dim, int64_t v_stride_tok, int64_t v_stride_head,
+                   int64_t v_stride_dim, const int32_t* slot_mapping, void* kv_pool,
+                   int64_t num_blocks, int block_size, int32_t* err_flag, void* stream) {
+  return write_common<false>(k_src, v_src, src_dtype, num_tokens, num_kv_heads, head_dim,
+                             k_stride_tok, k_stride_head, k_stride_dim, v_stride_tok,
+                             v_stride_head, v_stride_dim, slot_mapping, kv_pool, num_blocks,
+                             block_size, err_flag, stream);
+}
+
+int paged_attn_decode_int8(void* out, int out_dtype, int64_t out_stride_seq,
+                           int64_t out_stride_head, const void* q, int q_dtype,
+                           int64_t q_stride_seq, int64_t q_stride_head, const void* kv_pool,
+                           int64_t num_blocks, int block_size, const int32_t* block_tables,
+                           int64_t block_table_stride, const int32_t* context_lens,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int max_context_len, float sm_scale, void* workspace,
+                           size_t workspace_bytes, int32_t* err_flag, void* stream) {
+  return decode_common<true>(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
+                             q_stride_seq, q_stride_head, kv_pool, num_blocks, block_size,
+                             block_tables, block_table_stride, context_lens, num_seqs,
+                             num_q_heads, num_kv_heads, head_dim, max_context_len, sm_scale,
+                             workspace, workspace_bytes, err_flag, stream);
+}
+
+int paged_attn_decode_fp16(void* out, int out_dtype, int64_t out_stride_seq,
+                           int64_t out_stride_head, const void* q, int q_dtype,
+                           int64_t q_stride_seq, int64_t q_stride_head, const void* kv_pool,
+                           int64_t num_blocks, int block_size, const int32_t* block_tables,
+                           int64_t block_table_stride, const int32_t* context_lens,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int max_context_len, float sm_scale, void* workspace,
+                           size_t workspace_bytes, int32_t* err_flag, void* stream) {
+  return decode_common<false>(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
+                              q_stride_seq, q_stride_head, kv_pool, num_blocks, block_size,
+                              block_tables, block_table_stride, context_lens, num_seqs,
+                              num_q_heads, num_kv_heads, head_dim, max_context_len, sm_scale,
+                              workspace, workspace_bytes, err_flag, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Internal interface between the C-ABI layer (abi.cpp) and the kernel
+// translation units. Not installed; the public contract is include/pdakv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pdakv {
+
+constexpr int kBlockSize = 16;        // tokens per page
+constexpr int kMaxGroup = 16;         // query heads per KV head (one MFMA N tile)
+constexpr int kWaves = 4;             // waves per decode workgroup
+constexpr int kMaxPagesPerSplit = 64; // LDS block-table cache size
+
+struct WriteArgs {
+  const void* k;
+  const void* v;
+  int64_t num_tokens;
+  int num_kv_heads;
+  int64_t k_st, k_sh, k_sd;  // element strides
+  int64_t v_st, v_sh, v_sd;
+  const int32_t* slots;
+  uint8_t* pool;
+  int64_t num_blocks;
+  int64_t page_bytes;
+  int32_t* err;
+};
+
+struct DecodeArgs {
+  void* out;
+  int out_dtype;
+  int64_t out_ss, out_sh;
+  const void* q;
+  int64_t q_ss, q_sh;
+  const uint8_t* pool;
+  int64_t num_blocks;
+  int64_t page_bytes;
+  const int32_t* bt;
+  int64_t bt_stride;
+  const int32_t* ctx;
+  int num_seqs, num_q_heads, num_kv_heads, group, max_ctx;
+  float scale_log2;  // sm_scale * log2(e): logits are kept in base 2
+  float* ws;         // split partials [B][Hq][max_splits][D + 2]
+  int pages_per_split, max_splits;
+  int32_t* err;
+};
+
+// Each returns hipSuccess or the launch error. Arguments are validated by the
+// caller; the launchers only pick the template instance.
+hipError_t launch_quant_write_int8(const WriteArgs& a, int head_dim, bool src_bf16,
+                                   hipStream_t s);
+hipError_t launch_write_16bit(const WriteArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_decode_int8(const DecodeArgs& a, int head_dim, bool q_bf16, hipStream_t s);
+hipError_t launch_decode_16bit(const DecodeArgs& a, int head_dim, bool kv_bf16,
+                               hipStream_t s);
+
+}  // namespace pdakv

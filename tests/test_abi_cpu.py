@@ -1,0 +1,120 @@
+"""CPU checks of the C-ABI library: it loads, exports every function the
+header declares, and its host-side validation returns the documented status
+codes before any device work (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "pdakv.h")
+
+
+@pytest.fixture(scope="module")
+def P():
+    from paged_decode_attention_kv_amd import _lib as lib_mod
+    return lib_mod
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function(P):
+    names = _declared_functions()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(P._lib, n), n
+    assert set(names) == set(P.EXPORTED)
+
+
+def test_version_and_status_strings(P):
+    assert P.pdakv_version() >= 100
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        s = P.pdakv_status_string(code)
+        assert s and s != "unknown status"
+    assert P.pdakv_status_string(-99) == "unknown status"
+
+
+def test_page_bytes_match_the_printed_totals(P, golden):
+    (row,) = golden("page_bytes.txt")
+    bs, hkv, d, i8, f16, ratio = row[0].split()
+    assert P.pdakv_page_bytes(P.KV_INT8_SYM, int(bs), int(hkv), int(d)) == int(i8)
+    assert P.pdakv_page_bytes(P.KV_16BIT, int(bs), int(hkv), int(d)) == int(f16)
+    assert P.pdakv_page_bytes(P.KV_INT8_SYM, 16, 2, 64) == 4224
+    assert P.pdakv_page_bytes(7, 16, 8, 128) == 0
+    assert P.pdakv_page_bytes(P.KV_INT8_SYM, 15, 8, 128) == 0
+
+
+def test_page_bytes_agree_with_oracle(P):
+    import oracle
+    for fmt in (P.KV_INT8_SYM, P.KV_16BIT):
+        for hkv in (1, 2, 8, 32):
+            for d in (64, 128):
+                assert P.pdakv_page_bytes(fmt, 16, hkv, d) == oracle.page_bytes(fmt, 16, hkv, d)
+
+
+@pytest.mark.parametrize("B,hkv,L", [(1, 8, 256), (1, 8, 2048), (64, 8, 8193), (8, 8, 32768),
+                                     (32, 2, 4104), (8, 8, 8192), (3, 1, 0), (1, 32, 1)])
+def test_decode_plan_is_consistent(P, B, hkv, L):
+    pps, n = P.pdakv_decode_plan(B, hkv, L)
+    pages = -(-L // 16)
+    assert 16 <= pps <= 64 and pps % 4 == 0
+    assert n >= 1 and (n - 1) * pps < max(pages, 1) <= n * pps
+    ws = P.pdakv_decode_workspace_bytes(B, 4 * hkv, hkv, 128, L)
+    assert ws == (0 if n == 1 else B * 4 * hkv * n * 130 * 4)
+
+
+def test_capabilities_without_device(P):
+    flags = ctypes.c_uint32(123)
+    assert P._lib.pdakv_capabilities(None) == P.ERR_INVALID_ARG
+    st = P._lib.pdakv_capabilities(ctypes.byref(flags))
+    assert st in (P.OK, P.ERR_NO_DEVICE)
+
+
+FAKE = 0x10000  # a non-null, 16-byte aligned pointer value that is never dereferenced
+
+
+def _write_args(**kw):
+    a = dict(k=FAKE, v=FAKE, dtype=1, T=4, hkv=8, d=128, kst=1024, ksh=128, ksd=1, vst=1024,
+             vsh=128, vsd=1, slots=FAKE, pool=FAKE, nblk=4, bs=16, err=None, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("fn", ["kv_quant_int8_sym_write", "kv_write_16bit"])
+@pytest.mark.parametrize("change,status", [
+    (dict(dtype=0), -3), (dict(dtype=5), -3), (dict(T=-1), -1), (dict(hkv=0), -1),
+    (dict(d=96), -2), (dict(bs=32), -2), (dict(ksd=-1), -1), (dict(vst=-4), -1),
+    (dict(k=None), -1), (dict(slots=None), -1), (dict(pool=FAKE + 4), -1),
+    (dict(nblk=-1), -1), (dict(nblk=2 ** 28), -2), (dict(T=0, k=None), 0),
+])
+def test_write_validation(P, fn, change, status):
+    assert getattr(P._lib, fn)(*_write_args(**change)) == status
+
+
+def _decode_args(**kw):
+    a = dict(out=FAKE, odt=0, oss=4096, osh=128, q=FAKE, qdt=1, qss=4096, qsh=128, pool=FAKE,
+             nblk=16, bs=16, bt=FAKE, bts=16, ctx=FAKE, B=1, hq=32, hkv=8, d=128, maxL=256,
+             sm=0.088, ws=None, wsb=0, err=None, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("fn", ["paged_attn_decode_int8", "paged_attn_decode_fp16"])
+@pytest.mark.parametrize("change,status", [
+    (dict(qdt=0), -3), (dict(odt=9), -3), (dict(hq=30), -2), (dict(hq=8 * 17), -2),
+    (dict(d=256), -2), (dict(bs=8), -2), (dict(bts=15), -1), (dict(maxL=-1), -1),
+    (dict(B=-1), -1), (dict(q=None), -1), (dict(bt=None), -1), (dict(ctx=None), -1),
+    (dict(out=None), -1), (dict(pool=FAKE + 8), -1), (dict(sm=float("nan")), -1),
+    (dict(oss=-1), -1), (dict(maxL=2048, bts=128), -4),
+    (dict(maxL=2048, bts=128, ws=FAKE, wsb=16), -4), (dict(B=0), 0),
+    (dict(B=70000, maxL=16, bts=1), -2),
+])
+def test_decode_validation(P, fn, change, status):
+    assert getattr(P._lib, fn)(*_decode_args(**change)) == status

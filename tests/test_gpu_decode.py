@@ -1,0 +1,212 @@
+"""GPU parity of the paged decode kernels (INT8 pages and the 16-bit control)
+against the CPU oracle: max abs diff <= 2e-3 on FP32 outputs (the bound the
+task fixes for the FP32-dequantized oracle), plus bitwise properties
+(block-shuffle invariance, run-to-run determinism), 16-bit output rounding,
+error flags and guard bands."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import (FILL, MAX_ABS_TOL, dev_i32, gpu_decode, gpu_pool, oracle_decode,
+                            oracle_pair_from_sources, oracle_pool, require_gpu, to_dev)
+from workloads import build, make_config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def P():
+    return require_gpu()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _maxdiff(got, want):
+    g = got.float().cpu().numpy().astype(np.float64)
+    assert not np.isnan(g).any()
+    return float(np.max(np.abs(g - want)))
+
+
+CONFIGS = [(1, 1.0), (2, 1.0), (3, 0.1), (4, 0.05), (5, 1.0), ("s8k", 0.1)]
+
+
+@pytest.mark.parametrize("idx,scale", CONFIGS)
+def test_int8_decode_on_oracle_pool(P, idx, scale):
+    """Decode kernel alone: it reads the pool the oracle wrote."""
+    wl = make_config(idx, scale)
+    _say(f"int8 decode (oracle pool): config {idx} scale {scale}")
+    host = oracle_pool(wl, oracle.KV_INT8_SYM)
+    out = gpu_decode(P, wl, torch.from_numpy(host).cuda(), P.KV_INT8_SYM)
+    want = oracle_decode(wl, host, oracle.KV_INT8_SYM)
+    d = _maxdiff(out, want)
+    _say(f"  max abs diff {d:.3e}")
+    assert d <= MAX_ABS_TOL
+
+
+@pytest.mark.parametrize("idx,scale", CONFIGS)
+def test_int8_write_then_decode(P, idx, scale):
+    """The whole path on the GPU: quantize-on-write, then decode."""
+    wl = make_config(idx, scale)
+    _say(f"int8 write+decode: config {idx} scale {scale}")
+    pool, _ = gpu_pool(P, wl, P.KV_INT8_SYM)
+    out = gpu_decode(P, wl, pool, P.KV_INT8_SYM)
+    want = oracle_decode(wl, oracle_pool(wl, oracle.KV_INT8_SYM), oracle.KV_INT8_SYM)
+    assert _maxdiff(out, want) <= MAX_ABS_TOL
+
+
+@pytest.mark.parametrize("idx,scale", [(1, 1.0), (2, 1.0), (3, 0.1), (4, 0.05), (5, 1.0)])
+def test_16bit_decode(P, idx, scale):
+    wl = make_config(idx, scale)
+    _say(f"16-bit decode: config {idx} scale {scale}")
+    pool, _ = gpu_pool(P, wl, P.KV_16BIT)
+    out = gpu_decode(P, wl, pool, P.KV_16BIT)
+    want = oracle_decode(wl, oracle_pool(wl, oracle.KV_16BIT), oracle.KV_16BIT)
+    d = _maxdiff(out, want)
+    _say(f"  max abs diff {d:.3e}")
+    assert d <= MAX_ABS_TOL
+
+
+EDGE = [
+    # (hq, hkv, d, dtype, lens)
+    (32, 8, 128, "f16", [0, 1, 15, 16, 17, 33, 300, 1029]),
+    (8, 8, 128, "bf16", [1, 64, 65, 700]),          # MHA
+    (14, 2, 64, "bf16", [0, 7, 31, 257, 1100]),     # G = 7, D = 64
+    (16, 1, 64, "f16", [5, 48, 2000]),              # G = 16
+    (4, 2, 128, "bf16", [4095, 1]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(EDGE)))
+@pytest.mark.parametrize("fmt_name", ["int8", "16bit"])
+def test_edge_shapes(P, case, fmt_name):
+    hq, hkv, d, dt, lens = EDGE[case]
+    fmt = P.KV_INT8_SYM if fmt_name == "int8" else P.KV_16BIT
+    wl = build(f"edge{case}", 100 + case, [("prefill", lens)], hq, hkv, d, dt, "outlier",
+               shuffle=True, spare_blocks=3)
+    _say(f"edge {case} {fmt_name}: hq {hq} hkv {hkv} d {d} {dt} lens {lens}")
+    pool, _ = gpu_pool(P, wl, fmt)
+    out = gpu_decode(P, wl, pool, fmt)
+    want = oracle_decode(wl, oracle_pool(wl, fmt), fmt)
+    assert _maxdiff(out, want) <= MAX_ABS_TOL
+    zero_rows = [b for b, L in enumerate(lens) if L == 0]
+    for b in zero_rows:
+        assert torch.all(out[b] == 0)
+
+
+@pytest.mark.parametrize("fmt_name", ["int8", "16bit"])
+@pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16])
+def test_16bit_outputs_are_rounded_fp32_outputs(P, fmt_name, out_dtype):
+    fmt = P.KV_INT8_SYM if fmt_name == "int8" else P.KV_16BIT
+    wl = make_config(3, 0.05)
+    pool, _ = gpu_pool(P, wl, fmt)
+    o32 = gpu_decode(P, wl, pool, fmt)
+    o16 = gpu_decode(P, wl, pool, fmt, out_dtype=out_dtype)
+    assert torch.equal(o16, o32.to(out_dtype))
+
+
+@pytest.mark.parametrize("fmt_name", ["int8", "16bit"])
+def test_block_shuffle_invariance_and_determinism(P, fmt_name):
+    fmt = P.KV_INT8_SYM if fmt_name == "int8" else P.KV_16BIT
+    wl = make_config(4, 0.03)
+    pool, _ = gpu_pool(P, wl, fmt)
+    o1 = gpu_decode(P, wl, pool, fmt)
+    o2 = gpu_decode(P, wl, pool, fmt)
+    assert torch.equal(o1, o2)
+    perm = np.random.default_rng(5).permutation(wl.num_blocks)
+    pool2 = torch.empty_like(pool)
+    pool2[torch.from_numpy(perm).cuda()] = pool
+    bt2 = perm[wl.block_tables].astype(np.int32)
+    o3 = gpu_decode(P, wl, pool2, fmt, block_tables=bt2)
+    assert torch.equal(o1, o3)
+
+
+def test_strided_query_and_output(P):
+    """q and out given as strided views (head stride != head_dim)."""
+    wl = make_config(5, 0.05)   # q is a view of a fused QKV buffer already
+    pool, _ = gpu_pool(P, wl, P.KV_INT8_SYM)
+    big = torch.full((wl.num_seqs, wl.num_q_heads, 2 * wl.head_dim), float("nan"),
+                     device="cuda")
+    out = big[:, :, :wl.head_dim]
+    gpu_decode(P, wl, pool, P.KV_INT8_SYM, out=out)
+    want = oracle_decode(wl, oracle_pool(wl, oracle.KV_INT8_SYM), oracle.KV_INT8_SYM)
+    assert _maxdiff(out, want) <= MAX_ABS_TOL
+    assert torch.isnan(big[:, :, wl.head_dim:]).all()
+
+
+def test_flags_and_guards(P):
+    """Out-of-range block ids and context lengths are flagged and skipped; the
+    kernels read and write nothing outside their buffers."""
+    wl = build("flags", 31, [("prefill", [100, 40, 300])], 8, 2, 128, "f16", "outlier",
+               shuffle=True)
+    pool, full = gpu_pool(P, wl, P.KV_INT8_SYM, guard_pages=2)
+    ref = gpu_decode(P, wl, pool, P.KV_INT8_SYM)
+    bt = wl.block_tables.copy()
+    bt[1, 1] = wl.num_blocks + 1          # sequence 1, second page: outside the pool
+    ctx = wl.context_lens.copy()
+    ctx[2] = wl.max_context_len + 50      # beyond max_context_len: clamped
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    outbuf = torch.full((wl.num_seqs + 2, 8, 128), float("nan"), device="cuda")
+    out = outbuf[1:-1]
+    gpu_decode(P, wl, pool, P.KV_INT8_SYM, block_tables=bt, context_lens=ctx, err_flag=err,
+               out=out)
+    torch.cuda.synchronize()
+    assert int(err.item()) == P.EFLAG_BLOCK_RANGE | P.EFLAG_CONTEXT_RANGE
+    assert torch.equal(out[0], ref[0]) and torch.equal(out[2], ref[2])
+    assert torch.isnan(outbuf[0]).all() and torch.isnan(outbuf[-1]).all()
+    f = full.cpu().numpy()
+    assert np.all(f[:2] == FILL) and np.all(f[-2:] == FILL)
+    # sequence 1 without its second page equals the oracle over the remaining tokens
+    host = oracle_pool(wl, oracle.KV_INT8_SYM)
+    kc, ks, vc, vs = oracle.gather_int8_sequence(host, wl.block_tables[1], 40, 16, 2, 128)
+    keep = np.r_[0:16, 32:40]
+    k = oracle.dequantize_rows(kc[keep], ks[keep])
+    v = oracle.dequantize_rows(vc[keep], vs[keep])
+    want = oracle.attend_one_sequence(oracle.as_f32(wl.q[1]), k, v, wl.sm_scale)
+    assert _maxdiff(out[1], want) <= MAX_ABS_TOL
+
+
+def test_int8_matches_16bit_when_dequantization_is_exact(P):
+    """With K/V values c * 2^k (|c| <= 127, max |c| = 127 per row), the INT8
+    pages dequantize exactly to the 16-bit values, so both kernels compute the
+    same attention (up to FP32 summation order)."""
+    rng = np.random.default_rng(8)
+    L, hq, hkv, d = 777, 16, 4, 128
+    codes = rng.integers(-127, 128, (L, hkv, d))
+    codes[:, :, 0] = 127
+    e = rng.integers(-8, 2, (L, hkv, 1)).astype(np.float64)
+    x = (codes * 2.0 ** e).astype(np.float32)
+    wl = build("exact", 3, [("prefill", [L])], hq, hkv, d, "f16", "normal", shuffle=True)
+    wl.phases[0].k.copy_(torch.from_numpy(x).half())
+    wl.phases[0].v.copy_(torch.from_numpy(x[::-1].copy()).half())
+    p8, _ = gpu_pool(P, wl, P.KV_INT8_SYM)
+    p16, _ = gpu_pool(P, wl, P.KV_16BIT)
+    o8 = gpu_decode(P, wl, p8, P.KV_INT8_SYM)
+    o16 = gpu_decode(P, wl, p16, P.KV_16BIT)
+    assert float((o8 - o16).abs().max()) <= 1e-4
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("idx", [3, 4])
+def test_full_size_decode_sampled(P, idx):
+    """Full-size configuration in the launch shape the bench times: the whole
+    GPU path (write, decode), checked on sampled (sequence, head) rows that
+    the oracle computes from the source K/V."""
+    wl = make_config(idx)
+    _say(f"full-size decode: config {idx}: {wl.num_seqs} seqs, max ctx {wl.max_context_len}")
+    pool, _ = gpu_pool(P, wl, P.KV_INT8_SYM)
+    out = gpu_decode(P, wl, pool, P.KV_INT8_SYM).cpu().numpy()
+    assert not np.isnan(out).any()
+    rng = np.random.default_rng(7)
+    worst = 0.0
+    for b in rng.choice(wl.num_seqs, 3, replace=False):
+        for h in rng.choice(wl.num_q_heads, 3, replace=False):
+            want = oracle_pair_from_sources(wl, int(b), int(h), oracle.KV_INT8_SYM)
+            worst = max(worst, float(np.max(np.abs(out[b, h] - want))))
+    _say(f"  worst sampled max abs diff {worst:.3e}")
+    assert worst <= MAX_ABS_TOL

@@ -1,0 +1,137 @@
+"""GPU parity of the quantize-on-write kernel (and the 16-bit writer): the
+pools written through the C ABI must equal, byte for byte, the pools the CPU
+oracle writes from the same seeded inputs (codes and FP16 scales bit-exact;
+untouched bytes untouched)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import (FILL, bits16, dev_i32, gpu_pool, oracle_pool, require_gpu,
+                            to_dev)
+from workloads import build, make_config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def P():
+    return require_gpu()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("idx,scale", [(1, 1.0), (2, 1.0), (3, 0.1), (4, 0.05), (5, 1.0),
+                                       ("s8k", 0.1)])
+def test_int8_pool_bit_exact(P, idx, scale):
+    wl = make_config(idx, scale)
+    _say(f"int8 write: config {idx} scale {scale} blocks {wl.num_blocks}")
+    pool, _ = gpu_pool(P, wl, P.KV_INT8_SYM)
+    got = pool.cpu().numpy()
+    want = oracle_pool(wl, oracle.KV_INT8_SYM)
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, f"{bad[0].size} bytes differ, first at page {bad[0][0]} byte {bad[1][0]}"
+
+
+@pytest.mark.parametrize("idx,scale", [(1, 1.0), (4, 0.03), (5, 1.0)])
+def test_16bit_pool_exact(P, idx, scale):
+    wl = make_config(idx, scale)
+    _say(f"16-bit write: config {idx} scale {scale}")
+    pool, _ = gpu_pool(P, wl, P.KV_16BIT)
+    assert np.array_equal(pool.cpu().numpy(), oracle_pool(wl, oracle.KV_16BIT))
+
+
+def test_writes_stay_inside_the_pool(P):
+    wl = make_config(5, 0.1)
+    for fmt in (P.KV_INT8_SYM, P.KV_16BIT):
+        _, full = gpu_pool(P, wl, fmt, guard_pages=2)
+        f = full.cpu().numpy()
+        assert np.all(f[:2] == FILL) and np.all(f[-2:] == FILL)
+
+
+def test_padding_and_out_of_range_slots(P):
+    """slot < 0: skipped silently; slot >= num_blocks*16: skipped and flagged."""
+    wl = build("slots", 11, [("prefill", [40])], 8, 2, 128, "f16", "outlier")
+    ph = wl.phases[0]
+    slots = ph.slot_mapping.copy()
+    slots[3] = -1
+    slots[7] = wl.num_blocks * 16 + 5
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pool = torch.full((wl.num_blocks, P.pdakv_page_bytes(P.KV_INT8_SYM, 16, 2, 128)), FILL,
+                      dtype=torch.uint8, device="cuda")
+    P.kv_quant_int8_sym_write(to_dev(ph.k), to_dev(ph.v), dev_i32(slots), pool, wl.num_blocks,
+                              err_flag=err)
+    assert int(err.item()) == P.EFLAG_SLOT_RANGE
+    want = oracle.new_pool(oracle.KV_INT8_SYM, wl.num_blocks, 16, 2, 128, fill=FILL)
+    keep = np.ones(len(slots), bool)
+    keep[[3, 7]] = False
+    kc, ks = oracle.quantize_rows(ph.k)
+    vc, vs = oracle.quantize_rows(ph.v)
+    oracle.write_int8_tokens(want, kc[keep], ks[keep], vc[keep], vs[keep], slots[keep], 16)
+    assert np.array_equal(pool.cpu().numpy(), want)
+
+
+def test_scale_overflow_is_flagged_and_row_left_unwritten(P):
+    k = torch.zeros((2, 1, 64), dtype=torch.bfloat16)
+    k[0, 0, 5] = 2.0 ** 24  # absmax / 127 > 65504
+    k[1, 0, 3] = 1.5
+    v = torch.ones((2, 1, 64), dtype=torch.bfloat16)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    pb = P.pdakv_page_bytes(P.KV_INT8_SYM, 16, 1, 64)
+    pool = torch.full((1, pb), FILL, dtype=torch.uint8, device="cuda")
+    P.kv_quant_int8_sym_write(k.cuda(), v.cuda(), dev_i32([0, 1]), pool, 1, err_flag=err)
+    assert int(err.item()) == P.EFLAG_SCALE_RANGE
+    got = pool.cpu().numpy()
+    want = oracle.new_pool(oracle.KV_INT8_SYM, 1, 16, 1, 64, fill=FILL)
+    kc, ks = oracle.quantize_rows(k[1:])
+    vc, vs = oracle.quantize_rows(v[1:])
+    oracle.write_int8_tokens(want, kc, ks, vc, vs, [1], 16)
+    assert np.array_equal(got, want)
+
+
+def test_subnormal_and_tie_rows(P):
+    """Rows whose scales are FP16 subnormals and rows with exact .5 ties."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((64, 4, 128)).astype(np.float32)
+    x[:16] *= 1e-5                     # subnormal scales
+    x[16:32] = np.round(x[16:32] * 20) / 2   # many half-integers
+    x[16:32, :, 0] = 127.0             # absmax 127 -> scale 1.0 -> ties at .5
+    x[32:34] = 0.0                     # all-zero tokens
+    x[34, :, 9] = -0.0
+    k = torch.from_numpy(x).half()
+    v = torch.from_numpy(x[::-1].copy()).half()
+    slots = np.arange(64, dtype=np.int32)[::-1].copy()
+    pb = P.pdakv_page_bytes(P.KV_INT8_SYM, 16, 4, 128)
+    pool = torch.full((4, pb), FILL, dtype=torch.uint8, device="cuda")
+    P.kv_quant_int8_sym_write(k.cuda(), v.cuda(), dev_i32(slots), pool, 4)
+    want = oracle.new_pool(oracle.KV_INT8_SYM, 4, 16, 4, 128, fill=FILL)
+    kc, ks = oracle.quantize_rows(k)
+    vc, vs = oracle.quantize_rows(v)
+    oracle.write_int8_tokens(want, kc, ks, vc, vs, slots, 16)
+    assert np.array_equal(pool.cpu().numpy(), want)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("idx", [3, 4])
+def test_full_size_write_sampled(P, idx):
+    """Full-size configuration, written in the launch shape the bench uses;
+    sampled (sequence, KV head) rows are compared with the oracle."""
+    wl = make_config(idx)
+    _say(f"full-size write: config {idx}: {wl.num_seqs} seqs, {wl.num_blocks} pages")
+    pool, _ = gpu_pool(P, wl, P.KV_INT8_SYM)
+    host = pool.cpu().numpy()
+    rng = np.random.default_rng(99)
+    for b in rng.choice(wl.num_seqs, 3, replace=False):
+        for g in rng.choice(wl.num_kv_heads, 2, replace=False):
+            L = int(wl.context_lens[b])
+            kc, ks, vc, vs = oracle.gather_int8_sequence(host, wl.block_tables[b], L, 16,
+                                                         wl.num_kv_heads, wl.head_dim, heads=[g])
+            k, v = wl.tokens_of_seq(int(b))
+            wkc, wks = oracle.quantize_rows(k[:, g])
+            wvc, wvs = oracle.quantize_rows(v[:, g])
+            assert np.array_equal(kc[:, 0], wkc) and np.array_equal(vc[:, 0], wvc)
+            assert np.array_equal(ks[:, 0].view(np.uint16), wks.view(np.uint16))
+            assert np.array_equal(vs[:, 0].view(np.uint16), wvs.view(np.uint16))
