@@ -136,7 +136,8 @@ int pdakv_decode_plan(int num_seqs, int num_kv_heads, int max_context_len,
                       int* pages_per_split, int* max_splits);
 
 /* Device workspace the decode calls need for these sizes (0 when no split
- * merge is needed). The same value serves the INT8 and the 16-bit decode. */
+ * merge is needed). The same value serves the INT8 and the 16-bit decode.
+ * Layout: float partials [num_seqs][num_q_heads][max_splits][head_dim + 2]. */
 size_t pdakv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                     int head_dim, int max_context_len);
 
@@ -185,9 +186,10 @@ int kv_write_16bit(const void* k_src, const void* v_src, int src_dtype,
  *                  above max_context_len are clamped and flagged.
  *   max_context_len host upper bound of context_lens (sizes the launch).
  *   sm_scale       logit scale (usually 1/sqrt(head_dim)).
- *   workspace      device scratch of at least pdakv_decode_workspace_bytes();
- *                  may be NULL when that is 0. Its contents need no
- *                  initialization and are garbage afterwards.
+ *   workspace      device scratch of at least pdakv_decode_workspace_bytes(),
+ *                  4-byte aligned; may be NULL when that is 0. Its contents
+ *                  need no initialization and are garbage afterwards. Calls
+ *                  that share one workspace must not overlap in time.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads). The output
  * must not alias any input. */
 int paged_attn_decode_int8(void* out, int out_dtype, int64_t out_stride_seq,

@@ -124,8 +124,8 @@ int decode_common(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, cons
   a.group = num_q_heads / num_kv_heads;
   a.max_ctx = max_context_len;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
-  a.ws = static_cast<float*>(workspace);
   plan(num_seqs, num_kv_heads, max_context_len, &a.pages_per_split, &a.max_splits);
+  a.ws = static_cast<float*>(workspace);
   a.err = err_flag;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = q_dtype == PDAKV_DTYPE_BF16;

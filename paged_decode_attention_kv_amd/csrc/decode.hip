@@ -12,7 +12,8 @@
 // ------------------
 // grid = (split, KV head, sequence); a workgroup of four waves owns one
 // (sequence, KV head) and a run of `pages_per_split` pages; wave w takes the
-// pages w, w+4, ... of that run. One page = 16 tokens = one 16x16 MFMA tile:
+// pages w, w+4, w+8, ... and keeps the next page's loads in flight while it
+// computes the current one. One page = 16 tokens = one 16x16 MFMA tile:
 //  * QK: S[t][h] = sum_d K[t][d] * q[h][d] with K in the A operand (row t =
 //    lane % 16) and the G query heads of the group in the B operand (column
 //    h = lane % 16, zero-padded to 16). Every K byte is fetched once and
@@ -24,18 +25,20 @@
 //    l % 16 — exactly the B-operand layout the PV product needs, so the
 //    probabilities never leave registers.
 //  * PV: O^T[d][h] = sum_t V[t][d] * P[h][t]. The V codes of four tokens of
-//    one dimension share a 32-bit word in the page, which is the A operand of
-//    one lane. The fp32 probability (with the V scale folded in) is split into
-//    a high and a low fp16 part (22 significant bits), both contracted in one
-//    16x16x32 instruction.
-//  * Online softmax state (running max M, sum l, accumulator) lives in the
-//    lanes of head l % 16; the V scale sV = f * 2^e (f in [0.5, 1)) enters
-//    the running max as a base-2 exponent so that the folded probabilities
-//    P = 2^(s + e - M) * f stay in [0, 1] (times 2^12 to keep the low fp16
-//    parts out of the subnormal range).
-// After the page loop the four waves combine through LDS; one split either
-// writes the final row (single-split launches) or a partial (max, sum,
-// accumulator) that merge_splits_kernel combines.
+//    one dimension share a 32-bit word in the page: the A operand of one lane
+//    of a 16x16x16 instruction. The fp32 probability (V scale folded in) is
+//    split into a high and a low fp16 part (22 significant bits), contracted
+//    by two instructions.
+//  * Online softmax state (running max m, sum l, accumulator) lives in the
+//    lanes of head l % 16. The V scale sV = f * 2^e (f in [0.5, 1)) enters
+//    the logit as the base-2 exponent e, so the folded probabilities
+//    P = 2^(s + e - m) * f never leave the fp16 range whatever the scales.
+// After the page loop the four waves combine through LDS. A sequence with a
+// single split writes its rows directly; otherwise every split writes a
+// partial (max, sum, accumulator) and merge_splits_kernel combines them.
+// (Merging in the last-arriving workgroup would need device-scope fences,
+// which write back and invalidate the L2 of the XCD: far dearer than the
+// second launch.)
 #include "device_util.h"
 #include "launch.h"
 
@@ -43,7 +46,13 @@ namespace pdakv {
 
 namespace {
 
-constexpr float kPScale = 12.0f;  // probabilities are carried times 2^12
+// Probabilities are carried times 2^kPScale relative to the running max m; m
+// is raised only when a new logit exceeds it by more than kTau (base-2
+// units), so the accumulator is rescaled rarely and probabilities stay below
+// 2^(kPScale + kTau) = 2^15, inside the fp16 range of the PV operand, with
+// their low fp16 parts clear of the subnormal range.
+constexpr float kTau = 8.0f;
+constexpr float kPScale = 7.0f;
 
 template <int D>
 struct DecodeShared {
@@ -81,7 +90,7 @@ __device__ __forceinline__ void load_block_ids(const DecodeArgs& a, int* sblk, i
   }
 }
 
-// Write zeros to the G output rows of (b, group g): empty context.
+// Zero output rows of (b, group g): empty context.
 __device__ void write_zero_rows(const DecodeArgs& a, int b, int g, int D) {
   for (int i = threadIdx.x; i < a.group * D; i += blockDim.x) {
     const int h = g * a.group + i / D;
@@ -89,12 +98,12 @@ __device__ void write_zero_rows(const DecodeArgs& a, int b, int g, int D) {
   }
 }
 
-// Combine the four waves' (m, l, acc) of this workgroup and emit the final
-// rows or a split partial.
+// Combine the four waves' (m, l, acc); write the final rows (the sequence has
+// a single split) or this split's partial for merge_splits_kernel.
 template <int D>
-__device__ void combine_and_store(const DecodeArgs& a, DecodeShared<D>& sh, int b, int g,
-                                  int split) {
-  const bool direct = a.max_splits == 1;
+__device__ void finish(const DecodeArgs& a, DecodeShared<D>& sh, int b, int g, int split,
+                       int nsplit) {
+  const bool direct = nsplit == 1;
   for (int i = threadIdx.x; i < a.group * D; i += blockDim.x) {
     const int hh = i / D, d = i % D;
     float ms = -INFINITY;
@@ -122,16 +131,193 @@ __device__ void combine_and_store(const DecodeArgs& a, DecodeShared<D>& sh, int 
   }
 }
 
+template <int ND>
+struct SoftmaxState {
+  float m;   // running max (base-2 units)
+  float mk;  // m - kPScale
+  float l;
+  f4_t acc[ND];
+};
+
+template <int ND>
+__device__ __forceinline__ void softmax_init(SoftmaxState<ND>& st) {
+  st.m = -INFINITY;
+  st.mk = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int k = 0; k < ND; ++k) st.acc[k] = f4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+template <int ND>
+__device__ __forceinline__ void raise_max(SoftmaxState<ND>& st, float zmax) {
+  zmax = col_max(zmax);
+  if (__any(zmax > st.m + kTau)) {
+    const float m_new = fmaxf(st.m, zmax);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 on the first page
+    st.m = m_new;
+    st.mk = m_new - kPScale;
+    st.l *= alpha;
+#pragma unroll
+    for (int k = 0; k < ND; ++k) st.acc[k] *= alpha;
+  }
+}
+
+// Four int8 codes (byte i = element i) -> four fp16 values, exactly: bias the
+// bytes to c + 128, place each in the mantissa of the fp16 constant 1024
+// (0x6400) with one byte permute per pair, and subtract 1024 + 128.
+__device__ __forceinline__ u2_t i8x4_to_f16x4_perm(uint32_t w) {
+  const uint32_t u = w ^ 0x80808080u;
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  const h2_t bias = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+  u2_t r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, lo) - bias);
+  r.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, hi) - bias);
+  return r;
+}
+
+// q fragments as fp16 scaled by 2^kq so that max|q| of the head lies in
+// [2^14, 2^15); fragment j, slot r holds dim qdim(j, r). Returns the factor
+// that turns the MFMA dot products into base-2 logits.
+template <int NJ, bool QBF16, typename DimFn>
+__device__ __forceinline__ float load_q_scaled(const DecodeArgs& a, int b, int h, bool hvalid,
+                                               DimFn qdim, h8_t* qf) {
+  float qv[NJ * 8];
+  float qmax = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float x = hvalid ? bits16_to_f32<QBF16>(q_bits(a, b, h, qdim(j, r))) : 0.f;
+      qv[j * 8 + r] = x;
+      qmax = fmaxf(qmax, fabsf(x));
+    }
+  qmax = col_max(qmax);
+  const int kq = qmax > 0.f ? 15 - __builtin_amdgcn_frexp_expf(qmax) : 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      qf[j][r] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(qv[j * 8 + r], kq));
+  return __builtin_amdgcn_ldexpf(a.scale_log2, -kq);
+}
+
 // ---------------------------------------------------------------------------
 // INT8 pages
 // ---------------------------------------------------------------------------
+template <int D>
+struct Int8Page {
+  u4_t k[D / 64];  // K codes: token i16, dims 64*i + 16*kb + (0..15)
+  u4_t v[D / 64];  // V codes: dims 64*i + 4*i16 + (0..3), tokens 4*kb + (0..3)
+  u2_t ks, vs;     // scales of tokens 4*kb + (0..3)
+};
+
+template <int D>
+__device__ __forceinline__ void load_int8_page(Int8Page<D>& pg, const uint8_t* hp, int i16,
+                                               int kb) {
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i)
+    pg.k[i] = *reinterpret_cast<const u4_t*>(hp + i16 * D + 64 * i + 16 * kb);
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i)
+    pg.v[i] = *reinterpret_cast<const u4_t*>(hp + 16 * D + kb * 4 * D + 256 * i + 16 * i16);
+  pg.ks = *reinterpret_cast<const u2_t*>(hp + 32 * D + 8 * kb);
+  pg.vs = *reinterpret_cast<const u2_t*>(hp + 32 * D + 32 + 8 * kb);
+}
+
+template <int D>
+__device__ __forceinline__ f4_t int8_qk(const Int8Page<D>& pg, const h8_t* qf) {
+  f4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j) {
+    const u2_t c0 = i8x4_to_f16x4_perm(pg.k[j / 2][2 * (j % 2)]);
+    const u2_t c1 = i8x4_to_f16x4_perm(pg.k[j / 2][2 * (j % 2) + 1]);
+    const u4_t kw = {c0.x, c0.y, c1.x, c1.y};
+    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, kw), qf[j], s, 0, 0, 0);
+  }
+  return s;
+}
+
+// One page; tok0 = position of this lane's first token (4*kb within the
+// page). MASK: a token may lie at or beyond L, or the page is missing
+// (valid false); without MASK every token is valid.
+template <int D, bool MASK>
+__device__ __forceinline__ void int8_page_step(const Int8Page<D>& pg, bool valid, const h8_t* qf,
+                                               float qscale, int tok0, int L,
+                                               SoftmaxState<D / 16>& st) {
+  constexpr int ND = D / 16;
+  const f4_t s = int8_qk<D>(pg, qf);
+  const uint32_t ksw[2] = {pg.ks.x, pg.ks.y}, vsw[2] = {pg.vs.x, pg.vs.y};
+  float z[4];
+  int e[4];
+  _Float16 f[4];
+  float zmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float sk = f16_bits_to_f32(static_cast<uint16_t>(ksw[j / 2] >> (16 * (j % 2))));
+    const _Float16 sv =
+        __builtin_bit_cast(_Float16, static_cast<uint16_t>(vsw[j / 2] >> (16 * (j % 2))));
+    e[j] = __builtin_amdgcn_frexp_exph(sv);
+    f[j] = __builtin_amdgcn_frexp_manth(sv);
+    // base-2 logit plus the exponent of the V scale: P = 2^(z - m) * f
+    z[j] = s[j] * sk * qscale + static_cast<float>(e[j]);
+    if (MASK) {
+      const bool ok = valid && tok0 + j < L;
+      z[j] = ok ? z[j] : -INFINITY;
+      f[j] = ok ? f[j] : static_cast<_Float16>(0.0f);
+      e[j] = ok ? e[j] : 0;
+    }
+    zmax = fmaxf(zmax, z[j]);
+  }
+  raise_max(st, zmax);
+  float hi[4], lo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float x = __builtin_amdgcn_exp2f(z[j] - st.mk);  // 2^(kPScale + z - m)
+    st.l += __builtin_amdgcn_ldexpf(x, -e[j]);
+    const float p = x * static_cast<float>(f[j]);
+    hi[j] = static_cast<float>(static_cast<_Float16>(p));
+    lo[j] = p - hi[j];
+  }
+  const h4_t ph = __builtin_bit_cast(h4_t, u2_t{pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3])});
+  const h4_t pl = __builtin_bit_cast(h4_t, u2_t{pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3])});
+  // O^T += V^T P^T; instruction k covers dims 64*(k/4) + 4*(row) + k%4, its
+  // K-slots hold tokens 4*kb + (0..3)
+#pragma unroll
+  for (int k = 0; k < ND; ++k) {
+    const h4_t vw = __builtin_bit_cast(h4_t, i8x4_to_f16x4_perm(pg.v[k / 4][k % 4]));
+    st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(vw, ph, st.acc[k], 0, 0, 0);
+    st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(vw, pl, st.acc[k], 0, 0, 0);
+  }
+}
+
+// Load page p of the split (if present and valid) into pg.
+template <int D>
+__device__ __forceinline__ bool int8_load(Int8Page<D>& pg, const DecodeShared<D>& sh, int p,
+                                          int np, const uint8_t* base, int64_t page_bytes,
+                                          int i16, int kb) {
+  const int blk = p < np ? sh.blk[p] : -1;
+  if (blk >= 0) load_int8_page<D>(pg, base + blk * page_bytes, i16, kb);
+  return blk >= 0;
+}
+
+// page_tok = position of the page's first token. (A separate unmasked path
+// for full pages costs more registers than the masks cost instructions.)
+template <int D>
+__device__ __forceinline__ void int8_step(const Int8Page<D>& pg, bool valid, const h8_t* qf,
+                                          float qscale, int page_tok, int kb, int L,
+                                          SoftmaxState<D / 16>& st) {
+  if (!valid) return;  // missing or flagged page: nothing to attend
+  int8_page_step<D, true>(pg, valid, qf, qscale, page_tok + 4 * kb, L, st);
+}
+
+// 4 waves per SIMD: the compiler keeps this kernel within 128 VGPRs
 template <int D, bool QBF16>
-__global__ __launch_bounds__(64 * kWaves) void decode_int8_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))) void
+decode_int8_kernel(DecodeArgs a) {
   constexpr int HB = 32 * D + 64;  // head block bytes
   constexpr int NJ = D / 32;       // QK instructions (16x16x32)
-  constexpr int NK = D / 64;       // 16-byte K loads per lane
-  constexpr int ND = D / 16;       // PV instructions (one per 16 output dims)
-  constexpr int NV = D / 64;       // 16-byte V loads per lane
+  constexpr int ND = D / 16;       // PV output blocks of 16 dims
   __shared__ DecodeShared<D> sh;
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -142,135 +328,54 @@ __global__ __launch_bounds__(64 * kWaves) void decode_int8_kernel(DecodeArgs a) 
   const int npages = (L + kBlockSize - 1) / kBlockSize;
   const int p0 = split * a.pages_per_split;
   if (p0 >= npages) {
-    if (a.max_splits == 1 && split == 0) write_zero_rows(a, b, g, D);
+    if (npages == 0 && split == 0) write_zero_rows(a, b, g, D);
     return;
   }
+  const int nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
   const int np = min(npages - p0, a.pages_per_split);
   load_block_ids(a, sh.blk, b, p0, np);
 
-  // q fragment for QK instruction j: dims 64*(j/2) + 16*kb + 8*(j%2) + r,
-  // the same dims the K loads below place in the A operand.
   const bool hvalid = i16 < a.group;
-  const int h = g * a.group + i16;
-  float qv[NJ * 8];
-  float qmax = 0.f;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j)
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int d = 64 * (j / 2) + 16 * kb + 8 * (j % 2) + r;
-      const float x = hvalid ? bits16_to_f32<QBF16>(q_bits(a, b, h, d)) : 0.f;
-      qv[j * 8 + r] = x;
-      qmax = fmaxf(qmax, fabsf(x));
-    }
-  qmax = col_max(qmax);
-  // power of two putting max|q| in [2^14, 2^15): exact for fp16 and bf16 q
-  const int kq = qmax > 0.f ? 15 - __builtin_amdgcn_frexp_expf(qmax) : 0;
   h8_t qf[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j)
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-      qf[j][r] = static_cast<_Float16>(__builtin_amdgcn_ldexpf(qv[j * 8 + r], kq));
-  const float qscale = __builtin_amdgcn_ldexpf(a.scale_log2, -kq);
+  const float qscale = load_q_scaled<NJ, QBF16>(
+      a, b, g * a.group + i16, hvalid,
+      [kb](int j, int r) { return 64 * (j / 2) + 16 * kb + 8 * (j % 2) + r; }, qf);
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f4_t acc[ND];
-#pragma unroll
-  for (int k = 0; k < ND; ++k) acc[k] = f4_t{0.f, 0.f, 0.f, 0.f};
-
+  SoftmaxState<ND> st;
+  softmax_init(st);
   __syncthreads();
 
-  for (int pi = wave; pi < np; pi += kWaves) {
-    const int blk = sh.blk[pi];
-    if (blk < 0) continue;  // flagged page: skipped
-    const uint8_t* hp = a.pool + static_cast<int64_t>(blk) * a.page_bytes + g * HB;
-    u4_t kr[NK], vr[NV];
-#pragma unroll
-    for (int i = 0; i < NK; ++i)
-      kr[i] = *reinterpret_cast<const u4_t*>(hp + i16 * D + 64 * i + 16 * kb);
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-      vr[i] = *reinterpret_cast<const u4_t*>(hp + 16 * D + kb * 4 * D + 256 * i + 16 * i16);
-    const u2_t ksr = *reinterpret_cast<const u2_t*>(hp + 32 * D + 8 * kb);
-    const u2_t vsr = *reinterpret_cast<const u2_t*>(hp + 32 * D + 32 + 8 * kb);
-
-    // S = K q^T for 16 tokens x 16 (padded) heads
-    f4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const u2_t c0 = i8x4_to_f16x4(kr[j / 2][2 * (j % 2)]);
-      const u2_t c1 = i8x4_to_f16x4(kr[j / 2][2 * (j % 2) + 1]);
-      const u4_t kw = {c0.x, c0.y, c1.x, c1.y};
-      s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, kw), qf[j], s, 0, 0, 0);
-    }
-
-    // lane holds tokens tok0 + j of head i16
-    const int tok0 = (p0 + pi) * kBlockSize + 4 * kb;
-    const uint16_t skb[4] = {static_cast<uint16_t>(ksr.x), static_cast<uint16_t>(ksr.x >> 16),
-                             static_cast<uint16_t>(ksr.y), static_cast<uint16_t>(ksr.y >> 16)};
-    const uint16_t svb[4] = {static_cast<uint16_t>(vsr.x), static_cast<uint16_t>(vsr.x >> 16),
-                             static_cast<uint16_t>(vsr.y), static_cast<uint16_t>(vsr.y >> 16)};
-    float z[4], f[4];
-    int e[4];
-    float zmax = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool valid = tok0 + j < L;
-      const float sv = f16_bits_to_f32(svb[j]);
-      const float logit2 = s[j] * f16_bits_to_f32(skb[j]) * qscale;
-      const int ej = __builtin_amdgcn_frexp_expf(sv);
-      e[j] = valid ? ej : 0;
-      f[j] = valid ? __builtin_amdgcn_frexp_mantf(sv) : 0.f;
-      z[j] = valid ? logit2 + static_cast<float>(ej) : -INFINITY;
-      zmax = fmaxf(zmax, z[j]);
-    }
-    zmax = col_max(zmax);
-    const float m_new = fmaxf(m_run, zmax);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int k = 0; k < ND; ++k) acc[k] *= alpha;
-
-    float hi[4], lo[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float pe = exp2f(z[j] - m_new + kPScale);          // <= 2^12
-      l_run += __builtin_amdgcn_ldexpf(pe, -e[j]);            // 2^(12 + logit2 - M)
-      const float p = pe * f[j];                               // 2^(12 - M) 2^logit2 sV
-      const _Float16 ph = static_cast<_Float16>(p);
-      hi[j] = static_cast<float>(ph);
-      lo[j] = p - hi[j];
-    }
-    const u4_t pw = {pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3]),
-                     pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3])};
-    const h8_t pf = __builtin_bit_cast(h8_t, pw);
-
-    // O^T += V^T P^T: instruction k covers dims 64*(k/4) + 4*(row) + k%4
-#pragma unroll
-    for (int k = 0; k < ND; ++k) {
-      const u2_t c = i8x4_to_f16x4(vr[k / 4][k % 4]);
-      const u4_t vw = {c.x, c.y, c.x, c.y};
-      acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, vw), pf, acc[k],
-                                                      0, 0, 0);
-    }
+  // Ping-pong register buffers: page i+4's loads are in flight while page i
+  // is computed. Wave w owns pages w, w+4, w+8, ... of the split.
+  const uint8_t* base = a.pool + static_cast<int64_t>(g) * HB;
+  Int8Page<D> pa, pb;
+  int p = wave;
+  bool va = int8_load<D>(pa, sh, p, np, base, a.page_bytes, i16, kb);
+  while (p < np) {
+    const int p1 = p + kWaves;
+    const bool vb = int8_load<D>(pb, sh, p1, np, base, a.page_bytes, i16, kb);
+    int8_step<D>(pa, va, qf, qscale, (p0 + p) * kBlockSize, kb, L, st);
+    if (p1 >= np) break;
+    const int p2 = p1 + kWaves;
+    va = int8_load<D>(pa, sh, p2, np, base, a.page_bytes, i16, kb);
+    int8_step<D>(pb, vb, qf, qscale, (p0 + p1) * kBlockSize, kb, L, st);
+    p = p2;
   }
 
-  l_run = col_sum(l_run);
+  st.l = col_sum(st.l);
   if (hvalid) {
     if (kb == 0) {
-      sh.m[wave][i16] = m_run;
-      sh.l[wave][i16] = l_run;
+      sh.m[wave][i16] = st.m;
+      sh.l[wave][i16] = st.l;
     }
 #pragma unroll
     for (int k = 0; k < ND; ++k)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        sh.acc[wave][i16][64 * (k / 4) + 16 * kb + 4 * j + (k % 4)] = acc[k][j];
+        sh.acc[wave][i16][64 * (k / 4) + 16 * kb + 4 * j + (k % 4)] = st.acc[k][j];
   }
   __syncthreads();
-  combine_and_store<D>(a, sh, b, g, split);
+  finish<D>(a, sh, b, g, split, nsplit);
 }
 
 // ---------------------------------------------------------------------------
@@ -286,12 +391,121 @@ __device__ __forceinline__ f4_t mfma16x16x32(u4_t a_bits, u4_t b_bits, f4_t c) {
                                                   __builtin_bit_cast(h8_t, b_bits), c, 0, 0, 0);
 }
 
+template <int D>
+struct Page16 {
+  u4_t k[D / 32];  // K: token i16, dims 32*j + 8*kb + (0..7)
+  u4_t v[D / 32];  // V: dims 32*i + 2*i16 + (0,1), tokens 4*kb + (0..3)
+};
+
+template <int D>
+__device__ __forceinline__ void load_page16(Page16<D>& pg, const uint8_t* hp, int i16, int kb) {
+#pragma unroll
+  for (int j = 0; j < D / 32; ++j)
+    pg.k[j] = *reinterpret_cast<const u4_t*>(hp + i16 * 2 * D + 64 * j + 16 * kb);
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i)
+    pg.v[i] = *reinterpret_cast<const u4_t*>(hp + 32 * D + kb * 8 * D + 256 * i + 16 * i16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ f4_t mfma16x16x16(u2_t a_bits, u2_t b_bits, f4_t c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4_t, a_bits),
+                                                     __builtin_bit_cast(s4_t, b_bits), c, 0, 0,
+                                                     0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4_t, a_bits),
+                                                 __builtin_bit_cast(h4_t, b_bits), c, 0, 0, 0);
+}
+
+template <int D, bool BF16, bool MASK>
+__device__ __forceinline__ void page16_step(const Page16<D>& pg, bool valid, const u4_t* qf,
+                                            float scale_log2, int tok0, int L,
+                                            SoftmaxState<D / 16>& st) {
+  constexpr int NJ = D / 32, ND = D / 16;
+  f4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) s = mfma16x16x32<BF16>(pg.k[j], qf[j], s);
+  float z[4];
+  float zmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    z[j] = s[j] * scale_log2;
+    if (MASK) z[j] = valid && tok0 + j < L ? z[j] : -INFINITY;
+    zmax = fmaxf(zmax, z[j]);
+  }
+  raise_max(st, zmax);
+  float pe[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    pe[j] = __builtin_amdgcn_exp2f(z[j] - st.mk);
+    st.l += pe[j];
+  }
+  if constexpr (BF16) {
+    // exact three-way split into truncated bf16 parts (8 + 8 + 8 bits)
+    uint32_t p1[4], p2[4], p3[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t u = __float_as_uint(pe[j]);
+      p1[j] = u >> 16;
+      const float r1 = pe[j] - __uint_as_float(u & 0xFFFF0000u);
+      const uint32_t u1 = __float_as_uint(r1);
+      p2[j] = u1 >> 16;
+      const float r2 = r1 - __uint_as_float(u1 & 0xFFFF0000u);
+      p3[j] = __float_as_uint(r2) >> 16;
+    }
+    const u2_t w1 = {p1[0] | (p1[1] << 16), p1[2] | (p1[3] << 16)};
+    const u2_t w2 = {p2[0] | (p2[1] << 16), p2[2] | (p2[3] << 16)};
+    const u2_t w3 = {p3[0] | (p3[1] << 16), p3[2] | (p3[3] << 16)};
+#pragma unroll
+    for (int k = 0; k < ND; ++k) {
+      const u2_t vw = {pg.v[k / 2][2 * (k % 2)], pg.v[k / 2][2 * (k % 2) + 1]};
+      st.acc[k] = mfma16x16x16<true>(vw, w1, st.acc[k]);
+      st.acc[k] = mfma16x16x16<true>(vw, w2, st.acc[k]);
+      st.acc[k] = mfma16x16x16<true>(vw, w3, st.acc[k]);
+    }
+  } else {
+    float hi[4], lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hi[j] = static_cast<float>(static_cast<_Float16>(pe[j]));
+      lo[j] = pe[j] - hi[j];
+    }
+    const u2_t ph = {pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3])};
+    const u2_t pl = {pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3])};
+#pragma unroll
+    for (int k = 0; k < ND; ++k) {
+      const u2_t vw = {pg.v[k / 2][2 * (k % 2)], pg.v[k / 2][2 * (k % 2) + 1]};
+      st.acc[k] = mfma16x16x16<false>(vw, ph, st.acc[k]);
+      st.acc[k] = mfma16x16x16<false>(vw, pl, st.acc[k]);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ bool load16(Page16<D>& pg, const DecodeShared<D>& sh, int p, int np,
+                                       const uint8_t* base, int64_t page_bytes, int i16,
+                                       int kb) {
+  const int blk = p < np ? sh.blk[p] : -1;
+  if (blk >= 0) load_page16<D>(pg, base + blk * page_bytes, i16, kb);
+  return blk >= 0;
+}
+
 template <int D, bool BF16>
-__global__ __launch_bounds__(64 * kWaves) void decode_16bit_kernel(DecodeArgs a) {
+__device__ __forceinline__ void step16(const Page16<D>& pg, bool valid, const u4_t* qf,
+                                       float scale_log2, int page_tok, int kb, int L,
+                                       SoftmaxState<D / 16>& st) {
+  if (!valid) return;  // missing or flagged page: nothing to attend
+  page16_step<D, BF16, true>(pg, valid, qf, scale_log2, page_tok + 4 * kb, L, st);
+}
+
+// 3 waves per SIMD: the compiler keeps this kernel within 168 VGPRs
+template <int D, bool BF16>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))) void
+decode_16bit_kernel(DecodeArgs a) {
   constexpr int HB = 64 * D;  // head block bytes
-  constexpr int NJ = D / 32;  // QK instructions; also 16-byte K loads per lane
-  constexpr int ND = D / 16;  // PV instructions
-  constexpr int NV = D / 32;  // 16-byte V loads per lane (two instructions each)
+  constexpr int NJ = D / 32;  // QK instructions
+  constexpr int ND = D / 16;  // PV output blocks
   __shared__ DecodeShared<D> sh;
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -302,9 +516,10 @@ __global__ __launch_bounds__(64 * kWaves) void decode_16bit_kernel(DecodeArgs a)
   const int npages = (L + kBlockSize - 1) / kBlockSize;
   const int p0 = split * a.pages_per_split;
   if (p0 >= npages) {
-    if (a.max_splits == 1 && split == 0) write_zero_rows(a, b, g, D);
+    if (npages == 0 && split == 0) write_zero_rows(a, b, g, D);
     return;
   }
+  const int nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
   const int np = min(npages - p0, a.pages_per_split);
   load_block_ids(a, sh.blk, b, p0, np);
 
@@ -325,111 +540,44 @@ __global__ __launch_bounds__(64 * kWaves) void decode_16bit_kernel(DecodeArgs a)
     qf[j] = u4_t{w[0], w[1], w[2], w[3]};
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
-  f4_t acc[ND];
-#pragma unroll
-  for (int k = 0; k < ND; ++k) acc[k] = f4_t{0.f, 0.f, 0.f, 0.f};
-
+  SoftmaxState<ND> st;
+  softmax_init(st);
   __syncthreads();
 
-  for (int pi = wave; pi < np; pi += kWaves) {
-    const int blk = sh.blk[pi];
-    if (blk < 0) continue;
-    const uint8_t* hp = a.pool + static_cast<int64_t>(blk) * a.page_bytes + g * HB;
-    u4_t kr[NJ], vr[NV];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      kr[j] = *reinterpret_cast<const u4_t*>(hp + i16 * 2 * D + 64 * j + 16 * kb);
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-      vr[i] = *reinterpret_cast<const u4_t*>(hp + 32 * D + kb * 8 * D + 256 * i + 16 * i16);
-
-    f4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) s = mfma16x16x32<BF16>(kr[j], qf[j], s);
-
-    const int tok0 = (p0 + pi) * kBlockSize + 4 * kb;
-    float z[4];
-    float zmax = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      z[j] = tok0 + j < L ? s[j] * a.scale_log2 : -INFINITY;
-      zmax = fmaxf(zmax, z[j]);
-    }
-    zmax = col_max(zmax);
-    const float m_new = fmaxf(m_run, zmax);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-#pragma unroll
-    for (int k = 0; k < ND; ++k) acc[k] *= alpha;
-
-    float pe[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pe[j] = exp2f(z[j] - m_new + kPScale);
-      l_run += pe[j];
-    }
-    if constexpr (BF16) {
-      // exact three-way split into truncated bf16 parts (8 + 8 + 8 bits)
-      uint32_t p1[4], p2[4], p3[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t u = __float_as_uint(pe[j]);
-        p1[j] = u >> 16;
-        const float r1 = pe[j] - __uint_as_float(u & 0xFFFF0000u);
-        const uint32_t u1 = __float_as_uint(r1);
-        p2[j] = u1 >> 16;
-        const float r2 = r1 - __uint_as_float(u1 & 0xFFFF0000u);
-        p3[j] = __float_as_uint(r2) >> 16;
-      }
-      const u4_t pa = {p1[0] | (p1[1] << 16), p1[2] | (p1[3] << 16), p2[0] | (p2[1] << 16),
-                       p2[2] | (p2[3] << 16)};
-      const u4_t pb = {p3[0] | (p3[1] << 16), p3[2] | (p3[3] << 16), 0u, 0u};
-#pragma unroll
-      for (int k = 0; k < ND; ++k) {
-        const uint32_t w0 = vr[k / 2][2 * (k % 2)], w1 = vr[k / 2][2 * (k % 2) + 1];
-        const u4_t vw = {w0, w1, w0, w1};
-        acc[k] = mfma16x16x32<true>(vw, pa, acc[k]);
-        acc[k] = mfma16x16x32<true>(vw, pb, acc[k]);
-      }
-    } else {
-      float hi[4], lo[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        hi[j] = static_cast<float>(static_cast<_Float16>(pe[j]));
-        lo[j] = pe[j] - hi[j];
-      }
-      const u4_t pw = {pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3]),
-                       pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3])};
-#pragma unroll
-      for (int k = 0; k < ND; ++k) {
-        const uint32_t w0 = vr[k / 2][2 * (k % 2)], w1 = vr[k / 2][2 * (k % 2) + 1];
-        const u4_t vw = {w0, w1, w0, w1};
-        acc[k] = mfma16x16x32<false>(vw, pw, acc[k]);
-      }
-    }
+  // Ping-pong register buffers, as in the INT8 kernel.
+  const uint8_t* base = a.pool + static_cast<int64_t>(g) * HB;
+  Page16<D> pa, pb;
+  int p = wave;
+  bool va = load16<D>(pa, sh, p, np, base, a.page_bytes, i16, kb);
+  while (p < np) {
+    const int p1 = p + kWaves;
+    const bool vb = load16<D>(pb, sh, p1, np, base, a.page_bytes, i16, kb);
+    step16<D, BF16>(pa, va, qf, a.scale_log2, (p0 + p) * kBlockSize, kb, L, st);
+    if (p1 >= np) break;
+    const int p2 = p1 + kWaves;
+    va = load16<D>(pa, sh, p2, np, base, a.page_bytes, i16, kb);
+    step16<D, BF16>(pb, vb, qf, a.scale_log2, (p0 + p1) * kBlockSize, kb, L, st);
+    p = p2;
   }
 
-  l_run = col_sum(l_run);
+  st.l = col_sum(st.l);
   if (hvalid) {
     if (kb == 0) {
-      sh.m[wave][i16] = m_run;
-      sh.l[wave][i16] = l_run;
+      sh.m[wave][i16] = st.m;
+      sh.l[wave][i16] = st.l;
     }
 #pragma unroll
     for (int k = 0; k < ND; ++k)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        sh.acc[wave][i16][32 * (k / 2) + 8 * kb + 2 * j + (k % 2)] = acc[k][j];
+        sh.acc[wave][i16][32 * (k / 2) + 8 * kb + 2 * j + (k % 2)] = st.acc[k][j];
   }
   __syncthreads();
-  combine_and_store<D>(a, sh, b, g, split);
+  finish<D>(a, sh, b, g, split, nsplit);
 }
 
-// ---------------------------------------------------------------------------
-// split merge: out = sum_i 2^(m_i - m) acc_i / sum_i 2^(m_i - m) l_i
-// ---------------------------------------------------------------------------
+// split merge: out = sum_i 2^(m_i - m) acc_i / sum_i 2^(m_i - m) l_i for the
+// sequences with more than one split (the others were written directly)
 template <int D>
 __global__ __launch_bounds__(D) void merge_splits_kernel(DecodeArgs a) {
   const int bh = blockIdx.x;
@@ -438,6 +586,7 @@ __global__ __launch_bounds__(D) void merge_splits_kernel(DecodeArgs a) {
   const int L = context_len(a, b, false);
   const int npages = (L + kBlockSize - 1) / kBlockSize;
   const int n = (npages + a.pages_per_split - 1) / a.pages_per_split;
+  if (n <= 1) return;
   const float* p = a.ws + static_cast<int64_t>(bh) * a.max_splits * (D + 2);
   float ms = -INFINITY;
   for (int i = 0; i < n; ++i) ms = fmaxf(ms, p[i * (D + 2) + D]);
@@ -447,7 +596,7 @@ __global__ __launch_bounds__(D) void merge_splits_kernel(DecodeArgs a) {
     num += c * p[i * (D + 2) + d];
     den += c * p[i * (D + 2) + D + 1];
   }
-  store_out(a.out, a.out_dtype, b * a.out_ss + h * a.out_sh + d, n > 0 ? num / den : 0.f);
+  store_out(a.out, a.out_dtype, b * a.out_ss + h * a.out_sh + d, num / den);
 }
 
 template <int D>
@@ -477,7 +626,7 @@ hipError_t launch_decode_int8(const DecodeArgs& a, int head_dim, bool q_bf16, hi
     else
       hipLaunchKernelGGL((decode_int8_kernel<64, false>), grid, block, 0, s, a);
   }
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return head_dim == 128 ? launch_merge<128>(a, s) : launch_merge<64>(a, s);
 }
@@ -496,7 +645,7 @@ hipError_t launch_decode_16bit(const DecodeArgs& a, int head_dim, bool kv_bf16,
     else
       hipLaunchKernelGGL((decode_16bit_kernel<64, false>), grid, block, 0, s, a);
   }
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return head_dim == 128 ? launch_merge<128>(a, s) : launch_merge<64>(a, s);
 }

@@ -24,7 +24,8 @@ def alloc_pool(kv_format: int, num_blocks: int, num_kv_heads: int, head_dim: int
 
 def alloc_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                     max_context_len: int, device="cuda"):
-    """float32 scratch for the split merge, or None when the plan needs none."""
+    """Scratch for the split merge, or None when the plan needs none. One
+    workspace serves any number of non-overlapping calls of up to this size."""
     nbytes = pdakv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                           max_context_len)
     if nbytes == 0:

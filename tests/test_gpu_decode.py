@@ -188,7 +188,9 @@ def test_int8_matches_16bit_when_dequantization_is_exact(P):
     p16, _ = gpu_pool(P, wl, P.KV_16BIT)
     o8 = gpu_decode(P, wl, p8, P.KV_INT8_SYM)
     o16 = gpu_decode(P, wl, p16, P.KV_16BIT)
-    assert float((o8 - o16).abs().max()) <= 1e-4
+    # outputs reach |254|; FP32 sums in different orders agree to a few ulps
+    vmax = float(o16.abs().max())
+    assert float((o8 - o16).abs().max()) <= 4e-6 * vmax
 
 
 @pytest.mark.slow
