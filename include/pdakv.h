@@ -178,7 +178,8 @@ int kv_write_16bit(const void* k_src, const void* v_src, int src_dtype,
  *   out            device [num_seqs][num_q_heads][head_dim] of out_dtype
  *                  (F32, F16 or BF16), strides out_stride_seq/_head.
  *   q              device [num_seqs][num_q_heads][head_dim], q_dtype F16/BF16.
- *   kv_pool        INT8 pool of num_blocks pages (layout above).
+ *   kv_pool        INT8 pool of num_blocks pages (layout above); at least one
+ *                  page when max_context_len > 0.
  *   block_tables   device int32 [num_seqs][block_table_stride]; row b lists the
  *                  pages of sequence b; only the first ceil(context_lens[b]/16)
  *                  entries are read.

@@ -76,7 +76,9 @@ int check_decode(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, const
   if (bt_stride < ceil_div(max_context_len, block_size)) return PDAKV_ERR_INVALID_ARG;
   if (num_seqs == 0) return PDAKV_OK;
   if (!out || !q || !block_tables || !context_lens) return PDAKV_ERR_INVALID_ARG;
-  if (max_context_len > 0 && !kv_pool) return PDAKV_ERR_INVALID_ARG;
+  // a non-empty context needs a pool with at least one page (the kernels read
+  // page 0 in place of a missing page)
+  if (max_context_len > 0 && (!kv_pool || num_blocks < 1)) return PDAKV_ERR_INVALID_ARG;
   if (kv_pool && !aligned16(kv_pool)) return PDAKV_ERR_INVALID_ARG;
   const size_t need = pdakv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
                                                    head_dim, max_context_len);
@@ -111,6 +113,7 @@ int decode_common(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, cons
   a.q = q;
   a.q_ss = q_ss;
   a.q_sh = q_sh;
+  a.q_vec16 = aligned16(q) && q_ss % 8 == 0 && q_sh % 8 == 0;
   a.pool = static_cast<const uint8_t*>(kv_pool);
   a.num_blocks = num_blocks;
   a.page_bytes = static_cast<int64_t>(pdakv_page_bytes(

@@ -62,9 +62,17 @@ struct DecodeShared {
   float acc[kWaves][kMaxGroup][D];
 };
 
-// Element loads of q (any stride, 2-byte aligned).
-__device__ __forceinline__ uint16_t q_bits(const DecodeArgs& a, int b, int h, int d) {
-  return static_cast<const uint16_t*>(a.q)[b * a.q_ss + h * a.q_sh + d];
+// Eight consecutive 16-bit q elements (dims d0..d0+7) of head h, as four
+// words. One 16-byte load when the host found q's pointer and strides 16-byte
+// aligned, else eight 2-byte loads. Always issued (no per-lane branch), so the
+// loads of a wave overlap.
+__device__ __forceinline__ u4_t q_chunk8(const DecodeArgs& a, int b, int h, int d0) {
+  const uint16_t* row = static_cast<const uint16_t*>(a.q) + b * a.q_ss + h * a.q_sh + d0;
+  if (a.q_vec16) return *reinterpret_cast<const u4_t*>(row);
+  u4_t w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = row[2 * i] | (static_cast<uint32_t>(row[2 * i + 1]) << 16);
+  return w;
 }
 
 // Clamped context length of sequence b (flags an out-of-range value).
@@ -177,18 +185,23 @@ __device__ __forceinline__ u2_t i8x4_to_f16x4_perm(uint32_t w) {
 }
 
 // q fragments as fp16 scaled by 2^kq so that max|q| of the head lies in
-// [2^14, 2^15); fragment j, slot r holds dim qdim(j, r). Returns the factor
-// that turns the MFMA dot products into base-2 logits.
+// [2^14, 2^15); fragment j, slot r holds dim qdim0(j) + r. Lanes of padding
+// heads (hvalid false) read head h_load and use zeros. Returns the factor that
+// turns the MFMA dot products into base-2 logits.
 template <int NJ, bool QBF16, typename DimFn>
-__device__ __forceinline__ float load_q_scaled(const DecodeArgs& a, int b, int h, bool hvalid,
-                                               DimFn qdim, h8_t* qf) {
+__device__ __forceinline__ float load_q_scaled(const DecodeArgs& a, int b, int h_load,
+                                               bool hvalid, DimFn qdim0, h8_t* qf) {
+  u4_t raw[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) raw[j] = q_chunk8(a, b, h_load, qdim0(j));
   float qv[NJ * 8];
   float qmax = 0.f;
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const float x = hvalid ? bits16_to_f32<QBF16>(q_bits(a, b, h, qdim(j, r))) : 0.f;
+      const uint16_t bits = static_cast<uint16_t>(raw[j][r / 2] >> (16 * (r % 2)));
+      const float x = hvalid ? bits16_to_f32<QBF16>(bits) : 0.f;
       qv[j * 8 + r] = x;
       qmax = fmaxf(qmax, fabsf(x));
     }
@@ -291,13 +304,16 @@ __device__ __forceinline__ void int8_page_step(const Int8Page<D>& pg, bool valid
   }
 }
 
-// Load page p of the split (if present and valid) into pg.
+// Load page p of the split into pg. The loads are issued unconditionally (a
+// missing or flagged page reads page 0, which exists, and is then skipped) so
+// that the number of loads in flight is the same on every path and the
+// compiler can wait for the current page only.
 template <int D>
 __device__ __forceinline__ bool int8_load(Int8Page<D>& pg, const DecodeShared<D>& sh, int p,
                                           int np, const uint8_t* base, int64_t page_bytes,
                                           int i16, int kb) {
   const int blk = p < np ? sh.blk[p] : -1;
-  if (blk >= 0) load_int8_page<D>(pg, base + blk * page_bytes, i16, kb);
+  load_int8_page<D>(pg, base + (blk >= 0 ? blk : 0) * page_bytes, i16, kb);
   return blk >= 0;
 }
 
@@ -338,8 +354,8 @@ decode_int8_kernel(DecodeArgs a) {
   const bool hvalid = i16 < a.group;
   h8_t qf[NJ];
   const float qscale = load_q_scaled<NJ, QBF16>(
-      a, b, g * a.group + i16, hvalid,
-      [kb](int j, int r) { return 64 * (j / 2) + 16 * kb + 8 * (j % 2) + r; }, qf);
+      a, b, g * a.group + (hvalid ? i16 : 0), hvalid,
+      [kb](int j) { return 64 * (j / 2) + 16 * kb + 8 * (j % 2); }, qf);
 
   SoftmaxState<ND> st;
   softmax_init(st);
@@ -482,12 +498,13 @@ __device__ __forceinline__ void page16_step(const Page16<D>& pg, bool valid, con
   }
 }
 
+// Unconditional loads, as int8_load.
 template <int D>
 __device__ __forceinline__ bool load16(Page16<D>& pg, const DecodeShared<D>& sh, int p, int np,
                                        const uint8_t* base, int64_t page_bytes, int i16,
                                        int kb) {
   const int blk = p < np ? sh.blk[p] : -1;
-  if (blk >= 0) load_page16<D>(pg, base + blk * page_bytes, i16, kb);
+  load_page16<D>(pg, base + (blk >= 0 ? blk : 0) * page_bytes, i16, kb);
   return blk >= 0;
 }
 
@@ -525,20 +542,13 @@ decode_16bit_kernel(DecodeArgs a) {
 
   // q fragment j: dims 32*j + 8*kb + r (raw 16-bit values, same dtype as K)
   const bool hvalid = i16 < a.group;
-  const int h = g * a.group + i16;
+  const int h_load = g * a.group + (hvalid ? i16 : 0);
   u4_t qf[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    uint32_t w[4];
+  for (int j = 0; j < NJ; ++j) qf[j] = q_chunk8(a, b, h_load, 32 * j + 8 * kb);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int d = 32 * j + 8 * kb + 2 * r;
-      const uint32_t x0 = hvalid ? q_bits(a, b, h, d) : 0u;
-      const uint32_t x1 = hvalid ? q_bits(a, b, h, d + 1) : 0u;
-      w[r] = x0 | (x1 << 16);
-    }
-    qf[j] = u4_t{w[0], w[1], w[2], w[3]};
-  }
+  for (int j = 0; j < NJ; ++j)
+    if (!hvalid) qf[j] = u4_t{0u, 0u, 0u, 0u};
 
   SoftmaxState<ND> st;
   softmax_init(st);

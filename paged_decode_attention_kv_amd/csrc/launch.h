@@ -34,6 +34,7 @@ struct DecodeArgs {
   int64_t out_ss, out_sh;
   const void* q;
   int64_t q_ss, q_sh;
+  int q_vec16;  // q pointer and strides allow 16-byte loads of 8 elements
   const uint8_t* pool;
   int64_t num_blocks;
   int64_t page_bytes;

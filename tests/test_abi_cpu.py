@@ -114,7 +114,7 @@ def _decode_args(**kw):
     (dict(out=None), -1), (dict(pool=FAKE + 8), -1), (dict(sm=float("nan")), -1),
     (dict(oss=-1), -1), (dict(maxL=2048, bts=128), -4),
     (dict(maxL=2048, bts=128, ws=FAKE, wsb=16), -4), (dict(B=0), 0),
-    (dict(B=70000, maxL=16, bts=1), -2),
+    (dict(B=70000, maxL=16, bts=1), -2), (dict(nblk=0), -1), (dict(nblk=0, B=0), 0),
 ])
 def test_decode_validation(P, fn, change, status):
     assert getattr(P._lib, fn)(*_decode_args(**change)) == status
