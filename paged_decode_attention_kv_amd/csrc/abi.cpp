@@ -14,7 +14,9 @@ namespace {
 using pdakv::DecodeArgs;
 using pdakv::WriteArgs;
 
-constexpr int kTargetWorkgroups = 2048;  // about 8 per CU on 256 CUs
+// Resident decode workgroups on MI355X: 256 CUs x 4 (the INT8 kernel's
+// register and LDS budget allows four 256-thread workgroups per CU).
+constexpr int kResidentWorkgroups = 1024;
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
@@ -22,14 +24,15 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Pages per workgroup and number of splits for a launch. Aim for about
-// kTargetWorkgroups workgroups; each split holds 16..64 pages (a multiple of
-// the four waves) so no workgroup is too small to amortize its start-up and
-// none is large enough to leave the chip idle at the tail.
+// Pages per workgroup and number of splits for a launch. Each workgroup has a
+// fixed start-up and wind-down cost of several memory round trips, so splits
+// are made as long as possible while the longest sequences still spread over
+// all resident workgroups: about one workgroup per resident slot for the
+// largest context, 16..128 pages (a multiple of the four waves) each.
 void plan(int num_seqs, int num_kv_heads, int max_context_len, int* pps, int* nsplit) {
   const int64_t max_pages = ceil_div(max_context_len, pdakv::kBlockSize);
   const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads;
-  int64_t p = ceil_div(units * max_pages, kTargetWorkgroups);
+  int64_t p = ceil_div(units * max_pages, kResidentWorkgroups);
   p = ceil_div(p, pdakv::kWaves) * pdakv::kWaves;
   if (p < 16) p = 16;
   if (p > pdakv::kMaxPagesPerSplit) p = pdakv::kMaxPagesPerSplit;
@@ -130,6 +133,7 @@ int decode_common(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, cons
   plan(num_seqs, num_kv_heads, max_context_len, &a.pages_per_split, &a.max_splits);
   a.ws = static_cast<float*>(workspace);
   a.err = err_flag;
+  a.heads_fastest = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = q_dtype == PDAKV_DTYPE_BF16;
   return hip_status(Int8 ? pdakv::launch_decode_int8(a, head_dim, bf16, s)

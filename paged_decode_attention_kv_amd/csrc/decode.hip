@@ -252,15 +252,24 @@ __device__ __forceinline__ f4_t int8_qk(const Int8Page<D>& pg, const h8_t* qf) {
 }
 
 // One page; tok0 = position of this lane's first token (4*kb within the
-// page). MASK: a token may lie at or beyond L, or the page is missing
-// (valid false); without MASK every token is valid.
+// page). MASK: the page may extend past L (its last page); then the V scales of
+// the tokens past L are replaced by 1.0 (the slots may hold anything) and their
+// logits by -inf.
 template <int D, bool MASK>
 __device__ __forceinline__ void int8_page_step(const Int8Page<D>& pg, bool valid, const h8_t* qf,
                                                float qscale, int tok0, int L,
                                                SoftmaxState<D / 16>& st) {
   constexpr int ND = D / 16;
   const f4_t s = int8_qk<D>(pg, qf);
-  const uint32_t ksw[2] = {pg.ks.x, pg.ks.y}, vsw[2] = {pg.vs.x, pg.vs.y};
+  const uint32_t ksw[2] = {pg.ks.x, pg.ks.y};
+  uint32_t vsw[2] = {pg.vs.x, pg.vs.y};
+  const bool tail = MASK && tok0 - 4 * static_cast<int>((threadIdx.x & 63) >> 4) + kBlockSize > L;
+  if (tail) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (tok0 + j >= L) vsw[j / 2] = (vsw[j / 2] & (0xFFFF0000u >> (16 * (j % 2)))) |
+                                      (0x3C00u << (16 * (j % 2)));
+  }
   float z[4];
   int e[4];
   _Float16 f[4];
@@ -274,13 +283,8 @@ __device__ __forceinline__ void int8_page_step(const Int8Page<D>& pg, bool valid
     f[j] = __builtin_amdgcn_frexp_manth(sv);
     // base-2 logit plus the exponent of the V scale: P = 2^(z - m) * f
     z[j] = s[j] * sk * qscale + static_cast<float>(e[j]);
-    if (MASK) {
-      const bool ok = valid && tok0 + j < L;
-      z[j] = ok ? z[j] : -INFINITY;
-      f[j] = ok ? f[j] : static_cast<_Float16>(0.0f);
-      e[j] = ok ? e[j] : 0;
-    }
-    zmax = fmaxf(zmax, z[j]);
+    if (tail) z[j] = tok0 + j < L ? z[j] : -INFINITY;
+    zmax = max_nc(zmax, z[j]);
   }
   raise_max(st, zmax);
   float hi[4], lo[4];
@@ -324,7 +328,7 @@ __device__ __forceinline__ void int8_step(const Int8Page<D>& pg, bool valid, con
                                           float qscale, int page_tok, int kb, int L,
                                           SoftmaxState<D / 16>& st) {
   if (!valid) return;  // missing or flagged page: nothing to attend
-  int8_page_step<D, true>(pg, valid, qf, qscale, page_tok + 4 * kb, L, st);
+  int8_page_step<D, true>(pg, true, qf, qscale, page_tok + 4 * kb, L, st);
 }
 
 // 4 waves per SIMD: the compiler keeps this kernel within 128 VGPRs
@@ -336,7 +340,8 @@ decode_int8_kernel(DecodeArgs a) {
   constexpr int ND = D / 16;       // PV output blocks of 16 dims
   __shared__ DecodeShared<D> sh;
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int split = a.heads_fastest ? blockIdx.y : blockIdx.x;
+  const int g = a.heads_fastest ? blockIdx.x : blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, i16 = lane & 15, kb = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -442,13 +447,14 @@ __device__ __forceinline__ void page16_step(const Page16<D>& pg, bool valid, con
   f4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < NJ; ++j) s = mfma16x16x32<BF16>(pg.k[j], qf[j], s);
+  const bool tail = MASK && tok0 - 4 * static_cast<int>((threadIdx.x & 63) >> 4) + kBlockSize > L;
   float z[4];
   float zmax = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     z[j] = s[j] * scale_log2;
-    if (MASK) z[j] = valid && tok0 + j < L ? z[j] : -INFINITY;
-    zmax = fmaxf(zmax, z[j]);
+    if (tail) z[j] = tok0 + j < L ? z[j] : -INFINITY;
+    zmax = max_nc(zmax, z[j]);
   }
   raise_max(st, zmax);
   float pe[4];
@@ -525,7 +531,8 @@ decode_16bit_kernel(DecodeArgs a) {
   constexpr int ND = D / 16;  // PV output blocks
   __shared__ DecodeShared<D> sh;
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int split = a.heads_fastest ? blockIdx.y : blockIdx.x;
+  const int g = a.heads_fastest ? blockIdx.x : blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, i16 = lane & 15, kb = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -618,7 +625,8 @@ hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
 }
 
 dim3 decode_grid(const DecodeArgs& a) {
-  return dim3(a.max_splits, a.num_kv_heads, a.num_seqs);
+  return a.heads_fastest ? dim3(a.num_kv_heads, a.max_splits, a.num_seqs)
+                         : dim3(a.max_splits, a.num_kv_heads, a.num_seqs);
 }
 
 }  // namespace

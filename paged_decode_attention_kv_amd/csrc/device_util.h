@@ -68,14 +68,26 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 
 // Max / sum over the four lanes l, l^16, l^32, l^48 (same column of a 16x16
-// MFMA tile).
+// MFMA tile), with the gfx950 row-swap instructions (VALU only, no LDS round
+// trip): swapping a value with itself across 32-lane halves, then across
+// 16-lane rows, pairs every lane with its partner.
+__device__ __forceinline__ float max_nc(float a, float b) { return a > b ? a : b; }
+
 __device__ __forceinline__ float col_max(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  const uint32_t u = __float_as_uint(x);
+  const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = max_nc(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max_nc(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float col_sum(float x) {
-  x += __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  const uint32_t u = __float_as_uint(x);
+  const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  const uint32_t v = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ void store_out(void* out, int dtype, int64_t idx, float v) {

@@ -12,7 +12,7 @@ namespace pdakv {
 constexpr int kBlockSize = 16;        // tokens per page
 constexpr int kMaxGroup = 16;         // query heads per KV head (one MFMA N tile)
 constexpr int kWaves = 4;             // waves per decode workgroup
-constexpr int kMaxPagesPerSplit = 64; // LDS block-table cache size
+constexpr int kMaxPagesPerSplit = 128; // LDS block-table cache size
 
 struct WriteArgs {
   const void* k;
@@ -46,6 +46,7 @@ struct DecodeArgs {
   float* ws;         // split partials [B][Hq][max_splits][D + 2]
   int pages_per_split, max_splits;
   int32_t* err;
+  int heads_fastest;  // grid x = KV head (the heads of one page run side by side)
 };
 
 // Each returns hipSuccess or the launch error. Arguments are validated by the

@@ -64,7 +64,7 @@ def test_page_bytes_agree_with_oracle(P):
 def test_decode_plan_is_consistent(P, B, hkv, L):
     pps, n = P.pdakv_decode_plan(B, hkv, L)
     pages = -(-L // 16)
-    assert 16 <= pps <= 64 and pps % 4 == 0
+    assert 16 <= pps <= 128 and pps % 4 == 0
     assert n >= 1 and (n - 1) * pps < max(pages, 1) <= n * pps
     ws = P.pdakv_decode_workspace_bytes(B, 4 * hkv, hkv, 128, L)
     assert ws == (0 if n == 1 else B * 4 * hkv * n * 130 * 4)
