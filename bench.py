@@ -34,7 +34,38 @@ def parse():
     ap.add_argument("--no-points", action="store_true", help="skip the 2K/8K/32K points")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rotate-gb", type=float, default=2.2)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy a 1 GiB buffer 3 times (reference kernel of known size for "
+                         "calibrating the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_int8_llama8b-batched-1k8k-b64_traffic.txt")
+DECODE_SOURCE = os.path.join(ROOT, "paged_decode_attention_kv_amd", "csrc", "decode.hip")
+
+
+def source_hash() -> str:
+    import hashlib
+    with open(DECODE_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when the decode source changed since the counters were taken."""
+    try:
+        fields = {}
+        with open(TRAFFIC_PROFILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip()] = v.strip()
+        if fields.get("decode_source_sha256") != source_hash():
+            return None
+        return int(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def decode_bytes(wl, fmt_int8: bool) -> int:
@@ -73,6 +104,15 @@ def main():
         sys.exit(1)
     torch.cuda.init()
     stream = torch.cuda.current_stream()
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel(), "copies": 3}))
+        return
 
     def to_dev(t):
         if t.is_contiguous():
@@ -201,7 +241,7 @@ def main():
                    "paged_attn_decode_int8", "pages_per_split": pps, "max_splits": nsplit},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(),
                      "kernel": "paged_attn_decode_int8 (decode + split merge)",
                      "bytes_per_launch": dec_b, "launch_us": round(i8["decode_ms"] * 1e3, 2)},
         "step_bytes": step_b,
@@ -215,18 +255,17 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(wl, budget_s: float = 15.0):
-    """Time the oracle (as it stands) on a bounded sample of the same step.
+def cpu_baseline(wl, budget_s: float = 15.0, sample_seqs: int = 8):
+    """Time the oracle (as it stands, untuned) on a bounded sample of the step.
 
-    Per sampled sequence: its prefill K/V are quantized untimed (that is the
-    cache the step starts from); the timed part is the step itself for that
-    sequence — quantize the appended token, dequantize the cache, run the
-    oracle's FP64 decode for all 32 query heads. Sequences are processed until
-    ``budget_s`` of timed work is spent; the rate is sequences (= decoded
-    tokens) per second.
+    Setup (untimed): an oracle pool holding the prefill of ``sample_seqs``
+    sequences of the batch, quantized and written by the oracle. Timed: the
+    step for those sequences with the oracle's own functions — quantize the
+    appended tokens, write them into the pool, decode all query heads from the
+    pool — repeated until ``budget_s`` is spent. The rate is decoded tokens
+    (one per sequence per step) per second.
     """
     import numpy as np
-    import torch
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -234,27 +273,51 @@ def cpu_baseline(wl, budget_s: float = 15.0):
     except Exception:  # pragma: no cover
         cores = 1
     pre, app = wl.phase("prefill"), wl.phase("append")
-    done, spent = 0, 0.0
-    for b in np.random.default_rng(0).permutation(wl.num_seqs):
+    seqs = sorted(np.random.default_rng(0).choice(wl.num_seqs, sample_seqs, replace=False))
+    # compact pool for the sample: each sampled sequence keeps its page order
+    tables, ctx, total = [], [], 0
+    for b in seqs:
+        n = -(-int(wl.context_lens[b]) // 16)
+        tables.append(np.arange(total, total + n, dtype=np.int32))
+        ctx.append(int(wl.context_lens[b]))
+        total += n
+    bt = np.zeros((len(seqs), max(len(t) for t in tables)), np.int32)
+    for i, t in enumerate(tables):
+        bt[i, :len(t)] = t
+    ctx = np.array(ctx, np.int32)
+    pool = oracle.new_pool(oracle.KV_INT8_SYM, total, 16, wl.num_kv_heads, wl.head_dim)
+    a_k, a_v, a_slots, qs = [], [], [], []
+    for i, b in enumerate(seqs):
         rows = pre.seq_rows(int(b))
+        n_pre = rows.stop - rows.start
+        pos = np.arange(n_pre)
         kc, ks = oracle.quantize_rows(pre.k[rows])
         vc, vs = oracle.quantize_rows(pre.v[rows])
+        oracle.write_int8_tokens(pool, kc, ks, vc, vs, bt[i, pos // 16] * 16 + pos % 16, 16)
         arow = app.seq_rows(int(b))
+        a_k.append(app.k[arow])
+        a_v.append(app.v[arow])
+        a_slots.append(bt[i, n_pre // 16] * 16 + n_pre % 16)
+        qs.append(wl.q[int(b)])
+    import torch
+    ak, av, q = torch.cat(a_k), torch.cat(a_v), torch.stack(qs)
+    slots = np.array(a_slots, np.int32)
+    steps, spent = 0, 0.0
+    while spent < budget_s:
         t0 = time.perf_counter()
-        akc, aks = oracle.quantize_rows(app.k[arow])
-        avc, avs = oracle.quantize_rows(app.v[arow])
-        kf = oracle.dequantize_rows(np.concatenate([kc, akc]), np.concatenate([ks, aks]))
-        vf = oracle.dequantize_rows(np.concatenate([vc, avc]), np.concatenate([vs, avs]))
-        oracle.attend_one_sequence(oracle.as_f32(wl.q[int(b)]), kf, vf, wl.sm_scale)
+        kc, ks = oracle.quantize_rows(ak)
+        vc, vs = oracle.quantize_rows(av)
+        oracle.write_int8_tokens(pool, kc, ks, vc, vs, slots, 16)
+        oracle.decode_int8_from_pool(pool, bt, ctx, q, wl.sm_scale, 16, wl.num_kv_heads,
+                                     wl.head_dim)
         spent += time.perf_counter() - t0
-        done += 1
-        if spent >= budget_s:
-            break
-    del torch
-    return {"value": round(done / spent, 3), "unit": "tokens/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{done} of {wl.num_seqs} sequences of the batched step (append-token "
-                      f"quantize + dequantize + FP64 decode of 32 heads), {spent:.1f} s timed"}
+        steps += 1
+    return {"value": round(steps * len(seqs) / spent, 3), "unit": "tokens/s",
+            "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(seqs)} of {wl.num_seqs} sequences of the batched step "
+                      f"(mean context {float(ctx.mean()):.0f}); oracle quantize + page write of "
+                      f"the appended tokens and FP64 paged decode of all 32 query heads, "
+                      f"{steps} steps in {spent:.1f} s"}
 
 
 if __name__ == "__main__":
