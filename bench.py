@@ -187,7 +187,8 @@ def main():
             rotate_replicas=len(st["pools"]))
         del st
         torch.cuda.empty_cache()
-    pps, nsplit = P.pdakv_decode_plan(wl.num_seqs, wl.num_kv_heads, wl.max_context_len)
+    waves, ppw = P.pdakv_decode_plan(P.KV_INT8_SYM, wl.num_seqs, wl.num_kv_heads,
+                                     wl.max_context_len)
     i8 = res["int8"]
     dec_b = decode_bytes(wl, True)
     step_b = dec_b + write_bytes(wl.num_seqs, wl.num_kv_heads, wl.head_dim, True)
@@ -238,11 +239,11 @@ def main():
                    "mean_context": round(float(wl.context_lens.mean()), 1),
                    "heads_q_kv": [wl.num_q_heads, wl.num_kv_heads], "head_dim": wl.head_dim,
                    "block_size": 16, "step": "kv_quant_int8_sym_write(64 tokens) + "
-                   "paged_attn_decode_int8", "pages_per_split": pps, "max_splits": nsplit},
+                   "paged_attn_decode_int8", "decode_waves": waves},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "paged_attn_decode_int8 (decode + split merge)",
+                     "kernel": "paged_attn_decode_int8 (decode + partial merge)",
                      "bytes_per_launch": dec_b, "launch_us": round(i8["decode_ms"] * 1e3, 2)},
         "step_bytes": step_b,
         "step_gbs": round(step_b / (i8["step_ms"] * 1e-3) / 1e9, 1),

@@ -127,17 +127,24 @@ size_t pdakv_page_bytes(int kv_format, int block_size, int num_kv_heads, int hea
  * device, PDAKV_ERR_INVALID_ARG for a NULL flags_out. */
 int pdakv_capabilities(uint32_t* flags_out);
 
-/* Split plan the decode calls use for these sizes: the context of every
- * sequence is cut into chunks of *pages_per_split pages that run in separate
- * workgroups and are merged afterwards; *max_splits chunks cover
- * max_context_len. Either output pointer may be NULL. Returns
- * PDAKV_ERR_INVALID_ARG for negative sizes. Host arithmetic only. */
-int pdakv_decode_plan(int num_seqs, int num_kv_heads, int max_context_len,
-                      int* pages_per_split, int* max_splits);
+/* Launch plan of the decode calls for these sizes. The work of a call is the
+ * list of (sequence, KV head, page) items; the kernel splits the items of
+ * the actual context lengths evenly over *num_waves 64-lane waves (at least
+ * 4 items each, a unit that spans several waves is merged afterwards).
+ * *max_pages_per_wave is the share when every sequence is at
+ * max_context_len (<= 128). kv_format is PDAKV_KV_INT8_SYM or
+ * PDAKV_KV_16BIT. Either output pointer may be NULL. Returns
+ * PDAKV_ERR_INVALID_ARG for a bad format or negative sizes and
+ * PDAKV_ERR_UNSUPPORTED above 2^30 items. Host arithmetic only. */
+int pdakv_decode_plan(int kv_format, int num_seqs, int num_kv_heads, int max_context_len,
+                      int* num_waves, int* max_pages_per_wave);
 
-/* Device workspace the decode calls need for these sizes (0 when no split
- * merge is needed). The same value serves the INT8 and the 16-bit decode.
- * Layout: float partials [num_seqs][num_q_heads][max_splits][head_dim + 2]. */
+/* Device workspace the decode calls need for these sizes (0 when
+ * max_context_len or num_seqs is 0). The same value serves the INT8 and the
+ * 16-bit decode. Layout: float partials
+ * [num_waves + num_seqs * num_kv_heads][num_q_heads / num_kv_heads][head_dim + 2]
+ * (num_waves from the INT8 plan; the region padded to a multiple of 16
+ * bytes), then int32 [num_seqs * num_kv_heads][2] merge records. */
 size_t pdakv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                     int head_dim, int max_context_len);
 
@@ -184,11 +191,13 @@ int kv_write_16bit(const void* k_src, const void* v_src, int src_dtype,
  *                  pages of sequence b; only the first ceil(context_lens[b]/16)
  *                  entries are read.
  *   context_lens   device int32 [num_seqs]; 0 gives a zero output row; values
- *                  above max_context_len are clamped and flagged.
+ *                  above max_context_len are clamped and flagged. Pages
+ *                  whose block id is out of range are flagged and skipped; a
+ *                  (sequence, KV head) left with no token gives zero rows.
  *   max_context_len host upper bound of context_lens (sizes the launch).
  *   sm_scale       logit scale (usually 1/sqrt(head_dim)).
  *   workspace      device scratch of at least pdakv_decode_workspace_bytes(),
- *                  4-byte aligned; may be NULL when that is 0. Its contents
+ *                  16-byte aligned; may be NULL when that is 0. Its contents
  *                  need no initialization and are garbage afterwards. Calls
  *                  that share one workspace must not overlap in time.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads). The output

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpdakv.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m paged_decode_attention_kv_amd.build` "
+        f"{LIB_PATH} is not built; run `python paged_decode_attention_kv_amd/build.py` "
         "(the HIP library is required; there is no fallback)")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -43,7 +43,7 @@ _SIGS = {
     "pdakv_status_string": (ctypes.c_char_p, [_c_int]),
     "pdakv_page_bytes": (ctypes.c_size_t, [_c_int, _c_int, _c_int, _c_int]),
     "pdakv_capabilities": (_c_int, [ctypes.POINTER(ctypes.c_uint32)]),
-    "pdakv_decode_plan": (_c_int, [_c_int, _c_int, _c_int, ctypes.POINTER(_c_int),
+    "pdakv_decode_plan": (_c_int, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_int),
                                    ctypes.POINTER(_c_int)]),
     "pdakv_decode_workspace_bytes": (ctypes.c_size_t, [_c_int] * 5),
     "kv_quant_int8_sym_write": (_c_int, [_c_vp, _c_vp, _c_int, _c_i64, _c_int, _c_int] +
@@ -111,11 +111,13 @@ def pdakv_capabilities() -> int:
     return int(flags.value)
 
 
-def pdakv_decode_plan(num_seqs: int, num_kv_heads: int, max_context_len: int):
-    pps, n = _c_int(0), _c_int(0)
-    _check("pdakv_decode_plan", _lib.pdakv_decode_plan(num_seqs, num_kv_heads, max_context_len,
-                                                       ctypes.byref(pps), ctypes.byref(n)))
-    return pps.value, n.value
+def pdakv_decode_plan(kv_format: int, num_seqs: int, num_kv_heads: int, max_context_len: int):
+    """Returns (num_waves, max_pages_per_wave) of the decode launch."""
+    waves, pages = _c_int(0), _c_int(0)
+    _check("pdakv_decode_plan", _lib.pdakv_decode_plan(kv_format, num_seqs, num_kv_heads,
+                                                       max_context_len, ctypes.byref(waves),
+                                                       ctypes.byref(pages)))
+    return waves.value, pages.value
 
 
 def pdakv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int,

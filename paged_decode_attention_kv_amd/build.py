@@ -1,6 +1,7 @@
 """Build libpdakv.so (the HIP kernels + C ABI) for gfx950 with hipcc.
 
-Usage: python -m paged_decode_attention_kv_amd.build [--isa]
+Usage: python paged_decode_attention_kv_amd/build.py [--isa]
+(run by path: importing the package itself needs the built library)
 
 --isa additionally keeps the AMD assembly of every kernel under _build/ for
 register / occupancy review.
@@ -44,18 +45,17 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(isa: bool = False, verbose: bool = False) -> str:
+def build(isa: bool = False, verbose: bool = False, defines=(), out: str = LIB) -> str:
     srcs = []
     for s in SOURCES:
         p = os.path.join(CSRC, s)
         srcs += (["-x", "hip", p] if s.endswith(".cpp") else [p])
-    cmd = [hipcc()] + FLAGS + srcs + ["-o", LIB + ".tmp"]
+    cmd = [hipcc()] + FLAGS + [f"-D{d}" for d in defines] + srcs + ["-o", out + ".tmp"]
     cwd = None
     if isa:
-        out = os.path.join(ROOT, "_build")
-        os.makedirs(out, exist_ok=True)
+        cwd = os.path.join(ROOT, "_build")
+        os.makedirs(cwd, exist_ok=True)
         cmd.insert(1, "--save-temps")
-        cwd = out
     if verbose:
         print(" ".join(cmd))
     r = subprocess.run(cmd, cwd=cwd, capture_output=True, text=True)
@@ -66,8 +66,8 @@ def build(isa: bool = False, verbose: bool = False) -> str:
             if "warning" in ln and "packed-fp32-ops" not in ln]
     if verbose and errs:
         print("\n".join(errs))
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":

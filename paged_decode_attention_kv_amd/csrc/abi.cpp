@@ -1,7 +1,8 @@
-// C-ABI entry points of libpdakv.so: argument validation, split planning,
+// C-ABI entry points of libpdakv.so: argument validation, work planning,
 // and dispatch to the gfx950 kernels. See include/pdakv.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -14,9 +15,16 @@ namespace {
 using pdakv::DecodeArgs;
 using pdakv::WriteArgs;
 
-// Resident decode workgroups on MI355X: 256 CUs x 4 (the INT8 kernel's
-// register and LDS budget allows four 256-thread workgroups per CU).
-constexpr int kResidentWorkgroups = 1024;
+// Decode waves resident at once on MI355X: 256 CUs x 4 SIMDs x the waves per
+// SIMD the kernel's register budget allows.
+int64_t resident_waves(int kv_format) {
+  return int64_t{pdakv::kCUs} * 4 *
+         (kv_format == PDAKV_KV_INT8_SYM ? pdakv::kInt8WavesPerSimd : pdakv::k16WavesPerSimd);
+}
+
+// Largest item count (sequence x KV head x page) a launch may hold, so that
+// item indexes and wave * pages products stay in int32 on the device.
+constexpr int64_t kMaxItems = int64_t{1} << 30;
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
@@ -24,21 +32,34 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Pages per workgroup and number of splits for a launch. Each workgroup has a
-// fixed start-up and wind-down cost of several memory round trips, so splits
-// are made as long as possible while the longest sequences still spread over
-// all resident workgroups: about one workgroup per resident slot for the
-// largest context, 16..128 pages (a multiple of the four waves) each.
-void plan(int num_seqs, int num_kv_heads, int max_context_len, int* pps, int* nsplit) {
-  const int64_t max_pages = ceil_div(max_context_len, pdakv::kBlockSize);
-  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads;
-  int64_t p = ceil_div(units * max_pages, kResidentWorkgroups);
-  p = ceil_div(p, pdakv::kWaves) * pdakv::kWaves;
-  if (p < 16) p = 16;
-  if (p > pdakv::kMaxPagesPerSplit) p = pdakv::kMaxPagesPerSplit;
-  *pps = static_cast<int>(p);
-  const int64_t n = ceil_div(max_pages, p);
-  *nsplit = static_cast<int>(n < 1 ? 1 : n);
+// Upper bound of the items of a launch: every sequence at max_context_len.
+int64_t item_bound(int num_seqs, int num_kv_heads, int max_context_len) {
+  return static_cast<int64_t>(num_seqs) * num_kv_heads *
+         ceil_div(max_context_len, pdakv::kBlockSize);
+}
+
+// Waves of the decode grid. The device splits the actual items evenly over
+// them (at least kMinPagesPerWave each), so one resident round of waves is
+// used whenever that keeps every wave at <= kMaxPagesPerWave items; small
+// launches get fewer waves so that each still has a few pages to pipeline.
+int64_t plan_waves(int kv_format, int num_seqs, int num_kv_heads, int max_context_len) {
+  const int64_t items = item_bound(num_seqs, num_kv_heads, max_context_len);
+  int64_t v = std::max(resident_waves(kv_format), ceil_div(items, pdakv::kMaxPagesPerWave));
+  v = std::min(v, ceil_div(items, pdakv::kMinPagesPerWave));
+  v = std::max<int64_t>(v, 1);
+  return ceil_div(v, pdakv::kWaves) * pdakv::kWaves;
+}
+
+// Partial results region of the decode workspace (a multiple of 16 bytes):
+// [waves + units][G][D + 2] floats. The INT8 plan has the most waves; its
+// slots serve the 16-bit call too.
+size_t partials_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                      int max_context_len) {
+  const int64_t v = plan_waves(PDAKV_KV_INT8_SYM, num_seqs, num_kv_heads, max_context_len);
+  const int64_t slots = v + static_cast<int64_t>(num_seqs) * num_kv_heads;
+  const size_t bytes = static_cast<size_t>(slots) * (num_q_heads / num_kv_heads) *
+                       (head_dim + 2) * sizeof(float);
+  return (bytes + 15) / 16 * 16;
 }
 
 int check_write(const void* k_src, const void* v_src, int src_dtype, int64_t num_tokens,
@@ -86,9 +107,10 @@ int check_decode(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, const
   const size_t need = pdakv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
                                                    head_dim, max_context_len);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PDAKV_ERR_WORKSPACE;
-  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 3u)) return PDAKV_ERR_INVALID_ARG;
-  // grid limits: sequences on grid z, (sequence, head) pairs on grid x
-  if (num_seqs > 65535 || num_kv_heads > 65535) return PDAKV_ERR_UNSUPPORTED;
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15u)) return PDAKV_ERR_INVALID_ARG;
+  // device indexes are int32: items, (sequence, query head) pairs of the merge grid
+  if (item_bound(num_seqs, num_kv_heads, max_context_len) > kMaxItems)
+    return PDAKV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(num_seqs) * num_q_heads > INT32_MAX) return PDAKV_ERR_UNSUPPORTED;
   return PDAKV_OK;
 }
@@ -130,10 +152,13 @@ int decode_common(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, cons
   a.group = num_q_heads / num_kv_heads;
   a.max_ctx = max_context_len;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
-  plan(num_seqs, num_kv_heads, max_context_len, &a.pages_per_split, &a.max_splits);
+  a.num_waves = static_cast<int>(plan_waves(Int8 ? PDAKV_KV_INT8_SYM : PDAKV_KV_16BIT,
+                                             num_seqs, num_kv_heads, max_context_len));
   a.ws = static_cast<float*>(workspace);
+  a.desc = reinterpret_cast<int2*>(
+      static_cast<uint8_t*>(workspace) +
+      partials_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len));
   a.err = err_flag;
-  a.heads_fastest = 1;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = q_dtype == PDAKV_DTYPE_BF16;
   return hip_status(Int8 ? pdakv::launch_decode_int8(a, head_dim, bf16, s)
@@ -215,25 +240,29 @@ int pdakv_capabilities(uint32_t* flags_out) {
   return PDAKV_OK;
 }
 
-int pdakv_decode_plan(int num_seqs, int num_kv_heads, int max_context_len, int* pages_per_split,
-                      int* max_splits) {
+int pdakv_decode_plan(int kv_format, int num_seqs, int num_kv_heads, int max_context_len,
+                      int* num_waves, int* max_pages_per_wave) {
+  if (kv_format != PDAKV_KV_INT8_SYM && kv_format != PDAKV_KV_16BIT)
+    return PDAKV_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0) return PDAKV_ERR_INVALID_ARG;
-  int p = 0, n = 0;
-  plan(num_seqs, num_kv_heads, max_context_len, &p, &n);
-  if (pages_per_split) *pages_per_split = p;
-  if (max_splits) *max_splits = n;
+  if (item_bound(num_seqs, num_kv_heads, max_context_len) > kMaxItems)
+    return PDAKV_ERR_UNSUPPORTED;
+  const int64_t v = plan_waves(kv_format, num_seqs, num_kv_heads, max_context_len);
+  const int64_t p = std::max<int64_t>(
+      pdakv::kMinPagesPerWave, ceil_div(item_bound(num_seqs, num_kv_heads, max_context_len), v));
+  if (num_waves) *num_waves = static_cast<int>(v);
+  if (max_pages_per_wave) *max_pages_per_wave = static_cast<int>(p);
   return PDAKV_OK;
 }
 
 size_t pdakv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                     int head_dim, int max_context_len) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      max_context_len < 0)
+      max_context_len <= 0 || num_q_heads % num_kv_heads != 0)
     return 0;
-  int p = 0, n = 0;
-  plan(num_seqs, num_kv_heads, max_context_len, &p, &n);
-  if (n <= 1) return 0;
-  return static_cast<size_t>(num_seqs) * num_q_heads * n * (head_dim + 2) * sizeof(float);
+  if (item_bound(num_seqs, num_kv_heads, max_context_len) > kMaxItems) return 0;
+  return partials_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len) +
+         static_cast<size_t>(num_seqs) * num_kv_heads * 2 * sizeof(int32_t);
 }
 
 int kv_quant_int8_sym_write(const void* k_src, const void* v_src, int src_dtype,

@@ -10,10 +10,17 @@
 //
 // Work decomposition
 // ------------------
-// grid = (split, KV head, sequence); a workgroup of four waves owns one
-// (sequence, KV head) and a run of `pages_per_split` pages; wave w takes the
-// pages w, w+4, w+8, ... and keeps the next page's loads in flight while it
-// computes the current one. One page = 16 tokens = one 16x16 MFMA tile:
+// The work of one call is the list of (sequence, KV head, page) items, in
+// that order: KV head g of sequence b owns the items of its pages
+// 0..ceil(L_b/16)-1 (a "unit"). Every wave of the grid takes an equal,
+// contiguous run of P items (P = max(4, ceil(total / waves))), so all waves
+// stream the same number of pages whatever the spread of context lengths, and
+// they run independently: no LDS, no barrier. Each wave derives the total and
+// its start from the context lengths itself (a prefix sum over the batch,
+// 64 sequences per step, in registers).
+// A wave walks its run unit by unit ("segments"); in a segment it keeps the
+// next page's loads in flight while it computes the current one. One page =
+// 16 tokens = one 16x16 MFMA tile:
 //  * QK: S[t][h] = sum_d K[t][d] * q[h][d] with K in the A operand (row t =
 //    lane % 16) and the G query heads of the group in the B operand (column
 //    h = lane % 16, zero-padded to 16). Every K byte is fetched once and
@@ -33,12 +40,13 @@
 //    lanes of head l % 16. The V scale sV = f * 2^e (f in [0.5, 1)) enters
 //    the logit as the base-2 exponent e, so the folded probabilities
 //    P = 2^(s + e - m) * f never leave the fp16 range whatever the scales.
-// After the page loop the four waves combine through LDS. A sequence with a
-// single split writes its rows directly; otherwise every split writes a
-// partial (max, sum, accumulator) and merge_splits_kernel combines them.
-// (Merging in the last-arriving workgroup would need device-scope fences,
-// which write back and invalidate the L2 of the XCD: far dearer than the
-// second launch.)
+// A segment that covers a whole unit writes the output rows directly;
+// otherwise it writes a partial (max, sum, accumulator) into the slot
+// wave + unit (unique: along the item order both indexes only grow and one of
+// them grows at every segment boundary), and merge_kernel combines the
+// partials of each unit that spans several waves. (Merging in the last
+// arriving wave would need device-scope fences, which write back and
+// invalidate the L2 of the XCD: far dearer than the second launch.)
 #include "device_util.h"
 #include "launch.h"
 
@@ -54,13 +62,74 @@ namespace {
 constexpr float kTau = 8.0f;
 constexpr float kPScale = 7.0f;
 
-template <int D>
-struct DecodeShared {
-  int blk[kMaxPagesPerSplit];
-  float m[kWaves][kMaxGroup];
-  float l[kWaves][kMaxGroup];
-  float acc[kWaves][kMaxGroup][D];
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ int readlane(int x, int l) { return __builtin_amdgcn_readlane(x, l); }
+
+// ---------------------------------------------------------------------------
+// Work partition
+// ---------------------------------------------------------------------------
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// 64 sequences of the batch, one per lane: sequence 64 * c + lane.
+struct SeqChunk {
+  int c;     // chunk index
+  int L;     // lane's clamped context length (0 past the batch)
+  int np;    // lane's page count
+  int excl;  // pages (per KV head) of all sequences before the lane's
 };
+
+// Context lengths are clamped to [0, max_ctx]; an out-of-range value is
+// flagged when `report`.
+__device__ __forceinline__ SeqChunk load_chunk(const DecodeArgs& a, int c, int base, bool report,
+                                               int lane) {
+  SeqChunk s;
+  s.c = c;
+  const int b = 64 * c + lane;
+  int L = b < a.num_seqs ? a.ctx[b] : 0;
+  if (L < 0 || L > a.max_ctx) {
+    if (report) raise_flag(a.err, PDAKV_EFLAG_CONTEXT_RANGE);
+    L = L < 0 ? 0 : a.max_ctx;
+  }
+  s.L = L;
+  s.np = (L + kBlockSize - 1) / kBlockSize;
+  s.excl = base + wave_incl_scan(s.np, lane) - s.np;
+  return s;
+}
+
+// Pages (per KV head) of all sequences up to the end of the chunk.
+__device__ __forceinline__ int chunk_end(const SeqChunk& s) { return readlane(s.excl + s.np, 63); }
+
+__device__ __forceinline__ int pages_per_wave(int total, int waves) {
+  const int p = (total + waves - 1) / waves;
+  return p > kMinPagesPerWave ? p : kMinPagesPerWave;
+}
+
+// Zero output rows of the empty sequences of the chunk; sequence b is done by
+// wave b % waves.
+__device__ void zero_rows(const DecodeArgs& a, const SeqChunk& s, int wave, int D, int lane) {
+  const int b = 64 * s.c + lane;
+  uint64_t m = __ballot(b < a.num_seqs && s.np == 0 && b % a.num_waves == wave);
+  while (m) {
+    const int bb = 64 * s.c + __builtin_ctzll(m);
+    m &= m - 1;
+    for (int i = lane; i < a.num_q_heads * D; i += 64)
+      store_out(a.out, a.out_dtype, bb * a.out_ss + (i / D) * a.out_sh + i % D, 0.f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Online softmax state and shared helpers
+// ---------------------------------------------------------------------------
 
 // Eight consecutive 16-bit q elements (dims d0..d0+7) of head h, as four
 // words. One 16-byte load when the host found q's pointer and strides 16-byte
@@ -75,70 +144,6 @@ __device__ __forceinline__ u4_t q_chunk8(const DecodeArgs& a, int b, int h, int 
   return w;
 }
 
-// Clamped context length of sequence b (flags an out-of-range value).
-__device__ __forceinline__ int context_len(const DecodeArgs& a, int b, bool report) {
-  int L = a.ctx[b];
-  if (L < 0 || L > a.max_ctx) {
-    if (report) raise_flag(a.err, PDAKV_EFLAG_CONTEXT_RANGE);
-    L = L < 0 ? 0 : a.max_ctx;
-  }
-  return L;
-}
-
-// Load this split's block-table entries into LDS (invalid ids -> -1).
-__device__ __forceinline__ void load_block_ids(const DecodeArgs& a, int* sblk, int b, int p0,
-                                               int np) {
-  if (static_cast<int>(threadIdx.x) < np) {
-    int blk = a.bt[static_cast<int64_t>(b) * a.bt_stride + p0 + threadIdx.x];
-    if (blk < 0 || blk >= a.num_blocks) {
-      raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
-      blk = -1;
-    }
-    sblk[threadIdx.x] = blk;
-  }
-}
-
-// Zero output rows of (b, group g): empty context.
-__device__ void write_zero_rows(const DecodeArgs& a, int b, int g, int D) {
-  for (int i = threadIdx.x; i < a.group * D; i += blockDim.x) {
-    const int h = g * a.group + i / D;
-    store_out(a.out, a.out_dtype, b * a.out_ss + h * a.out_sh + i % D, 0.f);
-  }
-}
-
-// Combine the four waves' (m, l, acc); write the final rows (the sequence has
-// a single split) or this split's partial for merge_splits_kernel.
-template <int D>
-__device__ void finish(const DecodeArgs& a, DecodeShared<D>& sh, int b, int g, int split,
-                       int nsplit) {
-  const bool direct = nsplit == 1;
-  for (int i = threadIdx.x; i < a.group * D; i += blockDim.x) {
-    const int hh = i / D, d = i % D;
-    float ms = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) ms = fmaxf(ms, sh.m[w][hh]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float c = exp2f(sh.m[w][hh] - ms);  // 0 for a wave without pages
-      num += c * sh.acc[w][hh][d];
-      den += c * sh.l[w][hh];
-    }
-    const int h = g * a.group + hh;
-    if (direct) {
-      store_out(a.out, a.out_dtype, b * a.out_ss + h * a.out_sh + d, num / den);
-    } else {
-      float* p = a.ws + ((static_cast<int64_t>(b) * a.num_q_heads + h) * a.max_splits + split) *
-                            (D + 2);
-      p[d] = num;
-      if (d == 0) {
-        p[D] = ms;
-        p[D + 1] = den;
-      }
-    }
-  }
-}
-
 template <int ND>
 struct SoftmaxState {
   float m;   // running max (base-2 units)
@@ -147,10 +152,14 @@ struct SoftmaxState {
   f4_t acc[ND];
 };
 
+// Start value of the running max: finite, so that a page whose tokens are all
+// masked (logit -inf) adds exactly 0 before any token was seen.
+constexpr float kMaxInit = -1e30f;
+
 template <int ND>
 __device__ __forceinline__ void softmax_init(SoftmaxState<ND>& st) {
-  st.m = -INFINITY;
-  st.mk = -INFINITY;
+  st.m = kMaxInit;
+  st.mk = kMaxInit;
   st.l = 0.f;
 #pragma unroll
   for (int k = 0; k < ND; ++k) st.acc[k] = f4_t{0.f, 0.f, 0.f, 0.f};
@@ -161,7 +170,7 @@ __device__ __forceinline__ void raise_max(SoftmaxState<ND>& st, float zmax) {
   zmax = col_max(zmax);
   if (__any(zmax > st.m + kTau)) {
     const float m_new = fmaxf(st.m, zmax);
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 on the first page
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 on the first token
     st.m = m_new;
     st.mk = m_new - kPScale;
     st.l *= alpha;
@@ -225,17 +234,33 @@ struct Int8Page {
   u2_t ks, vs;     // scales of tokens 4*kb + (0..3)
 };
 
+// Page reads go through a buffer resource made for each page's head block
+// (base in SGPRs, 32-bit lane offsets, constant parts in the instruction's
+// offset field): no 64-bit per-lane address arithmetic, and a read outside
+// the head block would return 0 instead of touching other memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_block(const uint8_t* hp, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(hp), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ u4_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u2_t ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 template <int D>
 __device__ __forceinline__ void load_int8_page(Int8Page<D>& pg, const uint8_t* hp, int i16,
                                                int kb) {
+  const __amdgpu_buffer_rsrc_t r = head_block(hp, 32 * D + 64);
+  const uint32_t ko = i16 * D + 16 * kb;           // K: token i16
+  const uint32_t vo = kb * 4 * D + 16 * i16;       // V: token group kb (after 16*D)
+  const uint32_t so = 32 * D + 8 * kb;             // scales of tokens 4*kb..4*kb+3
 #pragma unroll
-  for (int i = 0; i < D / 64; ++i)
-    pg.k[i] = *reinterpret_cast<const u4_t*>(hp + i16 * D + 64 * i + 16 * kb);
+  for (int i = 0; i < D / 64; ++i) pg.k[i] = ld16(r, ko + 64 * i);
 #pragma unroll
-  for (int i = 0; i < D / 64; ++i)
-    pg.v[i] = *reinterpret_cast<const u4_t*>(hp + 16 * D + kb * 4 * D + 256 * i + 16 * i16);
-  pg.ks = *reinterpret_cast<const u2_t*>(hp + 32 * D + 8 * kb);
-  pg.vs = *reinterpret_cast<const u2_t*>(hp + 32 * D + 32 + 8 * kb);
+  for (int i = 0; i < D / 64; ++i) pg.v[i] = ld16(r, vo + 16 * D + 256 * i);
+  pg.ks = ld8(r, so);
+  pg.vs = ld8(r, so + 32);
 }
 
 template <int D>
@@ -251,19 +276,27 @@ __device__ __forceinline__ f4_t int8_qk(const Int8Page<D>& pg, const h8_t* qf) {
   return s;
 }
 
-// One page; tok0 = position of this lane's first token (4*kb within the
-// page). MASK: the page may extend past L (its last page); then the V scales of
-// the tokens past L are replaced by 1.0 (the slots may hold anything) and their
-// logits by -inf.
-template <int D, bool MASK>
-__device__ __forceinline__ void int8_page_step(const Int8Page<D>& pg, bool valid, const h8_t* qf,
-                                               float qscale, int tok0, int L,
+// Position of this lane's first token in a page starting at page_tok: lane
+// (i16, kb) holds tokens 4*kb + (0..3) of the tile.
+__device__ __forceinline__ int lane_token(int page_tok) {
+  return page_tok + 4 * static_cast<int>((threadIdx.x & 63) >> 4);
+}
+
+// One page starting at token page_tok (wave-uniform). The tokens at or past
+// the limit L (the context length; the page start for a skipped page) get V
+// scale 1.0 (their slots may hold anything) and logit -inf. (A separate
+// unmasked path for full pages costs more registers than the masks cost
+// instructions.)
+template <int D>
+__device__ __forceinline__ void int8_page_step(const Int8Page<D>& pg, const h8_t* qf,
+                                               float qscale, int page_tok, int L,
                                                SoftmaxState<D / 16>& st) {
   constexpr int ND = D / 16;
   const f4_t s = int8_qk<D>(pg, qf);
   const uint32_t ksw[2] = {pg.ks.x, pg.ks.y};
   uint32_t vsw[2] = {pg.vs.x, pg.vs.y};
-  const bool tail = MASK && tok0 - 4 * static_cast<int>((threadIdx.x & 63) >> 4) + kBlockSize > L;
+  const bool tail = page_tok + kBlockSize > L;
+  const int tok0 = tail ? lane_token(page_tok) : 0;
   if (tail) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -308,96 +341,34 @@ __device__ __forceinline__ void int8_page_step(const Int8Page<D>& pg, bool valid
   }
 }
 
-// Load page p of the split into pg. The loads are issued unconditionally (a
-// missing or flagged page reads page 0, which exists, and is then skipped) so
-// that the number of loads in flight is the same on every path and the
-// compiler can wait for the current page only.
-template <int D>
-__device__ __forceinline__ bool int8_load(Int8Page<D>& pg, const DecodeShared<D>& sh, int p,
-                                          int np, const uint8_t* base, int64_t page_bytes,
-                                          int i16, int kb) {
-  const int blk = p < np ? sh.blk[p] : -1;
-  load_int8_page<D>(pg, base + (blk >= 0 ? blk : 0) * page_bytes, i16, kb);
-  return blk >= 0;
-}
+// The INT8 page format as seen by the decode loop.
+template <int D_, bool QBF16, int G_ = 1>
+struct Int8Kind {
+  static constexpr int D = D_;
+  static constexpr int kGroup = G_;  // pages per register buffer
+  static constexpr int kHeadBytes = 32 * D + 64;
+  using Page = Int8Page<D>;
+  h8_t qf[D / 32];
+  float qscale;
 
-// page_tok = position of the page's first token. (A separate unmasked path
-// for full pages costs more registers than the masks cost instructions.)
-template <int D>
-__device__ __forceinline__ void int8_step(const Int8Page<D>& pg, bool valid, const h8_t* qf,
-                                          float qscale, int page_tok, int kb, int L,
-                                          SoftmaxState<D / 16>& st) {
-  if (!valid) return;  // missing or flagged page: nothing to attend
-  int8_page_step<D, true>(pg, true, qf, qscale, page_tok + 4 * kb, L, st);
-}
-
-// 4 waves per SIMD: the compiler keeps this kernel within 128 VGPRs
-template <int D, bool QBF16>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(4))) void
-decode_int8_kernel(DecodeArgs a) {
-  constexpr int HB = 32 * D + 64;  // head block bytes
-  constexpr int NJ = D / 32;       // QK instructions (16x16x32)
-  constexpr int ND = D / 16;       // PV output blocks of 16 dims
-  __shared__ DecodeShared<D> sh;
-
-  const int split = a.heads_fastest ? blockIdx.y : blockIdx.x;
-  const int g = a.heads_fastest ? blockIdx.x : blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, i16 = lane & 15, kb = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-  const int L = context_len(a, b, threadIdx.x == 0 && split == 0);
-  const int npages = (L + kBlockSize - 1) / kBlockSize;
-  const int p0 = split * a.pages_per_split;
-  if (p0 >= npages) {
-    if (npages == 0 && split == 0) write_zero_rows(a, b, g, D);
-    return;
+  __device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int g, int i16, int kb,
+                                         bool hvalid) {
+    qscale = load_q_scaled<D / 32, QBF16>(
+        a, b, g * a.group + (hvalid ? i16 : 0), hvalid,
+        [kb](int j) { return 64 * (j / 2) + 16 * kb + 8 * (j % 2); }, qf);
   }
-  const int nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
-  const int np = min(npages - p0, a.pages_per_split);
-  load_block_ids(a, sh.blk, b, p0, np);
-
-  const bool hvalid = i16 < a.group;
-  h8_t qf[NJ];
-  const float qscale = load_q_scaled<NJ, QBF16>(
-      a, b, g * a.group + (hvalid ? i16 : 0), hvalid,
-      [kb](int j) { return 64 * (j / 2) + 16 * kb + 8 * (j % 2); }, qf);
-
-  SoftmaxState<ND> st;
-  softmax_init(st);
-  __syncthreads();
-
-  // Ping-pong register buffers: page i+4's loads are in flight while page i
-  // is computed. Wave w owns pages w, w+4, w+8, ... of the split.
-  const uint8_t* base = a.pool + static_cast<int64_t>(g) * HB;
-  Int8Page<D> pa, pb;
-  int p = wave;
-  bool va = int8_load<D>(pa, sh, p, np, base, a.page_bytes, i16, kb);
-  while (p < np) {
-    const int p1 = p + kWaves;
-    const bool vb = int8_load<D>(pb, sh, p1, np, base, a.page_bytes, i16, kb);
-    int8_step<D>(pa, va, qf, qscale, (p0 + p) * kBlockSize, kb, L, st);
-    if (p1 >= np) break;
-    const int p2 = p1 + kWaves;
-    va = int8_load<D>(pa, sh, p2, np, base, a.page_bytes, i16, kb);
-    int8_step<D>(pb, vb, qf, qscale, (p0 + p1) * kBlockSize, kb, L, st);
-    p = p2;
+  static __device__ __forceinline__ void load(Page& pg, const uint8_t* hp, int i16, int kb) {
+    load_int8_page<D>(pg, hp, i16, kb);
   }
-
-  st.l = col_sum(st.l);
-  if (hvalid) {
-    if (kb == 0) {
-      sh.m[wave][i16] = st.m;
-      sh.l[wave][i16] = st.l;
-    }
-#pragma unroll
-    for (int k = 0; k < ND; ++k)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        sh.acc[wave][i16][64 * (k / 4) + 16 * kb + 4 * j + (k % 4)] = st.acc[k][j];
+  __device__ __forceinline__ void step(const Page& pg, int page_tok, int L,
+                                       SoftmaxState<D / 16>& st) const {
+    int8_page_step<D>(pg, qf, qscale, page_tok, L, st);
   }
-  __syncthreads();
-  finish<D>(a, sh, b, g, split, nsplit);
-}
+  // dimension of accumulator element acc[k][j] in lane (i16, kb)
+  static __device__ __forceinline__ int acc_dim(int k, int j, int kb) {
+    return 64 * (k / 4) + 16 * kb + 4 * j + (k % 4);
+  }
+};
 
 // ---------------------------------------------------------------------------
 // 16-bit pages (control)
@@ -420,12 +391,13 @@ struct Page16 {
 
 template <int D>
 __device__ __forceinline__ void load_page16(Page16<D>& pg, const uint8_t* hp, int i16, int kb) {
+  const __amdgpu_buffer_rsrc_t r = head_block(hp, 64 * D);
+  const uint32_t ko = i16 * 2 * D + 16 * kb;
+  const uint32_t vo = 32 * D + kb * 8 * D + 16 * i16;
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j)
-    pg.k[j] = *reinterpret_cast<const u4_t*>(hp + i16 * 2 * D + 64 * j + 16 * kb);
+  for (int j = 0; j < D / 32; ++j) pg.k[j] = ld16(r, ko + 64 * j);
 #pragma unroll
-  for (int i = 0; i < D / 32; ++i)
-    pg.v[i] = *reinterpret_cast<const u4_t*>(hp + 32 * D + kb * 8 * D + 256 * i + 16 * i16);
+  for (int i = 0; i < D / 32; ++i) pg.v[i] = ld16(r, vo + 256 * i);
 }
 
 template <bool BF16>
@@ -439,15 +411,16 @@ __device__ __forceinline__ f4_t mfma16x16x16(u2_t a_bits, u2_t b_bits, f4_t c) {
                                                  __builtin_bit_cast(h4_t, b_bits), c, 0, 0, 0);
 }
 
-template <int D, bool BF16, bool MASK>
-__device__ __forceinline__ void page16_step(const Page16<D>& pg, bool valid, const u4_t* qf,
-                                            float scale_log2, int tok0, int L,
+template <int D, bool BF16>
+__device__ __forceinline__ void page16_step(const Page16<D>& pg, const u4_t* qf,
+                                            float scale_log2, int page_tok, int L,
                                             SoftmaxState<D / 16>& st) {
   constexpr int NJ = D / 32, ND = D / 16;
   f4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < NJ; ++j) s = mfma16x16x32<BF16>(pg.k[j], qf[j], s);
-  const bool tail = MASK && tok0 - 4 * static_cast<int>((threadIdx.x & 63) >> 4) + kBlockSize > L;
+  const bool tail = page_tok + kBlockSize > L;
+  const int tok0 = tail ? lane_token(page_tok) : 0;
   float z[4];
   float zmax = -INFINITY;
 #pragma unroll
@@ -462,6 +435,23 @@ __device__ __forceinline__ void page16_step(const Page16<D>& pg, bool valid, con
   for (int j = 0; j < 4; ++j) {
     pe[j] = __builtin_amdgcn_exp2f(z[j] - st.mk);
     st.l += pe[j];
+  }
+  // V of masked tokens -> 0 (a slot past the context may hold NaN bits, and
+  // 0 * NaN would reach the accumulator). Word 2r + w of pg.v[i] holds
+  // tokens 2w, 2w+1 of one dimension.
+  u4_t v[D / 32];
+#pragma unroll
+  for (int i = 0; i < D / 32; ++i) v[i] = pg.v[i];
+  if (tail) {
+    const uint32_t m01 = (tok0 < L ? 0xFFFFu : 0u) | (tok0 + 1 < L ? 0xFFFF0000u : 0u);
+    const uint32_t m23 = (tok0 + 2 < L ? 0xFFFFu : 0u) | (tok0 + 3 < L ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      v[i][0] &= m01;
+      v[i][1] &= m23;
+      v[i][2] &= m01;
+      v[i][3] &= m23;
+    }
   }
   if constexpr (BF16) {
     // exact three-way split into truncated bf16 parts (8 + 8 + 8 bits)
@@ -481,7 +471,7 @@ __device__ __forceinline__ void page16_step(const Page16<D>& pg, bool valid, con
     const u2_t w3 = {p3[0] | (p3[1] << 16), p3[2] | (p3[3] << 16)};
 #pragma unroll
     for (int k = 0; k < ND; ++k) {
-      const u2_t vw = {pg.v[k / 2][2 * (k % 2)], pg.v[k / 2][2 * (k % 2) + 1]};
+      const u2_t vw = {v[k / 2][2 * (k % 2)], v[k / 2][2 * (k % 2) + 1]};
       st.acc[k] = mfma16x16x16<true>(vw, w1, st.acc[k]);
       st.acc[k] = mfma16x16x16<true>(vw, w2, st.acc[k]);
       st.acc[k] = mfma16x16x16<true>(vw, w3, st.acc[k]);
@@ -497,142 +487,318 @@ __device__ __forceinline__ void page16_step(const Page16<D>& pg, bool valid, con
     const u2_t pl = {pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3])};
 #pragma unroll
     for (int k = 0; k < ND; ++k) {
-      const u2_t vw = {pg.v[k / 2][2 * (k % 2)], pg.v[k / 2][2 * (k % 2) + 1]};
+      const u2_t vw = {v[k / 2][2 * (k % 2)], v[k / 2][2 * (k % 2) + 1]};
       st.acc[k] = mfma16x16x16<false>(vw, ph, st.acc[k]);
       st.acc[k] = mfma16x16x16<false>(vw, pl, st.acc[k]);
     }
   }
 }
 
-// Unconditional loads, as int8_load.
-template <int D>
-__device__ __forceinline__ bool load16(Page16<D>& pg, const DecodeShared<D>& sh, int p, int np,
-                                       const uint8_t* base, int64_t page_bytes, int i16,
-                                       int kb) {
-  const int blk = p < np ? sh.blk[p] : -1;
-  load_page16<D>(pg, base + (blk >= 0 ? blk : 0) * page_bytes, i16, kb);
-  return blk >= 0;
-}
+// The 16-bit page format as seen by the decode loop (q stays in K's dtype).
+template <int D_, bool BF16, int G_ = 1>
+struct F16Kind {
+  static constexpr int D = D_;
+  static constexpr int kGroup = G_;  // pages per register buffer
+  static constexpr int kHeadBytes = 64 * D;
+  using Page = Page16<D>;
+  u4_t qf[D / 32];  // fragment j: dims 32*j + 8*kb + (0..7)
+  float scale_log2;
 
-template <int D, bool BF16>
-__device__ __forceinline__ void step16(const Page16<D>& pg, bool valid, const u4_t* qf,
-                                       float scale_log2, int page_tok, int kb, int L,
-                                       SoftmaxState<D / 16>& st) {
-  if (!valid) return;  // missing or flagged page: nothing to attend
-  page16_step<D, BF16, true>(pg, valid, qf, scale_log2, page_tok + 4 * kb, L, st);
-}
-
-// 3 waves per SIMD: the compiler keeps this kernel within 168 VGPRs
-template <int D, bool BF16>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(3))) void
-decode_16bit_kernel(DecodeArgs a) {
-  constexpr int HB = 64 * D;  // head block bytes
-  constexpr int NJ = D / 32;  // QK instructions
-  constexpr int ND = D / 16;  // PV output blocks
-  __shared__ DecodeShared<D> sh;
-
-  const int split = a.heads_fastest ? blockIdx.y : blockIdx.x;
-  const int g = a.heads_fastest ? blockIdx.x : blockIdx.y, b = blockIdx.z;
-  const int lane = threadIdx.x & 63, i16 = lane & 15, kb = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-
-  const int L = context_len(a, b, threadIdx.x == 0 && split == 0);
-  const int npages = (L + kBlockSize - 1) / kBlockSize;
-  const int p0 = split * a.pages_per_split;
-  if (p0 >= npages) {
-    if (npages == 0 && split == 0) write_zero_rows(a, b, g, D);
-    return;
-  }
-  const int nsplit = (npages + a.pages_per_split - 1) / a.pages_per_split;
-  const int np = min(npages - p0, a.pages_per_split);
-  load_block_ids(a, sh.blk, b, p0, np);
-
-  // q fragment j: dims 32*j + 8*kb + r (raw 16-bit values, same dtype as K)
-  const bool hvalid = i16 < a.group;
-  const int h_load = g * a.group + (hvalid ? i16 : 0);
-  u4_t qf[NJ];
+  __device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int g, int i16, int kb,
+                                         bool hvalid) {
+    const int h_load = g * a.group + (hvalid ? i16 : 0);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) qf[j] = q_chunk8(a, b, h_load, 32 * j + 8 * kb);
+    for (int j = 0; j < D / 32; ++j) qf[j] = q_chunk8(a, b, h_load, 32 * j + 8 * kb);
 #pragma unroll
-  for (int j = 0; j < NJ; ++j)
-    if (!hvalid) qf[j] = u4_t{0u, 0u, 0u, 0u};
-
-  SoftmaxState<ND> st;
-  softmax_init(st);
-  __syncthreads();
-
-  // Ping-pong register buffers, as in the INT8 kernel.
-  const uint8_t* base = a.pool + static_cast<int64_t>(g) * HB;
-  Page16<D> pa, pb;
-  int p = wave;
-  bool va = load16<D>(pa, sh, p, np, base, a.page_bytes, i16, kb);
-  while (p < np) {
-    const int p1 = p + kWaves;
-    const bool vb = load16<D>(pb, sh, p1, np, base, a.page_bytes, i16, kb);
-    step16<D, BF16>(pa, va, qf, a.scale_log2, (p0 + p) * kBlockSize, kb, L, st);
-    if (p1 >= np) break;
-    const int p2 = p1 + kWaves;
-    va = load16<D>(pa, sh, p2, np, base, a.page_bytes, i16, kb);
-    step16<D, BF16>(pb, vb, qf, a.scale_log2, (p0 + p1) * kBlockSize, kb, L, st);
-    p = p2;
+    for (int j = 0; j < D / 32; ++j)
+      if (!hvalid) qf[j] = u4_t{0u, 0u, 0u, 0u};
+    scale_log2 = a.scale_log2;
   }
+  static __device__ __forceinline__ void load(Page& pg, const uint8_t* hp, int i16, int kb) {
+    load_page16<D>(pg, hp, i16, kb);
+  }
+  __device__ __forceinline__ void step(const Page& pg, int page_tok, int L,
+                                       SoftmaxState<D / 16>& st) const {
+    page16_step<D, BF16>(pg, qf, scale_log2, page_tok, L, st);
+  }
+  static __device__ __forceinline__ int acc_dim(int k, int j, int kb) {
+    return 32 * (k / 2) + 8 * kb + 2 * j + (k % 2);
+  }
+};
 
-  st.l = col_sum(st.l);
-  if (hvalid) {
-    if (kb == 0) {
-      sh.m[wave][i16] = st.m;
-      sh.l[wave][i16] = st.l;
-    }
+// ---------------------------------------------------------------------------
+// Decode loop
+// ---------------------------------------------------------------------------
+
+// Final rows (whole unit) or the partial of slot `slot`: [D] accumulator,
+// then the running max and the sum. A unit without any attendable token (all
+// its pages flagged) gets zero rows.
+template <class K>
+__device__ __forceinline__ void write_result(const DecodeArgs& a, SoftmaxState<K::D / 16>& st,
+                                             int b, int g, int slot, bool whole, int i16,
+                                             int kb) {
+  constexpr int D = K::D, ND = D / 16;
+  const float l = col_sum(st.l);
+  if (i16 >= a.group) return;
+  const int h = g * a.group + i16;
+  if (whole) {
+    const int64_t o = b * a.out_ss + h * a.out_sh;
 #pragma unroll
     for (int k = 0; k < ND; ++k)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        sh.acc[wave][i16][32 * (k / 2) + 8 * kb + 2 * j + (k % 2)] = st.acc[k][j];
+        store_out(a.out, a.out_dtype, o + K::acc_dim(k, j, kb), l > 0.f ? st.acc[k][j] / l : 0.f);
+  } else {
+    float* pp = a.ws + (static_cast<int64_t>(slot) * a.group + i16) * (D + 2);
+#pragma unroll
+    for (int k = 0; k < ND; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pp[K::acc_dim(k, j, kb)] = st.acc[k][j];
+    if (kb == 0) {
+      pp[D] = st.m;
+      pp[D + 1] = l;
+    }
   }
-  __syncthreads();
-  finish<D>(a, sh, b, g, split, nsplit);
 }
 
-// split merge: out = sum_i 2^(m_i - m) acc_i / sum_i 2^(m_i - m) l_i for the
-// sequences with more than one split (the others were written directly)
-template <int D>
-__global__ __launch_bounds__(D) void merge_splits_kernel(DecodeArgs a) {
-  const int bh = blockIdx.x;
-  const int b = bh / a.num_q_heads, h = bh % a.num_q_heads;
-  const int d = threadIdx.x;
-  const int L = context_len(a, b, false);
-  const int npages = (L + kBlockSize - 1) / kBlockSize;
-  const int n = (npages + a.pages_per_split - 1) / a.pages_per_split;
-  if (n <= 1) return;
-  const float* p = a.ws + static_cast<int64_t>(bh) * a.max_splits * (D + 2);
-  float ms = -INFINITY;
-  for (int i = 0; i < n; ++i) ms = fmaxf(ms, p[i * (D + 2) + D]);
-  float num = 0.f, den = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const float c = exp2f(p[i * (D + 2) + D] - ms);
-    num += c * p[i * (D + 2) + d];
-    den += c * p[i * (D + 2) + D + 1];
+// Pages p .. p+n-1 (n <= kMaxPagesPerWave) of KV head g of sequence b.
+template <class K>
+__device__ __forceinline__ void run_segment(const DecodeArgs& a, K& kind, int b, int g, int p,
+                                            int n, int L, int slot, bool whole, int lane) {
+  constexpr int ND = K::D / 16;
+  const int i16 = lane & 15, kb = lane >> 4;
+  kind.load_q(a, b, g, i16, kb, i16 < a.group);
+
+  // block ids: lane i holds pages p + i and p + 64 + i; out-of-range ids are
+  // flagged and become -1 (the page is skipped)
+  const int32_t* row = a.bt + static_cast<int64_t>(b) * a.bt_stride + p;
+  int blk0 = lane < n ? row[lane] : 0;
+  int blk1 = lane + 64 < n ? row[lane + 64] : 0;
+  if (blk0 < 0 || blk0 >= a.num_blocks) {
+    raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
+    blk0 = -1;
   }
-  store_out(a.out, a.out_dtype, b * a.out_ss + h * a.out_sh + d, num / den);
+  if (blk1 < 0 || blk1 >= a.num_blocks) {
+    raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
+    blk1 = -1;
+  }
+  const uint8_t* base = a.pool + static_cast<int64_t>(g) * K::kHeadBytes;
+  auto block_of = [&](int i) { return i < 64 ? readlane(blk0, i) : readlane(blk1, i - 64); };
+  // Missing pages read page 0 (it exists) with all tokens masked, so every
+  // iteration issues the same loads and consumes them, and the compiler waits
+  // for the current page only.
+  auto page_at = [&](int blk) { return base + (blk >= 0 ? blk : 0) * a.page_bytes; };
+  auto limit = [&](int blk, int page_tok) { return blk >= 0 ? L : page_tok; };
+
+  SoftmaxState<ND> st;
+  softmax_init(st);
+  // Two register buffers of G pages each (a "group"), each refilled right
+  // after its pages are consumed: while one group is computed the next is in
+  // flight. Pages past the end of the segment load the last page again (a
+  // cache hit) and are fully masked, so every refill issues the same loads.
+  constexpr int G = K::kGroup;
+  typename K::Page ga[G], gb[G];
+  int la[G], lb[G];  // mask limits
+  const int tok = p * kBlockSize;
+  auto fill = [&](typename K::Page* grp, int* lim, int first) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int q = first + j;
+      const int bq = block_of(q < n ? q : n - 1);
+      const int tq = tok + q * kBlockSize;
+      lim[j] = q < n ? limit(bq, tq) : tq;
+      K::load(grp[j], page_at(bq), i16, kb);
+    }
+  };
+  auto consume = [&](const typename K::Page* grp, const int* lim, int first) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) kind.step(grp[j], tok + (first + j) * kBlockSize, lim[j], st);
+  };
+  fill(ga, la, 0);
+  __builtin_amdgcn_sched_barrier(0);  // keep the groups' loads in order
+  fill(gb, lb, G);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0;; i += 2 * G) {
+    consume(ga, la, i);
+    if (i + G >= n) break;
+    __builtin_amdgcn_sched_barrier(0);
+    fill(ga, la, i + 2 * G);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(gb, lb, i + G);
+    __builtin_amdgcn_sched_barrier(0);
+    fill(gb, lb, i + 3 * G);
+    __builtin_amdgcn_sched_barrier(0);
+    if (i + 2 * G >= n) break;
+  }
+  write_result<K>(a, st, b, g, slot, whole, i16, kb);
+}
+
+template <class K>
+__device__ __forceinline__ void decode_wave(const DecodeArgs& a) {
+  const int lane = lane_id();
+  const int wave = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hkv = a.num_kv_heads;
+
+  // total pages; zero rows of empty sequences
+  const int nchunk = (a.num_seqs + 63) / 64;
+  SeqChunk s = load_chunk(a, 0, 0, wave == 0, lane);
+  zero_rows(a, s, wave, K::D, lane);
+  int pages = chunk_end(s);
+  for (int c = 1; c < nchunk; ++c) {
+    const SeqChunk t = load_chunk(a, c, pages, wave == 0, lane);
+    zero_rows(a, t, wave, K::D, lane);
+    pages = chunk_end(t);
+  }
+  const int total = pages * hkv;
+  const int P = pages_per_wave(total, a.num_waves);
+  const int x0 = wave * P;
+  if (x0 >= total) return;
+  const int x1 = min(x0 + P, total);
+
+  // the sequence holding item x0: items of sequence b are
+  // [hkv * excl_b, hkv * (excl_b + np_b))
+  int hit;
+  while (true) {
+    const int lo = hkv * s.excl;
+    const uint64_t m = __ballot(s.np > 0 && lo <= x0 && x0 < lo + hkv * s.np);
+    if (m) {
+      hit = __builtin_ctzll(m);
+      break;
+    }
+    if (s.c + 1 >= nchunk) return;  // only if the lengths changed under the call
+    s = load_chunk(a, s.c + 1, chunk_end(s), false, lane);
+  }
+  // from here on only the lanes' context lengths of the current chunk are kept
+  int c = s.c;
+  int lens = s.L;
+  int b = 64 * c + hit;
+  int L = readlane(lens, hit);
+  int np = (L + kBlockSize - 1) / kBlockSize;
+  const int off = x0 - hkv * readlane(s.excl, hit);
+  int g = off / np;
+  int p = off - g * np;
+
+  K kind;
+  int x = x0;
+  while (true) {
+    const int n = min(np - p, x1 - x);
+    const int u = b * hkv + g;
+    if (p == 0 && lane == 0) {
+      // this wave holds the unit's first item: record which waves cover it
+      a.desc[u] = make_int2(wave, (x + np - 1) / P - wave + 1);
+    }
+    run_segment<K>(a, kind, b, g, p, n, L, wave + u, p == 0 && n == np, lane);
+    x += n;
+    if (x >= x1) break;
+    p = 0;
+    if (++g == hkv) {  // next sequence with pages
+      g = 0;
+      while (true) {
+        const uint64_t m = __ballot(lens > 0 && lane > hit);
+        if (m) {
+          hit = __builtin_ctzll(m);
+          break;
+        }
+        if (c + 1 >= nchunk) return;  // only if the lengths changed under the call
+        lens = load_chunk(a, ++c, 0, false, lane).L;
+        hit = -1;
+      }
+      b = 64 * c + hit;
+      L = readlane(lens, hit);
+      np = (L + kBlockSize - 1) / kBlockSize;
+    }
+  }
+}
+
+// The register budget per wave (waves per SIMD) sets how many pages a
+// buffer group holds; the host plans one resident round of waves for it.
+template <int D, bool QBF16>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
+    kInt8WavesPerSimd))) void decode_int8_kernel(DecodeArgs a) {
+  decode_wave<Int8Kind<D, QBF16, kInt8PageGroup>>(a);
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
+    k16WavesPerSimd))) void decode_16bit_kernel(DecodeArgs a) {
+  decode_wave<F16Kind<D, BF16, k16PageGroup>>(a);
+}
+
+// Combine the partials of a unit that spans several waves, per query head:
+// out = sum_i 2^(m_i - m) acc_i / sum_i 2^(m_i - m) l_i over the waves i that
+// cover the unit (m = max_i m_i), as recorded by the unit's first wave. One
+// workgroup per unit, one wave per query head (heads w, w + 4, ...); lane j
+// holds dims j, j + 64, and eight partials are loaded at a time.
+constexpr int kMergeWaves = 4;
+constexpr int kMergeBatch = 8;
+
+template <int D>
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(DecodeArgs a) {
+  constexpr int ND = D / 64;  // dims per lane
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int u = blockIdx.x;
+  const int b = u / a.num_kv_heads, g = u % a.num_kv_heads;
+  // the unit's record is this call's only if the sequence has pages (its
+  // first wave wrote it)
+  const int2 rec = a.desc[u];
+  const int L = a.ctx[b];
+  if (L <= 0 || rec.y <= 1) return;  // no pages, or written directly
+  const int n = rec.y;
+  const int64_t stride = static_cast<int64_t>(a.group) * (D + 2);
+  for (int hh = w; hh < a.group; hh += kMergeWaves) {
+    const float* base = a.ws + (static_cast<int64_t>(rec.x) + u) * stride + hh * (D + 2);
+    float mw = kMaxInit, lw = 0.f, acc[ND];
+#pragma unroll
+    for (int k = 0; k < ND; ++k) acc[k] = 0.f;
+    for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
+      float m[kMergeBatch], l[kMergeBatch], v[kMergeBatch][ND];
+#pragma unroll
+      for (int r = 0; r < kMergeBatch; ++r) {
+        // entries past n repeat the last partial's loads and are zeroed
+        const int i = i0 + r;
+        const float* pi = base + (i < n ? i : n - 1) * stride;
+        m[r] = i < n ? pi[D] : kMaxInit;
+        l[r] = i < n ? pi[D + 1] : 0.f;
+#pragma unroll
+        for (int k = 0; k < ND; ++k) v[r][k] = i < n ? pi[lane + 64 * k] : 0.f;
+      }
+      float mn = mw;
+#pragma unroll
+      for (int r = 0; r < kMergeBatch; ++r) mn = fmaxf(mn, m[r]);
+      const float c = exp2f(mw - mn);
+      lw *= c;
+#pragma unroll
+      for (int k = 0; k < ND; ++k) acc[k] *= c;
+#pragma unroll
+      for (int r = 0; r < kMergeBatch; ++r) {
+        const float e = exp2f(m[r] - mn);
+        lw += e * l[r];
+#pragma unroll
+        for (int k = 0; k < ND; ++k) acc[k] += e * v[r][k];
+      }
+      mw = mn;
+    }
+    // lw == 0: no attendable token in the unit
+    const int64_t o = b * a.out_ss + (g * a.group + hh) * a.out_sh;
+#pragma unroll
+    for (int k = 0; k < ND; ++k)
+      store_out(a.out, a.out_dtype, o + lane + 64 * k, lw > 0.f ? acc[k] / lw : 0.f);
+  }
 }
 
 template <int D>
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
-  if (a.max_splits == 1) return hipSuccess;
-  hipLaunchKernelGGL((merge_splits_kernel<D>), dim3(a.num_seqs * a.num_q_heads), dim3(D), 0, s,
-                     a);
+  if (a.max_ctx == 0) return hipSuccess;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(a.num_seqs * a.num_kv_heads),
+                     dim3(64 * kMergeWaves), 0, s, a);
   return hipGetLastError();
-}
-
-dim3 decode_grid(const DecodeArgs& a) {
-  return a.heads_fastest ? dim3(a.num_kv_heads, a.max_splits, a.num_seqs)
-                         : dim3(a.max_splits, a.num_kv_heads, a.num_seqs);
 }
 
 }  // namespace
 
 hipError_t launch_decode_int8(const DecodeArgs& a, int head_dim, bool q_bf16, hipStream_t s) {
-  const dim3 grid = decode_grid(a), block(64 * kWaves);
+  const dim3 grid(a.num_waves / kWaves), block(64 * kWaves);
   if (head_dim == 128) {
     if (q_bf16)
       hipLaunchKernelGGL((decode_int8_kernel<128, true>), grid, block, 0, s, a);
@@ -651,7 +817,7 @@ hipError_t launch_decode_int8(const DecodeArgs& a, int head_dim, bool q_bf16, hi
 
 hipError_t launch_decode_16bit(const DecodeArgs& a, int head_dim, bool kv_bf16,
                                hipStream_t s) {
-  const dim3 grid = decode_grid(a), block(64 * kWaves);
+  const dim3 grid(a.num_waves / kWaves), block(64 * kWaves);
   if (head_dim == 128) {
     if (kv_bf16)
       hipLaunchKernelGGL((decode_16bit_kernel<128, true>), grid, block, 0, s, a);

@@ -67,6 +67,12 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
 // Max / sum over the four lanes l, l^16, l^32, l^48 (same column of a 16x16
 // MFMA tile), with the gfx950 row-swap instructions (VALU only, no LDS round
 // trip): swapping a value with itself across 32-lane halves, then across

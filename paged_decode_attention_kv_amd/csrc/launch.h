@@ -12,7 +12,19 @@ namespace pdakv {
 constexpr int kBlockSize = 16;        // tokens per page
 constexpr int kMaxGroup = 16;         // query heads per KV head (one MFMA N tile)
 constexpr int kWaves = 4;             // waves per decode workgroup
-constexpr int kMaxPagesPerSplit = 128; // LDS block-table cache size
+constexpr int kMinPagesPerWave = 4;   // decode: fewest pages a busy wave gets
+#ifndef PDAKV_I8_W
+#define PDAKV_I8_W 2
+#define PDAKV_I8_G 2
+#define PDAKV_16_W 2
+#define PDAKV_16_G 2
+#endif
+constexpr int kInt8WavesPerSimd = PDAKV_I8_W;  // INT8 decode occupancy
+constexpr int kInt8PageGroup = PDAKV_I8_G;     // pages per register buffer
+constexpr int k16WavesPerSimd = PDAKV_16_W;    // 16-bit decode occupancy
+constexpr int k16PageGroup = PDAKV_16_G;
+constexpr int kCUs = 256;                      // MI355X compute units
+constexpr int kMaxPagesPerWave = 128; // decode: block ids a wave holds (2 per lane)
 
 struct WriteArgs {
   const void* k;
@@ -43,10 +55,10 @@ struct DecodeArgs {
   const int32_t* ctx;
   int num_seqs, num_q_heads, num_kv_heads, group, max_ctx;
   float scale_log2;  // sm_scale * log2(e): logits are kept in base 2
-  float* ws;         // split partials [B][Hq][max_splits][D + 2]
-  int pages_per_split, max_splits;
+  float* ws;         // partials [num_waves + B * Hkv][G][D + 2]
+  int2* desc;        // per (sequence, KV head): first covering wave, wave count
+  int num_waves;     // waves of the decode grid (a multiple of kWaves)
   int32_t* err;
-  int heads_fastest;  // grid x = KV head (the heads of one page run side by side)
 };
 
 // Each returns hipSuccess or the launch error. Arguments are validated by the

@@ -60,14 +60,32 @@ def test_page_bytes_agree_with_oracle(P):
 
 
 @pytest.mark.parametrize("B,hkv,L", [(1, 8, 256), (1, 8, 2048), (64, 8, 8193), (8, 8, 32768),
-                                     (32, 2, 4104), (8, 8, 8192), (3, 1, 0), (1, 32, 1)])
+                                     (32, 2, 4104), (8, 8, 8192), (3, 1, 0), (1, 32, 1),
+                                     (256, 8, 131072)])
 def test_decode_plan_is_consistent(P, B, hkv, L):
-    pps, n = P.pdakv_decode_plan(B, hkv, L)
-    pages = -(-L // 16)
-    assert 16 <= pps <= 128 and pps % 4 == 0
-    assert n >= 1 and (n - 1) * pps < max(pages, 1) <= n * pps
+    items = B * hkv * -(-L // 16)
+    resident = {P.KV_INT8_SYM: 2048, P.KV_16BIT: 2048}
+    for fmt in (P.KV_INT8_SYM, P.KV_16BIT):
+        waves, ppw = P.pdakv_decode_plan(fmt, B, hkv, L)
+        assert waves >= 4 and waves % 4 == 0
+        assert 4 <= ppw <= 128 and ppw == max(4, -(-items // waves))
+        # one resident round unless the items need more than 128 per wave;
+        # never more waves than 4-page shares (rounded to whole workgroups)
+        assert waves <= max(4, -(-max(resident[fmt], -(-items // 128)) // 4) * 4)
+        assert waves <= max(4, -(-(-(-items // 4)) // 4) * 4)
+    w8, _ = P.pdakv_decode_plan(P.KV_INT8_SYM, B, hkv, L)
     ws = P.pdakv_decode_workspace_bytes(B, 4 * hkv, hkv, 128, L)
-    assert ws == (0 if n == 1 else B * 4 * hkv * n * 130 * 4)
+    partials = -(-(w8 + B * hkv) * 4 * 130 * 4 // 16) * 16
+    assert ws == (0 if L == 0 else partials + B * hkv * 8)
+
+
+def test_decode_plan_rejects_bad_arguments(P):
+    assert P._lib.pdakv_decode_plan(7, 1, 8, 16, None, None) == P.ERR_INVALID_ARG
+    assert P._lib.pdakv_decode_plan(P.KV_INT8_SYM, -1, 8, 16, None, None) == P.ERR_INVALID_ARG
+    assert P._lib.pdakv_decode_plan(P.KV_INT8_SYM, 1, 0, 16, None, None) == P.ERR_INVALID_ARG
+    # more than 2^30 (sequence, KV head, page) items
+    assert (P._lib.pdakv_decode_plan(P.KV_INT8_SYM, 4096, 64, 1 << 17, None, None) ==
+            P.ERR_UNSUPPORTED)
 
 
 def test_capabilities_without_device(P):
@@ -114,7 +132,8 @@ def _decode_args(**kw):
     (dict(out=None), -1), (dict(pool=FAKE + 8), -1), (dict(sm=float("nan")), -1),
     (dict(oss=-1), -1), (dict(maxL=2048, bts=128), -4),
     (dict(maxL=2048, bts=128, ws=FAKE, wsb=16), -4), (dict(B=0), 0),
-    (dict(B=70000, maxL=16, bts=1), -2), (dict(nblk=0), -1), (dict(nblk=0, B=0), 0),
+    (dict(maxL=2048, bts=128, ws=FAKE + 8, wsb=1 << 30), -1),
+    (dict(B=65536, maxL=32784, bts=2050), -2), (dict(nblk=0), -1), (dict(nblk=0, B=0), 0),
 ])
 def test_decode_validation(P, fn, change, status):
     assert getattr(P._lib, fn)(*_decode_args(**change)) == status
