@@ -42,13 +42,18 @@ def parse():
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_int8_llama8b-batched-1k8k-b64_traffic.txt")
-DECODE_SOURCE = os.path.join(ROOT, "paged_decode_attention_kv_amd", "csrc", "decode.hip")
+# the sources that decide what the decode call reads and writes
+DECODE_SOURCES = [os.path.join(ROOT, "paged_decode_attention_kv_amd", "csrc", f)
+                  for f in ("decode.hip", "launch.h", "device_util.h", "abi.cpp")]
 
 
 def source_hash() -> str:
     import hashlib
-    with open(DECODE_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in DECODE_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

@@ -50,6 +50,18 @@ int64_t plan_waves(int kv_format, int num_seqs, int num_kv_heads, int max_contex
   return ceil_div(v, pdakv::kWaves) * pdakv::kWaves;
 }
 
+// Waves per merge workgroup: about one per kMergeBatch partials of the
+// longest unit, estimated with every sequence at max_context_len (the
+// device's split of the actual items gives at most a few more).
+int merge_waves(int num_seqs, int num_kv_heads, int max_context_len, int64_t waves) {
+  const int64_t items = item_bound(num_seqs, num_kv_heads, max_context_len);
+  const int64_t ppw = std::max<int64_t>(pdakv::kMinPagesPerWave, ceil_div(items, waves));
+  const int64_t parts = ceil_div(ceil_div(max_context_len, pdakv::kBlockSize), ppw) + 1;
+  int w = 1;
+  while (w < pdakv::kMaxMergeWaves && w * 8 < parts) w *= 2;
+  return w;
+}
+
 // Partial results region of the decode workspace (a multiple of 16 bytes):
 // [waves + units][G][D + 2] floats. The INT8 plan has the most waves; its
 // slots serve the 16-bit call too.
@@ -154,6 +166,7 @@ int decode_common(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, cons
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.num_waves = static_cast<int>(plan_waves(Int8 ? PDAKV_KV_INT8_SYM : PDAKV_KV_16BIT,
                                              num_seqs, num_kv_heads, max_context_len));
+  a.merge_waves = merge_waves(num_seqs, num_kv_heads, max_context_len, a.num_waves);
   a.ws = static_cast<float*>(workspace);
   a.desc = reinterpret_cast<int2*>(
       static_cast<uint8_t*>(workspace) +

@@ -727,18 +727,23 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
 // Combine the partials of a unit that spans several waves, per query head:
 // out = sum_i 2^(m_i - m) acc_i / sum_i 2^(m_i - m) l_i over the waves i that
 // cover the unit (m = max_i m_i), as recorded by the unit's first wave. One
-// workgroup per unit, one wave per query head (heads w, w + 4, ...); lane j
-// holds dims j, j + 64, and eight partials are loaded at a time.
-constexpr int kMergeWaves = 4;
+// workgroup per (unit, query head) with a.merge_waves waves: wave w folds
+// the partials w, w + waves, ... into a running (max, sum, accumulator),
+// kMergeBatch partials per round trip (lane j holds dims j, j + 64); the
+// waves then combine through LDS.
 constexpr int kMergeBatch = 8;
 
 template <int D>
-__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kMaxMergeWaves) void merge_kernel(DecodeArgs a) {
   constexpr int ND = D / 64;  // dims per lane
+  __shared__ float s_m[kMaxMergeWaves], s_l[kMaxMergeWaves], s_acc[kMaxMergeWaves][D];
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int u = blockIdx.x;
-  const int b = u / a.num_kv_heads, g = u % a.num_kv_heads;
+  const int nw = blockDim.x >> 6;
+  const int bh = blockIdx.x;
+  const int b = bh / a.num_q_heads, h = bh % a.num_q_heads;
+  const int g = h / a.group, hh = h % a.group;
+  const int u = b * a.num_kv_heads + g;
   // the unit's record is this call's only if the sequence has pages (its
   // first wave wrote it)
   const int2 rec = a.desc[u];
@@ -746,52 +751,72 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(DecodeArgs a) {
   if (L <= 0 || rec.y <= 1) return;  // no pages, or written directly
   const int n = rec.y;
   const int64_t stride = static_cast<int64_t>(a.group) * (D + 2);
-  for (int hh = w; hh < a.group; hh += kMergeWaves) {
-    const float* base = a.ws + (static_cast<int64_t>(rec.x) + u) * stride + hh * (D + 2);
-    float mw = kMaxInit, lw = 0.f, acc[ND];
+  const float* base = a.ws + (static_cast<int64_t>(rec.x) + u) * stride + hh * (D + 2);
+
+  float mw = kMaxInit, lw = 0.f, acc[ND];
 #pragma unroll
-    for (int k = 0; k < ND; ++k) acc[k] = 0.f;
-    for (int i0 = 0; i0 < n; i0 += kMergeBatch) {
-      float m[kMergeBatch], l[kMergeBatch], v[kMergeBatch][ND];
+  for (int k = 0; k < ND; ++k) acc[k] = 0.f;
+  for (int i0 = w; i0 < n; i0 += nw * kMergeBatch) {
+    float m[kMergeBatch], l[kMergeBatch], v[kMergeBatch][ND];
 #pragma unroll
-      for (int r = 0; r < kMergeBatch; ++r) {
-        // entries past n repeat the last partial's loads and are zeroed
-        const int i = i0 + r;
-        const float* pi = base + (i < n ? i : n - 1) * stride;
-        m[r] = i < n ? pi[D] : kMaxInit;
-        l[r] = i < n ? pi[D + 1] : 0.f;
+    for (int r = 0; r < kMergeBatch; ++r) {
+      // entries past n repeat the last partial's loads and are zeroed
+      const int i = i0 + r * nw;
+      const float* pi = base + (i < n ? i : n - 1) * stride;
+      m[r] = i < n ? pi[D] : kMaxInit;
+      l[r] = i < n ? pi[D + 1] : 0.f;
 #pragma unroll
-        for (int k = 0; k < ND; ++k) v[r][k] = i < n ? pi[lane + 64 * k] : 0.f;
-      }
-      float mn = mw;
-#pragma unroll
-      for (int r = 0; r < kMergeBatch; ++r) mn = fmaxf(mn, m[r]);
-      const float c = exp2f(mw - mn);
-      lw *= c;
-#pragma unroll
-      for (int k = 0; k < ND; ++k) acc[k] *= c;
-#pragma unroll
-      for (int r = 0; r < kMergeBatch; ++r) {
-        const float e = exp2f(m[r] - mn);
-        lw += e * l[r];
-#pragma unroll
-        for (int k = 0; k < ND; ++k) acc[k] += e * v[r][k];
-      }
-      mw = mn;
+      for (int k = 0; k < ND; ++k) v[r][k] = i < n ? pi[lane + 64 * k] : 0.f;
     }
+    float mn = mw;
+#pragma unroll
+    for (int r = 0; r < kMergeBatch; ++r) mn = fmaxf(mn, m[r]);
+    const float c = exp2f(mw - mn);
+    lw *= c;
+#pragma unroll
+    for (int k = 0; k < ND; ++k) acc[k] *= c;
+#pragma unroll
+    for (int r = 0; r < kMergeBatch; ++r) {
+      const float e = exp2f(m[r] - mn);
+      lw += e * l[r];
+#pragma unroll
+      for (int k = 0; k < ND; ++k) acc[k] += e * v[r][k];
+    }
+    mw = mn;
+  }
+  const int64_t o = b * a.out_ss + h * a.out_sh;
+  if (nw == 1) {
     // lw == 0: no attendable token in the unit
-    const int64_t o = b * a.out_ss + (g * a.group + hh) * a.out_sh;
 #pragma unroll
     for (int k = 0; k < ND; ++k)
       store_out(a.out, a.out_dtype, o + lane + 64 * k, lw > 0.f ? acc[k] / lw : 0.f);
+    return;
+  }
+  if (lane == 0) {
+    s_m[w] = mw;
+    s_l[w] = lw;
+  }
+#pragma unroll
+  for (int k = 0; k < ND; ++k) s_acc[w][lane + 64 * k] = acc[k];
+  __syncthreads();
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float ms = kMaxInit;
+    for (int j = 0; j < nw; ++j) ms = fmaxf(ms, s_m[j]);
+    float num = 0.f, den = 0.f;
+    for (int j = 0; j < nw; ++j) {
+      const float e = exp2f(s_m[j] - ms);
+      num += e * s_acc[j][d];
+      den += e * s_l[j];
+    }
+    store_out(a.out, a.out_dtype, o + d, den > 0.f ? num / den : 0.f);
   }
 }
 
 template <int D>
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
   if (a.max_ctx == 0) return hipSuccess;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(a.num_seqs * a.num_kv_heads),
-                     dim3(64 * kMergeWaves), 0, s, a);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(a.num_seqs * a.num_q_heads),
+                     dim3(64 * a.merge_waves), 0, s, a);
   return hipGetLastError();
 }
 

@@ -24,6 +24,7 @@ constexpr int kInt8PageGroup = PDAKV_I8_G;     // pages per register buffer
 constexpr int k16WavesPerSimd = PDAKV_16_W;    // 16-bit decode occupancy
 constexpr int k16PageGroup = PDAKV_16_G;
 constexpr int kCUs = 256;                      // MI355X compute units
+constexpr int kMaxMergeWaves = 8;              // merge: waves per (sequence, q head)
 constexpr int kMaxPagesPerWave = 128; // decode: block ids a wave holds (2 per lane)
 
 struct WriteArgs {
@@ -58,6 +59,7 @@ struct DecodeArgs {
   float* ws;         // partials [num_waves + B * Hkv][G][D + 2]
   int2* desc;        // per (sequence, KV head): first covering wave, wave count
   int num_waves;     // waves of the decode grid (a multiple of kWaves)
+  int merge_waves;   // waves per merge workgroup (1 .. kMaxMergeWaves)
   int32_t* err;
 };
 

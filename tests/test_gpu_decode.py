@@ -100,6 +100,24 @@ def test_edge_shapes(P, case, fmt_name):
 
 
 @pytest.mark.parametrize("fmt_name", ["int8", "16bit"])
+def test_long_single_sequence_many_partials(P, fmt_name):
+    """One 40000-token sequence on one KV head: the split gives every wave
+    four pages, so hundreds of partials meet in the merge (several rounds of
+    its LDS slots)."""
+    fmt = P.KV_INT8_SYM if fmt_name == "int8" else P.KV_16BIT
+    wl = build("long1", 77, [("prefill", [40000])], 16, 1, 64, "bf16", "logmag", shuffle=True)
+    waves, ppw = P.pdakv_decode_plan(fmt, 1, 1, 40000)
+    assert ppw == 4 and 2500 // ppw > 512
+    _say(f"long single sequence {fmt_name}: {waves} waves")
+    pool, _ = gpu_pool(P, wl, fmt)
+    out = gpu_decode(P, wl, pool, fmt)
+    want = oracle_decode(wl, oracle_pool(wl, fmt), fmt)
+    d = _maxdiff(out, want)
+    _say(f"  max abs diff {d:.3e}")
+    assert d <= MAX_ABS_TOL
+
+
+@pytest.mark.parametrize("fmt_name", ["int8", "16bit"])
 @pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16])
 def test_16bit_outputs_are_rounded_fp32_outputs(P, fmt_name, out_dtype):
     fmt = P.KV_INT8_SYM if fmt_name == "int8" else P.KV_16BIT
