@@ -167,6 +167,13 @@ int decode_common(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, cons
   a.num_waves = static_cast<int>(plan_waves(Int8 ? PDAKV_KV_INT8_SYM : PDAKV_KV_16BIT,
                                              num_seqs, num_kv_heads, max_context_len));
   a.merge_waves = merge_waves(num_seqs, num_kv_heads, max_context_len, a.num_waves);
+  {
+    // LDS staging per decode pass and segment: the unit's q rows (16-bit) and
+    // its result (accumulator, max, sum per query head)
+    const int per_seg = a.group * head_dim * 2 + a.group * (head_dim + 2) * 4;
+    a.seg_cap = std::max(1, std::min(64, pdakv::kLdsPerWave / per_seg));
+    a.lds_wave_bytes = (a.seg_cap * per_seg + 15) / 16 * 16;
+  }
   a.ws = static_cast<float*>(workspace);
   a.desc = reinterpret_cast<int2*>(
       static_cast<uint8_t*>(workspace) +

@@ -194,15 +194,15 @@ __device__ __forceinline__ u2_t i8x4_to_f16x4_perm(uint32_t w) {
 }
 
 // q fragments as fp16 scaled by 2^kq so that max|q| of the head lies in
-// [2^14, 2^15); fragment j, slot r holds dim qdim0(j) + r. Lanes of padding
-// heads (hvalid false) read head h_load and use zeros. Returns the factor that
-// turns the MFMA dot products into base-2 logits.
-template <int NJ, bool QBF16, typename DimFn>
-__device__ __forceinline__ float load_q_scaled(const DecodeArgs& a, int b, int h_load,
-                                               bool hvalid, DimFn qdim0, h8_t* qf) {
+// [2^14, 2^15); fragment j holds the eight 16-bit values chunk(j). Lanes of
+// padding heads (hvalid false) use zeros. Returns the factor that turns the
+// MFMA dot products into base-2 logits.
+template <int NJ, bool QBF16, typename ChunkFn>
+__device__ __forceinline__ float load_q_scaled(const DecodeArgs& a, bool hvalid, ChunkFn chunk,
+                                               h8_t* qf) {
   u4_t raw[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) raw[j] = q_chunk8(a, b, h_load, qdim0(j));
+  for (int j = 0; j < NJ; ++j) raw[j] = chunk(j);
   float qv[NJ * 8];
   float qmax = 0.f;
 #pragma unroll
@@ -351,11 +351,16 @@ struct Int8Kind {
   h8_t qf[D / 32];
   float qscale;
 
-  __device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int g, int i16, int kb,
-                                         bool hvalid) {
+  // q of head i16 from the unit's rows in LDS ([G][D] 16-bit values)
+  __device__ __forceinline__ void load_q(const DecodeArgs& a, const uint16_t* q_rows, int i16,
+                                         int kb, bool hvalid) {
+    const uint16_t* row = q_rows + (hvalid ? i16 : 0) * D;
     qscale = load_q_scaled<D / 32, QBF16>(
-        a, b, g * a.group + (hvalid ? i16 : 0), hvalid,
-        [kb](int j) { return 64 * (j / 2) + 16 * kb + 8 * (j % 2); }, qf);
+        a, hvalid,
+        [row, kb](int j) {
+          return *reinterpret_cast<const u4_t*>(row + 64 * (j / 2) + 16 * kb + 8 * (j % 2));
+        },
+        qf);
   }
   static __device__ __forceinline__ void load(Page& pg, const uint8_t* hp, int i16, int kb) {
     load_int8_page<D>(pg, hp, i16, kb);
@@ -504,11 +509,11 @@ struct F16Kind {
   u4_t qf[D / 32];  // fragment j: dims 32*j + 8*kb + (0..7)
   float scale_log2;
 
-  __device__ __forceinline__ void load_q(const DecodeArgs& a, int b, int g, int i16, int kb,
-                                         bool hvalid) {
-    const int h_load = g * a.group + (hvalid ? i16 : 0);
+  __device__ __forceinline__ void load_q(const DecodeArgs& a, const uint16_t* q_rows, int i16,
+                                         int kb, bool hvalid) {
+    const uint16_t* row = q_rows + (hvalid ? i16 : 0) * D;
 #pragma unroll
-    for (int j = 0; j < D / 32; ++j) qf[j] = q_chunk8(a, b, h_load, 32 * j + 8 * kb);
+    for (int j = 0; j < D / 32; ++j) qf[j] = *reinterpret_cast<const u4_t*>(row + 32 * j + 8 * kb);
 #pragma unroll
     for (int j = 0; j < D / 32; ++j)
       if (!hvalid) qf[j] = u4_t{0u, 0u, 0u, 0u};
@@ -530,50 +535,141 @@ struct F16Kind {
 // Decode loop
 // ---------------------------------------------------------------------------
 
-// Final rows (whole unit) or the partial of slot `slot`: [D] accumulator,
-// then the running max and the sum. A unit without any attendable token (all
-// its pages flagged) gets zero rows.
-template <class K>
-__device__ __forceinline__ void write_result(const DecodeArgs& a, SoftmaxState<K::D / 16>& st,
-                                             int b, int g, int slot, bool whole, int i16,
-                                             int kb) {
-  constexpr int D = K::D, ND = D / 16;
-  const float l = col_sum(st.l);
-  if (i16 >= a.group) return;
-  const int h = g * a.group + i16;
-  if (whole) {
-    const int64_t o = b * a.out_ss + h * a.out_sh;
-#pragma unroll
-    for (int k = 0; k < ND; ++k)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        store_out(a.out, a.out_dtype, o + K::acc_dim(k, j, kb), l > 0.f ? st.acc[k][j] / l : 0.f);
-  } else {
-    float* pp = a.ws + (static_cast<int64_t>(slot) * a.group + i16) * (D + 2);
-#pragma unroll
-    for (int k = 0; k < ND; ++k)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pp[K::acc_dim(k, j, kb)] = st.acc[k][j];
-    if (kb == 0) {
-      pp[D] = st.m;
-      pp[D + 1] = l;
-    }
+// Per-wave LDS staging of one pass: the q rows of each segment's unit
+// ([G][D] 16-bit values) and each segment's result ([G][D + 2] floats:
+// accumulator, running max, sum). Sized on the host (a.seg_cap segments).
+struct PassLds {
+  uint16_t* q;   // [seg_cap][G][D]
+  float* res;    // [seg_cap][G][D + 2]
+};
+
+// Copy the q rows of unit (b, g) into LDS; 16-byte chunks dealt to the lanes.
+template <int D>
+__device__ __forceinline__ void stage_q(const DecodeArgs& a, int b, int g, uint16_t* dst,
+                                        int lane) {
+  const int chunks = a.group * D / 8;
+  for (int c = lane; c < chunks; c += 64) {
+    const int hh = c / (D / 8), d0 = (c % (D / 8)) * 8;
+    *reinterpret_cast<u4_t*>(dst + hh * D + d0) = q_chunk8(a, b, g * a.group + hh, d0);
   }
 }
 
-// Pages p .. p+n-1 (n <= kMaxPagesPerWave) of KV head g of sequence b.
+// Leave a segment's softmax state in LDS: [G][D + 2].
 template <class K>
-__device__ __forceinline__ void run_segment(const DecodeArgs& a, K& kind, int b, int g, int p,
-                                            int n, int L, int slot, bool whole, int lane) {
-  constexpr int ND = K::D / 16;
-  const int i16 = lane & 15, kb = lane >> 4;
-  kind.load_q(a, b, g, i16, kb, i16 < a.group);
+__device__ __forceinline__ void stash_result(const DecodeArgs& a, SoftmaxState<K::D / 16>& st,
+                                             float* res, int i16, int kb) {
+  constexpr int D = K::D, ND = D / 16;
+  const float l = col_sum(st.l);
+  if (i16 >= a.group) return;
+  float* r = res + i16 * (D + 2);
+#pragma unroll
+  for (int k = 0; k < ND; ++k)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[K::acc_dim(k, j, kb)] = st.acc[k][j];
+  if (kb == 0) {
+    r[D] = st.m;
+    r[D + 1] = l;
+  }
+}
 
-  // block ids: lane i holds pages p + i and p + 64 + i; out-of-range ids are
-  // flagged and become -1 (the page is skipped)
-  const int32_t* row = a.bt + static_cast<int64_t>(b) * a.bt_stride + p;
-  int blk0 = lane < n ? row[lane] : 0;
-  int blk1 = lane + 64 < n ? row[lane + 64] : 0;
+// Write a stashed result: the output rows when the segment covers its whole
+// unit (zero rows when no token was attendable), else the partial of `slot`.
+template <int D>
+__device__ __forceinline__ void write_result(const DecodeArgs& a, const float* res, int b, int g,
+                                             int slot, bool whole, int lane) {
+  if (whole) {
+    for (int e = lane; e < a.group * D; e += 64) {
+      const int hh = e / D, d = e % D;
+      const float l = res[hh * (D + 2) + D + 1];
+      const float v = l > 0.f ? res[hh * (D + 2) + d] / l : 0.f;
+      store_out(a.out, a.out_dtype, b * a.out_ss + (g * a.group + hh) * a.out_sh + d, v);
+    }
+  } else {
+    float* dst = a.ws + static_cast<int64_t>(slot) * a.group * (D + 2);
+    for (int e = lane; e < a.group * (D + 2); e += 64) dst[e] = res[e];
+  }
+}
+
+// Walks the units of a wave's item range: (b, g, p) is the current position,
+// np and L the current sequence's page count and length; lens holds the
+// context lengths of sequences 64*c .. 64*c+63 (one per lane), hit the lane of b.
+struct Cursor {
+  int b, g, p, np, L, c, lens, hit;
+};
+
+// Move to the first page of the next unit with pages; false if the lengths
+// changed under the call (no such unit).
+__device__ __forceinline__ bool next_unit(const DecodeArgs& a, Cursor& cu, int nchunk,
+                                          int lane) {
+  cu.p = 0;
+  if (++cu.g < a.num_kv_heads) return true;
+  cu.g = 0;
+  while (true) {
+    const uint64_t m = __ballot(cu.lens > 0 && lane > cu.hit);
+    if (m) {
+      cu.hit = __builtin_ctzll(m);
+      break;
+    }
+    if (cu.c + 1 >= nchunk) return false;
+    cu.lens = load_chunk(a, ++cu.c, 0, false, lane).L;
+    cu.hit = -1;
+  }
+  cu.b = 64 * cu.c + cu.hit;
+  cu.L = readlane(cu.lens, cu.hit);
+  cu.np = (cu.L + kBlockSize - 1) / kBlockSize;
+  return true;
+}
+
+// One pass over up to a.seg_cap segments (and up to 128 items) of the wave's
+// range starting at item x: plan the segments, stage every segment's q rows in
+// LDS and every item's block id in registers, stream all the pass's pages
+// through one pipeline (segment switches inside it touch only registers and
+// LDS, so the page loads in flight are never waited for early), then write
+// the stashed results. Returns the number of items done (0: lengths changed).
+template <class K>
+__device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu, int x, int x1,
+                                        int P, int wave, int nchunk, const PassLds& lds,
+                                        int lane) {
+  constexpr int D = K::D, ND = D / 16;
+  const int i16 = lane & 15, kb = lane >> 4;
+  const int hkv = a.num_kv_heads;
+
+  // plan: lane s keeps segment s's unit, first page, first item, length, L
+  int s_unit = 0, s_p = 0, s_start = 0, s_n = 0, s_L = 0, s_whole = 0;
+  int ns = 0, items = 0;
+  while (true) {
+    const int n = min(min(cu.np - cu.p, x1 - (x + items)), kMaxPagesPerWave - items);
+    const int u = cu.b * hkv + cu.g;
+    if (cu.p == 0 && lane == 0) {
+      // this wave holds the unit's first item: record which waves cover it
+      a.desc[u] = make_int2(wave, (x + items + cu.np - 1) / P - wave + 1);
+    }
+    if (lane == ns) {
+      s_unit = u;
+      s_p = cu.p;
+      s_start = items;
+      s_n = n;
+      s_L = cu.L;
+      s_whole = cu.p == 0 && n == cu.np;
+    }
+    stage_q<D>(a, cu.b, cu.g, lds.q + ns * a.group * D, lane);
+    ++ns;
+    items += n;
+    cu.p += n;
+    if (cu.p == cu.np && x + items < x1 && !next_unit(a, cu, nchunk, lane)) return 0;
+    if (x + items >= x1 || ns == a.seg_cap || items == kMaxPagesPerWave) break;
+  }
+
+  // block ids: lane i holds items i and 64 + i; out-of-range ids are flagged
+  // and become -1 (the page is masked)
+  int blk0 = 0, blk1 = 0;
+  for (int s = 0; s < ns; ++s) {
+    const int st = readlane(s_start, s), n = readlane(s_n, s);
+    const int u = readlane(s_unit, s);
+    const int32_t* row = a.bt + static_cast<int64_t>(u / hkv) * a.bt_stride + readlane(s_p, s);
+    if (lane >= st && lane < st + n) blk0 = row[lane - st];
+    if (lane + 64 >= st && lane + 64 < st + n) blk1 = row[lane + 64 - st];
+  }
   if (blk0 < 0 || blk0 >= a.num_blocks) {
     raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
     blk0 = -1;
@@ -582,62 +678,106 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, K& kind, int b,
     raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
     blk1 = -1;
   }
-  const uint8_t* base = a.pool + static_cast<int64_t>(g) * K::kHeadBytes;
   auto block_of = [&](int i) { return i < 64 ? readlane(blk0, i) : readlane(blk1, i - 64); };
-  // Missing pages read page 0 (it exists) with all tokens masked, so every
-  // iteration issues the same loads and consumes them, and the compiler waits
-  // for the current page only.
-  auto page_at = [&](int blk) { return base + (blk >= 0 ? blk : 0) * a.page_bytes; };
-  auto limit = [&](int blk, int page_tok) { return blk >= 0 ? L : page_tok; };
+  auto page_at = [&](int g, int blk) {
+    return a.pool + static_cast<int64_t>(g) * K::kHeadBytes +
+           static_cast<int64_t>(blk >= 0 ? blk : 0) * a.page_bytes;
+  };
+
+  // current segment: its unit's KV head, first page's token, first item,
+  // end item and length
+  int cs = 0, c_g = 0, c_tok = 0, c_start = 0, c_end = 0, c_L = 0;
+  auto enter = [&](int sidx) {
+    cs = sidx;
+    c_g = readlane(s_unit, sidx) % hkv;
+    c_tok = readlane(s_p, sidx) * kBlockSize;
+    c_start = readlane(s_start, sidx);
+    c_end = c_start + readlane(s_n, sidx);
+    c_L = readlane(s_L, sidx);
+  };
+  enter(0);
+  // the item of the pipeline's next load: its KV head moves with the segments
+  int f_s = 0, f_end = c_end, f_g = c_g;
+  auto head_of = [&](int i) {
+    while (i >= f_end && f_s + 1 < ns) {
+      ++f_s;
+      f_g = readlane(s_unit, f_s) % hkv;
+      f_end = readlane(s_start, f_s) + readlane(s_n, f_s);
+    }
+    return f_g;
+  };
 
   SoftmaxState<ND> st;
   softmax_init(st);
-  // Two register buffers of G pages each (a "group"), each refilled right
-  // after its pages are consumed: while one group is computed the next is in
-  // flight. Pages past the end of the segment load the last page again (a
-  // cache hit) and are fully masked, so every refill issues the same loads.
+  kind.load_q(a, lds.q, i16, kb, i16 < a.group);
+
+  // Two register buffers of G pages each, each refilled right after its pages
+  // are consumed; past the pass's last item the last page is loaded again (a
+  // cache hit) so that every refill issues the same loads.
   constexpr int G = K::kGroup;
   typename K::Page ga[G], gb[G];
-  int la[G], lb[G];  // mask limits
-  const int tok = p * kBlockSize;
-  auto fill = [&](typename K::Page* grp, int* lim, int first) {
+  int ba[G], bb[G];
+  auto fill = [&](typename K::Page* grp, int* blk, int first) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
-      const int q = first + j;
-      const int bq = block_of(q < n ? q : n - 1);
-      const int tq = tok + q * kBlockSize;
-      lim[j] = q < n ? limit(bq, tq) : tq;
-      K::load(grp[j], page_at(bq), i16, kb);
+      const int q = min(first + j, items - 1);
+      blk[j] = block_of(q);
+      K::load(grp[j], page_at(head_of(q), blk[j]), i16, kb);
     }
   };
-  auto consume = [&](const typename K::Page* grp, const int* lim, int first) {
+  // consume items first.. of a group; false once the pass's items are done
+  auto consume = [&](const typename K::Page* grp, const int* blk, int first) {
 #pragma unroll
-    for (int j = 0; j < G; ++j) kind.step(grp[j], tok + (first + j) * kBlockSize, lim[j], st);
+    for (int j = 0; j < G; ++j) {
+      const int i = first + j;
+      if (i >= items) return false;
+      if (i == c_end) {  // next segment: only registers and LDS are touched
+        stash_result<K>(a, st, lds.res + cs * a.group * (D + 2), i16, kb);
+        enter(cs + 1);
+        softmax_init(st);
+        kind.load_q(a, lds.q + cs * a.group * D, i16, kb, i16 < a.group);
+      }
+      const int t = c_tok + (i - c_start) * kBlockSize;
+      kind.step(grp[j], t, blk[j] >= 0 ? c_L : t, st);
+    }
+    return true;
   };
-  fill(ga, la, 0);
+  fill(ga, ba, 0);
   __builtin_amdgcn_sched_barrier(0);  // keep the groups' loads in order
-  fill(gb, lb, G);
+  fill(gb, bb, G);
   __builtin_amdgcn_sched_barrier(0);
   for (int i = 0;; i += 2 * G) {
-    consume(ga, la, i);
-    if (i + G >= n) break;
+    if (!consume(ga, ba, i)) break;
     __builtin_amdgcn_sched_barrier(0);
-    fill(ga, la, i + 2 * G);
+    fill(ga, ba, i + 2 * G);
     __builtin_amdgcn_sched_barrier(0);
-    consume(gb, lb, i + G);
+    const bool more = consume(gb, bb, i + G);
     __builtin_amdgcn_sched_barrier(0);
-    fill(gb, lb, i + 3 * G);
+    fill(gb, bb, i + 3 * G);
     __builtin_amdgcn_sched_barrier(0);
-    if (i + 2 * G >= n) break;
+    if (!more || i + 2 * G >= items) break;
   }
-  write_result<K>(a, st, b, g, slot, whole, i16, kb);
+  stash_result<K>(a, st, lds.res + cs * a.group * (D + 2), i16, kb);
+
+  for (int s = 0; s < ns; ++s) {
+    const int u = readlane(s_unit, s);
+    write_result<D>(a, lds.res + s * a.group * (D + 2), u / hkv, u % hkv, wave + u,
+                    readlane(s_whole, s) != 0, lane);
+  }
+  return items;
 }
 
 template <class K>
 __device__ __forceinline__ void decode_wave(const DecodeArgs& a) {
+  extern __shared__ __align__(16) uint8_t smem[];
   const int lane = lane_id();
-  const int wave = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = blockIdx.x * kWaves + wid;
   const int hkv = a.num_kv_heads;
+  PassLds lds;
+  lds.q = reinterpret_cast<uint16_t*>(smem + wid * a.lds_wave_bytes);
+  lds.res = reinterpret_cast<float*>(smem + wid * a.lds_wave_bytes +
+                                     a.seg_cap * a.group * K::D * 2);
 
   // total pages; zero rows of empty sequences
   const int nchunk = (a.num_seqs + 63) / 64;
@@ -668,45 +808,22 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs& a) {
     if (s.c + 1 >= nchunk) return;  // only if the lengths changed under the call
     s = load_chunk(a, s.c + 1, chunk_end(s), false, lane);
   }
-  // from here on only the lanes' context lengths of the current chunk are kept
-  int c = s.c;
-  int lens = s.L;
-  int b = 64 * c + hit;
-  int L = readlane(lens, hit);
-  int np = (L + kBlockSize - 1) / kBlockSize;
+  Cursor cu;
+  cu.c = s.c;
+  cu.lens = s.L;
+  cu.hit = hit;
+  cu.b = 64 * s.c + hit;
+  cu.L = readlane(s.L, hit);
+  cu.np = (cu.L + kBlockSize - 1) / kBlockSize;
   const int off = x0 - hkv * readlane(s.excl, hit);
-  int g = off / np;
-  int p = off - g * np;
+  cu.g = off / cu.np;
+  cu.p = off - cu.g * cu.np;
 
   K kind;
-  int x = x0;
-  while (true) {
-    const int n = min(np - p, x1 - x);
-    const int u = b * hkv + g;
-    if (p == 0 && lane == 0) {
-      // this wave holds the unit's first item: record which waves cover it
-      a.desc[u] = make_int2(wave, (x + np - 1) / P - wave + 1);
-    }
-    run_segment<K>(a, kind, b, g, p, n, L, wave + u, p == 0 && n == np, lane);
-    x += n;
-    if (x >= x1) break;
-    p = 0;
-    if (++g == hkv) {  // next sequence with pages
-      g = 0;
-      while (true) {
-        const uint64_t m = __ballot(lens > 0 && lane > hit);
-        if (m) {
-          hit = __builtin_ctzll(m);
-          break;
-        }
-        if (c + 1 >= nchunk) return;  // only if the lengths changed under the call
-        lens = load_chunk(a, ++c, 0, false, lane).L;
-        hit = -1;
-      }
-      b = 64 * c + hit;
-      L = readlane(lens, hit);
-      np = (L + kBlockSize - 1) / kBlockSize;
-    }
+  for (int x = x0; x < x1;) {
+    const int done = run_pass<K>(a, kind, cu, x, x1, P, wave, nchunk, lds, lane);
+    if (done == 0) return;
+    x += done;
   }
 }
 
@@ -824,16 +941,17 @@ hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_int8(const DecodeArgs& a, int head_dim, bool q_bf16, hipStream_t s) {
   const dim3 grid(a.num_waves / kWaves), block(64 * kWaves);
+  const size_t lds = static_cast<size_t>(kWaves) * a.lds_wave_bytes;
   if (head_dim == 128) {
     if (q_bf16)
-      hipLaunchKernelGGL((decode_int8_kernel<128, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_int8_kernel<128, true>), grid, block, lds, s, a);
     else
-      hipLaunchKernelGGL((decode_int8_kernel<128, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_int8_kernel<128, false>), grid, block, lds, s, a);
   } else {
     if (q_bf16)
-      hipLaunchKernelGGL((decode_int8_kernel<64, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_int8_kernel<64, true>), grid, block, lds, s, a);
     else
-      hipLaunchKernelGGL((decode_int8_kernel<64, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_int8_kernel<64, false>), grid, block, lds, s, a);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -843,16 +961,17 @@ hipError_t launch_decode_int8(const DecodeArgs& a, int head_dim, bool q_bf16, hi
 hipError_t launch_decode_16bit(const DecodeArgs& a, int head_dim, bool kv_bf16,
                                hipStream_t s) {
   const dim3 grid(a.num_waves / kWaves), block(64 * kWaves);
+  const size_t lds = static_cast<size_t>(kWaves) * a.lds_wave_bytes;
   if (head_dim == 128) {
     if (kv_bf16)
-      hipLaunchKernelGGL((decode_16bit_kernel<128, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_16bit_kernel<128, true>), grid, block, lds, s, a);
     else
-      hipLaunchKernelGGL((decode_16bit_kernel<128, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_16bit_kernel<128, false>), grid, block, lds, s, a);
   } else {
     if (kv_bf16)
-      hipLaunchKernelGGL((decode_16bit_kernel<64, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_16bit_kernel<64, true>), grid, block, lds, s, a);
     else
-      hipLaunchKernelGGL((decode_16bit_kernel<64, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((decode_16bit_kernel<64, false>), grid, block, lds, s, a);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

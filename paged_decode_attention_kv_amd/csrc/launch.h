@@ -25,6 +25,7 @@ constexpr int k16WavesPerSimd = PDAKV_16_W;    // 16-bit decode occupancy
 constexpr int k16PageGroup = PDAKV_16_G;
 constexpr int kCUs = 256;                      // MI355X compute units
 constexpr int kMaxMergeWaves = 8;              // merge: waves per (sequence, q head)
+constexpr int kLdsPerWave = 16384;             // decode: LDS staging budget per wave
 constexpr int kMaxPagesPerWave = 128; // decode: block ids a wave holds (2 per lane)
 
 struct WriteArgs {
@@ -60,6 +61,8 @@ struct DecodeArgs {
   int2* desc;        // per (sequence, KV head): first covering wave, wave count
   int num_waves;     // waves of the decode grid (a multiple of kWaves)
   int merge_waves;   // waves per merge workgroup (1 .. kMaxMergeWaves)
+  int seg_cap;       // decode: segments staged in LDS per pass
+  int lds_wave_bytes;  // decode: LDS per wave (q rows + results of seg_cap segments)
   int32_t* err;
 };
 
