@@ -115,6 +115,8 @@ int check_decode(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, const
   // a non-empty context needs a pool with at least one page (the kernels read
   // page 0 in place of a missing page)
   if (max_context_len > 0 && (!kv_pool || num_blocks < 1)) return PDAKV_ERR_INVALID_ARG;
+  // head blocks are indexed as block * num_kv_heads + head in int32
+  if (num_blocks * num_kv_heads > INT32_MAX) return PDAKV_ERR_UNSUPPORTED;
   if (kv_pool && !aligned16(kv_pool)) return PDAKV_ERR_INVALID_ARG;
   const size_t need = pdakv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
                                                    head_dim, max_context_len);

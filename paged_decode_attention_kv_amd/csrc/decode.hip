@@ -652,7 +652,6 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
       s_L = cu.L;
       s_whole = cu.p == 0 && n == cu.np;
     }
-    stage_q<D>(a, cu.b, cu.g, lds.q + ns * a.group * D, lane);
     ++ns;
     items += n;
     cu.p += n;
@@ -660,15 +659,27 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     if (x + items >= x1 || ns == a.seg_cap || items == kMaxPagesPerWave) break;
   }
 
-  // block ids: lane i holds items i and 64 + i; out-of-range ids are flagged
-  // and become -1 (the page is masked)
-  int blk0 = 0, blk1 = 0;
+  // head blocks of the items: lane i holds items i and 64 + i as
+  // block * hkv + KV head (the head block's index in the pool); out-of-range
+  // block ids are flagged and become -1 (the page is masked)
+  int blk0 = 0, blk1 = 0, g0 = 0, g1 = 0;
   for (int s = 0; s < ns; ++s) {
     const int st = readlane(s_start, s), n = readlane(s_n, s);
     const int u = readlane(s_unit, s);
     const int32_t* row = a.bt + static_cast<int64_t>(u / hkv) * a.bt_stride + readlane(s_p, s);
-    if (lane >= st && lane < st + n) blk0 = row[lane - st];
-    if (lane + 64 >= st && lane + 64 < st + n) blk1 = row[lane + 64 - st];
+    if (lane >= st && lane < st + n) {
+      blk0 = row[lane - st];
+      g0 = u % hkv;
+    }
+    if (lane + 64 >= st && lane + 64 < st + n) {
+      blk1 = row[lane + 64 - st];
+      g1 = u % hkv;
+    }
+  }
+  // the q rows go to LDS while the block ids are in flight
+  for (int s = 0; s < ns; ++s) {
+    const int u = readlane(s_unit, s);
+    stage_q<D>(a, u / hkv, u % hkv, lds.q + s * a.group * D, lane);
   }
   if (blk0 < 0 || blk0 >= a.num_blocks) {
     raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
@@ -678,34 +689,28 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
     blk1 = -1;
   }
-  auto block_of = [&](int i) { return i < 64 ? readlane(blk0, i) : readlane(blk1, i - 64); };
-  auto page_at = [&](int g, int blk) {
-    return a.pool + static_cast<int64_t>(g) * K::kHeadBytes +
-           static_cast<int64_t>(blk >= 0 ? blk : 0) * a.page_bytes;
+  const int hb0 = blk0 >= 0 ? blk0 * hkv + g0 : -1;
+  const int hb1 = blk1 >= 0 ? blk1 * hkv + g1 : -1;
+  auto block_of = [&](int i) { return i < 64 ? readlane(hb0, i) : readlane(hb1, i - 64); };
+  // a missing page reads head block 0 (it exists) and is fully masked
+  // (hb is the same in every lane; saying so keeps the address in scalar
+  // registers, as the buffer resource requires)
+  auto page_at = [&](int hb) {
+    hb = __builtin_amdgcn_readfirstlane(hb);
+    return a.pool + static_cast<int64_t>(hb >= 0 ? hb : 0) * K::kHeadBytes;
   };
 
   // current segment: its unit's KV head, first page's token, first item,
   // end item and length
-  int cs = 0, c_g = 0, c_tok = 0, c_start = 0, c_end = 0, c_L = 0;
+  int cs = 0, c_tok = 0, c_start = 0, c_end = 0, c_L = 0;
   auto enter = [&](int sidx) {
     cs = sidx;
-    c_g = readlane(s_unit, sidx) % hkv;
     c_tok = readlane(s_p, sidx) * kBlockSize;
     c_start = readlane(s_start, sidx);
     c_end = c_start + readlane(s_n, sidx);
     c_L = readlane(s_L, sidx);
   };
   enter(0);
-  // the item of the pipeline's next load: its KV head moves with the segments
-  int f_s = 0, f_end = c_end, f_g = c_g;
-  auto head_of = [&](int i) {
-    while (i >= f_end && f_s + 1 < ns) {
-      ++f_s;
-      f_g = readlane(s_unit, f_s) % hkv;
-      f_end = readlane(s_start, f_s) + readlane(s_n, f_s);
-    }
-    return f_g;
-  };
 
   SoftmaxState<ND> st;
   softmax_init(st);
@@ -722,7 +727,7 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     for (int j = 0; j < G; ++j) {
       const int q = min(first + j, items - 1);
       blk[j] = block_of(q);
-      K::load(grp[j], page_at(head_of(q), blk[j]), i16, kb);
+      K::load(grp[j], page_at(blk[j]), i16, kb);
     }
   };
   // consume items first.. of a group; false once the pass's items are done
