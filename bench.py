@@ -41,10 +41,11 @@ def parse():
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_int8_llama8b-batched-1k8k-b64_traffic.txt")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
+                               "decode_int8_append_llama8b-batched-1k8k-b64_traffic.txt")
 # the sources that decide what the decode call reads and writes
 DECODE_SOURCES = [os.path.join(ROOT, "paged_decode_attention_kv_amd", "csrc", f)
-                  for f in ("decode.hip", "launch.h", "device_util.h", "abi.cpp")]
+                  for f in ("decode.hip", "launch.h", "device_util.h", "quant_row.h", "abi.cpp")]
 
 
 def source_hash() -> str:
@@ -85,10 +86,11 @@ def decode_bytes(wl, fmt_int8: bool) -> int:
     return total
 
 
-def write_bytes(T: int, hkv: int, d: int, fmt_int8: bool) -> int:
-    """Read 16-bit K and V, write codes + scales (or 16-bit values), read slots."""
-    written = T * hkv * (2 * d + 4) if fmt_int8 else T * hkv * 4 * d
-    return T * 4 * hkv * d + written + T * 4
+def append_bytes(wl, fmt_int8: bool) -> int:
+    """Algorithmic bytes of the fused append: read each sequence's new 16-bit
+    K and V rows, write their codes + scales (or 16-bit values)."""
+    return wl.num_seqs * wl.num_kv_heads * (4 * wl.head_dim +
+                                            (2 * wl.head_dim + 4 if fmt_int8 else 4 * wl.head_dim))
 
 
 def main():
@@ -140,6 +142,8 @@ def main():
         pools = [pool] + [pool.clone() for _ in range(nrep - 1)]
         st = dict(fmt_int8=fmt_int8, write=write, pools=pools,
                   decode=P.paged_attn_decode_int8 if fmt_int8 else P.paged_attn_decode_fp16,
+                  fused=(P.paged_attn_decode_int8_append if fmt_int8
+                         else P.paged_attn_decode_fp16_append),
                   q=to_dev(wl.q), bt=dev_i32(wl.block_tables), ctx=dev_i32(wl.context_lens),
                   out=torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim),
                                   dtype=torch.float32, device="cuda"),
@@ -151,20 +155,28 @@ def main():
         torch.cuda.synchronize()
         return st
 
-    def run(wl, st, steps, warmup, with_write):
+    def run(wl, st, steps, warmup, mode):
+        """mode "decode": decode calls only; "unfused": write the appended
+        tokens, then decode (events around the decode call); "fused": the
+        fused append + decode call (events around it)."""
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
         pools = st["pools"]
 
         def one(i, timed):
             pool = pools[i % len(pools)]
-            if with_write:
+            if mode == "unfused":
                 st["write"](st["ak"], st["av"], st["aslots"], pool, wl.num_blocks, stream=stream)
             if timed:
                 ev[i][0].record(stream)
-            st["decode"](st["out"], st["q"], pool, wl.num_blocks, st["bt"], st["ctx"],
-                         wl.num_kv_heads, wl.max_context_len, wl.sm_scale, st["ws"],
-                         stream=stream)
+            if mode == "fused":
+                st["fused"](st["out"], st["q"], st["ak"], st["av"], pool, wl.num_blocks, st["bt"],
+                            st["ctx"], wl.num_kv_heads, wl.max_context_len, wl.sm_scale,
+                            st["ws"], stream=stream)
+            else:
+                st["decode"](st["out"], st["q"], pool, wl.num_blocks, st["bt"], st["ctx"],
+                             wl.num_kv_heads, wl.max_context_len, wl.sm_scale, st["ws"],
+                             stream=stream)
             if timed:
                 ev[i][1].record(stream)
 
@@ -180,23 +192,32 @@ def main():
         return (t1 - t0) / steps * 1e3, float(np.mean(dec_ms)), float(np.median(dec_ms))
 
     # ---- headline: batched decode step (append + decode) ------------------
+    # fused: one call appends the 64 new tokens and decodes; unfused: the
+    # separate quantize-on-write call, then the decode call
     wl = make_config(3)
-    res = {}
+    res, unfused = {}, {}
     for fmt_int8 in (True, False):
         st = setup(wl, fmt_int8, "append")
-        step_ms, dec_ms, dec_med = run(wl, st, args.steps, args.warmup, with_write=True)
-        res["int8" if fmt_int8 else "fp16"] = dict(
-            step_ms=step_ms, decode_ms=dec_ms, decode_ms_median=dec_med,
+        key = "int8" if fmt_int8 else "fp16"
+        step_ms, dec_ms, dec_med = run(wl, st, args.steps, args.warmup, "fused")
+        res[key] = dict(
+            step_ms=step_ms, call_ms=dec_ms, call_ms_median=dec_med,
             tokens_per_s=wl.num_seqs / (step_ms * 1e-3),
-            decode_gbs=decode_bytes(wl, fmt_int8) / (dec_ms * 1e-3) / 1e9,
+            call_gbs=(decode_bytes(wl, fmt_int8) + append_bytes(wl, fmt_int8)) /
+            (dec_ms * 1e-3) / 1e9,
             rotate_replicas=len(st["pools"]))
+        step_ms, dec_ms, dec_med = run(wl, st, args.steps, args.warmup, "unfused")
+        unfused[key] = dict(step_ms=round(step_ms, 5), decode_ms=round(dec_ms, 5),
+                            tokens_per_s=round(wl.num_seqs / (step_ms * 1e-3), 1),
+                            decode_gbs=round(decode_bytes(wl, fmt_int8) / (dec_ms * 1e-3) / 1e9,
+                                             1))
         del st
         torch.cuda.empty_cache()
     waves, ppw = P.pdakv_decode_plan(P.KV_INT8_SYM, wl.num_seqs, wl.num_kv_heads,
                                      wl.max_context_len)
     i8 = res["int8"]
     dec_b = decode_bytes(wl, True)
-    step_b = dec_b + write_bytes(wl.num_seqs, wl.num_kv_heads, wl.head_dim, True)
+    call_b = dec_b + append_bytes(wl, True)
 
     # ---- supplementary decode-only points at 2K / 8K / 32K -------------------
     points = {}
@@ -207,7 +228,7 @@ def main():
                      "context": int(pwl.max_context_len)}
             for fmt_int8 in (True, False):
                 st = setup(pwl, fmt_int8, None)
-                _, dms, _ = run(pwl, st, max(10, args.steps), args.warmup, with_write=False)
+                _, dms, _ = run(pwl, st, max(10, args.steps), args.warmup, "decode")
                 b = decode_bytes(pwl, fmt_int8)
                 entry["int8" if fmt_int8 else "fp16"] = {
                     "decode_us": round(dms * 1e3, 2),
@@ -225,7 +246,7 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl)
 
-    achieved = dec_b / (i8["decode_ms"] * 1e-3) / 1e9
+    achieved = call_b / (i8["call_ms"] * 1e-3) / 1e9
     line = {
         "metric": "INT8-KV paged decode attention: tokens/s and achieved HBM GB/s at 2K/8K/32K",
         "value": round(i8["tokens_per_s"], 1),
@@ -243,18 +264,18 @@ def main():
                    "context": "uniform [1024, 8192] + 1 appended token",
                    "mean_context": round(float(wl.context_lens.mean()), 1),
                    "heads_q_kv": [wl.num_q_heads, wl.num_kv_heads], "head_dim": wl.head_dim,
-                   "block_size": 16, "step": "kv_quant_int8_sym_write(64 tokens) + "
-                   "paged_attn_decode_int8", "decode_waves": waves},
+                   "block_size": 16, "step": "paged_attn_decode_int8_append (quantize-on-write "
+                   "of the 64 new tokens fused into the decode launch)", "decode_waves": waves},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "paged_attn_decode_int8 (decode + partial merge)",
-                     "bytes_per_launch": dec_b, "launch_us": round(i8["decode_ms"] * 1e3, 2)},
-        "step_bytes": step_b,
-        "step_gbs": round(step_b / (i8["step_ms"] * 1e-3) / 1e9, 1),
+                     "kernel": "paged_attn_decode_int8_append (decode with fused append + "
+                               "partial merge)",
+                     "bytes_per_launch": call_b, "launch_us": round(i8["call_ms"] * 1e3, 2)},
         "fp16_control": {k: (round(v, 4) if isinstance(v, float) else v)
                          for k, v in res["fp16"].items()},
         "int8_over_fp16_tokens": round(i8["tokens_per_s"] / res["fp16"]["tokens_per_s"], 3),
+        "unfused_step": unfused,
         "points": points,
         "cpu_baseline": cpu,
     }

@@ -224,6 +224,47 @@ int paged_attn_decode_fp16(void* out, int out_dtype, int64_t out_stride_seq,
                            int max_context_len, float sm_scale, void* workspace,
                            size_t workspace_bytes, int32_t* err_flag, void* stream);
 
+/* Fused decode step: append each sequence's newest token and attend
+ * (InfiniLM PR #553 "fix: #552 int8 kv cache quantization cannot be enabled",
+ * benchmark note after "Summary": separate per-step quantize kernels cost
+ * INT8 decode 7-10%; here the quantize-on-write of the new token runs inside
+ * the decode launch).
+ * Same result as kv_quant_int8_sym_write of k_new/v_new with, for every
+ * sequence b with context_lens[b] >= 1, the slot of position
+ * context_lens[b] - 1 (page block_tables[b][(L - 1) / 16], offset (L - 1) % 16),
+ * followed by paged_attn_decode_int8 over all L positions.
+ *   k_new, v_new   device [num_seqs][num_kv_heads][head_dim] of q_dtype (F16
+ *                  or BF16) through the given element strides; row b is
+ *                  sequence b's newest token. Other arguments as
+ *                  paged_attn_decode_int8.
+ * A sequence with context length 0 gets zero rows and no write. A row whose
+ * scale would exceed 65504 is flagged PDAKV_EFLAG_SCALE_RANGE and not written
+ * (the slot keeps its old contents, which the attention then reads). With an
+ * out-of-range context length (flagged) the token is written at the clamped
+ * length's last position. */
+int paged_attn_decode_int8_append(
+    void* out, int out_dtype, int64_t out_stride_seq, int64_t out_stride_head, const void* q,
+    int q_dtype, int64_t q_stride_seq, int64_t q_stride_head, const void* k_new,
+    const void* v_new, int64_t k_stride_seq, int64_t k_stride_head, int64_t k_stride_dim,
+    int64_t v_stride_seq, int64_t v_stride_head, int64_t v_stride_dim, void* kv_pool,
+    int64_t num_blocks, int block_size, const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
+    int32_t* err_flag, void* stream);
+
+/* The fused step over 16-bit pages (the control for the fused INT8 step):
+ * kv_write_16bit of the newest tokens, then paged_attn_decode_fp16; same
+ * arguments as paged_attn_decode_int8_append. */
+int paged_attn_decode_fp16_append(
+    void* out, int out_dtype, int64_t out_stride_seq, int64_t out_stride_head, const void* q,
+    int q_dtype, int64_t q_stride_seq, int64_t q_stride_head, const void* k_new,
+    const void* v_new, int64_t k_stride_seq, int64_t k_stride_head, int64_t k_stride_dim,
+    int64_t v_stride_seq, int64_t v_stride_head, int64_t v_stride_dim, void* kv_pool,
+    int64_t num_blocks, int block_size, const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
+    int32_t* err_flag, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

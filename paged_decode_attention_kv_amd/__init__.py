@@ -29,7 +29,9 @@ from ._lib import (  # noqa: F401
     kv_quant_int8_sym_write,
     kv_write_16bit,
     paged_attn_decode_fp16,
+    paged_attn_decode_fp16_append,
     paged_attn_decode_int8,
+    paged_attn_decode_int8_append,
     pdakv_capabilities,
     pdakv_decode_plan,
     pdakv_decode_workspace_bytes,

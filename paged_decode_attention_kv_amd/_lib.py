@@ -56,6 +56,11 @@ _SIGS = {
                                         ctypes.c_size_t, _c_vp, _c_vp]),
 }
 _SIGS["paged_attn_decode_fp16"] = _SIGS["paged_attn_decode_int8"]
+_SIGS["paged_attn_decode_int8_append"] = (
+    _c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_vp] +
+    [_c_i64] * 6 + [_c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_int, _c_int, _c_int, _c_int,
+                    _c_int, _c_f, _c_vp, ctypes.c_size_t, _c_vp, _c_vp])
+_SIGS["paged_attn_decode_fp16_append"] = _SIGS["paged_attn_decode_int8_append"]
 
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -187,3 +192,48 @@ def paged_attn_decode_fp16(out, q, kv_pool, num_blocks: int, block_tables, conte
     """Decode over 16-bit (q's dtype) pages; writes out [B, Hq, D]."""
     _decode("paged_attn_decode_fp16", out, q, kv_pool, num_blocks, block_tables, context_lens,
             num_kv_heads, max_context_len, sm_scale, workspace, block_size, err_flag, stream)
+
+
+def _decode_append(fn_name, out, q, k_new, v_new, kv_pool, num_blocks, block_tables,
+                   context_lens, num_kv_heads, max_context_len, sm_scale, workspace, block_size,
+                   err_flag, stream):
+    B, hq, d = q.shape
+    if q.stride(2) != 1 or out.stride(2) != 1:
+        raise ValueError("the head_dim stride of q and out must be 1")
+    if tuple(out.shape) != (B, hq, d):
+        raise ValueError("out must have the shape of q")
+    if tuple(k_new.shape) != (B, num_kv_heads, d) or tuple(v_new.shape) != (B, num_kv_heads, d):
+        raise ValueError("k_new and v_new must be [num_seqs, num_kv_heads, head_dim]")
+    if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
+        raise ValueError("k_new and v_new must have q's dtype")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = getattr(_lib, fn_name)(
+        _ptr(out), _dtype_code(out.dtype), out.stride(0), out.stride(1),
+        _ptr(q), _dtype_code(q.dtype), q.stride(0), q.stride(1),
+        _ptr(k_new), _ptr(v_new), k_new.stride(0), k_new.stride(1), k_new.stride(2),
+        v_new.stride(0), v_new.stride(1), v_new.stride(2),
+        _ptr(kv_pool), num_blocks, block_size, _ptr(block_tables), block_tables.stride(0),
+        _ptr(context_lens), B, hq, num_kv_heads, d, max_context_len, float(sm_scale),
+        _ptr(workspace), ws_bytes, _ptr(err_flag), _stream(stream))
+    _check(fn_name, st)
+
+
+def paged_attn_decode_int8_append(out, q, k_new, v_new, kv_pool, num_blocks: int, block_tables,
+                                  context_lens, num_kv_heads: int, max_context_len: int,
+                                  sm_scale: float, workspace=None, block_size: int = 16,
+                                  err_flag=None, stream=None) -> None:
+    """Quantize-on-write each sequence's newest token (row b of k_new/v_new,
+    position context_lens[b] - 1) and decode over INT8 pages, in one launch."""
+    _decode_append("paged_attn_decode_int8_append", out, q, k_new, v_new, kv_pool, num_blocks,
+                   block_tables, context_lens, num_kv_heads, max_context_len, sm_scale,
+                   workspace, block_size, err_flag, stream)
+
+
+def paged_attn_decode_fp16_append(out, q, k_new, v_new, kv_pool, num_blocks: int, block_tables,
+                                  context_lens, num_kv_heads: int, max_context_len: int,
+                                  sm_scale: float, workspace=None, block_size: int = 16,
+                                  err_flag=None, stream=None) -> None:
+    """The fused step over 16-bit pages (the control)."""
+    _decode_append("paged_attn_decode_fp16_append", out, q, k_new, v_new, kv_pool, num_blocks,
+                   block_tables, context_lens, num_kv_heads, max_context_len, sm_scale,
+                   workspace, block_size, err_flag, stream)

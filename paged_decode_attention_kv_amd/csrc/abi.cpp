@@ -131,19 +131,33 @@ int check_decode(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, const
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PDAKV_OK : PDAKV_ERR_HIP; }
 
+// The newest token of every sequence for the fused append (absent: plain decode).
+struct AppendRows {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  int64_t kst = 0, ksh = 0, ksd = 0, vst = 0, vsh = 0, vsd = 0;
+};
+
 template <bool Int8>
 int decode_common(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, const void* q,
-                  int q_dtype, int64_t q_ss, int64_t q_sh, const void* kv_pool,
-                  int64_t num_blocks, int block_size, const int32_t* block_tables,
-                  int64_t bt_stride, const int32_t* context_lens, int num_seqs,
-                  int num_q_heads, int num_kv_heads, int head_dim, int max_context_len,
-                  float sm_scale, void* workspace, size_t workspace_bytes, int32_t* err_flag,
-                  void* stream) {
+                  int q_dtype, int64_t q_ss, int64_t q_sh, const AppendRows* app,
+                  const void* kv_pool, int64_t num_blocks, int block_size,
+                  const int32_t* block_tables, int64_t bt_stride, const int32_t* context_lens,
+                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                  int max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
+                  int32_t* err_flag, void* stream) {
   int st = check_decode(out, out_dtype, out_ss, out_sh, q, q_dtype, q_ss, q_sh, kv_pool,
                         num_blocks, block_size, block_tables, bt_stride, context_lens,
                         num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                         sm_scale, workspace, workspace_bytes);
-  if (st != PDAKV_OK || num_seqs == 0) return st;
+  if (st != PDAKV_OK) return st;
+  if (app) {
+    if (app->kst < 0 || app->ksh < 0 || app->ksd < 0 || app->vst < 0 || app->vsh < 0 ||
+        app->vsd < 0)
+      return PDAKV_ERR_INVALID_ARG;
+    if (num_seqs > 0 && max_context_len > 0 && (!app->k || !app->v)) return PDAKV_ERR_INVALID_ARG;
+  }
+  if (num_seqs == 0) return st;
   DecodeArgs a{};
   a.out = out;
   a.out_dtype = out_dtype;
@@ -153,7 +167,7 @@ int decode_common(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, cons
   a.q_ss = q_ss;
   a.q_sh = q_sh;
   a.q_vec16 = aligned16(q) && q_ss % 8 == 0 && q_sh % 8 == 0;
-  a.pool = static_cast<const uint8_t*>(kv_pool);
+  a.pool = static_cast<uint8_t*>(const_cast<void*>(kv_pool));
   a.num_blocks = num_blocks;
   a.page_bytes = static_cast<int64_t>(pdakv_page_bytes(
       Int8 ? PDAKV_KV_INT8_SYM : PDAKV_KV_16BIT, block_size, num_kv_heads, head_dim));
@@ -170,17 +184,30 @@ int decode_common(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, cons
                                              num_seqs, num_kv_heads, max_context_len));
   a.merge_waves = merge_waves(num_seqs, num_kv_heads, max_context_len, a.num_waves);
   {
-    // LDS staging per decode pass and segment: the unit's q rows (16-bit) and
-    // its result (accumulator, max, sum per query head)
-    const int per_seg = a.group * head_dim * 2 + a.group * (head_dim + 2) * 4;
-    a.seg_cap = std::max(1, std::min(64, pdakv::kLdsPerWave / per_seg));
-    a.lds_wave_bytes = (a.seg_cap * per_seg + 15) / 16 * 16;
+    // LDS staging per decode pass and segment: the unit's q rows (16-bit),
+    // its result (accumulator, max, sum per query head) and the appended
+    // token (4 * head_dim bytes), regions aligned to 16 bytes
+    const int qb = a.group * head_dim * 2, rb = a.group * (head_dim + 2) * 4;
+    const int nb = 4 * head_dim;
+    a.seg_cap = std::max(1, std::min(64, (pdakv::kLdsPerWave - 16) / (qb + rb + nb)));
+    a.lds_wave_bytes = (a.seg_cap * (qb + rb) + 15) / 16 * 16 + a.seg_cap * nb;
   }
   a.ws = static_cast<float*>(workspace);
   a.desc = reinterpret_cast<int2*>(
       static_cast<uint8_t*>(workspace) +
       partials_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len));
   a.err = err_flag;
+  if (app) {
+    a.append = 1;
+    a.k_new = app->k;
+    a.v_new = app->v;
+    a.kn_st = app->kst;
+    a.kn_sh = app->ksh;
+    a.kn_sd = app->ksd;
+    a.vn_st = app->vst;
+    a.vn_sh = app->vsh;
+    a.vn_sd = app->vsd;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = q_dtype == PDAKV_DTYPE_BF16;
   return hip_status(Int8 ? pdakv::launch_decode_int8(a, head_dim, bf16, s)
@@ -319,7 +346,7 @@ int paged_attn_decode_int8(void* out, int out_dtype, int64_t out_stride_seq,
                            int max_context_len, float sm_scale, void* workspace,
                            size_t workspace_bytes, int32_t* err_flag, void* stream) {
   return decode_common<true>(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
-                             q_stride_seq, q_stride_head, kv_pool, num_blocks, block_size,
+                             q_stride_seq, q_stride_head, nullptr, kv_pool, num_blocks, block_size,
                              block_tables, block_table_stride, context_lens, num_seqs,
                              num_q_heads, num_kv_heads, head_dim, max_context_len, sm_scale,
                              workspace, workspace_bytes, err_flag, stream);
@@ -334,10 +361,60 @@ int paged_attn_decode_fp16(void* out, int out_dtype, int64_t out_stride_seq,
                            int max_context_len, float sm_scale, void* workspace,
                            size_t workspace_bytes, int32_t* err_flag, void* stream) {
   return decode_common<false>(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
-                              q_stride_seq, q_stride_head, kv_pool, num_blocks, block_size,
+                              q_stride_seq, q_stride_head, nullptr, kv_pool, num_blocks, block_size,
                               block_tables, block_table_stride, context_lens, num_seqs,
                               num_q_heads, num_kv_heads, head_dim, max_context_len, sm_scale,
                               workspace, workspace_bytes, err_flag, stream);
+}
+
+int paged_attn_decode_int8_append(
+    void* out, int out_dtype, int64_t out_stride_seq, int64_t out_stride_head, const void* q,
+    int q_dtype, int64_t q_stride_seq, int64_t q_stride_head, const void* k_new,
+    const void* v_new, int64_t k_stride_seq, int64_t k_stride_head, int64_t k_stride_dim,
+    int64_t v_stride_seq, int64_t v_stride_head, int64_t v_stride_dim, void* kv_pool,
+    int64_t num_blocks, int block_size, const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
+    int32_t* err_flag, void* stream) {
+  AppendRows app;
+  app.k = k_new;
+  app.v = v_new;
+  app.kst = k_stride_seq;
+  app.ksh = k_stride_head;
+  app.ksd = k_stride_dim;
+  app.vst = v_stride_seq;
+  app.vsh = v_stride_head;
+  app.vsd = v_stride_dim;
+  return decode_common<true>(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
+                             q_stride_seq, q_stride_head, &app, kv_pool, num_blocks, block_size,
+                             block_tables, block_table_stride, context_lens, num_seqs,
+                             num_q_heads, num_kv_heads, head_dim, max_context_len, sm_scale,
+                             workspace, workspace_bytes, err_flag, stream);
+}
+
+int paged_attn_decode_fp16_append(
+    void* out, int out_dtype, int64_t out_stride_seq, int64_t out_stride_head, const void* q,
+    int q_dtype, int64_t q_stride_seq, int64_t q_stride_head, const void* k_new,
+    const void* v_new, int64_t k_stride_seq, int64_t k_stride_head, int64_t k_stride_dim,
+    int64_t v_stride_seq, int64_t v_stride_head, int64_t v_stride_dim, void* kv_pool,
+    int64_t num_blocks, int block_size, const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
+    int32_t* err_flag, void* stream) {
+  AppendRows app;
+  app.k = k_new;
+  app.v = v_new;
+  app.kst = k_stride_seq;
+  app.ksh = k_stride_head;
+  app.ksd = k_stride_dim;
+  app.vst = v_stride_seq;
+  app.vsh = v_stride_head;
+  app.vsd = v_stride_dim;
+  return decode_common<false>(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
+                              q_stride_seq, q_stride_head, &app, kv_pool, num_blocks,
+                              block_size, block_tables, block_table_stride, context_lens,
+                              num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                              sm_scale, workspace, workspace_bytes, err_flag, stream);
 }
 
 }  // extern "C"

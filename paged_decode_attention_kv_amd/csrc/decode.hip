@@ -49,6 +49,7 @@
 // invalidate the L2 of the XCD: far dearer than the second launch.)
 #include "device_util.h"
 #include "launch.h"
+#include "quant_row.h"
 
 namespace pdakv {
 
@@ -373,6 +374,92 @@ struct Int8Kind {
   static __device__ __forceinline__ int acc_dim(int k, int j, int kb) {
     return 64 * (k / 4) + 16 * kb + 4 * j + (k % 4);
   }
+
+  // Fused append: quantize the newest token's K and V rows of (b, g) with the
+  // quantize-on-write rule, store them at position pos of head block hb (if
+  // it exists), and leave them in nt ([D] K codes, [D] V codes, K scale, V
+  // scale) for patch(). False when a scale would exceed FP16 (flagged; the
+  // slot is left as it was, as the separate write leaves it).
+  static __device__ __forceinline__ bool append(const DecodeArgs& a, int b, int g, int pos, int hb,
+                                                uint8_t* nt, int lane) {
+    constexpr int EPL = D / 64;
+    float xk[EPL], xv[EPL];
+    float ak = 0.f, av = 0.f;
+    const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
+    const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int64_t d = lane * EPL + e;
+      xk[e] = bits16_to_f32<QBF16>(kn[b * a.kn_st + g * a.kn_sh + d * a.kn_sd]);
+      xv[e] = bits16_to_f32<QBF16>(vn[b * a.vn_st + g * a.vn_sh + d * a.vn_sd]);
+      ak = fmaxf(ak, fabsf(xk[e]));
+      av = fmaxf(av, fabsf(xv[e]));
+    }
+    ak = wave_max(ak);
+    av = wave_max(av);
+    uint16_t skb, svb;
+    const bool okk = row_scale(ak, skb), okv = row_scale(av, svb);
+    if (!okk || !okv) {
+      if (lane == 0) raise_flag(a.err, PDAKV_EFLAG_SCALE_RANGE);
+      return false;
+    }
+    const float sk = f16_bits_to_f32(skb), sv = f16_bits_to_f32(svb);
+    uint8_t* head = a.pool + static_cast<int64_t>(hb >= 0 ? hb : 0) * kHeadBytes;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int d = lane * EPL + e;
+      const uint8_t ck = row_code(xk[e], sk), cv = row_code(xv[e], sv);
+      if (hb >= 0) {
+        head[pos * D + d] = ck;
+        head[16 * D + (pos >> 2) * 4 * D + 4 * d + (pos & 3)] = cv;
+      }
+      nt[d] = ck;
+      nt[D + d] = cv;
+    }
+    if (lane == 0) {
+      if (hb >= 0) {
+        *reinterpret_cast<uint16_t*>(head + 32 * D + 2 * pos) = skb;
+        *reinterpret_cast<uint16_t*>(head + 32 * D + 32 + 2 * pos) = svb;
+      }
+      *reinterpret_cast<uint16_t*>(nt + 2 * D) = skb;
+      *reinterpret_cast<uint16_t*>(nt + 2 * D + 2) = svb;
+    }
+    return true;
+  }
+
+  // Put the appended token (from nt) into the registers of its page as
+  // loaded: K row in the lanes of token pos, V bytes and scales in the lanes
+  // of its token group.
+  static __device__ __forceinline__ void patch(Page& pg, const uint8_t* nt, int pos, int i16,
+                                               int kb) {
+    if (i16 == pos) {
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i)
+        pg.k[i] = *reinterpret_cast<const u4_t*>(nt + 64 * i + 16 * kb);
+    }
+    if (kb == (pos >> 2)) {
+      const int sh = 8 * (pos & 3);
+      const uint32_t keep = ~(0xFFu << sh);
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(nt + D + 64 * i + 4 * i16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          pg.v[i][j] = (pg.v[i][j] & keep) | (((w >> (8 * j)) & 0xFFu) << sh);
+      }
+      const int hs = 16 * (pos & 1);
+      const uint32_t hkeep = ~(0xFFFFu << hs);
+      const uint32_t kbits = *reinterpret_cast<const uint16_t*>(nt + 2 * D);
+      const uint32_t vbits = *reinterpret_cast<const uint16_t*>(nt + 2 * D + 2);
+      if ((pos & 3) < 2) {
+        pg.ks.x = (pg.ks.x & hkeep) | (kbits << hs);
+        pg.vs.x = (pg.vs.x & hkeep) | (vbits << hs);
+      } else {
+        pg.ks.y = (pg.ks.y & hkeep) | (kbits << hs);
+        pg.vs.y = (pg.vs.y & hkeep) | (vbits << hs);
+      }
+    }
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -529,6 +616,56 @@ struct F16Kind {
   static __device__ __forceinline__ int acc_dim(int k, int j, int kb) {
     return 32 * (k / 2) + 8 * kb + 2 * j + (k % 2);
   }
+
+  // Fused append: copy the newest token's K and V rows of (b, g) into
+  // position pos of head block hb (if it exists) and into nt ([D] K, [D] V,
+  // 16-bit) for patch().
+  static __device__ __forceinline__ bool append(const DecodeArgs& a, int b, int g, int pos, int hb,
+                                                uint8_t* nt, int lane) {
+    constexpr int EPL = D / 64;
+    const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
+    const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
+    uint16_t* head = reinterpret_cast<uint16_t*>(a.pool + static_cast<int64_t>(hb >= 0 ? hb : 0) *
+                                                              kHeadBytes);
+    uint16_t* nt16 = reinterpret_cast<uint16_t*>(nt);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int64_t d = lane * EPL + e;
+      const uint16_t k = kn[b * a.kn_st + g * a.kn_sh + d * a.kn_sd];
+      const uint16_t v = vn[b * a.vn_st + g * a.vn_sh + d * a.vn_sd];
+      if (hb >= 0) {
+        head[pos * D + d] = k;
+        head[16 * D + (pos >> 2) * 4 * D + 4 * d + (pos & 3)] = v;
+      }
+      nt16[d] = k;
+      nt16[D + d] = v;
+    }
+    return true;
+  }
+
+  // Put the appended token (from nt) into the registers of its page.
+  static __device__ __forceinline__ void patch(Page& pg, const uint8_t* nt, int pos, int i16,
+                                               int kb) {
+    const uint16_t* nt16 = reinterpret_cast<const uint16_t*>(nt);
+    if (i16 == pos) {
+#pragma unroll
+      for (int j = 0; j < D / 32; ++j)
+        pg.k[j] = *reinterpret_cast<const u4_t*>(nt16 + 32 * j + 8 * kb);
+    }
+    if (kb == (pos >> 2)) {
+      const int tt = pos & 3;
+      const int hs = 16 * (tt & 1);
+      const uint32_t keep = ~(0xFFFFu << hs);
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) {
+        // V values of dims 32*i + 2*i16 and + 1: word (tt >> 1) and 2 + (tt >> 1)
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(nt16 + D + 32 * i + 2 * i16);
+        const int w0 = tt >> 1;
+        pg.v[i][w0] = (pg.v[i][w0] & keep) | ((w & 0xFFFFu) << hs);
+        pg.v[i][2 + w0] = (pg.v[i][2 + w0] & keep) | ((w >> 16) << hs);
+      }
+    }
+  }
 };
 
 // ---------------------------------------------------------------------------
@@ -541,7 +678,12 @@ struct F16Kind {
 struct PassLds {
   uint16_t* q;   // [seg_cap][G][D]
   float* res;    // [seg_cap][G][D + 2]
+  uint8_t* nt;   // [seg_cap][kNewTokenBytes(D)]: appended token per segment
 };
+
+// LDS bytes that hold one segment's appended token (16-bit K and V rows, or
+// INT8 codes and scales); a multiple of 16.
+__host__ __device__ constexpr int new_token_bytes(int D) { return 4 * D; }
 
 // Copy the q rows of unit (b, g) into LDS; 16-byte chunks dealt to the lanes.
 template <int D>
@@ -635,7 +777,7 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   const int hkv = a.num_kv_heads;
 
   // plan: lane s keeps segment s's unit, first page, first item, length, L
-  int s_unit = 0, s_p = 0, s_start = 0, s_n = 0, s_L = 0, s_whole = 0;
+  int s_unit = 0, s_p = 0, s_start = 0, s_n = 0, s_L = 0, s_whole = 0, s_last = 0;
   int ns = 0, items = 0;
   while (true) {
     const int n = min(min(cu.np - cu.p, x1 - (x + items)), kMaxPagesPerWave - items);
@@ -651,6 +793,7 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
       s_n = n;
       s_L = cu.L;
       s_whole = cu.p == 0 && n == cu.np;
+      s_last = cu.p + n == cu.np;  // holds the unit's last page
     }
     ++ns;
     items += n;
@@ -692,6 +835,21 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   const int hb0 = blk0 >= 0 ? blk0 * hkv + g0 : -1;
   const int hb1 = blk1 >= 0 ? blk1 * hkv + g1 : -1;
   auto block_of = [&](int i) { return i < 64 ? readlane(hb0, i) : readlane(hb1, i - 64); };
+
+  // fused append: the wave holding a unit's last page writes the sequence's
+  // newest token for that KV head and patches it into the page as loaded
+  // (nobody else reads that slot during the call)
+  int s_patch = 0;
+  if (a.append) {
+    for (int s = 0; s < ns; ++s) {
+      if (!readlane(s_last, s)) continue;
+      const int u = readlane(s_unit, s), L = readlane(s_L, s);
+      const int hb = block_of(readlane(s_start, s) + readlane(s_n, s) - 1);
+      const bool ok = K::append(a, u / hkv, u % hkv, (L - 1) % kBlockSize, hb,
+                                lds.nt + s * new_token_bytes(D), lane);
+      if (lane == s) s_patch = ok;
+    }
+  }
   // a missing page reads head block 0 (it exists) and is fully masked
   // (hb is the same in every lane; saying so keeps the address in scalar
   // registers, as the buffer resource requires)
@@ -702,13 +860,14 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
 
   // current segment: its unit's KV head, first page's token, first item,
   // end item and length
-  int cs = 0, c_tok = 0, c_start = 0, c_end = 0, c_L = 0;
+  int cs = 0, c_tok = 0, c_start = 0, c_end = 0, c_L = 0, c_patch = 0;
   auto enter = [&](int sidx) {
     cs = sidx;
     c_tok = readlane(s_p, sidx) * kBlockSize;
     c_start = readlane(s_start, sidx);
     c_end = c_start + readlane(s_n, sidx);
     c_L = readlane(s_L, sidx);
+    c_patch = readlane(s_patch, sidx);
   };
   enter(0);
 
@@ -731,7 +890,7 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     }
   };
   // consume items first.. of a group; false once the pass's items are done
-  auto consume = [&](const typename K::Page* grp, const int* blk, int first) {
+  auto consume = [&](typename K::Page* grp, const int* blk, int first) {
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       const int i = first + j;
@@ -743,6 +902,8 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
         kind.load_q(a, lds.q + cs * a.group * D, i16, kb, i16 < a.group);
       }
       const int t = c_tok + (i - c_start) * kBlockSize;
+      if (c_patch && i == c_end - 1)
+        K::patch(grp[j], lds.nt + cs * new_token_bytes(D), (c_L - 1) % kBlockSize, i16, kb);
       kind.step(grp[j], t, blk[j] >= 0 ? c_L : t, st);
     }
     return true;
@@ -783,6 +944,8 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs& a) {
   lds.q = reinterpret_cast<uint16_t*>(smem + wid * a.lds_wave_bytes);
   lds.res = reinterpret_cast<float*>(smem + wid * a.lds_wave_bytes +
                                      a.seg_cap * a.group * K::D * 2);
+  lds.nt = smem + wid * a.lds_wave_bytes +
+           (a.seg_cap * a.group * K::D * 2 + a.seg_cap * a.group * (K::D + 2) * 4 + 15) / 16 * 16;
 
   // total pages; zero rows of empty sequences
   const int nchunk = (a.num_seqs + 63) / 64;

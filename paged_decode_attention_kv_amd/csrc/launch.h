@@ -49,7 +49,7 @@ struct DecodeArgs {
   const void* q;
   int64_t q_ss, q_sh;
   int q_vec16;  // q pointer and strides allow 16-byte loads of 8 elements
-  const uint8_t* pool;
+  uint8_t* pool;  // written only by the fused append
   int64_t num_blocks;
   int64_t page_bytes;
   const int32_t* bt;
@@ -62,7 +62,13 @@ struct DecodeArgs {
   int num_waves;     // waves of the decode grid (a multiple of kWaves)
   int merge_waves;   // waves per merge workgroup (1 .. kMaxMergeWaves)
   int seg_cap;       // decode: segments staged in LDS per pass
-  int lds_wave_bytes;  // decode: LDS per wave (q rows + results of seg_cap segments)
+  int lds_wave_bytes;  // decode: LDS per wave (q rows, results, appended tokens)
+  // append (fused write of each sequence's newest token, at position L - 1):
+  // 16-bit K and V rows [B][Hkv][D] in q's dtype, element strides
+  int append;
+  const void* k_new;
+  const void* v_new;
+  int64_t kn_st, kn_sh, kn_sd, vn_st, vn_sh, vn_sd;
   int32_t* err;
 };
 

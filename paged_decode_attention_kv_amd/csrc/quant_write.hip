@@ -1,17 +1,13 @@
 // Quantize-on-write and 16-bit write into paged KV pools (gfx950).
 //
 // One wave (64 lanes) owns one (token, KV head) pair and handles its K row and
-// its V row; a workgroup holds four waves. The per-token symmetric quantizer
+// its V row; a workgroup holds four waves. The row quantizer (quant_row.h)
 // follows MoE-Infinity PR #183 "feat: opt-in INT8 KV-cache quantization"
 // ("What landed", format-contract bullet; "Precision & memory") and the
-// zero-token rule of mlxcel PR #717 ("The Int8 bug and fix"):
-//   a = max|x|; scale = 1.0 if a == 0 else the smallest FP16 >= fl32(a/127);
-//   code = clamp(rint(fl32(x / scale)), -127, 127).
-// The division is IEEE binary32 (this file is built with correctly rounded
-// division and without denormal flushing), so codes are exact functions of
-// the input and match any other IEEE implementation bit for bit.
+// zero-token rule of mlxcel PR #717 ("The Int8 bug and fix").
 #include "device_util.h"
 #include "launch.h"
+#include "quant_row.h"
 
 namespace pdakv {
 
@@ -26,15 +22,6 @@ struct Int8Head {
   static constexpr int kKs = 2 * kBlockSize * D;     // K scales
   static constexpr int kVs = 2 * kBlockSize * D + 2 * kBlockSize;
 };
-
-// Smallest fp16 >= s (s finite, 0 < s <= 65504), as raw bits.
-__device__ __forceinline__ uint16_t round_up_f16(float s) {
-  _Float16 h = static_cast<_Float16>(s);  // round to nearest even
-  uint16_t bits = __builtin_bit_cast(uint16_t, h);
-  if (static_cast<float>(h) < s) bits += 1;  // next fp16 above (s > 0)
-  if (bits == 0) bits = 1;                     // s > 0 never rounds up to 0
-  return bits;
-}
 
 template <typename T>
 __device__ __forceinline__ uint16_t load_bits(const void* base, int64_t idx) {
@@ -73,24 +60,20 @@ __global__ __launch_bounds__(64 * kWriteWaves) void quant_write_int8_kernel(Writ
   ak = wave_max(ak);
   av = wave_max(av);
 
-  const float sk32 = ak / 127.0f;
-  const float sv32 = av / 127.0f;
-  if (sk32 > 65504.0f || sv32 > 65504.0f) {
+  uint16_t skb, svb;
+  const bool okk = row_scale(ak, skb), okv = row_scale(av, svb);
+  if (!okk || !okv) {
     if (lane == 0) raise_flag(a.err, PDAKV_EFLAG_SCALE_RANGE);
     return;
   }
-  const uint16_t skb = ak == 0.f ? 0x3C00 : round_up_f16(sk32);
-  const uint16_t svb = av == 0.f ? 0x3C00 : round_up_f16(sv32);
   const float sk = f16_bits_to_f32(skb);
   const float sv = f16_bits_to_f32(svb);
 
   uint8_t ck[EPL], cv[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    ck[e] = static_cast<uint8_t>(
-        static_cast<int8_t>(fminf(fmaxf(rintf(xk[e] / sk), -127.f), 127.f)));
-    cv[e] = static_cast<uint8_t>(
-        static_cast<int8_t>(fminf(fmaxf(rintf(xv[e] / sv), -127.f), 127.f)));
+    ck[e] = row_code(xk[e], sk);
+    cv[e] = row_code(xv[e], sv);
   }
   // K: token-major row; V: dimension d of tokens grouped by four.
 #pragma unroll

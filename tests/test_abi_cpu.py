@@ -27,7 +27,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function(P):
     names = _declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(P._lib, n), n
     assert set(names) == set(P.EXPORTED)
@@ -137,3 +137,23 @@ def _decode_args(**kw):
 ])
 def test_decode_validation(P, fn, change, status):
     assert getattr(P._lib, fn)(*_decode_args(**change)) == status
+
+
+def _append_args(**kw):
+    a = dict(out=FAKE, odt=0, oss=4096, osh=128, q=FAKE, qdt=1, qss=4096, qsh=128, kn=FAKE,
+             vn=FAKE, kst=1024, ksh=128, ksd=1, vst=1024, vsh=128, vsd=1, pool=FAKE, nblk=16,
+             bs=16, bt=FAKE, bts=16, ctx=FAKE, B=1, hq=32, hkv=8, d=128, maxL=256, sm=0.088,
+             ws=FAKE, wsb=1 << 30, err=None, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("fn", ["paged_attn_decode_int8_append", "paged_attn_decode_fp16_append"])
+@pytest.mark.parametrize("change,status", [
+    (dict(kn=None), -1), (dict(vn=None), -1), (dict(ksd=-1), -1), (dict(vst=-2), -1),
+    (dict(qdt=0), -3), (dict(d=96), -2), (dict(maxL=2048, bts=128, ws=None, wsb=0), -4),
+    (dict(B=0), 0),
+    (dict(B=0, kn=None, vn=None), 0),
+])
+def test_append_validation(P, fn, change, status):
+    assert getattr(P._lib, fn)(*_append_args(**change)) == status
