@@ -157,18 +157,18 @@ def main():
 
     def run(wl, st, steps, warmup, mode):
         """mode "decode": decode calls only; "unfused": write the appended
-        tokens, then decode (events around the decode call); "fused": the
-        fused append + decode call (events around it)."""
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
+        tokens, then decode; "fused": the fused append + decode call.
+        Returns (ms per step over `steps` steps with nothing else on the
+        stream, mean and median ms of the decode (or fused) call from HIP
+        events around it in a second run of `steps` steps)."""
         pools = st["pools"]
 
-        def one(i, timed):
+        def one(i, ev=None):
             pool = pools[i % len(pools)]
             if mode == "unfused":
                 st["write"](st["ak"], st["av"], st["aslots"], pool, wl.num_blocks, stream=stream)
-            if timed:
-                ev[i][0].record(stream)
+            if ev is not None:
+                ev[0].record(stream)
             if mode == "fused":
                 st["fused"](st["out"], st["q"], st["ak"], st["av"], pool, wl.num_blocks, st["bt"],
                             st["ctx"], wl.num_kv_heads, wl.max_context_len, wl.sm_scale,
@@ -177,18 +177,23 @@ def main():
                 st["decode"](st["out"], st["q"], pool, wl.num_blocks, st["bt"], st["ctx"],
                              wl.num_kv_heads, wl.max_context_len, wl.sm_scale, st["ws"],
                              stream=stream)
-            if timed:
-                ev[i][1].record(stream)
+            if ev is not None:
+                ev[1].record(stream)
 
         for i in range(warmup):
-            one(i, False)
+            one(i)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            one(i, True)
+            one(i)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        dec_ms = [a.elapsed_time(b) for a, b in ev]
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for i in range(steps):
+            one(i, evs[i])
+        torch.cuda.synchronize()
+        dec_ms = [a.elapsed_time(b) for a, b in evs]
         return (t1 - t0) / steps * 1e3, float(np.mean(dec_ms)), float(np.median(dec_ms))
 
     # ---- headline: batched decode step (append + decode) ------------------

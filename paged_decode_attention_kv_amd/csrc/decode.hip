@@ -375,13 +375,13 @@ struct Int8Kind {
     return 64 * (k / 4) + 16 * kb + 4 * j + (k % 4);
   }
 
-  // Fused append: quantize the newest token's K and V rows of (b, g) with the
-  // quantize-on-write rule, store them at position pos of head block hb (if
-  // it exists), and leave them in nt ([D] K codes, [D] V codes, K scale, V
-  // scale) for patch(). False when a scale would exceed FP16 (flagged; the
-  // slot is left as it was, as the separate write leaves it).
-  static __device__ __forceinline__ bool append(const DecodeArgs& a, int b, int g, int pos, int hb,
-                                                uint8_t* nt, int lane) {
+  // Fused append, first half: quantize the newest token's K and V rows of
+  // (b, g) with the quantize-on-write rule into nt ([D] K codes, [D] V codes,
+  // K scale, V scale) for patch() and store_new(). False when a scale would
+  // exceed FP16 (flagged; the slot is then left as it was, as the separate
+  // write leaves it).
+  static __device__ __forceinline__ bool prepare_new(const DecodeArgs& a, int b, int g,
+                                                     uint8_t* nt, int lane) {
     constexpr int EPL = D / 64;
     float xk[EPL], xv[EPL];
     float ak = 0.f, av = 0.f;
@@ -404,27 +404,34 @@ struct Int8Kind {
       return false;
     }
     const float sk = f16_bits_to_f32(skb), sv = f16_bits_to_f32(svb);
-    uint8_t* head = a.pool + static_cast<int64_t>(hb >= 0 ? hb : 0) * kHeadBytes;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const int d = lane * EPL + e;
-      const uint8_t ck = row_code(xk[e], sk), cv = row_code(xv[e], sv);
-      if (hb >= 0) {
-        head[pos * D + d] = ck;
-        head[16 * D + (pos >> 2) * 4 * D + 4 * d + (pos & 3)] = cv;
-      }
-      nt[d] = ck;
-      nt[D + d] = cv;
+      nt[d] = row_code(xk[e], sk);
+      nt[D + d] = row_code(xv[e], sv);
     }
     if (lane == 0) {
-      if (hb >= 0) {
-        *reinterpret_cast<uint16_t*>(head + 32 * D + 2 * pos) = skb;
-        *reinterpret_cast<uint16_t*>(head + 32 * D + 32 + 2 * pos) = svb;
-      }
       *reinterpret_cast<uint16_t*>(nt + 2 * D) = skb;
       *reinterpret_cast<uint16_t*>(nt + 2 * D + 2) = svb;
     }
     return true;
+  }
+
+  // Fused append, second half (after the page loop): store the token from nt
+  // at position pos of head block hb.
+  static __device__ __forceinline__ void store_new(const DecodeArgs& a, const uint8_t* nt,
+                                                   int pos, int hb, int lane) {
+    uint8_t* head = a.pool + static_cast<int64_t>(hb) * kHeadBytes;
+    for (int d = lane; d < D; d += 64) {
+      head[pos * D + d] = nt[d];
+      head[16 * D + (pos >> 2) * 4 * D + 4 * d + (pos & 3)] = nt[D + d];
+    }
+    if (lane == 0) {
+      *reinterpret_cast<uint16_t*>(head + 32 * D + 2 * pos) =
+          *reinterpret_cast<const uint16_t*>(nt + 2 * D);
+      *reinterpret_cast<uint16_t*>(head + 32 * D + 32 + 2 * pos) =
+          *reinterpret_cast<const uint16_t*>(nt + 2 * D + 2);
+    }
   }
 
   // Put the appended token (from nt) into the registers of its page as
@@ -617,30 +624,33 @@ struct F16Kind {
     return 32 * (k / 2) + 8 * kb + 2 * j + (k % 2);
   }
 
-  // Fused append: copy the newest token's K and V rows of (b, g) into
-  // position pos of head block hb (if it exists) and into nt ([D] K, [D] V,
-  // 16-bit) for patch().
-  static __device__ __forceinline__ bool append(const DecodeArgs& a, int b, int g, int pos, int hb,
-                                                uint8_t* nt, int lane) {
+  // Fused append, first half: the newest token's K and V rows of (b, g)
+  // into nt ([D] K, [D] V, 16-bit) for patch() and store_new().
+  static __device__ __forceinline__ bool prepare_new(const DecodeArgs& a, int b, int g,
+                                                     uint8_t* nt, int lane) {
     constexpr int EPL = D / 64;
     const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
     const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
-    uint16_t* head = reinterpret_cast<uint16_t*>(a.pool + static_cast<int64_t>(hb >= 0 ? hb : 0) *
-                                                              kHeadBytes);
     uint16_t* nt16 = reinterpret_cast<uint16_t*>(nt);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const int64_t d = lane * EPL + e;
-      const uint16_t k = kn[b * a.kn_st + g * a.kn_sh + d * a.kn_sd];
-      const uint16_t v = vn[b * a.vn_st + g * a.vn_sh + d * a.vn_sd];
-      if (hb >= 0) {
-        head[pos * D + d] = k;
-        head[16 * D + (pos >> 2) * 4 * D + 4 * d + (pos & 3)] = v;
-      }
-      nt16[d] = k;
-      nt16[D + d] = v;
+      nt16[d] = kn[b * a.kn_st + g * a.kn_sh + d * a.kn_sd];
+      nt16[D + d] = vn[b * a.vn_st + g * a.vn_sh + d * a.vn_sd];
     }
     return true;
+  }
+
+  // Fused append, second half (after the page loop): store the token from nt
+  // at position pos of head block hb.
+  static __device__ __forceinline__ void store_new(const DecodeArgs& a, const uint8_t* nt,
+                                                   int pos, int hb, int lane) {
+    uint16_t* head = reinterpret_cast<uint16_t*>(a.pool + static_cast<int64_t>(hb) * kHeadBytes);
+    const uint16_t* nt16 = reinterpret_cast<const uint16_t*>(nt);
+    for (int d = lane; d < D; d += 64) {
+      head[pos * D + d] = nt16[d];
+      head[16 * D + (pos >> 2) * 4 * D + 4 * d + (pos & 3)] = nt16[D + d];
+    }
   }
 
   // Put the appended token (from nt) into the registers of its page.
@@ -835,21 +845,6 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   const int hb0 = blk0 >= 0 ? blk0 * hkv + g0 : -1;
   const int hb1 = blk1 >= 0 ? blk1 * hkv + g1 : -1;
   auto block_of = [&](int i) { return i < 64 ? readlane(hb0, i) : readlane(hb1, i - 64); };
-
-  // fused append: the wave holding a unit's last page writes the sequence's
-  // newest token for that KV head and patches it into the page as loaded
-  // (nobody else reads that slot during the call)
-  int s_patch = 0;
-  if (a.append) {
-    for (int s = 0; s < ns; ++s) {
-      if (!readlane(s_last, s)) continue;
-      const int u = readlane(s_unit, s), L = readlane(s_L, s);
-      const int hb = block_of(readlane(s_start, s) + readlane(s_n, s) - 1);
-      const bool ok = K::append(a, u / hkv, u % hkv, (L - 1) % kBlockSize, hb,
-                                lds.nt + s * new_token_bytes(D), lane);
-      if (lane == s) s_patch = ok;
-    }
-  }
   // a missing page reads head block 0 (it exists) and is fully masked
   // (hb is the same in every lane; saying so keeps the address in scalar
   // registers, as the buffer resource requires)
@@ -858,8 +853,9 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     return a.pool + static_cast<int64_t>(hb >= 0 ? hb : 0) * K::kHeadBytes;
   };
 
-  // current segment: its unit's KV head, first page's token, first item,
-  // end item and length
+  // current segment: first page's token, first item, end item, length, and
+  // whether its last page gets the appended token
+  int s_patch = 0;  // lane s: segment s's appended token is in LDS
   int cs = 0, c_tok = 0, c_start = 0, c_end = 0, c_L = 0, c_patch = 0;
   auto enter = [&](int sidx) {
     cs = sidx;
@@ -869,11 +865,7 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     c_L = readlane(s_L, sidx);
     c_patch = readlane(s_patch, sidx);
   };
-  enter(0);
-
   SoftmaxState<ND> st;
-  softmax_init(st);
-  kind.load_q(a, lds.q, i16, kb, i16 < a.group);
 
   // Two register buffers of G pages each, each refilled right after its pages
   // are consumed; past the pass's last item the last page is loaded again (a
@@ -912,6 +904,23 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   __builtin_amdgcn_sched_barrier(0);  // keep the groups' loads in order
   fill(gb, bb, G);
   __builtin_amdgcn_sched_barrier(0);
+  // fused append (after the first pages are in flight): the wave holding a
+  // unit's last page quantizes the sequence's newest token for that KV head,
+  // patches it into the page as loaded and stores it into the page (nobody
+  // else reads that slot during the call)
+  // (its stores wait until after the page loop, so that the loop's waits
+  // count page loads only)
+  if (a.append) {
+    for (int s = 0; s < ns; ++s) {
+      if (!readlane(s_last, s)) continue;
+      const int u = readlane(s_unit, s);
+      const bool ok = K::prepare_new(a, u / hkv, u % hkv, lds.nt + s * new_token_bytes(D), lane);
+      if (lane == s) s_patch = ok;
+    }
+  }
+  enter(0);
+  softmax_init(st);
+  kind.load_q(a, lds.q, i16, kb, i16 < a.group);
   for (int i = 0;; i += 2 * G) {
     if (!consume(ga, ba, i)) break;
     __builtin_amdgcn_sched_barrier(0);
@@ -925,6 +934,14 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   }
   stash_result<K>(a, st, lds.res + cs * a.group * (D + 2), i16, kb);
 
+  if (a.append) {
+    for (int s = 0; s < ns; ++s) {
+      const int hb = block_of(readlane(s_start, s) + readlane(s_n, s) - 1);
+      if (!readlane(s_patch, s) || hb < 0) continue;
+      K::store_new(a, lds.nt + s * new_token_bytes(D), (readlane(s_L, s) - 1) % kBlockSize, hb,
+                   lane);
+    }
+  }
   for (int s = 0; s < ns; ++s) {
     const int u = readlane(s_unit, s);
     write_result<D>(a, lds.res + s * a.group * (D + 2), u / hkv, u % hkv, wave + u,
