@@ -8,7 +8,8 @@ table or constant with the HIP library, and it imports nothing from it.
 
 Modules
 -------
-quant      per-token symmetric INT8 quantizer (one FP16 scale per row)
+quant      per-token symmetric INT8 quantizer (one FP16 scale per row), and
+           the static variant (one given FP32 scale per tensor)
 pages      the paged byte layout of INT8 and 16-bit KV pools, written from
            the layout contract, plus page write / gather helpers
 attention  decode attention over dequantized K/V with FP64 accumulation
@@ -36,10 +37,15 @@ from .quant import (  # noqa: F401
     ru16,
     quantize_rows,
     dequantize_rows,
+    check_static_scale,
+    shared_static_scale,
+    quantize_static,
+    dequantize_static,
 )
 from .pages import (  # noqa: F401
     KV_INT8_SYM,
     KV_16BIT,
+    KV_INT8_STATIC,
     page_bytes,
     int8_head_offsets,
     new_pool,
@@ -47,10 +53,13 @@ from .pages import (  # noqa: F401
     write_16bit_tokens,
     gather_int8_sequence,
     gather_16bit_sequence,
+    write_int8_static_tokens,
+    gather_int8_static_sequence,
 )
 from .attention import (  # noqa: F401
     bits_to_f32,
     attend_one_sequence,
     decode_int8_from_pool,
     decode_16bit_from_pool,
+    decode_int8_static_from_pool,
 )

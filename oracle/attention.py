@@ -26,8 +26,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .pages import gather_16bit_sequence, gather_int8_sequence
-from .quant import as_f32, dequantize_rows
+from .pages import gather_16bit_sequence, gather_int8_sequence, gather_int8_static_sequence
+from .quant import as_f32, dequantize_rows, dequantize_static
 
 
 def bits_to_f32(bits: np.ndarray, kv_dtype: str) -> np.ndarray:
@@ -113,6 +113,35 @@ def decode_16bit_from_pool(pool, block_tables, context_lens, q, sm_scale: float,
                                        num_kv_heads, head_dim, heads=gs)
         k = bits_to_f32(kb, kv_dtype)
         v = bits_to_f32(vb, kv_dtype)
+        for h in sorted(hs):
+            j = gs.index(h // group)
+            out[b, h] = attend_one_sequence(qf[b, h][None], k[:, j:j + 1], v[:, j:j + 1],
+                                            sm_scale)[0]
+    return out
+
+
+def decode_int8_static_from_pool(pool, block_tables, context_lens, q, sm_scale: float,
+                                 k_scale, v_scale, block_size: int, num_kv_heads: int,
+                                 head_dim: int, pairs=None) -> np.ndarray:
+    """Reference output of the paged decode over static-scale INT8 pages:
+    the same attention with k_t = cK_t * k_scale and v_t = cV_t * v_scale
+    (one scalar each for the whole layer; InfiniLM PR #553, "Summary";
+    TensorRT-LLM PR #18953, "Summary"). Returns float64 [B, Hq, D]; rows
+    outside ``pairs`` stay NaN."""
+    qf = as_f32(q)
+    B, hq, d = qf.shape
+    group = hq // num_kv_heads
+    out = np.full((B, hq, d), np.nan)
+    want = {}
+    for b, h in (pairs if pairs is not None else [(b, h) for b in range(B) for h in range(hq)]):
+        want.setdefault(b, set()).add(h)
+    for b, hs in want.items():
+        L = int(context_lens[b])
+        gs = sorted({h // group for h in hs})
+        kc, vc = gather_int8_static_sequence(pool, block_tables[b], L, block_size,
+                                             num_kv_heads, head_dim, heads=gs)
+        k = dequantize_static(kc, k_scale)
+        v = dequantize_static(vc, v_scale)
         for h in sorted(hs):
             j = gs.index(h // group)
             out[b, h] = attend_one_sequence(qf[b, h][None], k[:, j:j + 1], v[:, j:j + 1],

@@ -24,6 +24,15 @@ block of ``4*bs*D`` bytes, ``page_bytes = Hkv * 4*bs*D``):
     K   [bs][D]                       token-major
     V   [bs/4][D][4]                  same token grouping as the INT8 V codes
 
+INT8 page with static scales (one calibrated scalar for K and one for V per
+layer, held by the caller; no per-token scales in the page), per KV head h
+(head block of ``2*bs*D`` bytes, ``page_bytes = Hkv * 2*bs*D`` — half the
+16-bit page, the one-byte-per-element saving of InfiniLM PR #553, "Benchmark
+/ Performance Impact"):
+
+    K codes   int8  [bs][D]           token-major
+    V codes   int8  [bs/4][D][4]      as in the per-token INT8 page
+
 A token at logical position t of a sequence lives in physical page
 ``block_table[t // bs]`` at slot ``t % bs``; a write addresses it by
 ``slot = page * bs + t % bs`` (paged decode, MoE-Infinity PR #183, "What
@@ -36,6 +45,7 @@ import numpy as np
 
 KV_INT8_SYM = 1
 KV_16BIT = 2
+KV_INT8_STATIC = 3
 
 
 def page_bytes(kv_format: int, block_size: int, num_kv_heads: int, head_dim: int) -> int:
@@ -46,6 +56,8 @@ def page_bytes(kv_format: int, block_size: int, num_kv_heads: int, head_dim: int
         return num_kv_heads * (2 * block_size * head_dim + 4 * block_size)
     if kv_format == KV_16BIT:
         return num_kv_heads * 4 * block_size * head_dim
+    if kv_format == KV_INT8_STATIC:
+        return num_kv_heads * 2 * block_size * head_dim
     raise ValueError("page_bytes: unknown format")
 
 
@@ -187,3 +199,42 @@ def gather_16bit_sequence(pool: np.ndarray, block_table_row, context_len: int,
         k.append(words[base[:, None] + pos[:, None] * d + dd])
         v.append(words[base[:, None] + block_size * d + _v_index(pos[:, None], dd[None, :], d)])
     return np.stack(k, axis=1), np.stack(v, axis=1)
+
+
+def write_int8_static_tokens(pool: np.ndarray, k_codes, v_codes, slot_mapping,
+                             block_size: int) -> None:
+    """Store static-scale codes [T,Hkv,D] of K and V at their slots
+    (negative slot: padding, skipped; a repeated slot: the later token wins)."""
+    t_n, hkv, d = k_codes.shape
+    hb = 2 * block_size * d
+    if pool.shape[1] != hkv * hb:
+        raise ValueError("pool page size does not match the shape")
+    keep, blk, pos = _slot_split(slot_mapping, pool.shape[0], block_size)
+    flat = pool.reshape(-1)
+    kc = np.ascontiguousarray(k_codes).view(np.uint8)
+    vc = np.ascontiguousarray(v_codes).view(np.uint8)
+    dd = np.arange(d)
+    tt = np.nonzero(keep)[0]
+    p = pos[tt]
+    for h in range(hkv):
+        base = blk[tt] * pool.shape[1] + h * hb
+        flat[base[:, None] + p[:, None] * d + dd[None, :]] = kc[tt, h]
+        flat[base[:, None] + block_size * d + _v_index(p[:, None], dd[None, :], d)] = vc[tt, h]
+
+
+def gather_int8_static_sequence(pool: np.ndarray, block_table_row, context_len: int,
+                                block_size: int, num_kv_heads: int, head_dim: int,
+                                heads=None):
+    """Read back (k_codes, v_codes) [L, H, D] int8 of one sequence."""
+    d = head_dim
+    hb = 2 * block_size * d
+    heads = list(range(num_kv_heads)) if heads is None else list(heads)
+    blk, pos = _seq_positions(block_table_row, context_len, block_size)
+    flat = pool.reshape(-1)
+    dd = np.arange(d)
+    kc, vc = [], []
+    for h in heads:
+        base = blk * pool.shape[1] + h * hb
+        kc.append(flat[base[:, None] + pos[:, None] * d + dd])
+        vc.append(flat[base[:, None] + block_size * d + _v_index(pos[:, None], dd[None, :], d)])
+    return np.stack(kc, axis=1).view(np.int8), np.stack(vc, axis=1).view(np.int8)

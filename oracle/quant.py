@@ -98,3 +98,51 @@ def dequantize_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     MoE-Infinity page's oracle, "What landed", runtime-integration bullet).
     """
     return codes.astype(np.float32) * scales.astype(np.float32)[..., None]
+
+
+# ---------------------------------------------------------------------------
+# Static (per-tensor) scales
+# ---------------------------------------------------------------------------
+#
+# The other scheme on the pages: one calibrated scalar scale for all of K and
+# one for all of V of a layer (InfiniLM PR #553, "Summary", bullets on the
+# kv_cache_k_scale / kv_cache_v_scale parameters and "Notes for Reviewers";
+# TensorRT-LLM PR #18953, "Summary": paired positive finite scalar k_scale /
+# v_scale in float32, whose maximum serves as one shared K/V scale). The pages
+# give the scales and their validity (finite, positive) but not the element
+# formula; the reading taken is the per-token scheme's formula with the given
+# scale: code = clip(rint(fl32(x / s)), -127, 127), x / s an IEEE binary32
+# division, round half to even, symmetric range (no -128; zero point 0). Values
+# beyond 127.5 * s saturate: that clipping is part of the static scheme.
+
+
+def check_static_scale(s) -> np.float32:
+    """The scale as binary32; raises unless it is finite and > 0 (the
+    validity rule of TensorRT-LLM PR #18953, "Summary")."""
+    s32 = np.float32(s)
+    if not np.isfinite(s32) or not s32 > 0:
+        raise ValueError("static scale must be finite and positive")
+    return s32
+
+
+def shared_static_scale(k_scale, v_scale) -> np.float32:
+    """One scale for both K and V: the larger of the two (TensorRT-LLM
+    PR #18953, "Summary": the maximum of the paired scales feeds the shared
+    K/V scale)."""
+    return np.float32(max(check_static_scale(k_scale), check_static_scale(v_scale)))
+
+
+def quantize_static(x, s) -> np.ndarray:
+    """Codes of ``x`` (any shape) under the static scale ``s``:
+    clip(rint(fl32(x / s)), -127, 127) as int8."""
+    s32 = check_static_scale(s)
+    x = as_f32(x)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("quantize_static: NaN/Inf input is outside the contract")
+    q = np.divide(x, s32, dtype=np.float32)
+    return np.clip(np.rint(q), -127, 127).astype(np.int8)
+
+
+def dequantize_static(codes: np.ndarray, s) -> np.ndarray:
+    """code * s in FP64 (exact: 8 bits times a 24-bit significand)."""
+    return codes.astype(np.float64) * float(check_static_scale(s))

@@ -172,3 +172,85 @@ def test_attention_mutant_is_caught(name, monkeypatch):
 
 def test_unmutated_attention_passes_the_same_pins():
     assert not _caught(ATT_PINS)
+
+
+# ---- static (per-tensor) scales -------------------------------------------
+from tests import test_oracle_static as TS  # noqa: E402
+
+
+def _static(divide=True, exact_quotient=False, round_fn=np.rint, lo=-127):
+    def q(x, s):
+        s32 = oquant.check_static_scale(s)
+        x = oquant.as_f32(x)
+        if exact_quotient:
+            qq = x.astype(np.float64) / np.float64(s32)
+        elif divide:
+            qq = np.divide(x, s32, dtype=np.float32)
+        else:
+            qq = x * (np.float32(1) / s32)
+        return np.clip(round_fn(qq), lo, 127).astype(np.int8)
+    return q
+
+
+STATIC_MUTANTS = {
+    "reciprocal multiply": _static(divide=False),
+    "quotient rounded exactly, not in binary32": _static(exact_quotient=True),
+    "round half away from zero": _static(round_fn=lambda v: np.sign(v) * np.floor(np.abs(v) + 0.5)),
+    "truncation": _static(round_fn=np.trunc),
+    "-128 allowed": _static(lo=-128),
+    "multiply by the scale": lambda x, s: np.clip(np.rint(oquant.as_f32(x) * np.float32(s)),
+                                                  -127, 127).astype(np.int8),
+}
+
+STATIC_PINS = [
+    lambda: TS.test_worked_examples(read_golden),
+    lambda: TS.test_codes_match_exact_rational_brute_force("f16", 0.0371),
+    lambda: TS.test_saturation_and_no_minus_128(),
+]
+
+
+@pytest.mark.parametrize("name", sorted(STATIC_MUTANTS))
+def test_static_quantizer_mutant_is_caught(name, monkeypatch):
+    monkeypatch.setattr(oracle, "quantize_static", STATIC_MUTANTS[name])
+    assert _caught(STATIC_PINS), name
+
+
+def test_unmutated_static_quantizer_passes_the_same_pins():
+    assert not _caught(STATIC_PINS)
+
+
+def _dequant_static_v_uses_k_scale():
+    calls = []
+
+    def f(codes, s):
+        calls.append(s)
+        return codes.astype(np.float64) * float(oquant.check_static_scale(calls[0]))
+    return f
+
+
+STATIC_ATT_MUTANTS = {
+    "V dequantized with the K scale": ("dequantize_static", _dequant_static_v_uses_k_scale),
+    "static V layout token-major": ("_v_index", lambda: _v_index_token_major),
+    "shared scale = min": ("shared_static_scale", lambda: lambda k, v: np.float32(min(k, v))),
+}
+
+STATIC_ATT_PINS = [
+    lambda: TS.test_static_decode_matches_pure_python_brute_force(33, 8, 2, 128),
+    lambda: TS.test_static_decode_closed_forms(),
+    lambda: TS.test_static_byte_offsets_by_hand(),
+    lambda: TS.test_scale_validity_and_shared_scale(),
+]
+
+
+@pytest.mark.parametrize("name", sorted(STATIC_ATT_MUTANTS))
+def test_static_attention_mutant_is_caught(name, monkeypatch):
+    attr, make = STATIC_ATT_MUTANTS[name]
+    fn = make()
+    for mod in (oatt, oquant, opages, oracle):
+        if hasattr(mod, attr):
+            monkeypatch.setattr(mod, attr, fn)
+    assert _caught(STATIC_ATT_PINS), name
+
+
+def test_unmutated_static_attention_passes_the_same_pins():
+    assert not _caught(STATIC_ATT_PINS)
