@@ -24,6 +24,15 @@
  *    "Scope & fallback").
  * 3. paged_attn_decode_fp16 — the same decode over 16-bit (fp16 or bf16) K/V
  *    pages with the same block-table layout, as a control.
+ * 4. Static-scale variant — kv_quant_int8_static_write and
+ *    paged_attn_decode_int8_static: one calibrated FP32 scalar for all of K
+ *    and one for all of V of a layer, held by the caller, and codes-only
+ *    pages (InfiniLM PR #553, "Summary" and "Notes for Reviewers";
+ *    TensorRT-LLM PR #18953, "Summary"). code = clamp(round_half_even(
+ *    fl32(x / scale)), -127, 127); values beyond 127.5 * scale saturate.
+ *    The pages do not write the element rule out; this is the per-token
+ *    rule with the given scale. A shared K/V scale is the case
+ *    k_scale == v_scale (for instance the larger of two calibrated scales).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -62,6 +71,11 @@
  *   (16, 2, 64). The V codes are grouped four tokens at a time so that one
  *   32-bit word holds one dimension of four consecutive tokens, which is the
  *   operand shape of the matrix instructions the reader uses.
+ * Static-scale INT8 page (kv_format PDAKV_KV_INT8_STATIC), for each KV head h,
+ * a head block of 2*16*D bytes:
+ *     +0          K codes  int8 [16][D]        token-major
+ *     +16*D       V codes  int8 [4][D][4]      as in the per-token page
+ *   page_bytes = Hkv * 32 * D: 32,768 for (16, 8, 128), half the 16-bit page.
  * 16-bit page (kv_format PDAKV_KV_16BIT), for each KV head h, 4*16*D bytes:
  *     +0          K  [16][D]                    token-major
  *     +32*D       V  [4][D][4]                  element (p/4)*4*D + 4*d + p%4
@@ -92,8 +106,9 @@ extern "C" {
 #define PDAKV_DTYPE_BF16 2
 
 /* ---- KV page formats -------------------------------------------------- */
-#define PDAKV_KV_INT8_SYM 1
-#define PDAKV_KV_16BIT    2
+#define PDAKV_KV_INT8_SYM    1
+#define PDAKV_KV_16BIT       2
+#define PDAKV_KV_INT8_STATIC 3
 
 /* ---- bits OR-ed into the optional device error flag ------------------- */
 #define PDAKV_EFLAG_SLOT_RANGE    1 /* slot_id >= num_blocks * block_size   */
@@ -132,16 +147,16 @@ int pdakv_capabilities(uint32_t* flags_out);
  * the actual context lengths evenly over *num_waves 64-lane waves (at least
  * 4 items each, a unit that spans several waves is merged afterwards).
  * *max_pages_per_wave is the share when every sequence is at
- * max_context_len (<= 128). kv_format is PDAKV_KV_INT8_SYM or
- * PDAKV_KV_16BIT. Either output pointer may be NULL. Returns
+ * max_context_len (<= 128). kv_format is one of the PDAKV_KV_* formats.
+ * Either output pointer may be NULL. Returns
  * PDAKV_ERR_INVALID_ARG for a bad format or negative sizes and
  * PDAKV_ERR_UNSUPPORTED above 2^30 items. Host arithmetic only. */
 int pdakv_decode_plan(int kv_format, int num_seqs, int num_kv_heads, int max_context_len,
                       int* num_waves, int* max_pages_per_wave);
 
 /* Device workspace the decode calls need for these sizes (0 when
- * max_context_len or num_seqs is 0). The same value serves the INT8 and the
- * 16-bit decode. Layout: float partials
+ * max_context_len or num_seqs is 0). The same value serves every decode
+ * entry point. Layout: float partials
  * [num_waves + num_seqs * num_kv_heads][num_q_heads / num_kv_heads][head_dim + 2]
  * (num_waves from the INT8 plan; the region padded to a multiple of 16
  * bytes), then int32 [num_seqs * num_kv_heads][2] merge records. */
@@ -264,6 +279,53 @@ int paged_attn_decode_fp16_append(
     const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
     int max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
     int32_t* err_flag, void* stream);
+
+/* Quantize-on-write with static scales (InfiniLM PR #553 "fix: #552 int8 kv
+ * cache quantization cannot be enabled", "Summary": per-tensor
+ * kv_cache_k_scale / kv_cache_v_scale; TensorRT-LLM PR #18953 "Add calibrated
+ * INT8 KV cache to PyTorch backend", "Summary": positive finite float32
+ * k_scale / v_scale). Same arguments as kv_quant_int8_sym_write plus
+ *   k_scale, v_scale   host float, the layer's scales; each must be finite
+ *                      and > 0, else PDAKV_ERR_INVALID_ARG.
+ * kv_pool is a PDAKV_KV_INT8_STATIC pool. Every element gets
+ * clamp(round_half_even(fl32(x / scale)), -127, 127); nothing is flagged for
+ * saturation (it is part of the scheme). */
+int kv_quant_int8_static_write(const void* k_src, const void* v_src, int src_dtype,
+                               int64_t num_tokens, int num_kv_heads, int head_dim,
+                               int64_t k_stride_tok, int64_t k_stride_head, int64_t k_stride_dim,
+                               int64_t v_stride_tok, int64_t v_stride_head, int64_t v_stride_dim,
+                               float k_scale, float v_scale, const int32_t* slot_mapping,
+                               void* kv_pool, int64_t num_blocks, int block_size,
+                               int32_t* err_flag, void* stream);
+
+/* Paged decode over static-scale INT8 pages: the attention of
+ * paged_attn_decode_int8 with k_t = code * k_scale and v_t = code * v_scale.
+ * Same arguments as paged_attn_decode_int8 plus k_scale and v_scale (host
+ * float, finite and > 0, and sm_scale * k_scale finite, else
+ * PDAKV_ERR_INVALID_ARG); kv_pool is a PDAKV_KV_INT8_STATIC pool. */
+int paged_attn_decode_int8_static(void* out, int out_dtype, int64_t out_stride_seq,
+                                  int64_t out_stride_head, const void* q, int q_dtype,
+                                  int64_t q_stride_seq, int64_t q_stride_head,
+                                  const void* kv_pool, int64_t num_blocks, int block_size,
+                                  const int32_t* block_tables, int64_t block_table_stride,
+                                  const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int max_context_len,
+                                  float sm_scale, float k_scale, float v_scale, void* workspace,
+                                  size_t workspace_bytes, int32_t* err_flag, void* stream);
+
+/* The fused append + decode step over static-scale pages:
+ * kv_quant_int8_static_write of the newest tokens (as for
+ * paged_attn_decode_int8_append), then paged_attn_decode_int8_static. Same
+ * arguments as paged_attn_decode_int8_append plus k_scale and v_scale. */
+int paged_attn_decode_int8_static_append(
+    void* out, int out_dtype, int64_t out_stride_seq, int64_t out_stride_head, const void* q,
+    int q_dtype, int64_t q_stride_seq, int64_t q_stride_head, const void* k_new,
+    const void* v_new, int64_t k_stride_seq, int64_t k_stride_head, int64_t k_stride_dim,
+    int64_t v_stride_seq, int64_t v_stride_head, int64_t v_stride_dim, void* kv_pool,
+    int64_t num_blocks, int block_size, const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int max_context_len, float sm_scale, float k_scale, float v_scale, void* workspace,
+    size_t workspace_bytes, int32_t* err_flag, void* stream);
 
 #ifdef __cplusplus
 }

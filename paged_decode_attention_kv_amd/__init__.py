@@ -23,15 +23,19 @@ from ._lib import (  # noqa: F401
     ERR_WORKSPACE,
     EXPORTED,
     KV_16BIT,
+    KV_INT8_STATIC,
     KV_INT8_SYM,
     LIB_PATH,
     PdakvError,
+    kv_quant_int8_static_write,
     kv_quant_int8_sym_write,
     kv_write_16bit,
     paged_attn_decode_fp16,
     paged_attn_decode_fp16_append,
     paged_attn_decode_int8,
     paged_attn_decode_int8_append,
+    paged_attn_decode_int8_static,
+    paged_attn_decode_int8_static_append,
     pdakv_capabilities,
     pdakv_decode_plan,
     pdakv_decode_workspace_bytes,

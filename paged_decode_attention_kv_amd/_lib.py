@@ -32,7 +32,7 @@ ERR_WORKSPACE = -4
 ERR_HIP = -5
 ERR_NO_DEVICE = -6
 DTYPE_F32, DTYPE_F16, DTYPE_BF16 = 0, 1, 2
-KV_INT8_SYM, KV_16BIT = 1, 2
+KV_INT8_SYM, KV_16BIT, KV_INT8_STATIC = 1, 2, 3
 EFLAG_SLOT_RANGE, EFLAG_BLOCK_RANGE, EFLAG_CONTEXT_RANGE, EFLAG_SCALE_RANGE = 1, 2, 4, 8
 CAP_GFX950 = 1
 
@@ -61,6 +61,13 @@ _SIGS["paged_attn_decode_int8_append"] = (
     [_c_i64] * 6 + [_c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_int, _c_int, _c_int, _c_int,
                     _c_int, _c_f, _c_vp, ctypes.c_size_t, _c_vp, _c_vp])
 _SIGS["paged_attn_decode_fp16_append"] = _SIGS["paged_attn_decode_int8_append"]
+# static scales: the two floats go before slot_mapping (write) / workspace (decode)
+_w = _SIGS["kv_quant_int8_sym_write"][1]
+_SIGS["kv_quant_int8_static_write"] = (_c_int, _w[:12] + [_c_f, _c_f] + _w[12:])
+_d = _SIGS["paged_attn_decode_int8"][1]
+_SIGS["paged_attn_decode_int8_static"] = (_c_int, _d[:20] + [_c_f, _c_f] + _d[20:])
+_a = _SIGS["paged_attn_decode_int8_append"][1]
+_SIGS["paged_attn_decode_int8_static_append"] = (_c_int, _a[:28] + [_c_f, _c_f] + _a[28:])
 
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -133,14 +140,15 @@ def pdakv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: 
 
 # ---- device entry points --------------------------------------------------
 
-def _write(fn_name, k, v, slot_mapping, kv_pool, num_blocks, block_size, err_flag, stream):
+def _write(fn_name, k, v, slot_mapping, kv_pool, num_blocks, block_size, err_flag, stream,
+           scales=()):
     T, hkv, d = k.shape
     if tuple(v.shape) != (T, hkv, d) or v.dtype != k.dtype:
         raise ValueError("k and v must have the same shape and dtype")
     st = getattr(_lib, fn_name)(
         _ptr(k), _ptr(v), _dtype_code(k.dtype), T, hkv, d,
         k.stride(0), k.stride(1), k.stride(2), v.stride(0), v.stride(1), v.stride(2),
-        _ptr(slot_mapping), _ptr(kv_pool), num_blocks, block_size, _ptr(err_flag),
+        *scales, _ptr(slot_mapping), _ptr(kv_pool), num_blocks, block_size, _ptr(err_flag),
         _stream(stream))
     _check(fn_name, st)
 
@@ -160,7 +168,7 @@ def kv_write_16bit(k, v, slot_mapping, kv_pool, num_blocks: int, block_size: int
 
 
 def _decode(fn_name, out, q, kv_pool, num_blocks, block_tables, context_lens, num_kv_heads,
-            max_context_len, sm_scale, workspace, block_size, err_flag, stream):
+            max_context_len, sm_scale, workspace, block_size, err_flag, stream, scales=()):
     B, hq, d = q.shape
     if q.stride(2) != 1 or out.stride(2) != 1:
         raise ValueError("the head_dim stride of q and out must be 1")
@@ -172,7 +180,7 @@ def _decode(fn_name, out, q, kv_pool, num_blocks, block_tables, context_lens, nu
         _ptr(q), _dtype_code(q.dtype), q.stride(0), q.stride(1),
         _ptr(kv_pool), num_blocks, block_size, _ptr(block_tables), block_tables.stride(0),
         _ptr(context_lens), B, hq, num_kv_heads, d, max_context_len, float(sm_scale),
-        _ptr(workspace), ws_bytes, _ptr(err_flag), _stream(stream))
+        *scales, _ptr(workspace), ws_bytes, _ptr(err_flag), _stream(stream))
     _check(fn_name, st)
 
 
@@ -196,7 +204,7 @@ def paged_attn_decode_fp16(out, q, kv_pool, num_blocks: int, block_tables, conte
 
 def _decode_append(fn_name, out, q, k_new, v_new, kv_pool, num_blocks, block_tables,
                    context_lens, num_kv_heads, max_context_len, sm_scale, workspace, block_size,
-                   err_flag, stream):
+                   err_flag, stream, scales=()):
     B, hq, d = q.shape
     if q.stride(2) != 1 or out.stride(2) != 1:
         raise ValueError("the head_dim stride of q and out must be 1")
@@ -214,7 +222,7 @@ def _decode_append(fn_name, out, q, k_new, v_new, kv_pool, num_blocks, block_tab
         v_new.stride(0), v_new.stride(1), v_new.stride(2),
         _ptr(kv_pool), num_blocks, block_size, _ptr(block_tables), block_tables.stride(0),
         _ptr(context_lens), B, hq, num_kv_heads, d, max_context_len, float(sm_scale),
-        _ptr(workspace), ws_bytes, _ptr(err_flag), _stream(stream))
+        *scales, _ptr(workspace), ws_bytes, _ptr(err_flag), _stream(stream))
     _check(fn_name, st)
 
 
@@ -237,3 +245,36 @@ def paged_attn_decode_fp16_append(out, q, k_new, v_new, kv_pool, num_blocks: int
     _decode_append("paged_attn_decode_fp16_append", out, q, k_new, v_new, kv_pool, num_blocks,
                    block_tables, context_lens, num_kv_heads, max_context_len, sm_scale,
                    workspace, block_size, err_flag, stream)
+
+
+# ---- static (per-tensor) scales --------------------------------------------
+
+def kv_quant_int8_static_write(k, v, slot_mapping, kv_pool, num_blocks: int, k_scale: float,
+                               v_scale: float, block_size: int = 16, err_flag=None,
+                               stream=None) -> None:
+    """Quantize k, v [T, Hkv, D] with the layer's scalar scales into a
+    static-scale (codes-only) INT8 pool."""
+    _write("kv_quant_int8_static_write", k, v, slot_mapping, kv_pool, num_blocks, block_size,
+           err_flag, stream, scales=(float(k_scale), float(v_scale)))
+
+
+def paged_attn_decode_int8_static(out, q, kv_pool, num_blocks: int, block_tables, context_lens,
+                                  num_kv_heads: int, max_context_len: int, sm_scale: float,
+                                  k_scale: float, v_scale: float, workspace=None,
+                                  block_size: int = 16, err_flag=None, stream=None) -> None:
+    """Decode over static-scale INT8 pages; writes out [B, Hq, D]."""
+    _decode("paged_attn_decode_int8_static", out, q, kv_pool, num_blocks, block_tables,
+            context_lens, num_kv_heads, max_context_len, sm_scale, workspace, block_size,
+            err_flag, stream, scales=(float(k_scale), float(v_scale)))
+
+
+def paged_attn_decode_int8_static_append(out, q, k_new, v_new, kv_pool, num_blocks: int,
+                                         block_tables, context_lens, num_kv_heads: int,
+                                         max_context_len: int, sm_scale: float, k_scale: float,
+                                         v_scale: float, workspace=None, block_size: int = 16,
+                                         err_flag=None, stream=None) -> None:
+    """The fused append + decode step over static-scale INT8 pages."""
+    _decode_append("paged_attn_decode_int8_static_append", out, q, k_new, v_new, kv_pool,
+                   num_blocks, block_tables, context_lens, num_kv_heads, max_context_len,
+                   sm_scale, workspace, block_size, err_flag, stream,
+                   scales=(float(k_scale), float(v_scale)))

@@ -19,8 +19,15 @@ using pdakv::WriteArgs;
 // SIMD the kernel's register budget allows.
 int64_t resident_waves(int kv_format) {
   return int64_t{pdakv::kCUs} * 4 *
-         (kv_format == PDAKV_KV_INT8_SYM ? pdakv::kInt8WavesPerSimd : pdakv::k16WavesPerSimd);
+         (kv_format == PDAKV_KV_16BIT ? pdakv::k16WavesPerSimd : pdakv::kInt8WavesPerSimd);
 }
+
+bool known_format(int f) {
+  return f == PDAKV_KV_INT8_SYM || f == PDAKV_KV_16BIT || f == PDAKV_KV_INT8_STATIC;
+}
+
+// A static scale must be finite and positive.
+bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
 
 // Largest item count (sequence x KV head x page) a launch may hold, so that
 // item indexes and wave * pages products stay in int32 on the device.
@@ -64,7 +71,7 @@ int merge_waves(int num_seqs, int num_kv_heads, int max_context_len, int64_t wav
 
 // Partial results region of the decode workspace (a multiple of 16 bytes):
 // [waves + units][G][D + 2] floats. The INT8 plan has the most waves; its
-// slots serve the 16-bit call too.
+// slots serve the other formats too.
 size_t partials_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                       int max_context_len) {
   const int64_t v = plan_waves(PDAKV_KV_INT8_SYM, num_seqs, num_kv_heads, max_context_len);
@@ -138,9 +145,13 @@ struct AppendRows {
   int64_t kst = 0, ksh = 0, ksd = 0, vst = 0, vsh = 0, vsd = 0;
 };
 
-template <bool Int8>
-int decode_common(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, const void* q,
-                  int q_dtype, int64_t q_ss, int64_t q_sh, const AppendRows* app,
+// The layer's K and V scales of the static-scale format (1, 1 otherwise).
+struct Scales {
+  float k = 1.f, v = 1.f;
+};
+
+int decode_common(int fmt, Scales sc, void* out, int out_dtype, int64_t out_ss, int64_t out_sh,
+                  const void* q, int q_dtype, int64_t q_ss, int64_t q_sh, const AppendRows* app,
                   const void* kv_pool, int64_t num_blocks, int block_size,
                   const int32_t* block_tables, int64_t bt_stride, const int32_t* context_lens,
                   int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
@@ -151,6 +162,9 @@ int decode_common(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, cons
                         num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                         sm_scale, workspace, workspace_bytes);
   if (st != PDAKV_OK) return st;
+  const double scale_log2 = static_cast<double>(sm_scale) * sc.k * 1.4426950408889634;
+  if (!valid_scale(sc.k) || !valid_scale(sc.v) || !std::isfinite(static_cast<float>(scale_log2)))
+    return PDAKV_ERR_INVALID_ARG;
   if (app) {
     if (app->kst < 0 || app->ksh < 0 || app->ksd < 0 || app->vst < 0 || app->vsh < 0 ||
         app->vsd < 0)
@@ -169,8 +183,8 @@ int decode_common(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, cons
   a.q_vec16 = aligned16(q) && q_ss % 8 == 0 && q_sh % 8 == 0;
   a.pool = static_cast<uint8_t*>(const_cast<void*>(kv_pool));
   a.num_blocks = num_blocks;
-  a.page_bytes = static_cast<int64_t>(pdakv_page_bytes(
-      Int8 ? PDAKV_KV_INT8_SYM : PDAKV_KV_16BIT, block_size, num_kv_heads, head_dim));
+  a.page_bytes =
+      static_cast<int64_t>(pdakv_page_bytes(fmt, block_size, num_kv_heads, head_dim));
   a.bt = block_tables;
   a.bt_stride = bt_stride;
   a.ctx = context_lens;
@@ -179,9 +193,11 @@ int decode_common(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, cons
   a.num_kv_heads = num_kv_heads;
   a.group = num_q_heads / num_kv_heads;
   a.max_ctx = max_context_len;
-  a.scale_log2 = sm_scale * 1.4426950408889634f;
-  a.num_waves = static_cast<int>(plan_waves(Int8 ? PDAKV_KV_INT8_SYM : PDAKV_KV_16BIT,
-                                             num_seqs, num_kv_heads, max_context_len));
+  a.scale_log2 = static_cast<float>(scale_log2);
+  a.out_mul = fmt == PDAKV_KV_INT8_STATIC ? sc.v : 1.f;
+  a.k_scale = sc.k;
+  a.v_scale = sc.v;
+  a.num_waves = static_cast<int>(plan_waves(fmt, num_seqs, num_kv_heads, max_context_len));
   a.merge_waves = merge_waves(num_seqs, num_kv_heads, max_context_len, a.num_waves);
   {
     // LDS staging per decode pass and segment: the unit's q rows (16-bit),
@@ -210,19 +226,24 @@ int decode_common(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, cons
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = q_dtype == PDAKV_DTYPE_BF16;
-  return hip_status(Int8 ? pdakv::launch_decode_int8(a, head_dim, bf16, s)
-                         : pdakv::launch_decode_16bit(a, head_dim, bf16, s));
+  switch (fmt) {
+    case PDAKV_KV_INT8_SYM: return hip_status(pdakv::launch_decode_int8(a, head_dim, bf16, s));
+    case PDAKV_KV_INT8_STATIC:
+      return hip_status(pdakv::launch_decode_int8_static(a, head_dim, bf16, s));
+    default: return hip_status(pdakv::launch_decode_16bit(a, head_dim, bf16, s));
+  }
 }
 
-template <bool Int8>
-int write_common(const void* k_src, const void* v_src, int src_dtype, int64_t num_tokens,
-                 int num_kv_heads, int head_dim, int64_t kst, int64_t ksh, int64_t ksd,
-                 int64_t vst, int64_t vsh, int64_t vsd, const int32_t* slot_mapping,
-                 void* kv_pool, int64_t num_blocks, int block_size, int32_t* err_flag,
-                 void* stream) {
+int write_common(int fmt, Scales sc, const void* k_src, const void* v_src, int src_dtype,
+                 int64_t num_tokens, int num_kv_heads, int head_dim, int64_t kst, int64_t ksh,
+                 int64_t ksd, int64_t vst, int64_t vsh, int64_t vsd,
+                 const int32_t* slot_mapping, void* kv_pool, int64_t num_blocks, int block_size,
+                 int32_t* err_flag, void* stream) {
   int st = check_write(k_src, v_src, src_dtype, num_tokens, num_kv_heads, head_dim, kst, ksh,
                        ksd, vst, vsh, vsd, slot_mapping, kv_pool, num_blocks, block_size);
-  if (st != PDAKV_OK || num_tokens == 0) return st;
+  if (st != PDAKV_OK) return st;
+  if (!valid_scale(sc.k) || !valid_scale(sc.v)) return PDAKV_ERR_INVALID_ARG;
+  if (num_tokens == 0) return st;
   if (num_tokens * num_kv_heads / 4 >= INT32_MAX) return PDAKV_ERR_UNSUPPORTED;
   WriteArgs a{};
   a.k = k_src;
@@ -238,13 +259,19 @@ int write_common(const void* k_src, const void* v_src, int src_dtype, int64_t nu
   a.slots = slot_mapping;
   a.pool = static_cast<uint8_t*>(kv_pool);
   a.num_blocks = num_blocks;
-  a.page_bytes = static_cast<int64_t>(pdakv_page_bytes(
-      Int8 ? PDAKV_KV_INT8_SYM : PDAKV_KV_16BIT, block_size, num_kv_heads, head_dim));
+  a.page_bytes =
+      static_cast<int64_t>(pdakv_page_bytes(fmt, block_size, num_kv_heads, head_dim));
+  a.k_scale = sc.k;
+  a.v_scale = sc.v;
   a.err = err_flag;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(Int8 ? pdakv::launch_quant_write_int8(a, head_dim,
-                                                          src_dtype == PDAKV_DTYPE_BF16, s)
-                         : pdakv::launch_write_16bit(a, head_dim, s));
+  const bool bf16 = src_dtype == PDAKV_DTYPE_BF16;
+  switch (fmt) {
+    case PDAKV_KV_INT8_SYM: return hip_status(pdakv::launch_quant_write_int8(a, head_dim, bf16, s));
+    case PDAKV_KV_INT8_STATIC:
+      return hip_status(pdakv::launch_quant_write_static(a, head_dim, bf16, s));
+    default: return hip_status(pdakv::launch_write_16bit(a, head_dim, s));
+  }
 }
 
 }  // namespace
@@ -272,6 +299,7 @@ size_t pdakv_page_bytes(int kv_format, int block_size, int num_kv_heads, int hea
   const size_t h = static_cast<size_t>(num_kv_heads);
   if (kv_format == PDAKV_KV_INT8_SYM) return h * (2 * bs * d + 4 * bs);
   if (kv_format == PDAKV_KV_16BIT) return h * 4 * bs * d;
+  if (kv_format == PDAKV_KV_INT8_STATIC) return h * 2 * bs * d;
   return 0;
 }
 
@@ -291,8 +319,7 @@ int pdakv_capabilities(uint32_t* flags_out) {
 
 int pdakv_decode_plan(int kv_format, int num_seqs, int num_kv_heads, int max_context_len,
                       int* num_waves, int* max_pages_per_wave) {
-  if (kv_format != PDAKV_KV_INT8_SYM && kv_format != PDAKV_KV_16BIT)
-    return PDAKV_ERR_INVALID_ARG;
+  if (!known_format(kv_format)) return PDAKV_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0) return PDAKV_ERR_INVALID_ARG;
   if (item_bound(num_seqs, num_kv_heads, max_context_len) > kMaxItems)
     return PDAKV_ERR_UNSUPPORTED;
@@ -320,10 +347,11 @@ int kv_quant_int8_sym_write(const void* k_src, const void* v_src, int src_dtype,
                             int64_t v_stride_tok, int64_t v_stride_head, int64_t v_stride_dim,
                             const int32_t* slot_mapping, void* kv_pool, int64_t num_blocks,
                             int block_size, int32_t* err_flag, void* stream) {
-  return write_common<true>(k_src, v_src, src_dtype, num_tokens, num_kv_heads, head_dim,
-                            k_stride_tok, k_stride_head, k_stride_dim, v_stride_tok,
-                            v_stride_head, v_stride_dim, slot_mapping, kv_pool, num_blocks,
-                            block_size, err_flag, stream);
+  return write_common(PDAKV_KV_INT8_SYM, Scales{},
+                      k_src, v_src, src_dtype, num_tokens, num_kv_heads, head_dim,
+                      k_stride_tok, k_stride_head, k_stride_dim, v_stride_tok,
+                      v_stride_head, v_stride_dim, slot_mapping, kv_pool, num_blocks,
+                      block_size, err_flag, stream);
 }
 
 int kv_write_16bit(const void* k_src, const void* v_src, int src_dtype, int64_t num_tokens,
@@ -331,10 +359,11 @@ int kv_write_16bit(const void* k_src, const void* v_src, int src_dtype, int64_t 
                    int64_t k_stride_dim, int64_t v_stride_tok, int64_t v_stride_head,
                    int64_t v_stride_dim, const int32_t* slot_mapping, void* kv_pool,
                    int64_t num_blocks, int block_size, int32_t* err_flag, void* stream) {
-  return write_common<false>(k_src, v_src, src_dtype, num_tokens, num_kv_heads, head_dim,
-                             k_stride_tok, k_stride_head, k_stride_dim, v_stride_tok,
-                             v_stride_head, v_stride_dim, slot_mapping, kv_pool, num_blocks,
-                             block_size, err_flag, stream);
+  return write_common(PDAKV_KV_16BIT, Scales{},
+                      k_src, v_src, src_dtype, num_tokens, num_kv_heads, head_dim,
+                      k_stride_tok, k_stride_head, k_stride_dim, v_stride_tok,
+                      v_stride_head, v_stride_dim, slot_mapping, kv_pool, num_blocks,
+                      block_size, err_flag, stream);
 }
 
 int paged_attn_decode_int8(void* out, int out_dtype, int64_t out_stride_seq,
@@ -345,11 +374,12 @@ int paged_attn_decode_int8(void* out, int out_dtype, int64_t out_stride_seq,
                            int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                            int max_context_len, float sm_scale, void* workspace,
                            size_t workspace_bytes, int32_t* err_flag, void* stream) {
-  return decode_common<true>(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
-                             q_stride_seq, q_stride_head, nullptr, kv_pool, num_blocks, block_size,
-                             block_tables, block_table_stride, context_lens, num_seqs,
-                             num_q_heads, num_kv_heads, head_dim, max_context_len, sm_scale,
-                             workspace, workspace_bytes, err_flag, stream);
+  return decode_common(PDAKV_KV_INT8_SYM, Scales{},
+                       out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
+                       q_stride_seq, q_stride_head, nullptr, kv_pool, num_blocks, block_size,
+                       block_tables, block_table_stride, context_lens, num_seqs,
+                       num_q_heads, num_kv_heads, head_dim, max_context_len, sm_scale,
+                       workspace, workspace_bytes, err_flag, stream);
 }
 
 int paged_attn_decode_fp16(void* out, int out_dtype, int64_t out_stride_seq,
@@ -360,11 +390,12 @@ int paged_attn_decode_fp16(void* out, int out_dtype, int64_t out_stride_seq,
                            int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                            int max_context_len, float sm_scale, void* workspace,
                            size_t workspace_bytes, int32_t* err_flag, void* stream) {
-  return decode_common<false>(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
-                              q_stride_seq, q_stride_head, nullptr, kv_pool, num_blocks, block_size,
-                              block_tables, block_table_stride, context_lens, num_seqs,
-                              num_q_heads, num_kv_heads, head_dim, max_context_len, sm_scale,
-                              workspace, workspace_bytes, err_flag, stream);
+  return decode_common(PDAKV_KV_16BIT, Scales{},
+                       out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
+                       q_stride_seq, q_stride_head, nullptr, kv_pool, num_blocks, block_size,
+                       block_tables, block_table_stride, context_lens, num_seqs,
+                       num_q_heads, num_kv_heads, head_dim, max_context_len, sm_scale,
+                       workspace, workspace_bytes, err_flag, stream);
 }
 
 int paged_attn_decode_int8_append(
@@ -385,11 +416,12 @@ int paged_attn_decode_int8_append(
   app.vst = v_stride_seq;
   app.vsh = v_stride_head;
   app.vsd = v_stride_dim;
-  return decode_common<true>(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
-                             q_stride_seq, q_stride_head, &app, kv_pool, num_blocks, block_size,
-                             block_tables, block_table_stride, context_lens, num_seqs,
-                             num_q_heads, num_kv_heads, head_dim, max_context_len, sm_scale,
-                             workspace, workspace_bytes, err_flag, stream);
+  return decode_common(PDAKV_KV_INT8_SYM, Scales{},
+                       out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
+                       q_stride_seq, q_stride_head, &app, kv_pool, num_blocks, block_size,
+                       block_tables, block_table_stride, context_lens, num_seqs,
+                       num_q_heads, num_kv_heads, head_dim, max_context_len, sm_scale,
+                       workspace, workspace_bytes, err_flag, stream);
 }
 
 int paged_attn_decode_fp16_append(
@@ -410,11 +442,67 @@ int paged_attn_decode_fp16_append(
   app.vst = v_stride_seq;
   app.vsh = v_stride_head;
   app.vsd = v_stride_dim;
-  return decode_common<false>(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
-                              q_stride_seq, q_stride_head, &app, kv_pool, num_blocks,
-                              block_size, block_tables, block_table_stride, context_lens,
-                              num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                              sm_scale, workspace, workspace_bytes, err_flag, stream);
+  return decode_common(PDAKV_KV_16BIT, Scales{},
+                       out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
+                       q_stride_seq, q_stride_head, &app, kv_pool, num_blocks,
+                       block_size, block_tables, block_table_stride, context_lens,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                       sm_scale, workspace, workspace_bytes, err_flag, stream);
+}
+
+int kv_quant_int8_static_write(const void* k_src, const void* v_src, int src_dtype,
+                               int64_t num_tokens, int num_kv_heads, int head_dim,
+                               int64_t k_stride_tok, int64_t k_stride_head, int64_t k_stride_dim,
+                               int64_t v_stride_tok, int64_t v_stride_head, int64_t v_stride_dim,
+                               float k_scale, float v_scale, const int32_t* slot_mapping,
+                               void* kv_pool, int64_t num_blocks, int block_size,
+                               int32_t* err_flag, void* stream) {
+  return write_common(PDAKV_KV_INT8_STATIC, Scales{k_scale, v_scale}, k_src, v_src, src_dtype,
+                      num_tokens, num_kv_heads, head_dim, k_stride_tok, k_stride_head,
+                      k_stride_dim, v_stride_tok, v_stride_head, v_stride_dim, slot_mapping,
+                      kv_pool, num_blocks, block_size, err_flag, stream);
+}
+
+int paged_attn_decode_int8_static(void* out, int out_dtype, int64_t out_stride_seq,
+                                  int64_t out_stride_head, const void* q, int q_dtype,
+                                  int64_t q_stride_seq, int64_t q_stride_head,
+                                  const void* kv_pool, int64_t num_blocks, int block_size,
+                                  const int32_t* block_tables, int64_t block_table_stride,
+                                  const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int max_context_len,
+                                  float sm_scale, float k_scale, float v_scale, void* workspace,
+                                  size_t workspace_bytes, int32_t* err_flag, void* stream) {
+  return decode_common(PDAKV_KV_INT8_STATIC, Scales{k_scale, v_scale}, out, out_dtype,
+                       out_stride_seq, out_stride_head, q, q_dtype, q_stride_seq, q_stride_head,
+                       nullptr, kv_pool, num_blocks, block_size, block_tables,
+                       block_table_stride, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, max_context_len, sm_scale, workspace, workspace_bytes, err_flag,
+                       stream);
+}
+
+int paged_attn_decode_int8_static_append(
+    void* out, int out_dtype, int64_t out_stride_seq, int64_t out_stride_head, const void* q,
+    int q_dtype, int64_t q_stride_seq, int64_t q_stride_head, const void* k_new,
+    const void* v_new, int64_t k_stride_seq, int64_t k_stride_head, int64_t k_stride_dim,
+    int64_t v_stride_seq, int64_t v_stride_head, int64_t v_stride_dim, void* kv_pool,
+    int64_t num_blocks, int block_size, const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int max_context_len, float sm_scale, float k_scale, float v_scale, void* workspace,
+    size_t workspace_bytes, int32_t* err_flag, void* stream) {
+  AppendRows app;
+  app.k = k_new;
+  app.v = v_new;
+  app.kst = k_stride_seq;
+  app.ksh = k_stride_head;
+  app.ksd = k_stride_dim;
+  app.vst = v_stride_seq;
+  app.vsh = v_stride_head;
+  app.vsd = v_stride_dim;
+  return decode_common(PDAKV_KV_INT8_STATIC, Scales{k_scale, v_scale}, out, out_dtype,
+                       out_stride_seq, out_stride_head, q, q_dtype, q_stride_seq, q_stride_head,
+                       &app, kv_pool, num_blocks, block_size, block_tables, block_table_stride,
+                       context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                       max_context_len, sm_scale, workspace, workspace_bytes, err_flag, stream);
 }
 
 }  // extern "C"

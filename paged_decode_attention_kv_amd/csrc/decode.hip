@@ -1,5 +1,6 @@
-// Paged decode attention over INT8 pages (codes + FP16 per-token scales) and
-// over 16-bit pages (the control), for gfx950.
+// Paged decode attention over INT8 pages (codes + FP16 per-token scales, or
+// codes only with static per-tensor scales) and over 16-bit pages (the
+// control), for gfx950.
 //
 // What is computed (MoE-Infinity PR #183 "feat: opt-in INT8 KV-cache
 // quantization", "What landed", native-kernel bullet): for sequence b and
@@ -47,6 +48,8 @@
 // partials of each unit that spans several waves. (Merging in the last
 // arriving wave would need device-scope fences, which write back and
 // invalidate the L2 of the XCD: far dearer than the second launch.)
+#include <type_traits>
+
 #include "device_util.h"
 #include "launch.h"
 #include "quant_row.h"
@@ -264,8 +267,8 @@ __device__ __forceinline__ void load_int8_page(Int8Page<D>& pg, const uint8_t* h
   pg.vs = ld8(r, so + 32);
 }
 
-template <int D>
-__device__ __forceinline__ f4_t int8_qk(const Int8Page<D>& pg, const h8_t* qf) {
+template <int D, class Pg>
+__device__ __forceinline__ f4_t int8_qk(const Pg& pg, const h8_t* qf) {
   f4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < D / 32; ++j) {
@@ -342,13 +345,74 @@ __device__ __forceinline__ void int8_page_step(const Int8Page<D>& pg, const h8_t
   }
 }
 
-// The INT8 page format as seen by the decode loop.
-template <int D_, bool QBF16, int G_ = 1>
+// INT8 pages with static scales: the codes only, laid out as in the
+// per-token page (one calibrated scalar for all of K and one for all of V;
+// InfiniLM PR #553 "Summary", TensorRT-LLM PR #18953 "Summary"). The K scale
+// is folded into the logit factor on the host and the V scale multiplies the
+// final output, so a page step is the per-token step without the scales.
+template <int D>
+struct StaticPage {
+  u4_t k[D / 64];  // as Int8Page
+  u4_t v[D / 64];
+};
+
+template <int D>
+__device__ __forceinline__ void load_static_page(StaticPage<D>& pg, const uint8_t* hp, int i16,
+                                                 int kb) {
+  const __amdgpu_buffer_rsrc_t r = head_block(hp, 32 * D);
+  const uint32_t ko = i16 * D + 16 * kb;
+  const uint32_t vo = kb * 4 * D + 16 * i16;
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) pg.k[i] = ld16(r, ko + 64 * i);
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) pg.v[i] = ld16(r, vo + 16 * D + 256 * i);
+}
+
+// Tokens at or past the limit L get logit -inf (probability 0; any byte in
+// their slots is a finite code, so 0 * code adds nothing).
+template <int D>
+__device__ __forceinline__ void static_page_step(const StaticPage<D>& pg, const h8_t* qf,
+                                                 float qscale, int page_tok, int L,
+                                                 SoftmaxState<D / 16>& st) {
+  constexpr int ND = D / 16;
+  const f4_t s = int8_qk<D>(pg, qf);
+  const bool tail = page_tok + kBlockSize > L;
+  const int tok0 = tail ? lane_token(page_tok) : 0;
+  float z[4];
+  float zmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    z[j] = s[j] * qscale;
+    if (tail) z[j] = tok0 + j < L ? z[j] : -INFINITY;
+    zmax = max_nc(zmax, z[j]);
+  }
+  raise_max(st, zmax);
+  float hi[4], lo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float x = __builtin_amdgcn_exp2f(z[j] - st.mk);  // 2^(kPScale + z - m)
+    st.l += x;
+    hi[j] = static_cast<float>(static_cast<_Float16>(x));
+    lo[j] = x - hi[j];
+  }
+  const h4_t ph = __builtin_bit_cast(h4_t, u2_t{pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3])});
+  const h4_t pl = __builtin_bit_cast(h4_t, u2_t{pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3])});
+#pragma unroll
+  for (int k = 0; k < ND; ++k) {
+    const h4_t vw = __builtin_bit_cast(h4_t, i8x4_to_f16x4_perm(pg.v[k / 4][k % 4]));
+    st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(vw, ph, st.acc[k], 0, 0, 0);
+    st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(vw, pl, st.acc[k], 0, 0, 0);
+  }
+}
+
+// The INT8 page formats as seen by the decode loop: per-token FP16 scales in
+// the page, or (Static) codes only with the layer's two scalar scales.
+template <int D_, bool QBF16, int G_ = 1, bool Static = false>
 struct Int8Kind {
   static constexpr int D = D_;
   static constexpr int kGroup = G_;  // pages per register buffer
-  static constexpr int kHeadBytes = 32 * D + 64;
-  using Page = Int8Page<D>;
+  static constexpr int kHeadBytes = Static ? 32 * D : 32 * D + 64;
+  using Page = typename std::conditional<Static, StaticPage<D>, Int8Page<D>>::type;
   h8_t qf[D / 32];
   float qscale;
 
@@ -364,11 +428,17 @@ struct Int8Kind {
         qf);
   }
   static __device__ __forceinline__ void load(Page& pg, const uint8_t* hp, int i16, int kb) {
-    load_int8_page<D>(pg, hp, i16, kb);
+    if constexpr (Static)
+      load_static_page<D>(pg, hp, i16, kb);
+    else
+      load_int8_page<D>(pg, hp, i16, kb);
   }
   __device__ __forceinline__ void step(const Page& pg, int page_tok, int L,
                                        SoftmaxState<D / 16>& st) const {
-    int8_page_step<D>(pg, qf, qscale, page_tok, L, st);
+    if constexpr (Static)
+      static_page_step<D>(pg, qf, qscale, page_tok, L, st);
+    else
+      int8_page_step<D>(pg, qf, qscale, page_tok, L, st);
   }
   // dimension of accumulator element acc[k][j] in lane (i16, kb)
   static __device__ __forceinline__ int acc_dim(int k, int j, int kb) {
@@ -394,6 +464,16 @@ struct Int8Kind {
       xv[e] = bits16_to_f32<QBF16>(vn[b * a.vn_st + g * a.vn_sh + d * a.vn_sd]);
       ak = fmaxf(ak, fabsf(xk[e]));
       av = fmaxf(av, fabsf(xv[e]));
+    }
+    if constexpr (Static) {
+      // the layer's scales: nothing can overflow
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int d = lane * EPL + e;
+        nt[d] = row_code(xk[e], a.k_scale);
+        nt[D + d] = row_code(xv[e], a.v_scale);
+      }
+      return true;
     }
     ak = wave_max(ak);
     av = wave_max(av);
@@ -426,7 +506,7 @@ struct Int8Kind {
       head[pos * D + d] = nt[d];
       head[16 * D + (pos >> 2) * 4 * D + 4 * d + (pos & 3)] = nt[D + d];
     }
-    if (lane == 0) {
+    if (!Static && lane == 0) {
       *reinterpret_cast<uint16_t*>(head + 32 * D + 2 * pos) =
           *reinterpret_cast<const uint16_t*>(nt + 2 * D);
       *reinterpret_cast<uint16_t*>(head + 32 * D + 32 + 2 * pos) =
@@ -454,17 +534,22 @@ struct Int8Kind {
         for (int j = 0; j < 4; ++j)
           pg.v[i][j] = (pg.v[i][j] & keep) | (((w >> (8 * j)) & 0xFFu) << sh);
       }
-      const int hs = 16 * (pos & 1);
-      const uint32_t hkeep = ~(0xFFFFu << hs);
-      const uint32_t kbits = *reinterpret_cast<const uint16_t*>(nt + 2 * D);
-      const uint32_t vbits = *reinterpret_cast<const uint16_t*>(nt + 2 * D + 2);
-      if ((pos & 3) < 2) {
-        pg.ks.x = (pg.ks.x & hkeep) | (kbits << hs);
-        pg.vs.x = (pg.vs.x & hkeep) | (vbits << hs);
-      } else {
-        pg.ks.y = (pg.ks.y & hkeep) | (kbits << hs);
-        pg.vs.y = (pg.vs.y & hkeep) | (vbits << hs);
-      }
+      if constexpr (!Static) patch_scales(pg, nt, pos);
+    }
+  }
+
+  // the appended token's K and V scales into the scale words of its group
+  static __device__ __forceinline__ void patch_scales(Page& pg, const uint8_t* nt, int pos) {
+    const int hs = 16 * (pos & 1);
+    const uint32_t hkeep = ~(0xFFFFu << hs);
+    const uint32_t kbits = *reinterpret_cast<const uint16_t*>(nt + 2 * D);
+    const uint32_t vbits = *reinterpret_cast<const uint16_t*>(nt + 2 * D + 2);
+    if ((pos & 3) < 2) {
+      pg.ks.x = (pg.ks.x & hkeep) | (kbits << hs);
+      pg.vs.x = (pg.vs.x & hkeep) | (vbits << hs);
+    } else {
+      pg.ks.y = (pg.ks.y & hkeep) | (kbits << hs);
+      pg.vs.y = (pg.vs.y & hkeep) | (vbits << hs);
     }
   }
 };
@@ -733,7 +818,7 @@ __device__ __forceinline__ void write_result(const DecodeArgs& a, const float* r
     for (int e = lane; e < a.group * D; e += 64) {
       const int hh = e / D, d = e % D;
       const float l = res[hh * (D + 2) + D + 1];
-      const float v = l > 0.f ? res[hh * (D + 2) + d] / l : 0.f;
+      const float v = l > 0.f ? res[hh * (D + 2) + d] / l * a.out_mul : 0.f;
       store_out(a.out, a.out_dtype, b * a.out_ss + (g * a.group + hh) * a.out_sh + d, v);
     }
   } else {
@@ -1020,6 +1105,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
   decode_wave<Int8Kind<D, QBF16, kInt8PageGroup>>(a);
 }
 
+template <int D, bool QBF16>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
+    kInt8WavesPerSimd))) void decode_int8_static_kernel(DecodeArgs a) {
+  decode_wave<Int8Kind<D, QBF16, kInt8PageGroup, true>>(a);
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
     k16WavesPerSimd))) void decode_16bit_kernel(DecodeArgs a) {
@@ -1091,7 +1182,7 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void merge_kernel(DecodeArgs a
     // lw == 0: no attendable token in the unit
 #pragma unroll
     for (int k = 0; k < ND; ++k)
-      store_out(a.out, a.out_dtype, o + lane + 64 * k, lw > 0.f ? acc[k] / lw : 0.f);
+      store_out(a.out, a.out_dtype, o + lane + 64 * k, lw > 0.f ? acc[k] / lw * a.out_mul : 0.f);
     return;
   }
   if (lane == 0) {
@@ -1110,7 +1201,7 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void merge_kernel(DecodeArgs a
       num += e * s_acc[j][d];
       den += e * s_l[j];
     }
-    store_out(a.out, a.out_dtype, o + d, den > 0.f ? num / den : 0.f);
+    store_out(a.out, a.out_dtype, o + d, den > 0.f ? num / den * a.out_mul : 0.f);
   }
 }
 
@@ -1137,6 +1228,26 @@ hipError_t launch_decode_int8(const DecodeArgs& a, int head_dim, bool q_bf16, hi
       hipLaunchKernelGGL((decode_int8_kernel<64, true>), grid, block, lds, s, a);
     else
       hipLaunchKernelGGL((decode_int8_kernel<64, false>), grid, block, lds, s, a);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return head_dim == 128 ? launch_merge<128>(a, s) : launch_merge<64>(a, s);
+}
+
+hipError_t launch_decode_int8_static(const DecodeArgs& a, int head_dim, bool q_bf16,
+                                     hipStream_t s) {
+  const dim3 grid(a.num_waves / kWaves), block(64 * kWaves);
+  const size_t lds = static_cast<size_t>(kWaves) * a.lds_wave_bytes;
+  if (head_dim == 128) {
+    if (q_bf16)
+      hipLaunchKernelGGL((decode_int8_static_kernel<128, true>), grid, block, lds, s, a);
+    else
+      hipLaunchKernelGGL((decode_int8_static_kernel<128, false>), grid, block, lds, s, a);
+  } else {
+    if (q_bf16)
+      hipLaunchKernelGGL((decode_int8_static_kernel<64, true>), grid, block, lds, s, a);
+    else
+      hipLaunchKernelGGL((decode_int8_static_kernel<64, false>), grid, block, lds, s, a);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -39,6 +39,7 @@ struct WriteArgs {
   uint8_t* pool;
   int64_t num_blocks;
   int64_t page_bytes;
+  float k_scale, v_scale;  // static-scale format: the layer's K and V scales
   int32_t* err;
 };
 
@@ -56,7 +57,10 @@ struct DecodeArgs {
   int64_t bt_stride;
   const int32_t* ctx;
   int num_seqs, num_q_heads, num_kv_heads, group, max_ctx;
-  float scale_log2;  // sm_scale * log2(e): logits are kept in base 2
+  float scale_log2;  // sm_scale * log2(e) (times the K scale for static
+                     // scales): logits are kept in base 2
+  float out_mul;     // output factor: the V scale for static scales, else 1
+  float k_scale, v_scale;  // static scales (quantizer of the fused append)
   float* ws;         // partials [num_waves + B * Hkv][G][D + 2]
   int2* desc;        // per (sequence, KV head): first covering wave, wave count
   int num_waves;     // waves of the decode grid (a multiple of kWaves)
@@ -80,5 +84,9 @@ hipError_t launch_write_16bit(const WriteArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_decode_int8(const DecodeArgs& a, int head_dim, bool q_bf16, hipStream_t s);
 hipError_t launch_decode_16bit(const DecodeArgs& a, int head_dim, bool kv_bf16,
                                hipStream_t s);
+hipError_t launch_quant_write_static(const WriteArgs& a, int head_dim, bool src_bf16,
+                                     hipStream_t s);
+hipError_t launch_decode_int8_static(const DecodeArgs& a, int head_dim, bool q_bf16,
+                                     hipStream_t s);
 
 }  // namespace pdakv

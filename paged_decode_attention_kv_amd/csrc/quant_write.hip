@@ -1,10 +1,11 @@
 // Quantize-on-write and 16-bit write into paged KV pools (gfx950).
 //
 // One wave (64 lanes) owns one (token, KV head) pair and handles its K row and
-// its V row; a workgroup holds four waves. The row quantizer (quant_row.h)
-// follows MoE-Infinity PR #183 "feat: opt-in INT8 KV-cache quantization"
-// ("What landed", format-contract bullet; "Precision & memory") and the
-// zero-token rule of mlxcel PR #717 ("The Int8 bug and fix").
+// its V row; a workgroup holds four waves. Three pool formats: per-token INT8
+// (codes + FP16 scales), static-scale INT8 (codes only) and 16-bit. The row
+// quantizer (quant_row.h) follows MoE-Infinity PR #183 "feat: opt-in INT8
+// KV-cache quantization" ("What landed", format-contract bullet; "Precision &
+// memory") and the zero-token rule of mlxcel PR #717 ("The Int8 bug and fix").
 #include "device_util.h"
 #include "launch.h"
 #include "quant_row.h"
@@ -88,6 +89,39 @@ __global__ __launch_bounds__(64 * kWriteWaves) void quant_write_int8_kernel(Writ
   }
 }
 
+// Static scales (InfiniLM PR #553 "Summary"; TensorRT-LLM PR #18953
+// "Summary"): the layer's K scale and V scale are given, so a row needs no
+// reduction: code = clamp(rint(fl32(x / scale)), -127, 127), stored into a
+// codes-only head block (K codes, then V codes grouped by four tokens).
+template <int D, bool BF16>
+__global__ __launch_bounds__(64 * kWriteWaves) void quant_write_static_kernel(WriteArgs a) {
+  constexpr int EPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWriteWaves + (threadIdx.x >> 6);
+  if (row >= a.num_tokens * a.num_kv_heads) return;
+  const int64_t t = row / a.num_kv_heads;
+  const int h = static_cast<int>(row - t * a.num_kv_heads);
+  const int32_t slot = a.slots[t];
+  if (slot < 0) return;
+  if (slot >= a.num_blocks * kBlockSize) {
+    if (lane == 0) raise_flag(a.err, PDAKV_EFLAG_SLOT_RANGE);
+    return;
+  }
+  const int64_t blk = slot / kBlockSize;
+  const int pos = slot % kBlockSize;
+  uint8_t* head = a.pool + blk * a.page_bytes + static_cast<int64_t>(h) * 2 * kBlockSize * D;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int d = lane * EPL + e;
+    const float xk =
+        bits16_to_f32<BF16>(load_bits<uint16_t>(a.k, t * a.k_st + h * a.k_sh + d * a.k_sd));
+    const float xv =
+        bits16_to_f32<BF16>(load_bits<uint16_t>(a.v, t * a.v_st + h * a.v_sh + d * a.v_sd));
+    head[pos * D + d] = row_code(xk, a.k_scale);
+    head[kBlockSize * D + (pos >> 2) * 4 * D + d * 4 + (pos & 3)] = row_code(xv, a.v_scale);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * kWriteWaves) void write_16bit_kernel(WriteArgs a) {
   constexpr int EPL = D / 64;
@@ -136,6 +170,23 @@ hipError_t launch_quant_write_int8(const WriteArgs& a, int head_dim, bool src_bf
       hipLaunchKernelGGL((quant_write_int8_kernel<64, true>), grid, block, 0, s, a);
     else
       hipLaunchKernelGGL((quant_write_int8_kernel<64, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_write_static(const WriteArgs& a, int head_dim, bool src_bf16,
+                                     hipStream_t s) {
+  const dim3 grid(write_grid(a)), block(64 * kWriteWaves);
+  if (head_dim == 128) {
+    if (src_bf16)
+      hipLaunchKernelGGL((quant_write_static_kernel<128, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((quant_write_static_kernel<128, false>), grid, block, 0, s, a);
+  } else {
+    if (src_bf16)
+      hipLaunchKernelGGL((quant_write_static_kernel<64, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((quant_write_static_kernel<64, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -113,3 +113,24 @@ def oracle_pair_from_sources(wl, b: int, h: int, fmt) -> np.ndarray:
 
 
 MAX_ABS_TOL = 2e-3  # decode outputs vs the FP32-dequantized oracle (FP32 output)
+
+
+def calibrated_scales(wl, shrink: float = 1.0):
+    """Static K and V scales for a workload, the input the static-scale
+    variant takes: the absolute maximum of all K (or V) values the workload
+    writes, divided by 127 and by ``shrink`` (shrink > 1 makes the largest
+    values saturate), as binary32. The calibration itself happens outside the
+    path (the pages take calibrated scales from a checkpoint)."""
+    ak = max(float(ph.k.float().abs().max()) for ph in wl.phases if ph.k.numel())
+    av = max(float(ph.v.float().abs().max()) for ph in wl.phases if ph.v.numel())
+    return float(np.float32(ak / 127.0 / shrink)), float(np.float32(av / 127.0 / shrink))
+
+
+def oracle_static_pool(wl, k_scale: float, v_scale: float) -> np.ndarray:
+    pool = oracle.new_pool(oracle.KV_INT8_STATIC, wl.num_blocks, wl.block_size,
+                           wl.num_kv_heads, wl.head_dim, fill=FILL)
+    for ph in wl.phases:
+        oracle.write_int8_static_tokens(pool, oracle.quantize_static(ph.k, k_scale),
+                                        oracle.quantize_static(ph.v, v_scale), ph.slot_mapping,
+                                        wl.block_size)
+    return pool

@@ -27,7 +27,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function(P):
     names = _declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(P._lib, n), n
     assert set(names) == set(P.EXPORTED)
@@ -49,11 +49,14 @@ def test_page_bytes_match_the_printed_totals(P, golden):
     assert P.pdakv_page_bytes(P.KV_INT8_SYM, 16, 2, 64) == 4224
     assert P.pdakv_page_bytes(7, 16, 8, 128) == 0
     assert P.pdakv_page_bytes(P.KV_INT8_SYM, 15, 8, 128) == 0
+    # static scales: codes only, half the 16-bit page
+    assert P.pdakv_page_bytes(P.KV_INT8_STATIC, 16, 8, 128) == 32768
+    assert P.pdakv_page_bytes(P.KV_INT8_STATIC, 16, 2, 64) == 4096
 
 
 def test_page_bytes_agree_with_oracle(P):
     import oracle
-    for fmt in (P.KV_INT8_SYM, P.KV_16BIT):
+    for fmt in (P.KV_INT8_SYM, P.KV_16BIT, P.KV_INT8_STATIC):
         for hkv in (1, 2, 8, 32):
             for d in (64, 128):
                 assert P.pdakv_page_bytes(fmt, 16, hkv, d) == oracle.page_bytes(fmt, 16, hkv, d)
@@ -64,8 +67,8 @@ def test_page_bytes_agree_with_oracle(P):
                                      (256, 8, 131072)])
 def test_decode_plan_is_consistent(P, B, hkv, L):
     items = B * hkv * -(-L // 16)
-    resident = {P.KV_INT8_SYM: 2048, P.KV_16BIT: 2048}
-    for fmt in (P.KV_INT8_SYM, P.KV_16BIT):
+    resident = {P.KV_INT8_SYM: 2048, P.KV_16BIT: 2048, P.KV_INT8_STATIC: 2048}
+    for fmt in (P.KV_INT8_SYM, P.KV_16BIT, P.KV_INT8_STATIC):
         waves, ppw = P.pdakv_decode_plan(fmt, B, hkv, L)
         assert waves >= 4 and waves % 4 == 0
         assert 4 <= ppw <= 128 and ppw == max(4, -(-items // waves))
@@ -157,3 +160,53 @@ def _append_args(**kw):
 ])
 def test_append_validation(P, fn, change, status):
     assert getattr(P._lib, fn)(*_append_args(**change)) == status
+
+
+# ---- static scales --------------------------------------------------------
+
+def _with_scales(args, at, ks=0.05, vs=0.07):
+    return args[:at] + [ks, vs] + args[at:]
+
+
+BAD_SCALES = [(0.0, 1.0), (1.0, 0.0), (-0.5, 1.0), (1.0, -2.0), (float("nan"), 1.0),
+              (1.0, float("inf"))]
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(dtype=0), -3), (dict(d=96), -2), (dict(k=None), -1), (dict(pool=FAKE + 4), -1),
+    (dict(T=0, k=None), 0),
+])
+def test_static_write_validation(P, change, status):
+    assert P._lib.kv_quant_int8_static_write(*_with_scales(_write_args(**change), 12)) == status
+
+
+@pytest.mark.parametrize("ks,vs", BAD_SCALES)
+def test_static_write_rejects_bad_scales(P, ks, vs):
+    assert P._lib.kv_quant_int8_static_write(*_with_scales(_write_args(), 12, ks, vs)) == -1
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(qdt=0), -3), (dict(hq=30), -2), (dict(d=256), -2), (dict(bts=15), -1),
+    (dict(q=None), -1), (dict(pool=FAKE + 8), -1), (dict(maxL=2048, bts=128), -4),
+    (dict(B=0), 0),
+])
+def test_static_decode_validation(P, change, status):
+    assert P._lib.paged_attn_decode_int8_static(*_with_scales(_decode_args(**change), 20)) == status
+
+
+@pytest.mark.parametrize("ks,vs", BAD_SCALES + [(3e38, 1.0)])
+def test_static_decode_rejects_bad_scales(P, ks, vs):
+    # (3e38 * sm_scale * log2(e) is beyond the float range: rejected too)
+    args = _with_scales(_decode_args(sm=1.0, ws=FAKE, wsb=1 << 30), 20, ks, vs)
+    assert P._lib.paged_attn_decode_int8_static(*args) == -1
+    args = _with_scales(_append_args(sm=1.0), 28, ks, vs)
+    assert P._lib.paged_attn_decode_int8_static_append(*args) == -1
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(kn=None), -1), (dict(ksd=-1), -1), (dict(qdt=0), -3),
+    (dict(maxL=2048, bts=128, ws=None, wsb=0), -4), (dict(B=0, kn=None, vn=None), 0),
+])
+def test_static_append_validation(P, change, status):
+    args = _with_scales(_append_args(**change), 28)
+    assert P._lib.paged_attn_decode_int8_static_append(*args) == status

@@ -1,0 +1,184 @@
+"""GPU parity of the static-scale INT8 variant (one calibrated scalar scale
+for all of K and one for all of V; InfiniLM PR #553 "Summary", TensorRT-LLM
+PR #18953 "Summary"): pools written by the library are bit-identical to the
+oracle's, and the decode matches the oracle's decode over the same pool
+within the FP32-output tolerance, on the benchmark configurations (reduced
+sizes) and on edge shapes; the fused append + decode step leaves the same
+pool and output as a write followed by a decode."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import (FILL, MAX_ABS_TOL, calibrated_scales, dev_i32, oracle_static_pool,
+                            require_gpu, to_dev)
+from workloads import build, make_config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def P():
+    return require_gpu()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _gpu_static_pool(P, wl, ks, vs, phases=None):
+    pb = P.pdakv_page_bytes(P.KV_INT8_STATIC, wl.block_size, wl.num_kv_heads, wl.head_dim)
+    pool = torch.full((wl.num_blocks, pb), FILL, dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for ph in (wl.phases if phases is None else phases):
+        if len(ph.slot_mapping):
+            P.kv_quant_int8_static_write(to_dev(ph.k), to_dev(ph.v), dev_i32(ph.slot_mapping),
+                                         pool, wl.num_blocks, ks, vs, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    return pool
+
+
+def _gpu_static_decode(P, wl, pool, ks, vs, out_dtype=torch.float32):
+    out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), dtype=out_dtype,
+                      device="cuda")
+    ws = P.alloc_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                           wl.max_context_len)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    P.paged_attn_decode_int8_static(out, to_dev(wl.q), pool, wl.num_blocks,
+                                    dev_i32(wl.block_tables), dev_i32(wl.context_lens),
+                                    wl.num_kv_heads, wl.max_context_len, wl.sm_scale, ks, vs,
+                                    ws, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    return out
+
+
+def _oracle_decode(wl, host, ks, vs, pairs=None):
+    return oracle.decode_int8_static_from_pool(host, wl.block_tables, wl.context_lens, wl.q,
+                                               wl.sm_scale, ks, vs, wl.block_size,
+                                               wl.num_kv_heads, wl.head_dim, pairs=pairs)
+
+
+def _max_diff(out, want):
+    got = out.float().cpu().numpy().astype(np.float64)
+    m = ~np.isnan(want)
+    return float(np.max(np.abs(got[m] - want[m])))
+
+
+@pytest.mark.parametrize("idx,scale,shrink", [(1, 1.0, 1.0), (1, 1.0, 8.0), (2, 1.0, 1.0),
+                                              (3, 0.05, 1.0), (4, 0.03, 1.0), (4, 0.03, 50.0),
+                                              (5, 0.1, 1.0), ("s8k", 0.1, 1.0)])
+def test_static_pool_and_decode_match_oracle(P, idx, scale, shrink):
+    """shrink > 1: the scales are that much below the calibrated ones, so
+    many values saturate at +-127."""
+    wl = make_config(idx, scale)
+    ks, vs = calibrated_scales(wl, shrink)
+    _say(f"static config {idx} scale {scale} shrink {shrink}: ks {ks:.4g} vs {vs:.4g}")
+    pool = _gpu_static_pool(P, wl, ks, vs)
+    host = oracle_static_pool(wl, ks, vs)
+    assert np.array_equal(pool.cpu().numpy(), host), "static pool differs from the oracle's"
+    out = _gpu_static_decode(P, wl, pool, ks, vs)
+    want = _oracle_decode(wl, host, ks, vs)
+    d = _max_diff(out, want)
+    _say(f"  max abs diff {d:.3e}")
+    assert d <= MAX_ABS_TOL
+
+
+@pytest.mark.parametrize("hq,hkv,d,dt", [(32, 8, 128, "f16"), (8, 8, 64, "bf16"),
+                                         (14, 2, 64, "bf16"), (16, 1, 128, "f16")])
+def test_static_edge_lengths(P, hq, hkv, d, dt):
+    """Context lengths 0, 1, 15, 16, 17, 33 and a long one in one batch;
+    MHA, GQA 4 / 7 / 16, head_dim 64 and 128, fp16 and bf16."""
+    wl = build("static-edge", 77, [("prefill", [0, 1, 15, 16, 17, 33, 700])], hq, hkv, d, dt,
+               "outlier", shuffle=True, spare_blocks=3)
+    ks, vs = calibrated_scales(wl)
+    _say(f"static edges {hq}/{hkv}/{d} {dt}")
+    pool = _gpu_static_pool(P, wl, ks, vs)
+    host = oracle_static_pool(wl, ks, vs)
+    assert np.array_equal(pool.cpu().numpy(), host)
+    out = _gpu_static_decode(P, wl, pool, ks, vs)
+    want = _oracle_decode(wl, host, ks, vs)
+    assert _max_diff(out, want) <= MAX_ABS_TOL
+    assert torch.all(out[0] == 0)  # empty context -> zero rows
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16])
+def test_static_16bit_outputs_round_the_fp32_output(P, out_dtype):
+    wl = make_config(2, 0.5)
+    ks, vs = calibrated_scales(wl)
+    pool = _gpu_static_pool(P, wl, ks, vs)
+    ref = _gpu_static_decode(P, wl, pool, ks, vs)
+    low = _gpu_static_decode(P, wl, pool, ks, vs, out_dtype)
+    assert torch.equal(low, ref.to(out_dtype))
+
+
+def test_static_shared_scale(P):
+    """One scale for K and V (the larger of the two calibrated scales)."""
+    wl = make_config(3, 0.03)
+    ks, vs = calibrated_scales(wl)
+    s = float(oracle.shared_static_scale(ks, vs))
+    pool = _gpu_static_pool(P, wl, s, s)
+    host = oracle_static_pool(wl, s, s)
+    assert np.array_equal(pool.cpu().numpy(), host)
+    out = _gpu_static_decode(P, wl, pool, s, s)
+    assert _max_diff(out, _oracle_decode(wl, host, s, s)) <= MAX_ABS_TOL
+
+
+@pytest.mark.parametrize("idx,scale", [(3, 0.05), (5, 0.2)])
+def test_static_fused_append_matches_write_then_decode(P, idx, scale):
+    wl = make_config(idx, scale)
+    ks, vs = calibrated_scales(wl)
+    last = wl.phases[-1]
+    assert np.all(last.counts == 1)
+    _say(f"static fused append: config {idx} scale {scale}")
+    pool = _gpu_static_pool(P, wl, ks, vs, phases=wl.phases[:-1])
+    out = torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim), dtype=torch.float32,
+                      device="cuda")
+    ws = P.alloc_workspace(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                           wl.max_context_len)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    P.paged_attn_decode_int8_static_append(
+        out, to_dev(wl.q), to_dev(last.k), to_dev(last.v), pool, wl.num_blocks,
+        dev_i32(wl.block_tables), dev_i32(wl.context_lens), wl.num_kv_heads,
+        wl.max_context_len, wl.sm_scale, ks, vs, ws, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    host = oracle_static_pool(wl, ks, vs)
+    assert np.array_equal(pool.cpu().numpy(), host), "pool after the fused step differs"
+    d = _max_diff(out, _oracle_decode(wl, host, ks, vs))
+    _say(f"  max abs diff {d:.3e}")
+    assert d <= MAX_ABS_TOL
+    # the pool it leaves decodes to the same rows with the plain call
+    again = _gpu_static_decode(P, wl, pool, ks, vs)
+    assert torch.equal(out, again)
+
+
+def test_static_full_size_sampled(P):
+    """Batched step at full size in the launch shape the bench times: the
+    pool of a sample of sequences and a sample of (sequence, head) rows
+    against the oracle."""
+    wl = make_config(3)
+    ks, vs = calibrated_scales(wl)
+    pool = _gpu_static_pool(P, wl, ks, vs)
+    out = _gpu_static_decode(P, wl, pool, ks, vs)
+    rng = np.random.default_rng(0)
+    pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, wl.num_seqs, 12),
+                                               rng.integers(0, wl.num_q_heads, 12))]
+    # oracle pool of just the sampled sequences' tokens (same slots)
+    host = oracle.new_pool(oracle.KV_INT8_STATIC, wl.num_blocks, 16, wl.num_kv_heads,
+                           wl.head_dim, fill=FILL)
+    seqs = sorted({b for b, _ in pairs})
+    for ph in wl.phases:
+        rows = np.concatenate([np.arange(ph.seq_rows(b).start, ph.seq_rows(b).stop)
+                               for b in seqs])
+        oracle.write_int8_static_tokens(host, oracle.quantize_static(ph.k[rows], ks),
+                                        oracle.quantize_static(ph.v[rows], vs),
+                                        ph.slot_mapping[rows], 16)
+    gp = pool.cpu().numpy()
+    for b in seqs:
+        blocks = wl.block_tables[b, :-(-int(wl.context_lens[b]) // 16)]
+        assert np.array_equal(gp[blocks], host[blocks]), b
+    want = _oracle_decode(wl, host, ks, vs, pairs=pairs)
+    assert _max_diff(out, want) <= MAX_ABS_TOL
