@@ -3,10 +3,11 @@
 Default workload: the batched decode step — 64 Llama-3.1-8B-shaped sequences
 (32 query / 8 KV heads, head_dim 128, fp16) with contexts drawn uniformly in
 [1024, 8192] over shuffled pages; one step quantizes and appends one new token
-per sequence (kv_quant_int8_sym_write) and then runs the INT8 paged decode
-(paged_attn_decode_int8) over contexts L_b + 1. The FP16-KV control runs the
-same step with kv_write_16bit + paged_attn_decode_fp16. Supplementary decode
-points at 2K, 8K and 32K context are reported alongside.
+per sequence and decodes over contexts L_b + 1, in one call
+(paged_attn_decode_int8_append). Alongside: the FP16-KV control of the same
+step (paged_attn_decode_fp16_append), the unfused form of both (write kernel,
+then decode), the static-scale INT8 variant of the step, and decode-only
+points at 2K, 8K and 32K context for the three page formats.
 
 Prints ONE JSON line. Timing: W warm-up steps, then K timed steps between
 device synchronizations; HIP events on the launch stream time each decode call
@@ -74,11 +75,12 @@ def measured_traffic():
         return None
 
 
-def decode_bytes(wl, fmt_int8: bool) -> int:
+def decode_bytes(wl, fmt: str) -> int:
     """Algorithmic HBM bytes of one decode call: K/V payload (+ scales),
-    block-table entries, context lengths, q, FP32 output."""
+    block-table entries, context lengths, q, FP32 output. fmt: "int8"
+    (per-token scales), "static" (codes only) or "fp16"."""
     hkv, d = wl.num_kv_heads, wl.head_dim
-    per_tok = hkv * (2 * d + 4) if fmt_int8 else hkv * 4 * d
+    per_tok = hkv * {"int8": 2 * d + 4, "static": 2 * d, "fp16": 4 * d}[fmt]
     total = 0
     for L in wl.context_lens.tolist():
         total += L * per_tok + math.ceil(L / 16) * 4 + 4
@@ -86,11 +88,12 @@ def decode_bytes(wl, fmt_int8: bool) -> int:
     return total
 
 
-def append_bytes(wl, fmt_int8: bool) -> int:
+def append_bytes(wl, fmt: str) -> int:
     """Algorithmic bytes of the fused append: read each sequence's new 16-bit
-    K and V rows, write their codes + scales (or 16-bit values)."""
-    return wl.num_seqs * wl.num_kv_heads * (4 * wl.head_dim +
-                                            (2 * wl.head_dim + 4 if fmt_int8 else 4 * wl.head_dim))
+    K and V rows, write their codes (+ scales) or 16-bit values."""
+    d = wl.head_dim
+    written = {"int8": 2 * d + 4, "static": 2 * d, "fp16": 4 * d}[fmt]
+    return wl.num_seqs * wl.num_kv_heads * (4 * d + written)
 
 
 def main():
@@ -130,9 +133,33 @@ def main():
     def dev_i32(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to("cuda")
 
-    def setup(wl, fmt_int8, append_phase):
-        fmt = P.KV_INT8_SYM if fmt_int8 else P.KV_16BIT
-        write = P.kv_quant_int8_sym_write if fmt_int8 else P.kv_write_16bit
+    def static_scales(wl):
+        """The layer's K and V scales for the static-scale format: an input
+        of that format (calibrated outside the path; here the absolute
+        maximum of all K or V values of the workload over 127)."""
+        ak = max(float(ph.k.float().abs().max()) for ph in wl.phases)
+        av = max(float(ph.v.float().abs().max()) for ph in wl.phases)
+        return float(np.float32(ak / 127.0)), float(np.float32(av / 127.0))
+
+    def setup(wl, fmt_name, append_phase):
+        if fmt_name == "static":
+            ks, vs = static_scales(wl)
+
+            def write(k, v, slots, pool, nb, stream=None):
+                P.kv_quant_int8_static_write(k, v, slots, pool, nb, ks, vs, stream=stream)
+
+            def decode(*a, **kw):
+                P.paged_attn_decode_int8_static(*a[:9], ks, vs, *a[9:], **kw)
+
+            def fused(*a, **kw):
+                P.paged_attn_decode_int8_static_append(*a[:11], ks, vs, *a[11:], **kw)
+            fmt = P.KV_INT8_STATIC
+        elif fmt_name == "int8":
+            fmt, write = P.KV_INT8_SYM, P.kv_quant_int8_sym_write
+            decode, fused = P.paged_attn_decode_int8, P.paged_attn_decode_int8_append
+        else:
+            fmt, write = P.KV_16BIT, P.kv_write_16bit
+            decode, fused = P.paged_attn_decode_fp16, P.paged_attn_decode_fp16_append
         pb = P.pdakv_page_bytes(fmt, 16, wl.num_kv_heads, wl.head_dim)
         pool = torch.empty((wl.num_blocks, pb), dtype=torch.uint8, device="cuda")
         for ph in wl.phases:
@@ -140,10 +167,7 @@ def main():
                 write(to_dev(ph.k), to_dev(ph.v), dev_i32(ph.slot_mapping), pool, wl.num_blocks)
         nrep = max(1, math.ceil(args.rotate_gb * 1e9 / pool.numel()))
         pools = [pool] + [pool.clone() for _ in range(nrep - 1)]
-        st = dict(fmt_int8=fmt_int8, write=write, pools=pools,
-                  decode=P.paged_attn_decode_int8 if fmt_int8 else P.paged_attn_decode_fp16,
-                  fused=(P.paged_attn_decode_int8_append if fmt_int8
-                         else P.paged_attn_decode_fp16_append),
+        st = dict(write=write, pools=pools, decode=decode, fused=fused,
                   q=to_dev(wl.q), bt=dev_i32(wl.block_tables), ctx=dev_i32(wl.context_lens),
                   out=torch.empty((wl.num_seqs, wl.num_q_heads, wl.head_dim),
                                   dtype=torch.float32, device="cuda"),
@@ -201,41 +225,40 @@ def main():
     # separate quantize-on-write call, then the decode call
     wl = make_config(3)
     res, unfused = {}, {}
-    for fmt_int8 in (True, False):
-        st = setup(wl, fmt_int8, "append")
-        key = "int8" if fmt_int8 else "fp16"
+    for key in ("int8", "fp16", "static"):
+        st = setup(wl, key, "append")
         step_ms, dec_ms, dec_med = run(wl, st, args.steps, args.warmup, "fused")
         res[key] = dict(
             step_ms=step_ms, call_ms=dec_ms, call_ms_median=dec_med,
             tokens_per_s=wl.num_seqs / (step_ms * 1e-3),
-            call_gbs=(decode_bytes(wl, fmt_int8) + append_bytes(wl, fmt_int8)) /
-            (dec_ms * 1e-3) / 1e9,
+            call_gbs=(decode_bytes(wl, key) + append_bytes(wl, key)) / (dec_ms * 1e-3) / 1e9,
             rotate_replicas=len(st["pools"]))
-        step_ms, dec_ms, dec_med = run(wl, st, args.steps, args.warmup, "unfused")
-        unfused[key] = dict(step_ms=round(step_ms, 5), decode_ms=round(dec_ms, 5),
-                            tokens_per_s=round(wl.num_seqs / (step_ms * 1e-3), 1),
-                            decode_gbs=round(decode_bytes(wl, fmt_int8) / (dec_ms * 1e-3) / 1e9,
-                                             1))
+        if key != "static":
+            step_ms, dec_ms, dec_med = run(wl, st, args.steps, args.warmup, "unfused")
+            unfused[key] = dict(step_ms=round(step_ms, 5), decode_ms=round(dec_ms, 5),
+                                tokens_per_s=round(wl.num_seqs / (step_ms * 1e-3), 1),
+                                decode_gbs=round(decode_bytes(wl, key) / (dec_ms * 1e-3) / 1e9,
+                                                 1))
         del st
         torch.cuda.empty_cache()
     waves, ppw = P.pdakv_decode_plan(P.KV_INT8_SYM, wl.num_seqs, wl.num_kv_heads,
                                      wl.max_context_len)
     i8 = res["int8"]
-    dec_b = decode_bytes(wl, True)
-    call_b = dec_b + append_bytes(wl, True)
+    dec_b = decode_bytes(wl, "int8")
+    call_b = dec_b + append_bytes(wl, "int8")
 
     # ---- supplementary decode-only points at 2K / 8K / 32K -------------------
     points = {}
     if not args.no_points:
-        for key, idx in (("2k", 2), ("8k", "s8k"), ("32k", 4)):
+        for pname, idx in (("2k", 2), ("8k", "s8k"), ("32k", 4)):
             pwl = make_config(idx)
             entry = {"config": pwl.name, "batch": pwl.num_seqs,
                      "context": int(pwl.max_context_len)}
-            for fmt_int8 in (True, False):
-                st = setup(pwl, fmt_int8, None)
+            for key in ("int8", "fp16", "static"):
+                st = setup(pwl, key, None)
                 _, dms, _ = run(pwl, st, max(10, args.steps), args.warmup, "decode")
-                b = decode_bytes(pwl, fmt_int8)
-                entry["int8" if fmt_int8 else "fp16"] = {
+                b = decode_bytes(pwl, key)
+                entry[key] = {
                     "decode_us": round(dms * 1e3, 2),
                     "tokens_per_s": round(pwl.num_seqs / (dms * 1e-3), 1),
                     "gbs": round(b / (dms * 1e-3) / 1e9, 1),
@@ -244,7 +267,7 @@ def main():
                 torch.cuda.empty_cache()
             entry["int8_over_fp16"] = round(entry["int8"]["tokens_per_s"] /
                                             entry["fp16"]["tokens_per_s"], 3)
-            points[key] = entry
+            points[pname] = entry
 
     # ---- CPU baseline: the oracle on a bounded sample ------------------------
     cpu = None
@@ -280,6 +303,8 @@ def main():
         "fp16_control": {k: (round(v, 4) if isinstance(v, float) else v)
                          for k, v in res["fp16"].items()},
         "int8_over_fp16_tokens": round(i8["tokens_per_s"] / res["fp16"]["tokens_per_s"], 3),
+        "static_scale_step": {k: (round(v, 4) if isinstance(v, float) else v)
+                              for k, v in res["static"].items()},
         "unfused_step": unfused,
         "points": points,
         "cpu_baseline": cpu,
