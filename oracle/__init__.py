@@ -12,7 +12,8 @@ quant      per-token symmetric INT8 quantizer (one FP16 scale per row), and
            the static variant (one given FP32 scale per tensor)
 pages      the paged byte layout of INT8 and 16-bit KV pools, written from
            the layout contract, plus page write / gather helpers
-attention  decode attention over dequantized K/V with FP64 accumulation
+attention  decode attention over dequantized K/V with FP64 accumulation, for
+           one query token per sequence or several (causal among them)
 
 Every function cites the passage it follows. Sources are four pull-request
 pages; they are cited by project, PR number and section:
@@ -62,4 +63,5 @@ from .attention import (  # noqa: F401
     decode_int8_from_pool,
     decode_16bit_from_pool,
     decode_int8_static_from_pool,
+    decode_multi_from_pool,
 )

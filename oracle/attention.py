@@ -147,3 +147,58 @@ def decode_int8_static_from_pool(pool, block_tables, context_lens, q, sm_scale: 
             out[b, h] = attend_one_sequence(qf[b, h][None], k[:, j:j + 1], v[:, j:j + 1],
                                             sm_scale)[0]
     return out
+
+
+def _sequence_kv(kind, pool, bt_row, L, block_size, num_kv_heads, head_dim, heads,
+                 kv_dtype=None, k_scale=None, v_scale=None):
+    """Dequantized K, V [L, len(heads), D] of one sequence, any page format."""
+    if kind == "int8":
+        kc, ks, vc, vs = gather_int8_sequence(pool, bt_row, L, block_size, num_kv_heads,
+                                              head_dim, heads=heads)
+        return dequantize_rows(kc, ks), dequantize_rows(vc, vs)
+    if kind == "static":
+        kc, vc = gather_int8_static_sequence(pool, bt_row, L, block_size, num_kv_heads,
+                                             head_dim, heads=heads)
+        return dequantize_static(kc, k_scale), dequantize_static(vc, v_scale)
+    kb, vb = gather_16bit_sequence(pool, bt_row, L, block_size, num_kv_heads, head_dim,
+                                   heads=heads)
+    return bits_to_f32(kb, kv_dtype), bits_to_f32(vb, kv_dtype)
+
+
+def decode_multi_from_pool(kind: str, pool, block_tables, context_lens, q, sm_scale: float,
+                           block_size: int, num_kv_heads: int, head_dim: int, kv_dtype=None,
+                           k_scale=None, v_scale=None, triples=None) -> np.ndarray:
+    """Reference output of a paged decode with T query tokens per sequence
+    (speculative verification or a short chunk decoded against the cache;
+    mlxcel PR #717, "Server integration": INT8 chunked prefill followed by
+    decode).
+
+    q [B, T, Hq, D]. The T new tokens are the last T positions of each
+    sequence (context_lens[b] counts them): query token j sits at position
+    p = context_lens[b] - T + j and attends to positions 0..p (causal among
+    the new tokens); p < 0 gives a zero row. ``kind`` is "int8", "static" or
+    "16bit" (with ``kv_dtype``). Returns float64 [B, T, Hq, D]; rows outside
+    ``triples`` (a list of (b, j, h)) stay NaN.
+    """
+    qf = as_f32(q)
+    B, T, hq, d = qf.shape
+    group = hq // num_kv_heads
+    out = np.full((B, T, hq, d), np.nan)
+    want = {}
+    for b, j, h in (triples if triples is not None else
+                    [(b, j, h) for b in range(B) for j in range(T) for h in range(hq)]):
+        want.setdefault(b, set()).add((j, h))
+    for b, jh in want.items():
+        L = int(context_lens[b])
+        gs = sorted({h // group for _, h in jh})
+        k, v = _sequence_kv(kind, pool, block_tables[b], L, block_size, num_kv_heads,
+                            head_dim, gs, kv_dtype, k_scale, v_scale)
+        for j, h in sorted(jh):
+            n = L - T + j + 1  # positions this query token sees
+            i = gs.index(h // group)
+            if n <= 0:
+                out[b, j, h] = 0.0
+                continue
+            out[b, j, h] = attend_one_sequence(qf[b, j, h][None], k[:n, i:i + 1],
+                                               v[:n, i:i + 1], sm_scale)[0]
+    return out

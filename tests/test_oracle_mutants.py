@@ -254,3 +254,54 @@ def test_static_attention_mutant_is_caught(name, monkeypatch):
 
 def test_unmutated_static_attention_passes_the_same_pins():
     assert not _caught(STATIC_ATT_PINS)
+
+
+# ---- multi-token query ----------------------------------------------------
+from tests import test_oracle_multi as TM  # noqa: E402
+
+
+def _multi(visible):
+    """decode_multi_from_pool with the number of visible positions of query
+    token j given by visible(L, T, j)."""
+    def f(kind, pool, block_tables, context_lens, q, sm_scale, block_size, num_kv_heads,
+          head_dim, kv_dtype=None, k_scale=None, v_scale=None, triples=None):
+        qf = oquant.as_f32(q)
+        B, T, hq, d = qf.shape
+        g = hq // num_kv_heads
+        out = np.zeros((B, T, hq, d))
+        for b in range(B):
+            L = int(context_lens[b])
+            k, v = oatt._sequence_kv(kind, pool, block_tables[b], L, block_size, num_kv_heads,
+                                     head_dim, list(range(num_kv_heads)), kv_dtype, k_scale,
+                                     v_scale)
+            for j in range(T):
+                n = min(L, visible(L, T, j))
+                for h in range(hq):
+                    if n > 0:
+                        out[b, j, h] = oatt.attend_one_sequence(
+                            qf[b, j, h][None], k[:n, h // g:h // g + 1],
+                            v[:n, h // g:h // g + 1], sm_scale)[0]
+        return out
+    return f
+
+
+MULTI_MUTANTS = {
+    "no causal mask among the new tokens": _multi(lambda L, T, j: L),
+    "causal limit one short": _multi(lambda L, T, j: L - T + j),
+    "query tokens in reverse order": _multi(lambda L, T, j: L - j),
+}
+
+MULTI_PINS = [
+    lambda: TM.test_multi_matches_pure_python_brute_force("int8", 3, 8, 2, 64),
+    lambda: TM.test_one_visible_position_and_tokens_before_the_start(),
+]
+
+
+@pytest.mark.parametrize("name", sorted(MULTI_MUTANTS))
+def test_multi_mutant_is_caught(name, monkeypatch):
+    monkeypatch.setattr(oracle, "decode_multi_from_pool", MULTI_MUTANTS[name])
+    assert _caught(MULTI_PINS), name
+
+
+def test_unmutated_multi_passes_the_same_pins():
+    assert not _caught(MULTI_PINS)
