@@ -327,6 +327,55 @@ int paged_attn_decode_int8_static_append(
     int max_context_len, float sm_scale, float k_scale, float v_scale, void* workspace,
     size_t workspace_bytes, int32_t* err_flag, void* stream);
 
+/* Decode with several query tokens per sequence: speculative verification
+ * of draft tokens, or a short chunk decoded against the cache (mlxcel PR
+ * #717, "Server integration": INT8 chunked prefill followed by decode; the
+ * multi-token case of the paged decode of MoE-Infinity PR #183, "What
+ * landed"). The num_query_tokens = T new tokens are the last T positions of
+ * each sequence and must already be in the pool (written with
+ * kv_quant_int8_sym_write); context_lens[b] counts them. Query token j of
+ * sequence b sits at position context_lens[b] - T + j and attends to
+ * positions 0 .. context_lens[b] - T + j (causal among the new tokens); a
+ * token whose position is negative gets a zero row.
+ *   out   device [num_seqs][T][num_q_heads][head_dim] of out_dtype through
+ *         the strides out_stride_seq / _tok / _head (elements).
+ *   q     device [num_seqs][T][num_q_heads][head_dim] of q_dtype through
+ *         q_stride_seq / _tok / _head.
+ *   workspace  at least pdakv_decode_multi_workspace_bytes() for the same
+ *         sizes, 16-byte aligned.
+ * Other arguments as paged_attn_decode_int8. The T x (num_q_heads /
+ * num_kv_heads) query columns of a KV head are processed in tiles of 16
+ * matrix-instruction columns that stream the KV head's pages once per tile.
+ * Returns PDAKV_ERR_INVALID_ARG for num_query_tokens < 1. */
+int paged_attn_decode_int8_multi(
+    void* out, int out_dtype, int64_t out_stride_seq, int64_t out_stride_tok,
+    int64_t out_stride_head, const void* q, int q_dtype, int64_t q_stride_seq,
+    int64_t q_stride_tok, int64_t q_stride_head, int num_query_tokens, const void* kv_pool,
+    int64_t num_blocks, int block_size, const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
+    int32_t* err_flag, void* stream);
+
+/* The several-token decode over 16-bit pages (the control); same arguments
+ * as paged_attn_decode_int8_multi, kv_pool a PDAKV_KV_16BIT pool of q's
+ * dtype. */
+int paged_attn_decode_fp16_multi(
+    void* out, int out_dtype, int64_t out_stride_seq, int64_t out_stride_tok,
+    int64_t out_stride_head, const void* q, int q_dtype, int64_t q_stride_seq,
+    int64_t q_stride_tok, int64_t q_stride_head, int num_query_tokens, const void* kv_pool,
+    int64_t num_blocks, int block_size, const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
+    int32_t* err_flag, void* stream);
+
+/* Workspace of the several-token decode calls: the layout of
+ * pdakv_decode_workspace_bytes with units of (sequence, KV head, tile of 16
+ * query columns), min(T * G, 16) columns per partial slot; 0 when num_seqs,
+ * num_query_tokens or max_context_len is 0. With num_query_tokens = 1 it
+ * equals pdakv_decode_workspace_bytes. */
+size_t pdakv_decode_multi_workspace_bytes(int num_seqs, int num_query_tokens, int num_q_heads,
+                                          int num_kv_heads, int head_dim, int max_context_len);
+
 #ifdef __cplusplus
 }
 #endif

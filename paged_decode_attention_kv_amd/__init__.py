@@ -32,15 +32,19 @@ from ._lib import (  # noqa: F401
     kv_write_16bit,
     paged_attn_decode_fp16,
     paged_attn_decode_fp16_append,
+    paged_attn_decode_fp16_multi,
     paged_attn_decode_int8,
     paged_attn_decode_int8_append,
+    paged_attn_decode_int8_multi,
     paged_attn_decode_int8_static,
     paged_attn_decode_int8_static_append,
     pdakv_capabilities,
     pdakv_decode_plan,
+    pdakv_decode_multi_workspace_bytes,
     pdakv_decode_workspace_bytes,
     pdakv_page_bytes,
     pdakv_status_string,
     pdakv_version,
 )
-from .memory import DecodeBuffers, alloc_pool, alloc_workspace  # noqa: F401
+from .memory import (DecodeBuffers, alloc_multi_workspace, alloc_pool,  # noqa: F401
+                     alloc_workspace)

@@ -68,6 +68,12 @@ _d = _SIGS["paged_attn_decode_int8"][1]
 _SIGS["paged_attn_decode_int8_static"] = (_c_int, _d[:20] + [_c_f, _c_f] + _d[20:])
 _a = _SIGS["paged_attn_decode_int8_append"][1]
 _SIGS["paged_attn_decode_int8_static_append"] = (_c_int, _a[:28] + [_c_f, _c_f] + _a[28:])
+# several query tokens: token strides of out and q, and the token count
+_SIGS["paged_attn_decode_int8_multi"] = (
+    _c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int] +
+    _d[8:])
+_SIGS["paged_attn_decode_fp16_multi"] = _SIGS["paged_attn_decode_int8_multi"]
+_SIGS["pdakv_decode_multi_workspace_bytes"] = (ctypes.c_size_t, [_c_int] * 6)
 
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -136,6 +142,13 @@ def pdakv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: 
                                  head_dim: int, max_context_len: int) -> int:
     return int(_lib.pdakv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                  max_context_len))
+
+
+def pdakv_decode_multi_workspace_bytes(num_seqs: int, num_query_tokens: int, num_q_heads: int,
+                                       num_kv_heads: int, head_dim: int,
+                                       max_context_len: int) -> int:
+    return int(_lib.pdakv_decode_multi_workspace_bytes(num_seqs, num_query_tokens, num_q_heads,
+                                                       num_kv_heads, head_dim, max_context_len))
 
 
 # ---- device entry points --------------------------------------------------
@@ -278,3 +291,44 @@ def paged_attn_decode_int8_static_append(out, q, k_new, v_new, kv_pool, num_bloc
                    num_blocks, block_tables, context_lens, num_kv_heads, max_context_len,
                    sm_scale, workspace, block_size, err_flag, stream,
                    scales=(float(k_scale), float(v_scale)))
+
+
+# ---- several query tokens per sequence --------------------------------------
+
+def _decode_multi(fn_name, out, q, kv_pool, num_blocks, block_tables, context_lens,
+                  num_kv_heads, max_context_len, sm_scale, workspace, block_size, err_flag,
+                  stream):
+    B, T, hq, d = q.shape
+    if q.stride(3) != 1 or out.stride(3) != 1:
+        raise ValueError("the head_dim stride of q and out must be 1")
+    if tuple(out.shape) != (B, T, hq, d):
+        raise ValueError("out must have the shape of q")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = getattr(_lib, fn_name)(
+        _ptr(out), _dtype_code(out.dtype), out.stride(0), out.stride(1), out.stride(2),
+        _ptr(q), _dtype_code(q.dtype), q.stride(0), q.stride(1), q.stride(2), T,
+        _ptr(kv_pool), num_blocks, block_size, _ptr(block_tables), block_tables.stride(0),
+        _ptr(context_lens), B, hq, num_kv_heads, d, max_context_len, float(sm_scale),
+        _ptr(workspace), ws_bytes, _ptr(err_flag), _stream(stream))
+    _check(fn_name, st)
+
+
+def paged_attn_decode_int8_multi(out, q, kv_pool, num_blocks: int, block_tables, context_lens,
+                                 num_kv_heads: int, max_context_len: int, sm_scale: float,
+                                 workspace=None, block_size: int = 16, err_flag=None,
+                                 stream=None) -> None:
+    """Decode with q [B, T, Hq, D]: the last T positions of every sequence
+    (causal among them) over INT8 pages; writes out [B, T, Hq, D]."""
+    _decode_multi("paged_attn_decode_int8_multi", out, q, kv_pool, num_blocks, block_tables,
+                  context_lens, num_kv_heads, max_context_len, sm_scale, workspace, block_size,
+                  err_flag, stream)
+
+
+def paged_attn_decode_fp16_multi(out, q, kv_pool, num_blocks: int, block_tables, context_lens,
+                                 num_kv_heads: int, max_context_len: int, sm_scale: float,
+                                 workspace=None, block_size: int = 16, err_flag=None,
+                                 stream=None) -> None:
+    """The several-token decode over 16-bit pages (the control)."""
+    _decode_multi("paged_attn_decode_fp16_multi", out, q, kv_pool, num_blocks, block_tables,
+                  context_lens, num_kv_heads, max_context_len, sm_scale, workspace, block_size,
+                  err_flag, stream)

@@ -69,16 +69,43 @@ int merge_waves(int num_seqs, int num_kv_heads, int max_context_len, int64_t wav
   return w;
 }
 
+// Query columns of a call: T query tokens x G query heads per KV head, in
+// tiles of at most 16 (one MFMA operand); each (KV head, tile) is a unit.
+struct Columns {
+  int cols, ntile, slot_cols;
+};
+Columns columns(int num_q_heads, int num_kv_heads, int num_query_tokens) {
+  Columns c;
+  c.cols = num_query_tokens * (num_q_heads / num_kv_heads);
+  c.ntile = (c.cols + 15) / 16;
+  c.slot_cols = std::min(c.cols, 16);
+  return c;
+}
+
 // Partial results region of the decode workspace (a multiple of 16 bytes):
-// [waves + units][G][D + 2] floats. The INT8 plan has the most waves; its
-// slots serve the other formats too.
-size_t partials_bytes(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-                      int max_context_len) {
-  const int64_t v = plan_waves(PDAKV_KV_INT8_SYM, num_seqs, num_kv_heads, max_context_len);
-  const int64_t slots = v + static_cast<int64_t>(num_seqs) * num_kv_heads;
-  const size_t bytes = static_cast<size_t>(slots) * (num_q_heads / num_kv_heads) *
-                       (head_dim + 2) * sizeof(float);
+// [waves + units][C][D + 2] floats, C = columns per unit. The INT8 plan has
+// the most waves; its slots serve the other formats too.
+size_t partials_bytes(int num_seqs, int num_query_tokens, int num_q_heads, int num_kv_heads,
+                      int head_dim, int max_context_len) {
+  const Columns c = columns(num_q_heads, num_kv_heads, num_query_tokens);
+  const int vheads = num_kv_heads * c.ntile;
+  const int64_t v = plan_waves(PDAKV_KV_INT8_SYM, num_seqs, vheads, max_context_len);
+  const int64_t slots = v + static_cast<int64_t>(num_seqs) * vheads;
+  const size_t bytes = static_cast<size_t>(slots) * c.slot_cols * (head_dim + 2) * sizeof(float);
   return (bytes + 15) / 16 * 16;
+}
+
+size_t decode_ws_bytes(int num_seqs, int num_query_tokens, int num_q_heads, int num_kv_heads,
+                       int head_dim, int max_context_len) {
+  if (num_seqs <= 0 || num_query_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || max_context_len <= 0 || num_q_heads % num_kv_heads != 0)
+    return 0;
+  const Columns c = columns(num_q_heads, num_kv_heads, num_query_tokens);
+  const int vheads = num_kv_heads * c.ntile;
+  if (item_bound(num_seqs, vheads, max_context_len) > kMaxItems) return 0;
+  return partials_bytes(num_seqs, num_query_tokens, num_q_heads, num_kv_heads, head_dim,
+                        max_context_len) +
+         static_cast<size_t>(num_seqs) * vheads * 2 * sizeof(int32_t);
 }
 
 int check_write(const void* k_src, const void* v_src, int src_dtype, int64_t num_tokens,
@@ -98,8 +125,9 @@ int check_write(const void* k_src, const void* v_src, int src_dtype, int64_t num
   return PDAKV_OK;
 }
 
-int check_decode(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, const void* q,
-                 int q_dtype, int64_t q_ss, int64_t q_sh, const void* kv_pool,
+int check_decode(void* out, int out_dtype, int64_t out_ss, int64_t out_st, int64_t out_sh,
+                 const void* q, int q_dtype, int64_t q_ss, int64_t q_st, int64_t q_sh, int qtok,
+                 const void* kv_pool,
                  int64_t num_blocks, int block_size, const int32_t* block_tables,
                  int64_t bt_stride, const int32_t* context_lens, int num_seqs, int num_q_heads,
                  int num_kv_heads, int head_dim, int max_context_len, float sm_scale,
@@ -109,7 +137,8 @@ int check_decode(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, const
       out_dtype != PDAKV_DTYPE_BF16)
     return PDAKV_ERR_DTYPE;
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
-      num_blocks < 0 || bt_stride < 0 || out_ss < 0 || out_sh < 0 || q_ss < 0 || q_sh < 0)
+      num_blocks < 0 || bt_stride < 0 || out_ss < 0 || out_st < 0 || out_sh < 0 || q_ss < 0 ||
+      q_st < 0 || q_sh < 0 || qtok <= 0)
     return PDAKV_ERR_INVALID_ARG;
   if (!std::isfinite(sm_scale)) return PDAKV_ERR_INVALID_ARG;
   if (num_q_heads % num_kv_heads != 0) return PDAKV_ERR_UNSUPPORTED;
@@ -125,14 +154,17 @@ int check_decode(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, const
   // head blocks are indexed as block * num_kv_heads + head in int32
   if (num_blocks * num_kv_heads > INT32_MAX) return PDAKV_ERR_UNSUPPORTED;
   if (kv_pool && !aligned16(kv_pool)) return PDAKV_ERR_INVALID_ARG;
-  const size_t need = pdakv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
-                                                   head_dim, max_context_len);
+  // device indexes are int32: items, (sequence, query token, query head) rows
+  // of the merge grid
+  const Columns c = columns(num_q_heads, num_kv_heads, qtok);
+  if (item_bound(num_seqs, num_kv_heads * c.ntile, max_context_len) > kMaxItems)
+    return PDAKV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(num_seqs) * qtok * num_q_heads > INT32_MAX)
+    return PDAKV_ERR_UNSUPPORTED;
+  const size_t need = decode_ws_bytes(num_seqs, qtok, num_q_heads, num_kv_heads, head_dim,
+                                      max_context_len);
   if (need > 0 && (!workspace || workspace_bytes < need)) return PDAKV_ERR_WORKSPACE;
   if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15u)) return PDAKV_ERR_INVALID_ARG;
-  // device indexes are int32: items, (sequence, query head) pairs of the merge grid
-  if (item_bound(num_seqs, num_kv_heads, max_context_len) > kMaxItems)
-    return PDAKV_ERR_UNSUPPORTED;
-  if (static_cast<int64_t>(num_seqs) * num_q_heads > INT32_MAX) return PDAKV_ERR_UNSUPPORTED;
   return PDAKV_OK;
 }
 
@@ -150,17 +182,35 @@ struct Scales {
   float k = 1.f, v = 1.f;
 };
 
-int decode_common(int fmt, Scales sc, void* out, int out_dtype, int64_t out_ss, int64_t out_sh,
-                  const void* q, int q_dtype, int64_t q_ss, int64_t q_sh, const AppendRows* app,
+// Output and query views: [num_seqs][tokens][num_q_heads][head_dim] through
+// element strides (one token: the token stride is unused).
+struct Rows {
+  void* out;
+  int out_dtype;
+  int64_t out_ss, out_st, out_sh;
+  const void* q;
+  int q_dtype;
+  int64_t q_ss, q_st, q_sh;
+  int tokens;
+  bool multi;  // launch the several-token kernels
+};
+
+Rows one_token(void* out, int out_dtype, int64_t out_ss, int64_t out_sh, const void* q,
+               int q_dtype, int64_t q_ss, int64_t q_sh) {
+  return Rows{out, out_dtype, out_ss, 0, out_sh, q, q_dtype, q_ss, 0, q_sh, 1, false};
+}
+
+int decode_common(int fmt, Scales sc, const Rows& r, const AppendRows* app,
                   const void* kv_pool, int64_t num_blocks, int block_size,
                   const int32_t* block_tables, int64_t bt_stride, const int32_t* context_lens,
                   int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                   int max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
                   int32_t* err_flag, void* stream) {
-  int st = check_decode(out, out_dtype, out_ss, out_sh, q, q_dtype, q_ss, q_sh, kv_pool,
-                        num_blocks, block_size, block_tables, bt_stride, context_lens,
-                        num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
-                        sm_scale, workspace, workspace_bytes);
+  int st = check_decode(r.out, r.out_dtype, r.out_ss, r.out_st, r.out_sh, r.q, r.q_dtype, r.q_ss,
+                        r.q_st, r.q_sh, r.tokens, kv_pool, num_blocks, block_size,
+                        block_tables, bt_stride, context_lens, num_seqs, num_q_heads,
+                        num_kv_heads, head_dim, max_context_len, sm_scale, workspace,
+                        workspace_bytes);
   if (st != PDAKV_OK) return st;
   const double scale_log2 = static_cast<double>(sm_scale) * sc.k * 1.4426950408889634;
   if (!valid_scale(sc.k) || !valid_scale(sc.v) || !std::isfinite(static_cast<float>(scale_log2)))
@@ -173,14 +223,16 @@ int decode_common(int fmt, Scales sc, void* out, int out_dtype, int64_t out_ss, 
   }
   if (num_seqs == 0) return st;
   DecodeArgs a{};
-  a.out = out;
-  a.out_dtype = out_dtype;
-  a.out_ss = out_ss;
-  a.out_sh = out_sh;
-  a.q = q;
-  a.q_ss = q_ss;
-  a.q_sh = q_sh;
-  a.q_vec16 = aligned16(q) && q_ss % 8 == 0 && q_sh % 8 == 0;
+  a.out = r.out;
+  a.out_dtype = r.out_dtype;
+  a.out_ss = r.out_ss;
+  a.out_st = r.out_st;
+  a.out_sh = r.out_sh;
+  a.q = r.q;
+  a.q_ss = r.q_ss;
+  a.q_st = r.q_st;
+  a.q_sh = r.q_sh;
+  a.q_vec16 = aligned16(r.q) && r.q_ss % 8 == 0 && r.q_st % 8 == 0 && r.q_sh % 8 == 0;
   a.pool = static_cast<uint8_t*>(const_cast<void*>(kv_pool));
   a.num_blocks = num_blocks;
   a.page_bytes =
@@ -192,18 +244,24 @@ int decode_common(int fmt, Scales sc, void* out, int out_dtype, int64_t out_ss, 
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.group = num_q_heads / num_kv_heads;
+  const Columns cols = columns(num_q_heads, num_kv_heads, r.tokens);
+  a.qtok = r.tokens;
+  a.cols = cols.cols;
+  a.ntile = cols.ntile;
+  a.vheads = num_kv_heads * cols.ntile;
+  a.slot_cols = cols.slot_cols;
   a.max_ctx = max_context_len;
   a.scale_log2 = static_cast<float>(scale_log2);
   a.out_mul = fmt == PDAKV_KV_INT8_STATIC ? sc.v : 1.f;
   a.k_scale = sc.k;
   a.v_scale = sc.v;
-  a.num_waves = static_cast<int>(plan_waves(fmt, num_seqs, num_kv_heads, max_context_len));
-  a.merge_waves = merge_waves(num_seqs, num_kv_heads, max_context_len, a.num_waves);
+  a.num_waves = static_cast<int>(plan_waves(fmt, num_seqs, a.vheads, max_context_len));
+  a.merge_waves = merge_waves(num_seqs, a.vheads, max_context_len, a.num_waves);
   {
     // LDS staging per decode pass and segment: the unit's q rows (16-bit),
-    // its result (accumulator, max, sum per query head) and the appended
-    // token (4 * head_dim bytes), regions aligned to 16 bytes
-    const int qb = a.group * head_dim * 2, rb = a.group * (head_dim + 2) * 4;
+    // its result (accumulator, max, sum per column) and the appended token
+    // (4 * head_dim bytes), regions aligned to 16 bytes
+    const int qb = a.slot_cols * head_dim * 2, rb = a.slot_cols * (head_dim + 2) * 4;
     const int nb = 4 * head_dim;
     a.seg_cap = std::max(1, std::min(64, (pdakv::kLdsPerWave - 16) / (qb + rb + nb)));
     a.lds_wave_bytes = (a.seg_cap * (qb + rb) + 15) / 16 * 16 + a.seg_cap * nb;
@@ -211,7 +269,7 @@ int decode_common(int fmt, Scales sc, void* out, int out_dtype, int64_t out_ss, 
   a.ws = static_cast<float*>(workspace);
   a.desc = reinterpret_cast<int2*>(
       static_cast<uint8_t*>(workspace) +
-      partials_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len));
+      partials_bytes(num_seqs, r.tokens, num_q_heads, num_kv_heads, head_dim, max_context_len));
   a.err = err_flag;
   if (app) {
     a.append = 1;
@@ -225,7 +283,11 @@ int decode_common(int fmt, Scales sc, void* out, int out_dtype, int64_t out_ss, 
     a.vn_sd = app->vsd;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool bf16 = q_dtype == PDAKV_DTYPE_BF16;
+  const bool bf16 = r.q_dtype == PDAKV_DTYPE_BF16;
+  if (r.multi)
+    return hip_status(fmt == PDAKV_KV_INT8_SYM
+                          ? pdakv::launch_decode_int8_multi(a, head_dim, bf16, s)
+                          : pdakv::launch_decode_16bit_multi(a, head_dim, bf16, s));
   switch (fmt) {
     case PDAKV_KV_INT8_SYM: return hip_status(pdakv::launch_decode_int8(a, head_dim, bf16, s));
     case PDAKV_KV_INT8_STATIC:
@@ -333,12 +395,14 @@ int pdakv_decode_plan(int kv_format, int num_seqs, int num_kv_heads, int max_con
 
 size_t pdakv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                     int head_dim, int max_context_len) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-      max_context_len <= 0 || num_q_heads % num_kv_heads != 0)
-    return 0;
-  if (item_bound(num_seqs, num_kv_heads, max_context_len) > kMaxItems) return 0;
-  return partials_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len) +
-         static_cast<size_t>(num_seqs) * num_kv_heads * 2 * sizeof(int32_t);
+  return decode_ws_bytes(num_seqs, 1, num_q_heads, num_kv_heads, head_dim, max_context_len);
+}
+
+size_t pdakv_decode_multi_workspace_bytes(int num_seqs, int num_query_tokens, int num_q_heads,
+                                          int num_kv_heads, int head_dim,
+                                          int max_context_len) {
+  return decode_ws_bytes(num_seqs, num_query_tokens, num_q_heads, num_kv_heads, head_dim,
+                         max_context_len);
 }
 
 int kv_quant_int8_sym_write(const void* k_src, const void* v_src, int src_dtype,
@@ -375,8 +439,9 @@ int paged_attn_decode_int8(void* out, int out_dtype, int64_t out_stride_seq,
                            int max_context_len, float sm_scale, void* workspace,
                            size_t workspace_bytes, int32_t* err_flag, void* stream) {
   return decode_common(PDAKV_KV_INT8_SYM, Scales{},
-                       out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
-                       q_stride_seq, q_stride_head, nullptr, kv_pool, num_blocks, block_size,
+                       one_token(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
+                                 q_stride_seq, q_stride_head),
+                       nullptr, kv_pool, num_blocks, block_size,
                        block_tables, block_table_stride, context_lens, num_seqs,
                        num_q_heads, num_kv_heads, head_dim, max_context_len, sm_scale,
                        workspace, workspace_bytes, err_flag, stream);
@@ -391,8 +456,9 @@ int paged_attn_decode_fp16(void* out, int out_dtype, int64_t out_stride_seq,
                            int max_context_len, float sm_scale, void* workspace,
                            size_t workspace_bytes, int32_t* err_flag, void* stream) {
   return decode_common(PDAKV_KV_16BIT, Scales{},
-                       out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
-                       q_stride_seq, q_stride_head, nullptr, kv_pool, num_blocks, block_size,
+                       one_token(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
+                                 q_stride_seq, q_stride_head),
+                       nullptr, kv_pool, num_blocks, block_size,
                        block_tables, block_table_stride, context_lens, num_seqs,
                        num_q_heads, num_kv_heads, head_dim, max_context_len, sm_scale,
                        workspace, workspace_bytes, err_flag, stream);
@@ -417,8 +483,9 @@ int paged_attn_decode_int8_append(
   app.vsh = v_stride_head;
   app.vsd = v_stride_dim;
   return decode_common(PDAKV_KV_INT8_SYM, Scales{},
-                       out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
-                       q_stride_seq, q_stride_head, &app, kv_pool, num_blocks, block_size,
+                       one_token(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
+                                 q_stride_seq, q_stride_head),
+                       &app, kv_pool, num_blocks, block_size,
                        block_tables, block_table_stride, context_lens, num_seqs,
                        num_q_heads, num_kv_heads, head_dim, max_context_len, sm_scale,
                        workspace, workspace_bytes, err_flag, stream);
@@ -443,8 +510,9 @@ int paged_attn_decode_fp16_append(
   app.vsh = v_stride_head;
   app.vsd = v_stride_dim;
   return decode_common(PDAKV_KV_16BIT, Scales{},
-                       out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
-                       q_stride_seq, q_stride_head, &app, kv_pool, num_blocks,
+                       one_token(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
+                                 q_stride_seq, q_stride_head),
+                       &app, kv_pool, num_blocks,
                        block_size, block_tables, block_table_stride, context_lens,
                        num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                        sm_scale, workspace, workspace_bytes, err_flag, stream);
@@ -472,8 +540,9 @@ int paged_attn_decode_int8_static(void* out, int out_dtype, int64_t out_stride_s
                                   int num_kv_heads, int head_dim, int max_context_len,
                                   float sm_scale, float k_scale, float v_scale, void* workspace,
                                   size_t workspace_bytes, int32_t* err_flag, void* stream) {
-  return decode_common(PDAKV_KV_INT8_STATIC, Scales{k_scale, v_scale}, out, out_dtype,
-                       out_stride_seq, out_stride_head, q, q_dtype, q_stride_seq, q_stride_head,
+  return decode_common(PDAKV_KV_INT8_STATIC, Scales{k_scale, v_scale},
+                       one_token(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
+                                 q_stride_seq, q_stride_head),
                        nullptr, kv_pool, num_blocks, block_size, block_tables,
                        block_table_stride, context_lens, num_seqs, num_q_heads, num_kv_heads,
                        head_dim, max_context_len, sm_scale, workspace, workspace_bytes, err_flag,
@@ -498,11 +567,44 @@ int paged_attn_decode_int8_static_append(
   app.vst = v_stride_seq;
   app.vsh = v_stride_head;
   app.vsd = v_stride_dim;
-  return decode_common(PDAKV_KV_INT8_STATIC, Scales{k_scale, v_scale}, out, out_dtype,
-                       out_stride_seq, out_stride_head, q, q_dtype, q_stride_seq, q_stride_head,
+  return decode_common(PDAKV_KV_INT8_STATIC, Scales{k_scale, v_scale},
+                       one_token(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
+                                 q_stride_seq, q_stride_head),
                        &app, kv_pool, num_blocks, block_size, block_tables, block_table_stride,
                        context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                        max_context_len, sm_scale, workspace, workspace_bytes, err_flag, stream);
+}
+
+int paged_attn_decode_int8_multi(
+    void* out, int out_dtype, int64_t out_stride_seq, int64_t out_stride_tok,
+    int64_t out_stride_head, const void* q, int q_dtype, int64_t q_stride_seq,
+    int64_t q_stride_tok, int64_t q_stride_head, int num_query_tokens, const void* kv_pool,
+    int64_t num_blocks, int block_size, const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
+    int32_t* err_flag, void* stream) {
+  const Rows r{out, out_dtype, out_stride_seq, out_stride_tok, out_stride_head, q,
+               q_dtype, q_stride_seq, q_stride_tok, q_stride_head, num_query_tokens, true};
+  return decode_common(PDAKV_KV_INT8_SYM, Scales{}, r, nullptr, kv_pool, num_blocks, block_size,
+                       block_tables, block_table_stride, context_lens, num_seqs, num_q_heads,
+                       num_kv_heads, head_dim, max_context_len, sm_scale, workspace,
+                       workspace_bytes, err_flag, stream);
+}
+
+int paged_attn_decode_fp16_multi(
+    void* out, int out_dtype, int64_t out_stride_seq, int64_t out_stride_tok,
+    int64_t out_stride_head, const void* q, int q_dtype, int64_t q_stride_seq,
+    int64_t q_stride_tok, int64_t q_stride_head, int num_query_tokens, const void* kv_pool,
+    int64_t num_blocks, int block_size, const int32_t* block_tables, int64_t block_table_stride,
+    const int32_t* context_lens, int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+    int max_context_len, float sm_scale, void* workspace, size_t workspace_bytes,
+    int32_t* err_flag, void* stream) {
+  const Rows r{out, out_dtype, out_stride_seq, out_stride_tok, out_stride_head, q,
+               q_dtype, q_stride_seq, q_stride_tok, q_stride_head, num_query_tokens, true};
+  return decode_common(PDAKV_KV_16BIT, Scales{}, r, nullptr, kv_pool, num_blocks, block_size,
+                       block_tables, block_table_stride, context_lens, num_seqs, num_q_heads,
+                       num_kv_heads, head_dim, max_context_len, sm_scale, workspace,
+                       workspace_bytes, err_flag, stream);
 }
 
 }  // extern "C"

@@ -126,8 +126,14 @@ __device__ void zero_rows(const DecodeArgs& a, const SeqChunk& s, int wave, int 
   while (m) {
     const int bb = 64 * s.c + __builtin_ctzll(m);
     m &= m - 1;
-    for (int i = lane; i < a.num_q_heads * D; i += 64)
-      store_out(a.out, a.out_dtype, bb * a.out_ss + (i / D) * a.out_sh + i % D, 0.f);
+    const int rows = a.qtok * a.num_q_heads;  // (query token, head) rows
+    for (int i = lane; i < rows * D; i += 64) {
+      const int r = i / D;
+      store_out(a.out, a.out_dtype,
+                bb * a.out_ss + (r / a.num_q_heads) * a.out_st + (r % a.num_q_heads) * a.out_sh +
+                    i % D,
+                0.f);
+    }
   }
 }
 
@@ -135,12 +141,13 @@ __device__ void zero_rows(const DecodeArgs& a, const SeqChunk& s, int wave, int 
 // Online softmax state and shared helpers
 // ---------------------------------------------------------------------------
 
-// Eight consecutive 16-bit q elements (dims d0..d0+7) of head h, as four
-// words. One 16-byte load when the host found q's pointer and strides 16-byte
-// aligned, else eight 2-byte loads. Always issued (no per-lane branch), so the
-// loads of a wave overlap.
-__device__ __forceinline__ u4_t q_chunk8(const DecodeArgs& a, int b, int h, int d0) {
-  const uint16_t* row = static_cast<const uint16_t*>(a.q) + b * a.q_ss + h * a.q_sh + d0;
+// Eight consecutive 16-bit q elements (dims d0..d0+7) of query token j, head
+// h, as four words. One 16-byte load when the host found q's pointer and
+// strides 16-byte aligned, else eight 2-byte loads. Always issued (no per-lane
+// branch), so the loads of a wave overlap.
+__device__ __forceinline__ u4_t q_chunk8(const DecodeArgs& a, int b, int j, int h, int d0) {
+  const uint16_t* row =
+      static_cast<const uint16_t*>(a.q) + b * a.q_ss + j * a.q_st + h * a.q_sh + d0;
   if (a.q_vec16) return *reinterpret_cast<const u4_t*>(row);
   u4_t w;
 #pragma unroll
@@ -286,20 +293,25 @@ __device__ __forceinline__ int lane_token(int page_tok) {
   return page_tok + 4 * static_cast<int>((threadIdx.x & 63) >> 4);
 }
 
+// Limits of one page step: tokens at or past L (wave-uniform: the context
+// length, or the page start for a skipped page) hold no data; the lane's
+// query column attends to tokens below Lc (<= L; below L only for the
+// earlier tokens of a multi-token query); Lmin (wave-uniform) is the
+// smallest Lc of the wave, so pages below it need no mask at all.
+
 // One page starting at token page_tok (wave-uniform). The tokens at or past
-// the limit L (the context length; the page start for a skipped page) get V
-// scale 1.0 (their slots may hold anything) and logit -inf. (A separate
-// unmasked path for full pages costs more registers than the masks cost
-// instructions.)
+// L get V scale 1.0 (their slots may hold anything); those at or past Lc get
+// logit -inf. (A separate unmasked path for full pages costs more registers
+// than the masks cost instructions.)
 template <int D>
 __device__ __forceinline__ void int8_page_step(const Int8Page<D>& pg, const h8_t* qf,
-                                               float qscale, int page_tok, int L,
-                                               SoftmaxState<D / 16>& st) {
+                                               float qscale, int page_tok, int L, int Lmin,
+                                               int Lc, SoftmaxState<D / 16>& st) {
   constexpr int ND = D / 16;
   const f4_t s = int8_qk<D>(pg, qf);
   const uint32_t ksw[2] = {pg.ks.x, pg.ks.y};
   uint32_t vsw[2] = {pg.vs.x, pg.vs.y};
-  const bool tail = page_tok + kBlockSize > L;
+  const bool tail = page_tok + kBlockSize > Lmin;
   const int tok0 = tail ? lane_token(page_tok) : 0;
   if (tail) {
 #pragma unroll
@@ -320,7 +332,7 @@ __device__ __forceinline__ void int8_page_step(const Int8Page<D>& pg, const h8_t
     f[j] = __builtin_amdgcn_frexp_manth(sv);
     // base-2 logit plus the exponent of the V scale: P = 2^(z - m) * f
     z[j] = s[j] * sk * qscale + static_cast<float>(e[j]);
-    if (tail) z[j] = tok0 + j < L ? z[j] : -INFINITY;
+    if (tail) z[j] = tok0 + j < Lc ? z[j] : -INFINITY;
     zmax = max_nc(zmax, z[j]);
   }
   raise_max(st, zmax);
@@ -372,18 +384,18 @@ __device__ __forceinline__ void load_static_page(StaticPage<D>& pg, const uint8_
 // their slots is a finite code, so 0 * code adds nothing).
 template <int D>
 __device__ __forceinline__ void static_page_step(const StaticPage<D>& pg, const h8_t* qf,
-                                                 float qscale, int page_tok, int L,
+                                                 float qscale, int page_tok, int Lmin, int Lc,
                                                  SoftmaxState<D / 16>& st) {
   constexpr int ND = D / 16;
   const f4_t s = int8_qk<D>(pg, qf);
-  const bool tail = page_tok + kBlockSize > L;
+  const bool tail = page_tok + kBlockSize > Lmin;
   const int tok0 = tail ? lane_token(page_tok) : 0;
   float z[4];
   float zmax = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     z[j] = s[j] * qscale;
-    if (tail) z[j] = tok0 + j < L ? z[j] : -INFINITY;
+    if (tail) z[j] = tok0 + j < Lc ? z[j] : -INFINITY;
     zmax = max_nc(zmax, z[j]);
   }
   raise_max(st, zmax);
@@ -433,12 +445,12 @@ struct Int8Kind {
     else
       load_int8_page<D>(pg, hp, i16, kb);
   }
-  __device__ __forceinline__ void step(const Page& pg, int page_tok, int L,
+  __device__ __forceinline__ void step(const Page& pg, int page_tok, int L, int Lmin, int Lc,
                                        SoftmaxState<D / 16>& st) const {
     if constexpr (Static)
-      static_page_step<D>(pg, qf, qscale, page_tok, L, st);
+      static_page_step<D>(pg, qf, qscale, page_tok, Lmin, Lc, st);
     else
-      int8_page_step<D>(pg, qf, qscale, page_tok, L, st);
+      int8_page_step<D>(pg, qf, qscale, page_tok, L, Lmin, Lc, st);
   }
   // dimension of accumulator element acc[k][j] in lane (i16, kb)
   static __device__ __forceinline__ int acc_dim(int k, int j, int kb) {
@@ -597,20 +609,20 @@ __device__ __forceinline__ f4_t mfma16x16x16(u2_t a_bits, u2_t b_bits, f4_t c) {
 
 template <int D, bool BF16>
 __device__ __forceinline__ void page16_step(const Page16<D>& pg, const u4_t* qf,
-                                            float scale_log2, int page_tok, int L,
-                                            SoftmaxState<D / 16>& st) {
+                                            float scale_log2, int page_tok, int L, int Lmin,
+                                            int Lc, SoftmaxState<D / 16>& st) {
   constexpr int NJ = D / 32, ND = D / 16;
   f4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < NJ; ++j) s = mfma16x16x32<BF16>(pg.k[j], qf[j], s);
-  const bool tail = page_tok + kBlockSize > L;
+  const bool tail = page_tok + kBlockSize > Lmin;
   const int tok0 = tail ? lane_token(page_tok) : 0;
   float z[4];
   float zmax = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     z[j] = s[j] * scale_log2;
-    if (tail) z[j] = tok0 + j < L ? z[j] : -INFINITY;
+    if (tail) z[j] = tok0 + j < Lc ? z[j] : -INFINITY;
     zmax = max_nc(zmax, z[j]);
   }
   raise_max(st, zmax);
@@ -701,9 +713,9 @@ struct F16Kind {
   static __device__ __forceinline__ void load(Page& pg, const uint8_t* hp, int i16, int kb) {
     load_page16<D>(pg, hp, i16, kb);
   }
-  __device__ __forceinline__ void step(const Page& pg, int page_tok, int L,
+  __device__ __forceinline__ void step(const Page& pg, int page_tok, int L, int Lmin, int Lc,
                                        SoftmaxState<D / 16>& st) const {
-    page16_step<D, BF16>(pg, qf, scale_log2, page_tok, L, st);
+    page16_step<D, BF16>(pg, qf, scale_log2, page_tok, L, Lmin, Lc, st);
   }
   static __device__ __forceinline__ int acc_dim(int k, int j, int kb) {
     return 32 * (k / 2) + 8 * kb + 2 * j + (k % 2);
@@ -768,36 +780,58 @@ struct F16Kind {
 // ---------------------------------------------------------------------------
 
 // Per-wave LDS staging of one pass: the q rows of each segment's unit
-// ([G][D] 16-bit values) and each segment's result ([G][D + 2] floats:
-// accumulator, running max, sum). Sized on the host (a.seg_cap segments).
+// ([C][D] 16-bit values, C = a.slot_cols columns) and each segment's result
+// ([C][D + 2] floats: accumulator, running max, sum). Sized on the host
+// (a.seg_cap segments).
 struct PassLds {
-  uint16_t* q;   // [seg_cap][G][D]
-  float* res;    // [seg_cap][G][D + 2]
+  uint16_t* q;   // [seg_cap][C][D]
+  float* res;    // [seg_cap][C][D + 2]
   uint8_t* nt;   // [seg_cap][kNewTokenBytes(D)]: appended token per segment
 };
+
+// The MFMA columns of virtual KV head vg of a sequence: KV head g, whose
+// columns 0..n-1 are the (query token, head) pairs col0 + c with
+// col = token * group + (head - g * group). One query token: all of KV
+// head vg's query heads. Several: KV head vg / ntile, tile vg % ntile of 16
+// columns.
+struct UnitCols {
+  int g, col0, n;
+};
+template <bool Multi>
+__device__ __forceinline__ UnitCols unit_cols(const DecodeArgs& a, int vg) {
+  if constexpr (!Multi) {
+    return {vg, 0, a.group};
+  } else {
+    const int tile = vg % a.ntile;
+    return {vg / a.ntile, 16 * tile, min(16, a.cols - 16 * tile)};
+  }
+}
 
 // LDS bytes that hold one segment's appended token (16-bit K and V rows, or
 // INT8 codes and scales); a multiple of 16.
 __host__ __device__ constexpr int new_token_bytes(int D) { return 4 * D; }
 
-// Copy the q rows of unit (b, g) into LDS; 16-byte chunks dealt to the lanes.
-template <int D>
-__device__ __forceinline__ void stage_q(const DecodeArgs& a, int b, int g, uint16_t* dst,
+// Copy the q rows of unit (b, vg) into LDS; 16-byte chunks dealt to the lanes.
+template <int D, bool Multi>
+__device__ __forceinline__ void stage_q(const DecodeArgs& a, int b, int vg, uint16_t* dst,
                                         int lane) {
-  const int chunks = a.group * D / 8;
+  const UnitCols uc = unit_cols<Multi>(a, vg);
+  const int chunks = uc.n * D / 8;
   for (int c = lane; c < chunks; c += 64) {
-    const int hh = c / (D / 8), d0 = (c % (D / 8)) * 8;
-    *reinterpret_cast<u4_t*>(dst + hh * D + d0) = q_chunk8(a, b, g * a.group + hh, d0);
+    const int cc = c / (D / 8), d0 = (c % (D / 8)) * 8;
+    const int col = uc.col0 + cc;
+    *reinterpret_cast<u4_t*>(dst + cc * D + d0) =
+        q_chunk8(a, b, col / a.group, uc.g * a.group + col % a.group, d0);
   }
 }
 
-// Leave a segment's softmax state in LDS: [G][D + 2].
+// Leave a segment's softmax state in LDS: [n][D + 2] for its n columns.
 template <class K>
 __device__ __forceinline__ void stash_result(const DecodeArgs& a, SoftmaxState<K::D / 16>& st,
-                                             float* res, int i16, int kb) {
+                                             float* res, int i16, int kb, int n) {
   constexpr int D = K::D, ND = D / 16;
   const float l = col_sum(st.l);
-  if (i16 >= a.group) return;
+  if (i16 >= n) return;
   float* r = res + i16 * (D + 2);
 #pragma unroll
   for (int k = 0; k < ND; ++k)
@@ -809,21 +843,27 @@ __device__ __forceinline__ void stash_result(const DecodeArgs& a, SoftmaxState<K
   }
 }
 
-// Write a stashed result: the output rows when the segment covers its whole
-// unit (zero rows when no token was attendable), else the partial of `slot`.
-template <int D>
-__device__ __forceinline__ void write_result(const DecodeArgs& a, const float* res, int b, int g,
-                                             int slot, bool whole, int lane) {
+// Write a stashed result of unit (b, vg): the output rows when the segment
+// covers its whole unit (zero rows when no token was attendable), else the
+// partial of `slot`.
+template <int D, bool Multi>
+__device__ __forceinline__ void write_result(const DecodeArgs& a, const float* res, int b,
+                                             int vg, int slot, bool whole, int lane) {
+  const UnitCols uc = unit_cols<Multi>(a, vg);
   if (whole) {
-    for (int e = lane; e < a.group * D; e += 64) {
-      const int hh = e / D, d = e % D;
-      const float l = res[hh * (D + 2) + D + 1];
-      const float v = l > 0.f ? res[hh * (D + 2) + d] / l * a.out_mul : 0.f;
-      store_out(a.out, a.out_dtype, b * a.out_ss + (g * a.group + hh) * a.out_sh + d, v);
+    for (int e = lane; e < uc.n * D; e += 64) {
+      const int cc = e / D, d = e % D;
+      const int col = uc.col0 + cc;
+      const float l = res[cc * (D + 2) + D + 1];
+      const float v = l > 0.f ? res[cc * (D + 2) + d] / l * a.out_mul : 0.f;
+      store_out(a.out, a.out_dtype,
+                b * a.out_ss + (col / a.group) * a.out_st +
+                    (uc.g * a.group + col % a.group) * a.out_sh + d,
+                v);
     }
   } else {
-    float* dst = a.ws + static_cast<int64_t>(slot) * a.group * (D + 2);
-    for (int e = lane; e < a.group * (D + 2); e += 64) dst[e] = res[e];
+    float* dst = a.ws + static_cast<int64_t>(slot) * a.slot_cols * (D + 2);
+    for (int e = lane; e < uc.n * (D + 2); e += 64) dst[e] = res[e];
   }
 }
 
@@ -836,10 +876,10 @@ struct Cursor {
 
 // Move to the first page of the next unit with pages; false if the lengths
 // changed under the call (no such unit).
-__device__ __forceinline__ bool next_unit(const DecodeArgs& a, Cursor& cu, int nchunk,
+__device__ __forceinline__ bool next_unit(const DecodeArgs& a, Cursor& cu, int nchunk, int vh,
                                           int lane) {
   cu.p = 0;
-  if (++cu.g < a.num_kv_heads) return true;
+  if (++cu.g < vh) return true;
   cu.g = 0;
   while (true) {
     const uint64_t m = __ballot(cu.lens > 0 && lane > cu.hit);
@@ -863,20 +903,22 @@ __device__ __forceinline__ bool next_unit(const DecodeArgs& a, Cursor& cu, int n
 // through one pipeline (segment switches inside it touch only registers and
 // LDS, so the page loads in flight are never waited for early), then write
 // the stashed results. Returns the number of items done (0: lengths changed).
-template <class K>
+template <class K, bool Multi>
 __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu, int x, int x1,
                                         int P, int wave, int nchunk, const PassLds& lds,
                                         int lane) {
   constexpr int D = K::D, ND = D / 16;
   const int i16 = lane & 15, kb = lane >> 4;
   const int hkv = a.num_kv_heads;
+  const int vh = Multi ? a.vheads : hkv;  // units per sequence
+  const int C = a.slot_cols;              // LDS columns per segment
 
   // plan: lane s keeps segment s's unit, first page, first item, length, L
   int s_unit = 0, s_p = 0, s_start = 0, s_n = 0, s_L = 0, s_whole = 0, s_last = 0;
   int ns = 0, items = 0;
   while (true) {
     const int n = min(min(cu.np - cu.p, x1 - (x + items)), kMaxPagesPerWave - items);
-    const int u = cu.b * hkv + cu.g;
+    const int u = cu.b * vh + cu.g;
     if (cu.p == 0 && lane == 0) {
       // this wave holds the unit's first item: record which waves cover it
       a.desc[u] = make_int2(wave, (x + items + cu.np - 1) / P - wave + 1);
@@ -893,7 +935,7 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     ++ns;
     items += n;
     cu.p += n;
-    if (cu.p == cu.np && x + items < x1 && !next_unit(a, cu, nchunk, lane)) return 0;
+    if (cu.p == cu.np && x + items < x1 && !next_unit(a, cu, nchunk, vh, lane)) return 0;
     if (x + items >= x1 || ns == a.seg_cap || items == kMaxPagesPerWave) break;
   }
 
@@ -904,20 +946,21 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   for (int s = 0; s < ns; ++s) {
     const int st = readlane(s_start, s), n = readlane(s_n, s);
     const int u = readlane(s_unit, s);
-    const int32_t* row = a.bt + static_cast<int64_t>(u / hkv) * a.bt_stride + readlane(s_p, s);
+    const int32_t* row = a.bt + static_cast<int64_t>(u / vh) * a.bt_stride + readlane(s_p, s);
+    const int g = unit_cols<Multi>(a, u % vh).g;
     if (lane >= st && lane < st + n) {
       blk0 = row[lane - st];
-      g0 = u % hkv;
+      g0 = g;
     }
     if (lane + 64 >= st && lane + 64 < st + n) {
       blk1 = row[lane + 64 - st];
-      g1 = u % hkv;
+      g1 = g;
     }
   }
   // the q rows go to LDS while the block ids are in flight
   for (int s = 0; s < ns; ++s) {
     const int u = readlane(s_unit, s);
-    stage_q<D>(a, u / hkv, u % hkv, lds.q + s * a.group * D, lane);
+    stage_q<D, Multi>(a, u / vh, u % vh, lds.q + s * C * D, lane);
   }
   if (blk0 < 0 || blk0 >= a.num_blocks) {
     raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
@@ -938,10 +981,12 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     return a.pool + static_cast<int64_t>(hb >= 0 ? hb : 0) * K::kHeadBytes;
   };
 
-  // current segment: first page's token, first item, end item, length, and
-  // whether its last page gets the appended token
+  // current segment: first page's token, first item, end item, length,
+  // whether its last page gets the appended token, its column count and (for
+  // several query tokens) the smallest and the lane's own attention limit
   int s_patch = 0;  // lane s: segment s's appended token is in LDS
-  int cs = 0, c_tok = 0, c_start = 0, c_end = 0, c_L = 0, c_patch = 0;
+  int cs = 0, c_tok = 0, c_start = 0, c_end = 0, c_L = 0, c_patch = 0, c_n = a.group;
+  int c_Lmin = 0, c_Lc = 0;
   auto enter = [&](int sidx) {
     cs = sidx;
     c_tok = readlane(s_p, sidx) * kBlockSize;
@@ -949,6 +994,13 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     c_end = c_start + readlane(s_n, sidx);
     c_L = readlane(s_L, sidx);
     c_patch = readlane(s_patch, sidx);
+    if constexpr (Multi) {
+      // query token j sits at position L - qtok + j and sees positions up to it
+      const UnitCols uc = unit_cols<true>(a, readlane(s_unit, sidx) % vh);
+      c_n = uc.n;
+      c_Lmin = c_L - a.qtok + 1;
+      c_Lc = min(c_Lmin + (uc.col0 + i16) / a.group, c_L);
+    }
   };
   SoftmaxState<ND> st;
 
@@ -973,15 +1025,22 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
       const int i = first + j;
       if (i >= items) return false;
       if (i == c_end) {  // next segment: only registers and LDS are touched
-        stash_result<K>(a, st, lds.res + cs * a.group * (D + 2), i16, kb);
+        stash_result<K>(a, st, lds.res + cs * C * (D + 2), i16, kb, c_n);
         enter(cs + 1);
         softmax_init(st);
-        kind.load_q(a, lds.q + cs * a.group * D, i16, kb, i16 < a.group);
+        kind.load_q(a, lds.q + cs * C * D, i16, kb, i16 < c_n);
       }
       const int t = c_tok + (i - c_start) * kBlockSize;
-      if (c_patch && i == c_end - 1)
+      if (!Multi && c_patch && i == c_end - 1)
         K::patch(grp[j], lds.nt + cs * new_token_bytes(D), (c_L - 1) % kBlockSize, i16, kb);
-      kind.step(grp[j], t, blk[j] >= 0 ? c_L : t, st);
+      // a missing page (blk < 0) is masked whole
+      if constexpr (Multi) {
+        const bool ok = blk[j] >= 0;
+        kind.step(grp[j], t, ok ? c_L : t, ok ? c_Lmin : t, ok ? c_Lc : t, st);
+      } else {
+        const int Lv = blk[j] >= 0 ? c_L : t;
+        kind.step(grp[j], t, Lv, Lv, Lv, st);
+      }
     }
     return true;
   };
@@ -995,7 +1054,7 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   // else reads that slot during the call)
   // (its stores wait until after the page loop, so that the loop's waits
   // count page loads only)
-  if (a.append) {
+  if (!Multi && a.append) {
     for (int s = 0; s < ns; ++s) {
       if (!readlane(s_last, s)) continue;
       const int u = readlane(s_unit, s);
@@ -1005,7 +1064,7 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   }
   enter(0);
   softmax_init(st);
-  kind.load_q(a, lds.q, i16, kb, i16 < a.group);
+  kind.load_q(a, lds.q, i16, kb, i16 < c_n);
   for (int i = 0;; i += 2 * G) {
     if (!consume(ga, ba, i)) break;
     __builtin_amdgcn_sched_barrier(0);
@@ -1017,9 +1076,9 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     __builtin_amdgcn_sched_barrier(0);
     if (!more || i + 2 * G >= items) break;
   }
-  stash_result<K>(a, st, lds.res + cs * a.group * (D + 2), i16, kb);
+  stash_result<K>(a, st, lds.res + cs * C * (D + 2), i16, kb, c_n);
 
-  if (a.append) {
+  if (!Multi && a.append) {
     for (int s = 0; s < ns; ++s) {
       const int hb = block_of(readlane(s_start, s) + readlane(s_n, s) - 1);
       if (!readlane(s_patch, s) || hb < 0) continue;
@@ -1029,25 +1088,25 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   }
   for (int s = 0; s < ns; ++s) {
     const int u = readlane(s_unit, s);
-    write_result<D>(a, lds.res + s * a.group * (D + 2), u / hkv, u % hkv, wave + u,
-                    readlane(s_whole, s) != 0, lane);
+    write_result<D, Multi>(a, lds.res + s * C * (D + 2), u / vh, u % vh, wave + u,
+                           readlane(s_whole, s) != 0, lane);
   }
   return items;
 }
 
-template <class K>
+template <class K, bool Multi>
 __device__ __forceinline__ void decode_wave(const DecodeArgs& a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int lane = lane_id();
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wave = blockIdx.x * kWaves + wid;
-  const int hkv = a.num_kv_heads;
+  const int vh = Multi ? a.vheads : a.num_kv_heads;  // units per sequence
+  const int C = a.slot_cols;
   PassLds lds;
   lds.q = reinterpret_cast<uint16_t*>(smem + wid * a.lds_wave_bytes);
-  lds.res = reinterpret_cast<float*>(smem + wid * a.lds_wave_bytes +
-                                     a.seg_cap * a.group * K::D * 2);
+  lds.res = reinterpret_cast<float*>(smem + wid * a.lds_wave_bytes + a.seg_cap * C * K::D * 2);
   lds.nt = smem + wid * a.lds_wave_bytes +
-           (a.seg_cap * a.group * K::D * 2 + a.seg_cap * a.group * (K::D + 2) * 4 + 15) / 16 * 16;
+           (a.seg_cap * C * K::D * 2 + a.seg_cap * C * (K::D + 2) * 4 + 15) / 16 * 16;
 
   // total pages; zero rows of empty sequences
   const int nchunk = (a.num_seqs + 63) / 64;
@@ -1059,18 +1118,18 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs& a) {
     zero_rows(a, t, wave, K::D, lane);
     pages = chunk_end(t);
   }
-  const int total = pages * hkv;
+  const int total = pages * vh;
   const int P = pages_per_wave(total, a.num_waves);
   const int x0 = wave * P;
   if (x0 >= total) return;
   const int x1 = min(x0 + P, total);
 
   // the sequence holding item x0: items of sequence b are
-  // [hkv * excl_b, hkv * (excl_b + np_b))
+  // [vh * excl_b, vh * (excl_b + np_b))
   int hit;
   while (true) {
-    const int lo = hkv * s.excl;
-    const uint64_t m = __ballot(s.np > 0 && lo <= x0 && x0 < lo + hkv * s.np);
+    const int lo = vh * s.excl;
+    const uint64_t m = __ballot(s.np > 0 && lo <= x0 && x0 < lo + vh * s.np);
     if (m) {
       hit = __builtin_ctzll(m);
       break;
@@ -1085,13 +1144,13 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs& a) {
   cu.b = 64 * s.c + hit;
   cu.L = readlane(s.L, hit);
   cu.np = (cu.L + kBlockSize - 1) / kBlockSize;
-  const int off = x0 - hkv * readlane(s.excl, hit);
+  const int off = x0 - vh * readlane(s.excl, hit);
   cu.g = off / cu.np;
   cu.p = off - cu.g * cu.np;
 
   K kind;
   for (int x = x0; x < x1;) {
-    const int done = run_pass<K>(a, kind, cu, x, x1, P, wave, nchunk, lds, lane);
+    const int done = run_pass<K, Multi>(a, kind, cu, x, x1, P, wave, nchunk, lds, lane);
     if (done == 0) return;
     x += done;
   }
@@ -1102,25 +1161,38 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs& a) {
 template <int D, bool QBF16>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
     kInt8WavesPerSimd))) void decode_int8_kernel(DecodeArgs a) {
-  decode_wave<Int8Kind<D, QBF16, kInt8PageGroup>>(a);
+  decode_wave<Int8Kind<D, QBF16, kInt8PageGroup>, false>(a);
+}
+
+template <int D, bool QBF16>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
+    kInt8WavesPerSimd))) void decode_int8_multi_kernel(DecodeArgs a) {
+  decode_wave<Int8Kind<D, QBF16, kInt8PageGroup>, true>(a);
 }
 
 template <int D, bool QBF16>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
     kInt8WavesPerSimd))) void decode_int8_static_kernel(DecodeArgs a) {
-  decode_wave<Int8Kind<D, QBF16, kInt8PageGroup, true>>(a);
+  decode_wave<Int8Kind<D, QBF16, kInt8PageGroup, true>, false>(a);
 }
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
     k16WavesPerSimd))) void decode_16bit_kernel(DecodeArgs a) {
-  decode_wave<F16Kind<D, BF16, k16PageGroup>>(a);
+  decode_wave<F16Kind<D, BF16, k16PageGroup>, false>(a);
 }
 
-// Combine the partials of a unit that spans several waves, per query head:
-// out = sum_i 2^(m_i - m) acc_i / sum_i 2^(m_i - m) l_i over the waves i that
-// cover the unit (m = max_i m_i), as recorded by the unit's first wave. One
-// workgroup per (unit, query head) with a.merge_waves waves: wave w folds
+template <int D, bool BF16>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
+    k16WavesPerSimd))) void decode_16bit_multi_kernel(DecodeArgs a) {
+  decode_wave<F16Kind<D, BF16, k16PageGroup>, true>(a);
+}
+
+// Combine the partials of a unit that spans several waves, per (query token,
+// query head) column: out = sum_i 2^(m_i - m) acc_i / sum_i 2^(m_i - m) l_i
+// over the waves i that cover the unit (m = max_i m_i), as recorded by the
+// unit's first wave. One workgroup per (sequence, query token, query head)
+// with a.merge_waves waves: wave w folds
 // the partials w, w + waves, ... into a running (max, sum, accumulator),
 // kMergeBatch partials per round trip (lane j holds dims j, j + 64); the
 // waves then combine through LDS.
@@ -1133,18 +1205,22 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void merge_kernel(DecodeArgs a
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
-  const int bh = blockIdx.x;
-  const int b = bh / a.num_q_heads, h = bh % a.num_q_heads;
-  const int g = h / a.group, hh = h % a.group;
-  const int u = b * a.num_kv_heads + g;
+  const int rows = a.qtok * a.num_q_heads;
+  const int b = blockIdx.x / rows, r = blockIdx.x % rows;
+  const int j = r / a.num_q_heads, h = r % a.num_q_heads;
+  const int g = h / a.group;
+  const int col = j * a.group + h % a.group;  // column of KV head g
+  const int tile = col / 16;                  // 0 unless several tiles
+  const int cc = col - 16 * tile;             // column inside the unit
+  const int u = b * a.vheads + g * a.ntile + tile;
   // the unit's record is this call's only if the sequence has pages (its
   // first wave wrote it)
   const int2 rec = a.desc[u];
   const int L = a.ctx[b];
   if (L <= 0 || rec.y <= 1) return;  // no pages, or written directly
   const int n = rec.y;
-  const int64_t stride = static_cast<int64_t>(a.group) * (D + 2);
-  const float* base = a.ws + (static_cast<int64_t>(rec.x) + u) * stride + hh * (D + 2);
+  const int64_t stride = static_cast<int64_t>(a.slot_cols) * (D + 2);
+  const float* base = a.ws + (static_cast<int64_t>(rec.x) + u) * stride + cc * (D + 2);
 
   float mw = kMaxInit, lw = 0.f, acc[ND];
 #pragma unroll
@@ -1177,7 +1253,7 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void merge_kernel(DecodeArgs a
     }
     mw = mn;
   }
-  const int64_t o = b * a.out_ss + h * a.out_sh;
+  const int64_t o = b * a.out_ss + j * a.out_st + h * a.out_sh;
   if (nw == 1) {
     // lw == 0: no attendable token in the unit
 #pragma unroll
@@ -1208,70 +1284,66 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void merge_kernel(DecodeArgs a
 template <int D>
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
   if (a.max_ctx == 0) return hipSuccess;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(a.num_seqs * a.num_q_heads),
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(a.num_seqs * a.qtok * a.num_q_heads),
                      dim3(64 * a.merge_waves), 0, s, a);
   return hipGetLastError();
+}
+
+// The decode grid (one resident round of waves, planned on the host) with its
+// LDS, then the merge of the units split over several waves.
+using DecodeKernel = void (*)(DecodeArgs);
+
+hipError_t launch_pair(DecodeKernel k, const DecodeArgs& a, int head_dim, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(kWaves) * a.lds_wave_bytes;
+  hipLaunchKernelGGL(k, dim3(a.num_waves / kWaves), dim3(64 * kWaves), lds, s, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return head_dim == 128 ? launch_merge<128>(a, s) : launch_merge<64>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_int8(const DecodeArgs& a, int head_dim, bool q_bf16, hipStream_t s) {
-  const dim3 grid(a.num_waves / kWaves), block(64 * kWaves);
-  const size_t lds = static_cast<size_t>(kWaves) * a.lds_wave_bytes;
-  if (head_dim == 128) {
-    if (q_bf16)
-      hipLaunchKernelGGL((decode_int8_kernel<128, true>), grid, block, lds, s, a);
-    else
-      hipLaunchKernelGGL((decode_int8_kernel<128, false>), grid, block, lds, s, a);
-  } else {
-    if (q_bf16)
-      hipLaunchKernelGGL((decode_int8_kernel<64, true>), grid, block, lds, s, a);
-    else
-      hipLaunchKernelGGL((decode_int8_kernel<64, false>), grid, block, lds, s, a);
-  }
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return head_dim == 128 ? launch_merge<128>(a, s) : launch_merge<64>(a, s);
+  const DecodeKernel k =
+      head_dim == 128 ? (q_bf16 ? decode_int8_kernel<128, true> : decode_int8_kernel<128, false>)
+                      : (q_bf16 ? decode_int8_kernel<64, true> : decode_int8_kernel<64, false>);
+  return launch_pair(k, a, head_dim, s);
+}
+
+hipError_t launch_decode_int8_multi(const DecodeArgs& a, int head_dim, bool q_bf16,
+                                    hipStream_t s) {
+  const DecodeKernel k =
+      head_dim == 128
+          ? (q_bf16 ? decode_int8_multi_kernel<128, true> : decode_int8_multi_kernel<128, false>)
+          : (q_bf16 ? decode_int8_multi_kernel<64, true> : decode_int8_multi_kernel<64, false>);
+  return launch_pair(k, a, head_dim, s);
 }
 
 hipError_t launch_decode_int8_static(const DecodeArgs& a, int head_dim, bool q_bf16,
                                      hipStream_t s) {
-  const dim3 grid(a.num_waves / kWaves), block(64 * kWaves);
-  const size_t lds = static_cast<size_t>(kWaves) * a.lds_wave_bytes;
-  if (head_dim == 128) {
-    if (q_bf16)
-      hipLaunchKernelGGL((decode_int8_static_kernel<128, true>), grid, block, lds, s, a);
-    else
-      hipLaunchKernelGGL((decode_int8_static_kernel<128, false>), grid, block, lds, s, a);
-  } else {
-    if (q_bf16)
-      hipLaunchKernelGGL((decode_int8_static_kernel<64, true>), grid, block, lds, s, a);
-    else
-      hipLaunchKernelGGL((decode_int8_static_kernel<64, false>), grid, block, lds, s, a);
-  }
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return head_dim == 128 ? launch_merge<128>(a, s) : launch_merge<64>(a, s);
+  const DecodeKernel k =
+      head_dim == 128
+          ? (q_bf16 ? decode_int8_static_kernel<128, true> : decode_int8_static_kernel<128, false>)
+          : (q_bf16 ? decode_int8_static_kernel<64, true> : decode_int8_static_kernel<64, false>);
+  return launch_pair(k, a, head_dim, s);
 }
 
 hipError_t launch_decode_16bit(const DecodeArgs& a, int head_dim, bool kv_bf16,
                                hipStream_t s) {
-  const dim3 grid(a.num_waves / kWaves), block(64 * kWaves);
-  const size_t lds = static_cast<size_t>(kWaves) * a.lds_wave_bytes;
-  if (head_dim == 128) {
-    if (kv_bf16)
-      hipLaunchKernelGGL((decode_16bit_kernel<128, true>), grid, block, lds, s, a);
-    else
-      hipLaunchKernelGGL((decode_16bit_kernel<128, false>), grid, block, lds, s, a);
-  } else {
-    if (kv_bf16)
-      hipLaunchKernelGGL((decode_16bit_kernel<64, true>), grid, block, lds, s, a);
-    else
-      hipLaunchKernelGGL((decode_16bit_kernel<64, false>), grid, block, lds, s, a);
-  }
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return head_dim == 128 ? launch_merge<128>(a, s) : launch_merge<64>(a, s);
+  const DecodeKernel k =
+      head_dim == 128
+          ? (kv_bf16 ? decode_16bit_kernel<128, true> : decode_16bit_kernel<128, false>)
+          : (kv_bf16 ? decode_16bit_kernel<64, true> : decode_16bit_kernel<64, false>);
+  return launch_pair(k, a, head_dim, s);
+}
+
+hipError_t launch_decode_16bit_multi(const DecodeArgs& a, int head_dim, bool kv_bf16,
+                                     hipStream_t s) {
+  const DecodeKernel k =
+      head_dim == 128
+          ? (kv_bf16 ? decode_16bit_multi_kernel<128, true> : decode_16bit_multi_kernel<128, false>)
+          : (kv_bf16 ? decode_16bit_multi_kernel<64, true> : decode_16bit_multi_kernel<64, false>);
+  return launch_pair(k, a, head_dim, s);
 }
 
 }  // namespace pdakv

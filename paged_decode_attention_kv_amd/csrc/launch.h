@@ -46,9 +46,9 @@ struct WriteArgs {
 struct DecodeArgs {
   void* out;
   int out_dtype;
-  int64_t out_ss, out_sh;
+  int64_t out_ss, out_st, out_sh;  // element strides: sequence, query token, head
   const void* q;
-  int64_t q_ss, q_sh;
+  int64_t q_ss, q_st, q_sh;
   int q_vec16;  // q pointer and strides allow 16-byte loads of 8 elements
   uint8_t* pool;  // written only by the fused append
   int64_t num_blocks;
@@ -57,6 +57,12 @@ struct DecodeArgs {
   int64_t bt_stride;
   const int32_t* ctx;
   int num_seqs, num_q_heads, num_kv_heads, group, max_ctx;
+  // query tokens per sequence (the last qtok positions, causal among them);
+  // their cols = qtok * group (token, head) columns per KV head are split
+  // into ntile tiles of up to 16 MFMA columns, and each (KV head, tile) is a
+  // unit of its own: vheads = num_kv_heads * ntile units per sequence
+  int qtok, cols, ntile, vheads;
+  int slot_cols;  // columns per workspace slot and LDS segment: min(cols, 16)
   float scale_log2;  // sm_scale * log2(e) (times the K scale for static
                      // scales): logits are kept in base 2
   float out_mul;     // output factor: the V scale for static scales, else 1
@@ -82,6 +88,11 @@ hipError_t launch_quant_write_int8(const WriteArgs& a, int head_dim, bool src_bf
                                    hipStream_t s);
 hipError_t launch_write_16bit(const WriteArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_decode_int8(const DecodeArgs& a, int head_dim, bool q_bf16, hipStream_t s);
+// several query tokens per sequence (a.qtok >= 1)
+hipError_t launch_decode_int8_multi(const DecodeArgs& a, int head_dim, bool q_bf16,
+                                    hipStream_t s);
+hipError_t launch_decode_16bit_multi(const DecodeArgs& a, int head_dim, bool kv_bf16,
+                                     hipStream_t s);
 hipError_t launch_decode_16bit(const DecodeArgs& a, int head_dim, bool kv_bf16,
                                hipStream_t s);
 hipError_t launch_quant_write_static(const WriteArgs& a, int head_dim, bool src_bf16,

@@ -10,7 +10,8 @@ from dataclasses import dataclass
 
 import torch
 
-from ._lib import pdakv_decode_workspace_bytes, pdakv_page_bytes
+from ._lib import (pdakv_decode_multi_workspace_bytes, pdakv_decode_workspace_bytes,
+                   pdakv_page_bytes)
 
 
 def alloc_pool(kv_format: int, num_blocks: int, num_kv_heads: int, head_dim: int,
@@ -28,6 +29,17 @@ def alloc_workspace(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim
     workspace serves any number of non-overlapping calls of up to this size."""
     nbytes = pdakv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                           max_context_len)
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes // 4, dtype=torch.float32, device=device)
+
+
+def alloc_multi_workspace(num_seqs: int, num_query_tokens: int, num_q_heads: int,
+                          num_kv_heads: int, head_dim: int, max_context_len: int,
+                          device="cuda"):
+    """Scratch of the several-query-token decode calls (None when none is needed)."""
+    nbytes = pdakv_decode_multi_workspace_bytes(num_seqs, num_query_tokens, num_q_heads,
+                                                num_kv_heads, head_dim, max_context_len)
     if nbytes == 0:
         return None
     return torch.empty(nbytes // 4, dtype=torch.float32, device=device)

@@ -27,7 +27,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function(P):
     names = _declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(P._lib, n), n
     assert set(names) == set(P.EXPORTED)
@@ -210,3 +210,44 @@ def test_static_decode_rejects_bad_scales(P, ks, vs):
 def test_static_append_validation(P, change, status):
     args = _with_scales(_append_args(**change), 28)
     assert P._lib.paged_attn_decode_int8_static_append(*args) == status
+
+
+# ---- several query tokens ---------------------------------------------------
+
+def _multi_args(**kw):
+    a = dict(out=FAKE, odt=0, oss=4 * 4096, ost=4096, osh=128, q=FAKE, qdt=1, qss=4 * 4096,
+             qst=4096, qsh=128, T=4, pool=FAKE, nblk=16, bs=16, bt=FAKE, bts=16, ctx=FAKE, B=1,
+             hq=32, hkv=8, d=128, maxL=256, sm=0.088, ws=FAKE, wsb=1 << 30, err=None,
+             stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("fn", ["paged_attn_decode_int8_multi", "paged_attn_decode_fp16_multi"])
+@pytest.mark.parametrize("change,status", [
+    (dict(T=0), -1), (dict(T=-2), -1), (dict(ost=-1), -1), (dict(qst=-8), -1), (dict(qdt=0), -3),
+    (dict(hq=30), -2), (dict(d=96), -2), (dict(q=None), -1), (dict(ws=None, wsb=0), -4),
+    (dict(ws=FAKE, wsb=64), -4), (dict(B=0), 0), (dict(ws=FAKE + 4), -1),
+])
+def test_multi_validation(P, fn, change, status):
+    assert getattr(P._lib, fn)(*_multi_args(**change)) == status
+
+
+@pytest.mark.parametrize("B,T,hq,hkv,L", [(64, 1, 32, 8, 8193), (64, 4, 32, 8, 8193),
+                                          (8, 8, 32, 8, 32768), (32, 3, 14, 2, 4104),
+                                          (1, 16, 8, 8, 100), (3, 2, 16, 1, 40)])
+def test_multi_workspace_formula(P, B, T, hq, hkv, L):
+    """[waves + B * Hkv * tiles][min(T * G, 16)][D + 2] floats (16-byte
+    padded), then B * Hkv * tiles records; the waves are those of the plan
+    with Hkv * tiles heads. T = 1 is the one-token workspace."""
+    G = hq // hkv
+    cols = T * G
+    tiles = -(-cols // 16)
+    vh = hkv * tiles
+    waves, _ = P.pdakv_decode_plan(P.KV_INT8_SYM, B, vh, L)
+    partials = -(-(waves + B * vh) * min(cols, 16) * 130 * 4 // 16) * 16
+    assert P.pdakv_decode_multi_workspace_bytes(B, T, hq, hkv, 128, L) == partials + B * vh * 8
+    if T == 1:
+        assert (P.pdakv_decode_multi_workspace_bytes(B, 1, hq, hkv, 128, L) ==
+                P.pdakv_decode_workspace_bytes(B, hq, hkv, 128, L))
+    assert P.pdakv_decode_multi_workspace_bytes(B, 0, hq, hkv, 128, L) == 0

@@ -21,5 +21,6 @@ from .gen import (  # noqa: F401
     WritePhase,
     build,
     make_config,
+    multi_query,
     CONFIG_NAMES,
 )

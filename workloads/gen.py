@@ -270,3 +270,13 @@ def make_config(idx, scale: float = 1.0) -> Workload:
         return build(CONFIG_NAMES["s8k"], 6, [("prefill", [sc(8192)] * B)], 32, 8, 128,
                      "f16", "outlier", shuffle=True)
     raise KeyError(idx)
+
+
+def multi_query(wl: Workload, num_tokens: int, seed: int) -> torch.Tensor:
+    """Query rows [B, T, Hq, D] for a decode with T query tokens per sequence
+    (the sequence's last T positions): N(0, 1) draws from its own seeded
+    generator, in the workload's dtype."""
+    rng = np.random.default_rng(seed)
+    qx = rng.standard_normal((wl.num_seqs, num_tokens, wl.num_q_heads, wl.head_dim),
+                             dtype=np.float32)
+    return _cast(qx, wl.kv_dtype)
