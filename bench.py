@@ -107,7 +107,7 @@ def main():
     import torch
 
     import paged_decode_attention_kv_amd as P
-    from workloads import make_config
+    from workloads import make_config, multi_query
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -197,6 +197,10 @@ def main():
                 st["fused"](st["out"], st["q"], st["ak"], st["av"], pool, wl.num_blocks, st["bt"],
                             st["ctx"], wl.num_kv_heads, wl.max_context_len, wl.sm_scale,
                             st["ws"], stream=stream)
+            elif mode == "multi":
+                st["multi"](st["mout"], st["mq"], pool, wl.num_blocks, st["bt"], st["ctx"],
+                            wl.num_kv_heads, wl.max_context_len, wl.sm_scale, st["mws"],
+                            stream=stream)
             else:
                 st["decode"](st["out"], st["q"], pool, wl.num_blocks, st["bt"], st["ctx"],
                              wl.num_kv_heads, wl.max_context_len, wl.sm_scale, st["ws"],
@@ -269,6 +273,35 @@ def main():
                                             entry["fp16"]["tokens_per_s"], 3)
             points[pname] = entry
 
+    # ---- several query tokens: verify 4 draft tokens per sequence -----------
+    # the batched step's pool (contexts L_b + 1); the last 4 positions of every
+    # sequence are the query tokens (causal among them)
+    multi = None
+    if not args.no_points:
+        T = 4
+        multi = {"query_tokens": T, "config": wl.name}
+        for key in ("int8", "fp16"):
+            st = setup(wl, key, None)
+            st["multi"] = (P.paged_attn_decode_int8_multi if key == "int8"
+                           else P.paged_attn_decode_fp16_multi)
+            st["mq"] = to_dev(multi_query(wl, T, seed=2024))
+            st["mout"] = torch.empty((wl.num_seqs, T, wl.num_q_heads, wl.head_dim),
+                                     dtype=torch.float32, device="cuda")
+            st["mws"] = P.alloc_multi_workspace(wl.num_seqs, T, wl.num_q_heads,
+                                                wl.num_kv_heads, wl.head_dim,
+                                                wl.max_context_len)
+            _, mms, _ = run(wl, st, args.steps, args.warmup, "multi")
+            _, dms, _ = run(wl, st, args.steps, args.warmup, "decode")
+            b = decode_bytes(wl, key) + wl.num_seqs * (T - 1) * wl.num_q_heads * wl.head_dim * 6
+            multi[key] = {"call_us": round(mms * 1e3, 2),
+                          "query_tokens_per_s": round(wl.num_seqs * T / (mms * 1e-3), 1),
+                          "gbs": round(b / (mms * 1e-3) / 1e9, 1),
+                          "one_token_call_us": round(dms * 1e3, 2),
+                          "vs_T_one_token_calls": round(T * dms / mms, 3)}
+            del st
+            torch.cuda.empty_cache()
+        multi["int8_over_fp16"] = round(multi["fp16"]["call_us"] / multi["int8"]["call_us"], 3)
+
     # ---- CPU baseline: the oracle on a bounded sample ------------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -306,6 +339,7 @@ def main():
         "static_scale_step": {k: (round(v, 4) if isinstance(v, float) else v)
                               for k, v in res["static"].items()},
         "unfused_step": unfused,
+        "multi_token": multi,
         "points": points,
         "cpu_baseline": cpu,
     }
