@@ -14,6 +14,7 @@ pages      the paged byte layout of INT8 and 16-bit KV pools, written from
            the layout contract, plus page write / gather helpers
 attention  decode attention over dequantized K/V with FP64 accumulation, for
            one query token per sequence or several (causal among them)
+lifecycle  page swap-out / swap-in and the front trim that keeps sink tokens
 
 Every function cites the passage it follows. Sources are four pull-request
 pages; they are cited by project, PR number and section:
@@ -64,4 +65,9 @@ from .attention import (  # noqa: F401
     decode_16bit_from_pool,
     decode_int8_static_from_pool,
     decode_multi_from_pool,
+)
+from .lifecycle import (  # noqa: F401
+    swap_out_pages,
+    swap_in_pages,
+    trim_keep_sink,
 )

@@ -305,3 +305,61 @@ def test_multi_mutant_is_caught(name, monkeypatch):
 
 def test_unmutated_multi_passes_the_same_pins():
     assert not _caught(MULTI_PINS)
+
+
+# ---- page lifecycle -----------------------------------------------------------
+import oracle.lifecycle as olife  # noqa: E402
+from tests import test_oracle_lifecycle as TL  # noqa: E402
+
+
+def _trim(mode):
+    real = olife.trim_keep_sink
+
+    def f(kv_format, pool, block_tables, context_lens, trim_lens, keep, block_size,
+          num_kv_heads, head_dim):
+        if mode == "oldest":       # drops the n oldest tokens (ignores the sink)
+            return real(kv_format, pool, block_tables, context_lens, trim_lens, 0, block_size,
+                        num_kv_heads, head_dim)
+        if mode == "one_less":     # drops one token fewer
+            return real(kv_format, pool, block_tables, context_lens,
+                        [max(int(t) - 1, 0) for t in trim_lens], keep, block_size, num_kv_heads,
+                        head_dim) - np.where(np.asarray(trim_lens) > 0, 1, 0).astype(np.int32)
+        raise ValueError(mode)
+    return f
+
+
+def _index_codes_only(kv_format, block_size, head_dim, num_kv_heads, page_len, blk, pos, head):
+    """Byte index of a token without its scales (scales left behind)."""
+    full = _ORIG_INDEX(kv_format, block_size, head_dim, num_kv_heads, page_len, blk, pos, head)
+    return full[:, :2 * head_dim] if kv_format == oracle.KV_INT8_SYM else full
+
+
+_ORIG_INDEX = olife._token_byte_index
+
+LIFE_MUTANTS = {
+    "trim drops the oldest tokens": ("trim_keep_sink", _trim("oldest")),
+    "trim drops one token fewer": ("trim_keep_sink", _trim("one_less")),
+    "scales do not move with their codes": ("_token_byte_index", _index_codes_only),
+    "swap-out ignores the id order": ("swap_out_pages",
+                                      lambda pool, ids: _ORIG_SWAP(pool, np.sort(ids))),
+}
+_ORIG_SWAP = olife.swap_out_pages
+
+LIFE_PINS = [
+    lambda: TL.test_trim_keeps_the_sink_and_the_tail("int8"),
+    lambda: TL.test_trim_byte_positions_by_hand(),
+    lambda: TL.test_swap_round_trip_and_relocation(),
+]
+
+
+@pytest.mark.parametrize("name", sorted(LIFE_MUTANTS))
+def test_lifecycle_mutant_is_caught(name, monkeypatch):
+    attr, fn = LIFE_MUTANTS[name]
+    monkeypatch.setattr(olife, attr, fn)
+    if hasattr(oracle, attr):
+        monkeypatch.setattr(oracle, attr, fn)
+    assert _caught(LIFE_PINS), name
+
+
+def test_unmutated_lifecycle_passes_the_same_pins():
+    assert not _caught(LIFE_PINS)
