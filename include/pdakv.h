@@ -376,6 +376,55 @@ int paged_attn_decode_fp16_multi(
 size_t pdakv_decode_multi_workspace_bytes(int num_seqs, int num_query_tokens, int num_q_heads,
                                           int num_kv_heads, int head_dim, int max_context_len);
 
+/* Page swap-out (MoE-Infinity PR #183, "What landed", serving-lifecycle
+ * bullet: pages are swapped out of GPU memory and back in, INT8 scales
+ * included). Copies page block_ids[i] of the pool (num_blocks pages of
+ * page_bytes each; page_bytes = pdakv_page_bytes() of the pool's format, a
+ * multiple of 16) to dst + i * page_bytes, for i < num_pages. Every format
+ * keeps a token's scales inside its page, so whole pages carry them.
+ *   dst        device memory, or pinned host memory (hipHostMalloc; passed
+ *              as its host address, the library looks up the address the GPU
+ *              uses); 16-byte aligned; num_pages * page_bytes bytes. Pageable
+ *              host memory is rejected with PDAKV_ERR_INVALID_ARG.
+ *   block_ids  device int32 [num_pages]; an id outside [0, num_blocks) is
+ *              flagged PDAKV_EFLAG_BLOCK_RANGE and its entry left unwritten.
+ * Rolling a swap back (the transaction of a residency change) is the
+ * caller's: this call only moves bytes. */
+int kv_pages_swap_out(const void* kv_pool, int64_t num_blocks, int64_t page_bytes,
+                      const int32_t* block_ids, int64_t num_pages, void* dst, int32_t* err_flag,
+                      void* stream);
+
+/* Page swap-in: copies src + i * page_bytes into page block_ids[i] of the
+ * pool (the pages may differ from the ones swapped out; the caller updates
+ * its block tables). The ids must be distinct; out-of-range ids are flagged
+ * and skipped. src is device or pinned host memory, 16-byte aligned. */
+int kv_pages_swap_in(const void* src, int64_t num_pages, const int32_t* block_ids, void* kv_pool,
+                     int64_t num_blocks, int64_t page_bytes, int32_t* err_flag, void* stream);
+
+/* Front trim that keeps sink tokens (mlxcel PR #717 and its follow-up on the
+ * same page: drop the n tokens after the first `keep` positions instead of
+ * the n oldest, so the first tokens survive; the INT8 scales move with their
+ * tokens). For every sequence b with L = context_lens[b] and
+ * n = clamp(trim_lens[b], 0, max(L - keep, 0)), the tokens at positions
+ * keep + n .. L - 1 move to positions keep .. L - n - 1 through the
+ * sequence's block table, in place, and new_context_lens[b] = L - n. Slots at
+ * or past the new length keep what they held; pages no longer needed are
+ * the caller's to free. Cutting the end of a sequence (truncation) moves
+ * nothing: it is a shorter context length.
+ *   kv_format  any PDAKV_KV_* format; the pool layout above.
+ *   trim_lens, context_lens   device int32 [num_seqs].
+ *   new_context_lens  device int32 [num_seqs]; must not alias context_lens.
+ *   keep       host int >= 0.
+ * Pages the trim rewrites (positions >= keep) must belong to that sequence
+ * alone. Context lengths beyond block_table_stride * 16 are clamped and
+ * flagged; a token whose source or destination page is out of range is not
+ * moved (flagged). */
+int kv_trim_keep_sink(int kv_format, void* kv_pool, int64_t num_blocks, int block_size,
+                      int num_kv_heads, int head_dim, const int32_t* block_tables,
+                      int64_t block_table_stride, const int32_t* context_lens,
+                      const int32_t* trim_lens, int num_seqs, int keep,
+                      int32_t* new_context_lens, int32_t* err_flag, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

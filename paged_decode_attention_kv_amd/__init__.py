@@ -27,8 +27,11 @@ from ._lib import (  # noqa: F401
     KV_INT8_SYM,
     LIB_PATH,
     PdakvError,
+    kv_pages_swap_in,
+    kv_pages_swap_out,
     kv_quant_int8_static_write,
     kv_quant_int8_sym_write,
+    kv_trim_keep_sink,
     kv_write_16bit,
     paged_attn_decode_fp16,
     paged_attn_decode_fp16_append,

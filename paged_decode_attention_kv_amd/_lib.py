@@ -74,6 +74,12 @@ _SIGS["paged_attn_decode_int8_multi"] = (
     _d[8:])
 _SIGS["paged_attn_decode_fp16_multi"] = _SIGS["paged_attn_decode_int8_multi"]
 _SIGS["pdakv_decode_multi_workspace_bytes"] = (ctypes.c_size_t, [_c_int] * 6)
+_SIGS["kv_pages_swap_out"] = (_c_int, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_vp,
+                                       _c_vp])
+_SIGS["kv_pages_swap_in"] = (_c_int, [_c_vp, _c_i64, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_vp])
+_SIGS["kv_trim_keep_sink"] = (_c_int, [_c_int, _c_vp, _c_i64, _c_int, _c_int, _c_int, _c_vp,
+                                       _c_i64, _c_vp, _c_vp, _c_int, _c_int, _c_vp, _c_vp,
+                                       _c_vp])
 
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -332,3 +338,43 @@ def paged_attn_decode_fp16_multi(out, q, kv_pool, num_blocks: int, block_tables,
     _decode_multi("paged_attn_decode_fp16_multi", out, q, kv_pool, num_blocks, block_tables,
                   context_lens, num_kv_heads, max_context_len, sm_scale, workspace, block_size,
                   err_flag, stream)
+
+
+# ---- page lifecycle ---------------------------------------------------------
+
+def kv_pages_swap_out(kv_pool, num_blocks: int, block_ids, dst, err_flag=None,
+                      stream=None) -> None:
+    """Copy pages block_ids[i] of the pool into dst[i] (dst: [n, page_bytes]
+    uint8, device or pinned host memory)."""
+    n = block_ids.numel()
+    pb = kv_pool.shape[1]
+    if dst.numel() * dst.element_size() < n * pb:
+        raise ValueError("dst is too small")
+    _check("kv_pages_swap_out", _lib.kv_pages_swap_out(
+        _ptr(kv_pool), num_blocks, pb, _ptr(block_ids), n, _ptr(dst), _ptr(err_flag),
+        _stream(stream)))
+
+
+def kv_pages_swap_in(src, block_ids, kv_pool, num_blocks: int, err_flag=None,
+                     stream=None) -> None:
+    """Copy src[i] ([n, page_bytes] uint8, device or pinned host memory) into
+    page block_ids[i] of the pool."""
+    n = block_ids.numel()
+    pb = kv_pool.shape[1]
+    if src.numel() * src.element_size() < n * pb:
+        raise ValueError("src is too small")
+    _check("kv_pages_swap_in", _lib.kv_pages_swap_in(
+        _ptr(src), n, _ptr(block_ids), _ptr(kv_pool), num_blocks, pb, _ptr(err_flag),
+        _stream(stream)))
+
+
+def kv_trim_keep_sink(kv_format: int, kv_pool, num_blocks: int, num_kv_heads: int,
+                      head_dim: int, block_tables, context_lens, trim_lens, keep: int,
+                      new_context_lens, block_size: int = 16, err_flag=None,
+                      stream=None) -> None:
+    """Drop trim_lens[b] tokens after the first `keep` of every sequence, in
+    place; writes the new lengths to new_context_lens."""
+    _check("kv_trim_keep_sink", _lib.kv_trim_keep_sink(
+        kv_format, _ptr(kv_pool), num_blocks, block_size, num_kv_heads, head_dim,
+        _ptr(block_tables), block_tables.stride(0), _ptr(context_lens), _ptr(trim_lens),
+        context_lens.numel(), keep, _ptr(new_context_lens), _ptr(err_flag), _stream(stream)))

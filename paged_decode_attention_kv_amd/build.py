@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpdakv.so")
-SOURCES = ["abi.cpp", "quant_write.hip", "decode.hip"]
+SOURCES = ["abi.cpp", "quant_write.hip", "decode.hip", "lifecycle.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950",

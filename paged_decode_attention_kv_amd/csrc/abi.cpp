@@ -336,6 +336,42 @@ int write_common(int fmt, Scales sc, const void* k_src, const void* v_src, int s
   }
 }
 
+// The address under which the GPU reaches `p`: p itself for device memory,
+// the mapped device address for pinned host memory, nullptr for memory the
+// GPU cannot reach (pageable host memory) or an unknown pointer.
+void* gpu_address(void* p) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the error state the query left
+    return nullptr;
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) return p;
+  if (at.type == hipMemoryTypeHost) return at.devicePointer;
+  return nullptr;
+}
+
+int page_copy(void* pool, int64_t num_blocks, int64_t page_bytes, const int32_t* ids,
+              int64_t num_pages, void* packed, bool gather, int32_t* err_flag, void* stream) {
+  if (num_blocks < 0 || num_pages < 0 || page_bytes <= 0 || page_bytes % 16 != 0)
+    return PDAKV_ERR_INVALID_ARG;
+  if (num_pages > INT32_MAX) return PDAKV_ERR_UNSUPPORTED;  // one workgroup per page
+  if (num_pages == 0) return PDAKV_OK;
+  if (!pool || !ids || !packed || !aligned16(pool) || !aligned16(packed))
+    return PDAKV_ERR_INVALID_ARG;
+  void* far = gpu_address(packed);
+  if (!far || !aligned16(far)) return PDAKV_ERR_INVALID_ARG;
+  pdakv::PageCopyArgs a{};
+  a.pool = static_cast<uint8_t*>(pool);
+  a.num_blocks = num_blocks;
+  a.page_bytes = page_bytes;
+  a.packed = static_cast<uint8_t*>(far);
+  a.ids = ids;
+  a.num_pages = num_pages;
+  a.gather = gather ? 1 : 0;
+  a.err = err_flag;
+  return hip_status(pdakv::launch_page_copy(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -605,6 +641,55 @@ int paged_attn_decode_fp16_multi(
                        block_tables, block_table_stride, context_lens, num_seqs, num_q_heads,
                        num_kv_heads, head_dim, max_context_len, sm_scale, workspace,
                        workspace_bytes, err_flag, stream);
+}
+
+int kv_pages_swap_out(const void* kv_pool, int64_t num_blocks, int64_t page_bytes,
+                      const int32_t* block_ids, int64_t num_pages, void* dst, int32_t* err_flag,
+                      void* stream) {
+  return page_copy(const_cast<void*>(kv_pool), num_blocks, page_bytes, block_ids, num_pages, dst,
+                   true, err_flag, stream);
+}
+
+int kv_pages_swap_in(const void* src, int64_t num_pages, const int32_t* block_ids, void* kv_pool,
+                     int64_t num_blocks, int64_t page_bytes, int32_t* err_flag, void* stream) {
+  return page_copy(kv_pool, num_blocks, page_bytes, block_ids, num_pages, const_cast<void*>(src),
+                   false, err_flag, stream);
+}
+
+int kv_trim_keep_sink(int kv_format, void* kv_pool, int64_t num_blocks, int block_size,
+                      int num_kv_heads, int head_dim, const int32_t* block_tables,
+                      int64_t block_table_stride, const int32_t* context_lens,
+                      const int32_t* trim_lens, int num_seqs, int keep,
+                      int32_t* new_context_lens, int32_t* err_flag, void* stream) {
+  if (!known_format(kv_format)) return PDAKV_ERR_INVALID_ARG;
+  if (num_seqs < 0 || num_kv_heads <= 0 || num_blocks < 0 || block_table_stride < 0 || keep < 0)
+    return PDAKV_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim) || block_size != pdakv::kBlockSize)
+    return PDAKV_ERR_UNSUPPORTED;
+  // device indexes: head blocks (block * heads + head) and the grid in int32
+  if (num_blocks * num_kv_heads > INT32_MAX) return PDAKV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(num_seqs) * num_kv_heads > INT32_MAX) return PDAKV_ERR_UNSUPPORTED;
+  if (block_table_stride * block_size > INT32_MAX) return PDAKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PDAKV_OK;
+  if (!kv_pool || !block_tables || !context_lens || !trim_lens || !new_context_lens)
+    return PDAKV_ERR_INVALID_ARG;
+  if (!aligned16(kv_pool)) return PDAKV_ERR_INVALID_ARG;
+  pdakv::TrimArgs a{};
+  a.pool = static_cast<uint8_t*>(kv_pool);
+  a.num_blocks = num_blocks;
+  a.page_bytes =
+      static_cast<int64_t>(pdakv_page_bytes(kv_format, block_size, num_kv_heads, head_dim));
+  a.bt = block_tables;
+  a.bt_stride = block_table_stride;
+  a.ctx = context_lens;
+  a.trim = trim_lens;
+  a.new_ctx = new_context_lens;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.keep = keep;
+  a.err = err_flag;
+  return hip_status(pdakv::launch_trim_keep_sink(a, kv_format, head_dim,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -82,6 +82,32 @@ struct DecodeArgs {
   int32_t* err;
 };
 
+// Whole-page copies between a pool and a packed page array.
+struct PageCopyArgs {
+  uint8_t* pool;
+  int64_t num_blocks;
+  int64_t page_bytes;  // a multiple of 16
+  uint8_t* packed;     // [num_pages][page_bytes]
+  const int32_t* ids;  // [num_pages] pool block of packed page i
+  int64_t num_pages;
+  int gather;          // 1: pool -> packed (swap-out), 0: packed -> pool (swap-in)
+  int32_t* err;
+};
+
+// Front trim keeping `keep` sink tokens of every sequence.
+struct TrimArgs {
+  uint8_t* pool;
+  int64_t num_blocks;
+  int64_t page_bytes;
+  const int32_t* bt;
+  int64_t bt_stride;
+  const int32_t* ctx;
+  const int32_t* trim;  // tokens to drop after the sink, per sequence
+  int32_t* new_ctx;
+  int num_seqs, num_kv_heads, keep;
+  int32_t* err;
+};
+
 // Each returns hipSuccess or the launch error. Arguments are validated by the
 // caller; the launchers only pick the template instance.
 hipError_t launch_quant_write_int8(const WriteArgs& a, int head_dim, bool src_bf16,
@@ -97,6 +123,8 @@ hipError_t launch_decode_16bit(const DecodeArgs& a, int head_dim, bool kv_bf16,
                                hipStream_t s);
 hipError_t launch_quant_write_static(const WriteArgs& a, int head_dim, bool src_bf16,
                                      hipStream_t s);
+hipError_t launch_page_copy(const PageCopyArgs& a, hipStream_t s);
+hipError_t launch_trim_keep_sink(const TrimArgs& a, int kv_format, int head_dim, hipStream_t s);
 hipError_t launch_decode_int8_static(const DecodeArgs& a, int head_dim, bool q_bf16,
                                      hipStream_t s);
 

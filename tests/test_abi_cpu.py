@@ -27,7 +27,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function(P):
     names = _declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(P._lib, n), n
     assert set(names) == set(P.EXPORTED)
@@ -251,3 +251,40 @@ def test_multi_workspace_formula(P, B, T, hq, hkv, L):
         assert (P.pdakv_decode_multi_workspace_bytes(B, 1, hq, hkv, 128, L) ==
                 P.pdakv_decode_workspace_bytes(B, hq, hkv, 128, L))
     assert P.pdakv_decode_multi_workspace_bytes(B, 0, hq, hkv, 128, L) == 0
+
+
+# ---- page lifecycle ---------------------------------------------------------
+
+def _swap_args(**kw):
+    a = dict(pool=FAKE, nblk=16, pb=33280, ids=FAKE, n=4, dst=FAKE, err=None, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(pb=33281), -1), (dict(pb=0), -1), (dict(n=-1), -1), (dict(nblk=-1), -1),
+    (dict(ids=None), -1), (dict(dst=None), -1), (dict(dst=FAKE + 8), -1),
+    (dict(pool=FAKE + 4), -1), (dict(n=0, ids=None, dst=None), 0), (dict(n=1 << 31), -2),
+])
+def test_swap_validation(P, change, status):
+    assert P._lib.kv_pages_swap_out(*_swap_args(**change)) == status
+    a = dict(zip(["pool", "nblk", "pb", "ids", "n", "dst", "err", "stream"], _swap_args(**change)))
+    assert P._lib.kv_pages_swap_in(a["dst"], a["n"], a["ids"], a["pool"], a["nblk"], a["pb"],
+                                   None, None) == status
+
+
+def _trim_args(**kw):
+    a = dict(fmt=1, pool=FAKE, nblk=64, bs=16, hkv=8, d=128, bt=FAKE, bts=8, ctx=FAKE,
+             trim=FAKE, B=2, keep=4, new=FAKE, err=None, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(fmt=0), -1), (dict(fmt=4), -1), (dict(keep=-1), -1), (dict(B=-1), -1),
+    (dict(hkv=0), -1), (dict(d=96), -2), (dict(bs=32), -2), (dict(bts=-1), -1),
+    (dict(trim=None), -1), (dict(new=None), -1), (dict(ctx=None), -1), (dict(pool=FAKE + 4), -1),
+    (dict(B=0, pool=None), 0), (dict(nblk=1 << 28), -2),
+])
+def test_trim_validation(P, change, status):
+    assert P._lib.kv_trim_keep_sink(*_trim_args(**change)) == status

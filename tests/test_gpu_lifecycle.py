@@ -1,0 +1,145 @@
+"""GPU parity of the page lifecycle operations: page swap-out / swap-in
+(device and pinned host memory on the far side) and the front trim that
+keeps sink tokens, for the three page formats, against the oracle byte for
+byte, and decodes over the results against the oracle's decode."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import (FILL, MAX_ABS_TOL, dev_i32, gpu_decode, gpu_pool, oracle_decode,
+                            oracle_pool, require_gpu, to_dev)
+from workloads import build, make_config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def P():
+    return require_gpu()
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _static_pool(P, wl, ks=0.05, vs=0.05):
+    pb = P.pdakv_page_bytes(P.KV_INT8_STATIC, 16, wl.num_kv_heads, wl.head_dim)
+    pool = torch.full((wl.num_blocks, pb), FILL, dtype=torch.uint8, device="cuda")
+    for ph in wl.phases:
+        P.kv_quant_int8_static_write(to_dev(ph.k), to_dev(ph.v), dev_i32(ph.slot_mapping), pool,
+                                     wl.num_blocks, ks, vs)
+    return pool
+
+
+def _pool(P, wl, kind):
+    if kind == "int8":
+        return P.KV_INT8_SYM, oracle.KV_INT8_SYM, gpu_pool(P, wl, P.KV_INT8_SYM)[0]
+    if kind == "static":
+        return P.KV_INT8_STATIC, oracle.KV_INT8_STATIC, _static_pool(P, wl)
+    return P.KV_16BIT, oracle.KV_16BIT, gpu_pool(P, wl, P.KV_16BIT)[0]
+
+
+@pytest.mark.parametrize("to_host", [False, True])
+def test_swap_out_and_in(P, to_host):
+    wl = make_config(3, 0.05)
+    pool, _ = gpu_pool(P, wl, P.KV_INT8_SYM)
+    host_ref = pool.cpu().numpy()
+    rng = np.random.default_rng(0)
+    ids = rng.permutation(wl.num_blocks)[:9].astype(np.int32)
+    ids_bad = np.concatenate([ids[:4], [-1, wl.num_blocks], ids[4:]]).astype(np.int32)
+    pb = pool.shape[1]
+    dst = torch.full((len(ids_bad), pb), FILL, dtype=torch.uint8,
+                     device="cpu" if to_host else "cuda", pin_memory=to_host)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    P.kv_pages_swap_out(pool, wl.num_blocks, dev_i32(ids_bad), dst, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == P.EFLAG_BLOCK_RANGE
+    got = dst.cpu().numpy()
+    want = oracle.swap_out_pages(host_ref, ids_bad)
+    ok = (ids_bad >= 0) & (ids_bad < wl.num_blocks)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.all(got[~ok] == FILL)  # entries of bad ids are left as they were
+    # swap the valid pages back in to free pages, remap, decode: same rows, bitwise
+    before = gpu_decode(P, wl, pool, P.KV_INT8_SYM)
+    torch.cuda.synchronize()
+    pages = dst[torch.from_numpy(np.nonzero(ok)[0])].contiguous()
+    if to_host:
+        pages = pages.pin_memory()
+    extra = torch.full((len(ids), pb), 0, dtype=torch.uint8, device="cuda")
+    big = torch.cat([pool, extra])  # room for the relocated pages
+    new_ids = np.arange(wl.num_blocks, wl.num_blocks + len(ids), dtype=np.int32)
+    P.kv_pages_swap_in(pages, dev_i32(new_ids), big, big.shape[0])
+    bt = wl.block_tables.copy()
+    for old, new in zip(ids, new_ids):
+        bt[bt == old] = new
+    after = gpu_decode(P, wl, big, P.KV_INT8_SYM, block_tables=bt)
+    torch.cuda.synchronize()
+    assert torch.equal(before, after)
+
+
+KINDS = ["int8", "static", "16bit"]
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("keep", [0, 4])
+def test_trim_keep_sink_matches_oracle(P, kind, keep):
+    """Trims below a chunk, across many chunks, page-aligned, clamped, and
+    zero, over shuffled pages; the pool after the trim is the oracle's byte
+    for byte."""
+    lens = [700, 300, 40, 3, 129, 1030]
+    trims = [100, 3, 999, 1, 16, 777]
+    wl = build("trim", 31 + keep, [("prefill", lens)], 8, 2, 128 if kind != "static" else 64,
+               "f16", "outlier", shuffle=True, spare_blocks=2)
+    fmt, ofmt, pool = _pool(P, wl, kind)
+    host = pool.cpu().numpy()
+    new = torch.zeros(len(lens), dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _say(f"trim {kind} keep {keep}")
+    P.kv_trim_keep_sink(fmt, pool, wl.num_blocks, wl.num_kv_heads, wl.head_dim,
+                        dev_i32(wl.block_tables), dev_i32(wl.context_lens), dev_i32(trims), keep,
+                        new, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    want_lens = oracle.trim_keep_sink(ofmt, host, wl.block_tables, wl.context_lens, trims, keep,
+                                      16, wl.num_kv_heads, wl.head_dim)
+    assert new.cpu().numpy().tolist() == want_lens.tolist()
+    assert np.array_equal(pool.cpu().numpy(), host)
+
+
+def test_decode_after_trim(P):
+    wl = make_config(3, 0.1)
+    pool, _ = gpu_pool(P, wl, P.KV_INT8_SYM)
+    host = oracle_pool(wl, oracle.KV_INT8_SYM)
+    trims = (np.arange(wl.num_seqs) * 37 % 300).astype(np.int32)
+    new = torch.zeros(wl.num_seqs, dtype=torch.int32, device="cuda")
+    P.kv_trim_keep_sink(P.KV_INT8_SYM, pool, wl.num_blocks, wl.num_kv_heads, wl.head_dim,
+                        dev_i32(wl.block_tables), dev_i32(wl.context_lens), dev_i32(trims), 4,
+                        new)
+    new_lens = oracle.trim_keep_sink(oracle.KV_INT8_SYM, host, wl.block_tables, wl.context_lens,
+                                     trims, 4, 16, wl.num_kv_heads, wl.head_dim)
+    torch.cuda.synchronize()
+    assert new.cpu().numpy().tolist() == new_lens.tolist()
+    out = gpu_decode(P, wl, pool, P.KV_INT8_SYM, context_lens=new_lens)
+    wl.context_lens = new_lens
+    want = oracle_decode(wl, host, oracle.KV_INT8_SYM)
+    d = float(np.max(np.abs(out.cpu().numpy().astype(np.float64) - want)))
+    _say(f"decode after trim: max abs diff {d:.3e}")
+    assert d <= MAX_ABS_TOL
+
+
+def test_trim_flags_a_missing_page(P):
+    """A block id outside the pool in the moved range is flagged; the tokens
+    on it are not moved and nothing else faults."""
+    wl = build("trim-bad", 8, [("prefill", [90])], 8, 2, 64, "f16", "normal", spare_blocks=1)
+    pool, _ = gpu_pool(P, wl, P.KV_16BIT)
+    bt = wl.block_tables.copy()
+    bt[0, 3] = wl.num_blocks + 5
+    new = torch.zeros(1, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    P.kv_trim_keep_sink(P.KV_16BIT, pool, wl.num_blocks, 2, 64, dev_i32(bt),
+                        dev_i32(wl.context_lens), dev_i32([10]), 4, new, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == P.EFLAG_BLOCK_RANGE
+    assert int(new.item()) == 80
