@@ -302,6 +302,59 @@ def main():
             torch.cuda.empty_cache()
         multi["int8_over_fp16"] = round(multi["fp16"]["call_us"] / multi["int8"]["call_us"], 3)
 
+    # ---- page lifecycle: swap-out / swap-in and the sink-keeping trim -----------
+    lifecycle = None
+    if not args.no_points:
+        def timed(fn, reps):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps * 1e-3  # seconds per call
+        st = setup(wl, "int8", None)
+        pool = st["pools"][0]
+        pb = pool.shape[1]
+        npages = 2048
+        ids = dev_i32(np.random.default_rng(5).permutation(wl.num_blocks)[:npages])
+        dev_buf = torch.empty((npages, pb), dtype=torch.uint8, device="cuda")
+        host_buf = torch.empty((npages, pb), dtype=torch.uint8, pin_memory=True)
+        nbytes = npages * pb
+        t_dev = timed(lambda: P.kv_pages_swap_out(pool, wl.num_blocks, ids, dev_buf,
+                                                  stream=stream), 20)
+        t_out = timed(lambda: P.kv_pages_swap_out(pool, wl.num_blocks, ids, host_buf,
+                                                  stream=stream), 5)
+        t_in = timed(lambda: P.kv_pages_swap_in(host_buf, ids, pool, wl.num_blocks,
+                                                stream=stream), 5)
+        keep, ntrim = 4, 1024
+        trims = dev_i32(np.full(wl.num_seqs, ntrim))
+        new_lens = torch.empty(wl.num_seqs, dtype=torch.int32, device="cuda")
+        t_trim = timed(lambda: P.kv_trim_keep_sink(P.KV_INT8_SYM, pool, wl.num_blocks,
+                                                   wl.num_kv_heads, wl.head_dim, st["bt"],
+                                                   st["ctx"], trims, keep, new_lens,
+                                                   stream=stream), 5)
+        moved = int(np.maximum(wl.context_lens.astype(np.int64) - keep - ntrim, 0).sum())
+        trim_bytes = 2 * moved * wl.num_kv_heads * (2 * wl.head_dim + 4)
+        lifecycle = {
+            "pages": npages, "page_bytes": pb,
+            "swap_out_to_device": {"us": round(t_dev * 1e6, 2),
+                                   "gbs": round(2 * nbytes / t_dev / 1e9, 1),
+                                   "hbm_frac": round(2 * nbytes / t_dev / 1e9 / HBM_PEAK_GBS, 4)},
+            "swap_out_to_pinned_host": {"us": round(t_out * 1e6, 2),
+                                        "gbs": round(nbytes / t_out / 1e9, 1)},
+            "swap_in_from_pinned_host": {"us": round(t_in * 1e6, 2),
+                                         "gbs": round(nbytes / t_in / 1e9, 1)},
+            "trim_keep_sink": {"keep": keep, "trim": ntrim, "tokens_moved": moved,
+                               "us": round(t_trim * 1e6, 2),
+                               "gbs": round(trim_bytes / t_trim / 1e9, 1),
+                               "hbm_frac": round(trim_bytes / t_trim / 1e9 / HBM_PEAK_GBS, 4)},
+        }
+        del st, dev_buf, host_buf
+        torch.cuda.empty_cache()
+
     # ---- CPU baseline: the oracle on a bounded sample ------------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -340,6 +393,7 @@ def main():
                               for k, v in res["static"].items()},
         "unfused_step": unfused,
         "multi_token": multi,
+        "lifecycle": lifecycle,
         "points": points,
         "cpu_baseline": cpu,
     }

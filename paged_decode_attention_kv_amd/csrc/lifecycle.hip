@@ -10,11 +10,12 @@
 //   the same page: drop the n tokens after the first `keep` positions, the
 //   INT8 scales moving with their tokens). Every later token moves n
 //   positions toward the front through the sequence's own block table. One
-//   workgroup per (sequence, KV head) moves the tokens in chunks in
-//   increasing position order, each chunk read completely into LDS before
-//   any of it is written: a chunk's destinations lie below its sources and
-//   below every later chunk's sources, so no token is overwritten before it
-//   has been read.
+//   workgroup per (sequence, KV head) moves the tokens in rounds of 128 in
+//   increasing position order, each round read completely (K rows as
+//   16-byte vectors, V as words holding a dimension of four tokens) into
+//   LDS before any of it is written: a round's destinations lie below its
+//   sources and below every later round's sources, so no token is
+//   overwritten before it has been read.
 #include "device_util.h"
 #include "launch.h"
 
@@ -52,19 +53,25 @@ __global__ __launch_bounds__(kCopyThreads) void page_copy_kernel(PageCopyArgs a)
 }
 
 constexpr int kTrimThreads = 256;
-constexpr int kTrimChunk = 64;  // tokens moved per round
+// tokens moved per round (a multiple of 4); rounds of 512 were measured no
+// faster, and the smaller LDS footprint lets several workgroups share a CU
+template <int E>
+constexpr int trim_chunk() {
+  return 128;
+}
 
 // Token layout of a head block: element size E (1: INT8 codes, 2: 16-bit
-// values), K row of D elements at pos * D, V element d of token pos at
-// 16 * D + (pos / 4) * 4 * D + 4 * d + pos % 4 (in elements), and for
-// per-token INT8 the K and V scales (fp16) after the codes.
+// values), K row of D elements at pos * D, V grouped four tokens at a time
+// (element d of token pos at 16 * D + (pos / 4) * 4 * D + 4 * d + pos % 4,
+// so one "V word" of 4 * E bytes holds dimension d of a whole group), and
+// for per-token INT8 the fp16 K and V scales after the codes.
 template <int D, int E, bool Scales>
 struct TokenLayout {
   static constexpr int kHeadBytes = 32 * D * E + (Scales ? 64 : 0);
   static constexpr int kRowBytes = D * E;
   static __device__ __forceinline__ int k_off(int pos) { return pos * D * E; }
-  static __device__ __forceinline__ int v_off(int pos, int d) {
-    return (16 * D + (pos >> 2) * 4 * D + 4 * d + (pos & 3)) * E;
+  static __device__ __forceinline__ int vword_off(int group, int d) {  // group of the page
+    return (16 * D + group * 4 * D + 4 * d) * E;
   }
   static __device__ __forceinline__ int ks_off(int pos) { return 32 * D + 2 * pos; }
   static __device__ __forceinline__ int vs_off(int pos) { return 32 * D + 32 + 2 * pos; }
@@ -74,22 +81,32 @@ template <int E>
 struct Elem;
 template <>
 struct Elem<1> {
-  using T = uint8_t;
+  using T = uint8_t;   // one element
+  using W = uint32_t;  // one V word (4 elements)
 };
 template <>
 struct Elem<2> {
   using T = uint16_t;
+  using W = uint64_t;
 };
 
 template <int D, int E, bool Scales>
 __global__ __launch_bounds__(kTrimThreads) void trim_keep_sink_kernel(TrimArgs a) {
   using Lay = TokenLayout<D, E, Scales>;
   using T = typename Elem<E>::T;
+  using W = typename Elem<E>::W;
+  constexpr int C = trim_chunk<E>();
   constexpr int KV = Lay::kRowBytes / 16;  // 16-byte vectors per K row
-  __shared__ u4_t s_k[kTrimChunk][KV];
-  __shared__ T s_v[kTrimChunk][D];
-  __shared__ uint32_t s_sc[kTrimChunk];  // K scale | V scale << 16
-  __shared__ int s_src[kTrimChunk], s_dst[kTrimChunk];  // head block byte offsets, -1: skip
+  constexpr int KPT = (C * KV + kTrimThreads - 1) / kTrimThreads;  // K vectors per thread
+  constexpr int VG = C / 4 + 1;  // source groups a round touches
+  constexpr int VPT = (VG * D + kTrimThreads - 1) / kTrimThreads;  // V words per thread
+  constexpr int TPT = (C + kTrimThreads - 1) / kTrimThreads;        // tokens per thread
+  __shared__ u4_t s_k[C][KV];
+  __shared__ T s_v[C][D];
+  __shared__ uint32_t s_sc[C];        // K scale | V scale << 16
+  // head-block index of each token's source page (-1: missing) and of its
+  // destination page (-1: missing, or the token is not moved)
+  __shared__ int s_src[C], s_dst[C];
 
   const int b = blockIdx.x / a.num_kv_heads, g = blockIdx.x % a.num_kv_heads;
   const int tid = threadIdx.x;
@@ -106,81 +123,134 @@ __global__ __launch_bounds__(kTrimThreads) void trim_keep_sink_kernel(TrimArgs a
   const int count = L - a.keep - n;  // tokens that move
   if (n == 0 || count <= 0) return;
   const int32_t* row = a.bt + static_cast<int64_t>(b) * a.bt_stride;
+  auto head = [&](int hb) { return a.pool + static_cast<int64_t>(hb) * Lay::kHeadBytes; };
 
-  // byte offset of the head block holding position p, or -1 (flagged)
-  auto head_at = [&](int p) -> int64_t {
-    const int32_t blk = row[p / kBlockSize];
-    if (blk < 0 || blk >= a.num_blocks) {
-      raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
-      return -1;
-    }
-    return static_cast<int64_t>(blk) * a.page_bytes + static_cast<int64_t>(g) * Lay::kHeadBytes;
-  };
-
-  for (int c0 = 0; c0 < count; c0 += kTrimChunk) {
-    const int m = min(kTrimChunk, count - c0);
-    // head blocks of the chunk's sources and destinations (-1: a missing
-    // page on either side; that token is not moved)
-    if (tid < m) {
-      const int64_t hs = head_at(a.keep + n + c0 + tid);
-      const int64_t hd = head_at(a.keep + c0 + tid);
-      const bool ok = hs >= 0 && hd >= 0;
-      // the offsets fit in int32 after dividing out the head block (pool
-      // sizes are checked on the host); keep them as head-block indexes
-      s_src[tid] = ok ? static_cast<int>(hs / Lay::kHeadBytes) : -1;
-      s_dst[tid] = ok ? static_cast<int>(hd / Lay::kHeadBytes) : -1;
+  for (int c0 = 0; c0 < count; c0 += C) {
+    const int m = min(C, count - c0);
+    const int s0 = a.keep + n + c0;  // first source position of the round
+    const int q0 = a.keep + c0;      // its destination
+    for (int i = tid; i < m; i += kTrimThreads) {
+      const int32_t bs = row[(s0 + i) / kBlockSize], bd = row[(q0 + i) / kBlockSize];
+      const bool src_ok = bs >= 0 && bs < a.num_blocks;
+      const bool dst_ok = bd >= 0 && bd < a.num_blocks;
+      if (!src_ok || !dst_ok) raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
+      // the four tokens of a source group share its page, so they share
+      // src_ok: a group's V word is read whenever one of them is moved
+      s_src[i] = src_ok ? bs * a.num_kv_heads + g : -1;
+      s_dst[i] = src_ok && dst_ok ? bd * a.num_kv_heads + g : -1;
     }
     __syncthreads();
-    // read the chunk
-    for (int e = tid; e < m * KV; e += kTrimThreads) {
+
+    // read the round: every load is issued before any is used
+    u4_t kreg[KPT];
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int e = tid + r * kTrimThreads;
       const int i = e / KV, c = e % KV;
-      if (s_src[i] < 0) continue;
-      const int pos = (a.keep + n + c0 + i) % kBlockSize;
-      const uint8_t* h = a.pool + static_cast<int64_t>(s_src[i]) * Lay::kHeadBytes;
-      s_k[i][c] = reinterpret_cast<const u4_t*>(h + Lay::k_off(pos))[c];
+      if (e < m * KV && s_src[i] >= 0) {
+        const uint8_t* h = head(s_src[i]) + Lay::k_off((s0 + i) % kBlockSize);
+        kreg[r] = reinterpret_cast<const u4_t*>(h)[c];
+      }
     }
-    for (int e = tid; e < m * D; e += kTrimThreads) {
-      const int i = e / D, d = e % D;
-      if (s_src[i] < 0) continue;
-      const int pos = (a.keep + n + c0 + i) % kBlockSize;
-      const uint8_t* h = a.pool + static_cast<int64_t>(s_src[i]) * Lay::kHeadBytes;
-      s_v[i][d] = *reinterpret_cast<const T*>(h + Lay::v_off(pos, d));
+    const int gfirst = s0 / 4, ngroups = (s0 + m - 1) / 4 - gfirst + 1;
+    W vreg[VPT];
+#pragma unroll
+    for (int r = 0; r < VPT; ++r) {
+      const int e = tid + r * kTrimThreads;
+      const int gi = e / D, d = e % D;
+      const int p = max(4 * (gfirst + gi), s0);  // an in-round token of the group
+      if (e < ngroups * D && s_src[p - s0] >= 0)
+        vreg[r] = *reinterpret_cast<const W*>(head(s_src[p - s0]) +
+                                              Lay::vword_off((p % kBlockSize) / 4, d));
+    }
+    uint32_t sc[TPT];
+    if constexpr (Scales) {
+#pragma unroll
+      for (int r = 0; r < TPT; ++r) {
+        const int i = tid + r * kTrimThreads;
+        if (i < m && s_src[i] >= 0) {
+          const int pos = (s0 + i) % kBlockSize;
+          const uint8_t* h = head(s_src[i]);
+          sc[r] = *reinterpret_cast<const uint16_t*>(h + Lay::ks_off(pos)) |
+                  (static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(h + Lay::vs_off(pos)))
+                   << 16);
+        }
+      }
+    }
+    // into LDS, token-major
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int e = tid + r * kTrimThreads;
+      if (e < m * KV) s_k[e / KV][e % KV] = kreg[r];
+    }
+#pragma unroll
+    for (int r = 0; r < VPT; ++r) {
+      const int e = tid + r * kTrimThreads;
+      if (e >= ngroups * D) continue;
+      const int gi = e / D, d = e % D;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = 4 * (gfirst + gi) + j;
+        if (p >= s0 && p < s0 + m) s_v[p - s0][d] = static_cast<T>(vreg[r] >> (8 * E * j));
+      }
     }
     if constexpr (Scales) {
-      if (tid < m && s_src[tid] >= 0) {
-        const int pos = (a.keep + n + c0 + tid) % kBlockSize;
-        const uint8_t* h = a.pool + static_cast<int64_t>(s_src[tid]) * Lay::kHeadBytes;
-        s_sc[tid] = *reinterpret_cast<const uint16_t*>(h + Lay::ks_off(pos)) |
-                    (static_cast<uint32_t>(*reinterpret_cast<const uint16_t*>(h + Lay::vs_off(pos)))
-                     << 16);
+#pragma unroll
+      for (int r = 0; r < TPT; ++r) {
+        const int i = tid + r * kTrimThreads;
+        if (i < m) s_sc[i] = sc[r];
       }
     }
     __syncthreads();
-    // write it n positions further to the front
-    for (int e = tid; e < m * KV; e += kTrimThreads) {
+
+    // write the round n positions further to the front: whole V words where
+    // all four tokens of the destination group move in this round, single
+    // elements at the edges (the other tokens of such a word are a sink
+    // token, a token of the next round, or past the new length)
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int e = tid + r * kTrimThreads;
       const int i = e / KV, c = e % KV;
-      if (s_dst[i] < 0) continue;
-      const int pos = (a.keep + c0 + i) % kBlockSize;
-      uint8_t* h = a.pool + static_cast<int64_t>(s_dst[i]) * Lay::kHeadBytes;
-      reinterpret_cast<u4_t*>(h + Lay::k_off(pos))[c] = s_k[i][c];
-    }
-    for (int e = tid; e < m * D; e += kTrimThreads) {
-      const int i = e / D, d = e % D;
-      if (s_dst[i] < 0) continue;
-      const int pos = (a.keep + c0 + i) % kBlockSize;
-      uint8_t* h = a.pool + static_cast<int64_t>(s_dst[i]) * Lay::kHeadBytes;
-      *reinterpret_cast<T*>(h + Lay::v_off(pos, d)) = s_v[i][d];
-    }
-    if constexpr (Scales) {
-      if (tid < m && s_dst[tid] >= 0) {
-        const int pos = (a.keep + c0 + tid) % kBlockSize;
-        uint8_t* h = a.pool + static_cast<int64_t>(s_dst[tid]) * Lay::kHeadBytes;
-        *reinterpret_cast<uint16_t*>(h + Lay::ks_off(pos)) = static_cast<uint16_t>(s_sc[tid]);
-        *reinterpret_cast<uint16_t*>(h + Lay::vs_off(pos)) =
-            static_cast<uint16_t>(s_sc[tid] >> 16);
+      if (e < m * KV && s_dst[i] >= 0) {
+        uint8_t* h = head(s_dst[i]) + Lay::k_off((q0 + i) % kBlockSize);
+        reinterpret_cast<u4_t*>(h)[c] = s_k[i][c];
       }
     }
-    __syncthreads();  // the next chunk reuses the LDS
+    const int hfirst = q0 / 4, nhead = (q0 + m - 1) / 4 - hfirst + 1;
+    for (int e = tid; e < nhead * D; e += kTrimThreads) {
+      const int gi = e / D, d = e % D;
+      const int p0 = 4 * (hfirst + gi);  // first destination position of the group
+      bool whole = p0 >= q0 && p0 + 3 < q0 + m;
+      if (whole) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) whole = whole && s_dst[p0 + j - q0] >= 0;
+      }
+      if (whole) {
+        W w = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w |= static_cast<W>(s_v[p0 + j - q0][d]) << (8 * E * j);
+        uint8_t* h = head(s_dst[p0 - q0]) + Lay::vword_off((p0 % kBlockSize) / 4, d);
+        *reinterpret_cast<W*>(h) = w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int p = p0 + j;
+          if (p < q0 || p >= q0 + m || s_dst[p - q0] < 0) continue;
+          *reinterpret_cast<T*>(head(s_dst[p - q0]) +
+                                Lay::vword_off((p % kBlockSize) / 4, d) + j * E) = s_v[p - q0][d];
+        }
+      }
+    }
+    if constexpr (Scales) {
+      for (int i = tid; i < m; i += kTrimThreads) {
+        if (s_dst[i] < 0) continue;
+        const int pos = (q0 + i) % kBlockSize;
+        uint8_t* h = head(s_dst[i]);
+        *reinterpret_cast<uint16_t*>(h + Lay::ks_off(pos)) = static_cast<uint16_t>(s_sc[i]);
+        *reinterpret_cast<uint16_t*>(h + Lay::vs_off(pos)) = static_cast<uint16_t>(s_sc[i] >> 16);
+      }
+    }
+    __syncthreads();  // the next round reuses the LDS
   }
 }
 
