@@ -50,11 +50,19 @@ DECODE_SOURCES = [os.path.join(ROOT, "paged_decode_attention_kv_amd", "csrc", f)
 
 
 def source_hash() -> str:
+    """Hash of the decode sources' code: comments, blank lines and trailing
+    spaces are left out, so that only a change of the code itself invalidates
+    the committed counter summary."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for path in DECODE_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        code = "\n".join(line.rstrip() for line in text.split("\n") if line.strip())
+        h.update(code.encode())
     return h.hexdigest()[:16]
 
 

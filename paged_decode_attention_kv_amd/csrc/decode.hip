@@ -16,38 +16,46 @@
 // 0..ceil(L_b/16)-1 (a "unit"). Every wave of the grid takes an equal,
 // contiguous run of P items (P = max(4, ceil(total / waves))), so all waves
 // stream the same number of pages whatever the spread of context lengths, and
-// they run independently: no LDS, no barrier. Each wave derives the total and
-// its start from the context lengths itself (a prefix sum over the batch,
-// 64 sequences per step, in registers).
-// A wave walks its run unit by unit ("segments"); in a segment it keeps the
-// next page's loads in flight while it computes the current one. One page =
-// 16 tokens = one 16x16 MFMA tile:
-//  * QK: S[t][h] = sum_d K[t][d] * q[h][d] with K in the A operand (row t =
-//    lane % 16) and the G query heads of the group in the B operand (column
-//    h = lane % 16, zero-padded to 16). Every K byte is fetched once and
-//    shared by the whole GQA group inside the matrix instruction. INT8 codes
-//    become fp16 exactly; q is scaled by a power of two into fp16 range
-//    (exact for fp16/bf16 inputs down to far below any contributing term) and
-//    the scale is undone on the fp32 logits. Products are exact, sums fp32.
-//  * The result tile holds, in lane l, tokens 4*(l/16)+j (j = 0..3) of head
+// they run independently (LDS is private to each wave; no barrier). Each wave
+// derives the total and its start from the context lengths itself (a prefix
+// sum over the batch, 64 sequences per step, in registers).
+// A wave's run crosses one or more units ("segments"). It handles them in
+// passes: a pass plans up to seg_cap segments, reads all their block ids at
+// once, stages their q rows in LDS, and then streams every page of the pass
+// through one pipeline; a segment switch only stashes the finished softmax
+// state in LDS and loads the next q rows from LDS, so the page loads in
+// flight are never waited for early. One page = 16 tokens = one 16x16 MFMA
+// tile:
+//  * QK: S[t][c] = sum_d K[t][d] * q_c[d] with K in the A operand (row t =
+//    lane % 16) and up to 16 query columns in the B operand (column c =
+//    lane % 16, zero-padded): the G query heads of the KV head, or with
+//    several query tokens per sequence the (token, head) pairs of a tile.
+//    Every K byte is fetched once and shared by all columns inside the
+//    matrix instruction. INT8 codes become fp16 exactly; q is scaled by a
+//    power of two into fp16 range (exact for fp16/bf16 inputs down to far
+//    below any contributing term) and the scale is undone on the fp32
+//    logits. Products are exact, sums fp32.
+//  * The result tile holds, in lane l, tokens 4*(l/16)+j (j = 0..3) of column
 //    l % 16 — exactly the B-operand layout the PV product needs, so the
 //    probabilities never leave registers.
-//  * PV: O^T[d][h] = sum_t V[t][d] * P[h][t]. The V codes of four tokens of
+//  * PV: O^T[d][c] = sum_t V[t][d] * P[c][t]. The V codes of four tokens of
 //    one dimension share a 32-bit word in the page: the A operand of one lane
 //    of a 16x16x16 instruction. The fp32 probability (V scale folded in) is
 //    split into a high and a low fp16 part (22 significant bits), contracted
 //    by two instructions.
 //  * Online softmax state (running max m, sum l, accumulator) lives in the
-//    lanes of head l % 16. The V scale sV = f * 2^e (f in [0.5, 1)) enters
+//    lanes of column l % 16. The V scale sV = f * 2^e (f in [0.5, 1)) enters
 //    the logit as the base-2 exponent e, so the folded probabilities
 //    P = 2^(s + e - m) * f never leave the fp16 range whatever the scales.
+//    With static scales the K scale is part of the logit factor and the V
+//    scale multiplies the output.
 // A segment that covers a whole unit writes the output rows directly;
 // otherwise it writes a partial (max, sum, accumulator) into the slot
 // wave + unit (unique: along the item order both indexes only grow and one of
 // them grows at every segment boundary), and merge_kernel combines the
 // partials of each unit that spans several waves. (Merging in the last
-// arriving wave would need device-scope fences, which write back and
-// invalidate the L2 of the XCD: far dearer than the second launch.)
+// arriving wave would need agent-scope fences, which write back and
+// invalidate the L2 of the XCD: measured far dearer than the second launch.)
 #include <type_traits>
 
 #include "device_util.h"
