@@ -105,6 +105,7 @@ struct TrimArgs {
   const int32_t* trim;  // tokens to drop after the sink, per sequence
   int32_t* new_ctx;
   int num_seqs, num_kv_heads, keep;
+  int windows;  // workgroups per (sequence, KV head); set by the launcher
   int32_t* err;
 };
 

@@ -85,11 +85,12 @@ KINDS = ["int8", "static", "16bit"]
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("keep", [0, 4])
 def test_trim_keep_sink_matches_oracle(P, kind, keep):
-    """Trims below a chunk, across many chunks, page-aligned, clamped, and
-    zero, over shuffled pages; the pool after the trim is the oracle's byte
-    for byte."""
-    lens = [700, 300, 40, 3, 129, 1030]
-    trims = [100, 3, 999, 1, 16, 777]
+    """Trims below a round of 128 tokens (one workgroup walks the sequence),
+    of 128 and more (windows of 128 residues mod n, several rounds each, n not
+    a multiple of 4), page-aligned, clamped, and zero, over shuffled pages;
+    the pool after the trim is the oracle's byte for byte."""
+    lens = [700, 300, 40, 3, 129, 1030, 2000, 1000, 700]
+    trims = [100, 3, 999, 1, 16, 777, 301, 128, 130]
     wl = build("trim", 31 + keep, [("prefill", lens)], 8, 2, 128 if kind != "static" else 64,
                "f16", "outlier", shuffle=True, spare_blocks=2)
     fmt, ofmt, pool = _pool(P, wl, kind)
@@ -103,6 +104,32 @@ def test_trim_keep_sink_matches_oracle(P, kind, keep):
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     want_lens = oracle.trim_keep_sink(ofmt, host, wl.block_tables, wl.context_lens, trims, keep,
+                                      16, wl.num_kv_heads, wl.head_dim)
+    assert new.cpu().numpy().tolist() == want_lens.tolist()
+    assert np.array_equal(pool.cpu().numpy(), host)
+
+
+@pytest.mark.parametrize("kind", ["int8", "16bit"])
+def test_trim_many_sequences(P, kind):
+    """1024 (sequence, KV head) pairs: the launch runs one workgroup per pair,
+    which then walks every window of a large trim in turn; mixed small and
+    large trims, random lengths."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(1, 900, size=128).tolist()
+    trims = rng.integers(0, 1000, size=128).astype(np.int32)
+    wl = build("trim-many", 78, [("prefill", lens)], 8, 8, 64, "f16", "normal", shuffle=True,
+               spare_blocks=1)
+    fmt, ofmt, pool = _pool(P, wl, kind)
+    host = pool.cpu().numpy()
+    new = torch.zeros(len(lens), dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _say(f"trim many sequences {kind}")
+    P.kv_trim_keep_sink(fmt, pool, wl.num_blocks, wl.num_kv_heads, wl.head_dim,
+                        dev_i32(wl.block_tables), dev_i32(wl.context_lens), dev_i32(trims), 4,
+                        new, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    want_lens = oracle.trim_keep_sink(ofmt, host, wl.block_tables, wl.context_lens, trims, 4,
                                       16, wl.num_kv_heads, wl.head_dim)
     assert new.cpu().numpy().tolist() == want_lens.tolist()
     assert np.array_equal(pool.cpu().numpy(), host)
@@ -143,3 +170,20 @@ def test_trim_flags_a_missing_page(P):
     torch.cuda.synchronize()
     assert int(err.item()) == P.EFLAG_BLOCK_RANGE
     assert int(new.item()) == 80
+
+
+def test_trim_flags_a_missing_page_large_trim(P):
+    """The same with a trim above 128 tokens (several windows): the missing
+    page is flagged and the new length is still the clamped one."""
+    wl = build("trim-bad-wide", 9, [("prefill", [900])], 8, 2, 64, "f16", "normal",
+               spare_blocks=1)
+    pool, _ = gpu_pool(P, wl, P.KV_INT8_SYM)
+    bt = wl.block_tables.copy()
+    bt[0, 40] = -1
+    new = torch.zeros(1, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    P.kv_trim_keep_sink(P.KV_INT8_SYM, pool, wl.num_blocks, 2, 64, dev_i32(bt),
+                        dev_i32(wl.context_lens), dev_i32([300]), 4, new, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == P.EFLAG_BLOCK_RANGE
+    assert int(new.item()) == 600
