@@ -62,8 +62,8 @@ template <int E>
 constexpr int trim_chunk() {
   return kTrimRound;
 }
-// workgroups a trim launch aims for (about four per compute unit)
-constexpr int64_t kTrimWorkgroups = 1024;
+// workgroups a trim launch aims for (about sixteen per compute unit)
+constexpr int64_t kTrimWorkgroups = 4096;
 
 // Token layout of a head block: element size E (1: INT8 codes, 2: 16-bit
 // values), K row of D elements at pos * D, V grouped four tokens at a time
@@ -137,9 +137,11 @@ __global__ __launch_bounds__(kTrimThreads) void trim_keep_sink_kernel(TrimArgs a
   __shared__ int s_src[C], s_dst[C];
   __shared__ int s_whole[VG];  // destination group: all four tokens move in this round
 
-  const int per_seq = a.num_kv_heads * a.windows;
-  const int b = blockIdx.x / per_seq;
-  const int g = blockIdx.x % per_seq / a.windows, w0 = blockIdx.x % a.windows;
+  // window-major: the first windows of all pairs come first, so that the
+  // busy workgroups of a small trim (window 0 only) spread over the XCDs
+  const int units = a.num_seqs * a.num_kv_heads;
+  const int w0 = blockIdx.x / units, unit = blockIdx.x % units;
+  const int b = unit / a.num_kv_heads, g = unit % a.num_kv_heads;
   const int tid = threadIdx.x;
   const bool leader = g == 0 && w0 == 0 && tid == 0;
   int L = a.ctx[b];
