@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from tests.gpu_util import (FILL, MAX_ABS_TOL, dev_i32, gpu_decode, gpu_pool, oracle_decode,
-                            oracle_pool, require_gpu, to_dev)
+                            oracle_pool, oracle_static_pool, require_gpu)
 from workloads import build, make_config
 
 pytestmark = pytest.mark.gpu
@@ -24,28 +24,24 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _static_pool(P, wl, ks=0.05, vs=0.05):
-    pb = P.pdakv_page_bytes(P.KV_INT8_STATIC, 16, wl.num_kv_heads, wl.head_dim)
-    pool = torch.full((wl.num_blocks, pb), FILL, dtype=torch.uint8, device="cuda")
-    for ph in wl.phases:
-        P.kv_quant_int8_static_write(to_dev(ph.k), to_dev(ph.v), dev_i32(ph.slot_mapping), pool,
-                                     wl.num_blocks, ks, vs)
-    return pool
-
-
 def _pool(P, wl, kind):
+    """(library format, oracle format, device pool, host pool): the pool is
+    built by the oracle on the host and copied to the device, so the
+    lifecycle kernels and the oracle start from the same bytes."""
     if kind == "int8":
-        return P.KV_INT8_SYM, oracle.KV_INT8_SYM, gpu_pool(P, wl, P.KV_INT8_SYM)[0]
-    if kind == "static":
-        return P.KV_INT8_STATIC, oracle.KV_INT8_STATIC, _static_pool(P, wl)
-    return P.KV_16BIT, oracle.KV_16BIT, gpu_pool(P, wl, P.KV_16BIT)[0]
+        fmt, ofmt, host = P.KV_INT8_SYM, oracle.KV_INT8_SYM, oracle_pool(wl, oracle.KV_INT8_SYM)
+    elif kind == "static":
+        fmt, ofmt = P.KV_INT8_STATIC, oracle.KV_INT8_STATIC
+        host = oracle_static_pool(wl, 0.05, 0.05)
+    else:
+        fmt, ofmt, host = P.KV_16BIT, oracle.KV_16BIT, oracle_pool(wl, oracle.KV_16BIT)
+    return fmt, ofmt, torch.from_numpy(host).cuda(), host.copy()
 
 
 @pytest.mark.parametrize("to_host", [False, True])
 def test_swap_out_and_in(P, to_host):
     wl = make_config(3, 0.05)
-    pool, _ = gpu_pool(P, wl, P.KV_INT8_SYM)
-    host_ref = pool.cpu().numpy()
+    _, _, pool, host_ref = _pool(P, wl, "int8")
     rng = np.random.default_rng(0)
     ids = rng.permutation(wl.num_blocks)[:9].astype(np.int32)
     ids_bad = np.concatenate([ids[:4], [-1, wl.num_blocks], ids[4:]]).astype(np.int32)
@@ -93,8 +89,7 @@ def test_trim_keep_sink_matches_oracle(P, kind, keep):
     trims = [100, 3, 999, 1, 16, 777, 301, 128, 130]
     wl = build("trim", 31 + keep, [("prefill", lens)], 8, 2, 128 if kind != "static" else 64,
                "f16", "outlier", shuffle=True, spare_blocks=2)
-    fmt, ofmt, pool = _pool(P, wl, kind)
-    host = pool.cpu().numpy()
+    fmt, ofmt, pool, host = _pool(P, wl, kind)
     new = torch.zeros(len(lens), dtype=torch.int32, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     _say(f"trim {kind} keep {keep}")
@@ -119,8 +114,7 @@ def test_trim_many_sequences(P, kind):
     trims = rng.integers(0, 1000, size=128).astype(np.int32)
     wl = build("trim-many", 78, [("prefill", lens)], 8, 8, 64, "f16", "normal", shuffle=True,
                spare_blocks=1)
-    fmt, ofmt, pool = _pool(P, wl, kind)
-    host = pool.cpu().numpy()
+    fmt, ofmt, pool, host = _pool(P, wl, kind)
     new = torch.zeros(len(lens), dtype=torch.int32, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     _say(f"trim many sequences {kind}")
@@ -187,3 +181,51 @@ def test_trim_flags_a_missing_page_large_trim(P):
     torch.cuda.synchronize()
     assert int(err.item()) == P.EFLAG_BLOCK_RANGE
     assert int(new.item()) == 600
+
+
+@pytest.mark.slow
+def test_trim_full_size_sampled(P):
+    """The batched step's full pool (64 sequences, 1K-8K tokens, 8 KV heads,
+    written by the library) trimmed as the bench times it (1,024 tokens after
+    4 sinks, every sequence), then trimmed again by seeded amounts from 0 to
+    3,000 on the new lengths. For sampled sequences every kept token's codes
+    and scales, all heads, equal the oracle's quantization of the source
+    rows at the positions the two trims leave them."""
+    wl = make_config(3)
+    _say(f"full-size trim: {wl.num_seqs} seqs, max ctx {wl.max_context_len}")
+    pool, _ = gpu_pool(P, wl, P.KV_INT8_SYM)
+    keep = 4
+    first = np.full(wl.num_seqs, 1024, dtype=np.int32)
+    second = np.random.default_rng(12).integers(0, 3001, size=wl.num_seqs).astype(np.int32)
+    lens0 = wl.context_lens.astype(np.int64)
+    mid = torch.zeros(wl.num_seqs, dtype=torch.int32, device="cuda")
+    end = torch.zeros(wl.num_seqs, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bt = dev_i32(wl.block_tables)
+    P.kv_trim_keep_sink(P.KV_INT8_SYM, pool, wl.num_blocks, wl.num_kv_heads, wl.head_dim, bt,
+                        dev_i32(wl.context_lens), dev_i32(first), keep, mid, err_flag=err)
+    P.kv_trim_keep_sink(P.KV_INT8_SYM, pool, wl.num_blocks, wl.num_kv_heads, wl.head_dim, bt,
+                        mid, dev_i32(second), keep, end, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+
+    def kept(L, n):  # positions a trim keeps, in order (the trim's definition)
+        n = min(max(int(n), 0), max(L - keep, 0))
+        return np.concatenate([np.arange(min(keep, L)), np.arange(keep + n, L)]).astype(np.int64)
+
+    host = pool.cpu().numpy()
+    got_end = end.cpu().numpy()
+    for b in np.random.default_rng(13).choice(wl.num_seqs, 6, replace=False):
+        L = int(lens0[b])
+        idx1 = kept(L, first[b])
+        idx = idx1[kept(len(idx1), second[b])]
+        assert int(got_end[b]) == len(idx)
+        k, v = wl.tokens_of_seq(int(b))
+        kc, ks = oracle.quantize_rows(k)
+        vc, vs = oracle.quantize_rows(v)
+        gk, gks, gv, gvs = oracle.gather_int8_sequence(host, wl.block_tables[b], len(idx), 16,
+                                                       wl.num_kv_heads, wl.head_dim)
+        assert np.array_equal(gk, kc[idx]) and np.array_equal(gv, vc[idx])
+        assert np.array_equal(gks.view(np.uint16), ks[idx].view(np.uint16))
+        assert np.array_equal(gvs.view(np.uint16), vs[idx].view(np.uint16))
+        _say(f"  seq {b}: {L} -> {len(idx)} tokens, codes and scales exact")
