@@ -9,13 +9,13 @@
 // * Front trim that keeps sink tokens (mlxcel PR #717 and its follow-up on
 //   the same page: drop the n tokens after the first `keep` positions, the
 //   INT8 scales moving with their tokens). Every later token moves n
-//   positions toward the front through the sequence's own block table. One
-//   workgroup per (sequence, KV head) moves the tokens in rounds of 128 in
-//   increasing position order, each round read completely (K rows as
-//   16-byte vectors, V as words holding a dimension of four tokens) into
-//   LDS before any of it is written: a round's destinations lie below its
-//   sources and below every later round's sources, so no token is
-//   overwritten before it has been read.
+//   positions toward the front through the sequence's own block table.
+//   Workgroups move rounds of up to 128 tokens, each round read completely
+//   (K rows as 16-byte vectors, V as words holding a dimension of four
+//   tokens) into LDS before any of it is written. A small trim is one chain
+//   of rounds per (sequence, KV head); a trim of 128 or more splits into
+//   windows of residues mod n that run in parallel (the ordering argument is
+//   given above the kernel).
 #include <algorithm>
 
 #include "device_util.h"
@@ -55,13 +55,9 @@ __global__ __launch_bounds__(kCopyThreads) void page_copy_kernel(PageCopyArgs a)
 }
 
 constexpr int kTrimThreads = 256;
-// tokens moved per round (a multiple of 4); rounds of 512 were measured no
-// faster, and the smaller LDS footprint lets several workgroups share a CU
+// tokens moved per round (a multiple of 4); rounds of 256 measured slower
+// (fewer workgroups per CU and fewer windows), 512 no faster
 constexpr int kTrimRound = 128;
-template <int E>
-constexpr int trim_chunk() {
-  return kTrimRound;
-}
 // workgroups a trim launch aims for (about sixteen per compute unit)
 constexpr int64_t kTrimWorkgroups = 4096;
 
@@ -119,7 +115,7 @@ __global__ __launch_bounds__(kTrimThreads) void trim_keep_sink_kernel(TrimArgs a
   using Lay = TokenLayout<D, E, Scales>;
   using T = typename Elem<E>::T;
   using W = typename Elem<E>::W;
-  constexpr int C = trim_chunk<E>();
+  constexpr int C = kTrimRound;
   constexpr int KV = Lay::kRowBytes / 16;  // 16-byte vectors per K row
   static_assert(C * KV % kTrimThreads == 0, "K vectors split evenly over the threads");
   constexpr int KPT = C * KV / kTrimThreads;  // K vectors per thread
