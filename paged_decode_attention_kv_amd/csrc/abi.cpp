@@ -258,13 +258,23 @@ int decode_common(int fmt, Scales sc, const Rows& r, const AppendRows* app,
   a.num_waves = static_cast<int>(plan_waves(fmt, num_seqs, a.vheads, max_context_len));
   a.merge_waves = merge_waves(num_seqs, a.vheads, max_context_len, a.num_waves);
   {
-    // LDS staging per decode pass and segment: the unit's q rows (16-bit),
-    // its result (accumulator, max, sum per column) and the appended token
-    // (4 * head_dim bytes), regions aligned to 16 bytes
+    // LDS staging of a decode pass of n segments: each segment's q rows
+    // (16-bit, n slots at the top of the q/result area), each segment's
+    // result (accumulator, max, sum per column; slots from the bottom) and,
+    // with the fused append, each segment's new token (4 * head_dim bytes).
+    // A segment's result is stashed at the switch to the next segment, after
+    // that segment's q rows are read, and may cover q slots already read;
+    // the last result is stashed after the others are written out. So the
+    // area needs max(n * qb, (n - 1) * rb, rb) bytes (rb > qb).
     const int qb = a.slot_cols * head_dim * 2, rb = a.slot_cols * (head_dim + 2) * 4;
-    const int nb = 4 * head_dim;
-    a.seg_cap = std::max(1, std::min(64, (pdakv::kLdsPerWave - 16) / (qb + rb + nb)));
-    a.lds_wave_bytes = (a.seg_cap * (qb + rb) + 15) / 16 * 16 + a.seg_cap * nb;
+    const int nb = app ? 4 * head_dim : 0;
+    auto area = [&](int n) { return (std::max({n * qb, (n - 1) * rb, rb}) + 15) / 16 * 16; };
+    int n = 1;
+    while (n < 64 && area(n + 1) + (n + 1) * nb <= pdakv::kLdsPerWave) ++n;
+    a.seg_cap = n;
+    a.lds_q_off = area(n) - n * qb;
+    a.lds_nt_off = area(n);
+    a.lds_wave_bytes = area(n) + n * nb;
   }
   a.ws = static_cast<float*>(workspace);
   a.desc = reinterpret_cast<int2*>(
