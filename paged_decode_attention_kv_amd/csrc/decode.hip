@@ -1205,51 +1205,63 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
 // Combine the partials of a unit that spans several waves, per (query token,
 // query head) column: out = sum_i 2^(m_i - m) acc_i / sum_i 2^(m_i - m) l_i
 // over the waves i that cover the unit (m = max_i m_i), as recorded by the
-// unit's first wave. One workgroup per (sequence, query token, query head)
-// with a.merge_waves waves: wave w folds
-// the partials w, w + waves, ... into a running (max, sum, accumulator),
-// kMergeBatch partials per round trip (lane j holds dims j, j + 64); the
-// waves then combine through LDS.
+// unit's first wave. One workgroup per MC columns of a unit (64 / MC lanes
+// per column, lane l of a column holding dims l, l + 64 / MC, ...) with
+// a.merge_waves waves: wave w folds the partials w, w + waves, ... into a
+// running (max, sum, accumulator), kMergeBatch partials per round trip; the
+// waves then combine through LDS. Four columns per workgroup pay off once a
+// unit has 16 columns (several query tokens): a quarter of the workgroups,
+// each with four times the loads in flight.
 constexpr int kMergeBatch = 8;
 
-template <int D>
+template <int MC>
+__host__ __device__ constexpr int merge_groups(int slot_cols) {
+  return (slot_cols + MC - 1) / MC;
+}
+
+template <int D, int MC>
 __global__ __launch_bounds__(64 * kMaxMergeWaves) void merge_kernel(DecodeArgs a) {
-  constexpr int ND = D / 64;  // dims per lane
-  __shared__ float s_m[kMaxMergeWaves], s_l[kMaxMergeWaves], s_acc[kMaxMergeWaves][D];
+  constexpr int LPC = 64 / MC;   // lanes per column
+  constexpr int DPL = D / LPC;   // dims per lane
+  // with several waves: per wave and column the accumulator, max and sum
+  // ([waves][MC][D + 2] floats, sized at launch)
+  extern __shared__ float merge_lds[];
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
-  const int rows = a.qtok * a.num_q_heads;
-  const int b = blockIdx.x / rows, r = blockIdx.x % rows;
-  const int j = r / a.num_q_heads, h = r % a.num_q_heads;
-  const int g = h / a.group;
-  const int col = j * a.group + h % a.group;  // column of KV head g
-  const int tile = col / 16;                  // 0 unless several tiles
-  const int cc = col - 16 * tile;             // column inside the unit
-  const int u = b * a.vheads + g * a.ntile + tile;
+  const int groups = merge_groups<MC>(a.slot_cols);
+  const int per_seq = a.vheads * groups;
+  const int b = blockIdx.x / per_seq, vg = blockIdx.x % per_seq / groups;
+  const int grp = blockIdx.x % groups;
+  const int u = b * a.vheads + vg;
   // the unit's record is this call's only if the sequence has pages (its
   // first wave wrote it)
   const int2 rec = a.desc[u];
   const int L = a.ctx[b];
   if (L <= 0 || rec.y <= 1) return;  // no pages, or written directly
+  const UnitCols uc = unit_cols<true>(a, vg);
+  const int ci = lane / LPC, li = lane % LPC;
+  const int cc = grp * MC + ci;  // column inside the unit
+  const bool valid = cc < uc.n;
   const int n = rec.y;
   const int64_t stride = static_cast<int64_t>(a.slot_cols) * (D + 2);
-  const float* base = a.ws + (static_cast<int64_t>(rec.x) + u) * stride + cc * (D + 2);
+  const float* base = a.ws + (static_cast<int64_t>(rec.x) + u) * stride +
+                      (valid ? cc : 0) * (D + 2) + li;
 
-  float mw = kMaxInit, lw = 0.f, acc[ND];
+  float mw = kMaxInit, lw = 0.f, acc[DPL];
 #pragma unroll
-  for (int k = 0; k < ND; ++k) acc[k] = 0.f;
+  for (int k = 0; k < DPL; ++k) acc[k] = 0.f;
   for (int i0 = w; i0 < n; i0 += nw * kMergeBatch) {
-    float m[kMergeBatch], l[kMergeBatch], v[kMergeBatch][ND];
+    float m[kMergeBatch], l[kMergeBatch], v[kMergeBatch][DPL];
 #pragma unroll
     for (int r = 0; r < kMergeBatch; ++r) {
       // entries past n repeat the last partial's loads and are zeroed
       const int i = i0 + r * nw;
       const float* pi = base + (i < n ? i : n - 1) * stride;
-      m[r] = i < n ? pi[D] : kMaxInit;
-      l[r] = i < n ? pi[D + 1] : 0.f;
+      m[r] = i < n ? pi[D - li] : kMaxInit;
+      l[r] = i < n ? pi[D + 1 - li] : 0.f;
 #pragma unroll
-      for (int k = 0; k < ND; ++k) v[r][k] = i < n ? pi[lane + 64 * k] : 0.f;
+      for (int k = 0; k < DPL; ++k) v[r][k] = i < n ? pi[LPC * k] : 0.f;
     }
     float mn = mw;
 #pragma unroll
@@ -1257,50 +1269,64 @@ __global__ __launch_bounds__(64 * kMaxMergeWaves) void merge_kernel(DecodeArgs a
     const float c = exp2f(mw - mn);
     lw *= c;
 #pragma unroll
-    for (int k = 0; k < ND; ++k) acc[k] *= c;
+    for (int k = 0; k < DPL; ++k) acc[k] *= c;
 #pragma unroll
     for (int r = 0; r < kMergeBatch; ++r) {
       const float e = exp2f(m[r] - mn);
       lw += e * l[r];
 #pragma unroll
-      for (int k = 0; k < ND; ++k) acc[k] += e * v[r][k];
+      for (int k = 0; k < DPL; ++k) acc[k] += e * v[r][k];
     }
     mw = mn;
   }
-  const int64_t o = b * a.out_ss + j * a.out_st + h * a.out_sh;
+  const int col = uc.col0 + (valid ? cc : 0);
+  const int64_t o = b * a.out_ss + (col / a.group) * a.out_st +
+                    (uc.g * a.group + col % a.group) * a.out_sh;
   if (nw == 1) {
     // lw == 0: no attendable token in the unit
+    if (valid) {
 #pragma unroll
-    for (int k = 0; k < ND; ++k)
-      store_out(a.out, a.out_dtype, o + lane + 64 * k, lw > 0.f ? acc[k] / lw * a.out_mul : 0.f);
+      for (int k = 0; k < DPL; ++k)
+        store_out(a.out, a.out_dtype, o + li + LPC * k, lw > 0.f ? acc[k] / lw * a.out_mul : 0.f);
+    }
     return;
   }
-  if (lane == 0) {
-    s_m[w] = mw;
-    s_l[w] = lw;
+  auto slot = [&](int wave) { return merge_lds + (wave * MC + ci) * (D + 2); };
+  float* mine = slot(w);
+  if (li == 0) {
+    mine[D] = mw;
+    mine[D + 1] = lw;
   }
 #pragma unroll
-  for (int k = 0; k < ND; ++k) s_acc[w][lane + 64 * k] = acc[k];
+  for (int k = 0; k < DPL; ++k) mine[li + LPC * k] = acc[k];
   __syncthreads();
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float ms = kMaxInit;
-    for (int j = 0; j < nw; ++j) ms = fmaxf(ms, s_m[j]);
-    float num = 0.f, den = 0.f;
-    for (int j = 0; j < nw; ++j) {
-      const float e = exp2f(s_m[j] - ms);
-      num += e * s_acc[j][d];
-      den += e * s_l[j];
-    }
-    store_out(a.out, a.out_dtype, o + d, den > 0.f ? num / den * a.out_mul : 0.f);
+  if (!valid || w != 0) return;
+  float ms = kMaxInit;
+  for (int j = 0; j < nw; ++j) ms = fmaxf(ms, slot(j)[D]);
+  float den = 0.f;
+  for (int j = 0; j < nw; ++j) den += exp2f(slot(j)[D] - ms) * slot(j)[D + 1];
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) {
+    float num = 0.f;
+    for (int j = 0; j < nw; ++j) num += exp2f(slot(j)[D] - ms) * slot(j)[li + LPC * k];
+    store_out(a.out, a.out_dtype, o + li + LPC * k, den > 0.f ? num / den * a.out_mul : 0.f);
   }
+}
+
+template <int D, int MC>
+hipError_t launch_merge_cols(const DecodeArgs& a, hipStream_t s) {
+  const size_t lds =
+      a.merge_waves > 1 ? static_cast<size_t>(a.merge_waves) * MC * (D + 2) * 4 : 0;
+  hipLaunchKernelGGL((merge_kernel<D, MC>),
+                     dim3(a.num_seqs * a.vheads * merge_groups<MC>(a.slot_cols)),
+                     dim3(64 * a.merge_waves), lds, s, a);
+  return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
   if (a.max_ctx == 0) return hipSuccess;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(a.num_seqs * a.qtok * a.num_q_heads),
-                     dim3(64 * a.merge_waves), 0, s, a);
-  return hipGetLastError();
+  return a.slot_cols > 8 ? launch_merge_cols<D, 4>(a, s) : launch_merge_cols<D, 1>(a, s);
 }
 
 // The decode grid (one resident round of waves, planned on the host) with its

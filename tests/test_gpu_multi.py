@@ -92,6 +92,17 @@ def test_multi_other_shapes(P, fmt_name, hq, hkv, d, dt, T):
     assert torch.all(out[0] == 0)  # empty sequence: zero rows
 
 
+@pytest.mark.parametrize("fmt_name", ["int8", "16bit"])
+def test_multi_long_context_many_partials(P, fmt_name):
+    """One 20,000-token sequence and a short one, 4 query tokens: each
+    16-column unit is split over hundreds of waves, so the merge runs its
+    most waves per workgroup and combines them through LDS."""
+    wl = build("multi-long", 61, [("prefill", [20000, 40])], 32, 8, 128, "f16", "outlier",
+               shuffle=True)
+    _say(f"multi {fmt_name} long context")
+    _check(P, wl, fmt_name, 4, seed=62)
+
+
 def test_multi_one_token_equals_the_plain_decode(P):
     wl = make_config(3, 0.05)
     pool, _ = gpu_pool(P, wl, P.KV_INT8_SYM)
