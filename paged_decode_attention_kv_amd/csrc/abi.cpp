@@ -259,20 +259,26 @@ int decode_common(int fmt, Scales sc, const Rows& r, const AppendRows* app,
   a.merge_waves = merge_waves(num_seqs, a.vheads, max_context_len, a.num_waves);
   {
     // LDS staging of a decode pass of n segments: each segment's q rows
-    // (16-bit, n slots at the top of the q/result area), each segment's
-    // result (accumulator, max, sum per column; slots from the bottom) and,
-    // with the fused append, each segment's new token (4 * head_dim bytes).
-    // A segment's result is stashed at the switch to the next segment, after
-    // that segment's q rows are read, and may cover q slots already read;
-    // the last result is stashed after the others are written out. So the
-    // area needs max(n * qb, (n - 1) * rb, rb) bytes (rb > qb).
+    // (16-bit), each segment's result (accumulator, max, sum per column)
+    // and, with the fused append, each segment's new token (4 * head_dim
+    // bytes). One-token kernels keep three separate regions. The
+    // several-token kernels (16-column segments) let a segment's result,
+    // stashed at the switch to the next segment before that segment's q
+    // rows are read, cover q slots already read: q slots at the top of the
+    // area, result slots from the bottom, the last result stashed in slot 0
+    // once the others are written out; the area then needs
+    // max(n * qb, (n - 1) * rb + qb, rb) bytes (rb > qb).
     const int qb = a.slot_cols * head_dim * 2, rb = a.slot_cols * (head_dim + 2) * 4;
     const int nb = app ? 4 * head_dim : 0;
-    auto area = [&](int n) { return (std::max({n * qb, (n - 1) * rb, rb}) + 15) / 16 * 16; };
+    auto up16 = [](int x) { return (x + 15) / 16 * 16; };
+    auto area = [&](int n) {
+      return r.multi ? up16(std::max({n * qb, (n - 1) * rb + qb, rb})) : up16(n * (qb + rb));
+    };
     int n = 1;
     while (n < 64 && area(n + 1) + (n + 1) * nb <= pdakv::kLdsPerWave) ++n;
     a.seg_cap = n;
-    a.lds_q_off = area(n) - n * qb;
+    a.lds_q_off = r.multi ? area(n) - n * qb : 0;
+    a.lds_res_off = r.multi ? 0 : n * qb;
     a.lds_nt_off = area(n);
     a.lds_wave_bytes = area(n) + n * nb;
   }

@@ -788,13 +788,15 @@ struct F16Kind {
 // ---------------------------------------------------------------------------
 
 // Per-wave LDS staging of one pass: the q rows of each segment's unit
-// ([C][D] 16-bit values, C = a.slot_cols columns; slots at the top of the
-// area) and each segment's result ([C][D + 2] floats: accumulator, running
-// max, sum; slots from the bottom). Segment s's result is stashed when
-// segment s + 1 starts, after s + 1's q rows are in registers, and may cover
-// the q slots up to s + 1; the host sizes the area (a.seg_cap segments) so
-// that it never reaches a later segment's q rows. The last segment's result
-// is stashed in slot 0 once the others are written out.
+// ([C][D] 16-bit values, C = a.slot_cols columns) and each segment's result
+// ([C][D + 2] floats: accumulator, running max, sum), a.seg_cap segments
+// (offsets set on the host). One-token kernels keep the two in separate
+// regions. The several-token kernels put the q slots at the top of the area
+// and the result slots at its bottom: segment s's result, stashed when
+// segment s + 1 starts and before s + 1's q rows are read, may cover the q
+// slots up to s but never a later one, and the last segment's result is
+// stashed in slot 0 once the others are written out (so a pass holds two
+// 16-column segments where separate regions held one).
 struct PassLds {
   uint16_t* q;   // [seg_cap][C][D]
   float* res;    // [C][D + 2] per slot
@@ -1037,13 +1039,10 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
       const int i = first + j;
       if (i >= items) return false;
       if (i == c_end) {  // next segment: only registers and LDS are touched
-        // the next q rows are read before this result is stashed (it may
-        // cover their slot)
-        const int done = cs, done_n = c_n;
+        stash_result<K>(a, st, lds.res + cs * C * (D + 2), i16, kb, c_n);
         enter(cs + 1);
-        kind.load_q(a, lds.q + cs * C * D, i16, kb, i16 < c_n);
-        stash_result<K>(a, st, lds.res + done * C * (D + 2), i16, kb, done_n);
         softmax_init(st);
+        kind.load_q(a, lds.q + cs * C * D, i16, kb, i16 < c_n);
       }
       const int t = c_tok + (i - c_start) * kBlockSize;
       if (!Multi && c_patch && i == c_end - 1)
@@ -1091,6 +1090,8 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     __builtin_amdgcn_sched_barrier(0);
     if (!more || i + 2 * G >= items) break;
   }
+  if constexpr (!Multi) stash_result<K>(a, st, lds.res + cs * C * (D + 2), i16, kb, c_n);
+
   if (!Multi && a.append) {
     for (int s = 0; s < ns; ++s) {
       const int hb = block_of(readlane(s_start, s) + readlane(s_n, s) - 1);
@@ -1099,13 +1100,21 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
                    lane);
     }
   }
-  // the earlier segments' results from their slots, then the last one's
-  // (still in registers) through slot 0
-  for (int s = 0; s <= ns - 1; ++s) {
-    if (s == ns - 1) stash_result<K>(a, st, lds.res, i16, kb, c_n);
-    const int u = readlane(s_unit, s);
-    write_result<D, Multi>(a, lds.res + (s == ns - 1 ? 0 : s) * C * (D + 2), u / vh, u % vh,
-                           wave + u, readlane(s_whole, s) != 0, lane);
+  if constexpr (Multi) {
+    // the earlier segments' results from their slots, then the last one's
+    // (still in registers) through slot 0
+    for (int s = 0; s <= ns - 1; ++s) {
+      if (s == ns - 1) stash_result<K>(a, st, lds.res, i16, kb, c_n);
+      const int u = readlane(s_unit, s);
+      write_result<D, Multi>(a, lds.res + (s == ns - 1 ? 0 : s) * C * (D + 2), u / vh, u % vh,
+                             wave + u, readlane(s_whole, s) != 0, lane);
+    }
+  } else {
+    for (int s = 0; s < ns; ++s) {
+      const int u = readlane(s_unit, s);
+      write_result<D, Multi>(a, lds.res + s * C * (D + 2), u / vh, u % vh, wave + u,
+                             readlane(s_whole, s) != 0, lane);
+    }
   }
   return items;
 }
@@ -1119,7 +1128,7 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs& a) {
   const int vh = Multi ? a.vheads : a.num_kv_heads;  // units per sequence
   PassLds lds;
   lds.q = reinterpret_cast<uint16_t*>(smem + wid * a.lds_wave_bytes + a.lds_q_off);
-  lds.res = reinterpret_cast<float*>(smem + wid * a.lds_wave_bytes);
+  lds.res = reinterpret_cast<float*>(smem + wid * a.lds_wave_bytes + a.lds_res_off);
   lds.nt = smem + wid * a.lds_wave_bytes + a.lds_nt_off;
 
   // total pages; zero rows of empty sequences

@@ -73,8 +73,9 @@ struct DecodeArgs {
   int merge_waves;   // waves per merge workgroup (1 .. kMaxMergeWaves)
   int seg_cap;       // decode: segments staged in LDS per pass
   int lds_wave_bytes;  // decode: LDS per wave (q rows, results, appended tokens)
-  int lds_q_off;       // decode: offset of the q rows in a wave's LDS (results at 0)
-  int lds_nt_off;      // decode: offset of the appended tokens in a wave's LDS
+  int lds_q_off;       // decode: offsets of the q rows, results and appended
+  int lds_res_off;     // tokens in a wave's LDS
+  int lds_nt_off;
   // append (fused write of each sequence's newest token, at position L - 1):
   // 16-bit K and V rows [B][Hkv][D] in q's dtype, element strides
   int append;
