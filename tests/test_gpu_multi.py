@@ -103,6 +103,18 @@ def test_multi_long_context_many_partials(P, fmt_name):
     _check(P, wl, fmt_name, 4, seed=62)
 
 
+@pytest.mark.parametrize("fmt_name", ["int8", "16bit"])
+def test_multi_many_short_sequences(P, fmt_name):
+    """40 sequences of 1 to 60 tokens (1 to 4 pages), 4 query tokens at the
+    Llama shape: a wave's items cross several 16-column units, more than the
+    two segments a pass holds, so waves run several passes."""
+    lens = (np.arange(40) * 37 % 60 + 1).tolist()
+    wl = build("multi-short", 63, [("prefill", lens)], 32, 8, 128, "f16", "outlier",
+               shuffle=True)
+    _say(f"multi {fmt_name} many short sequences")
+    _check(P, wl, fmt_name, 4, seed=64)
+
+
 def test_multi_one_token_equals_the_plain_decode(P):
     wl = make_config(3, 0.05)
     pool, _ = gpu_pool(P, wl, P.KV_INT8_SYM)
