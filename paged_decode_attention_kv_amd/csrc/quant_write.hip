@@ -1,11 +1,19 @@
 // Quantize-on-write and 16-bit write into paged KV pools (gfx950).
 //
-// One wave (64 lanes) owns one (token, KV head) pair and handles its K row and
-// its V row; a workgroup holds four waves. Three pool formats: per-token INT8
-// (codes + FP16 scales), static-scale INT8 (codes only) and 16-bit. The row
-// quantizer (quant_row.h) follows MoE-Infinity PR #183 "feat: opt-in INT8
-// KV-cache quantization" ("What landed", format-contract bullet; "Precision &
-// memory") and the zero-token rule of mlxcel PR #717 ("The Int8 bug and fix").
+// One wave (64 lanes) owns about four consecutive tokens of the call for one
+// KV head (a span aligned to the V groups of the pages, below) and handles
+// their K and V rows; a workgroup holds four waves. Three
+// pool formats: per-token INT8 (codes + FP16 scales), static-scale INT8
+// (codes only) and 16-bit. The row quantizer (quant_row.h) follows
+// MoE-Infinity PR #183 "feat: opt-in INT8 KV-cache quantization" ("What
+// landed", format-contract bullet; "Precision & memory") and the zero-token
+// rule of mlxcel PR #717 ("The Int8 bug and fix"). Four tokens that fill one
+// V group of a page are stored with whole group words, so a prefill writes
+// whole cache lines instead of a byte scatter. The INT8 kernels give each
+// token 16 lanes, so the per-row reductions and scale arithmetic of the four
+// tokens run side by side in the same instructions.
+#include <type_traits>
+
 #include "device_util.h"
 #include "launch.h"
 #include "quant_row.h"
@@ -15,188 +23,403 @@ namespace pdakv {
 namespace {
 
 constexpr int kWriteWaves = 4;
+constexpr int kQuad = 4;  // tokens per wave: one V group of the page layout
 
-template <int D>
-struct Int8Head {
-  static constexpr int kBytes = 2 * kBlockSize * D + 4 * kBlockSize;
-  static constexpr int kV = kBlockSize * D;          // V codes
-  static constexpr int kKs = 2 * kBlockSize * D;     // K scales
-  static constexpr int kVs = 2 * kBlockSize * D + 2 * kBlockSize;
+// Head block of a page: element size E (1: INT8 codes, 2: 16-bit values), K
+// rows at pos * D elements, V grouped four tokens at a time from 16 * D
+// elements on (dimension d of tokens 4g .. 4g+3 in one group word), and for
+// per-token INT8 the fp16 K and V scales after the codes.
+template <int D, int E, bool Scales>
+struct HeadLayout {
+  static constexpr int kBytes = 32 * D * E + (Scales ? 64 : 0);
+  static constexpr int kV = kBlockSize * D * E;  // byte offset of the V groups
+  static constexpr int kKs = 32 * D;             // K scales
+  static constexpr int kVs = 32 * D + 32;        // V scales
 };
 
-template <typename T>
-__device__ __forceinline__ uint16_t load_bits(const void* base, int64_t idx) {
-  return static_cast<const uint16_t*>(base)[idx];
+// Tokens are dealt to waves four at a time, with each boundary between the
+// fours moved back to the start of the V group its token lands in: boundary
+// b moves to b - k when token b's slot is 4g + k and tokens b - k .. b - 1
+// hold slots 4g .. 4g + k - 1. Both waves next to a boundary compute the
+// same move, so every token is handled once; inside a run of consecutive
+// slots (a prefill chunk, whatever its start offset in the page) every wave
+// then holds whole V groups. A wave reads the slots of tokens 4q - 4 ..
+// 4q + 7 at once (one per lane), which covers both of its boundaries and its
+// up to seven tokens.
+struct Span {
+  int64_t t0;       // first token
+  int n;            // tokens (1 .. 7)
+  int32_t slot[8];  // their slots (-1: padding or out of range)
+};
+__device__ __forceinline__ Span load_span(const WriteArgs& a, int64_t qd, int lane) {
+  const int64_t base = qd * kQuad - kQuad, T = a.num_tokens;
+  const int64_t cap = a.num_blocks * kBlockSize;
+  // one load per lane, then every lane reads the twelve slots
+  const int64_t tl = base + lane;
+  int32_t mine = a.slots[tl < 0 ? 0 : (tl >= T ? T - 1 : tl)];
+  if (tl < 0 || tl >= T) mine = -1;
+  int32_t S[3 * kQuad];
+#pragma unroll
+  for (int j = 0; j < 3 * kQuad; ++j) S[j] = __builtin_amdgcn_readlane(mine, j);
+  // boundary at token base + c
+  auto bnd = [&](int c) -> int64_t {
+    const int64_t b = base + c;
+    if (b <= 0 || b >= T) return b;
+    const int32_t s = S[c];
+    const int k = s & 3;
+    if (s < 0 || s >= cap || k == 0) return b;
+    bool run = b >= k;
+#pragma unroll
+    for (int j = 1; j < kQuad; ++j) run = run && (j > k || S[c - j] == s - j);
+    return run ? b - k : b;
+  };
+  Span sp;
+  sp.t0 = bnd(kQuad);
+  sp.n = static_cast<int>(min(bnd(2 * kQuad), T) - sp.t0);
+  // token t0 + j is S[off + j], off in 1 .. 4 (selected with constant
+  // indexes: S stays in registers)
+  const int off = static_cast<int>(sp.t0 - base);
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int32_t s = off == 1 ? S[1 + j] : off == 2 ? S[2 + j] : off == 3 ? S[3 + j] : S[4 + j];
+    if (j >= sp.n) s = -1;
+    bad = bad || s >= cap;
+    sp.slot[j] = s >= cap ? -1 : s;
+  }
+  if (bad && lane == 0) raise_flag(a.err, PDAKV_EFLAG_SLOT_RANGE);
+  return sp;
 }
 
-template <int D, bool BF16>
-__global__ __launch_bounds__(64 * kWriteWaves) void quant_write_int8_kernel(WriteArgs a) {
-  constexpr int EPL = D / 64;  // elements per lane
-  using H = Int8Head<D>;
-  const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWriteWaves + (threadIdx.x >> 6);
-  if (row >= a.num_tokens * a.num_kv_heads) return;
-  const int64_t t = row / a.num_kv_heads;
-  const int h = static_cast<int>(row - t * a.num_kv_heads);
-  const int32_t slot = a.slots[t];
-  if (slot < 0) return;  // padding token
-  if (slot >= a.num_blocks * kBlockSize) {
-    if (lane == 0) raise_flag(a.err, PDAKV_EFLAG_SLOT_RANGE);
-    return;
-  }
-  const int64_t blk = slot / kBlockSize;
-  const int pos = slot % kBlockSize;
-  uint8_t* head = a.pool + blk * a.page_bytes + static_cast<int64_t>(h) * H::kBytes;
+// Up to four consecutive tokens t0 .. t0+nt-1 of a wave and their slots.
+struct Quad {
+  int32_t slot[kQuad];
+  int nt;
+};
+template <int Round>
+__device__ __forceinline__ Quad quad_of(const Span& sp) {
+  Quad q;
+  q.nt = min(kQuad, sp.n - kQuad * Round);
+#pragma unroll
+  for (int j = 0; j < kQuad; ++j) q.slot[j] = sp.slot[kQuad * Round + j];
+  return q;
+}
 
+template <int D, int E, bool Scales>
+__device__ __forceinline__ uint8_t* head_of(const WriteArgs& a, int32_t slot, int h) {
+  return a.pool + static_cast<int64_t>(slot / kBlockSize) * a.page_bytes +
+         static_cast<int64_t>(h) * HeadLayout<D, E, Scales>::kBytes;
+}
+
+// Max over the 16 lanes of each row of the wave (DPP rotations inside the
+// row: VALU only); every lane of the row gets it.
+template <int Ror>
+__device__ __forceinline__ float row_rotate(float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 | Ror, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, row_rotate<8>(x));
+  x = fmaxf(x, row_rotate<4>(x));
+  x = fmaxf(x, row_rotate<2>(x));
+  return fmaxf(x, row_rotate<1>(x));
+}
+
+// Quantize-on-write into INT8 pages (Static = false: per-token scales;
+// true: the layer's scales) of the K and V rows of up to four consecutive tokens
+// of the call for one KV head. Lane (r, i) = (lane / 16, lane % 16) holds
+// elements 8i .. 8i+7 (D = 128; 4i .. 4i+3 for D = 64) of token r's rows,
+// so a row's absolute maximum is a 16-lane reduction and the per-row scale
+// work of the four tokens shares instructions. The per-row rules
+// (MoE-Infinity PR #183 "feat: opt-in INT8 KV-cache quantization", "What
+// landed", format-contract bullet; zero rows per mlxcel PR #717 "The Int8
+// bug and fix"; static scales per InfiniLM PR #553 "Summary"):
+//   per-token: a = max|x|; s = 1.0 if a == 0 else the smallest FP16 >=
+//   fl32(a/127); code = clamp(rint(fl32(x / s)), -127, 127);
+//   static: code = clamp(rint(fl32(x / scale)), -127, 127).
+// A token with a negative slot is padding (skipped); an out-of-range slot or
+// a per-token scale beyond FP16 is flagged and that (token, head) is left
+// unwritten. K rows are stored per token (8 or 4 contiguous bytes per lane).
+// When the four tokens are one whole V group, the codes go through LDS to
+// become group words (one dimension of the four tokens) and every lane
+// stores whole words; otherwise each token's V codes are stored byte by byte.
+template <int D, bool Static, bool BF16, bool Vec, class CW>
+__device__ __forceinline__ void quant_quad(const WriteArgs& a, const Quad& q, int64_t t0, int h,
+                                           CW* s_codes, int lane) {
+  constexpr int EPL = D / 16;  // elements per lane
+  using L = HeadLayout<D, 1, !Static>;
+  const int r = lane >> 4, i = lane & 15;
+  const int32_t my_slot = r == 0 ? q.slot[0] : r == 1 ? q.slot[1] : r == 2 ? q.slot[2] : q.slot[3];
+
+  // token r's K and V elements 8i.. (or 4i..); past the call's end the last
+  // token is loaded again
+  const int64_t t = t0 + (r < q.nt ? r : q.nt - 1);
+  uint16_t kb[EPL], vb[EPL];
+  if constexpr (Vec) {
+    using LV = typename std::conditional<EPL == 8, u4_t, u2_t>::type;
+    const LV kl = *reinterpret_cast<const LV*>(static_cast<const uint16_t*>(a.k) + t * a.k_st +
+                                               h * a.k_sh + EPL * i);
+    const LV vl = *reinterpret_cast<const LV*>(static_cast<const uint16_t*>(a.v) + t * a.v_st +
+                                               h * a.v_sh + EPL * i);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      kb[e] = static_cast<uint16_t>(kl[e / 2] >> (16 * (e % 2)));
+      vb[e] = static_cast<uint16_t>(vl[e / 2] >> (16 * (e % 2)));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const int64_t d = EPL * i + e;
+      kb[e] = static_cast<const uint16_t*>(a.k)[t * a.k_st + h * a.k_sh + d * a.k_sd];
+      vb[e] = static_cast<const uint16_t*>(a.v)[t * a.v_st + h * a.v_sh + d * a.v_sd];
+    }
+  }
   float xk[EPL], xv[EPL];
   float ak = 0.f, av = 0.f;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    const int64_t d = lane * EPL + e;
-    xk[e] = bits16_to_f32<BF16>(load_bits<uint16_t>(a.k, t * a.k_st + h * a.k_sh + d * a.k_sd));
-    xv[e] = bits16_to_f32<BF16>(load_bits<uint16_t>(a.v, t * a.v_st + h * a.v_sh + d * a.v_sd));
+    xk[e] = bits16_to_f32<BF16>(kb[e]);
+    xv[e] = bits16_to_f32<BF16>(vb[e]);
     ak = fmaxf(ak, fabsf(xk[e]));
     av = fmaxf(av, fabsf(xv[e]));
   }
-  ak = wave_max(ak);
-  av = wave_max(av);
-
-  uint16_t skb, svb;
-  const bool okk = row_scale(ak, skb), okv = row_scale(av, svb);
-  if (!okk || !okv) {
-    if (lane == 0) raise_flag(a.err, PDAKV_EFLAG_SCALE_RANGE);
-    return;
+  bool ok = my_slot >= 0;
+  float sk = a.k_scale, sv = a.v_scale;
+  uint16_t skb = 0, svb = 0;
+  if constexpr (!Static) {
+    ak = row_max(ak);
+    av = row_max(av);
+    const bool okk = row_scale(ak, skb), okv = row_scale(av, svb);
+    if (ok && !(okk && okv)) {
+      if (i == 0) raise_flag(a.err, PDAKV_EFLAG_SCALE_RANGE);
+      ok = false;
+    }
+    sk = f16_bits_to_f32(skb);
+    sv = f16_bits_to_f32(svb);
   }
-  const float sk = f16_bits_to_f32(skb);
-  const float sv = f16_bits_to_f32(svb);
-
-  uint8_t ck[EPL], cv[EPL];
+  CW kc = 0, vc = 0;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    ck[e] = row_code(xk[e], sk);
-    cv[e] = row_code(xv[e], sv);
+    kc |= static_cast<CW>(row_code(xk[e], sk)) << (8 * e);
+    vc |= static_cast<CW>(row_code(xv[e], sv)) << (8 * e);
   }
-  // K: token-major row; V: dimension d of tokens grouped by four.
+  // tokens stored (uniform over the wave)
+  const uint64_t stored = __ballot(ok);
+  const bool whole = q.nt == kQuad && stored == ~0ull && q.slot[0] % 4 == 0 &&
+                     q.slot[1] == q.slot[0] + 1 && q.slot[2] == q.slot[0] + 2 &&
+                     q.slot[3] == q.slot[0] + 3;
+  const int pos = my_slot % kBlockSize;
+  uint8_t* head = head_of<D, 1, !Static>(a, ok ? my_slot : 0, h);
+  if (ok) {
+    *reinterpret_cast<CW*>(head + pos * D + EPL * i) = kc;
+    if constexpr (!Static) {
+      if (i == 0) {
+        *reinterpret_cast<uint16_t*>(head + L::kKs + 2 * pos) = skb;
+        *reinterpret_cast<uint16_t*>(head + L::kVs + 2 * pos) = svb;
+      }
+    }
+  }
+  if (whole) {
+    // lane (r, i) builds the group words of dimensions EPL*i + (EPL/4)*r ..,
+    // (EPL/4 of them: one byte of each token per word)
+    s_codes[lane] = vc;
+    __builtin_amdgcn_wave_barrier();
+    const uint8_t* cb = reinterpret_cast<const uint8_t*>(s_codes);
+    constexpr int WPL = EPL / 4;  // group words per lane
+    uint32_t gw[WPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const int d = lane * EPL + e;
-    head[pos * D + d] = ck[e];
-    head[H::kV + (pos >> 2) * 4 * D + d * 4 + (pos & 3)] = cv[e];
-  }
-  if (lane == 0) {
-    *reinterpret_cast<uint16_t*>(head + H::kKs + 2 * pos) = skb;
-    *reinterpret_cast<uint16_t*>(head + H::kVs + 2 * pos) = svb;
+    for (int k = 0; k < WPL; ++k) {
+      const int e = WPL * r + k;  // element of the lanes i of every token
+      gw[k] = 0;
+#pragma unroll
+      for (int j = 0; j < kQuad; ++j)
+        gw[k] |= static_cast<uint32_t>(cb[(16 * j + i) * sizeof(CW) + e]) << (8 * j);
+    }
+    uint8_t* vg = head + L::kV + (pos / 4) * 4 * D + 4 * (EPL * i + WPL * r);
+    if constexpr (WPL == 2)
+      *reinterpret_cast<uint64_t*>(vg) = gw[0] | (static_cast<uint64_t>(gw[1]) << 32);
+    else
+      *reinterpret_cast<uint32_t*>(vg) = gw[0];
+  } else if (ok) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      head[L::kV + (pos / 4) * 4 * D + 4 * (EPL * i + e) + pos % 4] =
+          static_cast<uint8_t>(vc >> (8 * e));
   }
 }
 
-// Static scales (InfiniLM PR #553 "Summary"; TensorRT-LLM PR #18953
-// "Summary"): the layer's K scale and V scale are given, so a row needs no
-// reduction: code = clamp(rint(fl32(x / scale)), -127, 127), stored into a
-// codes-only head block (K codes, then V codes grouped by four tokens).
-template <int D, bool BF16>
-__global__ __launch_bounds__(64 * kWriteWaves) void quant_write_static_kernel(WriteArgs a) {
-  constexpr int EPL = D / 64;
+// One wave per four tokens of the call (boundaries moved to V groups) and
+// KV head; a span that crosses runs of slots takes two rounds.
+template <int D, bool Static, bool BF16, bool Vec>
+__global__ __launch_bounds__(64 * kWriteWaves) void quant_write_kernel(WriteArgs a) {
+  constexpr int EPL = D / 16;  // elements per lane
+  using CW = typename std::conditional<EPL == 8, uint64_t, uint32_t>::type;  // a lane's codes
+  __shared__ CW s_codes[kWriteWaves][kQuad * 16];  // V codes of the quad, [token][lane]
   const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWriteWaves + (threadIdx.x >> 6);
-  if (row >= a.num_tokens * a.num_kv_heads) return;
-  const int64_t t = row / a.num_kv_heads;
-  const int h = static_cast<int>(row - t * a.num_kv_heads);
-  const int32_t slot = a.slots[t];
-  if (slot < 0) return;
-  if (slot >= a.num_blocks * kBlockSize) {
-    if (lane == 0) raise_flag(a.err, PDAKV_EFLAG_SLOT_RANGE);
-    return;
-  }
-  const int64_t blk = slot / kBlockSize;
-  const int pos = slot % kBlockSize;
-  uint8_t* head = a.pool + blk * a.page_bytes + static_cast<int64_t>(h) * 2 * kBlockSize * D;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // (wave-uniform, so the slots are scalar loads)
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWriteWaves + wv;
+  const int64_t quads = (a.num_tokens + kQuad - 1) / kQuad;
+  if (w >= quads * a.num_kv_heads) return;
+  const int64_t qd = w / a.num_kv_heads;
+  const int h = static_cast<int>(w - qd * a.num_kv_heads);
+  const Span sp = load_span(a, qd, lane);
+  quant_quad<D, Static, BF16, Vec>(a, quad_of<0>(sp), sp.t0, h, s_codes[wv], lane);
+  if (sp.n > kQuad)  // a span across two runs of slots
+    quant_quad<D, Static, BF16, Vec>(a, quad_of<1>(sp), sp.t0 + kQuad, h, s_codes[wv], lane);
+}
+
+// Plain 16-bit write (the control pool) of up to four consecutive tokens of
+// one KV head, lane l holding elements l * EPL .. of every row; four tokens
+// that are one whole V group are stored with whole group words.
+template <int D, bool Vec>
+__device__ __forceinline__ void write_16bit_quad(const WriteArgs& a, const Quad& q, int64_t t0,
+                                                 int h, int lane) {
+  constexpr int EPL = D / 64;  // elements per lane and row
+  using L = HeadLayout<D, 2, false>;
+  uint16_t kb[kQuad][EPL], vb[kQuad][EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const int d = lane * EPL + e;
-    const float xk =
-        bits16_to_f32<BF16>(load_bits<uint16_t>(a.k, t * a.k_st + h * a.k_sh + d * a.k_sd));
-    const float xv =
-        bits16_to_f32<BF16>(load_bits<uint16_t>(a.v, t * a.v_st + h * a.v_sh + d * a.v_sd));
-    head[pos * D + d] = row_code(xk, a.k_scale);
-    head[kBlockSize * D + (pos >> 2) * 4 * D + d * 4 + (pos & 3)] = row_code(xv, a.v_scale);
+  for (int j = 0; j < kQuad; ++j) {
+    const int64_t t = t0 + (j < q.nt ? j : q.nt - 1);
+    if constexpr (Vec && EPL == 2) {
+      const uint32_t kw = *reinterpret_cast<const uint32_t*>(
+          static_cast<const uint16_t*>(a.k) + t * a.k_st + h * a.k_sh + 2 * lane);
+      const uint32_t vw = *reinterpret_cast<const uint32_t*>(
+          static_cast<const uint16_t*>(a.v) + t * a.v_st + h * a.v_sh + 2 * lane);
+      kb[j][0] = static_cast<uint16_t>(kw);
+      kb[j][1] = static_cast<uint16_t>(kw >> 16);
+      vb[j][0] = static_cast<uint16_t>(vw);
+      vb[j][1] = static_cast<uint16_t>(vw >> 16);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int64_t d = lane * EPL + e;
+        kb[j][e] = static_cast<const uint16_t*>(a.k)[t * a.k_st + h * a.k_sh + d * a.k_sd];
+        vb[j][e] = static_cast<const uint16_t*>(a.v)[t * a.v_st + h * a.v_sh + d * a.v_sd];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kQuad; ++j) {
+    if (q.slot[j] < 0) continue;
+    uint8_t* head = head_of<D, 2, false>(a, q.slot[j], h);
+    const int pos = q.slot[j] % kBlockSize;
+    uint32_t kw = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) kw |= static_cast<uint32_t>(kb[j][e]) << (16 * e);
+    if constexpr (EPL == 2)
+      *reinterpret_cast<uint32_t*>(head + (pos * D + 2 * lane) * 2) = kw;
+    else
+      *reinterpret_cast<uint16_t*>(head + (pos * D + lane) * 2) = static_cast<uint16_t>(kw);
+  }
+  const bool whole = q.nt == kQuad && q.slot[0] >= 0 && q.slot[0] % 4 == 0 &&
+                     q.slot[1] == q.slot[0] + 1 && q.slot[2] == q.slot[0] + 2 &&
+                     q.slot[3] == q.slot[0] + 3;
+  if (whole) {
+    uint8_t* head = head_of<D, 2, false>(a, q.slot[0], h);
+    uint8_t* vg = head + L::kV + (q.slot[0] % kBlockSize / 4) * 4 * D * 2 + lane * EPL * 8;
+    uint64_t gw[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      gw[e] = 0;
+#pragma unroll
+      for (int j = 0; j < kQuad; ++j) gw[e] |= static_cast<uint64_t>(vb[j][e]) << (16 * j);
+    }
+    if constexpr (EPL == 2)
+      *reinterpret_cast<u4_t*>(vg) = u4_t{static_cast<uint32_t>(gw[0]),
+                                          static_cast<uint32_t>(gw[0] >> 32),
+                                          static_cast<uint32_t>(gw[1]),
+                                          static_cast<uint32_t>(gw[1] >> 32)};
+    else
+      *reinterpret_cast<uint64_t*>(vg) = gw[0];
+  } else {
+#pragma unroll
+    for (int j = 0; j < kQuad; ++j) {
+      if (q.slot[j] < 0) continue;
+      uint8_t* head = head_of<D, 2, false>(a, q.slot[j], h);
+      const int pos = q.slot[j] % kBlockSize;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const int d = lane * EPL + e;
+        *reinterpret_cast<uint16_t*>(head + L::kV + ((pos / 4) * 4 * D + 4 * d + pos % 4) * 2) =
+            vb[j][e];
+      }
+    }
   }
 }
 
-template <int D>
+template <int D, bool Vec>
 __global__ __launch_bounds__(64 * kWriteWaves) void write_16bit_kernel(WriteArgs a) {
-  constexpr int EPL = D / 64;
-  constexpr int kHeadElems = 2 * kBlockSize * D;
   const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWriteWaves + (threadIdx.x >> 6);
-  if (row >= a.num_tokens * a.num_kv_heads) return;
-  const int64_t t = row / a.num_kv_heads;
-  const int h = static_cast<int>(row - t * a.num_kv_heads);
-  const int32_t slot = a.slots[t];
-  if (slot < 0) return;
-  if (slot >= a.num_blocks * kBlockSize) {
-    if (lane == 0) raise_flag(a.err, PDAKV_EFLAG_SLOT_RANGE);
-    return;
-  }
-  const int64_t blk = slot / kBlockSize;
-  const int pos = slot % kBlockSize;
-  uint16_t* head = reinterpret_cast<uint16_t*>(a.pool + blk * a.page_bytes) +
-                   static_cast<int64_t>(h) * kHeadElems;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const int d = lane * EPL + e;
-    head[pos * D + d] = load_bits<uint16_t>(a.k, t * a.k_st + h * a.k_sh + d * a.k_sd);
-    head[kBlockSize * D + (pos >> 2) * 4 * D + d * 4 + (pos & 3)] =
-        load_bits<uint16_t>(a.v, t * a.v_st + h * a.v_sh + d * a.v_sd);
-  }
+  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWriteWaves +
+                    __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t quads = (a.num_tokens + kQuad - 1) / kQuad;
+  if (w >= quads * a.num_kv_heads) return;
+  const int64_t qd = w / a.num_kv_heads;
+  const int h = static_cast<int>(w - qd * a.num_kv_heads);
+  const Span sp = load_span(a, qd, lane);
+  write_16bit_quad<D, Vec>(a, quad_of<0>(sp), sp.t0, h, lane);
+  if (sp.n > kQuad) write_16bit_quad<D, Vec>(a, quad_of<1>(sp), sp.t0 + kQuad, h, lane);
 }
 
 unsigned write_grid(const WriteArgs& a) {
-  const int64_t rows = a.num_tokens * a.num_kv_heads;
-  return static_cast<unsigned>((rows + kWriteWaves - 1) / kWriteWaves);
+  const int64_t waves = (a.num_tokens + kQuad - 1) / kQuad * a.num_kv_heads;
+  return static_cast<unsigned>((waves + kWriteWaves - 1) / kWriteWaves);
+}
+
+// Whole-row vector loads: unit element stride, every row start aligned to
+// `bytes`
+bool vec_rows(const WriteArgs& a, int bytes) {
+  const int64_t el = bytes / 2;
+  auto al = [el](int64_t x) { return x % el == 0; };
+  return a.k_sd == 1 && a.v_sd == 1 && al(a.k_st) && al(a.k_sh) && al(a.v_st) && al(a.v_sh) &&
+         (reinterpret_cast<uintptr_t>(a.k) % bytes) == 0 &&
+         (reinterpret_cast<uintptr_t>(a.v) % bytes) == 0;
+}
+
+template <bool Static, bool BF16>
+hipError_t launch_quant(const WriteArgs& a, int head_dim, hipStream_t s) {
+  const dim3 grid(write_grid(a)), block(64 * kWriteWaves);
+  // lanes load 16 (D = 128) or 8 (D = 64) bytes of a row
+  const bool vec = vec_rows(a, head_dim / 8);
+  if (head_dim == 128) {
+    if (vec)
+      hipLaunchKernelGGL((quant_write_kernel<128, Static, BF16, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((quant_write_kernel<128, Static, BF16, false>), grid, block, 0, s, a);
+  } else {
+    if (vec)
+      hipLaunchKernelGGL((quant_write_kernel<64, Static, BF16, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((quant_write_kernel<64, Static, BF16, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_quant_write_int8(const WriteArgs& a, int head_dim, bool src_bf16,
                                    hipStream_t s) {
-  const dim3 grid(write_grid(a)), block(64 * kWriteWaves);
-  if (head_dim == 128) {
-    if (src_bf16)
-      hipLaunchKernelGGL((quant_write_int8_kernel<128, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((quant_write_int8_kernel<128, false>), grid, block, 0, s, a);
-  } else {
-    if (src_bf16)
-      hipLaunchKernelGGL((quant_write_int8_kernel<64, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((quant_write_int8_kernel<64, false>), grid, block, 0, s, a);
-  }
-  return hipGetLastError();
+  return src_bf16 ? launch_quant<false, true>(a, head_dim, s)
+                  : launch_quant<false, false>(a, head_dim, s);
 }
 
 hipError_t launch_quant_write_static(const WriteArgs& a, int head_dim, bool src_bf16,
                                      hipStream_t s) {
-  const dim3 grid(write_grid(a)), block(64 * kWriteWaves);
-  if (head_dim == 128) {
-    if (src_bf16)
-      hipLaunchKernelGGL((quant_write_static_kernel<128, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((quant_write_static_kernel<128, false>), grid, block, 0, s, a);
-  } else {
-    if (src_bf16)
-      hipLaunchKernelGGL((quant_write_static_kernel<64, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((quant_write_static_kernel<64, false>), grid, block, 0, s, a);
-  }
-  return hipGetLastError();
+  return src_bf16 ? launch_quant<true, true>(a, head_dim, s)
+                  : launch_quant<true, false>(a, head_dim, s);
 }
 
 hipError_t launch_write_16bit(const WriteArgs& a, int head_dim, hipStream_t s) {
   const dim3 grid(write_grid(a)), block(64 * kWriteWaves);
-  if (head_dim == 128)
-    hipLaunchKernelGGL((write_16bit_kernel<128>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((write_16bit_kernel<64>), grid, block, 0, s, a);
+  if (head_dim == 128) {
+    if (vec_rows(a, 4))
+      hipLaunchKernelGGL((write_16bit_kernel<128, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((write_16bit_kernel<128, false>), grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((write_16bit_kernel<64, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError();
 }
 

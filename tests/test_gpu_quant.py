@@ -135,3 +135,63 @@ def test_full_size_write_sampled(P, idx):
             assert np.array_equal(kc[:, 0], wkc) and np.array_equal(vc[:, 0], wvc)
             assert np.array_equal(ks[:, 0].view(np.uint16), wks.view(np.uint16))
             assert np.array_equal(vs[:, 0].view(np.uint16), wvs.view(np.uint16))
+
+
+def _mixed_slots(rng, num_blocks):
+    """Runs of consecutive slots (lengths 1..23, any start offset inside a
+    page, one of them reversed) in disjoint ranges, with padding and
+    out-of-range entries sprinkled in: every way the writer's four-token
+    spans can meet a V group."""
+    starts = rng.permutation(num_blocks * 16 // 32)[:18] * 32
+    runs = []
+    for j, st in enumerate(starts):
+        n = int(rng.integers(1, 24))
+        run = st + int(rng.integers(0, 8)) + np.arange(n)
+        runs.append(run[::-1] if j == 5 else run)
+    slots = np.concatenate(runs)
+    slots[rng.random(len(slots)) < 0.06] = -1
+    slots[rng.random(len(slots)) < 0.03] = num_blocks * 16 + 3
+    return slots.astype(np.int32)
+
+
+@pytest.mark.parametrize("kind", ["int8", "static", "16bit"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_write_spans_mixed_runs(P, kind, d):
+    """Slot runs of every length and page offset, reversed runs, padding and
+    out-of-range slots, token count not a multiple of four: the whole pool
+    equals the oracle's writes of the tokens with valid slots."""
+    rng = np.random.default_rng(30 + d)
+    nb, hkv = 64, 2
+    slots = _mixed_slots(rng, nb)
+    T = len(slots)
+    k = torch.from_numpy(rng.standard_normal((T, hkv, d)).astype(np.float32)).half()
+    v = torch.from_numpy(rng.standard_normal((T, hkv, d)).astype(np.float32) * 3).half()
+    k[1] = 0.0  # an all-zero token
+    keep = (slots >= 0) & (slots < nb * 16)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fmt = {"int8": P.KV_INT8_SYM, "static": P.KV_INT8_STATIC, "16bit": P.KV_16BIT}[kind]
+    ofmt = {"int8": oracle.KV_INT8_SYM, "static": oracle.KV_INT8_STATIC,
+            "16bit": oracle.KV_16BIT}[kind]
+    pool = torch.full((nb, P.pdakv_page_bytes(fmt, 16, hkv, d)), FILL, dtype=torch.uint8,
+                      device="cuda")
+    want = oracle.new_pool(ofmt, nb, 16, hkv, d, fill=FILL)
+    ks, vs = 0.03, 0.07
+    _say(f"mixed runs {kind} D={d}: {T} tokens")
+    if kind == "int8":
+        P.kv_quant_int8_sym_write(k.cuda(), v.cuda(), dev_i32(slots), pool, nb, err_flag=err)
+        kc, kss = oracle.quantize_rows(k[keep])
+        vc, vss = oracle.quantize_rows(v[keep])
+        oracle.write_int8_tokens(want, kc, kss, vc, vss, slots[keep], 16)
+    elif kind == "static":
+        P.kv_quant_int8_static_write(k.cuda(), v.cuda(), dev_i32(slots), pool, nb, ks, vs,
+                                     err_flag=err)
+        oracle.write_int8_static_tokens(want, oracle.quantize_static(k[keep], ks),
+                                        oracle.quantize_static(v[keep], vs), slots[keep], 16)
+    else:
+        P.kv_write_16bit(k.cuda(), v.cuda(), dev_i32(slots), pool, nb, err_flag=err)
+        oracle.write_16bit_tokens(want, bits16(k[keep]), bits16(v[keep]), slots[keep], 16)
+    torch.cuda.synchronize()
+    assert int(err.item()) == P.EFLAG_SLOT_RANGE
+    got = pool.cpu().numpy()
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, f"{bad[0].size} bytes differ, first at page {bad[0][0]} byte {bad[1][0]}"
