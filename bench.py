@@ -104,6 +104,14 @@ def append_bytes(wl, fmt: str) -> int:
     return wl.num_seqs * wl.num_kv_heads * (4 * d + written)
 
 
+def write_bytes(wl, fmt: str) -> int:
+    """Algorithmic bytes of writing one token: its 16-bit K and V rows read,
+    codes (+ scales) or 16-bit values written, and its slot."""
+    d = wl.head_dim
+    written = {"int8": 2 * d + 4, "static": 2 * d, "fp16": 4 * d}[fmt]
+    return wl.num_kv_heads * (4 * d + written) + 4
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -310,19 +318,21 @@ def main():
             torch.cuda.empty_cache()
         multi["int8_over_fp16"] = round(multi["fp16"]["call_us"] / multi["int8"]["call_us"], 3)
 
+    def timed(fn, reps):
+        """Seconds per call of fn, from HIP events on the launch stream."""
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e-3
+
     # ---- page lifecycle: swap-out / swap-in and the sink-keeping trim -----------
     lifecycle = None
     if not args.no_points:
-        def timed(fn, reps):
-            fn()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(reps):
-                fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / reps * 1e-3  # seconds per call
         st = setup(wl, "int8", None)
         pool = st["pools"][0]
         pb = pool.shape[1]
@@ -378,6 +388,37 @@ def main():
         del st, host_buf
         torch.cuda.empty_cache()
 
+    # ---- bulk quantize-on-write: the small-head chunk and the batched prefill -
+    # the 32 x 4,096-token chunk of the small-head configuration (strided bf16
+    # views of a fused QKV buffer, chunk starting at page offset 7), and the
+    # 296K-token prefill of the batched step's pool
+    writes = None
+    if not args.no_points:
+        writes = {}
+        for wname, wwl, phase in (("chunk_b32x4096_gqa7_d64", make_config(5), "chunk"),
+                                  ("prefill_" + wl.name, wl, "prefill")):
+            ph = wwl.phase(phase)
+            k, v, sl = to_dev(ph.k), to_dev(ph.v), dev_i32(ph.slot_mapping)
+            ntok = int(ph.k.shape[0])
+            entry = {"tokens": ntok, "kv_heads": wwl.num_kv_heads, "head_dim": wwl.head_dim}
+            wstatic = static_scales(wwl)
+            for key, fmt, fn in (
+                    ("int8", P.KV_INT8_SYM, P.kv_quant_int8_sym_write),
+                    ("static", P.KV_INT8_STATIC,
+                     lambda *x, **kw: P.kv_quant_int8_static_write(*x, *wstatic, **kw)),
+                    ("fp16", P.KV_16BIT, P.kv_write_16bit)):
+                pb = P.pdakv_page_bytes(fmt, 16, wwl.num_kv_heads, wwl.head_dim)
+                wpool = torch.empty((wwl.num_blocks, pb), dtype=torch.uint8, device="cuda")
+                reps = 50 if ntok < 200000 else 10
+                t_w = timed(lambda: fn(k, v, sl, wpool, wwl.num_blocks, stream=stream), reps)
+                wb = ntok * write_bytes(wwl, key)
+                entry[key] = {"us": round(t_w * 1e6, 2), "gbs": round(wb / t_w / 1e9, 1),
+                              "hbm_frac": round(wb / t_w / 1e9 / HBM_PEAK_GBS, 4)}
+                del wpool
+            writes[wname] = entry
+            del k, v, sl
+            torch.cuda.empty_cache()
+
     # ---- CPU baseline: the oracle on a bounded sample ------------------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -417,6 +458,7 @@ def main():
         "unfused_step": unfused,
         "multi_token": multi,
         "lifecycle": lifecycle,
+        "bulk_write": writes,
         "points": points,
         "cpu_baseline": cpu,
     }
