@@ -9,9 +9,10 @@
 // landed", format-contract bullet; "Precision & memory") and the zero-token
 // rule of mlxcel PR #717 ("The Int8 bug and fix"). Four tokens that fill one
 // V group of a page are stored with whole group words, so a prefill writes
-// whole cache lines instead of a byte scatter. The INT8 kernels give each
-// token 16 lanes, so the per-row reductions and scale arithmetic of the four
-// tokens run side by side in the same instructions.
+// whole cache lines instead of a byte scatter. The INT8 kernels give every
+// lane 8 elements of one row (D = 64: two KV heads per wave), so the per-row
+// reductions and scale arithmetic of all the wave's rows run side by side in
+// the same instructions.
 #include <type_traits>
 
 #include "device_util.h"
@@ -111,26 +112,36 @@ __device__ __forceinline__ uint8_t* head_of(const WriteArgs& a, int32_t slot, in
          static_cast<int64_t>(h) * HeadLayout<D, E, Scales>::kBytes;
 }
 
-// Max over the 16 lanes of each row of the wave (DPP rotations inside the
-// row: VALU only); every lane of the row gets it.
-template <int Ror>
-__device__ __forceinline__ float row_rotate(float x) {
+// Max over each group of LPT lanes (16: DPP rotations inside a 16-lane row;
+// 8: swaps inside quads, then the mirror inside each half row); VALU only,
+// and every lane of the group gets it.
+template <int Ctrl>
+__device__ __forceinline__ float dpp(float x) {
   return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 | Ror, 0xF, 0xF, false));
+      __builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float row_max(float x) {
-  x = fmaxf(x, row_rotate<8>(x));
-  x = fmaxf(x, row_rotate<4>(x));
-  x = fmaxf(x, row_rotate<2>(x));
-  return fmaxf(x, row_rotate<1>(x));
+template <int LPT>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (LPT == 16) {
+    x = fmaxf(x, dpp<0x128>(x));  // row_ror:8
+    x = fmaxf(x, dpp<0x124>(x));  // row_ror:4
+    x = fmaxf(x, dpp<0x122>(x));  // row_ror:2
+    return fmaxf(x, dpp<0x121>(x));  // row_ror:1
+  } else {
+    static_assert(LPT == 8, "8 or 16 lanes per token");
+    x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1, 0, 3, 2]
+    x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+    return fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+  }
 }
 
 // Quantize-on-write into INT8 pages (Static = false: per-token scales;
-// true: the layer's scales) of the K and V rows of up to four consecutive tokens
-// of the call for one KV head. Lane (r, i) = (lane / 16, lane % 16) holds
-// elements 8i .. 8i+7 (D = 128; 4i .. 4i+3 for D = 64) of token r's rows,
-// so a row's absolute maximum is a 16-lane reduction and the per-row scale
-// work of the four tokens shares instructions. The per-row rules
+// true: the layer's scales) of the K and V rows of up to four consecutive
+// tokens of the call, for HPW = 128 / D KV heads at once. Every lane holds 8
+// elements of one row: lane (head hh, token r, i) holds elements 8i .. 8i+7
+// of token r's rows of KV head h0 + hh (LPT = D / 8 lanes per token), so a
+// row's absolute maximum is an LPT-lane reduction and the per-row scale work
+// of all the wave's rows shares instructions. The per-row rules
 // (MoE-Infinity PR #183 "feat: opt-in INT8 KV-cache quantization", "What
 // landed", format-contract bullet; zero rows per mlxcel PR #717 "The Int8
 // bug and fix"; static scales per InfiniLM PR #553 "Summary"):
@@ -139,28 +150,33 @@ __device__ __forceinline__ float row_max(float x) {
 //   static: code = clamp(rint(fl32(x / scale)), -127, 127).
 // A token with a negative slot is padding (skipped); an out-of-range slot or
 // a per-token scale beyond FP16 is flagged and that (token, head) is left
-// unwritten. K rows are stored per token (8 or 4 contiguous bytes per lane).
-// When the four tokens are one whole V group, the codes go through LDS to
-// become group words (one dimension of the four tokens) and every lane
-// stores whole words; otherwise each token's V codes are stored byte by byte.
-template <int D, bool Static, bool BF16, bool Vec, class CW>
-__device__ __forceinline__ void quant_quad(const WriteArgs& a, const Quad& q, int64_t t0, int h,
-                                           CW* s_codes, int lane) {
-  constexpr int EPL = D / 16;  // elements per lane
+// unwritten. K rows are stored per token (8 contiguous bytes per lane).
+// When the four tokens are one whole V group of a head, the codes go through
+// LDS to become group words (one dimension of the four tokens) and every
+// lane stores two whole words; otherwise each token's V codes are stored
+// byte by byte.
+template <int D, bool Static, bool BF16, bool Vec>
+__device__ __forceinline__ void quant_quad(const WriteArgs& a, const Quad& q, int64_t t0, int h0,
+                                           uint64_t* s_codes, int lane) {
+  constexpr int EPL = 8;              // elements per lane
+  constexpr int LPT = D / EPL;        // lanes per token row
+  constexpr int LPH = kQuad * LPT;    // lanes per head
   using L = HeadLayout<D, 1, !Static>;
-  const int r = lane >> 4, i = lane & 15;
+  const int hh = lane / LPH, r = lane % LPH / LPT, i = lane % LPT;
+  const int h = h0 + hh;
+  const bool hvalid = h < a.num_kv_heads;
+  const int hl = hvalid ? h : a.num_kv_heads - 1;  // head whose rows are loaded
   const int32_t my_slot = r == 0 ? q.slot[0] : r == 1 ? q.slot[1] : r == 2 ? q.slot[2] : q.slot[3];
 
-  // token r's K and V elements 8i.. (or 4i..); past the call's end the last
-  // token is loaded again
+  // token r's K and V elements 8i ..; past the call's end the last token is
+  // loaded again
   const int64_t t = t0 + (r < q.nt ? r : q.nt - 1);
   uint16_t kb[EPL], vb[EPL];
   if constexpr (Vec) {
-    using LV = typename std::conditional<EPL == 8, u4_t, u2_t>::type;
-    const LV kl = *reinterpret_cast<const LV*>(static_cast<const uint16_t*>(a.k) + t * a.k_st +
-                                               h * a.k_sh + EPL * i);
-    const LV vl = *reinterpret_cast<const LV*>(static_cast<const uint16_t*>(a.v) + t * a.v_st +
-                                               h * a.v_sh + EPL * i);
+    const u4_t kl = *reinterpret_cast<const u4_t*>(static_cast<const uint16_t*>(a.k) +
+                                                   t * a.k_st + hl * a.k_sh + EPL * i);
+    const u4_t vl = *reinterpret_cast<const u4_t*>(static_cast<const uint16_t*>(a.v) +
+                                                   t * a.v_st + hl * a.v_sh + EPL * i);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       kb[e] = static_cast<uint16_t>(kl[e / 2] >> (16 * (e % 2)));
@@ -170,8 +186,8 @@ __device__ __forceinline__ void quant_quad(const WriteArgs& a, const Quad& q, in
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const int64_t d = EPL * i + e;
-      kb[e] = static_cast<const uint16_t*>(a.k)[t * a.k_st + h * a.k_sh + d * a.k_sd];
-      vb[e] = static_cast<const uint16_t*>(a.v)[t * a.v_st + h * a.v_sh + d * a.v_sd];
+      kb[e] = static_cast<const uint16_t*>(a.k)[t * a.k_st + hl * a.k_sh + d * a.k_sd];
+      vb[e] = static_cast<const uint16_t*>(a.v)[t * a.v_st + hl * a.v_sh + d * a.v_sd];
     }
   }
   float xk[EPL], xv[EPL];
@@ -183,12 +199,12 @@ __device__ __forceinline__ void quant_quad(const WriteArgs& a, const Quad& q, in
     ak = fmaxf(ak, fabsf(xk[e]));
     av = fmaxf(av, fabsf(xv[e]));
   }
-  bool ok = my_slot >= 0;
+  bool ok = my_slot >= 0 && hvalid;
   float sk = a.k_scale, sv = a.v_scale;
   uint16_t skb = 0, svb = 0;
   if constexpr (!Static) {
-    ak = row_max(ak);
-    av = row_max(av);
+    ak = group_max<LPT>(ak);
+    av = group_max<LPT>(av);
     const bool okk = row_scale(ak, skb), okv = row_scale(av, svb);
     if (ok && !(okk && okv)) {
       if (i == 0) raise_flag(a.err, PDAKV_EFLAG_SCALE_RANGE);
@@ -197,21 +213,23 @@ __device__ __forceinline__ void quant_quad(const WriteArgs& a, const Quad& q, in
     sk = f16_bits_to_f32(skb);
     sv = f16_bits_to_f32(svb);
   }
-  CW kc = 0, vc = 0;
+  uint64_t kc = 0, vc = 0;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    kc |= static_cast<CW>(row_code(xk[e], sk)) << (8 * e);
-    vc |= static_cast<CW>(row_code(xv[e], sv)) << (8 * e);
+    kc |= static_cast<uint64_t>(row_code(xk[e], sk)) << (8 * e);
+    vc |= static_cast<uint64_t>(row_code(xv[e], sv)) << (8 * e);
   }
-  // tokens stored (uniform over the wave)
+  // whole V group of this lane's head: all four tokens stored (uniform over
+  // the head's lanes)
   const uint64_t stored = __ballot(ok);
-  const bool whole = q.nt == kQuad && stored == ~0ull && q.slot[0] % 4 == 0 &&
-                     q.slot[1] == q.slot[0] + 1 && q.slot[2] == q.slot[0] + 2 &&
-                     q.slot[3] == q.slot[0] + 3;
+  const uint64_t head_lanes = LPH == 64 ? ~0ull : ((1ull << LPH) - 1) << (LPH * hh);
+  const bool whole = q.nt == kQuad && (stored & head_lanes) == head_lanes &&
+                     q.slot[0] % 4 == 0 && q.slot[1] == q.slot[0] + 1 &&
+                     q.slot[2] == q.slot[0] + 2 && q.slot[3] == q.slot[0] + 3;
   const int pos = my_slot % kBlockSize;
-  uint8_t* head = head_of<D, 1, !Static>(a, ok ? my_slot : 0, h);
+  uint8_t* head = head_of<D, 1, !Static>(a, ok ? my_slot : 0, ok ? h : 0);
   if (ok) {
-    *reinterpret_cast<CW*>(head + pos * D + EPL * i) = kc;
+    *reinterpret_cast<uint64_t*>(head + pos * D + EPL * i) = kc;
     if constexpr (!Static) {
       if (i == 0) {
         *reinterpret_cast<uint16_t*>(head + L::kKs + 2 * pos) = skb;
@@ -219,27 +237,23 @@ __device__ __forceinline__ void quant_quad(const WriteArgs& a, const Quad& q, in
       }
     }
   }
+  // (every lane passes the LDS exchange, so that the wave stays together)
+  s_codes[lane] = vc;
+  __builtin_amdgcn_wave_barrier();
   if (whole) {
-    // lane (r, i) builds the group words of dimensions EPL*i + (EPL/4)*r ..,
-    // (EPL/4 of them: one byte of each token per word)
-    s_codes[lane] = vc;
-    __builtin_amdgcn_wave_barrier();
+    // lane (hh, r, i) builds the group words of dimensions 8i + 2r and
+    // 8i + 2r + 1 of its head (one byte of each token per word)
     const uint8_t* cb = reinterpret_cast<const uint8_t*>(s_codes);
-    constexpr int WPL = EPL / 4;  // group words per lane
-    uint32_t gw[WPL];
+    uint32_t gw[2];
 #pragma unroll
-    for (int k = 0; k < WPL; ++k) {
-      const int e = WPL * r + k;  // element of the lanes i of every token
+    for (int k = 0; k < 2; ++k) {
       gw[k] = 0;
 #pragma unroll
       for (int j = 0; j < kQuad; ++j)
-        gw[k] |= static_cast<uint32_t>(cb[(16 * j + i) * sizeof(CW) + e]) << (8 * j);
+        gw[k] |= static_cast<uint32_t>(cb[(LPH * hh + LPT * j + i) * 8 + 2 * r + k]) << (8 * j);
     }
-    uint8_t* vg = head + L::kV + (pos / 4) * 4 * D + 4 * (EPL * i + WPL * r);
-    if constexpr (WPL == 2)
-      *reinterpret_cast<uint64_t*>(vg) = gw[0] | (static_cast<uint64_t>(gw[1]) << 32);
-    else
-      *reinterpret_cast<uint32_t*>(vg) = gw[0];
+    *reinterpret_cast<uint64_t*>(head + L::kV + (pos / 4) * 4 * D + 4 * (EPL * i + 2 * r)) =
+        gw[0] | (static_cast<uint64_t>(gw[1]) << 32);
   } else if (ok) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e)
@@ -249,24 +263,24 @@ __device__ __forceinline__ void quant_quad(const WriteArgs& a, const Quad& q, in
 }
 
 // One wave per four tokens of the call (boundaries moved to V groups) and
-// KV head; a span that crosses runs of slots takes two rounds.
+// 128 / D KV heads; a span that crosses runs of slots takes two rounds.
 template <int D, bool Static, bool BF16, bool Vec>
 __global__ __launch_bounds__(64 * kWriteWaves) void quant_write_kernel(WriteArgs a) {
-  constexpr int EPL = D / 16;  // elements per lane
-  using CW = typename std::conditional<EPL == 8, uint64_t, uint32_t>::type;  // a lane's codes
-  __shared__ CW s_codes[kWriteWaves][kQuad * 16];  // V codes of the quad, [token][lane]
+  constexpr int HPW = 128 / D;  // KV heads per wave
+  __shared__ uint64_t s_codes[kWriteWaves][64];  // a lane's V codes
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // (wave-uniform, so the slots are scalar loads)
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWriteWaves + wv;
   const int64_t quads = (a.num_tokens + kQuad - 1) / kQuad;
-  if (w >= quads * a.num_kv_heads) return;
-  const int64_t qd = w / a.num_kv_heads;
-  const int h = static_cast<int>(w - qd * a.num_kv_heads);
+  const int hgroups = (a.num_kv_heads + HPW - 1) / HPW;
+  if (w >= quads * hgroups) return;
+  const int64_t qd = w / hgroups;
+  const int h0 = static_cast<int>(w - qd * hgroups) * HPW;
   const Span sp = load_span(a, qd, lane);
-  quant_quad<D, Static, BF16, Vec>(a, quad_of<0>(sp), sp.t0, h, s_codes[wv], lane);
+  quant_quad<D, Static, BF16, Vec>(a, quad_of<0>(sp), sp.t0, h0, s_codes[wv], lane);
   if (sp.n > kQuad)  // a span across two runs of slots
-    quant_quad<D, Static, BF16, Vec>(a, quad_of<1>(sp), sp.t0 + kQuad, h, s_codes[wv], lane);
+    quant_quad<D, Static, BF16, Vec>(a, quad_of<1>(sp), sp.t0 + kQuad, h0, s_codes[wv], lane);
 }
 
 // Plain 16-bit write (the control pool) of up to four consecutive tokens of
@@ -362,8 +376,9 @@ __global__ __launch_bounds__(64 * kWriteWaves) void write_16bit_kernel(WriteArgs
   if (sp.n > kQuad) write_16bit_quad<D, Vec>(a, quad_of<1>(sp), sp.t0 + kQuad, h, lane);
 }
 
-unsigned write_grid(const WriteArgs& a) {
-  const int64_t waves = (a.num_tokens + kQuad - 1) / kQuad * a.num_kv_heads;
+unsigned write_grid(const WriteArgs& a, int heads_per_wave = 1) {
+  const int64_t waves = (a.num_tokens + kQuad - 1) / kQuad *
+                        ((a.num_kv_heads + heads_per_wave - 1) / heads_per_wave);
   return static_cast<unsigned>((waves + kWriteWaves - 1) / kWriteWaves);
 }
 
@@ -379,9 +394,9 @@ bool vec_rows(const WriteArgs& a, int bytes) {
 
 template <bool Static, bool BF16>
 hipError_t launch_quant(const WriteArgs& a, int head_dim, hipStream_t s) {
-  const dim3 grid(write_grid(a)), block(64 * kWriteWaves);
-  // lanes load 16 (D = 128) or 8 (D = 64) bytes of a row
-  const bool vec = vec_rows(a, head_dim / 8);
+  const dim3 grid(write_grid(a, 128 / head_dim)), block(64 * kWriteWaves);
+  // lanes load 16 bytes of a row
+  const bool vec = vec_rows(a, 16);
   if (head_dim == 128) {
     if (vec)
       hipLaunchKernelGGL((quant_write_kernel<128, Static, BF16, true>), grid, block, 0, s, a);
