@@ -9,10 +9,10 @@
 // landed", format-contract bullet; "Precision & memory") and the zero-token
 // rule of mlxcel PR #717 ("The Int8 bug and fix"). Four tokens that fill one
 // V group of a page are stored with whole group words, so a prefill writes
-// whole cache lines instead of a byte scatter. The INT8 kernels give every
-// lane 8 elements of one row (D = 64: two KV heads per wave), so the per-row
-// reductions and scale arithmetic of all the wave's rows run side by side in
-// the same instructions.
+// whole cache lines instead of a byte scatter. Every lane holds 8 elements
+// of one row (D = 64: two KV heads per wave), so the per-row reductions and
+// scale arithmetic of all the wave's rows run side by side in the same
+// instructions.
 #include <type_traits>
 
 #include "device_util.h"
@@ -135,33 +135,40 @@ __device__ __forceinline__ float group_max(float x) {
   }
 }
 
-// Quantize-on-write into INT8 pages (Static = false: per-token scales;
-// true: the layer's scales) of the K and V rows of up to four consecutive
-// tokens of the call, for HPW = 128 / D KV heads at once. Every lane holds 8
-// elements of one row: lane (head hh, token r, i) holds elements 8i .. 8i+7
-// of token r's rows of KV head h0 + hh (LPT = D / 8 lanes per token), so a
-// row's absolute maximum is an LPT-lane reduction and the per-row scale work
-// of all the wave's rows shares instructions. The per-row rules
-// (MoE-Infinity PR #183 "feat: opt-in INT8 KV-cache quantization", "What
-// landed", format-contract bullet; zero rows per mlxcel PR #717 "The Int8
-// bug and fix"; static scales per InfiniLM PR #553 "Summary"):
+enum WriteFormat { kInt8Sym = 0, kInt8Static = 1, kBits16 = 2 };
+
+// Write of the K and V rows of up to four consecutive tokens of the call,
+// for HPW = 128 / D KV heads at once: quantize-on-write into INT8 pages
+// (kInt8Sym: per-token scales; kInt8Static: the layer's scales) or a plain
+// copy into 16-bit pages (kBits16). Every lane holds 8 elements of one row:
+// lane (head hh, token r, i) holds elements 8i .. 8i+7 of token r's rows of
+// KV head h0 + hh (LPT = D / 8 lanes per token), so a row's absolute
+// maximum is an LPT-lane reduction and the per-row scale work of all the
+// wave's rows shares instructions. The per-row rules (MoE-Infinity PR #183
+// "feat: opt-in INT8 KV-cache quantization", "What landed", format-contract
+// bullet; zero rows per mlxcel PR #717 "The Int8 bug and fix"; static scales
+// per InfiniLM PR #553 "Summary"):
 //   per-token: a = max|x|; s = 1.0 if a == 0 else the smallest FP16 >=
 //   fl32(a/127); code = clamp(rint(fl32(x / s)), -127, 127);
 //   static: code = clamp(rint(fl32(x / scale)), -127, 127).
 // A token with a negative slot is padding (skipped); an out-of-range slot or
 // a per-token scale beyond FP16 is flagged and that (token, head) is left
-// unwritten. K rows are stored per token (8 contiguous bytes per lane).
-// When the four tokens are one whole V group of a head, the codes go through
-// LDS to become group words (one dimension of the four tokens) and every
-// lane stores two whole words; otherwise each token's V codes are stored
-// byte by byte.
-template <int D, bool Static, bool BF16, bool Vec>
-__device__ __forceinline__ void quant_quad(const WriteArgs& a, const Quad& q, int64_t t0, int h0,
-                                           uint64_t* s_codes, int lane) {
-  constexpr int EPL = 8;              // elements per lane
-  constexpr int LPT = D / EPL;        // lanes per token row
-  constexpr int LPH = kQuad * LPT;    // lanes per head
-  using L = HeadLayout<D, 1, !Static>;
+// unwritten. K rows are stored per token (8 contiguous elements per lane).
+// When the four tokens are one whole V group of a head, the elements go
+// through LDS to become group words (one dimension of the four tokens) and
+// every lane stores two whole words; otherwise each token's V elements are
+// stored one by one.
+template <int D, int F, bool BF16, bool Vec>
+__device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, int64_t t0, int h0,
+                                           u4_t* s_elems, int lane) {
+  constexpr int EPL = 8;            // elements per lane
+  constexpr int LPT = D / EPL;      // lanes per token row
+  constexpr int LPH = kQuad * LPT;  // lanes per head
+  constexpr int E = F == kBits16 ? 2 : 1;  // bytes per stored element
+  constexpr bool Scales = F == kInt8Sym;
+  using L = HeadLayout<D, E, Scales>;
+  using Packed = typename std::conditional<E == 2, u4_t, uint64_t>::type;  // a lane's 8
+  using Word = typename std::conditional<E == 2, uint64_t, uint32_t>::type;  // group word
   const int hh = lane / LPH, r = lane % LPH / LPT, i = lane % LPT;
   const int h = h0 + hh;
   const bool hvalid = h < a.num_kv_heads;
@@ -171,53 +178,62 @@ __device__ __forceinline__ void quant_quad(const WriteArgs& a, const Quad& q, in
   // token r's K and V elements 8i ..; past the call's end the last token is
   // loaded again
   const int64_t t = t0 + (r < q.nt ? r : q.nt - 1);
-  uint16_t kb[EPL], vb[EPL];
+  u4_t kl, vl;  // 8 raw 16-bit elements
   if constexpr (Vec) {
-    const u4_t kl = *reinterpret_cast<const u4_t*>(static_cast<const uint16_t*>(a.k) +
-                                                   t * a.k_st + hl * a.k_sh + EPL * i);
-    const u4_t vl = *reinterpret_cast<const u4_t*>(static_cast<const uint16_t*>(a.v) +
-                                                   t * a.v_st + hl * a.v_sh + EPL * i);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      kb[e] = static_cast<uint16_t>(kl[e / 2] >> (16 * (e % 2)));
-      vb[e] = static_cast<uint16_t>(vl[e / 2] >> (16 * (e % 2)));
-    }
+    kl = *reinterpret_cast<const u4_t*>(static_cast<const uint16_t*>(a.k) + t * a.k_st +
+                                        hl * a.k_sh + EPL * i);
+    vl = *reinterpret_cast<const u4_t*>(static_cast<const uint16_t*>(a.v) + t * a.v_st +
+                                        hl * a.v_sh + EPL * i);
   } else {
+    uint32_t kw[4] = {}, vw[4] = {};
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const int64_t d = EPL * i + e;
-      kb[e] = static_cast<const uint16_t*>(a.k)[t * a.k_st + hl * a.k_sh + d * a.k_sd];
-      vb[e] = static_cast<const uint16_t*>(a.v)[t * a.v_st + hl * a.v_sh + d * a.v_sd];
+      kw[e / 2] |= static_cast<uint32_t>(static_cast<const uint16_t*>(
+                       a.k)[t * a.k_st + hl * a.k_sh + d * a.k_sd])
+                   << (16 * (e % 2));
+      vw[e / 2] |= static_cast<uint32_t>(static_cast<const uint16_t*>(
+                       a.v)[t * a.v_st + hl * a.v_sh + d * a.v_sd])
+                   << (16 * (e % 2));
     }
-  }
-  float xk[EPL], xv[EPL];
-  float ak = 0.f, av = 0.f;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    xk[e] = bits16_to_f32<BF16>(kb[e]);
-    xv[e] = bits16_to_f32<BF16>(vb[e]);
-    ak = fmaxf(ak, fabsf(xk[e]));
-    av = fmaxf(av, fabsf(xv[e]));
+    kl = u4_t{kw[0], kw[1], kw[2], kw[3]};
+    vl = u4_t{vw[0], vw[1], vw[2], vw[3]};
   }
   bool ok = my_slot >= 0 && hvalid;
-  float sk = a.k_scale, sv = a.v_scale;
+  Packed kc, vc;
   uint16_t skb = 0, svb = 0;
-  if constexpr (!Static) {
-    ak = group_max<LPT>(ak);
-    av = group_max<LPT>(av);
-    const bool okk = row_scale(ak, skb), okv = row_scale(av, svb);
-    if (ok && !(okk && okv)) {
-      if (i == 0) raise_flag(a.err, PDAKV_EFLAG_SCALE_RANGE);
-      ok = false;
-    }
-    sk = f16_bits_to_f32(skb);
-    sv = f16_bits_to_f32(svb);
-  }
-  uint64_t kc = 0, vc = 0;
+  if constexpr (F == kBits16) {
+    kc = kl;
+    vc = vl;
+  } else {
+    float xk[EPL], xv[EPL];
+    float ak = 0.f, av = 0.f;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    kc |= static_cast<uint64_t>(row_code(xk[e], sk)) << (8 * e);
-    vc |= static_cast<uint64_t>(row_code(xv[e], sv)) << (8 * e);
+    for (int e = 0; e < EPL; ++e) {
+      xk[e] = bits16_to_f32<BF16>(static_cast<uint16_t>(kl[e / 2] >> (16 * (e % 2))));
+      xv[e] = bits16_to_f32<BF16>(static_cast<uint16_t>(vl[e / 2] >> (16 * (e % 2))));
+      ak = fmaxf(ak, fabsf(xk[e]));
+      av = fmaxf(av, fabsf(xv[e]));
+    }
+    float sk = a.k_scale, sv = a.v_scale;
+    if constexpr (Scales) {
+      ak = group_max<LPT>(ak);
+      av = group_max<LPT>(av);
+      const bool okk = row_scale(ak, skb), okv = row_scale(av, svb);
+      if (ok && !(okk && okv)) {
+        if (i == 0) raise_flag(a.err, PDAKV_EFLAG_SCALE_RANGE);
+        ok = false;
+      }
+      sk = f16_bits_to_f32(skb);
+      sv = f16_bits_to_f32(svb);
+    }
+    kc = 0;
+    vc = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      kc |= static_cast<uint64_t>(row_code(xk[e], sk)) << (8 * e);
+      vc |= static_cast<uint64_t>(row_code(xv[e], sv)) << (8 * e);
+    }
   }
   // whole V group of this lane's head: all four tokens stored (uniform over
   // the head's lanes)
@@ -227,10 +243,10 @@ __device__ __forceinline__ void quant_quad(const WriteArgs& a, const Quad& q, in
                      q.slot[0] % 4 == 0 && q.slot[1] == q.slot[0] + 1 &&
                      q.slot[2] == q.slot[0] + 2 && q.slot[3] == q.slot[0] + 3;
   const int pos = my_slot % kBlockSize;
-  uint8_t* head = head_of<D, 1, !Static>(a, ok ? my_slot : 0, ok ? h : 0);
+  uint8_t* head = head_of<D, E, Scales>(a, ok ? my_slot : 0, ok ? h : 0);
   if (ok) {
-    *reinterpret_cast<uint64_t*>(head + pos * D + EPL * i) = kc;
-    if constexpr (!Static) {
+    *reinterpret_cast<Packed*>(head + (pos * D + EPL * i) * E) = kc;
+    if constexpr (Scales) {
       if (i == 0) {
         *reinterpret_cast<uint16_t*>(head + L::kKs + 2 * pos) = skb;
         *reinterpret_cast<uint16_t*>(head + L::kVs + 2 * pos) = svb;
@@ -238,36 +254,49 @@ __device__ __forceinline__ void quant_quad(const WriteArgs& a, const Quad& q, in
     }
   }
   // (every lane passes the LDS exchange, so that the wave stays together)
-  s_codes[lane] = vc;
+  *reinterpret_cast<Packed*>(&s_elems[lane]) = vc;
   __builtin_amdgcn_wave_barrier();
   if (whole) {
     // lane (hh, r, i) builds the group words of dimensions 8i + 2r and
-    // 8i + 2r + 1 of its head (one byte of each token per word)
-    const uint8_t* cb = reinterpret_cast<const uint8_t*>(s_codes);
-    uint32_t gw[2];
+    // 8i + 2r + 1 of its head (one element of each token per word)
+    const uint8_t* eb = reinterpret_cast<const uint8_t*>(s_elems);
+    Word gw[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       gw[k] = 0;
 #pragma unroll
-      for (int j = 0; j < kQuad; ++j)
-        gw[k] |= static_cast<uint32_t>(cb[(LPH * hh + LPT * j + i) * 8 + 2 * r + k]) << (8 * j);
+      for (int j = 0; j < kQuad; ++j) {
+        const uint8_t* src = eb + (LPH * hh + LPT * j + i) * 16 + (2 * r + k) * E;
+        const Word el = E == 2 ? *reinterpret_cast<const uint16_t*>(src) : *src;
+        gw[k] |= el << (8 * E * j);
+      }
     }
-    *reinterpret_cast<uint64_t*>(head + L::kV + (pos / 4) * 4 * D + 4 * (EPL * i + 2 * r)) =
-        gw[0] | (static_cast<uint64_t>(gw[1]) << 32);
+    uint8_t* vg = head + L::kV + ((pos / 4) * 4 * D + 4 * (EPL * i + 2 * r)) * E;
+    if constexpr (E == 2)
+      *reinterpret_cast<u4_t*>(vg) = u4_t{static_cast<uint32_t>(gw[0]),
+                                          static_cast<uint32_t>(gw[0] >> 32),
+                                          static_cast<uint32_t>(gw[1]),
+                                          static_cast<uint32_t>(gw[1] >> 32)};
+    else
+      *reinterpret_cast<uint64_t*>(vg) = gw[0] | (static_cast<uint64_t>(gw[1]) << 32);
   } else if (ok) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e)
-      head[L::kV + (pos / 4) * 4 * D + 4 * (EPL * i + e) + pos % 4] =
-          static_cast<uint8_t>(vc >> (8 * e));
+    for (int e = 0; e < EPL; ++e) {
+      uint8_t* dst = head + L::kV + ((pos / 4) * 4 * D + 4 * (EPL * i + e) + pos % 4) * E;
+      if constexpr (E == 2)
+        *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(vc[e / 2] >> (16 * (e % 2)));
+      else
+        *dst = static_cast<uint8_t>(vc >> (8 * e));
+    }
   }
 }
 
 // One wave per four tokens of the call (boundaries moved to V groups) and
 // 128 / D KV heads; a span that crosses runs of slots takes two rounds.
-template <int D, bool Static, bool BF16, bool Vec>
-__global__ __launch_bounds__(64 * kWriteWaves) void quant_write_kernel(WriteArgs a) {
+template <int D, int F, bool BF16, bool Vec>
+__global__ __launch_bounds__(64 * kWriteWaves) void write_kernel(WriteArgs a) {
   constexpr int HPW = 128 / D;  // KV heads per wave
-  __shared__ uint64_t s_codes[kWriteWaves][64];  // a lane's V codes
+  __shared__ u4_t s_elems[kWriteWaves][64];  // a lane's V elements
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // (wave-uniform, so the slots are scalar loads)
@@ -278,102 +307,9 @@ __global__ __launch_bounds__(64 * kWriteWaves) void quant_write_kernel(WriteArgs
   const int64_t qd = w / hgroups;
   const int h0 = static_cast<int>(w - qd * hgroups) * HPW;
   const Span sp = load_span(a, qd, lane);
-  quant_quad<D, Static, BF16, Vec>(a, quad_of<0>(sp), sp.t0, h0, s_codes[wv], lane);
+  write_quad<D, F, BF16, Vec>(a, quad_of<0>(sp), sp.t0, h0, s_elems[wv], lane);
   if (sp.n > kQuad)  // a span across two runs of slots
-    quant_quad<D, Static, BF16, Vec>(a, quad_of<1>(sp), sp.t0 + kQuad, h0, s_codes[wv], lane);
-}
-
-// Plain 16-bit write (the control pool) of up to four consecutive tokens of
-// one KV head, lane l holding elements l * EPL .. of every row; four tokens
-// that are one whole V group are stored with whole group words.
-template <int D, bool Vec>
-__device__ __forceinline__ void write_16bit_quad(const WriteArgs& a, const Quad& q, int64_t t0,
-                                                 int h, int lane) {
-  constexpr int EPL = D / 64;  // elements per lane and row
-  using L = HeadLayout<D, 2, false>;
-  uint16_t kb[kQuad][EPL], vb[kQuad][EPL];
-#pragma unroll
-  for (int j = 0; j < kQuad; ++j) {
-    const int64_t t = t0 + (j < q.nt ? j : q.nt - 1);
-    if constexpr (Vec && EPL == 2) {
-      const uint32_t kw = *reinterpret_cast<const uint32_t*>(
-          static_cast<const uint16_t*>(a.k) + t * a.k_st + h * a.k_sh + 2 * lane);
-      const uint32_t vw = *reinterpret_cast<const uint32_t*>(
-          static_cast<const uint16_t*>(a.v) + t * a.v_st + h * a.v_sh + 2 * lane);
-      kb[j][0] = static_cast<uint16_t>(kw);
-      kb[j][1] = static_cast<uint16_t>(kw >> 16);
-      vb[j][0] = static_cast<uint16_t>(vw);
-      vb[j][1] = static_cast<uint16_t>(vw >> 16);
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const int64_t d = lane * EPL + e;
-        kb[j][e] = static_cast<const uint16_t*>(a.k)[t * a.k_st + h * a.k_sh + d * a.k_sd];
-        vb[j][e] = static_cast<const uint16_t*>(a.v)[t * a.v_st + h * a.v_sh + d * a.v_sd];
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < kQuad; ++j) {
-    if (q.slot[j] < 0) continue;
-    uint8_t* head = head_of<D, 2, false>(a, q.slot[j], h);
-    const int pos = q.slot[j] % kBlockSize;
-    uint32_t kw = 0;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) kw |= static_cast<uint32_t>(kb[j][e]) << (16 * e);
-    if constexpr (EPL == 2)
-      *reinterpret_cast<uint32_t*>(head + (pos * D + 2 * lane) * 2) = kw;
-    else
-      *reinterpret_cast<uint16_t*>(head + (pos * D + lane) * 2) = static_cast<uint16_t>(kw);
-  }
-  const bool whole = q.nt == kQuad && q.slot[0] >= 0 && q.slot[0] % 4 == 0 &&
-                     q.slot[1] == q.slot[0] + 1 && q.slot[2] == q.slot[0] + 2 &&
-                     q.slot[3] == q.slot[0] + 3;
-  if (whole) {
-    uint8_t* head = head_of<D, 2, false>(a, q.slot[0], h);
-    uint8_t* vg = head + L::kV + (q.slot[0] % kBlockSize / 4) * 4 * D * 2 + lane * EPL * 8;
-    uint64_t gw[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      gw[e] = 0;
-#pragma unroll
-      for (int j = 0; j < kQuad; ++j) gw[e] |= static_cast<uint64_t>(vb[j][e]) << (16 * j);
-    }
-    if constexpr (EPL == 2)
-      *reinterpret_cast<u4_t*>(vg) = u4_t{static_cast<uint32_t>(gw[0]),
-                                          static_cast<uint32_t>(gw[0] >> 32),
-                                          static_cast<uint32_t>(gw[1]),
-                                          static_cast<uint32_t>(gw[1] >> 32)};
-    else
-      *reinterpret_cast<uint64_t*>(vg) = gw[0];
-  } else {
-#pragma unroll
-    for (int j = 0; j < kQuad; ++j) {
-      if (q.slot[j] < 0) continue;
-      uint8_t* head = head_of<D, 2, false>(a, q.slot[j], h);
-      const int pos = q.slot[j] % kBlockSize;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const int d = lane * EPL + e;
-        *reinterpret_cast<uint16_t*>(head + L::kV + ((pos / 4) * 4 * D + 4 * d + pos % 4) * 2) =
-            vb[j][e];
-      }
-    }
-  }
-}
-
-template <int D, bool Vec>
-__global__ __launch_bounds__(64 * kWriteWaves) void write_16bit_kernel(WriteArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t w = static_cast<int64_t>(blockIdx.x) * kWriteWaves +
-                    __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t quads = (a.num_tokens + kQuad - 1) / kQuad;
-  if (w >= quads * a.num_kv_heads) return;
-  const int64_t qd = w / a.num_kv_heads;
-  const int h = static_cast<int>(w - qd * a.num_kv_heads);
-  const Span sp = load_span(a, qd, lane);
-  write_16bit_quad<D, Vec>(a, quad_of<0>(sp), sp.t0, h, lane);
-  if (sp.n > kQuad) write_16bit_quad<D, Vec>(a, quad_of<1>(sp), sp.t0 + kQuad, h, lane);
+    write_quad<D, F, BF16, Vec>(a, quad_of<1>(sp), sp.t0 + kQuad, h0, s_elems[wv], lane);
 }
 
 unsigned write_grid(const WriteArgs& a, int heads_per_wave = 1) {
@@ -392,21 +328,21 @@ bool vec_rows(const WriteArgs& a, int bytes) {
          (reinterpret_cast<uintptr_t>(a.v) % bytes) == 0;
 }
 
-template <bool Static, bool BF16>
-hipError_t launch_quant(const WriteArgs& a, int head_dim, hipStream_t s) {
+template <int F, bool BF16>
+hipError_t launch_format(const WriteArgs& a, int head_dim, hipStream_t s) {
   const dim3 grid(write_grid(a, 128 / head_dim)), block(64 * kWriteWaves);
   // lanes load 16 bytes of a row
   const bool vec = vec_rows(a, 16);
   if (head_dim == 128) {
     if (vec)
-      hipLaunchKernelGGL((quant_write_kernel<128, Static, BF16, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((write_kernel<128, F, BF16, true>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((quant_write_kernel<128, Static, BF16, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((write_kernel<128, F, BF16, false>), grid, block, 0, s, a);
   } else {
     if (vec)
-      hipLaunchKernelGGL((quant_write_kernel<64, Static, BF16, true>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((write_kernel<64, F, BF16, true>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((quant_write_kernel<64, Static, BF16, false>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((write_kernel<64, F, BF16, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -415,27 +351,18 @@ hipError_t launch_quant(const WriteArgs& a, int head_dim, hipStream_t s) {
 
 hipError_t launch_quant_write_int8(const WriteArgs& a, int head_dim, bool src_bf16,
                                    hipStream_t s) {
-  return src_bf16 ? launch_quant<false, true>(a, head_dim, s)
-                  : launch_quant<false, false>(a, head_dim, s);
+  return src_bf16 ? launch_format<kInt8Sym, true>(a, head_dim, s)
+                  : launch_format<kInt8Sym, false>(a, head_dim, s);
 }
 
 hipError_t launch_quant_write_static(const WriteArgs& a, int head_dim, bool src_bf16,
                                      hipStream_t s) {
-  return src_bf16 ? launch_quant<true, true>(a, head_dim, s)
-                  : launch_quant<true, false>(a, head_dim, s);
+  return src_bf16 ? launch_format<kInt8Static, true>(a, head_dim, s)
+                  : launch_format<kInt8Static, false>(a, head_dim, s);
 }
 
 hipError_t launch_write_16bit(const WriteArgs& a, int head_dim, hipStream_t s) {
-  const dim3 grid(write_grid(a)), block(64 * kWriteWaves);
-  if (head_dim == 128) {
-    if (vec_rows(a, 4))
-      hipLaunchKernelGGL((write_16bit_kernel<128, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((write_16bit_kernel<128, false>), grid, block, 0, s, a);
-  } else {
-    hipLaunchKernelGGL((write_16bit_kernel<64, false>), grid, block, 0, s, a);
-  }
-  return hipGetLastError();
+  return launch_format<kBits16, false>(a, head_dim, s);
 }
 
 }  // namespace pdakv
