@@ -229,10 +229,20 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, in
     }
     kc = 0;
     vc = 0;
+    if constexpr (Scales) {
+      // FP16 scales: the division-free form (same codes)
+      const float rk = __builtin_amdgcn_rcpf(sk), rv = __builtin_amdgcn_rcpf(sv);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      kc |= static_cast<uint64_t>(row_code(xk[e], sk)) << (8 * e);
-      vc |= static_cast<uint64_t>(row_code(xv[e], sv)) << (8 * e);
+      for (int e = 0; e < EPL; ++e) {
+        kc |= static_cast<uint64_t>(row_code_token(xk[e], sk, rk, 0.5f * sk)) << (8 * e);
+        vc |= static_cast<uint64_t>(row_code_token(xv[e], sv, rv, 0.5f * sv)) << (8 * e);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        kc |= static_cast<uint64_t>(row_code(xk[e], sk)) << (8 * e);
+        vc |= static_cast<uint64_t>(row_code(xv[e], sv)) << (8 * e);
+      }
     }
   }
   // whole V group of this lane's head: all four tokens stored (uniform over
