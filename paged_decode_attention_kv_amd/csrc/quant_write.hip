@@ -135,6 +135,24 @@ __device__ __forceinline__ float group_max(float x) {
   }
 }
 
+// row_code for a per-token scale (an FP16 value s with |x| <= 127 s) and an
+// FP16 or BF16 x, without a division per element; recip = the hardware
+// reciprocal of s (within one ulp), half = s / 2. Why this is the same code:
+// q = x / s is a ratio of two integers of at most 11 bits times a power of
+// two, so it is either exactly a half-integer or at least 2^-13 away from
+// every half-integer. rint(x * recip) differs from q by at most 2.3e-5 (|q|
+// <= 127.5) and so rounds like q except at exact ties, and the correctly
+// rounded quotient (error below 2^-17) also rounds like q. A tie shows as
+// |x - c s| == s / 2 (fma, exact here: at most 13 significant bits), and
+// then the even neighbour is taken.
+__device__ __forceinline__ uint8_t row_code_token(float x, float scale, float recip,
+                                                  float half) {
+  float c = rintf(x * recip);
+  const float e = fmaf(-c, scale, x);  // scale * (q - c), exact
+  if (fabsf(e) == half && (static_cast<int>(c) & 1) != 0) c += e > 0.f ? 1.f : -1.f;
+  return static_cast<uint8_t>(static_cast<int8_t>(fminf(fmaxf(c, -127.f), 127.f)));
+}
+
 enum WriteFormat { kInt8Sym = 0, kInt8Static = 1, kBits16 = 2 };
 
 // Write of the K and V rows of up to four consecutive tokens of the call,
