@@ -113,44 +113,93 @@ __device__ __forceinline__ uint8_t* head_of(const WriteArgs& a, int32_t slot, in
 }
 
 // Max over each group of LPT lanes (16: DPP rotations inside a 16-lane row;
-// 8: swaps inside quads, then the mirror inside each half row); VALU only,
-// and every lane of the group gets it.
+// 8: swaps inside quads, then the mirror inside each half row) of unsigned
+// values; VALU only, and every lane of the group gets it.
 template <int Ctrl>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(x), Ctrl, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t dpp(uint32_t x) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(x), Ctrl, 0xF, 0xF, false));
 }
 template <int LPT>
-__device__ __forceinline__ float group_max(float x) {
+__device__ __forceinline__ uint32_t group_max(uint32_t x) {
   if constexpr (LPT == 16) {
-    x = fmaxf(x, dpp<0x128>(x));  // row_ror:8
-    x = fmaxf(x, dpp<0x124>(x));  // row_ror:4
-    x = fmaxf(x, dpp<0x122>(x));  // row_ror:2
-    return fmaxf(x, dpp<0x121>(x));  // row_ror:1
+    x = max(x, dpp<0x128>(x));  // row_ror:8
+    x = max(x, dpp<0x124>(x));  // row_ror:4
+    x = max(x, dpp<0x122>(x));  // row_ror:2
+    return max(x, dpp<0x121>(x));  // row_ror:1
   } else {
     static_assert(LPT == 8, "8 or 16 lanes per token");
-    x = fmaxf(x, dpp<0xB1>(x));   // quad_perm [1, 0, 3, 2]
-    x = fmaxf(x, dpp<0x4E>(x));   // quad_perm [2, 3, 0, 1]
-    return fmaxf(x, dpp<0x141>(x));  // row_half_mirror
+    x = max(x, dpp<0xB1>(x));   // quad_perm [1, 0, 3, 2]
+    x = max(x, dpp<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+    return max(x, dpp<0x141>(x));  // row_half_mirror
   }
 }
 
-// row_code for a per-token scale (an FP16 value s with |x| <= 127 s) and an
-// FP16 or BF16 x, without a division per element; recip = the hardware
-// reciprocal of s (within one ulp), half = s / 2. Why this is the same code:
-// q = x / s is a ratio of two integers of at most 11 bits times a power of
-// two, so it is either exactly a half-integer or at least 2^-13 away from
-// every half-integer. rint(x * recip) differs from q by at most 2.3e-5 (|q|
-// <= 127.5) and so rounds like q except at exact ties, and the correctly
-// rounded quotient (error below 2^-17) also rounds like q. A tie shows as
-// |x - c s| == s / 2 (fma, exact here: at most 13 significant bits), and
-// then the even neighbour is taken.
-__device__ __forceinline__ uint8_t row_code_token(float x, float scale, float recip,
-                                                  float half) {
-  float c = rintf(x * recip);
-  const float e = fmaf(-c, scale, x);  // scale * (q - c), exact
-  if (fabsf(e) == half && (static_cast<int>(c) & 1) != 0) c += e > 0.f ? 1.f : -1.f;
-  return static_cast<uint8_t>(static_cast<int8_t>(fminf(fmaxf(c, -127.f), 127.f)));
+// Largest magnitude of the eight FP16 or BF16 values in w, as the 16-bit
+// pattern of |x|: without the sign bit both formats order like unsigned
+// integers (a NaN above the infinity, the infinity above every finite
+// value), so this is an integer max of packed halves.
+__device__ __forceinline__ uint32_t max_magnitude(const u4_t& w) {
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+  auto m = [](uint32_t x) { return __builtin_bit_cast(us2, x & 0x7fff7fffu); };
+  const us2 r = __builtin_elementwise_max(__builtin_elementwise_max(m(w[0]), m(w[1])),
+                                          __builtin_elementwise_max(m(w[2]), m(w[3])));
+  return max(static_cast<uint32_t>(r.x), static_cast<uint32_t>(r.y));
+}
+
+// Per-token scale of a row with absolute maximum a (an FP16 or BF16 value):
+// the row rule of quant_row.h with a / 127 taken without a division: q0 =
+// a * fl(1/127) is within an ulp, and one residual step (the residual is
+// exact in an fma) gives fl32(a / 127) for every FP16 and BF16 magnitude
+// (checked for all of them). False when the scale is beyond FP16 or a is not
+// finite.
+__device__ __forceinline__ bool row_scale_token(float a, uint16_t& bits) {
+  constexpr float r = 1.0f / 127.0f;
+  const float q0 = a * r;
+  const float s32 = fmaf(fmaf(-q0, 127.0f, a), r, q0);
+  if (!(s32 <= 65504.0f)) return false;
+  bits = a == 0.f ? 0x3C00 : round_up_f16(s32);
+  return true;
+}
+
+// Codes of the eight FP16 or BF16 values in w for a per-token scale s (an
+// FP16 value with |x| <= 127 s), equal to clamp(rint(fl32(x / s)), -127, 127)
+// but without a division; recip = the hardware reciprocal of s (within one
+// ulp), kinf = recip * (1 + 2^-15). Why these are the same codes:
+// * q = x / s is a ratio of two integers of at most 11 bits times a power of
+//   two, so it is exactly a half-integer (a tie) or at least 2^-13 away from
+//   every half-integer; |q| <= 127, so no clamp is needed.
+// * t = fma(x, recip, 1.5 * 2^23) rounds x * recip (within 127.5 * 2^-23 of
+//   q) to an integer c held in t's low mantissa bits: c = rint(q) except at
+//   ties, where it is one of the two neighbours.
+// * e = x - c s is exact in an fma, and e * kinf lies strictly inside
+//   (-0.5, 0.5) unless q is a tie, where it is just beyond +-0.5; clamped to
+//   [-0.5, 0.5] it is q - c at a tie and below 0.5 in magnitude otherwise.
+// * t + that rounds to nearest even at the integer spacing of t: c, or at a
+//   tie the even one of c and c +- 1 (t's parity is c's, 1.5 * 2^23 being
+//   even). The low byte of its bits is then the two's-complement code.
+// (Checked against IEEE division for every FP16 and BF16 x and FP16 s, with
+// the reciprocal anywhere within one ulp.)
+template <bool BF16>
+__device__ __forceinline__ uint64_t codes_token(const u4_t& w, float s, float recip,
+                                                float kinf) {
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+  uint32_t f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = bits16_to_f32<BF16>(static_cast<uint16_t>(w[e / 2] >> (16 * (e % 2))));
+    const float t = fmaf(x, recip, kMagic);
+    const float c = t - kMagic;
+    const float err = fmaf(-c, s, x);
+    const float tie = fminf(fmaxf(err * kinf, -0.5f), 0.5f);
+    f[e] = __float_as_uint(t + tie);
+  }
+  // low bytes of f[0..3] and f[4..7] into two words (byte-select 0x0c: zero)
+  auto pack = [](uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    return __builtin_amdgcn_perm(b, a, 0x0c0c0400u) | __builtin_amdgcn_perm(d, c, 0x04000c0cu);
+  };
+  return pack(f[0], f[1], f[2], f[3]) |
+         (static_cast<uint64_t>(pack(f[4], f[5], f[6], f[7])) << 32);
 }
 
 enum WriteFormat { kInt8Sym = 0, kInt8Static = 1, kBits16 = 2 };
@@ -186,7 +235,6 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, in
   constexpr bool Scales = F == kInt8Sym;
   using L = HeadLayout<D, E, Scales>;
   using Packed = typename std::conditional<E == 2, u4_t, uint64_t>::type;  // a lane's 8
-  using Word = typename std::conditional<E == 2, uint64_t, uint32_t>::type;  // group word
   const int hh = lane / LPH, r = lane % LPH / LPT, i = lane % LPT;
   const int h = h0 + hh;
   const bool hvalid = h < a.num_kv_heads;
@@ -223,44 +271,34 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, in
   if constexpr (F == kBits16) {
     kc = kl;
     vc = vl;
+  } else if constexpr (F == kInt8Sym) {
+    // row maxima as magnitude bits, reduced over the row's lanes (a NaN
+    // stays the largest and is flagged with the scale)
+    const float ak = bits16_to_f32<BF16>(static_cast<uint16_t>(group_max<LPT>(max_magnitude(kl))));
+    const float av = bits16_to_f32<BF16>(static_cast<uint16_t>(group_max<LPT>(max_magnitude(vl))));
+    const bool okk = row_scale_token(ak, skb), okv = row_scale_token(av, svb);
+    if (ok && !(okk && okv)) {
+      if (i == 0) raise_flag(a.err, PDAKV_EFLAG_SCALE_RANGE);
+      ok = false;
+    }
+    const float sk = f16_bits_to_f32(skb), sv = f16_bits_to_f32(svb);
+    const float rk = __builtin_amdgcn_rcpf(sk), rv = __builtin_amdgcn_rcpf(sv);
+    constexpr float kInflate = 1.000030517578125f;  // 1 + 2^-15
+    kc = codes_token<BF16>(kl, sk, rk, rk * kInflate);
+    vc = codes_token<BF16>(vl, sv, rv, rv * kInflate);
   } else {
-    float xk[EPL], xv[EPL];
-    float ak = 0.f, av = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      xk[e] = bits16_to_f32<BF16>(static_cast<uint16_t>(kl[e / 2] >> (16 * (e % 2))));
-      xv[e] = bits16_to_f32<BF16>(static_cast<uint16_t>(vl[e / 2] >> (16 * (e % 2))));
-      ak = fmaxf(ak, fabsf(xk[e]));
-      av = fmaxf(av, fabsf(xv[e]));
-    }
-    float sk = a.k_scale, sv = a.v_scale;
-    if constexpr (Scales) {
-      ak = group_max<LPT>(ak);
-      av = group_max<LPT>(av);
-      const bool okk = row_scale(ak, skb), okv = row_scale(av, svb);
-      if (ok && !(okk && okv)) {
-        if (i == 0) raise_flag(a.err, PDAKV_EFLAG_SCALE_RANGE);
-        ok = false;
-      }
-      sk = f16_bits_to_f32(skb);
-      sv = f16_bits_to_f32(svb);
-    }
     kc = 0;
     vc = 0;
-    if constexpr (Scales) {
-      // FP16 scales: the division-free form (same codes)
-      const float rk = __builtin_amdgcn_rcpf(sk), rv = __builtin_amdgcn_rcpf(sv);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        kc |= static_cast<uint64_t>(row_code_token(xk[e], sk, rk, 0.5f * sk)) << (8 * e);
-        vc |= static_cast<uint64_t>(row_code_token(xv[e], sv, rv, 0.5f * sv)) << (8 * e);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        kc |= static_cast<uint64_t>(row_code(xk[e], sk)) << (8 * e);
-        vc |= static_cast<uint64_t>(row_code(xv[e], sv)) << (8 * e);
-      }
+    for (int e = 0; e < EPL; ++e) {
+      kc |= static_cast<uint64_t>(
+                row_code(bits16_to_f32<BF16>(static_cast<uint16_t>(kl[e / 2] >> (16 * (e % 2)))),
+                         a.k_scale))
+            << (8 * e);
+      vc |= static_cast<uint64_t>(
+                row_code(bits16_to_f32<BF16>(static_cast<uint16_t>(vl[e / 2] >> (16 * (e % 2)))),
+                         a.v_scale))
+            << (8 * e);
     }
   }
   // whole V group of this lane's head: all four tokens stored (uniform over
@@ -286,27 +324,30 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, in
   __builtin_amdgcn_wave_barrier();
   if (whole) {
     // lane (hh, r, i) builds the group words of dimensions 8i + 2r and
-    // 8i + 2r + 1 of its head (one element of each token per word)
-    const uint8_t* eb = reinterpret_cast<const uint8_t*>(s_elems);
-    Word gw[2];
+    // 8i + 2r + 1 of its head (one element of each token per word): it reads
+    // the word of each token's lane that holds those two elements and
+    // gathers them with byte selects
+    const uint32_t* ew = reinterpret_cast<const uint32_t*>(s_elems + LPH * hh + i);
+    uint32_t d[kQuad];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      gw[k] = 0;
-#pragma unroll
-      for (int j = 0; j < kQuad; ++j) {
-        const uint8_t* src = eb + (LPH * hh + LPT * j + i) * 16 + (2 * r + k) * E;
-        const Word el = E == 2 ? *reinterpret_cast<const uint16_t*>(src) : *src;
-        gw[k] |= el << (8 * E * j);
-      }
-    }
+    for (int j = 0; j < kQuad; ++j) d[j] = ew[4 * LPT * j + (E == 2 ? r : r >> 1)];
     uint8_t* vg = head + L::kV + ((pos / 4) * 4 * D + 4 * (EPL * i + 2 * r)) * E;
-    if constexpr (E == 2)
-      *reinterpret_cast<u4_t*>(vg) = u4_t{static_cast<uint32_t>(gw[0]),
-                                          static_cast<uint32_t>(gw[0] >> 32),
-                                          static_cast<uint32_t>(gw[1]),
-                                          static_cast<uint32_t>(gw[1] >> 32)};
-    else
-      *reinterpret_cast<uint64_t*>(vg) = gw[0] | (static_cast<uint64_t>(gw[1]) << 32);
+    if constexpr (E == 2) {
+      // word j holds elements 2r (low half) and 2r + 1 (high half) of token j
+      *reinterpret_cast<u4_t*>(vg) = u4_t{__builtin_amdgcn_perm(d[1], d[0], 0x05040100u),
+                                          __builtin_amdgcn_perm(d[3], d[2], 0x05040100u),
+                                          __builtin_amdgcn_perm(d[1], d[0], 0x07060302u),
+                                          __builtin_amdgcn_perm(d[3], d[2], 0x07060302u)};
+    } else {
+      // elements 2r and 2r + 1 are bytes b and b + 1 of word j
+      const uint32_t b = 2 * (r & 1);
+      const uint32_t sel = b | (b + 4) << 8 | (b + 1) << 16 | (b + 5) << 24;
+      const uint32_t t01 = __builtin_amdgcn_perm(d[1], d[0], sel);  // d0.b d1.b d0.b+1 d1.b+1
+      const uint32_t t23 = __builtin_amdgcn_perm(d[3], d[2], sel);
+      *reinterpret_cast<uint64_t*>(vg) =
+          __builtin_amdgcn_perm(t23, t01, 0x05040100u) |
+          static_cast<uint64_t>(__builtin_amdgcn_perm(t23, t01, 0x07060302u)) << 32;
+    }
   } else if (ok) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {

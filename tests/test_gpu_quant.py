@@ -114,6 +114,54 @@ def test_subnormal_and_tie_rows(P):
     assert np.array_equal(pool.cpu().numpy(), want)
 
 
+def _near_tie_rows(rng, n_rows, d, dtype):
+    """Rows whose absolute maxima cover the FP16 scale range (subnormal
+    scales included) and whose other elements sit on the half-integer
+    multiples of the row's scale or one step of the input type beside them:
+    the values where a code is decided by the last bit of x / s."""
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    top = 15.9 if dtype == "f16" else 22.9                # scale within FP16
+    a = np.exp2(rng.uniform(-22.0, top, n_rows)).astype(np.float32)
+    a = torch.from_numpy(a).to(tdt).float().numpy()       # representable maxima
+    _, s = oracle.quantize_rows(a[:, None])                # the rows' scales
+    s = s.astype(np.float32)
+    k = rng.integers(-127, 127, (n_rows, d)) + 0.5
+    x = torch.from_numpy((k * s[:, None]).astype(np.float32)).to(tdt)
+    bits = x.view(torch.int16).numpy().astype(np.int32)
+    step = rng.integers(-1, 2, (n_rows, d))                # below, at, above
+    bits = np.where(bits == 0, 0, bits + step).astype(np.int16)
+    x = torch.from_numpy(bits).view(tdt).float().numpy()
+    x = np.where(np.abs(x) <= a[:, None], x, 0.0).astype(np.float32)
+    x[:, 0] = a * np.where(rng.random(n_rows) < 0.5, -1, 1)
+    return torch.from_numpy(x).to(tdt)
+
+
+@pytest.mark.parametrize("dtype,d", [("f16", 128), ("bf16", 128), ("f16", 64)])
+def test_codes_beside_ties_every_scale_range(P, dtype, d):
+    """Per-token codes at and one step beside every half-integer multiple of
+    the row scale, over scales from FP16 subnormals to the top of the FP16 range: bit-exact with
+    the oracle's IEEE division."""
+    rng = np.random.default_rng(77 if dtype == "f16" else 78)
+    T, hkv = 2048, 4
+    _say(f"near-tie rows: {dtype} D={d} tokens {T} heads {hkv}")
+    k = _near_tie_rows(rng, T * hkv, d, dtype).reshape(T, hkv, d)
+    v = _near_tie_rows(rng, T * hkv, d, dtype).reshape(T, hkv, d)
+    nb = T // 16
+    slots = rng.permutation(nb * 16).astype(np.int32)[:T]
+    pb = P.pdakv_page_bytes(P.KV_INT8_SYM, 16, hkv, d)
+    pool = torch.full((nb, pb), FILL, dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    P.kv_quant_int8_sym_write(k.cuda(), v.cuda(), dev_i32(slots), pool, nb, err_flag=err)
+    assert int(err.item()) == 0
+    want = oracle.new_pool(oracle.KV_INT8_SYM, nb, 16, hkv, d, fill=FILL)
+    kc, ks = oracle.quantize_rows(k)
+    vc, vs = oracle.quantize_rows(v)
+    oracle.write_int8_tokens(want, kc, ks, vc, vs, slots, 16)
+    got = pool.cpu().numpy()
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, f"{bad[0].size} bytes differ, first at page {bad[0][0]} byte {bad[1][0]}"
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("idx", [3, 4])
 def test_full_size_write_sampled(P, idx):
