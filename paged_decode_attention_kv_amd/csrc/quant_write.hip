@@ -202,6 +202,39 @@ __device__ __forceinline__ uint64_t codes_token(const u4_t& w, float s, float re
          (static_cast<uint64_t>(pack(f[4], f[5], f[6], f[7])) << 32);
 }
 
+// Codes of the eight FP16 or BF16 values in w for a static scale s in
+// [2^-64, 2^64] and r = fl(1/s), equal to clamp(rint(fl32(x / s)), -127,
+// 127) without a division: q0 = x r is within an ulp of x / s, the residual
+// x - q0 s is exact in an fma, and q0 + residual * r rounds to fl32(x / s)
+// (Markstein's theorem for a correctly rounded reciprocal; also checked
+// against IEEE division for every FP16 and BF16 x over scales across the
+// window). BF16 values are first clamped to +-128 s, which keeps every code
+// and keeps x r finite; FP16 values cannot overflow it. The clamped quotient
+// plus 1.5 * 2^23 rounds to nearest even, and its low byte is the code.
+__device__ __forceinline__ bool static_window(float s) {
+  return s >= 0x1p-64f && s <= 0x1p64f;
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint64_t codes_static(const u4_t& w, float s, float r) {
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+  const float lim = 128.0f * s;
+  uint32_t f[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float x = bits16_to_f32<BF16>(static_cast<uint16_t>(w[e / 2] >> (16 * (e % 2))));
+    if constexpr (BF16) x = fminf(fmaxf(x, -lim), lim);
+    const float q0 = fmaf(x, r, 0.0f);
+    const float q1 = fmaf(fmaf(-q0, s, x), r, q0);
+    f[e] = __float_as_uint(fminf(fmaxf(q1, -127.0f), 127.0f) + kMagic);
+  }
+  auto pack = [](uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+    return __builtin_amdgcn_perm(b, a, 0x0c0c0400u) | __builtin_amdgcn_perm(d, c, 0x04000c0cu);
+  };
+  return pack(f[0], f[1], f[2], f[3]) |
+         (static_cast<uint64_t>(pack(f[4], f[5], f[6], f[7])) << 32);
+}
+
 enum WriteFormat { kInt8Sym = 0, kInt8Static = 1, kBits16 = 2 };
 
 // Write of the K and V rows of up to four consecutive tokens of the call,
@@ -286,7 +319,11 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, in
     constexpr float kInflate = 1.000030517578125f;  // 1 + 2^-15
     kc = codes_token<BF16>(kl, sk, rk, rk * kInflate);
     vc = codes_token<BF16>(vl, sv, rv, rv * kInflate);
+  } else if (static_window(a.k_scale) && static_window(a.v_scale)) {
+    kc = codes_static<BF16>(kl, a.k_scale, 1.0f / a.k_scale);
+    vc = codes_static<BF16>(vl, a.v_scale, 1.0f / a.v_scale);
   } else {
+    // scales outside [2^-64, 2^64]: one IEEE division per element
     kc = 0;
     vc = 0;
 #pragma unroll

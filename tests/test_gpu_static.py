@@ -104,6 +104,56 @@ def test_static_edge_lengths(P, hq, hkv, d, dt):
     assert torch.all(out[0] == 0)  # empty context -> zero rows
 
 
+def _static_rows(rng, shape, s, dtype):
+    """Values at and one step of the input type beside the half-integer
+    multiples k + 1/2 of the scale (k in -130 .. 129, so some saturate),
+    mixed with values of random sign spread log-uniformly over a wide range
+    around the scale."""
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    n = int(np.prod(shape))
+    k = rng.integers(-130, 130, n) + 0.5
+    near = torch.from_numpy((k * s).astype(np.float32)).to(tdt)
+    bits = near.view(torch.int16).numpy().astype(np.int32)
+    bits = np.where(bits == 0, 0, bits + rng.integers(-1, 2, n)).astype(np.int16)
+    near = torch.from_numpy(bits).view(tdt).float().numpy()
+    lo, hi = (-24.0, 15.9) if dtype == "f16" else (-120.0, 120.0)
+    wide = np.exp2(rng.uniform(lo, hi, n)) * rng.choice([-1.0, 1.0], n)
+    x = np.where(rng.random(n) < 0.7, near, wide).astype(np.float32)
+    x = torch.from_numpy(x).to(tdt).float()
+    x[~torch.isfinite(x)] = 0.0
+    return x.to(tdt).reshape(shape)
+
+
+@pytest.mark.parametrize("dtype,ks,vs", [
+    ("f16", 0.0390625, 0.0123457), ("bf16", 0.0390625, 3.3e-3),
+    ("f16", 2.0 ** -64, 2.0 ** 64), ("bf16", 2.0 ** -64, 2.0 ** 64),
+    ("f16", 1e-21, 7e19), ("bf16", 3e-30, 1e25)])
+def test_static_codes_beside_ties_and_outside_the_scale_window(P, dtype, ks, vs):
+    """Static-scale codes at and beside the ties x = (k + 1/2) s, and for
+    scales at the ends of and outside [2^-64, 2^64] (where the writer keeps
+    one division per element): bit-exact with the oracle."""
+    rng = np.random.default_rng(91)
+    T, hkv, d = 1024, 2, 128
+    _say(f"static codes: {dtype} ks {ks:.4g} vs {vs:.4g}")
+    k = _static_rows(rng, (T, hkv, d), ks, dtype)
+    v = _static_rows(rng, (T, hkv, d), vs, dtype)
+    nb = T // 16
+    slots = rng.permutation(nb * 16).astype(np.int32)[:T]
+    pb = P.pdakv_page_bytes(P.KV_INT8_STATIC, 16, hkv, d)
+    pool = torch.full((nb, pb), FILL, dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    P.kv_quant_int8_static_write(k.cuda(), v.cuda(), dev_i32(slots), pool, nb, ks, vs,
+                                 err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    want = oracle.new_pool(oracle.KV_INT8_STATIC, nb, 16, hkv, d, fill=FILL)
+    oracle.write_int8_static_tokens(want, oracle.quantize_static(k, ks),
+                                    oracle.quantize_static(v, vs), slots, 16)
+    got = pool.cpu().numpy()
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, f"{bad[0].size} bytes differ, first at page {bad[0][0]} byte {bad[1][0]}"
+
+
 @pytest.mark.parametrize("out_dtype", [torch.float16, torch.bfloat16])
 def test_static_16bit_outputs_round_the_fp32_output(P, out_dtype):
     wl = make_config(2, 0.5)
