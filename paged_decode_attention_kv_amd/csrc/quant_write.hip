@@ -1,8 +1,9 @@
 // Quantize-on-write and 16-bit write into paged KV pools (gfx950).
 //
-// One wave (64 lanes) owns about four consecutive tokens of the call for one
-// KV head (a span aligned to the V groups of the pages, below) and handles
-// their K and V rows; a workgroup holds four waves. Three
+// One wave (64 lanes) owns one to three consecutive spans of about four
+// tokens of the call (each aligned to the V groups of the pages, below) for
+// one KV head and handles their K and V rows; a workgroup holds four waves.
+// Three
 // pool formats: per-token INT8 (codes + FP16 scales), static-scale INT8
 // (codes only) and 16-bit. The row quantizer (quant_row.h) follows
 // MoE-Infinity PR #183 "feat: opt-in INT8 KV-cache quantization" ("What
@@ -24,7 +25,8 @@ namespace pdakv {
 namespace {
 
 constexpr int kWriteWaves = 4;
-constexpr int kQuad = 4;  // tokens per wave: one V group of the page layout
+constexpr int kQuad = 4;  // tokens per span: one V group of the page layout
+
 
 // Head block of a page: element size E (1: INT8 codes, 2: 16-bit values), K
 // rows at pos * D elements, V grouped four tokens at a time from 16 * D
@@ -38,30 +40,34 @@ struct HeadLayout {
   static constexpr int kVs = 32 * D + 32;        // V scales
 };
 
-// Tokens are dealt to waves four at a time, with each boundary between the
-// fours moved back to the start of the V group its token lands in: boundary
-// b moves to b - k when token b's slot is 4g + k and tokens b - k .. b - 1
-// hold slots 4g .. 4g + k - 1. Both waves next to a boundary compute the
-// same move, so every token is handled once; inside a run of consecutive
-// slots (a prefill chunk, whatever its start offset in the page) every wave
-// then holds whole V groups. A wave reads the slots of tokens 4q - 4 ..
-// 4q + 7 at once (one per lane), which covers both of its boundaries and its
-// up to seven tokens.
+// Tokens are dealt out four at a time, with each boundary between the fours
+// moved back to the start of the V group its token lands in: boundary b
+// moves to b - k when token b's slot is 4g + k and tokens b - k .. b - 1 hold
+// slots 4g .. 4g + k - 1. Both sides of a boundary compute the same move, so
+// every token is handled once; inside a run of consecutive slots (a prefill
+// chunk, whatever its start offset in the page) every span then holds whole
+// V groups. A wave takes N consecutive fours (spans) and reads the slots of
+// tokens 4q - 4 .. 4q + 4N + 3 at once (one per lane), which covers all of
+// its boundaries and tokens.
 struct Span {
   int64_t t0;       // first token
-  int n;            // tokens (1 .. 7)
+  int n;            // tokens (1 .. 7; 0 or less past the call's end)
   int32_t slot[8];  // their slots (-1: padding or out of range)
 };
-__device__ __forceinline__ Span load_span(const WriteArgs& a, int64_t qd, int lane) {
+template <int N>
+__device__ __forceinline__ void load_spans(const WriteArgs& a, int64_t qd, int lane,
+                                           Span (&sp)[N]) {
+  constexpr int NS = kQuad * (N + 2);
+  static_assert(NS <= 64, "one slot per lane");
   const int64_t base = qd * kQuad - kQuad, T = a.num_tokens;
   const int64_t cap = a.num_blocks * kBlockSize;
-  // one load per lane, then every lane reads the twelve slots
+  // one load per lane, then every lane reads the slots
   const int64_t tl = base + lane;
   int32_t mine = a.slots[tl < 0 ? 0 : (tl >= T ? T - 1 : tl)];
   if (tl < 0 || tl >= T) mine = -1;
-  int32_t S[3 * kQuad];
+  int32_t S[NS];
 #pragma unroll
-  for (int j = 0; j < 3 * kQuad; ++j) S[j] = __builtin_amdgcn_readlane(mine, j);
+  for (int j = 0; j < NS; ++j) S[j] = __builtin_amdgcn_readlane(mine, j);
   // boundary at token base + c
   auto bnd = [&](int c) -> int64_t {
     const int64_t b = base + c;
@@ -74,22 +80,27 @@ __device__ __forceinline__ Span load_span(const WriteArgs& a, int64_t qd, int la
     for (int j = 1; j < kQuad; ++j) run = run && (j > k || S[c - j] == s - j);
     return run ? b - k : b;
   };
-  Span sp;
-  sp.t0 = bnd(kQuad);
-  sp.n = static_cast<int>(min(bnd(2 * kQuad), T) - sp.t0);
-  // token t0 + j is S[off + j], off in 1 .. 4 (selected with constant
-  // indexes: S stays in registers)
-  const int off = static_cast<int>(sp.t0 - base);
   bool bad = false;
+  int64_t lo = bnd(kQuad);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int32_t s = off == 1 ? S[1 + j] : off == 2 ? S[2 + j] : off == 3 ? S[3 + j] : S[4 + j];
-    if (j >= sp.n) s = -1;
-    bad = bad || s >= cap;
-    sp.slot[j] = s >= cap ? -1 : s;
+  for (int p = 0; p < N; ++p) {
+    const int64_t hi = bnd(kQuad * (p + 2));
+    sp[p].t0 = lo;
+    sp[p].n = static_cast<int>(min(hi, T) - lo);
+    // token t0 + j is S[4p + off + j], off in 1 .. 4 (selected with constant
+    // indexes: S stays in registers)
+    const int off = static_cast<int>(lo - base) - kQuad * p;
+    const int32_t* Sp = S + kQuad * p;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int32_t s = off == 1 ? Sp[1 + j] : off == 2 ? Sp[2 + j] : off == 3 ? Sp[3 + j] : Sp[4 + j];
+      if (j >= sp[p].n) s = -1;
+      bad = bad || s >= cap;
+      sp[p].slot[j] = s >= cap ? -1 : s;
+    }
+    lo = hi;
   }
   if (bad && lane == 0) raise_flag(a.err, PDAKV_EFLAG_SLOT_RANGE);
-  return sp;
 }
 
 // Up to four consecutive tokens t0 .. t0+nt-1 of a wave and their slots.
@@ -237,6 +248,12 @@ __device__ __forceinline__ uint64_t codes_static(const u4_t& w, float s, float r
 
 enum WriteFormat { kInt8Sym = 0, kInt8Static = 1, kBits16 = 2 };
 
+// Spans per wave (measured on 262K- and 296K-token prefills): the INT8
+// writers gain 5-8% from three spans' loads in flight at D = 128 (two at
+// D = 64, where more registers cost occupancy); the 16-bit writer, already
+// near the copy rate, is 10% slower with more than one.
+constexpr int spans_per_wave(int D, int F) { return F == kBits16 ? 1 : D == 128 ? 3 : 2; }
+
 // Write of the K and V rows of up to four consecutive tokens of the call,
 // for HPW = 128 / D KV heads at once: quantize-on-write into INT8 pages
 // (kInt8Sym: per-token scales; kInt8Static: the layer's scales) or a plain
@@ -258,31 +275,29 @@ enum WriteFormat { kInt8Sym = 0, kInt8Static = 1, kBits16 = 2 };
 // through LDS to become group words (one dimension of the four tokens) and
 // every lane stores two whole words; otherwise each token's V elements are
 // stored one by one.
-template <int D, int F, bool BF16, bool Vec>
-__device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, int64_t t0, int h0,
-                                           u4_t* s_elems, int lane) {
-  constexpr int EPL = 8;            // elements per lane
-  constexpr int LPT = D / EPL;      // lanes per token row
-  constexpr int LPH = kQuad * LPT;  // lanes per head
-  constexpr int E = F == kBits16 ? 2 : 1;  // bytes per stored element
-  constexpr bool Scales = F == kInt8Sym;
-  using L = HeadLayout<D, E, Scales>;
-  using Packed = typename std::conditional<E == 2, u4_t, uint64_t>::type;  // a lane's 8
+// A lane's 8 raw 16-bit K and V elements.
+struct Rows {
+  u4_t k, v;
+};
+
+// Loads of the rows of up to four consecutive tokens t0 .. t0 + nt - 1
+// (nt >= 1): lane (head hh, token r, i) gets elements 8i .. 8i+7 of token
+// r's rows of KV head h0 + hh; past the call's end the last token, and past
+// the last head the last head, are loaded again.
+template <int D, bool Vec>
+__device__ __forceinline__ Rows load_rows(const WriteArgs& a, const Quad& q, int64_t t0, int h0,
+                                          int lane) {
+  constexpr int EPL = 8, LPT = D / EPL, LPH = kQuad * LPT;
   const int hh = lane / LPH, r = lane % LPH / LPT, i = lane % LPT;
   const int h = h0 + hh;
-  const bool hvalid = h < a.num_kv_heads;
-  const int hl = hvalid ? h : a.num_kv_heads - 1;  // head whose rows are loaded
-  const int32_t my_slot = r == 0 ? q.slot[0] : r == 1 ? q.slot[1] : r == 2 ? q.slot[2] : q.slot[3];
-
-  // token r's K and V elements 8i ..; past the call's end the last token is
-  // loaded again
+  const int hl = h < a.num_kv_heads ? h : a.num_kv_heads - 1;
   const int64_t t = t0 + (r < q.nt ? r : q.nt - 1);
-  u4_t kl, vl;  // 8 raw 16-bit elements
+  Rows in;
   if constexpr (Vec) {
-    kl = *reinterpret_cast<const u4_t*>(static_cast<const uint16_t*>(a.k) + t * a.k_st +
-                                        hl * a.k_sh + EPL * i);
-    vl = *reinterpret_cast<const u4_t*>(static_cast<const uint16_t*>(a.v) + t * a.v_st +
-                                        hl * a.v_sh + EPL * i);
+    in.k = *reinterpret_cast<const u4_t*>(static_cast<const uint16_t*>(a.k) + t * a.k_st +
+                                          hl * a.k_sh + EPL * i);
+    in.v = *reinterpret_cast<const u4_t*>(static_cast<const uint16_t*>(a.v) + t * a.v_st +
+                                          hl * a.v_sh + EPL * i);
   } else {
     uint32_t kw[4] = {}, vw[4] = {};
 #pragma unroll
@@ -295,9 +310,28 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, in
                        a.v)[t * a.v_st + hl * a.v_sh + d * a.v_sd])
                    << (16 * (e % 2));
     }
-    kl = u4_t{kw[0], kw[1], kw[2], kw[3]};
-    vl = u4_t{vw[0], vw[1], vw[2], vw[3]};
+    in.k = u4_t{kw[0], kw[1], kw[2], kw[3]};
+    in.v = u4_t{vw[0], vw[1], vw[2], vw[3]};
   }
+  return in;
+}
+
+template <int D, int F, bool BF16>
+__device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, const Rows& in,
+                                           int h0, u4_t* s_elems, int lane) {
+  constexpr int EPL = 8;            // elements per lane
+  constexpr int LPT = D / EPL;      // lanes per token row
+  constexpr int LPH = kQuad * LPT;  // lanes per head
+  constexpr int E = F == kBits16 ? 2 : 1;  // bytes per stored element
+  constexpr bool Scales = F == kInt8Sym;
+  using L = HeadLayout<D, E, Scales>;
+  using Packed = typename std::conditional<E == 2, u4_t, uint64_t>::type;  // a lane's 8
+  const int hh = lane / LPH, r = lane % LPH / LPT, i = lane % LPT;
+  const int h = h0 + hh;
+  const bool hvalid = h < a.num_kv_heads;
+  const int32_t my_slot = r == 0 ? q.slot[0] : r == 1 ? q.slot[1] : r == 2 ? q.slot[2] : q.slot[3];
+  const u4_t kl = in.k, vl = in.v;
+
   bool ok = my_slot >= 0 && hvalid;
   Packed kc, vc;
   uint16_t skb = 0, svb = 0;
@@ -356,7 +390,9 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, in
       }
     }
   }
-  // (every lane passes the LDS exchange, so that the wave stays together)
+  // (every lane passes the LDS exchange, so that the wave stays together;
+  // the barrier keeps this store after the reads of an earlier span)
+  __builtin_amdgcn_wave_barrier();
   *reinterpret_cast<Packed*>(&s_elems[lane]) = vc;
   __builtin_amdgcn_wave_barrier();
   if (whole) {
@@ -397,30 +433,47 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, in
   }
 }
 
-// One wave per four tokens of the call (boundaries moved to V groups) and
-// 128 / D KV heads; a span that crosses runs of slots takes two rounds.
+// One wave per kSpans spans of about four tokens (boundaries moved to V
+// groups) and 128 / D KV heads. The rows of all its spans are loaded before
+// the first is quantized and stored, so a wave keeps kSpans times the bytes
+// in flight; a span across two runs of slots takes a second round.
 template <int D, int F, bool BF16, bool Vec>
 __global__ __launch_bounds__(64 * kWriteWaves) void write_kernel(WriteArgs a) {
   constexpr int HPW = 128 / D;  // KV heads per wave
+  constexpr int kSpans = spans_per_wave(D, F);
   __shared__ u4_t s_elems[kWriteWaves][64];  // a lane's V elements
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // (wave-uniform, so the slots are scalar loads)
   const int64_t w = static_cast<int64_t>(blockIdx.x) * kWriteWaves + wv;
   const int64_t quads = (a.num_tokens + kQuad - 1) / kQuad;
+  const int64_t groups = (quads + kSpans - 1) / kSpans;
   const int hgroups = (a.num_kv_heads + HPW - 1) / HPW;
-  if (w >= quads * hgroups) return;
-  const int64_t qd = w / hgroups;
-  const int h0 = static_cast<int>(w - qd * hgroups) * HPW;
-  const Span sp = load_span(a, qd, lane);
-  write_quad<D, F, BF16, Vec>(a, quad_of<0>(sp), sp.t0, h0, s_elems[wv], lane);
-  if (sp.n > kQuad)  // a span across two runs of slots
-    write_quad<D, F, BF16, Vec>(a, quad_of<1>(sp), sp.t0 + kQuad, h0, s_elems[wv], lane);
+  if (w >= groups * hgroups) return;
+  const int64_t g = w / hgroups;
+  const int h0 = static_cast<int>(w - g * hgroups) * HPW;
+  Span sp[kSpans];
+  load_spans<kSpans>(a, g * kSpans, lane, sp);
+  Rows in[kSpans];
+#pragma unroll
+  for (int p = 0; p < kSpans; ++p)
+    if (sp[p].n > 0) in[p] = load_rows<D, Vec>(a, quad_of<0>(sp[p]), sp[p].t0, h0, lane);
+#pragma unroll
+  for (int p = 0; p < kSpans; ++p)
+    if (sp[p].n > 0) write_quad<D, F, BF16>(a, quad_of<0>(sp[p]), in[p], h0, s_elems[wv], lane);
+#pragma unroll
+  for (int p = 0; p < kSpans; ++p)
+    if (sp[p].n > kQuad) {  // a span across two runs of slots
+      const Quad q = quad_of<1>(sp[p]);
+      const Rows in1 = load_rows<D, Vec>(a, q, sp[p].t0 + kQuad, h0, lane);
+      write_quad<D, F, BF16>(a, q, in1, h0, s_elems[wv], lane);
+    }
 }
 
-unsigned write_grid(const WriteArgs& a, int heads_per_wave = 1) {
-  const int64_t waves = (a.num_tokens + kQuad - 1) / kQuad *
-                        ((a.num_kv_heads + heads_per_wave - 1) / heads_per_wave);
+unsigned write_grid(const WriteArgs& a, int head_dim, int format) {
+  const int spans = spans_per_wave(head_dim, format), hpw = 128 / head_dim;
+  const int64_t quads = (a.num_tokens + kQuad - 1) / kQuad;
+  const int64_t waves = (quads + spans - 1) / spans * ((a.num_kv_heads + hpw - 1) / hpw);
   return static_cast<unsigned>((waves + kWriteWaves - 1) / kWriteWaves);
 }
 
@@ -436,7 +489,7 @@ bool vec_rows(const WriteArgs& a, int bytes) {
 
 template <int F, bool BF16>
 hipError_t launch_format(const WriteArgs& a, int head_dim, hipStream_t s) {
-  const dim3 grid(write_grid(a, 128 / head_dim)), block(64 * kWriteWaves);
+  const dim3 grid(write_grid(a, head_dim, F)), block(64 * kWriteWaves);
   // lanes load 16 bytes of a row
   const bool vec = vec_rows(a, 16);
   if (head_dim == 128) {
