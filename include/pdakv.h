@@ -175,8 +175,9 @@ size_t pdakv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_he
  *                  skipped; an entry >= num_blocks * block_size is skipped
  *                  and flagged PDAKV_EFLAG_SLOT_RANGE.
  *   kv_pool        device, num_blocks pages of the INT8 format.
- * Two tokens of one call must not name the same slot. Rows whose scale would
- * exceed 65504 are left unwritten and flagged PDAKV_EFLAG_SCALE_RANGE. */
+ * Two tokens of one call must not name the same slot. A (token, KV head)
+ * whose K or V scale would exceed 65504, or whose K or V row holds a NaN or
+ * an infinity, is left unwritten and flagged PDAKV_EFLAG_SCALE_RANGE. */
 int kv_quant_int8_sym_write(const void* k_src, const void* v_src, int src_dtype,
                             int64_t num_tokens, int num_kv_heads, int head_dim,
                             int64_t k_stride_tok, int64_t k_stride_head, int64_t k_stride_dim,

@@ -248,11 +248,15 @@ __device__ __forceinline__ uint64_t codes_static(const u4_t& w, float s, float r
 
 enum WriteFormat { kInt8Sym = 0, kInt8Static = 1, kBits16 = 2 };
 
-// Spans per wave (measured on 262K- and 296K-token prefills): the INT8
-// writers gain 5-8% from three spans' loads in flight at D = 128 (two at
-// D = 64, where more registers cost occupancy); the 16-bit writer, already
-// near the copy rate, is 10% slower with more than one.
+// Spans per wave of a large call (measured on 262K- and 296K-token
+// prefills): the INT8 writers gain 5-8% from three spans' loads in flight at
+// D = 128 (two at D = 64, where more registers cost occupancy); the 16-bit
+// writer, already near the copy rate, is 10% slower with more than one. A
+// call of fewer than kManySpanWaves one-span waves (a decode step's append)
+// keeps one span per wave: its time is one wave's latency, which more spans
+// per wave lengthen (64 tokens: 6 us with one span, 10 us with three).
 constexpr int spans_per_wave(int D, int F) { return F == kBits16 ? 1 : D == 128 ? 3 : 2; }
+constexpr int64_t kManySpanWaves = 2048;
 
 // Write of the K and V rows of up to four consecutive tokens of the call,
 // for HPW = 128 / D KV heads at once: quantize-on-write into INT8 pages
@@ -437,10 +441,9 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, co
 // groups) and 128 / D KV heads. The rows of all its spans are loaded before
 // the first is quantized and stored, so a wave keeps kSpans times the bytes
 // in flight; a span across two runs of slots takes a second round.
-template <int D, int F, bool BF16, bool Vec>
+template <int D, int F, bool BF16, bool Vec, int kSpans>
 __global__ __launch_bounds__(64 * kWriteWaves) void write_kernel(WriteArgs a) {
   constexpr int HPW = 128 / D;  // KV heads per wave
-  constexpr int kSpans = spans_per_wave(D, F);
   __shared__ u4_t s_elems[kWriteWaves][64];  // a lane's V elements
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -470,10 +473,14 @@ __global__ __launch_bounds__(64 * kWriteWaves) void write_kernel(WriteArgs a) {
     }
 }
 
-unsigned write_grid(const WriteArgs& a, int head_dim, int format) {
-  const int spans = spans_per_wave(head_dim, format), hpw = 128 / head_dim;
+// Waves of a call at `spans` spans per wave.
+int64_t write_waves(const WriteArgs& a, int head_dim, int spans) {
+  const int hpw = 128 / head_dim;
   const int64_t quads = (a.num_tokens + kQuad - 1) / kQuad;
-  const int64_t waves = (quads + spans - 1) / spans * ((a.num_kv_heads + hpw - 1) / hpw);
+  return (quads + spans - 1) / spans * ((a.num_kv_heads + hpw - 1) / hpw);
+}
+unsigned write_grid(const WriteArgs& a, int head_dim, int spans) {
+  const int64_t waves = write_waves(a, head_dim, spans);
   return static_cast<unsigned>((waves + kWriteWaves - 1) / kWriteWaves);
 }
 
@@ -487,23 +494,27 @@ bool vec_rows(const WriteArgs& a, int bytes) {
          (reinterpret_cast<uintptr_t>(a.v) % bytes) == 0;
 }
 
+template <int D, int F, bool BF16, int S>
+hipError_t launch_spans(const WriteArgs& a, hipStream_t s) {
+  const dim3 grid(write_grid(a, D, S)), block(64 * kWriteWaves);
+  // lanes load 16 bytes of a row
+  if (vec_rows(a, 16))
+    hipLaunchKernelGGL((write_kernel<D, F, BF16, true, S>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((write_kernel<D, F, BF16, false, S>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int F, bool BF16>
+hipError_t launch_dim(const WriteArgs& a, hipStream_t s) {
+  constexpr int S = spans_per_wave(D, F);
+  if (S > 1 && write_waves(a, D, 1) >= kManySpanWaves) return launch_spans<D, F, BF16, S>(a, s);
+  return launch_spans<D, F, BF16, 1>(a, s);
+}
+
 template <int F, bool BF16>
 hipError_t launch_format(const WriteArgs& a, int head_dim, hipStream_t s) {
-  const dim3 grid(write_grid(a, head_dim, F)), block(64 * kWriteWaves);
-  // lanes load 16 bytes of a row
-  const bool vec = vec_rows(a, 16);
-  if (head_dim == 128) {
-    if (vec)
-      hipLaunchKernelGGL((write_kernel<128, F, BF16, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((write_kernel<128, F, BF16, false>), grid, block, 0, s, a);
-  } else {
-    if (vec)
-      hipLaunchKernelGGL((write_kernel<64, F, BF16, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((write_kernel<64, F, BF16, false>), grid, block, 0, s, a);
-  }
-  return hipGetLastError();
+  return head_dim == 128 ? launch_dim<128, F, BF16>(a, s) : launch_dim<64, F, BF16>(a, s);
 }
 
 }  // namespace

@@ -92,6 +92,38 @@ def test_scale_overflow_is_flagged_and_row_left_unwritten(P):
     assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_non_finite_rows_are_flagged_and_left_unwritten(P, dtype):
+    """A K or V row holding a NaN or an infinity: that (token, KV head) is
+    flagged and left unwritten; every other row is written as the oracle
+    writes it."""
+    rng = np.random.default_rng(5)
+    T, hkv, d = 32, 2, 128
+    k = torch.from_numpy(rng.standard_normal((T, hkv, d)).astype(np.float32)).to(dtype)
+    v = torch.from_numpy(rng.standard_normal((T, hkv, d)).astype(np.float32)).to(dtype)
+    k[3, 1, 7] = float("nan")
+    k[10, 0, 0] = float("inf")
+    v[17, 1, 127] = float("-inf")
+    v[25, 0, 64] = float("nan")
+    bad = {(3, 1), (10, 0), (17, 1), (25, 0)}
+    slots = np.arange(T, dtype=np.int32)
+    pb = P.pdakv_page_bytes(P.KV_INT8_SYM, 16, hkv, d)
+    pool = torch.full((2, pb), FILL, dtype=torch.uint8, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    P.kv_quant_int8_sym_write(k.cuda(), v.cuda(), dev_i32(slots), pool, 2, err_flag=err)
+    assert int(err.item()) == P.EFLAG_SCALE_RANGE
+    want = oracle.new_pool(oracle.KV_INT8_SYM, 2, 16, hkv, d, fill=FILL)
+    for h in range(hkv):
+        keep = np.array([(t, h) not in bad for t in range(T)])
+        kc, ks = oracle.quantize_rows(k[keep][:, h:h + 1])
+        vc, vs = oracle.quantize_rows(v[keep][:, h:h + 1])
+        one = oracle.new_pool(oracle.KV_INT8_SYM, 2, 16, 1, d, fill=FILL)
+        oracle.write_int8_tokens(one, kc, ks, vc, vs, slots[keep], 16)
+        hb = pb // hkv
+        want[:, h * hb:(h + 1) * hb] = one
+    assert np.array_equal(pool.cpu().numpy(), want)
+
+
 def test_subnormal_and_tie_rows(P):
     """Rows whose scales are FP16 subnormals and rows with exact .5 ties."""
     rng = np.random.default_rng(21)
@@ -185,12 +217,12 @@ def test_full_size_write_sampled(P, idx):
             assert np.array_equal(vs[:, 0].view(np.uint16), wvs.view(np.uint16))
 
 
-def _mixed_slots(rng, num_blocks):
+def _mixed_slots(rng, num_blocks, runs=18):
     """Runs of consecutive slots (lengths 1..23, any start offset inside a
     page, one of them reversed) in disjoint ranges, with padding and
     out-of-range entries sprinkled in: every way the writer's four-token
     spans can meet a V group."""
-    starts = rng.permutation(num_blocks * 16 // 32)[:18] * 32
+    starts = rng.permutation(num_blocks * 16 // 32)[:runs] * 32
     runs = []
     for j, st in enumerate(starts):
         n = int(rng.integers(1, 24))
@@ -203,15 +235,18 @@ def _mixed_slots(rng, num_blocks):
 
 
 @pytest.mark.parametrize("kind", ["int8", "static", "16bit"])
-@pytest.mark.parametrize("d,hkv", [(64, 2), (64, 3), (128, 2)])
-def test_write_spans_mixed_runs(P, kind, d, hkv):
+@pytest.mark.parametrize("d,hkv,runs", [(64, 2, 18), (64, 3, 18), (128, 2, 18),
+                                        (64, 3, 3000), (128, 2, 3000)])
+def test_write_spans_mixed_runs(P, kind, d, hkv, runs):
     """Slot runs of every length and page offset, reversed runs, padding and
     out-of-range slots, token count not a multiple of four (and, at D = 64,
     an odd number of KV heads for the two-heads-per-wave INT8 writer): the
-    whole pool equals the oracle's writes of the tokens with valid slots."""
-    rng = np.random.default_rng(30 + d + hkv)
-    nb = 64
-    slots = _mixed_slots(rng, nb)
+    whole pool equals the oracle's writes of the tokens with valid slots.
+    3,000 runs (about 36K tokens) make a call large enough for the INT8
+    writers' several spans per wave; 18 runs keep one."""
+    rng = np.random.default_rng(30 + d + hkv + runs)
+    nb = 64 if runs <= 32 else 4 * runs
+    slots = _mixed_slots(rng, nb, runs)
     T = len(slots)
     k = torch.from_numpy(rng.standard_normal((T, hkv, d)).astype(np.float32)).half()
     v = torch.from_numpy(rng.standard_normal((T, hkv, d)).astype(np.float32) * 3).half()
