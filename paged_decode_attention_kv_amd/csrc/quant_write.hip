@@ -3,8 +3,7 @@
 // One wave (64 lanes) owns one to three consecutive spans of about four
 // tokens of the call (each aligned to the V groups of the pages, below) for
 // one KV head and handles their K and V rows; a workgroup holds four waves.
-// Three
-// pool formats: per-token INT8 (codes + FP16 scales), static-scale INT8
+// Three pool formats: per-token INT8 (codes + FP16 scales), static-scale INT8
 // (codes only) and 16-bit. The row quantizer (quant_row.h) follows
 // MoE-Infinity PR #183 "feat: opt-in INT8 KV-cache quantization" ("What
 // landed", format-contract bullet; "Precision & memory") and the zero-token
@@ -26,7 +25,6 @@ namespace {
 
 constexpr int kWriteWaves = 4;
 constexpr int kQuad = 4;  // tokens per span: one V group of the page layout
-
 
 // Head block of a page: element size E (1: INT8 codes, 2: 16-bit values), K
 // rows at pos * D elements, V grouped four tokens at a time from 16 * D
@@ -258,27 +256,6 @@ enum WriteFormat { kInt8Sym = 0, kInt8Static = 1, kBits16 = 2 };
 constexpr int spans_per_wave(int D, int F) { return F == kBits16 ? 1 : D == 128 ? 3 : 2; }
 constexpr int64_t kManySpanWaves = 2048;
 
-// Write of the K and V rows of up to four consecutive tokens of the call,
-// for HPW = 128 / D KV heads at once: quantize-on-write into INT8 pages
-// (kInt8Sym: per-token scales; kInt8Static: the layer's scales) or a plain
-// copy into 16-bit pages (kBits16). Every lane holds 8 elements of one row:
-// lane (head hh, token r, i) holds elements 8i .. 8i+7 of token r's rows of
-// KV head h0 + hh (LPT = D / 8 lanes per token), so a row's absolute
-// maximum is an LPT-lane reduction and the per-row scale work of all the
-// wave's rows shares instructions. The per-row rules (MoE-Infinity PR #183
-// "feat: opt-in INT8 KV-cache quantization", "What landed", format-contract
-// bullet; zero rows per mlxcel PR #717 "The Int8 bug and fix"; static scales
-// per InfiniLM PR #553 "Summary"):
-//   per-token: a = max|x|; s = 1.0 if a == 0 else the smallest FP16 >=
-//   fl32(a/127); code = clamp(rint(fl32(x / s)), -127, 127);
-//   static: code = clamp(rint(fl32(x / scale)), -127, 127).
-// A token with a negative slot is padding (skipped); an out-of-range slot or
-// a per-token scale beyond FP16 is flagged and that (token, head) is left
-// unwritten. K rows are stored per token (8 contiguous elements per lane).
-// When the four tokens are one whole V group of a head, the elements go
-// through LDS to become group words (one dimension of the four tokens) and
-// every lane stores two whole words; otherwise each token's V elements are
-// stored one by one.
 // A lane's 8 raw 16-bit K and V elements.
 struct Rows {
   u4_t k, v;
@@ -320,6 +297,27 @@ __device__ __forceinline__ Rows load_rows(const WriteArgs& a, const Quad& q, int
   return in;
 }
 
+// Write of the K and V rows (loaded by load_rows) of up to four consecutive
+// tokens of the call, for HPW = 128 / D KV heads at once: quantize-on-write
+// into INT8 pages (kInt8Sym: per-token scales; kInt8Static: the layer's
+// scales) or a plain copy into 16-bit pages (kBits16). Every lane holds 8
+// elements of one row: lane (head hh, token r, i) holds elements 8i .. 8i+7
+// of token r's rows of KV head h0 + hh (LPT = D / 8 lanes per token), so a
+// row's absolute maximum is an LPT-lane reduction and the per-row scale work
+// of all the wave's rows shares instructions. The per-row rules (MoE-Infinity
+// PR #183 "feat: opt-in INT8 KV-cache quantization", "What landed",
+// format-contract bullet; zero rows per mlxcel PR #717 "The Int8 bug and
+// fix"; static scales per InfiniLM PR #553 "Summary"):
+//   per-token: a = max|x|; s = 1.0 if a == 0 else the smallest FP16 >=
+//   fl32(a/127); code = clamp(rint(fl32(x / s)), -127, 127);
+//   static: code = clamp(rint(fl32(x / scale)), -127, 127).
+// A token with a negative slot is padding (skipped); an out-of-range slot, a
+// per-token scale beyond FP16 or a NaN or infinity in a row (per-token
+// format) is flagged and that (token, head) is left unwritten. K rows are
+// stored per token (8 contiguous elements per lane). When the four tokens
+// are one whole V group of a head, the elements go through LDS to become
+// group words (one dimension of the four tokens) and every lane stores two
+// whole words; otherwise each token's V elements are stored one by one.
 template <int D, int F, bool BF16>
 __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, const Rows& in,
                                            int h0, u4_t* s_elems, int lane) {
