@@ -8,8 +8,8 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_util import (FILL, MAX_ABS_TOL, dev_i32, oracle_decode, oracle_pool, require_gpu,
-                            to_dev)
+from tests.gpu_util import (FILL, MAX_ABS_TOL, dev_i32, oracle_decode, oracle_pair_from_sources,
+                            oracle_pool, require_gpu, to_dev)
 from workloads import build, make_config
 
 pytestmark = pytest.mark.gpu
@@ -95,3 +95,47 @@ def test_fused_append_then_plain_decode_agree(P):
                              wl.sm_scale, ws)
     torch.cuda.synchronize()
     assert torch.equal(out, again)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("fmt_name", ["int8", "16bit"])
+def test_full_size_fused_append_sampled(P, fmt_name):
+    """The batched step at full size (64 sequences, contexts 1K-8K, shuffled
+    pages) in the launch shape the bench times: the fused append + decode
+    call. Sampled sequences' newest tokens are read back from the pool and
+    compared with the oracle's codes and scales (INT8) or the source values
+    (16-bit), and sampled output rows with the oracle's attention over each
+    sequence's source K/V, newest token included."""
+    fmt = P.KV_INT8_SYM if fmt_name == "int8" else P.KV_16BIT
+    wl = make_config(3)
+    _say(f"full-size fused append {fmt_name}: {wl.num_seqs} seqs, max ctx {wl.max_context_len}")
+    out, pool = _fused(P, wl, fmt)
+    out = out.cpu().numpy()
+    assert not np.isnan(out).any()
+    host = pool.cpu().numpy()
+    last = wl.phases[-1]
+    rng = np.random.default_rng(17)
+    seqs = rng.choice(wl.num_seqs, 4, replace=False)
+    for b in seqs:
+        L = int(wl.context_lens[b])
+        if fmt == P.KV_INT8_SYM:
+            kc, ks, vc, vs = oracle.gather_int8_sequence(host, wl.block_tables[b], L, 16,
+                                                         wl.num_kv_heads, wl.head_dim)
+            wkc, wks = oracle.quantize_rows(last.k[b])
+            wvc, wvs = oracle.quantize_rows(last.v[b])
+            assert np.array_equal(kc[L - 1], wkc) and np.array_equal(vc[L - 1], wvc)
+            assert np.array_equal(ks[L - 1].view(np.uint16), wks.view(np.uint16))
+            assert np.array_equal(vs[L - 1].view(np.uint16), wvs.view(np.uint16))
+        else:
+            k16, v16 = oracle.gather_16bit_sequence(host, wl.block_tables[b], L, 16,
+                                                    wl.num_kv_heads, wl.head_dim)
+            assert np.array_equal(k16[L - 1], last.k[b].view(torch.int16).numpy().view(np.uint16))
+            assert np.array_equal(v16[L - 1], last.v[b].view(torch.int16).numpy().view(np.uint16))
+    worst = 0.0
+    for b in seqs:
+        for h in rng.choice(wl.num_q_heads, 3, replace=False):
+            want = oracle_pair_from_sources(wl, int(b), int(h), oracle.KV_INT8_SYM if
+                                            fmt == P.KV_INT8_SYM else oracle.KV_16BIT)
+            worst = max(worst, float(np.max(np.abs(out[b, h] - want))))
+    _say(f"  worst sampled max abs diff {worst:.3e}")
+    assert worst <= MAX_ABS_TOL
