@@ -279,3 +279,56 @@ def test_write_spans_mixed_runs(P, kind, d, hkv, runs):
     got = pool.cpu().numpy()
     bad = np.nonzero(got != want)
     assert bad[0].size == 0, f"{bad[0].size} bytes differ, first at page {bad[0][0]} byte {bad[1][0]}"
+
+
+@pytest.mark.parametrize("kind", ["int8", "static", "16bit"])
+@pytest.mark.parametrize("layout,T", [("dim-major", 200), ("dim-major", 9000),
+                                      ("offset", 9000)])
+def test_write_element_strided_sources(P, kind, layout, T):
+    """K/V sources that need element-by-element loads: views with the head
+    dimension not innermost (element stride = number of heads), or
+    contiguous rows starting one element past a 16-byte boundary; small
+    calls and calls large enough for several spans per wave. Pools
+    bit-exact with the oracle's writes of the same values."""
+    rng = np.random.default_rng(61 + T)
+    hkv, d = 2, 128
+    if layout == "dim-major":
+        kb = torch.from_numpy(rng.standard_normal((T, d, hkv)).astype(np.float32)).half()
+        vb = torch.from_numpy(rng.standard_normal((T, d, hkv)).astype(np.float32) * 2).half()
+        k, v = kb.cuda().permute(0, 2, 1), vb.cuda().permute(0, 2, 1)
+        assert k.stride(2) == hkv
+    else:
+        flat_k = torch.from_numpy(rng.standard_normal(T * hkv * d + 1).astype(np.float32)).half()
+        flat_v = torch.from_numpy(rng.standard_normal(T * hkv * d + 1).astype(np.float32)).half()
+        k = flat_k.cuda()[1:].view(T, hkv, d)
+        v = flat_v.cuda()[1:].view(T, hkv, d)
+    nb = (T + 15) // 16 + 3
+    slots = rng.permutation(nb * 16)[:T].astype(np.int32)
+    slots[: T // 2] = np.sort(slots[: T // 2])  # runs of consecutive slots too
+    fmt = {"int8": P.KV_INT8_SYM, "static": P.KV_INT8_STATIC, "16bit": P.KV_16BIT}[kind]
+    ofmt = {"int8": oracle.KV_INT8_SYM, "static": oracle.KV_INT8_STATIC,
+            "16bit": oracle.KV_16BIT}[kind]
+    pool = torch.full((nb, P.pdakv_page_bytes(fmt, 16, hkv, d)), FILL, dtype=torch.uint8,
+                      device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _say(f"element-strided {kind} {layout}: {T} tokens")
+    kh, vh = k.cpu(), v.cpu()
+    want = oracle.new_pool(ofmt, nb, 16, hkv, d, fill=FILL)
+    ks, vs = 0.02, 0.05
+    if kind == "int8":
+        P.kv_quant_int8_sym_write(k, v, dev_i32(slots), pool, nb, err_flag=err)
+        kc, kss = oracle.quantize_rows(kh)
+        vc, vss = oracle.quantize_rows(vh)
+        oracle.write_int8_tokens(want, kc, kss, vc, vss, slots, 16)
+    elif kind == "static":
+        P.kv_quant_int8_static_write(k, v, dev_i32(slots), pool, nb, ks, vs, err_flag=err)
+        oracle.write_int8_static_tokens(want, oracle.quantize_static(kh, ks),
+                                        oracle.quantize_static(vh, vs), slots, 16)
+    else:
+        P.kv_write_16bit(k, v, dev_i32(slots), pool, nb, err_flag=err)
+        oracle.write_16bit_tokens(want, bits16(kh), bits16(vh), slots, 16)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    got = pool.cpu().numpy()
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, f"{bad[0].size} bytes differ, first at page {bad[0][0]} byte {bad[1][0]}"
