@@ -1,6 +1,8 @@
 // Per-token symmetric INT8 quantizer of one row (D elements spread over the
-// 64 lanes of a wave), shared by the quantize-on-write kernel and the decode
-// kernel's append step so that both store bit-identical codes and scales.
+// 64 lanes of a wave), as the decode kernel's append step uses it. The
+// quantize-on-write kernel shares round_up_f16 (and row_code for static
+// scales outside its division-free window) and computes the same scale and
+// codes without a division, so both store bit-identical rows.
 //
 // MoE-Infinity PR #183 "feat: opt-in INT8 KV-cache quantization" ("What
 // landed", format-contract bullet; "Precision & memory") and the zero-token
