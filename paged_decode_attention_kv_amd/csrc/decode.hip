@@ -468,22 +468,27 @@ struct Int8Kind {
   // Fused append, first half: quantize the newest token's K and V rows of
   // (b, g) with the quantize-on-write rule into nt ([D] K codes, [D] V codes,
   // K scale, V scale) for patch() and store_new(). False when a scale would
-  // exceed FP16 (flagged; the slot is then left as it was, as the separate
-  // write leaves it).
+  // exceed FP16 or a row holds a NaN or an infinity (flagged; the slot is
+  // then left as it was, as the separate write leaves it).
   static __device__ __forceinline__ bool prepare_new(const DecodeArgs& a, int b, int g,
                                                      uint8_t* nt, int lane) {
     constexpr int EPL = D / 64;
     float xk[EPL], xv[EPL];
-    float ak = 0.f, av = 0.f;
+    // row maxima as 16-bit magnitude patterns (sign bit cleared): FP16 and
+    // BF16 magnitudes order like unsigned integers, with a NaN above the
+    // infinity, so a NaN or an infinity reaches the scale check
+    uint32_t mk = 0, mv = 0;
     const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
     const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const int64_t d = lane * EPL + e;
-      xk[e] = bits16_to_f32<QBF16>(kn[b * a.kn_st + g * a.kn_sh + d * a.kn_sd]);
-      xv[e] = bits16_to_f32<QBF16>(vn[b * a.vn_st + g * a.vn_sh + d * a.vn_sd]);
-      ak = fmaxf(ak, fabsf(xk[e]));
-      av = fmaxf(av, fabsf(xv[e]));
+      const uint16_t kbits = kn[b * a.kn_st + g * a.kn_sh + d * a.kn_sd];
+      const uint16_t vbits = vn[b * a.vn_st + g * a.vn_sh + d * a.vn_sd];
+      xk[e] = bits16_to_f32<QBF16>(kbits);
+      xv[e] = bits16_to_f32<QBF16>(vbits);
+      mk = max(mk, static_cast<uint32_t>(kbits & 0x7FFFu));
+      mv = max(mv, static_cast<uint32_t>(vbits & 0x7FFFu));
     }
     if constexpr (Static) {
       // the layer's scales: nothing can overflow
@@ -495,8 +500,8 @@ struct Int8Kind {
       }
       return true;
     }
-    ak = wave_max(ak);
-    av = wave_max(av);
+    const float ak = bits16_to_f32<QBF16>(static_cast<uint16_t>(wave_max_u32(mk)));
+    const float av = bits16_to_f32<QBF16>(static_cast<uint16_t>(wave_max_u32(mv)));
     uint16_t skb, svb;
     const bool okk = row_scale(ak, skb), okv = row_scale(av, svb);
     if (!okk || !okv) {

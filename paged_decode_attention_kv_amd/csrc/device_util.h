@@ -67,6 +67,12 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), o)));
+  return x;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);

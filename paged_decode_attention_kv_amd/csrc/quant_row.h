@@ -28,10 +28,10 @@ __device__ __forceinline__ uint16_t round_up_f16(float s) {
 }
 
 // Scale of a row with absmax a (already reduced over the wave): false when
-// a/127 exceeds the FP16 range (the row cannot be stored).
+// a/127 exceeds the FP16 range or a is not finite (the row cannot be stored).
 __device__ __forceinline__ bool row_scale(float a, uint16_t& bits) {
   const float s32 = a / 127.0f;
-  if (s32 > 65504.0f) return false;
+  if (!(s32 <= 65504.0f)) return false;
   bits = a == 0.f ? 0x3C00 : round_up_f16(s32);
   return true;
 }

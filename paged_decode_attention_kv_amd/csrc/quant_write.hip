@@ -217,8 +217,10 @@ __device__ __forceinline__ uint64_t codes_token(const u4_t& w, float s, float re
 // x - q0 s is exact in an fma, and q0 + residual * r rounds to fl32(x / s)
 // (Markstein's theorem for a correctly rounded reciprocal; also checked
 // against IEEE division for every FP16 and BF16 x over scales across the
-// window). BF16 values are first clamped to +-128 s, which keeps every code
-// and keeps x r finite; FP16 values cannot overflow it. The clamped quotient
+// window). Values are first clamped to +-128 s, which keeps every finite
+// value's code and keeps x r finite: an infinity then saturates to +-127 as
+// the division would, and a NaN (which the clamp turns into -128 s) gives
+// -127, the code the division-based rule gives it too. The clamped quotient
 // plus 1.5 * 2^23 rounds to nearest even, and its low byte is the code.
 __device__ __forceinline__ bool static_window(float s) {
   return s >= 0x1p-64f && s <= 0x1p64f;
@@ -232,7 +234,7 @@ __device__ __forceinline__ uint64_t codes_static(const u4_t& w, float s, float r
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float x = bits16_to_f32<BF16>(static_cast<uint16_t>(w[e / 2] >> (16 * (e % 2))));
-    if constexpr (BF16) x = fminf(fmaxf(x, -lim), lim);
+    x = fminf(fmaxf(x, -lim), lim);
     const float q0 = fmaf(x, r, 0.0f);
     const float q1 = fmaf(fmaf(-q0, s, x), r, q0);
     f[e] = __float_as_uint(fminf(fmaxf(q1, -127.0f), 127.0f) + kMagic);

@@ -205,30 +205,54 @@ def test_static_fused_append_matches_write_then_decode(P, idx, scale):
     assert torch.equal(out, again)
 
 
-def test_static_full_size_sampled(P):
-    """Batched step at full size in the launch shape the bench times: the
-    pool of a sample of sequences and a sample of (sequence, head) rows
-    against the oracle."""
-    wl = make_config(3)
-    ks, vs = calibrated_scales(wl)
-    pool = _gpu_static_pool(P, wl, ks, vs)
-    out = _gpu_static_decode(P, wl, pool, ks, vs)
-    rng = np.random.default_rng(0)
-    pairs = [(int(b), int(h)) for b, h in zip(rng.integers(0, wl.num_seqs, 12),
-                                               rng.integers(0, wl.num_q_heads, 12))]
-    # oracle pool of just the sampled sequences' tokens (same slots)
-    host = oracle.new_pool(oracle.KV_INT8_STATIC, wl.num_blocks, 16, wl.num_kv_heads,
-                           wl.head_dim, fill=FILL)
-    seqs = sorted({b for b, _ in pairs})
-    for ph in wl.phases:
-        rows = np.concatenate([np.arange(ph.seq_rows(b).start, ph.seq_rows(b).stop)
-                               for b in seqs])
-        oracle.write_int8_static_tokens(host, oracle.quantize_static(ph.k[rows], ks),
-                                        oracle.quantize_static(ph.v[rows], vs),
-                                        ph.slot_mapping[rows], 16)
-    gp = pool.cpu().numpy()
-    for b in seqs:
-        blocks = wl.block_tables[b, :-(-int(wl.context_lens[b]) // 16)]
-        assert np.array_equal(gp[blocks], host[blocks]), b
-    want = _oracle_decode(wl, host, ks, vs, pairs=pairs)
-    assert _max_diff(out, want) <= MAX_ABS_TOL
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_static_non_finite_inputs(P, dtype):
+    """Infinities saturate to +-127 and a NaN is stored as -127 (the clamp of
+    the division rule ignores a NaN operand), in the static writer and in the
+    static fused append alike. The oracle takes finite inputs only, so the
+    codes of the non-finite elements are pinned here by hand; the finite ones
+    come from the oracle."""
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    hq, hkv, d = 8, 2, 128
+    ks, vs = 0.0390625, 0.0123457
+    wl = build("nonfinite", 61, [("prefill", [5, 37]), ("append", [1, 1])], hq, hkv, d, dtype,
+               "normal", shuffle=True, spare_blocks=1)
+    last = wl.phases[-1]
+    special = {3: float("inf"), 17: float("-inf"), 40: float("nan"), 99: float("nan")}
+    want_code = {3: 127, 17: -127, 40: -127, 99: -127}
+    for t in (last.k, last.v):
+        for pos, val in special.items():
+            t[:, :, pos] = val
+    # pinned codes of the new rows: the oracle on the finite elements, then
+    # the hand-pinned non-finite ones
+    def pinned(x, s):
+        clean = x.float().clone()
+        clean[~torch.isfinite(clean)] = 0.0
+        c = oracle.quantize_static(clean.to(tdt), s).copy()
+        for pos, code in want_code.items():
+            c[..., pos] = code
+        return c
+    want_k, want_v = pinned(last.k, ks), pinned(last.v, vs)
+    for route in ("writer", "fused"):
+        _say(f"static non-finite {dtype}: {route}")
+        pool = _gpu_static_pool(P, wl, ks, vs, phases=wl.phases[:-1])
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        if route == "writer":
+            P.kv_quant_int8_static_write(to_dev(last.k), to_dev(last.v),
+                                         dev_i32(last.slot_mapping), pool, wl.num_blocks, ks, vs,
+                                         err_flag=err)
+        else:
+            out = torch.empty((wl.num_seqs, hq, d), dtype=torch.float32, device="cuda")
+            ws = P.alloc_workspace(wl.num_seqs, hq, hkv, d, wl.max_context_len)
+            P.paged_attn_decode_int8_static_append(
+                out, to_dev(wl.q), to_dev(last.k), to_dev(last.v), pool, wl.num_blocks,
+                dev_i32(wl.block_tables), dev_i32(wl.context_lens), hkv, wl.max_context_len,
+                wl.sm_scale, ks, vs, ws, err_flag=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0  # saturation is part of the scheme: nothing flagged
+        host = pool.cpu().numpy()
+        for b in range(wl.num_seqs):
+            L = int(wl.context_lens[b])
+            kc, vc = oracle.gather_int8_static_sequence(host, wl.block_tables[b], L, 16, hkv, d)
+            assert np.array_equal(kc[L - 1], want_k[b]), (route, b)
+            assert np.array_equal(vc[L - 1], want_v[b]), (route, b)
