@@ -163,6 +163,16 @@ int pdakv_decode_plan(int kv_format, int num_seqs, int num_kv_heads, int max_con
 size_t pdakv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                     int head_dim, int max_context_len);
 
+/* Device workspace of the decode calls for any KV-head count: the largest
+ * pdakv_decode_workspace_bytes() over every num_kv_heads that divides
+ * num_q_heads with at most 16 query heads per KV head (0 when num_seqs,
+ * max_context_len or num_q_heads is 0, or no such count exists). For callers
+ * that size one workspace before the KV-head count is known; a workspace of
+ * this size serves every one-token decode entry point with these sizes. Host
+ * arithmetic only. */
+size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
+                                         int max_context_len);
+
 /* Quantize-on-write (MoE-Infinity PR #183, "What landed": write_chunk into
  * the paged store; the quantizer of the format-contract bullet).
  *   k_src, v_src   device, [num_tokens][num_kv_heads][head_dim] of src_dtype
@@ -185,9 +195,13 @@ int kv_quant_int8_sym_write(const void* k_src, const void* v_src, int src_dtype,
                             const int32_t* slot_mapping, void* kv_pool, int64_t num_blocks,
                             int block_size, int32_t* err_flag, void* stream);
 
-/* Plain 16-bit write into a PDAKV_KV_16BIT pool (fills the control cache);
- * same arguments and conventions as kv_quant_int8_sym_write, values copied
- * unchanged. */
+/* Plain 16-bit write into a PDAKV_KV_16BIT pool: fills the cache of the
+ * FP16-KV control, whose pages hold the model-precision values, 65,536 bytes
+ * per (block 16, 8 KV heads, head_dim 128) page (MoE-Infinity PR #183,
+ * "Precision & memory"; the pre-existing FP16 paged cache of "What landed").
+ * Same arguments and conventions as kv_quant_int8_sym_write; values are
+ * copied unchanged (no scale, so nothing is flagged for range), in the
+ * 16-bit page layout above. */
 int kv_write_16bit(const void* k_src, const void* v_src, int src_dtype,
                    int64_t num_tokens, int num_kv_heads, int head_dim,
                    int64_t k_stride_tok, int64_t k_stride_head, int64_t k_stride_dim,
@@ -254,8 +268,9 @@ int paged_attn_decode_fp16(void* out, int out_dtype, int64_t out_stride_seq,
  *                  sequence b's newest token. Other arguments as
  *                  paged_attn_decode_int8.
  * A sequence with context length 0 gets zero rows and no write. A row whose
- * scale would exceed 65504 is flagged PDAKV_EFLAG_SCALE_RANGE and not written
- * (the slot keeps its old contents, which the attention then reads). With an
+ * scale would exceed 65504, or that holds a NaN or an infinity, is flagged
+ * PDAKV_EFLAG_SCALE_RANGE and not written, as kv_quant_int8_sym_write treats
+ * it (the slot keeps its old contents, which the attention then reads). With an
  * out-of-range context length (flagged) the token is written at the clamped
  * length's last position. */
 int paged_attn_decode_int8_append(
@@ -290,7 +305,9 @@ int paged_attn_decode_fp16_append(
  *                      and > 0, else PDAKV_ERR_INVALID_ARG.
  * kv_pool is a PDAKV_KV_INT8_STATIC pool. Every element gets
  * clamp(round_half_even(fl32(x / scale)), -127, 127); nothing is flagged for
- * saturation (it is part of the scheme). */
+ * saturation (it is part of the scheme). Non-finite inputs: +inf gives 127,
+ * -inf gives -127 and a NaN gives -127 (the clamp ignores a NaN operand);
+ * paged_attn_decode_int8_static_append stores the same codes. */
 int kv_quant_int8_static_write(const void* k_src, const void* v_src, int src_dtype,
                                int64_t num_tokens, int num_kv_heads, int head_dim,
                                int64_t k_stride_tok, int64_t k_stride_head, int64_t k_stride_dim,

@@ -41,6 +41,7 @@ from ._lib import (  # noqa: F401
     paged_attn_decode_int8_multi,
     paged_attn_decode_int8_static,
     paged_attn_decode_int8_static_append,
+    paged_attn_decode_workspace_bytes,
     pdakv_capabilities,
     pdakv_decode_plan,
     pdakv_decode_multi_workspace_bytes,

@@ -46,6 +46,7 @@ _SIGS = {
     "pdakv_decode_plan": (_c_int, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_int),
                                    ctypes.POINTER(_c_int)]),
     "pdakv_decode_workspace_bytes": (ctypes.c_size_t, [_c_int] * 5),
+    "paged_attn_decode_workspace_bytes": (ctypes.c_size_t, [_c_int] * 4),
     "kv_quant_int8_sym_write": (_c_int, [_c_vp, _c_vp, _c_int, _c_i64, _c_int, _c_int] +
                                 [_c_i64] * 6 + [_c_vp, _c_vp, _c_i64, _c_int, _c_vp, _c_vp]),
     "kv_write_16bit": (_c_int, [_c_vp, _c_vp, _c_int, _c_i64, _c_int, _c_int] +
@@ -109,6 +110,82 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+# ---- argument checks (raise ValueError before anything reaches the library) --
+# The C entry points take raw pointers; these checks keep a wrong dtype,
+# device, layout or size from being read as something else on the device
+# (an int64 slot_mapping read as int32 pairs, an undersized pool written
+# past its end).
+
+def _need_int32(name, t, numel=None):
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} entries, needs {numel}")
+
+
+def _need_gpu(name, t):
+    if t is not None and not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _need_block_tables(bt, num_seqs):
+    if bt.dtype != torch.int32:
+        raise ValueError(f"block_tables must be int32, got {bt.dtype}")
+    if not bt.is_cuda:
+        raise ValueError("block_tables must be a GPU tensor")
+    if bt.dim() != 2 or bt.stride(1) != 1:
+        raise ValueError("block_tables must be 2-D with unit stride along a row")
+    if bt.shape[0] < num_seqs:
+        raise ValueError(f"block_tables has {bt.shape[0]} rows, needs {num_seqs}")
+
+
+def _need_pool(kv_pool, num_blocks, page_bytes):
+    if not kv_pool.is_cuda:
+        raise ValueError("kv_pool must be a GPU tensor")
+    if not kv_pool.is_contiguous():
+        raise ValueError("kv_pool must be contiguous")
+    if num_blocks < 0:
+        raise ValueError("num_blocks must be >= 0")
+    have = kv_pool.numel() * kv_pool.element_size()
+    if page_bytes <= 0 or have < num_blocks * page_bytes:
+        raise ValueError(f"kv_pool holds {have} bytes, {num_blocks} pages need "
+                         f"{num_blocks * max(page_bytes, 0)}")
+
+
+def _need_err_flag(err_flag):
+    if err_flag is not None:
+        _need_int32("err_flag", err_flag, 1)
+
+
+_WRITE_FORMAT = {"kv_quant_int8_sym_write": KV_INT8_SYM, "kv_write_16bit": KV_16BIT,
+                 "kv_quant_int8_static_write": KV_INT8_STATIC}
+_DECODE_FORMAT = {"paged_attn_decode_int8": KV_INT8_SYM, "paged_attn_decode_fp16": KV_16BIT,
+                  "paged_attn_decode_int8_static": KV_INT8_STATIC,
+                  "paged_attn_decode_int8_append": KV_INT8_SYM,
+                  "paged_attn_decode_fp16_append": KV_16BIT,
+                  "paged_attn_decode_int8_static_append": KV_INT8_STATIC,
+                  "paged_attn_decode_int8_multi": KV_INT8_SYM,
+                  "paged_attn_decode_fp16_multi": KV_16BIT,
+                  "paged_attn_decode_int8_noalloc": KV_INT8_SYM}
+
+
+def _check_decode_args(fn_name, out, q, kv_pool, num_blocks, block_tables, context_lens,
+                       num_kv_heads, head_dim, block_size, workspace, err_flag):
+    B = q.shape[0]
+    _need_block_tables(block_tables, B)
+    _need_int32("context_lens", context_lens, B)
+    _need_gpu("q", q)
+    _need_gpu("out", out)
+    _need_pool(kv_pool, num_blocks, pdakv_page_bytes(_DECODE_FORMAT[fn_name], block_size,
+                                                    num_kv_heads, head_dim))
+    _need_gpu("workspace", workspace)
+    _need_err_flag(err_flag)
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -150,6 +227,13 @@ def pdakv_decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: 
                                                  max_context_len))
 
 
+def paged_attn_decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
+                                      max_context_len: int) -> int:
+    """Workspace of the one-token decode calls for any KV-head count."""
+    return int(_lib.paged_attn_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                      max_context_len))
+
+
 def pdakv_decode_multi_workspace_bytes(num_seqs: int, num_query_tokens: int, num_q_heads: int,
                                        num_kv_heads: int, head_dim: int,
                                        max_context_len: int) -> int:
@@ -164,6 +248,11 @@ def _write(fn_name, k, v, slot_mapping, kv_pool, num_blocks, block_size, err_fla
     T, hkv, d = k.shape
     if tuple(v.shape) != (T, hkv, d) or v.dtype != k.dtype:
         raise ValueError("k and v must have the same shape and dtype")
+    _need_int32("slot_mapping", slot_mapping, T)
+    _need_gpu("k", k)
+    _need_gpu("v", v)
+    _need_pool(kv_pool, num_blocks, pdakv_page_bytes(_WRITE_FORMAT[fn_name], block_size, hkv, d))
+    _need_err_flag(err_flag)
     st = getattr(_lib, fn_name)(
         _ptr(k), _ptr(v), _dtype_code(k.dtype), T, hkv, d,
         k.stride(0), k.stride(1), k.stride(2), v.stride(0), v.stride(1), v.stride(2),
@@ -193,6 +282,8 @@ def _decode(fn_name, out, q, kv_pool, num_blocks, block_tables, context_lens, nu
         raise ValueError("the head_dim stride of q and out must be 1")
     if tuple(out.shape) != (B, hq, d):
         raise ValueError("out must have the shape of q")
+    _check_decode_args(fn_name, out, q, kv_pool, num_blocks, block_tables, context_lens,
+                       num_kv_heads, d, block_size, workspace, err_flag)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = getattr(_lib, fn_name)(
         _ptr(out), _dtype_code(out.dtype), out.stride(0), out.stride(1),
@@ -233,6 +324,10 @@ def _decode_append(fn_name, out, q, k_new, v_new, kv_pool, num_blocks, block_tab
         raise ValueError("k_new and v_new must be [num_seqs, num_kv_heads, head_dim]")
     if k_new.dtype != q.dtype or v_new.dtype != q.dtype:
         raise ValueError("k_new and v_new must have q's dtype")
+    _need_gpu("k_new", k_new)
+    _need_gpu("v_new", v_new)
+    _check_decode_args(fn_name, out, q, kv_pool, num_blocks, block_tables, context_lens,
+                       num_kv_heads, d, block_size, workspace, err_flag)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = getattr(_lib, fn_name)(
         _ptr(out), _dtype_code(out.dtype), out.stride(0), out.stride(1),
@@ -309,6 +404,8 @@ def _decode_multi(fn_name, out, q, kv_pool, num_blocks, block_tables, context_le
         raise ValueError("the head_dim stride of q and out must be 1")
     if tuple(out.shape) != (B, T, hq, d):
         raise ValueError("out must have the shape of q")
+    _check_decode_args(fn_name, out, q, kv_pool, num_blocks, block_tables, context_lens,
+                       num_kv_heads, d, block_size, workspace, err_flag)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = getattr(_lib, fn_name)(
         _ptr(out), _dtype_code(out.dtype), out.stride(0), out.stride(1), out.stride(2),
@@ -348,6 +445,13 @@ def kv_pages_swap_out(kv_pool, num_blocks: int, block_ids, dst, err_flag=None,
     uint8, device or pinned host memory)."""
     n = block_ids.numel()
     pb = kv_pool.shape[1]
+    _need_int32("block_ids", block_ids)
+    _need_pool(kv_pool, num_blocks, pb)
+    _need_err_flag(err_flag)
+    if not (dst.is_cuda or dst.is_pinned()):
+        raise ValueError("dst must be GPU memory or pinned host memory")
+    if not dst.is_contiguous():
+        raise ValueError("dst must be contiguous")
     if dst.numel() * dst.element_size() < n * pb:
         raise ValueError("dst is too small")
     _check("kv_pages_swap_out", _lib.kv_pages_swap_out(
@@ -361,6 +465,13 @@ def kv_pages_swap_in(src, block_ids, kv_pool, num_blocks: int, err_flag=None,
     page block_ids[i] of the pool."""
     n = block_ids.numel()
     pb = kv_pool.shape[1]
+    _need_int32("block_ids", block_ids)
+    _need_pool(kv_pool, num_blocks, pb)
+    _need_err_flag(err_flag)
+    if not (src.is_cuda or src.is_pinned()):
+        raise ValueError("src must be GPU memory or pinned host memory")
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
     if src.numel() * src.element_size() < n * pb:
         raise ValueError("src is too small")
     _check("kv_pages_swap_in", _lib.kv_pages_swap_in(
@@ -374,6 +485,14 @@ def kv_trim_keep_sink(kv_format: int, kv_pool, num_blocks: int, num_kv_heads: in
                       stream=None) -> None:
     """Drop trim_lens[b] tokens after the first `keep` of every sequence, in
     place; writes the new lengths to new_context_lens."""
+    B = context_lens.numel()
+    _need_int32("context_lens", context_lens)
+    _need_int32("trim_lens", trim_lens, B)
+    _need_int32("new_context_lens", new_context_lens, B)
+    _need_block_tables(block_tables, B)
+    _need_pool(kv_pool, num_blocks, pdakv_page_bytes(kv_format, block_size, num_kv_heads,
+                                                    head_dim))
+    _need_err_flag(err_flag)
     _check("kv_trim_keep_sink", _lib.kv_trim_keep_sink(
         kv_format, _ptr(kv_pool), num_blocks, block_size, num_kv_heads, head_dim,
         _ptr(block_tables), block_tables.stride(0), _ptr(context_lens), _ptr(trim_lens),

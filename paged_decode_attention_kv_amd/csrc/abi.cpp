@@ -450,6 +450,20 @@ size_t pdakv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_he
   return decode_ws_bytes(num_seqs, 1, num_q_heads, num_kv_heads, head_dim, max_context_len);
 }
 
+size_t paged_attn_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
+                                         int max_context_len) {
+  // the largest workspace over every KV-head count this query-head count
+  // allows (num_kv_heads divides num_q_heads, at most 16 query heads each)
+  if (num_q_heads <= 0) return 0;
+  size_t need = 0;
+  for (int hkv = 1; hkv <= num_q_heads; ++hkv) {
+    if (num_q_heads % hkv != 0 || num_q_heads / hkv > pdakv::kMaxGroup) continue;
+    need = std::max(need, decode_ws_bytes(num_seqs, 1, num_q_heads, hkv, head_dim,
+                                          max_context_len));
+  }
+  return need;
+}
+
 size_t pdakv_decode_multi_workspace_bytes(int num_seqs, int num_query_tokens, int num_q_heads,
                                           int num_kv_heads, int head_dim,
                                           int max_context_len) {

@@ -27,10 +27,57 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function(P):
     names = _declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(P._lib, n), n
     assert set(names) == set(P.EXPORTED)
+
+
+# the calls of the boundary as the scope table names them: the two writers,
+# the INT8 decode and its FP16-KV control, and the sizing queries
+BOUNDARY_CALLS = {
+    "pdakv_page_bytes": "size_t pdakv_page_bytes(int kv_format, int block_size, "
+                        "int num_kv_heads, int head_dim)",
+    "pdakv_capabilities": "int pdakv_capabilities(uint32_t* flags_out)",
+    "paged_attn_decode_workspace_bytes": "size_t paged_attn_decode_workspace_bytes(int num_seqs, "
+                                         "int num_q_heads, int head_dim, int max_context_len)",
+    "kv_quant_int8_sym_write": None, "kv_write_16bit": None,
+    "paged_attn_decode_int8": None, "paged_attn_decode_fp16": None,
+}
+
+
+def _flat_header():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.sub(r"\s+", " ", src)
+
+
+def test_boundary_calls_are_declared_with_their_signatures(P):
+    flat = _flat_header()
+    for name, sig in BOUNDARY_CALLS.items():
+        assert name in _declared_functions(), name
+        assert hasattr(P._lib, name), name
+        if sig is not None:
+            assert sig + ";" in flat, sig
+    # the writers and decodes share one argument list per kind
+    for a, b in (("kv_quant_int8_sym_write", "kv_write_16bit"),
+                 ("paged_attn_decode_int8", "paged_attn_decode_fp16")):
+        args = [re.search(r"\b" + n + r"\((.*?)\);", flat).group(1) for n in (a, b)]
+        assert args[0] == args[1]
+
+
+@pytest.mark.parametrize("B,hq,d,L", [(64, 32, 128, 8193), (8, 32, 128, 32768),
+                                      (32, 14, 64, 4105), (1, 32, 128, 2048), (3, 16, 64, 40),
+                                      (2, 48, 128, 100)])
+def test_any_kv_heads_workspace_is_the_largest_over_kv_heads(P, B, hq, d, L):
+    """paged_attn_decode_workspace_bytes(B, Hq, D, L) is the largest
+    pdakv_decode_workspace_bytes over the KV-head counts Hq allows."""
+    sizes = [P.pdakv_decode_workspace_bytes(B, hq, hkv, d, L)
+             for hkv in range(1, hq + 1) if hq % hkv == 0 and hq // hkv <= 16]
+    assert P.paged_attn_decode_workspace_bytes(B, hq, d, L) == max(sizes) > 0
+    assert P.paged_attn_decode_workspace_bytes(0, hq, d, L) == 0
+    assert P.paged_attn_decode_workspace_bytes(B, hq, d, 0) == 0
+    assert P.paged_attn_decode_workspace_bytes(B, 0, d, L) == 0
 
 
 def test_version_and_status_strings(P):
@@ -288,3 +335,68 @@ def _trim_args(**kw):
 ])
 def test_trim_validation(P, change, status):
     assert P._lib.kv_trim_keep_sink(*_trim_args(**change)) == status
+
+
+# ---- the Python binding rejects wrong dtypes, devices, layouts and sizes ----
+# (CPU tensors: every check runs before the library is called)
+
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.float16)
+
+
+def test_binding_rejects_a_wrong_slot_mapping_dtype(P):
+    import torch
+    k = _t(4, 8, 128)
+    pool = _t(4, 33280, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="slot_mapping must be int32"):
+        P.kv_quant_int8_sym_write(k, k, _t(4, dtype=torch.int64), pool, 4)
+    with pytest.raises(ValueError, match="slot_mapping must be a GPU tensor"):
+        P.kv_quant_int8_sym_write(k, k, _t(4, dtype=torch.int32), pool, 4)
+
+
+def test_binding_rejects_wrong_table_and_length_dtypes(P):
+    import torch
+    q, out = _t(2, 32, 128), _t(2, 32, 128, dtype=torch.float32)
+    pool = _t(4, 33280, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="block_tables must be int32"):
+        P.paged_attn_decode_int8(out, q, pool, 4, _t(2, 4, dtype=torch.int64),
+                                 _t(2, dtype=torch.int32), 8, 64, 0.088)
+    with pytest.raises(ValueError, match="block_tables must be a GPU tensor"):
+        P.paged_attn_decode_int8(out, q, pool, 4, _t(2, 4, dtype=torch.int32),
+                                 _t(2, dtype=torch.int64), 8, 64, 0.088)
+    with pytest.raises(ValueError, match="context_lens must be int32"):
+        P.kv_trim_keep_sink(P.KV_INT8_SYM, pool, 4, 8, 128, _t(2, 4, dtype=torch.int32),
+                            _t(2, dtype=torch.int64), _t(2, dtype=torch.int32), 4,
+                            _t(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="block_ids must be int32"):
+        P.kv_pages_swap_out(pool, 4, _t(2, dtype=torch.int64), _t(2, 33280, dtype=torch.uint8))
+
+
+def test_binding_checks_pools_and_tables(P):
+    """Layout and size checks, with the dtype and device checks out of the way."""
+    import torch
+    from paged_decode_attention_kv_amd import _lib
+
+    class Dev:  # a stand-in that passes the device checks
+        def __init__(self, t):
+            self.t = t
+            self.is_cuda = True
+            self.dtype, self.shape = t.dtype, t.shape
+
+        def __getattr__(self, n):
+            return getattr(self.t, n)
+
+    bt = Dev(_t(4, 3, dtype=torch.int32).t())  # transposed: stride(1) != 1
+    with pytest.raises(ValueError, match="unit stride"):
+        _lib._need_block_tables(bt, 2)
+    with pytest.raises(ValueError, match="rows"):
+        _lib._need_block_tables(Dev(_t(1, 4, dtype=torch.int32)), 2)
+    pool = Dev(_t(3, 33280, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="kv_pool holds"):
+        _lib._need_pool(pool, 4, 33280)
+    _lib._need_pool(pool, 3, 33280)
+    with pytest.raises(ValueError, match="kv_pool holds"):
+        _lib._need_pool(pool, 3, 0)
+    with pytest.raises(ValueError, match="entries"):
+        _lib._need_int32("context_lens", Dev(_t(1, dtype=torch.int32)), 2)

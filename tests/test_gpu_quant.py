@@ -194,29 +194,6 @@ def test_codes_beside_ties_every_scale_range(P, dtype, d):
     assert bad[0].size == 0, f"{bad[0].size} bytes differ, first at page {bad[0][0]} byte {bad[1][0]}"
 
 
-@pytest.mark.slow
-@pytest.mark.parametrize("idx", [3, 4])
-def test_full_size_write_sampled(P, idx):
-    """Full-size configuration, written in the launch shape the bench uses;
-    sampled (sequence, KV head) rows are compared with the oracle."""
-    wl = make_config(idx)
-    _say(f"full-size write: config {idx}: {wl.num_seqs} seqs, {wl.num_blocks} pages")
-    pool, _ = gpu_pool(P, wl, P.KV_INT8_SYM)
-    host = pool.cpu().numpy()
-    rng = np.random.default_rng(99)
-    for b in rng.choice(wl.num_seqs, 3, replace=False):
-        for g in rng.choice(wl.num_kv_heads, 2, replace=False):
-            L = int(wl.context_lens[b])
-            kc, ks, vc, vs = oracle.gather_int8_sequence(host, wl.block_tables[b], L, 16,
-                                                         wl.num_kv_heads, wl.head_dim, heads=[g])
-            k, v = wl.tokens_of_seq(int(b))
-            wkc, wks = oracle.quantize_rows(k[:, g])
-            wvc, wvs = oracle.quantize_rows(v[:, g])
-            assert np.array_equal(kc[:, 0], wkc) and np.array_equal(vc[:, 0], wvc)
-            assert np.array_equal(ks[:, 0].view(np.uint16), wks.view(np.uint16))
-            assert np.array_equal(vs[:, 0].view(np.uint16), wvs.view(np.uint16))
-
-
 def _mixed_slots(rng, num_blocks, runs=18):
     """Runs of consecutive slots (lengths 1..23, any start offset inside a
     page, one of them reversed) in disjoint ranges, with padding and

@@ -234,7 +234,8 @@ def make_config(idx, scale: float = 1.0) -> Workload:
     """The five benchmark configurations (+ a supplementary 8K point).
 
     ``scale`` < 1 shrinks the context lengths (and batch where noted) for
-    quick CPU-side checks; 1.0 gives the full sizes.
+    quick checks; 1.0 gives the full sizes. A shrunk multi-sequence
+    configuration keeps at least two sequences.
     """
     def sc(n):
         return max(1, int(round(n * scale)))
@@ -249,16 +250,16 @@ def make_config(idx, scale: float = 1.0) -> Workload:
                      "outlier")
     if idx == 3:
         rng = np.random.default_rng(1003)  # context lengths: separate stream
-        B = sc(64)
+        B = max(2, sc(64))
         lens = rng.integers(sc(1024), sc(8192) + 1, size=B)
         return build(CONFIG_NAMES[3], 3, [("prefill", lens), ("append", [1] * B)],
                      32, 8, 128, "f16", "outlier", shuffle=True)
     if idx == 4:
-        B = sc(8)
+        B = max(2, sc(8))
         return build(CONFIG_NAMES[4], 4, [("prefill", [sc(32768)] * B)], 32, 8, 128,
                      "bf16", "logmag", shuffle=True)
     if idx == 5:
-        B = sc(32)
+        B = max(2, sc(32))
         chunk = sc(4096)
         nzero = max(1, chunk // 100)
         return build(CONFIG_NAMES[5], 5,
@@ -266,7 +267,7 @@ def make_config(idx, scale: float = 1.0) -> Workload:
                      14, 2, 64, "bf16", "normal", shuffle=True,
                      zero_tokens=("chunk", nzero), fused_qkv=True)
     if idx == "s8k":
-        B = sc(8)
+        B = max(2, sc(8))
         return build(CONFIG_NAMES["s8k"], 6, [("prefill", [sc(8192)] * B)], 32, 8, 128,
                      "f16", "outlier", shuffle=True)
     raise KeyError(idx)
