@@ -241,6 +241,35 @@ int paged_attn_decode_int8(void* out, int out_dtype, int64_t out_stride_seq,
                            int max_context_len, float sm_scale, void* workspace,
                            size_t workspace_bytes, int32_t* err_flag, void* stream);
 
+/* Bytes of the device scratch that paged_attn_decode_int8_noalloc uses in
+ * place of a workspace (32 MiB per GPU). */
+#define PDAKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* paged_attn_decode_int8 without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). Same arguments, result and error
+ * convention as paged_attn_decode_int8 minus workspace / workspace_bytes.
+ * The library's own scratch stands in for the workspace: a file-scope device
+ * array of PDAKV_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends;
+ * its device address is looked up on a device's first call (make that call
+ * outside graph capture). The call allocates nothing.
+ *   - A call whose pdakv_decode_workspace_bytes() exceeds
+ *     PDAKV_NOALLOC_SCRATCH_BYTES returns PDAKV_ERR_WORKSPACE and launches
+ *     nothing (use paged_attn_decode_int8 with a workspace instead).
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents (nothing in it needs to start at zero). Calls that
+ *     overlap in time on one GPU -- on different streams, or from different
+ *     threads without ordering -- race on it and give undefined results.
+ *   - PDAKV_ERR_NO_DEVICE without a current HIP device. */
+int paged_attn_decode_int8_noalloc(void* out, int out_dtype, int64_t out_stride_seq,
+                                   int64_t out_stride_head, const void* q, int q_dtype,
+                                   int64_t q_stride_seq, int64_t q_stride_head,
+                                   const void* kv_pool, int64_t num_blocks, int block_size,
+                                   const int32_t* block_tables, int64_t block_table_stride,
+                                   const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int max_context_len,
+                                   float sm_scale, int32_t* err_flag, void* stream);
+
 /* Paged decode over 16-bit pages (the FP16-KV control; MoE-Infinity PR #183,
  * "What landed": the pre-existing FP16 paged-attention kernel). Same
  * arguments as paged_attn_decode_int8; kv_pool is a PDAKV_KV_16BIT pool whose

@@ -26,6 +26,7 @@ from ._lib import (  # noqa: F401
     KV_INT8_STATIC,
     KV_INT8_SYM,
     LIB_PATH,
+    NOALLOC_SCRATCH_BYTES,
     PdakvError,
     kv_pages_swap_in,
     kv_pages_swap_out,
@@ -39,6 +40,7 @@ from ._lib import (  # noqa: F401
     paged_attn_decode_int8,
     paged_attn_decode_int8_append,
     paged_attn_decode_int8_multi,
+    paged_attn_decode_int8_noalloc,
     paged_attn_decode_int8_static,
     paged_attn_decode_int8_static_append,
     paged_attn_decode_workspace_bytes,

@@ -57,6 +57,9 @@ _SIGS = {
                                         ctypes.c_size_t, _c_vp, _c_vp]),
 }
 _SIGS["paged_attn_decode_fp16"] = _SIGS["paged_attn_decode_int8"]
+# no workspace arguments: the library's own per-GPU scratch
+_SIGS["paged_attn_decode_int8_noalloc"] = (_c_int, _SIGS["paged_attn_decode_int8"][1][:20] +
+                                           [_c_vp, _c_vp])
 _SIGS["paged_attn_decode_int8_append"] = (
     _c_int, [_c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_int, _c_i64, _c_i64, _c_vp, _c_vp] +
     [_c_i64] * 6 + [_c_vp, _c_i64, _c_int, _c_vp, _c_i64, _c_vp, _c_int, _c_int, _c_int, _c_int,
@@ -310,6 +313,33 @@ def paged_attn_decode_fp16(out, q, kv_pool, num_blocks: int, block_tables, conte
     """Decode over 16-bit (q's dtype) pages; writes out [B, Hq, D]."""
     _decode("paged_attn_decode_fp16", out, q, kv_pool, num_blocks, block_tables, context_lens,
             num_kv_heads, max_context_len, sm_scale, workspace, block_size, err_flag, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # PDAKV_NOALLOC_SCRATCH_BYTES
+
+
+def paged_attn_decode_int8_noalloc(out, q, kv_pool, num_blocks: int, block_tables,
+                                   context_lens, num_kv_heads: int, max_context_len: int,
+                                   sm_scale: float, block_size: int = 16, err_flag=None,
+                                   stream=None) -> None:
+    """paged_attn_decode_int8 with the library's per-GPU scratch in place of
+    a workspace (the call allocates nothing; calls that overlap on one GPU
+    race on the scratch)."""
+    fn_name = "paged_attn_decode_int8_noalloc"
+    B, hq, d = q.shape
+    if q.stride(2) != 1 or out.stride(2) != 1:
+        raise ValueError("the head_dim stride of q and out must be 1")
+    if tuple(out.shape) != (B, hq, d):
+        raise ValueError("out must have the shape of q")
+    _check_decode_args(fn_name, out, q, kv_pool, num_blocks, block_tables, context_lens,
+                       num_kv_heads, d, block_size, None, err_flag)
+    st = _lib.paged_attn_decode_int8_noalloc(
+        _ptr(out), _dtype_code(out.dtype), out.stride(0), out.stride(1),
+        _ptr(q), _dtype_code(q.dtype), q.stride(0), q.stride(1),
+        _ptr(kv_pool), num_blocks, block_size, _ptr(block_tables), block_tables.stride(0),
+        _ptr(context_lens), B, hq, num_kv_heads, d, max_context_len, float(sm_scale),
+        _ptr(err_flag), _stream(stream))
+    _check(fn_name, st)
 
 
 def _decode_append(fn_name, out, q, k_new, v_new, kv_pool, num_blocks, block_tables,

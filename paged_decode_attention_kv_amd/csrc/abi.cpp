@@ -3,9 +3,11 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/pdakv.h"
 #include "launch.h"
@@ -388,6 +390,42 @@ int page_copy(void* pool, int64_t num_blocks, int64_t page_bytes, const int32_t*
   return hip_status(pdakv::launch_page_copy(a, static_cast<hipStream_t>(stream)));
 }
 
+// Scratch of paged_attn_decode_int8_noalloc: the decode workspace (partial
+// results and merge records) as a file-scope device array, so that the call
+// allocates nothing. Every GPU the library runs on holds its own copy until
+// the process ends; in host code `scratch` only names the symbol, its device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[PDAKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch (looked up on the device's
+// first call, with that device current).
+int scratch_address(void** addr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return PDAKV_ERR_NO_DEVICE;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return PDAKV_ERR_NO_DEVICE;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return PDAKV_ERR_HIP;
+      }
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return PDAKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -511,6 +549,36 @@ int paged_attn_decode_int8(void* out, int out_dtype, int64_t out_stride_seq,
                        block_tables, block_table_stride, context_lens, num_seqs,
                        num_q_heads, num_kv_heads, head_dim, max_context_len, sm_scale,
                        workspace, workspace_bytes, err_flag, stream);
+}
+
+int paged_attn_decode_int8_noalloc(void* out, int out_dtype, int64_t out_stride_seq,
+                                   int64_t out_stride_head, const void* q, int q_dtype,
+                                   int64_t q_stride_seq, int64_t q_stride_head,
+                                   const void* kv_pool, int64_t num_blocks, int block_size,
+                                   const int32_t* block_tables, int64_t block_table_stride,
+                                   const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int max_context_len,
+                                   float sm_scale, int32_t* err_flag, void* stream) {
+  // every host check first, with a stand-in for the scratch (aligned, of the
+  // scratch's size): a call whose workspace would exceed the scratch returns
+  // PDAKV_ERR_WORKSPACE before anything touches the device
+  void* const stand_in = reinterpret_cast<void*>(uintptr_t{256});
+  int st = check_decode(out, out_dtype, out_stride_seq, 0, out_stride_head, q, q_dtype,
+                        q_stride_seq, 0, q_stride_head, 1, kv_pool, num_blocks, block_size,
+                        block_tables, block_table_stride, context_lens, num_seqs, num_q_heads,
+                        num_kv_heads, head_dim, max_context_len, sm_scale, stand_in,
+                        PDAKV_NOALLOC_SCRATCH_BYTES);
+  if (st != PDAKV_OK || num_seqs == 0) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != PDAKV_OK) return st;
+  return decode_common(PDAKV_KV_INT8_SYM, Scales{},
+                       one_token(out, out_dtype, out_stride_seq, out_stride_head, q, q_dtype,
+                                 q_stride_seq, q_stride_head),
+                       nullptr, kv_pool, num_blocks, block_size, block_tables,
+                       block_table_stride, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                       head_dim, max_context_len, sm_scale, ws, PDAKV_NOALLOC_SCRATCH_BYTES,
+                       err_flag, stream);
 }
 
 int paged_attn_decode_fp16(void* out, int out_dtype, int64_t out_stride_seq,

@@ -27,7 +27,7 @@ def _declared_functions():
 
 def test_library_exports_every_declared_function(P):
     names = _declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(P._lib, n), n
     assert set(names) == set(P.EXPORTED)
@@ -400,3 +400,29 @@ def test_binding_checks_pools_and_tables(P):
         _lib._need_pool(pool, 3, 0)
     with pytest.raises(ValueError, match="entries"):
         _lib._need_int32("context_lens", Dev(_t(1, dtype=torch.int32)), 2)
+
+
+# ---- the decode entry point without a workspace -----------------------------
+
+def _noalloc_args(**kw):
+    a = _decode_args(**kw)
+    return a[:20] + a[22:]  # no workspace, workspace_bytes
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(qdt=0), -3), (dict(hq=30), -2), (dict(d=96), -2), (dict(bts=15), -1),
+    (dict(q=None), -1), (dict(pool=FAKE + 8), -1), (dict(B=0), 0),
+    # a workspace beyond the 32 MiB scratch: refused before any device call
+    (dict(B=512, maxL=32768, bts=2048), -4),
+])
+def test_noalloc_validation(P, change, status):
+    assert P._lib.paged_attn_decode_int8_noalloc(*_noalloc_args(**change)) == status
+
+
+def test_noalloc_scratch_size_is_the_header_constant(P):
+    m = re.search(r"#define PDAKV_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == P.NOALLOC_SCRATCH_BYTES
+    # the batched step and the 32K workload fit; 512 sequences at 32K do not
+    assert P.pdakv_decode_workspace_bytes(64, 32, 8, 128, 8193) <= P.NOALLOC_SCRATCH_BYTES
+    assert P.pdakv_decode_workspace_bytes(8, 32, 8, 128, 32768) <= P.NOALLOC_SCRATCH_BYTES
+    assert P.pdakv_decode_workspace_bytes(512, 32, 8, 128, 32768) > P.NOALLOC_SCRATCH_BYTES
