@@ -24,6 +24,21 @@ import os
 import sys
 import time
 
+
+def _affinity_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+# The oracle's host threads: the cores this process may run on, set before
+# NumPy (and its BLAS) is imported. A thread count the environment already
+# fixes is kept (the GPU machines set one), and the JSON line records both.
+AFFINITY_CORES = _affinity_cores()
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_var, str(AFFINITY_CORES))
+
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 
 
@@ -38,7 +53,15 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB buffer 3 times (reference kernel of known size for "
                          "calibrating the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--profile", metavar="WORKLOAD:CALL",
+                    help="only run one call on one workload --steps times after --warmup "
+                         "(for profiler runs) and print its mean time; WORKLOAD is one of "
+                         "c1 c2 c3 c4 c5 s8k, CALL one of int8 fp16 static int8_append "
+                         "fp16_append static_append int8_multi4 fp16_multi4")
     return ap.parse_args()
+
+
+WORKLOADS = {"c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5, "s8k": "s8k"}
 
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -240,6 +263,31 @@ def main():
         dec_ms = [a.elapsed_time(b) for a, b in evs]
         return (t1 - t0) / steps * 1e3, float(np.mean(dec_ms)), float(np.median(dec_ms))
 
+    if args.profile:
+        wname, call = args.profile.split(":")
+        pwl = make_config(WORKLOADS[wname])
+        key = call.split("_")[0]
+        append = call.endswith("_append")
+        st = setup(pwl, key, "append" if append else None)
+        mode = "fused" if append else "decode"
+        if call.endswith("_multi4"):
+            T = 4
+            st["multi"] = (P.paged_attn_decode_int8_multi if key == "int8"
+                           else P.paged_attn_decode_fp16_multi)
+            st["mq"] = to_dev(multi_query(pwl, T, seed=2024))
+            st["mout"] = torch.empty((pwl.num_seqs, T, pwl.num_q_heads, pwl.head_dim),
+                                     dtype=torch.float32, device="cuda")
+            st["mws"] = P.alloc_multi_workspace(pwl.num_seqs, T, pwl.num_q_heads,
+                                                pwl.num_kv_heads, pwl.head_dim,
+                                                pwl.max_context_len)
+            mode = "multi"
+        _, ms, med = run(pwl, st, args.steps, args.warmup, mode)
+        print(json.dumps({"profile": args.profile, "workload": pwl.name,
+                          "dispatches": args.warmup + 2 * args.steps,
+                          "call_us": round(ms * 1e3, 2), "call_us_median": round(med * 1e3, 2)}),
+              flush=True)
+        return
+
     # ---- headline: batched decode step (append + decode) ------------------
     # fused: one call appends the 64 new tokens and decodes; unfused: the
     # separate quantize-on-write call, then the decode call
@@ -270,10 +318,15 @@ def main():
     # ---- supplementary decode-only points at 2K / 8K / 32K -------------------
     points = {}
     if not args.no_points:
-        for pname, idx in (("2k", 2), ("8k", "s8k"), ("32k", 4)):
+        for pname, idx, bound in (("c1", 1, "latency-bound (0.56 MB per call)"),
+                                  ("2k", 2, "latency-bound (4.3 MB per call)"),
+                                  ("8k", "s8k", "hbm"), ("32k", 4, "hbm"),
+                                  ("c5", 5, "latency/Infinity-Cache-bound (35 MB per call)")):
             pwl = make_config(idx)
             entry = {"config": pwl.name, "batch": pwl.num_seqs,
-                     "context": int(pwl.max_context_len)}
+                     "context": int(pwl.max_context_len), "bound": bound,
+                     "heads_q_kv": [pwl.num_q_heads, pwl.num_kv_heads],
+                     "head_dim": pwl.head_dim, "dtype": pwl.kv_dtype}
             for key in ("int8", "fp16", "static"):
                 st = setup(pwl, key, None)
                 _, dms, _ = run(pwl, st, max(10, args.steps), args.warmup, "decode")
@@ -287,6 +340,8 @@ def main():
                 torch.cuda.empty_cache()
             entry["int8_over_fp16"] = round(entry["int8"]["tokens_per_s"] /
                                             entry["fp16"]["tokens_per_s"], 3)
+            if not args.no_cpu_baseline:
+                entry["oracle"] = oracle_decode_rate(pwl)
             points[pname] = entry
 
     # ---- several query tokens: verify 4 draft tokens per sequence -----------
@@ -465,25 +520,112 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_threads() -> int:
+    """Threads of the BLAS pools NumPy uses (the oracle's host threads)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def host_info() -> dict:
+    return {"cpu_model": cpu_model(), "affinity_cores": AFFINITY_CORES,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def stratified_sample(lens, n: int):
+    """n sequences at evenly spaced ranks of the context lengths (ranks
+    (i + 1/2) * B / n): the sample's length distribution follows the batch's,
+    so its rate is that of the whole batch."""
+    import numpy as np
+    order = np.argsort(np.asarray(lens), kind="stable")
+    B = len(order)
+    if n >= B:
+        return sorted(order.tolist())
+    ranks = ((np.arange(n) + 0.5) * B / n).astype(int)
+    return sorted(int(order[r]) for r in ranks)
+
+
+def _oracle_pool_for(wl, seqs):
+    """An oracle pool holding every written token of the sampled sequences
+    (pages renumbered compactly, each sequence keeping its page order), with
+    its block table and context lengths. Untimed set-up."""
+    import numpy as np
+    import oracle
+    tables, ctx, total = [], [], 0
+    for b in seqs:
+        n = -(-int(wl.context_lens[b]) // 16)
+        tables.append(np.arange(total, total + n, dtype=np.int32))
+        ctx.append(int(wl.context_lens[b]))
+        total += n
+    bt = np.zeros((len(seqs), max(len(t) for t in tables)), np.int32)
+    for i, t in enumerate(tables):
+        bt[i, :len(t)] = t
+    pool = oracle.new_pool(oracle.KV_INT8_SYM, total, 16, wl.num_kv_heads, wl.head_dim)
+    for i, b in enumerate(seqs):
+        k, v = wl.tokens_of_seq(int(b))
+        pos = np.arange(k.shape[0])
+        kc, ks = oracle.quantize_rows(k)
+        vc, vs = oracle.quantize_rows(v)
+        oracle.write_int8_tokens(pool, kc, ks, vc, vs, bt[i, pos // 16] * 16 + pos % 16, 16)
+    return pool, bt, np.array(ctx, np.int32)
+
+
+def oracle_decode_rate(wl, budget_s: float = 4.0, max_seqs: int = 4) -> dict:
+    """The oracle's INT8 paged decode (FP64) on a bounded, length-stratified
+    sample of the workload's sequences, repeated for about budget_s seconds
+    (at least once). Returns decoded sequences (= tokens) per second and the
+    attended context tokens per second."""
+    import numpy as np
+    import oracle
+    import torch
+    seqs = stratified_sample(wl.context_lens, min(max_seqs, wl.num_seqs))
+    pool, bt, ctx = _oracle_pool_for(wl, seqs)
+    q = torch.stack([wl.q[b] for b in seqs])
+    reps, spent = 0, 0.0
+    while spent < budget_s or reps == 0:
+        t0 = time.perf_counter()
+        oracle.decode_int8_from_pool(pool, bt, ctx, q, wl.sm_scale, 16, wl.num_kv_heads,
+                                     wl.head_dim)
+        spent += time.perf_counter() - t0
+        reps += 1
+    return {"tokens_per_s": round(reps * len(seqs) / spent, 3),
+            "context_tokens_per_s": round(reps * float(np.sum(ctx)) / spent, 1),
+            "sample": f"{len(seqs)} of {wl.num_seqs} sequences (mean context "
+                      f"{float(ctx.mean()):.0f}, batch mean {float(wl.context_lens.mean()):.0f}), "
+                      f"{reps} oracle decodes in {spent:.1f} s",
+            "threads": blas_threads()}
+
+
 def cpu_baseline(wl, budget_s: float = 15.0, sample_seqs: int = 8):
     """Time the oracle (as it stands, untuned) on a bounded sample of the step.
 
-    Setup (untimed): an oracle pool holding the prefill of ``sample_seqs``
-    sequences of the batch, quantized and written by the oracle. Timed: the
-    step for those sequences with the oracle's own functions — quantize the
-    appended tokens, write them into the pool, decode all query heads from the
-    pool — repeated until ``budget_s`` is spent. The rate is decoded tokens
-    (one per sequence per step) per second.
+    Sample: ``sample_seqs`` sequences at evenly spaced ranks of the batch's
+    context lengths, so that the sample's mean context matches the batch's.
+    Setup (untimed): an oracle pool holding their prefill, quantized and
+    written by the oracle. Timed: the step for those sequences with the
+    oracle's own functions -- quantize the appended tokens, write them into
+    the pool, decode all query heads from the pool -- repeated until
+    ``budget_s`` is spent. The rate is decoded tokens (one per sequence per
+    step) per second; the attended context tokens per second are given too.
     """
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = 1
+    import torch
     pre, app = wl.phase("prefill"), wl.phase("append")
-    seqs = sorted(np.random.default_rng(0).choice(wl.num_seqs, sample_seqs, replace=False))
+    seqs = stratified_sample(wl.context_lens, sample_seqs)
     # compact pool for the sample: each sampled sequence keeps its page order
     tables, ctx, total = [], [], 0
     for b in seqs:
@@ -509,7 +651,6 @@ def cpu_baseline(wl, budget_s: float = 15.0, sample_seqs: int = 8):
         a_v.append(app.v[arow])
         a_slots.append(bt[i, n_pre // 16] * 16 + n_pre % 16)
         qs.append(wl.q[int(b)])
-    import torch
     ak, av, q = torch.cat(a_k), torch.cat(a_v), torch.stack(qs)
     slots = np.array(a_slots, np.int32)
     steps, spent = 0, 0.0
@@ -522,12 +663,17 @@ def cpu_baseline(wl, budget_s: float = 15.0, sample_seqs: int = 8):
                                      wl.head_dim)
         spent += time.perf_counter() - t0
         steps += 1
+    info = host_info()
     return {"value": round(steps * len(seqs) / spent, 3), "unit": "tokens/s",
-            "cores": int(cores), "kind": "oracle",
-            "sample": f"{len(seqs)} of {wl.num_seqs} sequences of the batched step "
-                      f"(mean context {float(ctx.mean()):.0f}); oracle quantize + page write of "
-                      f"the appended tokens and FP64 paged decode of all 32 query heads, "
-                      f"{steps} steps in {spent:.1f} s"}
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{len(seqs)} of {wl.num_seqs} sequences of the batched step at evenly "
+                      f"spaced context-length ranks (mean context {float(ctx.mean()):.0f}, "
+                      f"batch mean {float(wl.context_lens.mean()):.0f}); oracle quantize + "
+                      f"page write of the appended tokens and FP64 paged decode of all "
+                      f"{wl.num_q_heads} query heads, {steps} steps in {spent:.1f} s",
+            "context_tokens_per_s": round(steps * float(ctx.sum()) / spent, 1),
+            "cpu_model": info["cpu_model"], "affinity_cores": info["affinity_cores"],
+            "omp_num_threads": info["omp_num_threads"]}
 
 
 if __name__ == "__main__":
