@@ -57,7 +57,7 @@ def parse():
                     help="only run one call on one workload --steps times after --warmup "
                          "(for profiler runs) and print its mean time; WORKLOAD is one of "
                          "c1 c2 c3 c4 c5 s8k, CALL one of int8 fp16 static int8_append "
-                         "fp16_append static_append int8_multi4 fp16_multi4")
+                         "fp16_append static_append int8_multiT fp16_multiT (T query tokens)")
     return ap.parse_args()
 
 
@@ -270,8 +270,8 @@ def main():
         append = call.endswith("_append")
         st = setup(pwl, key, "append" if append else None)
         mode = "fused" if append else "decode"
-        if call.endswith("_multi4"):
-            T = 4
+        if "_multi" in call:
+            T = int(call.split("_multi")[1])
             st["multi"] = (P.paged_attn_decode_int8_multi if key == "int8"
                            else P.paged_attn_decode_fp16_multi)
             st["mq"] = to_dev(multi_query(pwl, T, seed=2024))
@@ -347,31 +347,39 @@ def main():
     # ---- several query tokens: verify 4 draft tokens per sequence -----------
     # the batched step's pool (contexts L_b + 1); the last 4 positions of every
     # sequence are the query tokens (causal among them)
+    # T = 4 and 8 draft tokens (16 and 32 query columns per KV head: one and
+    # two 16-column tiles, both streamed once) and a 64-token block (256
+    # columns, 16 tiles in units of 4)
     multi = None
     if not args.no_points:
-        T = 4
-        multi = {"query_tokens": T, "config": wl.name}
+        multi = {"config": wl.name}
         for key in ("int8", "fp16"):
             st = setup(wl, key, None)
             st["multi"] = (P.paged_attn_decode_int8_multi if key == "int8"
                            else P.paged_attn_decode_fp16_multi)
-            st["mq"] = to_dev(multi_query(wl, T, seed=2024))
-            st["mout"] = torch.empty((wl.num_seqs, T, wl.num_q_heads, wl.head_dim),
-                                     dtype=torch.float32, device="cuda")
-            st["mws"] = P.alloc_multi_workspace(wl.num_seqs, T, wl.num_q_heads,
-                                                wl.num_kv_heads, wl.head_dim,
-                                                wl.max_context_len)
-            _, mms, _ = run(wl, st, args.steps, args.warmup, "multi")
             _, dms, _ = run(wl, st, args.steps, args.warmup, "decode")
-            b = decode_bytes(wl, key) + wl.num_seqs * (T - 1) * wl.num_q_heads * wl.head_dim * 6
-            multi[key] = {"call_us": round(mms * 1e3, 2),
-                          "query_tokens_per_s": round(wl.num_seqs * T / (mms * 1e-3), 1),
-                          "gbs": round(b / (mms * 1e-3) / 1e9, 1),
-                          "one_token_call_us": round(dms * 1e3, 2),
-                          "vs_T_one_token_calls": round(T * dms / mms, 3)}
+            multi[key] = {"one_token_call_us": round(dms * 1e3, 2)}
+            for T in (4, 8, 64):
+                st["mq"] = to_dev(multi_query(wl, T, seed=2024))
+                st["mout"] = torch.empty((wl.num_seqs, T, wl.num_q_heads, wl.head_dim),
+                                         dtype=torch.float32, device="cuda")
+                st["mws"] = P.alloc_multi_workspace(wl.num_seqs, T, wl.num_q_heads,
+                                                    wl.num_kv_heads, wl.head_dim,
+                                                    wl.max_context_len)
+                _, mms, _ = run(wl, st, args.steps, args.warmup, "multi")
+                b = (decode_bytes(wl, key) +
+                     wl.num_seqs * (T - 1) * wl.num_q_heads * wl.head_dim * 6)
+                multi[key][f"T{T}"] = {
+                    "call_us": round(mms * 1e3, 2),
+                    "query_tokens_per_s": round(wl.num_seqs * T / (mms * 1e-3), 1),
+                    "gbs": round(b / (mms * 1e-3) / 1e9, 1),
+                    "vs_T_one_token_calls": round(T * dms / mms, 3)}
+            multi[key]["T8_over_T4"] = round(multi[key]["T8"]["call_us"] /
+                                             multi[key]["T4"]["call_us"], 3)
             del st
             torch.cuda.empty_cache()
-        multi["int8_over_fp16"] = round(multi["fp16"]["call_us"] / multi["int8"]["call_us"], 3)
+        multi["int8_over_fp16_T4"] = round(multi["fp16"]["T4"]["call_us"] /
+                                           multi["int8"]["T4"]["call_us"], 3)
 
     def timed(fn, reps):
         """Seconds per call of fn, from HIP events on the launch stream."""

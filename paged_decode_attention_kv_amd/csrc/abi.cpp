@@ -17,11 +17,29 @@ namespace {
 using pdakv::DecodeArgs;
 using pdakv::WriteArgs;
 
-// Decode waves resident at once on MI355X: 256 CUs x 4 SIMDs x the waves per
-// SIMD the kernel's register budget allows.
-int64_t resident_waves(int kv_format) {
-  return int64_t{pdakv::kCUs} * 4 *
-         (kv_format == PDAKV_KV_16BIT ? pdakv::k16WavesPerSimd : pdakv::kInt8WavesPerSimd);
+// Compute units of the current device (asked once; MI355X's 256 when no
+// device answers, e.g. for the host-only size queries on a machine without
+// a GPU).
+int device_cus() {
+  static const int cus = [] {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        n > 0)
+      return n;
+    (void)hipGetLastError();
+    return pdakv::kDefaultCUs;
+  }();
+  return cus;
+}
+
+// Decode waves resident at once: CUs x 4 SIMDs x the waves per SIMD the
+// kernel's register budget allows.
+int64_t resident_waves(int waves_per_simd) {
+  return int64_t{device_cus()} * pdakv::kSimdsPerCU * waves_per_simd;
+}
+int format_waves_per_simd(int kv_format) {
+  return kv_format == PDAKV_KV_16BIT ? pdakv::k16WavesPerSimd : pdakv::kInt8WavesPerSimd;
 }
 
 bool known_format(int f) {
@@ -51,9 +69,9 @@ int64_t item_bound(int num_seqs, int num_kv_heads, int max_context_len) {
 // them (at least kMinPagesPerWave each), so one resident round of waves is
 // used whenever that keeps every wave at <= kMaxPagesPerWave items; small
 // launches get fewer waves so that each still has a few pages to pipeline.
-int64_t plan_waves(int kv_format, int num_seqs, int num_kv_heads, int max_context_len) {
+int64_t plan_waves(int waves_per_simd, int num_seqs, int num_kv_heads, int max_context_len) {
   const int64_t items = item_bound(num_seqs, num_kv_heads, max_context_len);
-  int64_t v = std::max(resident_waves(kv_format), ceil_div(items, pdakv::kMaxPagesPerWave));
+  int64_t v = std::max(resident_waves(waves_per_simd), ceil_div(items, pdakv::kMaxPagesPerWave));
   v = std::min(v, ceil_div(items, pdakv::kMinPagesPerWave));
   v = std::max<int64_t>(v, 1);
   return ceil_div(v, pdakv::kWaves) * pdakv::kWaves;
@@ -72,15 +90,21 @@ int merge_waves(int num_seqs, int num_kv_heads, int max_context_len, int64_t wav
 }
 
 // Query columns of a call: T query tokens x G query heads per KV head, in
-// tiles of at most 16 (one MFMA operand); each (KV head, tile) is a unit.
+// tiles of at most 16 (one MFMA operand). A unit is one KV head's run of up
+// to unit_tiles tiles, whose pages are streamed once for all of them: one
+// tile per unit for up to 16 columns, two for up to 32, four beyond (those
+// kernels run one wave per SIMD for the registers of the tiles' states).
 struct Columns {
-  int cols, ntile, slot_cols;
+  int cols, unit_tiles, units_per_head, slot_cols, waves_per_simd;
 };
 Columns columns(int num_q_heads, int num_kv_heads, int num_query_tokens) {
   Columns c;
   c.cols = num_query_tokens * (num_q_heads / num_kv_heads);
-  c.ntile = (c.cols + 15) / 16;
-  c.slot_cols = std::min(c.cols, 16);
+  const int tiles = (c.cols + 15) / 16;
+  c.unit_tiles = tiles >= 3 ? 4 : tiles;
+  c.units_per_head = (tiles + c.unit_tiles - 1) / c.unit_tiles;
+  c.slot_cols = std::min(c.cols, 16 * c.unit_tiles);
+  c.waves_per_simd = pdakv::multi_waves_per_simd(c.unit_tiles);
   return c;
 }
 
@@ -90,8 +114,8 @@ Columns columns(int num_q_heads, int num_kv_heads, int num_query_tokens) {
 size_t partials_bytes(int num_seqs, int num_query_tokens, int num_q_heads, int num_kv_heads,
                       int head_dim, int max_context_len) {
   const Columns c = columns(num_q_heads, num_kv_heads, num_query_tokens);
-  const int vheads = num_kv_heads * c.ntile;
-  const int64_t v = plan_waves(PDAKV_KV_INT8_SYM, num_seqs, vheads, max_context_len);
+  const int vheads = num_kv_heads * c.units_per_head;
+  const int64_t v = plan_waves(c.waves_per_simd, num_seqs, vheads, max_context_len);
   const int64_t slots = v + static_cast<int64_t>(num_seqs) * vheads;
   const size_t bytes = static_cast<size_t>(slots) * c.slot_cols * (head_dim + 2) * sizeof(float);
   return (bytes + 15) / 16 * 16;
@@ -103,7 +127,7 @@ size_t decode_ws_bytes(int num_seqs, int num_query_tokens, int num_q_heads, int 
       head_dim <= 0 || max_context_len <= 0 || num_q_heads % num_kv_heads != 0)
     return 0;
   const Columns c = columns(num_q_heads, num_kv_heads, num_query_tokens);
-  const int vheads = num_kv_heads * c.ntile;
+  const int vheads = num_kv_heads * c.units_per_head;
   if (item_bound(num_seqs, vheads, max_context_len) > kMaxItems) return 0;
   return partials_bytes(num_seqs, num_query_tokens, num_q_heads, num_kv_heads, head_dim,
                         max_context_len) +
@@ -159,7 +183,7 @@ int check_decode(void* out, int out_dtype, int64_t out_ss, int64_t out_st, int64
   // device indexes are int32: items, (sequence, query token, query head) rows
   // of the merge grid
   const Columns c = columns(num_q_heads, num_kv_heads, qtok);
-  if (item_bound(num_seqs, num_kv_heads * c.ntile, max_context_len) > kMaxItems)
+  if (item_bound(num_seqs, num_kv_heads * c.units_per_head, max_context_len) > kMaxItems)
     return PDAKV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(num_seqs) * qtok * num_q_heads > INT32_MAX)
     return PDAKV_ERR_UNSUPPORTED;
@@ -249,15 +273,17 @@ int decode_common(int fmt, Scales sc, const Rows& r, const AppendRows* app,
   const Columns cols = columns(num_q_heads, num_kv_heads, r.tokens);
   a.qtok = r.tokens;
   a.cols = cols.cols;
-  a.ntile = cols.ntile;
-  a.vheads = num_kv_heads * cols.ntile;
+  a.unit_tiles = cols.unit_tiles;
+  a.units_per_head = cols.units_per_head;
+  a.vheads = num_kv_heads * cols.units_per_head;
   a.slot_cols = cols.slot_cols;
   a.max_ctx = max_context_len;
   a.scale_log2 = static_cast<float>(scale_log2);
   a.out_mul = fmt == PDAKV_KV_INT8_STATIC ? sc.v : 1.f;
   a.k_scale = sc.k;
   a.v_scale = sc.v;
-  a.num_waves = static_cast<int>(plan_waves(fmt, num_seqs, a.vheads, max_context_len));
+  const int wps = r.multi ? cols.waves_per_simd : format_waves_per_simd(fmt);
+  a.num_waves = static_cast<int>(plan_waves(wps, num_seqs, a.vheads, max_context_len));
   a.merge_waves = merge_waves(num_seqs, a.vheads, max_context_len, a.num_waves);
   {
     // LDS staging of a decode pass of n segments: each segment's q rows
@@ -283,6 +309,13 @@ int decode_common(int fmt, Scales sc, const Rows& r, const AppendRows* app,
     a.lds_res_off = r.multi ? 0 : n * qb;
     a.lds_nt_off = area(n);
     a.lds_wave_bytes = area(n) + n * nb;
+    if (cols.unit_tiles > 1) {
+      // several tiles per unit: passes of one segment, whose q rows are the
+      // only LDS staging (results are written from registers)
+      a.seg_cap = 1;
+      a.lds_q_off = a.lds_res_off = a.lds_nt_off = 0;
+      a.lds_wave_bytes = up16(qb);
+    }
   }
   a.ws = static_cast<float*>(workspace);
   a.desc = reinterpret_cast<int2*>(
@@ -475,7 +508,8 @@ int pdakv_decode_plan(int kv_format, int num_seqs, int num_kv_heads, int max_con
   if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0) return PDAKV_ERR_INVALID_ARG;
   if (item_bound(num_seqs, num_kv_heads, max_context_len) > kMaxItems)
     return PDAKV_ERR_UNSUPPORTED;
-  const int64_t v = plan_waves(kv_format, num_seqs, num_kv_heads, max_context_len);
+  const int64_t v = plan_waves(format_waves_per_simd(kv_format), num_seqs, num_kv_heads,
+                               max_context_len);
   const int64_t p = std::max<int64_t>(
       pdakv::kMinPagesPerWave, ceil_div(item_bound(num_seqs, num_kv_heads, max_context_len), v));
   if (num_waves) *num_waves = static_cast<int>(v);

@@ -291,17 +291,60 @@ __device__ __forceinline__ void load_int8_page(Int8Page<D>& pg, const uint8_t* h
   pg.vs = ld8(r, so + 32);
 }
 
+// The matrix-instruction operands of a page's codes: K fragment j (the A
+// operand of QK instruction j: 8 codes of token i16) and V fragment k (the A
+// operand of PV instruction k: one dimension of four tokens), as fp16.
+// Converted from the loaded codes where they are used (one query tile per
+// page), or once per page into a Int8Frag when several query tiles share it.
+template <class Pg>
+__device__ __forceinline__ h8_t k_frag(const Pg& pg, int j) {
+  const u2_t c0 = i8x4_to_f16x4_perm(pg.k[j / 2][2 * (j % 2)]);
+  const u2_t c1 = i8x4_to_f16x4_perm(pg.k[j / 2][2 * (j % 2) + 1]);
+  return __builtin_bit_cast(h8_t, u4_t{c0.x, c0.y, c1.x, c1.y});
+}
+template <class Pg>
+__device__ __forceinline__ h4_t v_frag(const Pg& pg, int k) {
+  return __builtin_bit_cast(h4_t, i8x4_to_f16x4_perm(pg.v[k / 4][k % 4]));
+}
+
+template <int D, bool Scales>
+struct Int8Frag {
+  h8_t kf[D / 32];
+  h4_t vf[D / 16];
+  u2_t ks, vs;  // (per-token scales only)
+};
+template <int D, bool Scales>
+__device__ __forceinline__ h8_t k_frag(const Int8Frag<D, Scales>& fr, int j) {
+  return fr.kf[j];
+}
+template <int D, bool Scales>
+__device__ __forceinline__ h4_t v_frag(const Int8Frag<D, Scales>& fr, int k) {
+  return fr.vf[k];
+}
+
 template <int D, class Pg>
 __device__ __forceinline__ f4_t int8_qk(const Pg& pg, const h8_t* qf) {
   f4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int j = 0; j < D / 32; ++j) {
-    const u2_t c0 = i8x4_to_f16x4_perm(pg.k[j / 2][2 * (j % 2)]);
-    const u2_t c1 = i8x4_to_f16x4_perm(pg.k[j / 2][2 * (j % 2) + 1]);
-    const u4_t kw = {c0.x, c0.y, c1.x, c1.y};
-    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, kw), qf[j], s, 0, 0, 0);
-  }
+  for (int j = 0; j < D / 32; ++j)
+    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_frag(pg, j), qf[j], s, 0, 0, 0);
   return s;
+}
+
+// High fp16 parts of four binary32 probabilities (rounded toward zero, one
+// conversion instruction per pair) and the fp16 rests p - hi, so that
+// hi + lo carries 22 significant bits of p.
+__device__ __forceinline__ h4_t split_hi(const float (&p)[4]) {
+  const auto a = __builtin_amdgcn_cvt_pkrtz(p[0], p[1]);
+  const auto b = __builtin_amdgcn_cvt_pkrtz(p[2], p[3]);
+  return __builtin_bit_cast(h4_t, u2_t{__builtin_bit_cast(uint32_t, a),
+                                       __builtin_bit_cast(uint32_t, b)});
+}
+__device__ __forceinline__ h4_t split_lo(const float (&p)[4], h4_t hi) {
+  float lo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) lo[j] = p[j] - static_cast<float>(hi[j]);
+  return __builtin_bit_cast(h4_t, u2_t{pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3])});
 }
 
 // Position of this lane's first token in a page starting at page_tok: lane
@@ -320,8 +363,8 @@ __device__ __forceinline__ int lane_token(int page_tok) {
 // L get V scale 1.0 (their slots may hold anything); those at or past Lc get
 // logit -inf. (A separate unmasked path for full pages costs more registers
 // than the masks cost instructions.)
-template <int D>
-__device__ __forceinline__ void int8_page_step(const Int8Page<D>& pg, const h8_t* qf,
+template <int D, class Pg>
+__device__ __forceinline__ void int8_page_step(const Pg& pg, const h8_t* qf,
                                                float qscale, int page_tok, int L, int Lmin,
                                                int Lc, SoftmaxState<D / 16>& st) {
   constexpr int ND = D / 16;
@@ -353,22 +396,23 @@ __device__ __forceinline__ void int8_page_step(const Int8Page<D>& pg, const h8_t
     zmax = max_nc(zmax, z[j]);
   }
   raise_max(st, zmax);
-  float hi[4], lo[4];
+  float p[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float x = __builtin_amdgcn_exp2f(z[j] - st.mk);  // 2^(kPScale + z - m)
     st.l += __builtin_amdgcn_ldexpf(x, -e[j]);
-    const float p = x * static_cast<float>(f[j]);
-    hi[j] = static_cast<float>(static_cast<_Float16>(p));
-    lo[j] = p - hi[j];
+    p[j] = x * static_cast<float>(f[j]);
   }
-  const h4_t ph = __builtin_bit_cast(h4_t, u2_t{pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3])});
-  const h4_t pl = __builtin_bit_cast(h4_t, u2_t{pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3])});
+  // p = hi + lo to 22 bits: hi is p converted to fp16 once (by the
+  // conversion instruction itself, so that the compiler cannot fold the
+  // product into a second, differently rounded conversion), lo the rest
+  const h4_t ph = split_hi(p);
+  const h4_t pl = split_lo(p, ph);
   // O^T += V^T P^T; instruction k covers dims 64*(k/4) + 4*(row) + k%4, its
   // K-slots hold tokens 4*kb + (0..3)
 #pragma unroll
   for (int k = 0; k < ND; ++k) {
-    const h4_t vw = __builtin_bit_cast(h4_t, i8x4_to_f16x4_perm(pg.v[k / 4][k % 4]));
+    const h4_t vw = v_frag(pg, k);
     st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(vw, ph, st.acc[k], 0, 0, 0);
     st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(vw, pl, st.acc[k], 0, 0, 0);
   }
@@ -399,8 +443,8 @@ __device__ __forceinline__ void load_static_page(StaticPage<D>& pg, const uint8_
 
 // Tokens at or past the limit L get logit -inf (probability 0; any byte in
 // their slots is a finite code, so 0 * code adds nothing).
-template <int D>
-__device__ __forceinline__ void static_page_step(const StaticPage<D>& pg, const h8_t* qf,
+template <int D, class Pg>
+__device__ __forceinline__ void static_page_step(const Pg& pg, const h8_t* qf,
                                                  float qscale, int page_tok, int Lmin, int Lc,
                                                  SoftmaxState<D / 16>& st) {
   constexpr int ND = D / 16;
@@ -428,7 +472,7 @@ __device__ __forceinline__ void static_page_step(const StaticPage<D>& pg, const 
   const h4_t pl = __builtin_bit_cast(h4_t, u2_t{pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3])});
 #pragma unroll
   for (int k = 0; k < ND; ++k) {
-    const h4_t vw = __builtin_bit_cast(h4_t, i8x4_to_f16x4_perm(pg.v[k / 4][k % 4]));
+    const h4_t vw = v_frag(pg, k);
     st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(vw, ph, st.acc[k], 0, 0, 0);
     st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(vw, pl, st.acc[k], 0, 0, 0);
   }
@@ -463,12 +507,29 @@ struct Int8Kind {
     else
       load_int8_page<D>(pg, hp, live, i16, kb);
   }
-  __device__ __forceinline__ void step(const Page& pg, int page_tok, int L, int Lmin, int Lc,
+  // one page against this query tile; Pg is the loaded page or its
+  // converted fragments (Frag)
+  template <class Pg>
+  __device__ __forceinline__ void step(const Pg& pg, int page_tok, int L, int Lmin, int Lc,
                                        SoftmaxState<D / 16>& st) const {
     if constexpr (Static)
       static_page_step<D>(pg, qf, qscale, page_tok, Lmin, Lc, st);
     else
       int8_page_step<D>(pg, qf, qscale, page_tok, L, Lmin, Lc, st);
+  }
+  // a page's codes as fp16 operands, converted once for several query tiles
+  using Frag = Int8Frag<D, !Static>;
+  static __device__ __forceinline__ Frag convert(const Page& pg) {
+    Frag fr;
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) fr.kf[j] = k_frag(pg, j);
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) fr.vf[k] = v_frag(pg, k);
+    if constexpr (!Static) {
+      fr.ks = pg.ks;
+      fr.vs = pg.vs;
+    }
+    return fr;
   }
   // dimension of accumulator element acc[k][j] in lane (i16, kb)
   static __device__ __forceinline__ int acc_dim(int k, int j, int kb) {
@@ -742,6 +803,9 @@ struct F16Kind {
                                        SoftmaxState<D / 16>& st) const {
     page16_step<D, BF16>(pg, qf, scale_log2, page_tok, L, Lmin, Lc, st);
   }
+  // 16-bit values are the operands as loaded
+  using Frag = Page;
+  static __device__ __forceinline__ const Page& convert(const Page& pg) { return pg; }
   static __device__ __forceinline__ int acc_dim(int k, int j, int kb) {
     return 32 * (k / 2) + 8 * kb + 2 * j + (k % 2);
   }
@@ -820,11 +884,11 @@ struct PassLds {
   uint8_t* nt;   // [seg_cap][kNewTokenBytes(D)]: appended token per segment
 };
 
-// The MFMA columns of virtual KV head vg of a sequence: KV head g, whose
-// columns 0..n-1 are the (query token, head) pairs col0 + c with
+// The MFMA columns of unit vg of a sequence: KV head g, whose columns
+// 0..n-1 are the (query token, head) pairs col0 + c with
 // col = token * group + (head - g * group). One query token: all of KV
-// head vg's query heads. Several: KV head vg / ntile, tile vg % ntile of 16
-// columns.
+// head vg's query heads. Several: KV head vg / units_per_head, the
+// unit_tiles tiles of 16 columns from tile (vg % units_per_head) * unit_tiles.
 struct UnitCols {
   int g, col0, n;
 };
@@ -833,8 +897,9 @@ __device__ __forceinline__ UnitCols unit_cols(const DecodeArgs& a, int vg) {
   if constexpr (!Multi) {
     return {vg, 0, a.group};
   } else {
-    const int tile = vg % a.ntile;
-    return {vg / a.ntile, 16 * tile, min(16, a.cols - 16 * tile)};
+    const int w = 16 * a.unit_tiles;
+    const int col0 = w * (vg % a.units_per_head);
+    return {vg / a.units_per_head, col0, min(w, a.cols - col0)};
   }
 }
 
@@ -1138,7 +1203,146 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   return items;
 }
 
-template <class K, bool Multi>
+// Write tile i's softmax state straight from registers (after the page
+// loop): the output rows of its columns when the segment covers the whole
+// unit (zero rows when no token was attendable), else the columns of the
+// unit's partial in `slot` (accumulator, running max, sum).
+template <class K>
+__device__ __forceinline__ void write_tile(const DecodeArgs& a, SoftmaxState<K::D / 16>& st,
+                                           int b, const UnitCols& uc, int tile, int slot,
+                                           bool whole, int i16, int kb) {
+  constexpr int D = K::D, ND = D / 16;
+  const float l = col_sum(st.l);
+  const int cc = 16 * tile + i16;  // column inside the unit
+  if (cc >= uc.n) return;
+  if (whole) {
+    const int col = uc.col0 + cc;
+    const int64_t o = b * a.out_ss + (col / a.group) * a.out_st +
+                      (uc.g * a.group + col % a.group) * a.out_sh;
+    const float f = l > 0.f ? a.out_mul / l : 0.f;
+#pragma unroll
+    for (int k = 0; k < ND; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) store_out(a.out, a.out_dtype, o + K::acc_dim(k, j, kb),
+                                            st.acc[k][j] * f);
+  } else {
+    float* r = a.ws + (static_cast<int64_t>(slot) * a.slot_cols + cc) * (D + 2);
+#pragma unroll
+    for (int k = 0; k < ND; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[K::acc_dim(k, j, kb)] = st.acc[k][j];
+    if (kb == 0) {
+      r[D] = st.m;
+      r[D + 1] = l;
+    }
+  }
+}
+
+// A pass of the several-token kernels with NT tiles per unit: the rest of
+// the current unit inside the wave's range (up to kMaxPagesPerWave items),
+// every page converted once and used by all NT query tiles, whose softmax
+// states stay in registers and are written after the page loop. Returns the
+// number of items done (0: the lengths changed under the call).
+template <class K, int NT>
+__device__ __forceinline__ int run_pass_wide(const DecodeArgs& a, K* kind, Cursor& cu, int x,
+                                             int x1, int P, int wave, int nchunk,
+                                             uint16_t* q_lds, int lane) {
+  constexpr int D = K::D, ND = D / 16;
+  const int i16 = lane & 15, kb = lane >> 4;
+  const int hkv = a.num_kv_heads, vh = a.vheads;
+  const int items = min(min(cu.np - cu.p, x1 - x), kMaxPagesPerWave);
+  const int u = cu.b * vh + cu.g;
+  if (cu.p == 0 && lane == 0) a.desc[u] = make_int2(wave, (x + cu.np - 1) / P - wave + 1);
+  const int b = cu.b, vg = cu.g, p0 = cu.p, L = cu.L;
+  const bool whole = cu.p == 0 && items == cu.np;
+  const UnitCols uc = unit_cols<true>(a, vg);
+  // block ids of the pass (lane i: items i and 64 + i), flagged and masked
+  // when out of range; then the q rows of every tile go to LDS
+  const int32_t* row = a.bt + static_cast<int64_t>(b) * a.bt_stride + p0;
+  int blk0 = lane < items ? row[lane] : 0;
+  int blk1 = lane + 64 < items ? row[lane + 64] : 0;
+  stage_q<D, true>(a, b, vg, q_lds, lane);
+  if (blk0 < 0 || blk0 >= a.num_blocks) {
+    raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
+    blk0 = -1;
+  }
+  if (blk1 < 0 || blk1 >= a.num_blocks) {
+    raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
+    blk1 = -1;
+  }
+  const int hb0 = blk0 >= 0 ? blk0 * hkv + uc.g : -1;
+  const int hb1 = blk1 >= 0 ? blk1 * hkv + uc.g : -1;
+  auto block_of = [&](int i) { return i < 64 ? readlane(hb0, i) : readlane(hb1, i - 64); };
+  auto page_at = [&](int hb) {
+    hb = __builtin_amdgcn_readfirstlane(hb);
+    return a.pool + static_cast<int64_t>(hb >= 0 ? hb : 0) * K::kHeadBytes;
+  };
+  cu.p += items;
+  if (cu.p == cu.np && x + items < x1 && !next_unit(a, cu, nchunk, vh, lane)) return 0;
+
+  // query token j of the sequence sits at position L - qtok + j and sees the
+  // positions up to it; Lmin: the first query token's limit
+  const int Lmin = L - a.qtok + 1;
+  int Lc[NT];
+  SoftmaxState<ND> st[NT];
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    Lc[i] = min(Lmin + (uc.col0 + 16 * i + i16) / a.group, L);
+    softmax_init(st[i]);
+    if (16 * i < uc.n) kind[i].load_q(a, q_lds + 16 * i * D, i16, kb, 16 * i + i16 < uc.n);
+  }
+
+  constexpr int G = K::kGroup;
+  typename K::Page ga[G], gb[G];
+  int ba[G], bb[G];
+  auto fill = [&](typename K::Page* grp, int* blk, int first) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int q = first + j;
+      blk[j] = q < items ? block_of(q) : -1;
+      K::load(grp[j], page_at(blk[j]), blk[j] >= 0, i16, kb);
+    }
+  };
+  auto consume = [&](typename K::Page* grp, const int* blk, int first) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int i = first + j;
+      if (i >= items) return false;
+      const int t = (p0 + i) * kBlockSize;
+      const bool ok = blk[j] >= 0;  // a missing page is masked whole
+      const typename K::Frag fr = K::convert(grp[j]);
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        if (16 * c < uc.n)
+          kind[c].step(fr, t, ok ? L : t, ok ? Lmin : t, ok ? Lc[c] : t, st[c]);
+        // one tile after the other (interleaving them costs registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    return true;
+  };
+  fill(ga, ba, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  fill(gb, bb, G);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0;; i += 2 * G) {
+    if (!consume(ga, ba, i)) break;
+    __builtin_amdgcn_sched_barrier(0);
+    fill(ga, ba, i + 2 * G);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool more = consume(gb, bb, i + G);
+    __builtin_amdgcn_sched_barrier(0);
+    fill(gb, bb, i + 3 * G);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!more || i + 2 * G >= items) break;
+  }
+#pragma unroll
+  for (int c = 0; c < NT; ++c)
+    if (16 * c < uc.n) write_tile<K>(a, st[c], b, uc, c, wave + u, whole, i16, kb);
+  return items;
+}
+
+template <class K, bool Multi, int NT = 1>
 __device__ __forceinline__ void decode_wave(const DecodeArgs& a) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int lane = lane_id();
@@ -1190,11 +1394,20 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs& a) {
   cu.g = off / cu.np;
   cu.p = off - cu.g * cu.np;
 
-  K kind;
-  for (int x = x0; x < x1;) {
-    const int done = run_pass<K, Multi>(a, kind, cu, x, x1, P, wave, nchunk, lds, lane);
-    if (done == 0) return;
-    x += done;
+  if constexpr (NT == 1) {
+    K kind;
+    for (int x = x0; x < x1;) {
+      const int done = run_pass<K, Multi>(a, kind, cu, x, x1, P, wave, nchunk, lds, lane);
+      if (done == 0) return;
+      x += done;
+    }
+  } else {
+    K kind[NT];
+    for (int x = x0; x < x1;) {
+      const int done = run_pass_wide<K, NT>(a, kind, cu, x, x1, P, wave, nchunk, lds.q, lane);
+      if (done == 0) return;
+      x += done;
+    }
   }
 }
 
@@ -1210,6 +1423,20 @@ template <int D, bool QBF16>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
     kInt8WavesPerSimd))) void decode_int8_multi_kernel(DecodeArgs a) {
   decode_wave<Int8Kind<D, QBF16, kInt8PageGroup>, true>(a);
+}
+
+// Several query tiles per unit: one wave per SIMD, for the registers of NT
+// tiles' softmax states and q fragments
+template <int D, bool QBF16, int NT>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1)))
+void decode_int8_wide_kernel(DecodeArgs a) {
+  decode_wave<Int8Kind<D, QBF16, NT == 2 ? kInt8PageGroup : 1>, true, NT>(a);
+}
+
+template <int D, bool BF16, int NT>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1)))
+void decode_16bit_wide_kernel(DecodeArgs a) {
+  decode_wave<F16Kind<D, BF16, NT == 2 ? k16PageGroup : 1>, true, NT>(a);
 }
 
 template <int D, bool QBF16>
@@ -1378,12 +1605,33 @@ hipError_t launch_decode_int8(const DecodeArgs& a, int head_dim, bool q_bf16, hi
   return launch_pair(k, a, head_dim, s);
 }
 
+int multi_waves_per_simd(int unit_tiles) { return unit_tiles == 1 ? kInt8WavesPerSimd : 1; }
+
+template <template <int, bool, int> class W, int D, bool B>
+DecodeKernel wide_kernel(int unit_tiles) {
+  return unit_tiles == 2 ? W<D, B, 2>::kernel : W<D, B, 4>::kernel;
+}
+template <int D, bool B, int NT>
+struct Int8Wide {
+  static constexpr DecodeKernel kernel = decode_int8_wide_kernel<D, B, NT>;
+};
+template <int D, bool B, int NT>
+struct Bits16Wide {
+  static constexpr DecodeKernel kernel = decode_16bit_wide_kernel<D, B, NT>;
+};
+
 hipError_t launch_decode_int8_multi(const DecodeArgs& a, int head_dim, bool q_bf16,
                                     hipStream_t s) {
-  const DecodeKernel k =
-      head_dim == 128
-          ? (q_bf16 ? decode_int8_multi_kernel<128, true> : decode_int8_multi_kernel<128, false>)
-          : (q_bf16 ? decode_int8_multi_kernel<64, true> : decode_int8_multi_kernel<64, false>);
+  DecodeKernel k;
+  if (a.unit_tiles == 1)
+    k = head_dim == 128
+            ? (q_bf16 ? decode_int8_multi_kernel<128, true> : decode_int8_multi_kernel<128, false>)
+            : (q_bf16 ? decode_int8_multi_kernel<64, true> : decode_int8_multi_kernel<64, false>);
+  else
+    k = head_dim == 128 ? (q_bf16 ? wide_kernel<Int8Wide, 128, true>(a.unit_tiles)
+                                  : wide_kernel<Int8Wide, 128, false>(a.unit_tiles))
+                        : (q_bf16 ? wide_kernel<Int8Wide, 64, true>(a.unit_tiles)
+                                  : wide_kernel<Int8Wide, 64, false>(a.unit_tiles));
   return launch_pair(k, a, head_dim, s);
 }
 
@@ -1407,10 +1655,17 @@ hipError_t launch_decode_16bit(const DecodeArgs& a, int head_dim, bool kv_bf16,
 
 hipError_t launch_decode_16bit_multi(const DecodeArgs& a, int head_dim, bool kv_bf16,
                                      hipStream_t s) {
-  const DecodeKernel k =
-      head_dim == 128
-          ? (kv_bf16 ? decode_16bit_multi_kernel<128, true> : decode_16bit_multi_kernel<128, false>)
-          : (kv_bf16 ? decode_16bit_multi_kernel<64, true> : decode_16bit_multi_kernel<64, false>);
+  DecodeKernel k;
+  if (a.unit_tiles == 1)
+    k = head_dim == 128 ? (kv_bf16 ? decode_16bit_multi_kernel<128, true>
+                                   : decode_16bit_multi_kernel<128, false>)
+                        : (kv_bf16 ? decode_16bit_multi_kernel<64, true>
+                                   : decode_16bit_multi_kernel<64, false>);
+  else
+    k = head_dim == 128 ? (kv_bf16 ? wide_kernel<Bits16Wide, 128, true>(a.unit_tiles)
+                                   : wide_kernel<Bits16Wide, 128, false>(a.unit_tiles))
+                        : (kv_bf16 ? wide_kernel<Bits16Wide, 64, true>(a.unit_tiles)
+                                   : wide_kernel<Bits16Wide, 64, false>(a.unit_tiles));
   return launch_pair(k, a, head_dim, s);
 }
 

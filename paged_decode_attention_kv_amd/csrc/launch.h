@@ -13,17 +13,12 @@ constexpr int kBlockSize = 16;        // tokens per page
 constexpr int kMaxGroup = 16;         // query heads per KV head (one MFMA N tile)
 constexpr int kWaves = 4;             // waves per decode workgroup
 constexpr int kMinPagesPerWave = 4;   // decode: fewest pages a busy wave gets
-#ifndef PDAKV_I8_W
-#define PDAKV_I8_W 2
-#define PDAKV_I8_G 2
-#define PDAKV_16_W 2
-#define PDAKV_16_G 2
-#endif
-constexpr int kInt8WavesPerSimd = PDAKV_I8_W;  // INT8 decode occupancy
-constexpr int kInt8PageGroup = PDAKV_I8_G;     // pages per register buffer
-constexpr int k16WavesPerSimd = PDAKV_16_W;    // 16-bit decode occupancy
-constexpr int k16PageGroup = PDAKV_16_G;
-constexpr int kCUs = 256;                      // MI355X compute units
+constexpr int kInt8WavesPerSimd = 2;  // INT8 decode occupancy
+constexpr int kInt8PageGroup = 2;     // pages per register buffer
+constexpr int k16WavesPerSimd = 2;    // 16-bit decode occupancy
+constexpr int k16PageGroup = 2;
+constexpr int kSimdsPerCU = 4;
+constexpr int kDefaultCUs = 256;      // MI355X compute units (when no device answers)
 constexpr int kMaxMergeWaves = 8;              // merge: waves per (sequence, q head)
 constexpr int kLdsPerWave = 16384;             // decode: LDS staging budget per wave
 constexpr int kMaxPagesPerWave = 128; // decode: block ids a wave holds (2 per lane)
@@ -59,10 +54,11 @@ struct DecodeArgs {
   int num_seqs, num_q_heads, num_kv_heads, group, max_ctx;
   // query tokens per sequence (the last qtok positions, causal among them);
   // their cols = qtok * group (token, head) columns per KV head are split
-  // into ntile tiles of up to 16 MFMA columns, and each (KV head, tile) is a
-  // unit of its own: vheads = num_kv_heads * ntile units per sequence
-  int qtok, cols, ntile, vheads;
-  int slot_cols;  // columns per workspace slot and LDS segment: min(cols, 16)
+  // into tiles of up to 16 MFMA columns, unit_tiles consecutive tiles of a
+  // KV head form a unit (streamed once for all its tiles), so a KV head has
+  // units_per_head units: vheads = num_kv_heads * units_per_head per sequence
+  int qtok, cols, unit_tiles, units_per_head, vheads;
+  int slot_cols;  // columns per workspace slot: min(cols, 16 * unit_tiles)
   float scale_log2;  // sm_scale * log2(e) (times the K scale for static
                      // scales): logits are kept in base 2
   float out_mul;     // output factor: the V scale for static scales, else 1
@@ -123,6 +119,9 @@ hipError_t launch_decode_int8_multi(const DecodeArgs& a, int head_dim, bool q_bf
                                     hipStream_t s);
 hipError_t launch_decode_16bit_multi(const DecodeArgs& a, int head_dim, bool kv_bf16,
                                      hipStream_t s);
+// Waves per SIMD of the several-token kernels with unit_tiles tiles per unit
+// (the host plans the grid for it).
+int multi_waves_per_simd(int unit_tiles);
 hipError_t launch_decode_16bit(const DecodeArgs& a, int head_dim, bool kv_bf16,
                                hipStream_t s);
 hipError_t launch_quant_write_static(const WriteArgs& a, int head_dim, bool src_bf16,

@@ -280,19 +280,36 @@ def test_multi_validation(P, fn, change, status):
     assert getattr(P._lib, fn)(*_multi_args(**change)) == status
 
 
+def _plan_waves(waves_per_simd, B, heads, L):
+    """The decode grid's wave count (256 CUs x 4 SIMDs resident per wave per
+    SIMD; at most 128 and at least 4 items per wave; a multiple of 4)."""
+    items = B * heads * -(-L // 16)
+    v = max(256 * 4 * waves_per_simd, -(-items // 128))
+    v = max(min(v, -(-items // 4)), 1)
+    return -(-v // 4) * 4
+
+
 @pytest.mark.parametrize("B,T,hq,hkv,L", [(64, 1, 32, 8, 8193), (64, 4, 32, 8, 8193),
                                           (8, 8, 32, 8, 32768), (32, 3, 14, 2, 4104),
-                                          (1, 16, 8, 8, 100), (3, 2, 16, 1, 40)])
+                                          (1, 16, 8, 8, 100), (3, 2, 16, 1, 40),
+                                          (4, 128, 32, 8, 3000), (2, 256, 14, 2, 4000),
+                                          (5, 11, 32, 8, 900)])
 def test_multi_workspace_formula(P, B, T, hq, hkv, L):
-    """[waves + B * Hkv * tiles][min(T * G, 16)][D + 2] floats (16-byte
-    padded), then B * Hkv * tiles records; the waves are those of the plan
-    with Hkv * tiles heads. T = 1 is the one-token workspace."""
+    """Units of a KV head: its T * G query columns in tiles of 16, one, two
+    or four tiles per unit (four from three tiles on). Workspace:
+    [waves + B * units][min(T * G, 16 * tiles per unit)][D + 2] floats
+    (16-byte padded), then B * units records; the waves are those of the
+    plan with units as heads (one wave per SIMD with several tiles per
+    unit). T = 1 is the one-token workspace."""
     G = hq // hkv
     cols = T * G
     tiles = -(-cols // 16)
-    vh = hkv * tiles
-    waves, _ = P.pdakv_decode_plan(P.KV_INT8_SYM, B, vh, L)
-    partials = -(-(waves + B * vh) * min(cols, 16) * 130 * 4 // 16) * 16
+    per_unit = 4 if tiles >= 3 else tiles
+    vh = hkv * -(-tiles // per_unit)
+    waves = _plan_waves(2 if per_unit == 1 else 1, B, vh, L)
+    if per_unit == 1:
+        assert waves == P.pdakv_decode_plan(P.KV_INT8_SYM, B, vh, L)[0]
+    partials = -(-(waves + B * vh) * min(cols, 16 * per_unit) * 130 * 4 // 16) * 16
     assert P.pdakv_decode_multi_workspace_bytes(B, T, hq, hkv, 128, L) == partials + B * vh * 8
     if T == 1:
         assert (P.pdakv_decode_multi_workspace_bytes(B, 1, hq, hkv, 128, L) ==

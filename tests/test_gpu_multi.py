@@ -156,3 +156,31 @@ def test_multi_16bit_outputs_round_the_fp32_output(P, out_dtype):
     ref = _gpu_multi(P, wl, pool, P.KV_INT8_SYM, q)
     low = _gpu_multi(P, wl, pool, P.KV_INT8_SYM, q, out_dtype)
     assert torch.equal(low, ref.to(out_dtype))
+
+
+@pytest.mark.parametrize("fmt_name", ["int8", "16bit"])
+@pytest.mark.parametrize("T", [16, 32, 64, 128])
+def test_multi_wide_query_blocks(P, fmt_name, T):
+    """Chunked-prefill widths at the Llama shape (G = 4): 64 to 512 query
+    columns per KV head, so units hold four 16-column tiles that share every
+    page they stream; ragged contexts, some shorter than T (zero rows for
+    query tokens before the sequence start)."""
+    wl = build("multi-wide", 300 + T, [("prefill", [700, 5, 130, 2 * T + 3, 1100])], 32, 8, 128,
+               "f16", "outlier", shuffle=True, spare_blocks=2)
+    _say(f"multi wide {fmt_name} T={T} ({T * 4} columns) lens {wl.context_lens.tolist()}")
+    out, _, _ = _check(P, wl, fmt_name, T, seed=400 + T)
+    assert torch.all(out[1, :T - 5] == 0)  # positions before the start of sequence 1
+
+
+@pytest.mark.parametrize("fmt_name", ["int8", "16bit"])
+@pytest.mark.parametrize("hq,hkv,d,dt", [(32, 8, 128, "f16"), (14, 2, 64, "bf16")])
+def test_multi_256_token_chunk(P, fmt_name, hq, hkv, d, dt):
+    """A 256-token chunk decoded against the cache it was just written to
+    (chunked prefill): each sequence's last 256 positions are the query
+    tokens, after prefixes of different lengths (Llama shape: 1,024 columns
+    per KV head; small-head GQA 7 at D = 64: 1,792)."""
+    T = 256
+    wl = build("multi-chunk", 500 + hq, [("prefix", [3000, 40]), ("chunk", [T, T])], hq, hkv, d,
+               dt, "outlier" if dt == "f16" else "normal", shuffle=True)
+    _say(f"multi chunk {fmt_name} {hq}/{hkv}/{d} {dt}: T={T}, lens {wl.context_lens.tolist()}")
+    _check(P, wl, fmt_name, T, seed=600 + hq)
