@@ -392,7 +392,8 @@ int paged_attn_decode_int8_static_append(
  *         sizes, 16-byte aligned.
  * Other arguments as paged_attn_decode_int8. The T x (num_q_heads /
  * num_kv_heads) query columns of a KV head are processed in tiles of 16
- * matrix-instruction columns that stream the KV head's pages once per tile.
+ * matrix-instruction columns; a KV head's pages are streamed once for every
+ * run of up to 4 tiles (once in all for up to 64 columns).
  * Returns PDAKV_ERR_INVALID_ARG for num_query_tokens < 1. */
 int paged_attn_decode_int8_multi(
     void* out, int out_dtype, int64_t out_stride_seq, int64_t out_stride_tok,
@@ -416,10 +417,10 @@ int paged_attn_decode_fp16_multi(
     int32_t* err_flag, void* stream);
 
 /* Workspace of the several-token decode calls: the layout of
- * pdakv_decode_workspace_bytes with units of (sequence, KV head, tile of 16
- * query columns), min(T * G, 16) columns per partial slot; 0 when num_seqs,
- * num_query_tokens or max_context_len is 0. With num_query_tokens = 1 it
- * equals pdakv_decode_workspace_bytes. */
+ * pdakv_decode_workspace_bytes with units of (sequence, KV head, run of up
+ * to 4 tiles of 16 query columns), min(T * G, 64) columns per partial slot;
+ * 0 when num_seqs, num_query_tokens or max_context_len is 0. With
+ * num_query_tokens = 1 it equals pdakv_decode_workspace_bytes. */
 size_t pdakv_decode_multi_workspace_bytes(int num_seqs, int num_query_tokens, int num_q_heads,
                                           int num_kv_heads, int head_dim, int max_context_len);
 

@@ -91,9 +91,10 @@ int merge_waves(int num_seqs, int num_kv_heads, int max_context_len, int64_t wav
 
 // Query columns of a call: T query tokens x G query heads per KV head, in
 // tiles of at most 16 (one MFMA operand). A unit is one KV head's run of up
-// to unit_tiles tiles, whose pages are streamed once for all of them: one
-// tile per unit for up to 16 columns, two for up to 32, four beyond (those
-// kernels run one wave per SIMD for the registers of the tiles' states).
+// to unit_tiles tiles, whose pages are streamed once for all of them: all
+// the tiles of a KV head up to kMaxUnitTiles, else units of that many.
+// waves_per_simd: that of the INT8 kernel, whose plan has the most waves
+// (its workspace serves the 16-bit kernel too).
 struct Columns {
   int cols, unit_tiles, units_per_head, slot_cols, waves_per_simd;
 };
@@ -101,10 +102,10 @@ Columns columns(int num_q_heads, int num_kv_heads, int num_query_tokens) {
   Columns c;
   c.cols = num_query_tokens * (num_q_heads / num_kv_heads);
   const int tiles = (c.cols + 15) / 16;
-  c.unit_tiles = tiles >= 3 ? 4 : tiles;
+  c.unit_tiles = std::min(tiles, pdakv::kMaxUnitTiles);
   c.units_per_head = (tiles + c.unit_tiles - 1) / c.unit_tiles;
   c.slot_cols = std::min(c.cols, 16 * c.unit_tiles);
-  c.waves_per_simd = pdakv::multi_waves_per_simd(c.unit_tiles);
+  c.waves_per_simd = pdakv::wide_waves_per_simd(PDAKV_KV_INT8_SYM, c.unit_tiles);
   return c;
 }
 
@@ -282,7 +283,8 @@ int decode_common(int fmt, Scales sc, const Rows& r, const AppendRows* app,
   a.out_mul = fmt == PDAKV_KV_INT8_STATIC ? sc.v : 1.f;
   a.k_scale = sc.k;
   a.v_scale = sc.v;
-  const int wps = r.multi ? cols.waves_per_simd : format_waves_per_simd(fmt);
+  const int wps = r.multi ? pdakv::wide_waves_per_simd(fmt, cols.unit_tiles)
+                          : format_waves_per_simd(fmt);
   a.num_waves = static_cast<int>(plan_waves(wps, num_seqs, a.vheads, max_context_len));
   a.merge_waves = merge_waves(num_seqs, a.vheads, max_context_len, a.num_waves);
   {

@@ -291,11 +291,10 @@ __device__ __forceinline__ void load_int8_page(Int8Page<D>& pg, const uint8_t* h
   pg.vs = ld8(r, so + 32);
 }
 
-// The matrix-instruction operands of a page's codes: K fragment j (the A
-// operand of QK instruction j: 8 codes of token i16) and V fragment k (the A
-// operand of PV instruction k: one dimension of four tokens), as fp16.
-// Converted from the loaded codes where they are used (one query tile per
-// page), or once per page into a Int8Frag when several query tiles share it.
+// The matrix-instruction operands of a page's codes, converted where they
+// are used: K fragment j (the A operand of QK instruction j: 8 codes of
+// token i16) and V fragment k (the A operand of PV instruction k: one
+// dimension of four tokens), as fp16.
 template <class Pg>
 __device__ __forceinline__ h8_t k_frag(const Pg& pg, int j) {
   const u2_t c0 = i8x4_to_f16x4_perm(pg.k[j / 2][2 * (j % 2)]);
@@ -305,21 +304,6 @@ __device__ __forceinline__ h8_t k_frag(const Pg& pg, int j) {
 template <class Pg>
 __device__ __forceinline__ h4_t v_frag(const Pg& pg, int k) {
   return __builtin_bit_cast(h4_t, i8x4_to_f16x4_perm(pg.v[k / 4][k % 4]));
-}
-
-template <int D, bool Scales>
-struct Int8Frag {
-  h8_t kf[D / 32];
-  h4_t vf[D / 16];
-  u2_t ks, vs;  // (per-token scales only)
-};
-template <int D, bool Scales>
-__device__ __forceinline__ h8_t k_frag(const Int8Frag<D, Scales>& fr, int j) {
-  return fr.kf[j];
-}
-template <int D, bool Scales>
-__device__ __forceinline__ h4_t v_frag(const Int8Frag<D, Scales>& fr, int k) {
-  return fr.vf[k];
 }
 
 template <int D, class Pg>
@@ -363,35 +347,50 @@ __device__ __forceinline__ int lane_token(int page_tok) {
 // L get V scale 1.0 (their slots may hold anything); those at or past Lc get
 // logit -inf. (A separate unmasked path for full pages costs more registers
 // than the masks cost instructions.)
-template <int D, class Pg>
-__device__ __forceinline__ void int8_page_step(const Pg& pg, const h8_t* qf,
-                                               float qscale, int page_tok, int L, int Lmin,
-                                               int Lc, SoftmaxState<D / 16>& st) {
-  constexpr int ND = D / 16;
-  const f4_t s = int8_qk<D>(pg, qf);
+// The scale terms of the lane's four tokens 4*kb + (0..3): the K scale, and
+// the V scale sV = f * 2^e (f in [0.5, 1)) as its exponent and mantissa;
+// tokens at or past L (tail pages only) get V scale 1.0, as their slots may
+// hold anything.
+struct TokenScales {
+  float sk[4];
+  int e[4];
+  _Float16 f[4];
+};
+template <class Pg>
+__device__ __forceinline__ TokenScales token_scales(const Pg& pg, bool tail, int tok0, int L) {
   const uint32_t ksw[2] = {pg.ks.x, pg.ks.y};
   uint32_t vsw[2] = {pg.vs.x, pg.vs.y};
-  const bool tail = page_tok + kBlockSize > Lmin;
-  const int tok0 = tail ? lane_token(page_tok) : 0;
   if (tail) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (tok0 + j >= L) vsw[j / 2] = (vsw[j / 2] & (0xFFFF0000u >> (16 * (j % 2)))) |
                                       (0x3C00u << (16 * (j % 2)));
   }
+  TokenScales ts;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    ts.sk[j] = f16_bits_to_f32(static_cast<uint16_t>(ksw[j / 2] >> (16 * (j % 2))));
+    const _Float16 sv =
+        __builtin_bit_cast(_Float16, static_cast<uint16_t>(vsw[j / 2] >> (16 * (j % 2))));
+    ts.e[j] = __builtin_amdgcn_frexp_exph(sv);
+    ts.f[j] = __builtin_amdgcn_frexp_manth(sv);
+  }
+  return ts;
+}
+
+// Softmax update of one query tile from its logit tile s: base-2 logits
+// plus the V scale's exponent (P = 2^(z - m) * f), tokens at or past Lc
+// masked, running max and sum, and the probabilities (V scale folded in) as
+// high and low fp16 parts for the PV product.
+template <int ND>
+__device__ __forceinline__ void int8_probs(const f4_t& s, const TokenScales& ts, float qscale,
+                                           bool tail, int tok0, int Lc, SoftmaxState<ND>& st,
+                                           h4_t& ph, h4_t& pl) {
   float z[4];
-  int e[4];
-  _Float16 f[4];
   float zmax = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float sk = f16_bits_to_f32(static_cast<uint16_t>(ksw[j / 2] >> (16 * (j % 2))));
-    const _Float16 sv =
-        __builtin_bit_cast(_Float16, static_cast<uint16_t>(vsw[j / 2] >> (16 * (j % 2))));
-    e[j] = __builtin_amdgcn_frexp_exph(sv);
-    f[j] = __builtin_amdgcn_frexp_manth(sv);
-    // base-2 logit plus the exponent of the V scale: P = 2^(z - m) * f
-    z[j] = s[j] * sk * qscale + static_cast<float>(e[j]);
+    z[j] = s[j] * ts.sk[j] * qscale + static_cast<float>(ts.e[j]);
     if (tail) z[j] = tok0 + j < Lc ? z[j] : -INFINITY;
     zmax = max_nc(zmax, z[j]);
   }
@@ -400,14 +399,31 @@ __device__ __forceinline__ void int8_page_step(const Pg& pg, const h8_t* qf,
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float x = __builtin_amdgcn_exp2f(z[j] - st.mk);  // 2^(kPScale + z - m)
-    st.l += __builtin_amdgcn_ldexpf(x, -e[j]);
-    p[j] = x * static_cast<float>(f[j]);
+    st.l += __builtin_amdgcn_ldexpf(x, -ts.e[j]);
+    p[j] = x * static_cast<float>(ts.f[j]);
   }
   // p = hi + lo to 22 bits: hi is p converted to fp16 once (by the
   // conversion instruction itself, so that the compiler cannot fold the
   // product into a second, differently rounded conversion), lo the rest
-  const h4_t ph = split_hi(p);
-  const h4_t pl = split_lo(p, ph);
+  ph = split_hi(p);
+  pl = split_lo(p, ph);
+}
+
+// One page starting at token page_tok (wave-uniform). The tokens at or past
+// L get V scale 1.0 (their slots may hold anything); those at or past Lc get
+// logit -inf. (A separate unmasked path for full pages costs more registers
+// than the masks cost instructions.)
+template <int D, class Pg>
+__device__ __forceinline__ void int8_page_step(const Pg& pg, const h8_t* qf,
+                                               float qscale, int page_tok, int L, int Lmin,
+                                               int Lc, SoftmaxState<D / 16>& st) {
+  constexpr int ND = D / 16;
+  const f4_t s = int8_qk<D>(pg, qf);
+  const bool tail = page_tok + kBlockSize > Lmin;
+  const int tok0 = tail ? lane_token(page_tok) : 0;
+  const TokenScales ts = token_scales(pg, tail, tok0, L);
+  h4_t ph, pl;
+  int8_probs(s, ts, qscale, tail, tok0, Lc, st, ph, pl);
   // O^T += V^T P^T; instruction k covers dims 64*(k/4) + 4*(row) + k%4, its
   // K-slots hold tokens 4*kb + (0..3)
 #pragma unroll
@@ -443,14 +459,13 @@ __device__ __forceinline__ void load_static_page(StaticPage<D>& pg, const uint8_
 
 // Tokens at or past the limit L get logit -inf (probability 0; any byte in
 // their slots is a finite code, so 0 * code adds nothing).
-template <int D, class Pg>
-__device__ __forceinline__ void static_page_step(const Pg& pg, const h8_t* qf,
-                                                 float qscale, int page_tok, int Lmin, int Lc,
-                                                 SoftmaxState<D / 16>& st) {
-  constexpr int ND = D / 16;
-  const f4_t s = int8_qk<D>(pg, qf);
-  const bool tail = page_tok + kBlockSize > Lmin;
-  const int tok0 = tail ? lane_token(page_tok) : 0;
+// Softmax update of one query tile over static-scale codes (the K scale is
+// part of qscale): tokens at or past Lc masked (any byte in a slot past the
+// context is a finite code, so 0 * code adds nothing), running max and sum,
+// probabilities as high and low fp16 parts.
+template <int ND>
+__device__ __forceinline__ void static_probs(const f4_t& s, float qscale, bool tail, int tok0,
+                                             int Lc, SoftmaxState<ND>& st, h4_t& ph, h4_t& pl) {
   float z[4];
   float zmax = -INFINITY;
 #pragma unroll
@@ -460,16 +475,26 @@ __device__ __forceinline__ void static_page_step(const Pg& pg, const h8_t* qf,
     zmax = max_nc(zmax, z[j]);
   }
   raise_max(st, zmax);
-  float hi[4], lo[4];
+  float x[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float x = __builtin_amdgcn_exp2f(z[j] - st.mk);  // 2^(kPScale + z - m)
-    st.l += x;
-    hi[j] = static_cast<float>(static_cast<_Float16>(x));
-    lo[j] = x - hi[j];
+    x[j] = __builtin_amdgcn_exp2f(z[j] - st.mk);  // 2^(kPScale + z - m)
+    st.l += x[j];
   }
-  const h4_t ph = __builtin_bit_cast(h4_t, u2_t{pack_f16x2(hi[0], hi[1]), pack_f16x2(hi[2], hi[3])});
-  const h4_t pl = __builtin_bit_cast(h4_t, u2_t{pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3])});
+  ph = split_hi(x);
+  pl = split_lo(x, ph);
+}
+
+template <int D, class Pg>
+__device__ __forceinline__ void static_page_step(const Pg& pg, const h8_t* qf,
+                                                 float qscale, int page_tok, int Lmin, int Lc,
+                                                 SoftmaxState<D / 16>& st) {
+  constexpr int ND = D / 16;
+  const f4_t s = int8_qk<D>(pg, qf);
+  const bool tail = page_tok + kBlockSize > Lmin;
+  const int tok0 = tail ? lane_token(page_tok) : 0;
+  h4_t ph, pl;
+  static_probs(s, qscale, tail, tok0, Lc, st, ph, pl);
 #pragma unroll
   for (int k = 0; k < ND; ++k) {
     const h4_t vw = v_frag(pg, k);
@@ -507,29 +532,72 @@ struct Int8Kind {
     else
       load_int8_page<D>(pg, hp, live, i16, kb);
   }
-  // one page against this query tile; Pg is the loaded page or its
-  // converted fragments (Frag)
-  template <class Pg>
-  __device__ __forceinline__ void step(const Pg& pg, int page_tok, int L, int Lmin, int Lc,
+  // one page against this query tile
+  __device__ __forceinline__ void step(const Page& pg, int page_tok, int L, int Lmin, int Lc,
                                        SoftmaxState<D / 16>& st) const {
     if constexpr (Static)
       static_page_step<D>(pg, qf, qscale, page_tok, Lmin, Lc, st);
     else
       int8_page_step<D>(pg, qf, qscale, page_tok, L, Lmin, Lc, st);
   }
-  // a page's codes as fp16 operands, converted once for several query tiles
-  using Frag = Int8Frag<D, !Static>;
-  static __device__ __forceinline__ Frag convert(const Page& pg) {
-    Frag fr;
+  // One page against the first nt of NT query tiles (tile c: q fragments
+  // kd[c], state st[c], column limit Lc[c]), two tiles at a time: every K and
+  // V fragment is converted once per pair of tiles and fed to the matrix
+  // instructions of both, and the token scales are decoded once per pair.
+  // (Four tiles at once need more registers than one wave has.)
+  template <int NT>
+  static __device__ __forceinline__ void step_tiles(const Page& pg, const Int8Kind* kd, int nt,
+                                                    int page_tok, int L, int Lmin,
+                                                    const int* Lc, SoftmaxState<D / 16>* st) {
+    if constexpr (NT > 2) {
 #pragma unroll
-    for (int j = 0; j < D / 32; ++j) fr.kf[j] = k_frag(pg, j);
-#pragma unroll
-    for (int k = 0; k < D / 16; ++k) fr.vf[k] = v_frag(pg, k);
-    if constexpr (!Static) {
-      fr.ks = pg.ks;
-      fr.vs = pg.vs;
+      for (int c = 0; c < NT; c += 2) {
+        if (c < nt) step_tiles<2>(pg, kd + c, nt - c, page_tok, L, Lmin, Lc + c, st + c);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
     }
-    return fr;
+    constexpr int ND = D / 16;
+    f4_t s[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) s[c] = f4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < D / 32; ++j) {
+      const h8_t kf = k_frag(pg, j);
+#pragma unroll
+      for (int c = 0; c < NT; ++c)
+        if (c < nt) s[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, kd[c].qf[j], s[c], 0, 0, 0);
+    }
+    const bool tail = page_tok + kBlockSize > Lmin;
+    const int tok0 = tail ? lane_token(page_tok) : 0;
+    h4_t ph[NT], pl[NT];
+    // (the tiles' softmax updates one after the other: interleaving them
+    // costs registers)
+    if constexpr (Static) {
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (c < nt) static_probs(s[c], kd[c].qscale, tail, tok0, Lc[c], st[c], ph[c], pl[c]);
+      }
+    } else {
+      const TokenScales ts = token_scales(pg, tail, tok0, L);
+#pragma unroll
+      for (int c = 0; c < NT; ++c) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (c < nt) int8_probs(s[c], ts, kd[c].qscale, tail, tok0, Lc[c], st[c], ph[c], pl[c]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < ND; ++k) {
+      const h4_t vw = v_frag(pg, k);
+#pragma unroll
+      for (int c = 0; c < NT; ++c)
+        if (c < nt) {
+          st[c].acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(vw, ph[c], st[c].acc[k], 0, 0, 0);
+          st[c].acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(vw, pl[c], st[c].acc[k], 0, 0, 0);
+        }
+    }
   }
   // dimension of accumulator element acc[k][j] in lane (i16, kb)
   static __device__ __forceinline__ int acc_dim(int k, int j, int kb) {
@@ -803,9 +871,19 @@ struct F16Kind {
                                        SoftmaxState<D / 16>& st) const {
     page16_step<D, BF16>(pg, qf, scale_log2, page_tok, L, Lmin, Lc, st);
   }
-  // 16-bit values are the operands as loaded
-  using Frag = Page;
-  static __device__ __forceinline__ const Page& convert(const Page& pg) { return pg; }
+  // One page against the first nt of NT query tiles: 16-bit values need no
+  // conversion, so each tile runs its own step on the loaded page.
+  template <int NT>
+  static __device__ __forceinline__ void step_tiles(const Page& pg, const F16Kind* kd, int nt,
+                                                    int page_tok, int L, int Lmin,
+                                                    const int* Lc, SoftmaxState<D / 16>* st) {
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      if (c < nt) kd[c].step(pg, page_tok, L, Lmin, Lc[c], st[c]);
+      // one tile after the other (interleaving them costs registers)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
   static __device__ __forceinline__ int acc_dim(int k, int j, int kb) {
     return 32 * (k / 2) + 8 * kb + 2 * j + (k % 2);
   }
@@ -1283,6 +1361,7 @@ __device__ __forceinline__ int run_pass_wide(const DecodeArgs& a, K* kind, Curso
   // query token j of the sequence sits at position L - qtok + j and sees the
   // positions up to it; Lmin: the first query token's limit
   const int Lmin = L - a.qtok + 1;
+  const int nt = (uc.n + 15) / 16;  // tiles of the unit (wave-uniform)
   int Lc[NT];
   SoftmaxState<ND> st[NT];
 #pragma unroll
@@ -1310,14 +1389,10 @@ __device__ __forceinline__ int run_pass_wide(const DecodeArgs& a, K* kind, Curso
       if (i >= items) return false;
       const int t = (p0 + i) * kBlockSize;
       const bool ok = blk[j] >= 0;  // a missing page is masked whole
-      const typename K::Frag fr = K::convert(grp[j]);
+      int lim[NT];
 #pragma unroll
-      for (int c = 0; c < NT; ++c) {
-        if (16 * c < uc.n)
-          kind[c].step(fr, t, ok ? L : t, ok ? Lmin : t, ok ? Lc[c] : t, st[c]);
-        // one tile after the other (interleaving them costs registers)
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int c = 0; c < NT; ++c) lim[c] = ok ? Lc[c] : t;
+      K::template step_tiles<NT>(grp[j], kind, nt, t, ok ? L : t, ok ? Lmin : t, lim, st);
     }
     return true;
   };
@@ -1425,18 +1500,19 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
   decode_wave<Int8Kind<D, QBF16, kInt8PageGroup>, true>(a);
 }
 
-// Several query tiles per unit: one wave per SIMD, for the registers of NT
-// tiles' softmax states and q fragments
+// Several query tiles per unit, one page per register buffer; the waves per
+// SIMD that the registers of NT tiles' softmax states and q fragments allow
+// (wide_waves_per_simd, which the host plans with)
 template <int D, bool QBF16, int NT>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1)))
-void decode_int8_wide_kernel(DecodeArgs a) {
-  decode_wave<Int8Kind<D, QBF16, NT == 2 ? kInt8PageGroup : 1>, true, NT>(a);
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
+    wide_waves_per_simd(PDAKV_KV_INT8_SYM, NT)))) void decode_int8_wide_kernel(DecodeArgs a) {
+  decode_wave<Int8Kind<D, QBF16, 1>, true, NT>(a);
 }
 
 template <int D, bool BF16, int NT>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(1)))
-void decode_16bit_wide_kernel(DecodeArgs a) {
-  decode_wave<F16Kind<D, BF16, NT == 2 ? k16PageGroup : 1>, true, NT>(a);
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
+    wide_waves_per_simd(PDAKV_KV_16BIT, NT)))) void decode_16bit_wide_kernel(DecodeArgs a) {
+  decode_wave<F16Kind<D, BF16, 1>, true, NT>(a);
 }
 
 template <int D, bool QBF16>
@@ -1605,11 +1681,10 @@ hipError_t launch_decode_int8(const DecodeArgs& a, int head_dim, bool q_bf16, hi
   return launch_pair(k, a, head_dim, s);
 }
 
-int multi_waves_per_simd(int unit_tiles) { return unit_tiles == 1 ? kInt8WavesPerSimd : 1; }
-
+// units of 2 or 4 tiles (a unit of 3 runs in the 4-tile kernel)
 template <template <int, bool, int> class W, int D, bool B>
 DecodeKernel wide_kernel(int unit_tiles) {
-  return unit_tiles == 2 ? W<D, B, 2>::kernel : W<D, B, 4>::kernel;
+  return unit_tiles == 2 ? W<D, B, 2>::kernel : W<D, B, kMaxUnitTiles>::kernel;
 }
 template <int D, bool B, int NT>
 struct Int8Wide {

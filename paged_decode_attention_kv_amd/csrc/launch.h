@@ -7,6 +7,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include "../../include/pdakv.h"
+
 namespace pdakv {
 
 constexpr int kBlockSize = 16;        // tokens per page
@@ -22,6 +24,14 @@ constexpr int kDefaultCUs = 256;      // MI355X compute units (when no device an
 constexpr int kMaxMergeWaves = 8;              // merge: waves per (sequence, q head)
 constexpr int kLdsPerWave = 16384;             // decode: LDS staging budget per wave
 constexpr int kMaxPagesPerWave = 128; // decode: block ids a wave holds (2 per lane)
+
+// Several-token decode: query tiles (16 columns each) per unit, at most
+// kMaxUnitTiles, and the waves per SIMD of the kernel for a unit of `tiles`
+// tiles (what the registers of that many tiles' states allow).
+constexpr int kMaxUnitTiles = 4;
+constexpr int wide_waves_per_simd(int kv_format, int tiles) {
+  return tiles == 1 ? 2 : (tiles == 2 && kv_format != PDAKV_KV_16BIT) ? 2 : 1;
+}
 
 struct WriteArgs {
   const void* k;
@@ -119,9 +129,7 @@ hipError_t launch_decode_int8_multi(const DecodeArgs& a, int head_dim, bool q_bf
                                     hipStream_t s);
 hipError_t launch_decode_16bit_multi(const DecodeArgs& a, int head_dim, bool kv_bf16,
                                      hipStream_t s);
-// Waves per SIMD of the several-token kernels with unit_tiles tiles per unit
-// (the host plans the grid for it).
-int multi_waves_per_simd(int unit_tiles);
+
 hipError_t launch_decode_16bit(const DecodeArgs& a, int head_dim, bool kv_bf16,
                                hipStream_t s);
 hipError_t launch_quant_write_static(const WriteArgs& a, int head_dim, bool src_bf16,

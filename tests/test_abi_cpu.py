@@ -295,18 +295,18 @@ def _plan_waves(waves_per_simd, B, heads, L):
                                           (4, 128, 32, 8, 3000), (2, 256, 14, 2, 4000),
                                           (5, 11, 32, 8, 900)])
 def test_multi_workspace_formula(P, B, T, hq, hkv, L):
-    """Units of a KV head: its T * G query columns in tiles of 16, one, two
-    or four tiles per unit (four from three tiles on). Workspace:
+    """Units of a KV head: its T * G query columns in tiles of 16, all of
+    them in one unit up to 4 tiles, else units of 4. Workspace:
     [waves + B * units][min(T * G, 16 * tiles per unit)][D + 2] floats
     (16-byte padded), then B * units records; the waves are those of the
-    plan with units as heads (one wave per SIMD with several tiles per
-    unit). T = 1 is the one-token workspace."""
+    INT8 plan with units as heads (two waves per SIMD up to two tiles per
+    unit, one beyond). T = 1 is the one-token workspace."""
     G = hq // hkv
     cols = T * G
     tiles = -(-cols // 16)
-    per_unit = 4 if tiles >= 3 else tiles
+    per_unit = min(tiles, 4)
     vh = hkv * -(-tiles // per_unit)
-    waves = _plan_waves(2 if per_unit == 1 else 1, B, vh, L)
+    waves = _plan_waves(2 if per_unit <= 2 else 1, B, vh, L)
     if per_unit == 1:
         assert waves == P.pdakv_decode_plan(P.KV_INT8_SYM, B, vh, L)[0]
     partials = -(-(waves + B * vh) * min(cols, 16 * per_unit) * 130 * 4 // 16) * 16
