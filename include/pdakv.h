@@ -61,16 +61,22 @@
  * A token at position t of a sequence lives in page block_table[t / 16] at
  * slot t % 16; writers address it as slot_id = page * 16 + t % 16.
  *
- * INT8 page (kv_format PDAKV_KV_INT8_SYM), for each KV head h in order, a head
- * block of 2*16*D + 4*16 bytes:
+ * INT8 page (kv_format PDAKV_KV_INT8_SYM): every KV head's codes, then every
+ * KV head's scales. For each KV head h in order, a code block of 2*16*D bytes
+ * at h*32*D:
  *     +0          K codes  int8 [16][D]        token-major
  *     +16*D       V codes  int8 [4][D][4]      byte (p/4)*4*D + 4*d + p%4
- *     +32*D       K scales fp16 [16]
- *     +32*D+32    V scales fp16 [16]
+ * then, at Hkv*32*D + 64*h, the head's scales as four 16-byte records, one
+ * per group of four tokens (record p/4 at 16*(p/4)):
+ *     +2*(p%4)     K scale fp16 of token p
+ *     +8+2*(p%4)   V scale fp16 of token p
  *   page_bytes = Hkv * (32*D + 64): 33,280 for (16, 8, 128), 4,224 for
  *   (16, 2, 64). The V codes are grouped four tokens at a time so that one
  *   32-bit word holds one dimension of four consecutive tokens, which is the
- *   operand shape of the matrix instructions the reader uses.
+ *   operand shape of the matrix instructions the reader uses; the scales sit
+ *   after all code blocks so that each code block starts at a multiple of
+ *   32*D bytes into the page, and one 16-byte read gives a token group's K
+ *   and V scales.
  * Static-scale INT8 page (kv_format PDAKV_KV_INT8_STATIC), for each KV head h,
  * a head block of 2*16*D bytes:
  *     +0          K codes  int8 [16][D]        token-major

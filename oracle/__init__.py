@@ -49,7 +49,8 @@ from .pages import (  # noqa: F401
     KV_16BIT,
     KV_INT8_STATIC,
     page_bytes,
-    int8_head_offsets,
+    int8_layout,
+    int8_token_bytes,
     new_pool,
     write_int8_tokens,
     write_16bit_tokens,

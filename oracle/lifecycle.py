@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .pages import (KV_16BIT, KV_INT8_STATIC, KV_INT8_SYM, _v_index, int8_head_offsets,
+from .pages import (KV_16BIT, KV_INT8_STATIC, KV_INT8_SYM, _v_index, int8_token_bytes,
                     page_bytes)
 
 
@@ -58,12 +58,8 @@ def _token_byte_index(kv_format: int, block_size: int, head_dim: int, num_kv_hea
     d = head_dim
     dd = np.arange(d)
     if kv_format == KV_INT8_SYM:
-        off = int8_head_offsets(block_size, d)
-        base = blk * page_len + head * off["head_bytes"]
-        parts = [base[:, None] + off["k_codes"] + pos[:, None] * d + dd,
-                 base[:, None] + off["v_codes"] + _v_index(pos[:, None], dd[None, :], d),
-                 base[:, None] + off["k_scales"] + 2 * pos[:, None] + np.arange(2),
-                 base[:, None] + off["v_scales"] + 2 * pos[:, None] + np.arange(2)]
+        page0 = (blk * page_len)[:, None]
+        parts = [page0 + i for i in int8_token_bytes(block_size, num_kv_heads, d, head, pos)]
     elif kv_format == KV_INT8_STATIC:
         base = blk * page_len + head * 2 * block_size * d
         parts = [base[:, None] + pos[:, None] * d + dd,

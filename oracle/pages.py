@@ -9,14 +9,17 @@ inside a page is not on the pages; this module implements the layout that the
 library's C header documents, written out again here from that description
 (no code or constant is shared with the library):
 
-INT8 page, per KV head h (head block of ``2*bs*D + 4*bs`` bytes, heads in
-order, ``page_bytes = Hkv * (2*bs*D + 4*bs)``):
+INT8 page (``page_bytes = Hkv * (2*bs*D + 4*bs)``): the codes of every KV
+head first, then the scales of every KV head:
 
-    K codes   int8  [bs][D]           token-major
-    V codes   int8  [bs/4][D][4]      groups of 4 tokens, dimension-major
-                                      inside a group: byte (p//4)*4D + 4d + p%4
-    K scales  fp16  [bs]
-    V scales  fp16  [bs]
+    head h's codes at h * 2*bs*D:
+        K codes   int8  [bs][D]           token-major
+        V codes   int8  [bs/4][D][4]      groups of 4 tokens, dimension-major
+                                          inside a group: byte (p//4)*4D + 4d + p%4
+    head h's scales at Hkv * 2*bs*D + h * 4*bs, one 16-byte record per group
+    of 4 tokens (g = p//4, at 16*g):
+        K scales  fp16  [4]               token 4g + i at 2*i
+        V scales  fp16  [4]               token 4g + i at 8 + 2*i
 
 16-bit page (fp16 or bf16, same dtype as the model), per KV head h (head
 block of ``4*bs*D`` bytes, ``page_bytes = Hkv * 4*bs*D``):
@@ -61,16 +64,36 @@ def page_bytes(kv_format: int, block_size: int, num_kv_heads: int, head_dim: int
     raise ValueError("page_bytes: unknown format")
 
 
-def int8_head_offsets(block_size: int, head_dim: int) -> dict:
-    """Byte offsets of the four sub-arrays inside one INT8 head block."""
+def int8_layout(block_size: int, num_kv_heads: int, head_dim: int) -> dict:
+    """Byte offsets of an INT8 page's regions: each KV head's code block
+    (``code_bytes`` long, K codes then V codes) and scale block
+    (``scale_bytes`` long) after all code blocks."""
     bs, d = block_size, head_dim
-    return {
-        "k_codes": 0,
-        "v_codes": bs * d,
-        "k_scales": 2 * bs * d,
-        "v_scales": 2 * bs * d + 2 * bs,
-        "head_bytes": 2 * bs * d + 4 * bs,
-    }
+    return {"code_bytes": 2 * bs * d, "v_codes": bs * d,
+            "scales": num_kv_heads * 2 * bs * d, "scale_bytes": 4 * bs}
+
+
+def _int8_scale_offset(pos, is_v: int):
+    """Byte offset of token ``pos``'s K (is_v=0) or V (is_v=1) scale inside
+    its head's scale block: 16-byte records per group of 4 tokens."""
+    return (pos // 4) * 16 + 8 * is_v + 2 * (pos % 4)
+
+
+def int8_token_bytes(block_size: int, num_kv_heads: int, head_dim: int, head: int, pos):
+    """Byte indexes inside an INT8 page of token slot(s) ``pos`` (array [n])
+    of KV head ``head``: K codes [n, D], V codes [n, D], K scale [n, 2] and V
+    scale [n, 2] (little-endian fp16)."""
+    lay = int8_layout(block_size, num_kv_heads, head_dim)
+    d = head_dim
+    pos = np.asarray(pos, dtype=np.int64)[:, None]
+    dd = np.arange(d)[None, :]
+    two = np.arange(2)[None, :]
+    code = head * lay["code_bytes"]
+    sc = lay["scales"] + head * lay["scale_bytes"]
+    return (code + pos * d + dd,
+            code + lay["v_codes"] + _v_index(pos, dd, d),
+            sc + _int8_scale_offset(pos, 0) + two,
+            sc + _int8_scale_offset(pos, 1) + two)
 
 
 def new_pool(kv_format: int, num_blocks: int, block_size: int, num_kv_heads: int,
@@ -101,9 +124,7 @@ def write_int8_tokens(pool: np.ndarray, k_codes, k_scales, v_codes, v_scales,
     name the same slot, the later one wins (plain sequential semantics).
     """
     t_n, hkv, d = k_codes.shape
-    off = int8_head_offsets(block_size, d)
-    hb = off["head_bytes"]
-    if pool.shape[1] != hkv * hb:
+    if pool.shape[1] != page_bytes(KV_INT8_SYM, block_size, hkv, d):
         raise ValueError("pool page size does not match the shape")
     keep, blk, pos = _slot_split(slot_mapping, pool.shape[0], block_size)
     flat = pool.reshape(-1)
@@ -111,19 +132,14 @@ def write_int8_tokens(pool: np.ndarray, k_codes, k_scales, v_codes, v_scales,
     vc = np.ascontiguousarray(v_codes).view(np.uint8)
     ks = np.ascontiguousarray(k_scales.astype(np.float16)).view(np.uint8).reshape(t_n, hkv, 2)
     vs = np.ascontiguousarray(v_scales.astype(np.float16)).view(np.uint8).reshape(t_n, hkv, 2)
-    dd = np.arange(d)
     tt = np.nonzero(keep)[0]
-    page0 = blk[tt] * pool.shape[1]                     # [n]
-    p = pos[tt]                                         # [n]
+    page0 = (blk[tt] * pool.shape[1])[:, None]          # [n, 1]
     for h in range(hkv):
-        base = page0 + h * hb                            # [n]
-        k_idx = base[:, None] + off["k_codes"] + p[:, None] * d + dd[None, :]
-        v_idx = base[:, None] + off["v_codes"] + _v_index(p[:, None], dd[None, :], d)
-        flat[k_idx] = kc[tt, h]
-        flat[v_idx] = vc[tt, h]
-        two = np.arange(2)
-        flat[base[:, None] + off["k_scales"] + 2 * p[:, None] + two] = ks[tt, h]
-        flat[base[:, None] + off["v_scales"] + 2 * p[:, None] + two] = vs[tt, h]
+        ki, vi, ksi, vsi = int8_token_bytes(block_size, hkv, d, h, pos[tt])
+        flat[page0 + ki] = kc[tt, h]
+        flat[page0 + vi] = vc[tt, h]
+        flat[page0 + ksi] = ks[tt, h]
+        flat[page0 + vsi] = vs[tt, h]
 
 
 def write_16bit_tokens(pool: np.ndarray, k_bits, v_bits, slot_mapping,
@@ -161,20 +177,17 @@ def gather_int8_sequence(pool: np.ndarray, block_table_row, context_len: int,
     order following the block table; H = len(heads) (default: all KV heads).
     """
     d = head_dim
-    off = int8_head_offsets(block_size, d)
-    hb = off["head_bytes"]
     heads = list(range(num_kv_heads)) if heads is None else list(heads)
     blk, pos = _seq_positions(block_table_row, context_len, block_size)
     flat = pool.reshape(-1)
-    dd = np.arange(d)
+    page0 = (blk * pool.shape[1])[:, None]                          # [L, 1]
     kc, vc, ks, vs = [], [], [], []
     for h in heads:
-        base = blk * pool.shape[1] + h * hb                          # [L]
-        kc.append(flat[base[:, None] + off["k_codes"] + pos[:, None] * d + dd])
-        vc.append(flat[base[:, None] + off["v_codes"] + _v_index(pos[:, None], dd[None, :], d)])
-        two = np.arange(2)
-        ks.append(flat[base[:, None] + off["k_scales"] + 2 * pos[:, None] + two])
-        vs.append(flat[base[:, None] + off["v_scales"] + 2 * pos[:, None] + two])
+        ki, vi, ksi, vsi = int8_token_bytes(block_size, num_kv_heads, d, h, pos)
+        kc.append(flat[page0 + ki])
+        vc.append(flat[page0 + vi])
+        ks.append(flat[page0 + ksi])
+        vs.append(flat[page0 + vsi])
     kc = np.stack(kc, axis=1).view(np.int8)
     vc = np.stack(vc, axis=1).view(np.int8)
     ks = np.ascontiguousarray(np.stack(ks, axis=1)).view(np.float16)[..., 0]

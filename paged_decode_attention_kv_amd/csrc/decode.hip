@@ -253,10 +253,29 @@ struct Int8Page {
   u2_t ks, vs;     // scales of tokens 4*kb + (0..3)
 };
 
-// Page reads go through a buffer resource made for each page's head block
-// (base in SGPRs, 32-bit lane offsets, constant parts in the instruction's
-// offset field): no 64-bit per-lane address arithmetic, and a read outside
-// the head block would return 0 instead of touching other memory.
+// One KV head's part of a page: its code block (K then V; 16-bit values in
+// the 16-bit format) and, for per-token INT8, the byte distance from there to
+// the head's scale records (every head's code block comes first in an INT8
+// page, then every head's scales, so that the code blocks stay aligned).
+struct HeadRef {
+  const uint8_t* code;
+  int scales;
+};
+template <class K>
+__device__ __forceinline__ HeadRef head_ref(const DecodeArgs& a, int blk, int g) {
+  // (wave-uniform: the address stays in scalar registers, as the buffer
+  // resource requires; a missing page (blk < 0) points at page 0)
+  blk = __builtin_amdgcn_readfirstlane(blk);
+  g = __builtin_amdgcn_readfirstlane(g);
+  const int64_t page = blk >= 0 ? blk : 0;
+  return {a.pool + page * a.page_bytes + g * K::kCodeBytes,
+          (a.num_kv_heads - g) * K::kCodeBytes + g * K::kScaleBytes};
+}
+
+// Page reads go through a buffer resource made for each page's head (base
+// in SGPRs, 32-bit lane offsets, constant parts in the instruction's offset
+// field): no 64-bit per-lane address arithmetic, and a read outside the
+// resource would return 0 instead of touching other memory.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_block(const uint8_t* hp, int bytes) {
   // (the size is wave-uniform; saying so keeps the resource in scalar
   // registers, without a loop over distinct lane values)
@@ -272,23 +291,23 @@ __device__ __forceinline__ u4_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u4_t,
                             __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStreamLoad));
 }
-__device__ __forceinline__ u2_t ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kStreamLoad));
-}
 
+// (the resource runs from the head's code block to the end of its scale
+// records, all inside the page)
 template <int D>
-__device__ __forceinline__ void load_int8_page(Int8Page<D>& pg, const uint8_t* hp, bool live,
-                                               int i16, int kb) {
-  const __amdgpu_buffer_rsrc_t r = head_block(hp, live ? 32 * D + 64 : 0);
-  const uint32_t ko = i16 * D + 16 * kb;           // K: token i16
-  const uint32_t vo = kb * 4 * D + 16 * i16;       // V: token group kb (after 16*D)
-  const uint32_t so = 32 * D + 8 * kb;             // scales of tokens 4*kb..4*kb+3
+__device__ __forceinline__ void load_int8_page(Int8Page<D>& pg, HeadRef h, bool live, int i16,
+                                               int kb) {
+  const __amdgpu_buffer_rsrc_t r = head_block(h.code, live ? h.scales + 64 : 0);
+  const uint32_t ko = i16 * D + 16 * kb;      // K: token i16
+  const uint32_t vo = kb * 4 * D + 16 * i16;  // V: token group kb (after 16*D)
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) pg.k[i] = ld16(r, ko + 64 * i);
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) pg.v[i] = ld16(r, vo + 16 * D + 256 * i);
-  pg.ks = ld8(r, so);
-  pg.vs = ld8(r, so + 32);
+  // the record of tokens 4*kb .. 4*kb+3: four K scales, then four V scales
+  const u4_t sc = ld16(r, h.scales + 16 * kb);
+  pg.ks = u2_t{sc.x, sc.y};
+  pg.vs = u2_t{sc.z, sc.w};
 }
 
 // The matrix-instruction operands of a page's codes, converted where they
@@ -446,9 +465,9 @@ struct StaticPage {
 };
 
 template <int D>
-__device__ __forceinline__ void load_static_page(StaticPage<D>& pg, const uint8_t* hp, bool live,
-                                                 int i16, int kb) {
-  const __amdgpu_buffer_rsrc_t r = head_block(hp, live ? 32 * D : 0);
+__device__ __forceinline__ void load_static_page(StaticPage<D>& pg, HeadRef h, bool live, int i16,
+                                                 int kb) {
+  const __amdgpu_buffer_rsrc_t r = head_block(h.code, live ? 32 * D : 0);
   const uint32_t ko = i16 * D + 16 * kb;
   const uint32_t vo = kb * 4 * D + 16 * i16;
 #pragma unroll
@@ -509,7 +528,8 @@ template <int D_, bool QBF16, int G_ = 1, bool Static = false>
 struct Int8Kind {
   static constexpr int D = D_;
   static constexpr int kGroup = G_;  // pages per register buffer
-  static constexpr int kHeadBytes = Static ? 32 * D : 32 * D + 64;
+  static constexpr int kCodeBytes = 32 * D;            // a head's K and V codes
+  static constexpr int kScaleBytes = Static ? 0 : 64;  // a head's scale records
   using Page = typename std::conditional<Static, StaticPage<D>, Int8Page<D>>::type;
   h8_t qf[D / 32];
   float qscale;
@@ -525,12 +545,11 @@ struct Int8Kind {
         },
         qf);
   }
-  static __device__ __forceinline__ void load(Page& pg, const uint8_t* hp, bool live, int i16,
-                                              int kb) {
+  static __device__ __forceinline__ void load(Page& pg, HeadRef h, bool live, int i16, int kb) {
     if constexpr (Static)
-      load_static_page<D>(pg, hp, live, i16, kb);
+      load_static_page<D>(pg, h, live, i16, kb);
     else
-      load_int8_page<D>(pg, hp, live, i16, kb);
+      load_int8_page<D>(pg, h, live, i16, kb);
   }
   // one page against this query tile
   __device__ __forceinline__ void step(const Page& pg, int page_tok, int L, int Lmin, int Lc,
@@ -662,19 +681,18 @@ struct Int8Kind {
   }
 
   // Fused append, second half (after the page loop): store the token from nt
-  // at position pos of head block hb.
+  // at position pos of head h.
   static __device__ __forceinline__ void store_new(const DecodeArgs& a, const uint8_t* nt,
-                                                   int pos, int hb, int lane) {
-    uint8_t* head = a.pool + static_cast<int64_t>(hb) * kHeadBytes;
+                                                   int pos, HeadRef h, int lane) {
+    uint8_t* head = const_cast<uint8_t*>(h.code);
     for (int d = lane; d < D; d += 64) {
       head[pos * D + d] = nt[d];
       head[16 * D + (pos >> 2) * 4 * D + 4 * d + (pos & 3)] = nt[D + d];
     }
     if (!Static && lane == 0) {
-      *reinterpret_cast<uint16_t*>(head + 32 * D + 2 * pos) =
-          *reinterpret_cast<const uint16_t*>(nt + 2 * D);
-      *reinterpret_cast<uint16_t*>(head + 32 * D + 32 + 2 * pos) =
-          *reinterpret_cast<const uint16_t*>(nt + 2 * D + 2);
+      uint8_t* rec = head + h.scales + 16 * (pos >> 2) + 2 * (pos & 3);
+      *reinterpret_cast<uint16_t*>(rec) = *reinterpret_cast<const uint16_t*>(nt + 2 * D);
+      *reinterpret_cast<uint16_t*>(rec + 8) = *reinterpret_cast<const uint16_t*>(nt + 2 * D + 2);
     }
   }
 
@@ -738,9 +756,9 @@ struct Page16 {
 };
 
 template <int D>
-__device__ __forceinline__ void load_page16(Page16<D>& pg, const uint8_t* hp, bool live, int i16,
+__device__ __forceinline__ void load_page16(Page16<D>& pg, HeadRef h, bool live, int i16,
                                             int kb) {
-  const __amdgpu_buffer_rsrc_t r = head_block(hp, live ? 64 * D : 0);
+  const __amdgpu_buffer_rsrc_t r = head_block(h.code, live ? 64 * D : 0);
   const uint32_t ko = i16 * 2 * D + 16 * kb;
   const uint32_t vo = 32 * D + kb * 8 * D + 16 * i16;
 #pragma unroll
@@ -848,7 +866,8 @@ template <int D_, bool BF16, int G_ = 1>
 struct F16Kind {
   static constexpr int D = D_;
   static constexpr int kGroup = G_;  // pages per register buffer
-  static constexpr int kHeadBytes = 64 * D;
+  static constexpr int kCodeBytes = 64 * D;  // a head's K and V values
+  static constexpr int kScaleBytes = 0;
   using Page = Page16<D>;
   u4_t qf[D / 32];  // fragment j: dims 32*j + 8*kb + (0..7)
   float scale_log2;
@@ -863,9 +882,8 @@ struct F16Kind {
       if (!hvalid) qf[j] = u4_t{0u, 0u, 0u, 0u};
     scale_log2 = a.scale_log2;
   }
-  static __device__ __forceinline__ void load(Page& pg, const uint8_t* hp, bool live, int i16,
-                                              int kb) {
-    load_page16<D>(pg, hp, live, i16, kb);
+  static __device__ __forceinline__ void load(Page& pg, HeadRef h, bool live, int i16, int kb) {
+    load_page16<D>(pg, h, live, i16, kb);
   }
   __device__ __forceinline__ void step(const Page& pg, int page_tok, int L, int Lmin, int Lc,
                                        SoftmaxState<D / 16>& st) const {
@@ -906,10 +924,10 @@ struct F16Kind {
   }
 
   // Fused append, second half (after the page loop): store the token from nt
-  // at position pos of head block hb.
+  // at position pos of head h.
   static __device__ __forceinline__ void store_new(const DecodeArgs& a, const uint8_t* nt,
-                                                   int pos, int hb, int lane) {
-    uint16_t* head = reinterpret_cast<uint16_t*>(a.pool + static_cast<int64_t>(hb) * kHeadBytes);
+                                                   int pos, HeadRef h, int lane) {
+    uint16_t* head = reinterpret_cast<uint16_t*>(const_cast<uint8_t*>(h.code));
     const uint16_t* nt16 = reinterpret_cast<const uint16_t*>(nt);
     for (int d = lane; d < D; d += 64) {
       head[pos * D + d] = nt16[d];
@@ -1113,9 +1131,9 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     if (x + items >= x1 || ns == a.seg_cap || items == kMaxPagesPerWave) break;
   }
 
-  // head blocks of the items: lane i holds items i and 64 + i as
-  // block * hkv + KV head (the head block's index in the pool); out-of-range
-  // block ids are flagged and become -1 (the page is masked)
+  // pages of the items: lane i holds the block ids and KV heads of items i
+  // and 64 + i; out-of-range block ids are flagged and become -1 (the page
+  // is masked)
   int blk0 = 0, blk1 = 0, g0 = 0, g1 = 0;
   for (int s = 0; s < ns; ++s) {
     const int st = readlane(s_start, s), n = readlane(s_n, s);
@@ -1144,16 +1162,10 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
     blk1 = -1;
   }
-  const int hb0 = blk0 >= 0 ? blk0 * hkv + g0 : -1;
-  const int hb1 = blk1 >= 0 ? blk1 * hkv + g1 : -1;
-  auto block_of = [&](int i) { return i < 64 ? readlane(hb0, i) : readlane(hb1, i - 64); };
-  // a missing page (no memory access: an empty resource at head block 0)
-  // is fully masked (hb is the same in every lane; saying so keeps the
-  // address in scalar registers, as the buffer resource requires)
-  auto page_at = [&](int hb) {
-    hb = __builtin_amdgcn_readfirstlane(hb);
-    return a.pool + static_cast<int64_t>(hb >= 0 ? hb : 0) * K::kHeadBytes;
-  };
+  auto block_of = [&](int i) { return i < 64 ? readlane(blk0, i) : readlane(blk1, i - 64); };
+  auto head_of = [&](int i) { return i < 64 ? readlane(g0, i) : readlane(g1, i - 64); };
+  // (a missing page is fully masked and loaded through an empty resource:
+  // no memory access)
 
   // current segment: first page's token, first item, end item, length,
   // whether its last page gets the appended token, its column count and (for
@@ -1191,7 +1203,7 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     for (int j = 0; j < G; ++j) {
       const int q = first + j;
       blk[j] = q < items ? block_of(q) : -1;
-      K::load(grp[j], page_at(blk[j]), blk[j] >= 0, i16, kb);
+      K::load(grp[j], head_ref<K>(a, blk[j], q < items ? head_of(q) : 0), blk[j] >= 0, i16, kb);
     }
   };
   // consume items first.. of a group; false once the pass's items are done
@@ -1256,10 +1268,11 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
 
   if (!Multi && a.append) {
     for (int s = 0; s < ns; ++s) {
-      const int hb = block_of(readlane(s_start, s) + readlane(s_n, s) - 1);
-      if (!readlane(s_patch, s) || hb < 0) continue;
-      K::store_new(a, lds.nt + s * new_token_bytes(D), (readlane(s_L, s) - 1) % kBlockSize, hb,
-                   lane);
+      const int it = readlane(s_start, s) + readlane(s_n, s) - 1;  // its last page
+      const int blk = block_of(it);
+      if (!readlane(s_patch, s) || blk < 0) continue;
+      K::store_new(a, lds.nt + s * new_token_bytes(D), (readlane(s_L, s) - 1) % kBlockSize,
+                   head_ref<K>(a, blk, head_of(it)), lane);
     }
   }
   if constexpr (Multi) {
@@ -1327,7 +1340,7 @@ __device__ __forceinline__ int run_pass_wide(const DecodeArgs& a, K* kind, Curso
                                              uint16_t* q_lds, int lane) {
   constexpr int D = K::D, ND = D / 16;
   const int i16 = lane & 15, kb = lane >> 4;
-  const int hkv = a.num_kv_heads, vh = a.vheads;
+  const int vh = a.vheads;
   const int items = min(min(cu.np - cu.p, x1 - x), kMaxPagesPerWave);
   const int u = cu.b * vh + cu.g;
   if (cu.p == 0 && lane == 0) a.desc[u] = make_int2(wave, (x + cu.np - 1) / P - wave + 1);
@@ -1348,13 +1361,7 @@ __device__ __forceinline__ int run_pass_wide(const DecodeArgs& a, K* kind, Curso
     raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
     blk1 = -1;
   }
-  const int hb0 = blk0 >= 0 ? blk0 * hkv + uc.g : -1;
-  const int hb1 = blk1 >= 0 ? blk1 * hkv + uc.g : -1;
-  auto block_of = [&](int i) { return i < 64 ? readlane(hb0, i) : readlane(hb1, i - 64); };
-  auto page_at = [&](int hb) {
-    hb = __builtin_amdgcn_readfirstlane(hb);
-    return a.pool + static_cast<int64_t>(hb >= 0 ? hb : 0) * K::kHeadBytes;
-  };
+  auto block_of = [&](int i) { return i < 64 ? readlane(blk0, i) : readlane(blk1, i - 64); };
   cu.p += items;
   if (cu.p == cu.np && x + items < x1 && !next_unit(a, cu, nchunk, vh, lane)) return 0;
 
@@ -1379,7 +1386,7 @@ __device__ __forceinline__ int run_pass_wide(const DecodeArgs& a, K* kind, Curso
     for (int j = 0; j < G; ++j) {
       const int q = first + j;
       blk[j] = q < items ? block_of(q) : -1;
-      K::load(grp[j], page_at(blk[j]), blk[j] >= 0, i16, kb);
+      K::load(grp[j], head_ref<K>(a, blk[j], uc.g), blk[j] >= 0, i16, kb);
     }
   };
   auto consume = [&](typename K::Page* grp, const int* blk, int first) {

@@ -61,21 +61,25 @@ constexpr int kTrimRound = 128;
 // workgroups a trim launch aims for (about sixteen per compute unit)
 constexpr int64_t kTrimWorkgroups = 4096;
 
-// Token layout of a head block: element size E (1: INT8 codes, 2: 16-bit
-// values), K row of D elements at pos * D, V grouped four tokens at a time
-// (element d of token pos at 16 * D + (pos / 4) * 4 * D + 4 * d + pos % 4,
-// so one "V word" of 4 * E bytes holds dimension d of a whole group), and
-// for per-token INT8 the fp16 K and V scales after the codes.
+// Token layout of a KV head's part of a page. Code block (every head's code
+// block comes first in a page, head g's at g * kCodeBytes): element size E
+// (1: INT8 codes, 2: 16-bit values), K row of D elements at pos * D, V
+// grouped four tokens at a time (element d of token pos at 16 * D +
+// (pos / 4) * 4 * D + 4 * d + pos % 4, so one "V word" of 4 * E bytes holds
+// dimension d of a whole group). Per-token INT8 pages then hold every head's
+// fp16 scales (head g's 64 bytes at Hkv * kCodeBytes + 64 * g), a 16-byte
+// record per four tokens: their K scales, then their V scales.
 template <int D, int E, bool Scales>
 struct TokenLayout {
-  static constexpr int kHeadBytes = 32 * D * E + (Scales ? 64 : 0);
+  static constexpr int kCodeBytes = 32 * D * E;
   static constexpr int kRowBytes = D * E;
   static __device__ __forceinline__ int k_off(int pos) { return pos * D * E; }
   static __device__ __forceinline__ int vword_off(int group, int d) {  // group of the page
     return (16 * D + group * 4 * D + 4 * d) * E;
   }
-  static __device__ __forceinline__ int ks_off(int pos) { return 32 * D + 2 * pos; }
-  static __device__ __forceinline__ int vs_off(int pos) { return 32 * D + 32 + 2 * pos; }
+  // from the head's scale records
+  static __device__ __forceinline__ int ks_off(int pos) { return 16 * (pos / 4) + 2 * (pos % 4); }
+  static __device__ __forceinline__ int vs_off(int pos) { return ks_off(pos) + 8; }
 };
 
 template <int E>
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(kTrimThreads) void trim_keep_sink_kernel(TrimArgs a
   __shared__ u4_t s_k[C][KV];
   __shared__ W s_vw[VG][D];     // the round's source V words
   __shared__ uint32_t s_sc[C];  // K scale | V scale << 16
-  // head-block index of each token's source page (-1: missing) and of its
+  // block id of each token's source page (-1: missing) and of its
   // destination page (-1: missing, or the token is not moved)
   __shared__ int s_src[C], s_dst[C];
   __shared__ int s_whole[VG];  // destination group: all four tokens move in this round
@@ -157,7 +161,14 @@ __global__ __launch_bounds__(kTrimThreads) void trim_keep_sink_kernel(TrimArgs a
     return;
   }
   const int32_t* row = a.bt + static_cast<int64_t>(b) * a.bt_stride;
-  auto head = [&](int hb) { return a.pool + static_cast<int64_t>(hb) * Lay::kHeadBytes; };
+  // KV head g's code block and scale records in page blk
+  auto head = [&](int blk) {
+    return a.pool + static_cast<int64_t>(blk) * a.page_bytes + g * Lay::kCodeBytes;
+  };
+  auto scales = [&](int blk) {
+    return a.pool + static_cast<int64_t>(blk) * a.page_bytes +
+           a.num_kv_heads * Lay::kCodeBytes + 64 * g;
+  };
   const int shift = n & 3;  // tokens between a destination group's start and its source group's
   const bool wide = n >= C;
   const int nwin = wide ? (min(n, count) + C - 1) / C : 1;
@@ -176,8 +187,8 @@ __global__ __launch_bounds__(kTrimThreads) void trim_keep_sink_kernel(TrimArgs a
         if (!src_ok || !dst_ok) raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
         // the four tokens of a source group share its page, so they share
         // src_ok: a group's V word is read whenever one of them is moved
-        s_src[i] = src_ok ? bs * a.num_kv_heads + g : -1;
-        s_dst[i] = src_ok && dst_ok ? bd * a.num_kv_heads + g : -1;
+        s_src[i] = src_ok ? bs : -1;
+        s_dst[i] = src_ok && dst_ok ? bd : -1;
       }
       __syncthreads();
 
@@ -211,7 +222,7 @@ __global__ __launch_bounds__(kTrimThreads) void trim_keep_sink_kernel(TrimArgs a
         for (int r = 0; r < TPT; ++r) {
           const int i = min(tid + r * kTrimThreads, m - 1);
           const int pos = (s0 + i) % kBlockSize, hs = s_src[i];
-          const uint8_t* h = hs >= 0 ? head(hs) : a.pool;
+          const uint8_t* h = hs >= 0 ? scales(hs) : a.pool;
           sc[r] = *reinterpret_cast<const uint16_t*>(h + (hs >= 0 ? Lay::ks_off(pos) : 0)) |
                   (static_cast<uint32_t>(
                        *reinterpret_cast<const uint16_t*>(h + (hs >= 0 ? Lay::vs_off(pos) : 0)))
@@ -298,7 +309,7 @@ __global__ __launch_bounds__(kTrimThreads) void trim_keep_sink_kernel(TrimArgs a
         for (int i = tid; i < m; i += kTrimThreads) {
           if (s_dst[i] < 0) continue;
           const int pos = (q0 + i) % kBlockSize;
-          uint8_t* h = head(s_dst[i]);
+          uint8_t* h = scales(s_dst[i]);
           *reinterpret_cast<uint16_t*>(h + Lay::ks_off(pos)) = static_cast<uint16_t>(s_sc[i]);
           *reinterpret_cast<uint16_t*>(h + Lay::vs_off(pos)) =
               static_cast<uint16_t>(s_sc[i] >> 16);

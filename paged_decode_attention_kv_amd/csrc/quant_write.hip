@@ -26,16 +26,19 @@ namespace {
 constexpr int kWriteWaves = 4;
 constexpr int kQuad = 4;  // tokens per span: one V group of the page layout
 
-// Head block of a page: element size E (1: INT8 codes, 2: 16-bit values), K
-// rows at pos * D elements, V grouped four tokens at a time from 16 * D
-// elements on (dimension d of tokens 4g .. 4g+3 in one group word), and for
-// per-token INT8 the fp16 K and V scales after the codes.
+// A KV head's code block in a page: element size E (1: INT8 codes, 2: 16-bit
+// values), K rows at pos * D elements, V grouped four tokens at a time from
+// 16 * D elements on (dimension d of tokens 4g .. 4g+3 in one group word).
+// Every head's code block comes first in a page; per-token INT8 pages then
+// hold every head's fp16 scales, a 16-byte record per four tokens (K scales
+// of tokens 4g .. 4g+3, then their V scales).
 template <int D, int E, bool Scales>
 struct HeadLayout {
-  static constexpr int kBytes = 32 * D * E + (Scales ? 64 : 0);
+  static constexpr int kBytes = 32 * D * E;      // a head's code block
   static constexpr int kV = kBlockSize * D * E;  // byte offset of the V groups
-  static constexpr int kKs = 32 * D;             // K scales
-  static constexpr int kVs = 32 * D + 32;        // V scales
+  static constexpr int kScaleBytes = 64;         // a head's scale records
+  // K scale of token pos, from the head's scale records (V: 8 bytes on)
+  static __device__ __forceinline__ int ks_off(int pos) { return 16 * (pos / 4) + 2 * (pos % 4); }
 };
 
 // Tokens are dealt out four at a time, with each boundary between the fours
@@ -119,6 +122,12 @@ template <int D, int E, bool Scales>
 __device__ __forceinline__ uint8_t* head_of(const WriteArgs& a, int32_t slot, int h) {
   return a.pool + static_cast<int64_t>(slot / kBlockSize) * a.page_bytes +
          static_cast<int64_t>(h) * HeadLayout<D, E, Scales>::kBytes;
+}
+// a head's scale records, from its code block
+template <int D, int E, bool Scales>
+__device__ __forceinline__ int scales_from_code(const WriteArgs& a, int h) {
+  using L = HeadLayout<D, E, Scales>;
+  return (a.num_kv_heads - h) * L::kBytes + h * L::kScaleBytes;
 }
 
 // Max over each group of LPT lanes (16: DPP rotations inside a 16-lane row;
@@ -389,8 +398,9 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, co
     *reinterpret_cast<Packed*>(head + (pos * D + EPL * i) * E) = kc;
     if constexpr (Scales) {
       if (i == 0) {
-        *reinterpret_cast<uint16_t*>(head + L::kKs + 2 * pos) = skb;
-        *reinterpret_cast<uint16_t*>(head + L::kVs + 2 * pos) = svb;
+        uint8_t* rec = head + scales_from_code<D, E, Scales>(a, h) + L::ks_off(pos);
+        *reinterpret_cast<uint16_t*>(rec) = skb;
+        *reinterpret_cast<uint16_t*>(rec + 8) = svb;
       }
     }
   }

@@ -112,15 +112,19 @@ def test_non_finite_rows_are_flagged_and_left_unwritten(P, dtype):
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     P.kv_quant_int8_sym_write(k.cuda(), v.cuda(), dev_i32(slots), pool, 2, err_flag=err)
     assert int(err.item()) == P.EFLAG_SCALE_RANGE
+    # the oracle writes every row (the bad rows as zeros), then the bytes of
+    # the bad (token, head) pairs go back to the fill pattern
+    kk, vv = k.float().clone(), v.float().clone()
+    for t, h in bad:
+        kk[t, h] = 0.0
+        vv[t, h] = 0.0
     want = oracle.new_pool(oracle.KV_INT8_SYM, 2, 16, hkv, d, fill=FILL)
-    for h in range(hkv):
-        keep = np.array([(t, h) not in bad for t in range(T)])
-        kc, ks = oracle.quantize_rows(k[keep][:, h:h + 1])
-        vc, vs = oracle.quantize_rows(v[keep][:, h:h + 1])
-        one = oracle.new_pool(oracle.KV_INT8_SYM, 2, 16, 1, d, fill=FILL)
-        oracle.write_int8_tokens(one, kc, ks, vc, vs, slots[keep], 16)
-        hb = pb // hkv
-        want[:, h * hb:(h + 1) * hb] = one
+    kc, ks = oracle.quantize_rows(kk.numpy())
+    vc, vs = oracle.quantize_rows(vv.numpy())
+    oracle.write_int8_tokens(want, kc, ks, vc, vs, slots, 16)
+    for t, h in bad:
+        for idx in oracle.int8_token_bytes(16, hkv, d, h, [t % 16]):
+            want[t // 16].reshape(-1)[idx.reshape(-1)] = FILL
     assert np.array_equal(pool.cpu().numpy(), want)
 
 

@@ -106,21 +106,23 @@ def test_trim_clamps_and_identities():
 
 def test_trim_byte_positions_by_hand():
     """Per-token INT8, (16, 1 head, D 64): keep 2, n 16 moves old position 21
-    (page 1, slot 5) to position 5 (page 0, slot 5). Head block = 2*16*64 + 64
-    = 2112 bytes: K row at 64*slot, V byte of dim d at 1024 + (slot//4)*256 +
-    4*d + slot%4, K scale at 2048 + 2*slot, V scale at 2080 + 2*slot."""
+    (page 1, slot 5) to position 5 (page 0, slot 5). Page = code block
+    (2*16*64 = 2048 bytes: K row at 64*slot, V byte of dim d at 1024 +
+    (slot//4)*256 + 4*d + slot%4) then 64 bytes of scales (16-byte records per
+    four tokens: slot 5's K scale at 2048 + 16 + 2, its V scale at
+    2048 + 16 + 8 + 2)."""
     pool = oracle.new_pool(KV_INT8_SYM, 2, 16, 1, 64)
     pool[1, 5 * 64:6 * 64] = np.arange(64, dtype=np.uint8) + 1            # K row of old 21
     pool[1, 1024 + 1 * 256 + 4 * 9 + 1] = 200                           # V dim 9 of old 21
-    pool[1, 2048 + 10:2048 + 12] = [0x11, 0x22]                         # K scale of old 21
-    pool[1, 2080 + 10:2080 + 12] = [0x33, 0x44]                         # V scale of old 21
+    pool[1, 2066:2068] = [0x11, 0x22]                                   # K scale of old 21
+    pool[1, 2074:2076] = [0x33, 0x44]                                   # V scale of old 21
     bt = np.array([[0, 1]], np.int32)
     new = oracle.trim_keep_sink(KV_INT8_SYM, pool, bt, [22], [16], 2, 16, 1, 64)
     assert new.tolist() == [6]
     assert np.array_equal(pool[0, 5 * 64:6 * 64], np.arange(64, dtype=np.uint8) + 1)
     assert pool[0, 1024 + 1 * 256 + 4 * 9 + 1] == 200
-    assert pool[0, 2048 + 10:2048 + 12].tolist() == [0x11, 0x22]
-    assert pool[0, 2080 + 10:2080 + 12].tolist() == [0x33, 0x44]
+    assert pool[0, 2066:2068].tolist() == [0x11, 0x22]
+    assert pool[0, 2074:2076].tolist() == [0x33, 0x44]
 
 
 @pytest.mark.parametrize("kind", KINDS)

@@ -81,15 +81,18 @@ def _v_index_token_major(pos, d, head_dim):
     return pos * head_dim + d
 
 
-def _offsets_scales_swapped(block_size, head_dim):
-    bs, d = block_size, head_dim
-    return {"k_codes": 0, "v_codes": bs * d, "k_scales": 2 * bs * d + 2 * bs,
-            "v_scales": 2 * bs * d, "head_bytes": 2 * bs * d + 4 * bs}
+def _scale_offset_swapped(pos, is_v):
+    return (pos // 4) * 16 + 8 * (1 - is_v) + 2 * (pos % 4)
+
+
+def _scale_offset_token_major(pos, is_v):
+    return 2 * pos + 2 * 16 * is_v
 
 
 PAGE_MUTANTS = {
     "V stored token-major": ("_v_index", _v_index_token_major),
-    "K and V scale slots swapped": ("int8_head_offsets", _offsets_scales_swapped),
+    "K and V scale slots swapped": ("_int8_scale_offset", _scale_offset_swapped),
+    "scales not grouped by four tokens": ("_int8_scale_offset", _scale_offset_token_major),
 }
 
 PAGE_PINS = [

@@ -1,8 +1,9 @@
 """Pins for the oracle's page layout (CPU only).
 
 The byte totals are the ones printed on MoE-Infinity PR #183 ("Precision &
-memory"); the offsets inside a page are the documented layout contract,
-checked here at hand-computed byte positions.
+memory"); the offsets inside a page are the documented layout contract
+(INT8: every KV head's codes, then every KV head's scales), checked here at
+hand-computed byte positions.
 """
 
 import numpy as np
@@ -44,14 +45,17 @@ def test_int8_byte_offsets_by_hand():
     vs[0, 3] = np.float16(0.25)      # 0x3400
     oracle.write_int8_tokens(pool, kc, ks, vc, vs, [2 * 16 + 5], 16)
     flat = pool.reshape(-1)
-    head = 2 * 33280 + 3 * 4160
-    assert flat[head + 5 * 128 + 5] == 11                               # K[pos 5][d 5]
-    assert flat[head + 2048 + (5 // 4) * 512 + 7 * 4 + 5 % 4] == (256 - 13)  # V[pos 5][d 7]
-    assert flat[head + 4096 + 10] == 0x00 and flat[head + 4096 + 11] == 0x38
-    assert flat[head + 4128 + 10] == 0x00 and flat[head + 4128 + 11] == 0x34
+    page = 2 * 33280
+    code = page + 3 * 4096                  # head 3's code block (8 blocks of 4096 bytes)
+    assert flat[code + 5 * 128 + 5] == 11                               # K[pos 5][d 5]
+    assert flat[code + 2048 + (5 // 4) * 512 + 7 * 4 + 5 % 4] == (256 - 13)  # V[pos 5][d 7]
+    # scales after the 8 code blocks: head 3's 64 bytes at 32768 + 192; token 5
+    # is token 1 of group 1: K scale at 16 + 2, V scale at 16 + 8 + 2
+    sc = page + 32768 + 3 * 64
+    assert flat[sc + 18] == 0x00 and flat[sc + 19] == 0x38
+    assert flat[sc + 26] == 0x00 and flat[sc + 27] == 0x34
     # the other heads' scales of that token are 1.0 = 0x3C00
-    h0 = 2 * 33280
-    assert flat[h0 + 4096 + 11] == 0x3C
+    assert flat[page + 32768 + 0 * 64 + 19] == 0x3C and flat[page + 32768 + 7 * 64 + 27] == 0x3C
     # nothing else in the page is non-zero except the scales of this token
     nz = np.nonzero(pool[2])[0]
     assert len(nz) == 2 + 8 * 2  # two codes + (one high scale byte) * 8 heads * 2
