@@ -131,8 +131,9 @@ __device__ __forceinline__ int scales_from_code(const WriteArgs& a, int h) {
 }
 
 // Max over each group of LPT lanes (16: DPP rotations inside a 16-lane row;
-// 8: swaps inside quads, then the mirror inside each half row) of unsigned
-// values; VALU only, and every lane of the group gets it.
+// 8: swaps inside quads, then the mirror inside each half row; 4: swaps
+// inside quads) of unsigned values; VALU only, and every lane of the group
+// gets it.
 template <int Ctrl>
 __device__ __forceinline__ uint32_t dpp(uint32_t x) {
   return static_cast<uint32_t>(
@@ -146,9 +147,10 @@ __device__ __forceinline__ uint32_t group_max(uint32_t x) {
     x = max(x, dpp<0x122>(x));  // row_ror:2
     return max(x, dpp<0x121>(x));  // row_ror:1
   } else {
-    static_assert(LPT == 8, "8 or 16 lanes per token");
+    static_assert(LPT == 8 || LPT == 4, "4, 8 or 16 lanes per token");
     x = max(x, dpp<0xB1>(x));   // quad_perm [1, 0, 3, 2]
     x = max(x, dpp<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+    if constexpr (LPT == 4) return x;
     return max(x, dpp<0x141>(x));  // row_half_mirror
   }
 }
@@ -267,95 +269,130 @@ enum WriteFormat { kInt8Sym = 0, kInt8Static = 1, kBits16 = 2 };
 constexpr int spans_per_wave(int D, int F) { return F == kBits16 ? 1 : D == 128 ? 3 : 2; }
 constexpr int64_t kManySpanWaves = 2048;
 
-// A lane's 8 raw 16-bit K and V elements.
+// Elements of a row each lane holds: 16 for the INT8 formats when the KV
+// heads fill whole waves at that width (twice the row work per lane, so the
+// per-row scale, address and store instructions are shared by twice the
+// bytes: the INT8 writers are instruction-bound), else 8.
+constexpr int kWideEpl = 16;
+constexpr int heads_per_wave(int D, int epl) { return 16 * epl / D; }
+
+// A lane's EPL raw 16-bit K and V elements, as EPL / 8 vectors of eight.
+template <int EPL>
 struct Rows {
-  u4_t k, v;
+  u4_t k[EPL / 8], v[EPL / 8];
 };
 
 // Loads of the rows of up to four consecutive tokens t0 .. t0 + nt - 1
-// (nt >= 1): lane (head hh, token r, i) gets elements 8i .. 8i+7 of token
-// r's rows of KV head h0 + hh; past the call's end the last token, and past
-// the last head the last head, are loaded again.
-template <int D, bool Vec>
-__device__ __forceinline__ Rows load_rows(const WriteArgs& a, const Quad& q, int64_t t0, int h0,
-                                          int lane) {
-  constexpr int EPL = 8, LPT = D / EPL, LPH = kQuad * LPT;
+// (nt >= 1): lane (head hh, token r, i) gets elements EPL*i .. EPL*i + EPL-1
+// of token r's rows of KV head h0 + hh; past the call's end the last token,
+// and past the last head the last head, are loaded again.
+template <int D, int EPL, bool Vec>
+__device__ __forceinline__ Rows<EPL> load_rows(const WriteArgs& a, const Quad& q, int64_t t0,
+                                               int h0, int lane) {
+  constexpr int NV = EPL / 8, LPT = D / EPL, LPH = kQuad * LPT;
   const int hh = lane / LPH, r = lane % LPH / LPT, i = lane % LPT;
   const int h = h0 + hh;
   const int hl = h < a.num_kv_heads ? h : a.num_kv_heads - 1;
   const int64_t t = t0 + (r < q.nt ? r : q.nt - 1);
-  Rows in;
+  const uint16_t* kr = static_cast<const uint16_t*>(a.k) + t * a.k_st + hl * a.k_sh;
+  const uint16_t* vr = static_cast<const uint16_t*>(a.v) + t * a.v_st + hl * a.v_sh;
+  Rows<EPL> in;
   if constexpr (Vec) {
-    in.k = *reinterpret_cast<const u4_t*>(static_cast<const uint16_t*>(a.k) + t * a.k_st +
-                                          hl * a.k_sh + EPL * i);
-    in.v = *reinterpret_cast<const u4_t*>(static_cast<const uint16_t*>(a.v) + t * a.v_st +
-                                          hl * a.v_sh + EPL * i);
-  } else {
-    uint32_t kw[4] = {}, vw[4] = {};
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const int64_t d = EPL * i + e;
-      kw[e / 2] |= static_cast<uint32_t>(static_cast<const uint16_t*>(
-                       a.k)[t * a.k_st + hl * a.k_sh + d * a.k_sd])
-                   << (16 * (e % 2));
-      vw[e / 2] |= static_cast<uint32_t>(static_cast<const uint16_t*>(
-                       a.v)[t * a.v_st + hl * a.v_sh + d * a.v_sd])
-                   << (16 * (e % 2));
+    for (int c = 0; c < NV; ++c) {
+      in.k[c] = *reinterpret_cast<const u4_t*>(kr + EPL * i + 8 * c);
+      in.v[c] = *reinterpret_cast<const u4_t*>(vr + EPL * i + 8 * c);
     }
-    in.k = u4_t{kw[0], kw[1], kw[2], kw[3]};
-    in.v = u4_t{vw[0], vw[1], vw[2], vw[3]};
+  } else {
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      uint32_t kw[4] = {}, vw[4] = {};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int64_t d = EPL * i + 8 * c + e;
+        kw[e / 2] |= static_cast<uint32_t>(kr[d * a.k_sd]) << (16 * (e % 2));
+        vw[e / 2] |= static_cast<uint32_t>(vr[d * a.v_sd]) << (16 * (e % 2));
+      }
+      in.k[c] = u4_t{kw[0], kw[1], kw[2], kw[3]};
+      in.v[c] = u4_t{vw[0], vw[1], vw[2], vw[3]};
+    }
   }
   return in;
 }
 
+// Codes of eight FP16 or BF16 values with a static scale outside the
+// division-free window: one IEEE division per element.
+template <bool BF16>
+__device__ __forceinline__ uint64_t codes_static_div(const u4_t& w, float s) {
+  uint64_t c = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    c |= static_cast<uint64_t>(
+             row_code(bits16_to_f32<BF16>(static_cast<uint16_t>(w[e / 2] >> (16 * (e % 2)))), s))
+         << (8 * e);
+  return c;
+}
+
 // Write of the K and V rows (loaded by load_rows) of up to four consecutive
-// tokens of the call, for HPW = 128 / D KV heads at once: quantize-on-write
-// into INT8 pages (kInt8Sym: per-token scales; kInt8Static: the layer's
-// scales) or a plain copy into 16-bit pages (kBits16). Every lane holds 8
-// elements of one row: lane (head hh, token r, i) holds elements 8i .. 8i+7
-// of token r's rows of KV head h0 + hh (LPT = D / 8 lanes per token), so a
-// row's absolute maximum is an LPT-lane reduction and the per-row scale work
-// of all the wave's rows shares instructions. The per-row rules (MoE-Infinity
-// PR #183 "feat: opt-in INT8 KV-cache quantization", "What landed",
-// format-contract bullet; zero rows per mlxcel PR #717 "The Int8 bug and
-// fix"; static scales per InfiniLM PR #553 "Summary"):
+// tokens of the call, for HPW = 16 * EPL / D KV heads at once: quantize-on-
+// write into INT8 pages (kInt8Sym: per-token scales; kInt8Static: the
+// layer's scales) or a plain copy into 16-bit pages (kBits16). Every lane
+// holds EPL elements of one row: lane (head hh, token r, i) holds elements
+// EPL*i .. EPL*i + EPL-1 of token r's rows of KV head h0 + hh (LPT = D / EPL
+// lanes per token), so a row's absolute maximum is an LPT-lane reduction and
+// the per-row scale work of all the wave's rows shares instructions. The
+// per-row rules (MoE-Infinity PR #183 "feat: opt-in INT8 KV-cache
+// quantization", "What landed", format-contract bullet; zero rows per mlxcel
+// PR #717 "The Int8 bug and fix"; static scales per InfiniLM PR #553
+// "Summary"):
 //   per-token: a = max|x|; s = 1.0 if a == 0 else the smallest FP16 >=
 //   fl32(a/127); code = clamp(rint(fl32(x / s)), -127, 127);
 //   static: code = clamp(rint(fl32(x / scale)), -127, 127).
 // A token with a negative slot is padding (skipped); an out-of-range slot, a
 // per-token scale beyond FP16 or a NaN or infinity in a row (per-token
 // format) is flagged and that (token, head) is left unwritten. K rows are
-// stored per token (8 contiguous elements per lane). When the four tokens
+// stored per token (EPL contiguous elements per lane). When the four tokens
 // are one whole V group of a head, the elements go through LDS to become
-// group words (one dimension of the four tokens) and every lane stores two
-// whole words; otherwise each token's V elements are stored one by one.
-template <int D, int F, bool BF16>
-__device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, const Rows& in,
-                                           int h0, u4_t* s_elems, int lane) {
-  constexpr int EPL = 8;            // elements per lane
+// group words (one dimension of the four tokens) and every lane stores
+// EPL / 4 whole words; otherwise each token's V elements are stored one by
+// one.
+template <int D, int EPL, int F, bool BF16>
+__device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q,
+                                           const Rows<EPL>& in, int h0, u4_t* s_elems,
+                                           int lane) {
+  constexpr int NV = EPL / 8;       // vectors of eight elements per lane
   constexpr int LPT = D / EPL;      // lanes per token row
   constexpr int LPH = kQuad * LPT;  // lanes per head
   constexpr int E = F == kBits16 ? 2 : 1;  // bytes per stored element
   constexpr bool Scales = F == kInt8Sym;
+  static_assert(NV * 8 * E <= 16, "a lane's V elements fit its 16 LDS bytes");
   using L = HeadLayout<D, E, Scales>;
-  using Packed = typename std::conditional<E == 2, u4_t, uint64_t>::type;  // a lane's 8
+  using Packed = typename std::conditional<E == 2, u4_t, uint64_t>::type;  // eight elements
   const int hh = lane / LPH, r = lane % LPH / LPT, i = lane % LPT;
   const int h = h0 + hh;
   const bool hvalid = h < a.num_kv_heads;
   const int32_t my_slot = r == 0 ? q.slot[0] : r == 1 ? q.slot[1] : r == 2 ? q.slot[2] : q.slot[3];
-  const u4_t kl = in.k, vl = in.v;
 
   bool ok = my_slot >= 0 && hvalid;
-  Packed kc, vc;
+  Packed kc[NV], vc[NV];
   uint16_t skb = 0, svb = 0;
   if constexpr (F == kBits16) {
-    kc = kl;
-    vc = vl;
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      kc[c] = in.k[c];
+      vc[c] = in.v[c];
+    }
   } else if constexpr (F == kInt8Sym) {
     // row maxima as magnitude bits, reduced over the row's lanes (a NaN
     // stays the largest and is flagged with the scale)
-    const float ak = bits16_to_f32<BF16>(static_cast<uint16_t>(group_max<LPT>(max_magnitude(kl))));
-    const float av = bits16_to_f32<BF16>(static_cast<uint16_t>(group_max<LPT>(max_magnitude(vl))));
+    uint32_t mk = max_magnitude(in.k[0]), mv = max_magnitude(in.v[0]);
+#pragma unroll
+    for (int c = 1; c < NV; ++c) {
+      mk = max(mk, max_magnitude(in.k[c]));
+      mv = max(mv, max_magnitude(in.v[c]));
+    }
+    const float ak = bits16_to_f32<BF16>(static_cast<uint16_t>(group_max<LPT>(mk)));
+    const float av = bits16_to_f32<BF16>(static_cast<uint16_t>(group_max<LPT>(mv)));
     const bool okk = row_scale_token(ak, skb), okv = row_scale_token(av, svb);
     if (ok && !(okk && okv)) {
       if (i == 0) raise_flag(a.err, PDAKV_EFLAG_SCALE_RANGE);
@@ -364,25 +401,23 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, co
     const float sk = f16_bits_to_f32(skb), sv = f16_bits_to_f32(svb);
     const float rk = __builtin_amdgcn_rcpf(sk), rv = __builtin_amdgcn_rcpf(sv);
     constexpr float kInflate = 1.000030517578125f;  // 1 + 2^-15
-    kc = codes_token<BF16>(kl, sk, rk, rk * kInflate);
-    vc = codes_token<BF16>(vl, sv, rv, rv * kInflate);
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      kc[c] = codes_token<BF16>(in.k[c], sk, rk, rk * kInflate);
+      vc[c] = codes_token<BF16>(in.v[c], sv, rv, rv * kInflate);
+    }
   } else if (static_window(a.k_scale) && static_window(a.v_scale)) {
-    kc = codes_static<BF16>(kl, a.k_scale, 1.0f / a.k_scale);
-    vc = codes_static<BF16>(vl, a.v_scale, 1.0f / a.v_scale);
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      kc[c] = codes_static<BF16>(in.k[c], a.k_scale, 1.0f / a.k_scale);
+      vc[c] = codes_static<BF16>(in.v[c], a.v_scale, 1.0f / a.v_scale);
+    }
   } else {
     // scales outside [2^-64, 2^64]: one IEEE division per element
-    kc = 0;
-    vc = 0;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      kc |= static_cast<uint64_t>(
-                row_code(bits16_to_f32<BF16>(static_cast<uint16_t>(kl[e / 2] >> (16 * (e % 2)))),
-                         a.k_scale))
-            << (8 * e);
-      vc |= static_cast<uint64_t>(
-                row_code(bits16_to_f32<BF16>(static_cast<uint16_t>(vl[e / 2] >> (16 * (e % 2)))),
-                         a.v_scale))
-            << (8 * e);
+    for (int c = 0; c < NV; ++c) {
+      kc[c] = codes_static_div<BF16>(in.k[c], a.k_scale);
+      vc[c] = codes_static_div<BF16>(in.v[c], a.v_scale);
     }
   }
   // whole V group of this lane's head: all four tokens stored (uniform over
@@ -395,7 +430,15 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, co
   const int pos = my_slot % kBlockSize;
   uint8_t* head = head_of<D, E, Scales>(a, ok ? my_slot : 0, ok ? h : 0);
   if (ok) {
-    *reinterpret_cast<Packed*>(head + (pos * D + EPL * i) * E) = kc;
+    uint8_t* krow = head + (pos * D + EPL * i) * E;
+    if constexpr (E == 1 && NV == 2) {
+      *reinterpret_cast<u4_t*>(krow) =
+          u4_t{static_cast<uint32_t>(kc[0]), static_cast<uint32_t>(kc[0] >> 32),
+               static_cast<uint32_t>(kc[1]), static_cast<uint32_t>(kc[1] >> 32)};
+    } else {
+#pragma unroll
+      for (int c = 0; c < NV; ++c) *reinterpret_cast<Packed*>(krow + 8 * c * E) = kc[c];
+    }
     if constexpr (Scales) {
       if (i == 0) {
         uint8_t* rec = head + scales_from_code<D, E, Scales>(a, h) + L::ks_off(pos);
@@ -407,53 +450,77 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q, co
   // (every lane passes the LDS exchange, so that the wave stays together;
   // the barrier keeps this store after the reads of an earlier span)
   __builtin_amdgcn_wave_barrier();
-  *reinterpret_cast<Packed*>(&s_elems[lane]) = vc;
+  if constexpr (E == 1 && NV == 2) {
+    s_elems[lane] = u4_t{static_cast<uint32_t>(vc[0]), static_cast<uint32_t>(vc[0] >> 32),
+                         static_cast<uint32_t>(vc[1]), static_cast<uint32_t>(vc[1] >> 32)};
+  } else {
+    *reinterpret_cast<Packed*>(&s_elems[lane]) = vc[0];
+  }
   __builtin_amdgcn_wave_barrier();
   if (whole) {
-    // lane (hh, r, i) builds the group words of dimensions 8i + 2r and
-    // 8i + 2r + 1 of its head (one element of each token per word): it reads
-    // the word of each token's lane that holds those two elements and
+    // lane (hh, r, i) builds the group words of EPL / 4 dimensions of its
+    // head (one element of each token per word): it reads from each token's
+    // lane (hh, j, i) the word that holds those dimensions' elements and
     // gathers them with byte selects
     const uint32_t* ew = reinterpret_cast<const uint32_t*>(s_elems + LPH * hh + i);
     uint32_t d[kQuad];
+    if constexpr (E == 1 && NV == 2) {
+      // dims 16i + 4r .. 16i + 4r + 3: word r of each token's 16 codes; a
+      // 4 x 4 byte transpose turns the four words into four group words
 #pragma unroll
-    for (int j = 0; j < kQuad; ++j) d[j] = ew[4 * LPT * j + (E == 2 ? r : r >> 1)];
-    uint8_t* vg = head + L::kV + ((pos / 4) * 4 * D + 4 * (EPL * i + 2 * r)) * E;
-    if constexpr (E == 2) {
-      // word j holds elements 2r (low half) and 2r + 1 (high half) of token j
-      *reinterpret_cast<u4_t*>(vg) = u4_t{__builtin_amdgcn_perm(d[1], d[0], 0x05040100u),
-                                          __builtin_amdgcn_perm(d[3], d[2], 0x05040100u),
-                                          __builtin_amdgcn_perm(d[1], d[0], 0x07060302u),
-                                          __builtin_amdgcn_perm(d[3], d[2], 0x07060302u)};
+      for (int j = 0; j < kQuad; ++j) d[j] = ew[4 * LPT * j + r];
+      const uint32_t t01l = __builtin_amdgcn_perm(d[1], d[0], 0x05010400u);  // d0.0 d1.0 d0.1 d1.1
+      const uint32_t t01h = __builtin_amdgcn_perm(d[1], d[0], 0x07030602u);  // d0.2 d1.2 d0.3 d1.3
+      const uint32_t t23l = __builtin_amdgcn_perm(d[3], d[2], 0x05010400u);
+      const uint32_t t23h = __builtin_amdgcn_perm(d[3], d[2], 0x07030602u);
+      uint8_t* vg = head + L::kV + (pos / 4) * 4 * D + 4 * (EPL * i + 4 * r);
+      *reinterpret_cast<u4_t*>(vg) = u4_t{__builtin_amdgcn_perm(t23l, t01l, 0x05040100u),
+                                          __builtin_amdgcn_perm(t23l, t01l, 0x07060302u),
+                                          __builtin_amdgcn_perm(t23h, t01h, 0x05040100u),
+                                          __builtin_amdgcn_perm(t23h, t01h, 0x07060302u)};
     } else {
-      // elements 2r and 2r + 1 are bytes b and b + 1 of word j
-      const uint32_t b = 2 * (r & 1);
-      const uint32_t sel = b | (b + 4) << 8 | (b + 1) << 16 | (b + 5) << 24;
-      const uint32_t t01 = __builtin_amdgcn_perm(d[1], d[0], sel);  // d0.b d1.b d0.b+1 d1.b+1
-      const uint32_t t23 = __builtin_amdgcn_perm(d[3], d[2], sel);
-      *reinterpret_cast<uint64_t*>(vg) =
-          __builtin_amdgcn_perm(t23, t01, 0x05040100u) |
-          static_cast<uint64_t>(__builtin_amdgcn_perm(t23, t01, 0x07060302u)) << 32;
+      // dims 8i + 2r and 8i + 2r + 1
+#pragma unroll
+      for (int j = 0; j < kQuad; ++j) d[j] = ew[4 * LPT * j + (E == 2 ? r : r >> 1)];
+      uint8_t* vg = head + L::kV + ((pos / 4) * 4 * D + 4 * (EPL * i + 2 * r)) * E;
+      if constexpr (E == 2) {
+        // word j holds elements 2r (low half) and 2r + 1 (high half) of token j
+        *reinterpret_cast<u4_t*>(vg) = u4_t{__builtin_amdgcn_perm(d[1], d[0], 0x05040100u),
+                                            __builtin_amdgcn_perm(d[3], d[2], 0x05040100u),
+                                            __builtin_amdgcn_perm(d[1], d[0], 0x07060302u),
+                                            __builtin_amdgcn_perm(d[3], d[2], 0x07060302u)};
+      } else {
+        // elements 2r and 2r + 1 are bytes b and b + 1 of word j
+        const uint32_t b = 2 * (r & 1);
+        const uint32_t sel = b | (b + 4) << 8 | (b + 1) << 16 | (b + 5) << 24;
+        const uint32_t t01 = __builtin_amdgcn_perm(d[1], d[0], sel);  // d0.b d1.b d0.b+1 d1.b+1
+        const uint32_t t23 = __builtin_amdgcn_perm(d[3], d[2], sel);
+        *reinterpret_cast<uint64_t*>(vg) =
+            __builtin_amdgcn_perm(t23, t01, 0x05040100u) |
+            static_cast<uint64_t>(__builtin_amdgcn_perm(t23, t01, 0x07060302u)) << 32;
+      }
     }
   } else if (ok) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       uint8_t* dst = head + L::kV + ((pos / 4) * 4 * D + 4 * (EPL * i + e) + pos % 4) * E;
+      const int c = e / 8, ee = e % 8;
       if constexpr (E == 2)
-        *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(vc[e / 2] >> (16 * (e % 2)));
+        *reinterpret_cast<uint16_t*>(dst) =
+            static_cast<uint16_t>(vc[c][ee / 2] >> (16 * (ee % 2)));
       else
-        *dst = static_cast<uint8_t>(vc >> (8 * e));
+        *dst = static_cast<uint8_t>(vc[c] >> (8 * ee));
     }
   }
 }
 
 // One wave per kSpans spans of about four tokens (boundaries moved to V
-// groups) and 128 / D KV heads. The rows of all its spans are loaded before
-// the first is quantized and stored, so a wave keeps kSpans times the bytes
-// in flight; a span across two runs of slots takes a second round.
-template <int D, int F, bool BF16, bool Vec, int kSpans>
+// groups) and 16 * EPL / D KV heads. The rows of all its spans are loaded
+// before the first is quantized and stored, so a wave keeps kSpans times the
+// bytes in flight; a span across two runs of slots takes a second round.
+template <int D, int F, bool BF16, bool Vec, int kSpans, int EPL>
 __global__ __launch_bounds__(64 * kWriteWaves) void write_kernel(WriteArgs a) {
-  constexpr int HPW = 128 / D;  // KV heads per wave
+  constexpr int HPW = heads_per_wave(D, EPL);  // KV heads per wave
   __shared__ u4_t s_elems[kWriteWaves][64];  // a lane's V elements
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -467,31 +534,28 @@ __global__ __launch_bounds__(64 * kWriteWaves) void write_kernel(WriteArgs a) {
   const int h0 = static_cast<int>(w - g * hgroups) * HPW;
   Span sp[kSpans];
   load_spans<kSpans>(a, g * kSpans, lane, sp);
-  Rows in[kSpans];
+  Rows<EPL> in[kSpans];
 #pragma unroll
   for (int p = 0; p < kSpans; ++p)
-    if (sp[p].n > 0) in[p] = load_rows<D, Vec>(a, quad_of<0>(sp[p]), sp[p].t0, h0, lane);
+    if (sp[p].n > 0) in[p] = load_rows<D, EPL, Vec>(a, quad_of<0>(sp[p]), sp[p].t0, h0, lane);
 #pragma unroll
   for (int p = 0; p < kSpans; ++p)
-    if (sp[p].n > 0) write_quad<D, F, BF16>(a, quad_of<0>(sp[p]), in[p], h0, s_elems[wv], lane);
+    if (sp[p].n > 0)
+      write_quad<D, EPL, F, BF16>(a, quad_of<0>(sp[p]), in[p], h0, s_elems[wv], lane);
 #pragma unroll
   for (int p = 0; p < kSpans; ++p)
     if (sp[p].n > kQuad) {  // a span across two runs of slots
       const Quad q = quad_of<1>(sp[p]);
-      const Rows in1 = load_rows<D, Vec>(a, q, sp[p].t0 + kQuad, h0, lane);
-      write_quad<D, F, BF16>(a, q, in1, h0, s_elems[wv], lane);
+      const Rows<EPL> in1 = load_rows<D, EPL, Vec>(a, q, sp[p].t0 + kQuad, h0, lane);
+      write_quad<D, EPL, F, BF16>(a, q, in1, h0, s_elems[wv], lane);
     }
 }
 
-// Waves of a call at `spans` spans per wave.
-int64_t write_waves(const WriteArgs& a, int head_dim, int spans) {
-  const int hpw = 128 / head_dim;
+// Waves of a call at `spans` spans per wave and `epl` elements per lane.
+int64_t write_waves(const WriteArgs& a, int head_dim, int spans, int epl) {
+  const int hpw = heads_per_wave(head_dim, epl);
   const int64_t quads = (a.num_tokens + kQuad - 1) / kQuad;
   return (quads + spans - 1) / spans * ((a.num_kv_heads + hpw - 1) / hpw);
-}
-unsigned write_grid(const WriteArgs& a, int head_dim, int spans) {
-  const int64_t waves = write_waves(a, head_dim, spans);
-  return static_cast<unsigned>((waves + kWriteWaves - 1) / kWriteWaves);
 }
 
 // Whole-row vector loads: unit element stride, every row start aligned to
@@ -504,22 +568,34 @@ bool vec_rows(const WriteArgs& a, int bytes) {
          (reinterpret_cast<uintptr_t>(a.v) % bytes) == 0;
 }
 
-template <int D, int F, bool BF16, int S>
+template <int D, int F, bool BF16, int S, int EPL>
 hipError_t launch_spans(const WriteArgs& a, hipStream_t s) {
-  const dim3 grid(write_grid(a, D, S)), block(64 * kWriteWaves);
+  const int64_t waves = write_waves(a, D, S, EPL);
+  const dim3 grid(static_cast<unsigned>((waves + kWriteWaves - 1) / kWriteWaves)),
+      block(64 * kWriteWaves);
   // lanes load 16 bytes of a row
   if (vec_rows(a, 16))
-    hipLaunchKernelGGL((write_kernel<D, F, BF16, true, S>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((write_kernel<D, F, BF16, true, S, EPL>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((write_kernel<D, F, BF16, false, S>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((write_kernel<D, F, BF16, false, S, EPL>), grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+template <int D, int F, bool BF16, int EPL>
+hipError_t launch_epl(const WriteArgs& a, hipStream_t s) {
+  constexpr int S = spans_per_wave(D, F);
+  if (S > 1 && write_waves(a, D, 1, EPL) >= kManySpanWaves)
+    return launch_spans<D, F, BF16, S, EPL>(a, s);
+  return launch_spans<D, F, BF16, 1, EPL>(a, s);
 }
 
 template <int D, int F, bool BF16>
 hipError_t launch_dim(const WriteArgs& a, hipStream_t s) {
-  constexpr int S = spans_per_wave(D, F);
-  if (S > 1 && write_waves(a, D, 1) >= kManySpanWaves) return launch_spans<D, F, BF16, S>(a, s);
-  return launch_spans<D, F, BF16, 1>(a, s);
+  if constexpr (F != kBits16) {
+    if (a.num_kv_heads % heads_per_wave(D, kWideEpl) == 0)
+      return launch_epl<D, F, BF16, kWideEpl>(a, s);
+  }
+  return launch_epl<D, F, BF16, 8>(a, s);
 }
 
 template <int F, bool BF16>
