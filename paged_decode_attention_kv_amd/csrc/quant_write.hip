@@ -261,12 +261,17 @@ enum WriteFormat { kInt8Sym = 0, kInt8Static = 1, kBits16 = 2 };
 
 // Spans per wave of a large call (measured on 262K- and 296K-token
 // prefills): the INT8 writers gain 5-8% from three spans' loads in flight at
-// D = 128 (two at D = 64, where more registers cost occupancy); the 16-bit
-// writer, already near the copy rate, is 10% slower with more than one. A
-// call of fewer than kManySpanWaves one-span waves (a decode step's append)
-// keeps one span per wave: its time is one wave's latency, which more spans
-// per wave lengthen (64 tokens: 6 us with one span, 10 us with three).
-constexpr int spans_per_wave(int D, int F) { return F == kBits16 ? 1 : D == 128 ? 3 : 2; }
+// D = 128 with 8 elements per lane, two with 16 (three and four measured 2%
+// and 5% slower there) and two at D = 64, where more registers cost
+// occupancy; the 16-bit writer, already near the copy rate, is 10% slower
+// with more than one. A call of fewer than kManySpanWaves one-span waves (a
+// decode step's append) keeps one span per wave: its time is one wave's
+// latency, which more spans per wave lengthen (64 tokens: 6 us with one span,
+// 10 us with three). (A persistent form, each wave looping over items with
+// the next item's slots and rows in flight, measured 12-30% slower.)
+constexpr int spans_per_wave(int D, int F, int epl) {
+  return F == kBits16 ? 1 : D == 128 && epl == 8 ? 3 : 2;
+}
 constexpr int64_t kManySpanWaves = 2048;
 
 // Elements of a row each lane holds: 16 for the INT8 formats when the KV
@@ -583,7 +588,7 @@ hipError_t launch_spans(const WriteArgs& a, hipStream_t s) {
 
 template <int D, int F, bool BF16, int EPL>
 hipError_t launch_epl(const WriteArgs& a, hipStream_t s) {
-  constexpr int S = spans_per_wave(D, F);
+  constexpr int S = spans_per_wave(D, F, EPL);
   if (S > 1 && write_waves(a, D, 1, EPL) >= kManySpanWaves)
     return launch_spans<D, F, BF16, S, EPL>(a, s);
   return launch_spans<D, F, BF16, 1, EPL>(a, s);
