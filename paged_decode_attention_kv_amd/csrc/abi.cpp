@@ -89,12 +89,22 @@ int merge_waves(int num_seqs, int num_kv_heads, int max_context_len, int64_t wav
   return w;
 }
 
+// Waves per SIMD of the kernel a decode call launches, which its plan fills:
+// the one-token kernels' occupancy per format, or that of the several-token
+// kernel for units of unit_tiles tiles.
+int launch_waves_per_simd(int kv_format, bool multi, int unit_tiles) {
+  return multi ? pdakv::wide_waves_per_simd(kv_format, unit_tiles)
+               : format_waves_per_simd(kv_format);
+}
+
 // Query columns of a call: T query tokens x G query heads per KV head, in
 // tiles of at most 16 (one MFMA operand). A unit is one KV head's run of up
 // to unit_tiles tiles, whose pages are streamed once for all of them: all
 // the tiles of a KV head up to kMaxUnitTiles, else units of that many.
-// waves_per_simd: that of the INT8 kernel, whose plan has the most waves
-// (its workspace serves the 16-bit kernel too).
+// waves_per_simd: the most that any decode kernel these columns can run in
+// has (every format; for one query token the one-token and the several-token
+// kernels), so that a workspace sized with it holds the partial slots of
+// every plan.
 struct Columns {
   int cols, unit_tiles, units_per_head, slot_cols, waves_per_simd;
 };
@@ -105,7 +115,12 @@ Columns columns(int num_q_heads, int num_kv_heads, int num_query_tokens) {
   c.unit_tiles = std::min(tiles, pdakv::kMaxUnitTiles);
   c.units_per_head = (tiles + c.unit_tiles - 1) / c.unit_tiles;
   c.slot_cols = std::min(c.cols, 16 * c.unit_tiles);
-  c.waves_per_simd = pdakv::wide_waves_per_simd(PDAKV_KV_INT8_SYM, c.unit_tiles);
+  c.waves_per_simd = 0;
+  for (int f : {PDAKV_KV_INT8_SYM, PDAKV_KV_INT8_STATIC, PDAKV_KV_16BIT}) {
+    c.waves_per_simd = std::max(c.waves_per_simd, launch_waves_per_simd(f, true, c.unit_tiles));
+    if (num_query_tokens == 1)
+      c.waves_per_simd = std::max(c.waves_per_simd, launch_waves_per_simd(f, false, 1));
+  }
   return c;
 }
 
@@ -283,8 +298,7 @@ int decode_common(int fmt, Scales sc, const Rows& r, const AppendRows* app,
   a.out_mul = fmt == PDAKV_KV_INT8_STATIC ? sc.v : 1.f;
   a.k_scale = sc.k;
   a.v_scale = sc.v;
-  const int wps = r.multi ? pdakv::wide_waves_per_simd(fmt, cols.unit_tiles)
-                          : format_waves_per_simd(fmt);
+  const int wps = launch_waves_per_simd(fmt, r.multi, cols.unit_tiles);
   a.num_waves = static_cast<int>(plan_waves(wps, num_seqs, a.vheads, max_context_len));
   a.merge_waves = merge_waves(num_seqs, a.vheads, max_context_len, a.num_waves);
   {
@@ -319,10 +333,15 @@ int decode_common(int fmt, Scales sc, const Rows& r, const AppendRows* app,
       a.lds_wave_bytes = up16(qb);
     }
   }
+  // the plan's partial slots (wave + unit) must lie inside the workspace's
+  // partials region, which the unit records follow
+  const size_t pbytes =
+      partials_bytes(num_seqs, r.tokens, num_q_heads, num_kv_heads, head_dim, max_context_len);
+  const size_t used = static_cast<size_t>(a.num_waves + static_cast<int64_t>(num_seqs) * a.vheads) *
+                      a.slot_cols * (head_dim + 2) * sizeof(float);
+  if (used > pbytes) return PDAKV_ERR_WORKSPACE;
   a.ws = static_cast<float*>(workspace);
-  a.desc = reinterpret_cast<int2*>(
-      static_cast<uint8_t*>(workspace) +
-      partials_bytes(num_seqs, r.tokens, num_q_heads, num_kv_heads, head_dim, max_context_len));
+  a.desc = reinterpret_cast<int2*>(static_cast<uint8_t*>(workspace) + pbytes);
   a.err = err_flag;
   if (app) {
     a.append = 1;

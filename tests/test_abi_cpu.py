@@ -123,9 +123,19 @@ def test_decode_plan_is_consistent(P, B, hkv, L):
         # never more waves than 4-page shares (rounded to whole workgroups)
         assert waves <= max(4, -(-max(resident[fmt], -(-items // 128)) // 4) * 4)
         assert waves <= max(4, -(-(-(-items // 4)) // 4) * 4)
-    w8, _ = P.pdakv_decode_plan(P.KV_INT8_SYM, B, hkv, L)
+
+
+@pytest.mark.parametrize("B,hkv,L", [(1, 8, 2048), (64, 8, 8193), (8, 8, 32768), (3, 1, 1),
+                                     (500, 2, 700), (8, 8, 0)])
+def test_workspace_holds_every_plan(P, B, hkv, L):
+    """The workspace holds the partial slots (wave + unit) of every format's
+    plan, whichever format a call then decodes: it is sized with the most
+    waves any of them plans (a workspace sized for fewer waves than a launch
+    uses would be written past its end)."""
+    wmax = max(P.pdakv_decode_plan(f, B, hkv, L)[0]
+               for f in (P.KV_INT8_SYM, P.KV_16BIT, P.KV_INT8_STATIC))
     ws = P.pdakv_decode_workspace_bytes(B, 4 * hkv, hkv, 128, L)
-    partials = -(-(w8 + B * hkv) * 4 * 130 * 4 // 16) * 16
+    partials = -(-(wmax + B * hkv) * 4 * 130 * 4 // 16) * 16
     assert ws == (0 if L == 0 else partials + B * hkv * 8)
 
 
