@@ -281,9 +281,12 @@ def main():
                                                 pwl.num_kv_heads, pwl.head_dim,
                                                 pwl.max_context_len)
             mode = "multi"
-        _, ms, med = run(pwl, st, args.steps, args.warmup, mode)
+        step, ms, med = run(pwl, st, args.steps, args.warmup, mode)
+        # step_us: back-to-back calls (as the headline's step loop runs them);
+        # call_us: each call between its own pair of events
         print(json.dumps({"profile": args.profile, "workload": pwl.name,
                           "dispatches": args.warmup + 2 * args.steps,
+                          "step_us": round(step * 1e3, 2),
                           "call_us": round(ms * 1e3, 2), "call_us_median": round(med * 1e3, 2)}),
               flush=True)
         return
