@@ -264,6 +264,10 @@ int decode_common(int fmt, Scales sc, const Rows& r, const AppendRows* app,
     if (num_seqs > 0 && max_context_len > 0 && (!app->k || !app->v)) return PDAKV_ERR_INVALID_ARG;
   }
   if (num_seqs == 0) return st;
+  // one query token through a several-token entry point is a one-token
+  // decode (the same columns, limits and layout): it runs the one-token
+  // kernels, so its results equal the one-token calls' bit for bit
+  const bool multi = r.multi && r.tokens > 1;
   DecodeArgs a{};
   a.out = r.out;
   a.out_dtype = r.out_dtype;
@@ -298,7 +302,7 @@ int decode_common(int fmt, Scales sc, const Rows& r, const AppendRows* app,
   a.out_mul = fmt == PDAKV_KV_INT8_STATIC ? sc.v : 1.f;
   a.k_scale = sc.k;
   a.v_scale = sc.v;
-  const int wps = launch_waves_per_simd(fmt, r.multi, cols.unit_tiles);
+  const int wps = launch_waves_per_simd(fmt, multi, cols.unit_tiles);
   a.num_waves = static_cast<int>(plan_waves(wps, num_seqs, a.vheads, max_context_len));
   a.merge_waves = merge_waves(num_seqs, a.vheads, max_context_len, a.num_waves);
   {
@@ -316,13 +320,13 @@ int decode_common(int fmt, Scales sc, const Rows& r, const AppendRows* app,
     const int nb = app ? 4 * head_dim : 0;
     auto up16 = [](int x) { return (x + 15) / 16 * 16; };
     auto area = [&](int n) {
-      return r.multi ? up16(std::max({n * qb, (n - 1) * rb + qb, rb})) : up16(n * (qb + rb));
+      return multi ? up16(std::max({n * qb, (n - 1) * rb + qb, rb})) : up16(n * (qb + rb));
     };
     int n = 1;
     while (n < 64 && area(n + 1) + (n + 1) * nb <= pdakv::kLdsPerWave) ++n;
     a.seg_cap = n;
-    a.lds_q_off = r.multi ? area(n) - n * qb : 0;
-    a.lds_res_off = r.multi ? 0 : n * qb;
+    a.lds_q_off = multi ? area(n) - n * qb : 0;
+    a.lds_res_off = multi ? 0 : n * qb;
     a.lds_nt_off = area(n);
     a.lds_wave_bytes = area(n) + n * nb;
     if (cols.unit_tiles > 1) {
@@ -354,9 +358,14 @@ int decode_common(int fmt, Scales sc, const Rows& r, const AppendRows* app,
     a.vn_sh = app->vsh;
     a.vn_sd = app->vsd;
   }
+  // few units with short contexts: one workgroup per unit, no merge launch
+  a.unit_path = !multi &&
+                static_cast<int64_t>(num_seqs) * num_kv_heads <= pdakv::kUnitMaxUnits &&
+                ceil_div(ceil_div(max_context_len, pdakv::kBlockSize), pdakv::kUnitWaves) <=
+                    pdakv::kUnitMaxPagesPerWave;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = r.q_dtype == PDAKV_DTYPE_BF16;
-  if (r.multi)
+  if (multi)
     return hip_status(fmt == PDAKV_KV_INT8_SYM
                           ? pdakv::launch_decode_int8_multi(a, head_dim, bf16, s)
                           : pdakv::launch_decode_16bit_multi(a, head_dim, bf16, s));

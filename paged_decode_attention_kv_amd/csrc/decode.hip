@@ -1493,6 +1493,139 @@ __device__ __forceinline__ void decode_wave(const DecodeArgs& a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Calls with few units: one workgroup per (sequence, KV head)
+// ---------------------------------------------------------------------------
+// With few units (a short batch: latency-bound), the even split over a whole
+// grid pays a context-length scan, partials in HBM and a second launch for
+// their merge, all in series with a small amount of streaming. Here workgroup
+// u takes unit u = (b, g) alone: its kUnitWaves waves split the unit's pages
+// evenly, each streams its share through the page pipeline of the large-call
+// kernels, leaves its softmax state (acc, max, sum per column) in LDS, and
+// after a barrier the workgroup merges the waves' states and writes the
+// output rows: one launch, no HBM round trip between the waves and the merge.
+// (It pays while each wave has a few pages: a wave streams its share alone.)
+template <class K>
+__device__ __forceinline__ void decode_unit(const DecodeArgs& a) {
+  constexpr int D = K::D;
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i16 = lane & 15, kb = lane >> 4;
+  const int G = a.group;
+  const int b = blockIdx.x / a.num_kv_heads, g = blockIdx.x % a.num_kv_heads;
+  // LDS: every wave's q rows [G][D] (16-bit), then every wave's state
+  // [G][D + 2], then every wave's appended token (new_token_bytes(D))
+  uint16_t* q_lds = reinterpret_cast<uint16_t*>(smem) + w * G * D;
+  float* res_all = reinterpret_cast<float*>(smem + kUnitWaves * G * D * 2);
+  float* res = res_all + w * G * (D + 2);
+  uint8_t* nt = smem + kUnitWaves * G * (D * 2 + (D + 2) * 4) + w * new_token_bytes(D);
+
+  int L = a.ctx[b];
+  if (L < 0 || L > a.max_ctx) {
+    if (g == 0 && w == 0 && lane == 0) raise_flag(a.err, PDAKV_EFLAG_CONTEXT_RANGE);
+    L = L < 0 ? 0 : a.max_ctx;
+  }
+  const int np = (L + kBlockSize - 1) / kBlockSize;
+  const int per = (np + kUnitWaves - 1) / kUnitWaves;  // at most 128 (host-checked)
+  const int p0 = min(w * per, np);
+  const int items = min(per, np - p0);
+
+  // the wave's block ids (lane i: items i and 64 + i), flagged and masked
+  // when out of range; the q rows go to LDS meanwhile
+  const int32_t* row = a.bt + static_cast<int64_t>(b) * a.bt_stride + p0;
+  int blk0 = lane < items ? row[lane] : 0;
+  int blk1 = lane + 64 < items ? row[lane + 64] : 0;
+  stage_q<D, false>(a, b, g, q_lds, lane);
+  if (blk0 < 0 || blk0 >= a.num_blocks) {
+    raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
+    blk0 = -1;
+  }
+  if (blk1 < 0 || blk1 >= a.num_blocks) {
+    raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
+    blk1 = -1;
+  }
+  auto block_of = [&](int i) { return i < 64 ? readlane(blk0, i) : readlane(blk1, i - 64); };
+
+  K kind;
+  SoftmaxState<D / 16> st;
+  softmax_init(st);
+  constexpr int GP = K::kGroup;
+  typename K::Page ga[GP], gb[GP];
+  int ba[GP], bb[GP];
+  auto fill = [&](typename K::Page* grp, int* blk, int first) {
+#pragma unroll
+    for (int j = 0; j < GP; ++j) {
+      const int q = first + j;
+      blk[j] = q < items ? block_of(q) : -1;
+      K::load(grp[j], head_ref<K>(a, blk[j], g), blk[j] >= 0, i16, kb);
+    }
+  };
+  // fused append: the wave holding the unit's last page quantizes the
+  // sequence's newest token for KV head g, patches it into that page as
+  // loaded and stores it after the loop (nobody else reads that slot)
+  const bool owner = a.append && items > 0 && p0 + items == np;
+  bool patched = false;
+  const int pos = (L - 1) % kBlockSize;
+  auto consume = [&](typename K::Page* grp, const int* blk, int first) {
+#pragma unroll
+    for (int j = 0; j < GP; ++j) {
+      const int i = first + j;
+      if (i >= items) return false;
+      const int t = (p0 + i) * kBlockSize;
+      if (patched && i == items - 1) K::patch(grp[j], nt, pos, i16, kb);
+      const int Lv = blk[j] >= 0 ? L : t;  // a missing page is masked whole
+      kind.step(grp[j], t, Lv, Lv, Lv, st);
+    }
+    return true;
+  };
+  fill(ga, ba, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  fill(gb, bb, GP);
+  __builtin_amdgcn_sched_barrier(0);
+  // (after the first pages are in flight; its stores wait until after the
+  // page loop, so that the loop's waits count page loads only)
+  if (owner) patched = K::prepare_new(a, b, g, nt, lane);
+  kind.load_q(a, q_lds, i16, kb, i16 < G);
+  for (int i = 0;; i += 2 * GP) {
+    if (!consume(ga, ba, i)) break;
+    __builtin_amdgcn_sched_barrier(0);
+    fill(ga, ba, i + 2 * GP);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool more = consume(gb, bb, i + GP);
+    __builtin_amdgcn_sched_barrier(0);
+    fill(gb, bb, i + 3 * GP);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!more || i + 2 * GP >= items) break;
+  }
+  stash_result<K>(a, st, res, i16, kb, G);
+  if (patched) {
+    const int blk = block_of(items - 1);
+    if (blk >= 0) K::store_new(a, nt, pos, head_ref<K>(a, blk, g), lane);
+  }
+  __syncthreads();
+
+  // out[c][d] = sum_w 2^(m_w - m) acc_w[c][d] / sum_w 2^(m_w - m) l_w (m = max_w m_w;
+  // a wave without pages has m_w = kMaxInit and adds nothing; no token at
+  // all gives a zero row)
+  for (int e = threadIdx.x; e < G * D; e += 64 * kUnitWaves) {
+    const int c = e / D, d = e % D;
+    float m = kMaxInit;
+#pragma unroll
+    for (int v = 0; v < kUnitWaves; ++v) m = fmaxf(m, res_all[(v * G + c) * (D + 2) + D]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int v = 0; v < kUnitWaves; ++v) {
+      const float* r = res_all + (v * G + c) * (D + 2);
+      const float f = __builtin_amdgcn_exp2f(r[D] - m);
+      num += f * r[d];
+      den += f * r[D + 1];
+    }
+    store_out(a.out, a.out_dtype, b * a.out_ss + (g * G + c) * a.out_sh + d,
+              den > 0.f ? num / den * a.out_mul : 0.f);
+  }
+}
+
 // The register budget per wave (waves per SIMD) sets how many pages a
 // buffer group holds; the host plans one resident round of waves for it.
 template <int D, bool QBF16>
@@ -1538,6 +1671,24 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
     k16WavesPerSimd))) void decode_16bit_multi_kernel(DecodeArgs a) {
   decode_wave<F16Kind<D, BF16, k16PageGroup>, true>(a);
+}
+
+// One workgroup per unit (small calls), at the occupancy of the large-call
+// kernels of the same format (two waves per SIMD).
+template <int D, bool QBF16>
+__global__ __launch_bounds__(64 * kUnitWaves) __attribute__((amdgpu_waves_per_eu(
+    kInt8WavesPerSimd))) void decode_int8_unit_kernel(DecodeArgs a) {
+  decode_unit<Int8Kind<D, QBF16, kInt8PageGroup>>(a);
+}
+template <int D, bool QBF16>
+__global__ __launch_bounds__(64 * kUnitWaves) __attribute__((amdgpu_waves_per_eu(
+    kInt8WavesPerSimd))) void decode_int8_static_unit_kernel(DecodeArgs a) {
+  decode_unit<Int8Kind<D, QBF16, kInt8PageGroup, true>>(a);
+}
+template <int D, bool BF16>
+__global__ __launch_bounds__(64 * kUnitWaves) __attribute__((amdgpu_waves_per_eu(
+    k16WavesPerSimd))) void decode_16bit_unit_kernel(DecodeArgs a) {
+  decode_unit<F16Kind<D, BF16, k16PageGroup>>(a);
 }
 
 // Combine the partials of a unit that spans several waves, per (query token,
@@ -1671,6 +1822,15 @@ hipError_t launch_merge(const DecodeArgs& a, hipStream_t s) {
 // LDS, then the merge of the units split over several waves.
 using DecodeKernel = void (*)(DecodeArgs);
 
+// A call of few units: one workgroup per unit (no merge launch).
+hipError_t launch_unit(DecodeKernel k, const DecodeArgs& a, int head_dim, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(kUnitWaves) *
+                     (a.group * (head_dim * 2 + (head_dim + 2) * 4) + new_token_bytes(head_dim));
+  hipLaunchKernelGGL(k, dim3(static_cast<unsigned>(a.num_seqs) * a.num_kv_heads),
+                     dim3(64 * kUnitWaves), lds, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_pair(DecodeKernel k, const DecodeArgs& a, int head_dim, hipStream_t s) {
   const size_t lds = static_cast<size_t>(kWaves) * a.lds_wave_bytes;
   hipLaunchKernelGGL(k, dim3(a.num_waves / kWaves), dim3(64 * kWaves), lds, s, a);
@@ -1682,6 +1842,13 @@ hipError_t launch_pair(DecodeKernel k, const DecodeArgs& a, int head_dim, hipStr
 }  // namespace
 
 hipError_t launch_decode_int8(const DecodeArgs& a, int head_dim, bool q_bf16, hipStream_t s) {
+  if (a.unit_path) {
+    const DecodeKernel k = head_dim == 128 ? (q_bf16 ? decode_int8_unit_kernel<128, true>
+                                                     : decode_int8_unit_kernel<128, false>)
+                                           : (q_bf16 ? decode_int8_unit_kernel<64, true>
+                                                     : decode_int8_unit_kernel<64, false>);
+    return launch_unit(k, a, head_dim, s);
+  }
   const DecodeKernel k =
       head_dim == 128 ? (q_bf16 ? decode_int8_kernel<128, true> : decode_int8_kernel<128, false>)
                       : (q_bf16 ? decode_int8_kernel<64, true> : decode_int8_kernel<64, false>);
@@ -1719,6 +1886,13 @@ hipError_t launch_decode_int8_multi(const DecodeArgs& a, int head_dim, bool q_bf
 
 hipError_t launch_decode_int8_static(const DecodeArgs& a, int head_dim, bool q_bf16,
                                      hipStream_t s) {
+  if (a.unit_path) {
+    const DecodeKernel k = head_dim == 128 ? (q_bf16 ? decode_int8_static_unit_kernel<128, true>
+                                                     : decode_int8_static_unit_kernel<128, false>)
+                                           : (q_bf16 ? decode_int8_static_unit_kernel<64, true>
+                                                     : decode_int8_static_unit_kernel<64, false>);
+    return launch_unit(k, a, head_dim, s);
+  }
   const DecodeKernel k =
       head_dim == 128
           ? (q_bf16 ? decode_int8_static_kernel<128, true> : decode_int8_static_kernel<128, false>)
@@ -1728,6 +1902,13 @@ hipError_t launch_decode_int8_static(const DecodeArgs& a, int head_dim, bool q_b
 
 hipError_t launch_decode_16bit(const DecodeArgs& a, int head_dim, bool kv_bf16,
                                hipStream_t s) {
+  if (a.unit_path) {
+    const DecodeKernel k = head_dim == 128 ? (kv_bf16 ? decode_16bit_unit_kernel<128, true>
+                                                      : decode_16bit_unit_kernel<128, false>)
+                                           : (kv_bf16 ? decode_16bit_unit_kernel<64, true>
+                                                      : decode_16bit_unit_kernel<64, false>);
+    return launch_unit(k, a, head_dim, s);
+  }
   const DecodeKernel k =
       head_dim == 128
           ? (kv_bf16 ? decode_16bit_kernel<128, true> : decode_16bit_kernel<128, false>)

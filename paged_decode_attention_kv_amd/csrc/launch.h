@@ -24,6 +24,15 @@ constexpr int kDefaultCUs = 256;      // MI355X compute units (when no device an
 constexpr int kMaxMergeWaves = 8;              // merge: waves per (sequence, q head)
 constexpr int kLdsPerWave = 16384;             // decode: LDS staging budget per wave
 constexpr int kMaxPagesPerWave = 128; // decode: block ids a wave holds (2 per lane)
+// Calls with few units: one workgroup of kUnitWaves waves per (sequence, KV
+// head), for one-token decodes of at most kUnitMaxUnits units whose pages
+// split into at most kUnitMaxPagesPerWave per wave (measured: a 256-token
+// context at batch 1, two pages per wave, 15.0 -> 9.4 us; at 2K, sixteen
+// pages per wave, 16.8 -> 23.8 us, so longer contexts keep the even split
+// over the grid).
+constexpr int kUnitWaves = 8;
+constexpr int kUnitMaxUnits = 64;
+constexpr int kUnitMaxPagesPerWave = 4;
 
 // Several-token decode: query tiles (16 columns each) per unit, at most
 // kMaxUnitTiles, and the waves per SIMD of the kernel for a unit of `tiles`
@@ -77,6 +86,7 @@ struct DecodeArgs {
   int2* desc;        // per (sequence, KV head): first covering wave, wave count
   int num_waves;     // waves of the decode grid (a multiple of kWaves)
   int merge_waves;   // waves per merge workgroup (1 .. kMaxMergeWaves)
+  int unit_path;     // decode: one workgroup per unit (a call with few units)
   int seg_cap;       // decode: segments staged in LDS per pass
   int lds_wave_bytes;  // decode: LDS per wave (q rows, results, appended tokens)
   int lds_q_off;       // decode: offsets of the q rows, results and appended
