@@ -260,17 +260,20 @@ __device__ __forceinline__ uint64_t codes_static(const u4_t& w, float s, float r
 enum WriteFormat { kInt8Sym = 0, kInt8Static = 1, kBits16 = 2 };
 
 // Spans per wave of a large call (measured on 262K- and 296K-token
-// prefills): the INT8 writers gain 5-8% from three spans' loads in flight at
-// D = 128 with 8 elements per lane, two with 16 (three and four measured 2%
-// and 5% slower there) and two at D = 64, where more registers cost
-// occupancy; the 16-bit writer, already near the copy rate, is 10% slower
-// with more than one. A call of fewer than kManySpanWaves one-span waves (a
-// decode step's append) keeps one span per wave: its time is one wave's
-// latency, which more spans per wave lengthen (64 tokens: 6 us with one span,
-// 10 us with three). (A persistent form, each wave looping over items with
-// the next item's slots and rows in flight, measured 12-30% slower.)
+// prefills): with 8 elements per lane the INT8 writers gain 5-8% from three
+// spans' loads in flight at D = 128 (two at D = 64, where more registers
+// cost occupancy). With 16 elements per lane the per-token writer is fastest
+// with one span (eight waves per SIMD: 361 us on the 296K-token prefill
+// against 384 us with two, 390 with three), the static-scale writer with two
+// (388 us; 604 us with one); the 16-bit writer, already near the copy rate,
+// is 10% slower with more than one. A call of fewer than kManySpanWaves
+// one-span waves (a decode step's append) keeps one span per wave: its time
+// is one wave's latency, which more spans per wave lengthen (64 tokens: 6 us
+// with one span, 10 us with three). (A persistent form, each wave looping
+// over items with the next item's slots and rows in flight, measured 12-30%
+// slower.)
 constexpr int spans_per_wave(int D, int F, int epl) {
-  return F == kBits16 ? 1 : D == 128 && epl == 8 ? 3 : 2;
+  return F == kBits16 || (F == kInt8Sym && epl == 16) ? 1 : D == 128 && epl == 8 ? 3 : 2;
 }
 constexpr int64_t kManySpanWaves = 2048;
 
