@@ -406,6 +406,8 @@ int write_common(int fmt, Scales sc, const void* k_src, const void* v_src, int s
       static_cast<int64_t>(pdakv_page_bytes(fmt, block_size, num_kv_heads, head_dim));
   a.k_scale = sc.k;
   a.v_scale = sc.v;
+  a.k_rcp = 1.0f / sc.k;  // IEEE binary32 division, correctly rounded
+  a.v_rcp = 1.0f / sc.v;
   a.err = err_flag;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = src_dtype == PDAKV_DTYPE_BF16;

@@ -54,6 +54,7 @@ struct WriteArgs {
   int64_t num_blocks;
   int64_t page_bytes;
   float k_scale, v_scale;  // static-scale format: the layer's K and V scales
+  float k_rcp, v_rcp;      // and their reciprocals fl(1 / scale)
   int32_t* err;
 };
 

@@ -233,7 +233,7 @@ __device__ __forceinline__ uint64_t codes_token(const u4_t& w, float s, float re
 // the division would, and a NaN (which the clamp turns into -128 s) gives
 // -127, the code the division-based rule gives it too. The clamped quotient
 // plus 1.5 * 2^23 rounds to nearest even, and its low byte is the code.
-__device__ __forceinline__ bool static_window(float s) {
+__host__ __device__ __forceinline__ bool static_window(float s) {
   return s >= 0x1p-64f && s <= 0x1p64f;
 }
 
@@ -257,15 +257,18 @@ __device__ __forceinline__ uint64_t codes_static(const u4_t& w, float s, float r
          (static_cast<uint64_t>(pack(f[4], f[5], f[6], f[7])) << 32);
 }
 
-enum WriteFormat { kInt8Sym = 0, kInt8Static = 1, kBits16 = 2 };
+// kInt8StaticDiv: static scales outside the division-free window (one IEEE
+// division per element), a kernel of its own so that the window's kernel
+// carries no division code
+enum WriteFormat { kInt8Sym = 0, kInt8Static = 1, kBits16 = 2, kInt8StaticDiv = 3 };
 
 // Spans per wave of a large call (measured on 262K- and 296K-token
 // prefills): with 8 elements per lane the INT8 writers gain 5-8% from three
 // spans' loads in flight at D = 128 (two at D = 64, where more registers
-// cost occupancy). With 16 elements per lane the per-token writer is fastest
-// with one span (eight waves per SIMD: 361 us on the 296K-token prefill
-// against 384 us with two, 390 with three), the static-scale writer with two
-// (388 us; 604 us with one); the 16-bit writer, already near the copy rate,
+// cost occupancy). With 16 elements per lane both INT8 writers are fastest
+// with one span (eight waves per SIMD; 296K-token prefill: per-token 361 us
+// against 384 us with two and 390 with three, static scales 373-376 us
+// against 407 us with two); the 16-bit writer, already near the copy rate,
 // is 10% slower with more than one. A call of fewer than kManySpanWaves
 // one-span waves (a decode step's append) keeps one span per wave: its time
 // is one wave's latency, which more spans per wave lengthen (64 tokens: 6 us
@@ -273,7 +276,7 @@ enum WriteFormat { kInt8Sym = 0, kInt8Static = 1, kBits16 = 2 };
 // over items with the next item's slots and rows in flight, measured 12-30%
 // slower.)
 constexpr int spans_per_wave(int D, int F, int epl) {
-  return F == kBits16 || (F == kInt8Sym && epl == 16) ? 1 : D == 128 && epl == 8 ? 3 : 2;
+  return F == kBits16 || epl == 16 ? 1 : D == 128 && epl == 8 ? 3 : 2;
 }
 constexpr int64_t kManySpanWaves = 2048;
 
@@ -414,11 +417,12 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q,
       kc[c] = codes_token<BF16>(in.k[c], sk, rk, rk * kInflate);
       vc[c] = codes_token<BF16>(in.v[c], sv, rv, rv * kInflate);
     }
-  } else if (static_window(a.k_scale) && static_window(a.v_scale)) {
+  } else if constexpr (F == kInt8Static) {
+    // (scales inside [2^-64, 2^64]; the reciprocals are fl(1/s), from the host)
 #pragma unroll
     for (int c = 0; c < NV; ++c) {
-      kc[c] = codes_static<BF16>(in.k[c], a.k_scale, 1.0f / a.k_scale);
-      vc[c] = codes_static<BF16>(in.v[c], a.v_scale, 1.0f / a.v_scale);
+      kc[c] = codes_static<BF16>(in.k[c], a.k_scale, a.k_rcp);
+      vc[c] = codes_static<BF16>(in.v[c], a.v_scale, a.v_rcp);
     }
   } else {
     // scales outside [2^-64, 2^64]: one IEEE division per element
@@ -621,8 +625,11 @@ hipError_t launch_quant_write_int8(const WriteArgs& a, int head_dim, bool src_bf
 
 hipError_t launch_quant_write_static(const WriteArgs& a, int head_dim, bool src_bf16,
                                      hipStream_t s) {
-  return src_bf16 ? launch_format<kInt8Static, true>(a, head_dim, s)
-                  : launch_format<kInt8Static, false>(a, head_dim, s);
+  if (static_window(a.k_scale) && static_window(a.v_scale))
+    return src_bf16 ? launch_format<kInt8Static, true>(a, head_dim, s)
+                    : launch_format<kInt8Static, false>(a, head_dim, s);
+  return src_bf16 ? launch_format<kInt8StaticDiv, true>(a, head_dim, s)
+                  : launch_format<kInt8StaticDiv, false>(a, head_dim, s);
 }
 
 hipError_t launch_write_16bit(const WriteArgs& a, int head_dim, hipStream_t s) {
