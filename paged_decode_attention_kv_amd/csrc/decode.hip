@@ -371,7 +371,7 @@ __device__ __forceinline__ int lane_token(int page_tok) {
 // tokens at or past L (tail pages only) get V scale 1.0, as their slots may
 // hold anything.
 struct TokenScales {
-  float sk[4];
+  _Float16 sk[4];
   int e[4];
   _Float16 f[4];
 };
@@ -388,7 +388,7 @@ __device__ __forceinline__ TokenScales token_scales(const Pg& pg, bool tail, int
   TokenScales ts;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    ts.sk[j] = f16_bits_to_f32(static_cast<uint16_t>(ksw[j / 2] >> (16 * (j % 2))));
+    ts.sk[j] = __builtin_bit_cast(_Float16, static_cast<uint16_t>(ksw[j / 2] >> (16 * (j % 2))));
     const _Float16 sv =
         __builtin_bit_cast(_Float16, static_cast<uint16_t>(vsw[j / 2] >> (16 * (j % 2))));
     ts.e[j] = __builtin_amdgcn_frexp_exph(sv);
@@ -405,27 +405,34 @@ template <int ND>
 __device__ __forceinline__ void int8_probs(const f4_t& s, const TokenScales& ts, float qscale,
                                            bool tail, int tok0, int Lc, SoftmaxState<ND>& st,
                                            h4_t& ph, h4_t& pl) {
+  // (the fp16 scale factors enter as mixed-precision fma operands, and the
+  // mask is one compare against the lane's count of attendable tokens)
+  const int lim = tail ? Lc - tok0 : 4;
   float z[4];
-  float zmax = -INFINITY;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    z[j] = s[j] * ts.sk[j] * qscale + static_cast<float>(ts.e[j]);
-    if (tail) z[j] = tok0 + j < Lc ? z[j] : -INFINITY;
-    zmax = max_nc(zmax, z[j]);
+    const float zj =
+        fmaf(s[j] * qscale, static_cast<float>(ts.sk[j]), static_cast<float>(ts.e[j]));
+    z[j] = j < lim ? zj : -INFINITY;
   }
-  raise_max(st, zmax);
-  float p[4];
+  raise_max(st, fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+  float x[4], p[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float x = __builtin_amdgcn_exp2f(z[j] - st.mk);  // 2^(kPScale + z - m)
-    st.l += __builtin_amdgcn_ldexpf(x, -ts.e[j]);
-    p[j] = x * static_cast<float>(ts.f[j]);
+    x[j] = __builtin_amdgcn_exp2f(z[j] - st.mk);  // 2^(kPScale + z - m)
+    st.l += __builtin_amdgcn_ldexpf(x[j], -ts.e[j]);
+    p[j] = fmaf(x[j], static_cast<float>(ts.f[j]), 0.f);  // = x * f (x, f >= 0)
   }
-  // p = hi + lo to 22 bits: hi is p converted to fp16 once (by the
+  // x * f = hi + lo to 22 bits: hi is p converted to fp16 once (by the
   // conversion instruction itself, so that the compiler cannot fold the
-  // product into a second, differently rounded conversion), lo the rest
+  // product into a second, differently rounded conversion), lo the exact
+  // rest x * f - hi (one fma) rounded to fp16
   ph = split_hi(p);
-  pl = split_lo(p, ph);
+  float lo[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    lo[j] = fmaf(x[j], static_cast<float>(ts.f[j]), -static_cast<float>(ph[j]));
+  pl = __builtin_bit_cast(h4_t, u2_t{pack_f16x2(lo[0], lo[1]), pack_f16x2(lo[2], lo[3])});
 }
 
 // One page starting at token page_tok (wave-uniform). The tokens at or past
@@ -485,15 +492,11 @@ __device__ __forceinline__ void load_static_page(StaticPage<D>& pg, HeadRef h, b
 template <int ND>
 __device__ __forceinline__ void static_probs(const f4_t& s, float qscale, bool tail, int tok0,
                                              int Lc, SoftmaxState<ND>& st, h4_t& ph, h4_t& pl) {
+  const int lim = tail ? Lc - tok0 : 4;  // the lane's attendable tokens
   float z[4];
-  float zmax = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    z[j] = s[j] * qscale;
-    if (tail) z[j] = tok0 + j < Lc ? z[j] : -INFINITY;
-    zmax = max_nc(zmax, z[j]);
-  }
-  raise_max(st, zmax);
+  for (int j = 0; j < 4; ++j) z[j] = j < lim ? s[j] * qscale : -INFINITY;
+  raise_max(st, fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
   float x[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {

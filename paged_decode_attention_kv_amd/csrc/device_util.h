@@ -85,13 +85,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 // 16-lane rows, pairs every lane with its partner.
 __device__ __forceinline__ float max_nc(float a, float b) { return a > b ? a : b; }
 
+// (col_max takes the larger of two with one median-of-three against +inf)
 __device__ __forceinline__ float col_max(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = max_nc(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  x = __builtin_amdgcn_fmed3f(__uint_as_float(h[0]), __uint_as_float(h[1]), INFINITY);
   const uint32_t v = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return max_nc(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_amdgcn_fmed3f(__uint_as_float(r[0]), __uint_as_float(r[1]), INFINITY);
 }
 __device__ __forceinline__ float col_sum(float x) {
   const uint32_t u = __float_as_uint(x);
