@@ -184,9 +184,17 @@ __device__ __forceinline__ void softmax_init(SoftmaxState<ND>& st) {
   for (int k = 0; k < ND; ++k) st.acc[k] = f4_t{0.f, 0.f, 0.f, 0.f};
 }
 
-template <int ND>
+// Lane i16 ^ 8 of the same 16-lane row (DPP row rotation by 8).
+__device__ __forceinline__ float row_partner8(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
+// Pair: the tile's columns i16 and i16 ^ 8 hold one head on two pages and
+// keep one running max, so that their accumulators add at the end.
+template <bool Pair = false, int ND>
 __device__ __forceinline__ void raise_max(SoftmaxState<ND>& st, float zmax) {
   zmax = col_max(zmax);
+  if constexpr (Pair) zmax = __builtin_amdgcn_fmed3f(zmax, row_partner8(zmax), INFINITY);
   if (__any(zmax > st.m + kTau)) {
     const float m_new = fmaxf(st.m, zmax);
     const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 on the first token
@@ -375,10 +383,10 @@ struct TokenScales {
   int e[4];
   _Float16 f[4];
 };
-template <class Pg>
-__device__ __forceinline__ TokenScales token_scales(const Pg& pg, bool tail, int tok0, int L) {
-  const uint32_t ksw[2] = {pg.ks.x, pg.ks.y};
-  uint32_t vsw[2] = {pg.vs.x, pg.vs.y};
+__device__ __forceinline__ TokenScales token_scales_w(u2_t ks, u2_t vs, bool tail, int tok0,
+                                                      int L) {
+  const uint32_t ksw[2] = {ks.x, ks.y};
+  uint32_t vsw[2] = {vs.x, vs.y};
   if (tail) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -396,12 +404,16 @@ __device__ __forceinline__ TokenScales token_scales(const Pg& pg, bool tail, int
   }
   return ts;
 }
+template <class Pg>
+__device__ __forceinline__ TokenScales token_scales(const Pg& pg, bool tail, int tok0, int L) {
+  return token_scales_w(pg.ks, pg.vs, tail, tok0, L);
+}
 
 // Softmax update of one query tile from its logit tile s: base-2 logits
 // plus the V scale's exponent (P = 2^(z - m) * f), tokens at or past Lc
 // masked, running max and sum, and the probabilities (V scale folded in) as
 // high and low fp16 parts for the PV product.
-template <int ND>
+template <bool Pair = false, int ND>
 __device__ __forceinline__ void int8_probs(const f4_t& s, const TokenScales& ts, float qscale,
                                            bool tail, int tok0, int Lc, SoftmaxState<ND>& st,
                                            h4_t& ph, h4_t& pl) {
@@ -415,7 +427,7 @@ __device__ __forceinline__ void int8_probs(const f4_t& s, const TokenScales& ts,
         fmaf(s[j] * qscale, static_cast<float>(ts.sk[j]), static_cast<float>(ts.e[j]));
     z[j] = j < lim ? zj : -INFINITY;
   }
-  raise_max(st, fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+  raise_max<Pair>(st, fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
   float x[4], p[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -489,14 +501,14 @@ __device__ __forceinline__ void load_static_page(StaticPage<D>& pg, HeadRef h, b
 // part of qscale): tokens at or past Lc masked (any byte in a slot past the
 // context is a finite code, so 0 * code adds nothing), running max and sum,
 // probabilities as high and low fp16 parts.
-template <int ND>
+template <bool Pair = false, int ND>
 __device__ __forceinline__ void static_probs(const f4_t& s, float qscale, bool tail, int tok0,
                                              int Lc, SoftmaxState<ND>& st, h4_t& ph, h4_t& pl) {
   const int lim = tail ? Lc - tok0 : 4;  // the lane's attendable tokens
   float z[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) z[j] = j < lim ? s[j] * qscale : -INFINITY;
-  raise_max(st, fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+  raise_max<Pair>(st, fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
   float x[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -525,12 +537,72 @@ __device__ __forceinline__ void static_page_step(const Pg& pg, const h8_t* qf,
   }
 }
 
+// Two consecutive pages a, b of one segment against one query tile for a
+// group of at most 8 heads: the tile's 16 MFMA columns hold the heads twice,
+// columns 0-7 (lanes with i16 < 8) for page a and 8-15 for page b, so one
+// softmax update covers 32 tokens. QK runs per page with the same q
+// fragments and each lane keeps its page's logits; in PV, page a's V meets
+// the probabilities of the columns 0-7 only (zeros in the others) and page
+// b's V those of columns 8-15, into one accumulator whose two column halves
+// share the running max and add up when the segment ends (fold_pair).
+// La, Lb: the pages' limits (a missing page gets its first token: masked).
+template <int D, bool Static, class Pg>
+__device__ __forceinline__ void int8_pair_step(const Pg& pa, const Pg& pb, const h8_t* qf,
+                                               float qscale, int tok_a, int La, int Lb,
+                                               SoftmaxState<D / 16>& st) {
+  constexpr int ND = D / 16;
+  const bool hi = (threadIdx.x & 8) != 0;
+  const f4_t sa = int8_qk<D>(pa, qf);
+  const f4_t sb = int8_qk<D>(pb, qf);
+  f4_t s;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s[r] = hi ? sb[r] : sa[r];
+  const bool tail = tok_a + 2 * kBlockSize > min(La, Lb);
+  const int L = hi ? Lb : La;
+  const int tok0 = tail ? lane_token(tok_a + (hi ? kBlockSize : 0)) : 0;
+  h4_t ph, pl;
+  if constexpr (Static) {
+    static_probs<true>(s, qscale, tail, tok0, L, st, ph, pl);
+  } else {
+    const TokenScales ts =
+        token_scales_w(hi ? pb.ks : pa.ks, hi ? pb.vs : pa.vs, tail, tok0, L);
+    int8_probs<true>(s, ts, qscale, tail, tok0, L, st, ph, pl);
+  }
+  const h4_t zero = {};
+  const h4_t pha = hi ? zero : ph, pla = hi ? zero : pl;
+  const h4_t phb = hi ? ph : zero, plb = hi ? pl : zero;
+#pragma unroll
+  for (int k = 0; k < ND; ++k) {
+    const h4_t va = v_frag(pa, k), vb = v_frag(pb, k);
+    st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pha, st.acc[k], 0, 0, 0);
+    st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pla, st.acc[k], 0, 0, 0);
+    st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(vb, phb, st.acc[k], 0, 0, 0);
+    st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(vb, plb, st.acc[k], 0, 0, 0);
+  }
+}
+
+// End of a pair segment: add the column halves (page a's and page b's
+// tokens of each head; same running max), in every lane of the row.
+template <int ND>
+__device__ __forceinline__ void fold_pair(SoftmaxState<ND>& st) {
+#pragma unroll
+  for (int k = 0; k < ND; ++k)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st.acc[k][j] += row_partner8(st.acc[k][j]);
+  st.l += row_partner8(st.l);
+}
+
 // The INT8 page formats as seen by the decode loop: per-token FP16 scales in
 // the page, or (Static) codes only with the layer's two scalar scales.
-template <int D_, bool QBF16, int G_ = 1, bool Static = false>
+template <int D_, bool QBF16, int G_ = 1, bool Static = false, bool Pair = false>
 struct Int8Kind {
   static constexpr int D = D_;
   static constexpr int kGroup = G_;  // pages per register buffer
+  // pairs of pages per softmax update (one-token calls, groups of <= 8 heads)
+  static constexpr bool kPair = Pair;
+  static_assert(!Pair || G_ == 2, "a pair kind streams pages two by two");
+  // the head of MFMA column i16
+  static __device__ __forceinline__ int col_head(int i16) { return Pair ? (i16 & 7) : i16; }
   static constexpr int kCodeBytes = 32 * D;            // a head's K and V codes
   static constexpr int kScaleBytes = Static ? 0 : 64;  // a head's scale records
   using Page = typename std::conditional<Static, StaticPage<D>, Int8Page<D>>::type;
@@ -561,6 +633,11 @@ struct Int8Kind {
       static_page_step<D>(pg, qf, qscale, page_tok, Lmin, Lc, st);
     else
       int8_page_step<D>(pg, qf, qscale, page_tok, L, Lmin, Lc, st);
+  }
+  // two consecutive pages of one segment (pair kinds)
+  __device__ __forceinline__ void step_pair(const Page& pa, const Page& pb, int tok_a, int La,
+                                            int Lb, SoftmaxState<D / 16>& st) const {
+    int8_pair_step<D, Static>(pa, pb, qf, qscale, tok_a, La, Lb, st);
   }
   // One page against the first nt of NT query tiles (tile c: q fragments
   // kd[c], state st[c], column limit Lc[c]), two tiles at a time: every K and
@@ -869,6 +946,8 @@ template <int D_, bool BF16, int G_ = 1>
 struct F16Kind {
   static constexpr int D = D_;
   static constexpr int kGroup = G_;  // pages per register buffer
+  static constexpr bool kPair = false;
+  static __device__ __forceinline__ int col_head(int i16) { return i16; }
   static constexpr int kCodeBytes = 64 * D;  // a head's K and V values
   static constexpr int kScaleBytes = 0;
   using Page = Page16<D>;
@@ -1025,6 +1104,7 @@ template <class K>
 __device__ __forceinline__ void stash_result(const DecodeArgs& a, SoftmaxState<K::D / 16>& st,
                                              float* res, int i16, int kb, int n) {
   constexpr int D = K::D, ND = D / 16;
+  if constexpr (K::kPair) fold_pair(st);
   const float l = col_sum(st.l);
   if (i16 >= n) return;
   float* r = res + i16 * (D + 2);
@@ -1109,14 +1189,17 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   const int C = a.slot_cols;              // LDS columns per segment
 
   // plan: lane s keeps segment s's unit, first page, first item, length, L
+  // (a pair kind pads each segment to whole pairs: `items` counts the
+  // pass's page slots, holes included, `real` the wave's items done)
+  constexpr bool kPair = K::kPair;
   int s_unit = 0, s_p = 0, s_start = 0, s_n = 0, s_L = 0, s_whole = 0, s_last = 0;
-  int ns = 0, items = 0;
+  int ns = 0, items = 0, real = 0;
   while (true) {
-    const int n = min(min(cu.np - cu.p, x1 - (x + items)), kMaxPagesPerWave - items);
+    const int n = min(min(cu.np - cu.p, x1 - (x + real)), kMaxPagesPerWave - items);
     const int u = cu.b * vh + cu.g;
     if (cu.p == 0 && lane == 0) {
       // this wave holds the unit's first item: record which waves cover it
-      a.desc[u] = make_int2(wave, (x + items + cu.np - 1) / P - wave + 1);
+      a.desc[u] = make_int2(wave, (x + real + cu.np - 1) / P - wave + 1);
     }
     if (lane == ns) {
       s_unit = u;
@@ -1128,16 +1211,19 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
       s_last = cu.p + n == cu.np;  // holds the unit's last page
     }
     ++ns;
-    items += n;
+    items += kPair ? n + (n & 1) : n;  // (items stays even for pairs: 128 - items > n)
+    real += n;
     cu.p += n;
-    if (cu.p == cu.np && x + items < x1 && !next_unit(a, cu, nchunk, vh, lane)) return 0;
-    if (x + items >= x1 || ns == a.seg_cap || items == kMaxPagesPerWave) break;
+    if (cu.p == cu.np && x + real < x1 && !next_unit(a, cu, nchunk, vh, lane)) return 0;
+    if (x + real >= x1 || ns == a.seg_cap || items >= kMaxPagesPerWave) break;
   }
 
   // pages of the items: lane i holds the block ids and KV heads of items i
   // and 64 + i; out-of-range block ids are flagged and become -1 (the page
   // is masked)
-  int blk0 = 0, blk1 = 0, g0 = 0, g1 = 0;
+  // (slots that hold no item, the holes of pair padding, stay -1)
+  int blk0 = -1, blk1 = -1, g0 = 0, g1 = 0;
+  bool own0 = false, own1 = false;
   for (int s = 0; s < ns; ++s) {
     const int st = readlane(s_start, s), n = readlane(s_n, s);
     const int u = readlane(s_unit, s);
@@ -1146,10 +1232,12 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     if (lane >= st && lane < st + n) {
       blk0 = row[lane - st];
       g0 = g;
+      own0 = true;
     }
     if (lane + 64 >= st && lane + 64 < st + n) {
       blk1 = row[lane + 64 - st];
       g1 = g;
+      own1 = true;
     }
   }
   // the q rows go to LDS while the block ids are in flight
@@ -1157,11 +1245,11 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
     const int u = readlane(s_unit, s);
     stage_q<D, Multi>(a, u / vh, u % vh, lds.q + s * C * D, lane);
   }
-  if (blk0 < 0 || blk0 >= a.num_blocks) {
+  if (own0 && (blk0 < 0 || blk0 >= a.num_blocks)) {
     raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
     blk0 = -1;
   }
-  if (blk1 < 0 || blk1 >= a.num_blocks) {
+  if (own1 && (blk1 < 0 || blk1 >= a.num_blocks)) {
     raise_flag(a.err, PDAKV_EFLAG_BLOCK_RANGE);
     blk1 = -1;
   }
@@ -1174,13 +1262,14 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   // whether its last page gets the appended token, its column count and (for
   // several query tokens) the smallest and the lane's own attention limit
   int s_patch = 0;  // lane s: segment s's appended token is in LDS
-  int cs = 0, c_tok = 0, c_start = 0, c_end = 0, c_L = 0, c_patch = 0, c_n = a.group;
-  int c_Lmin = 0, c_Lc = 0;
+  int cs = 0, c_tok = 0, c_start = 0, c_end = 0, c_endp = 0, c_L = 0, c_patch = 0;
+  int c_n = a.group, c_Lmin = 0, c_Lc = 0;
   auto enter = [&](int sidx) {
     cs = sidx;
     c_tok = readlane(s_p, sidx) * kBlockSize;
     c_start = readlane(s_start, sidx);
     c_end = c_start + readlane(s_n, sidx);
+    c_endp = kPair ? c_end + ((c_end - c_start) & 1) : c_end;  // with the hole
     c_L = readlane(s_L, sidx);
     c_patch = readlane(s_patch, sidx);
     if constexpr (Multi) {
@@ -1211,6 +1300,28 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   };
   // consume items first.. of a group; false once the pass's items are done
   auto consume = [&](typename K::Page* grp, const int* blk, int first) {
+    if constexpr (kPair) {
+      // the group is one pair of one segment
+      const int i = first;
+      if (i >= items) return false;
+      if (i == c_endp) {  // next segment: only registers and LDS are touched
+        stash_result<K>(a, st, lds.res + cs * C * (D + 2), i16, kb, c_n);
+        enter(cs + 1);
+        softmax_init(st);
+        const int h = K::col_head(i16);
+        kind.load_q(a, lds.q + cs * C * D, h, kb, h < c_n);
+      }
+      const int t = c_tok + (i - c_start) * kBlockSize;
+      if (c_patch) {
+        const int pos = (c_L - 1) % kBlockSize;
+        const uint8_t* nt = lds.nt + cs * new_token_bytes(D);
+        if (i == c_end - 1) K::patch(grp[0], nt, pos, i16, kb);
+        if (i + 1 == c_end - 1) K::patch(grp[1], nt, pos, i16, kb);
+      }
+      kind.step_pair(grp[0], grp[1], t, blk[0] >= 0 ? c_L : t,
+                     blk[1] >= 0 ? c_L : t + kBlockSize, st);
+      return true;
+    }
 #pragma unroll
     for (int j = 0; j < G; ++j) {
       const int i = first + j;
@@ -1255,7 +1366,7 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   }
   enter(0);
   softmax_init(st);
-  kind.load_q(a, lds.q, i16, kb, i16 < c_n);
+  kind.load_q(a, lds.q, K::col_head(i16), kb, K::col_head(i16) < c_n);
   for (int i = 0;; i += 2 * G) {
     if (!consume(ga, ba, i)) break;
     __builtin_amdgcn_sched_barrier(0);
@@ -1294,7 +1405,7 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
                              readlane(s_whole, s) != 0, lane);
     }
   }
-  return items;
+  return real;
 }
 
 // Write tile i's softmax state straight from registers (after the page
@@ -1631,10 +1742,11 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a) {
 
 // The register budget per wave (waves per SIMD) sets how many pages a
 // buffer group holds; the host plans one resident round of waves for it.
-template <int D, bool QBF16>
+// Pair: groups of at most 8 heads take two pages per softmax update
+template <int D, bool QBF16, bool Pair>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
     kInt8WavesPerSimd))) void decode_int8_kernel(DecodeArgs a) {
-  decode_wave<Int8Kind<D, QBF16, kInt8PageGroup>, false>(a);
+  decode_wave<Int8Kind<D, QBF16, kInt8PageGroup, false, Pair>, false>(a);
 }
 
 template <int D, bool QBF16>
@@ -1658,10 +1770,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
   decode_wave<F16Kind<D, BF16, 1>, true, NT>(a);
 }
 
-template <int D, bool QBF16>
+template <int D, bool QBF16, bool Pair>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(
     kInt8WavesPerSimd))) void decode_int8_static_kernel(DecodeArgs a) {
-  decode_wave<Int8Kind<D, QBF16, kInt8PageGroup, true>, false>(a);
+  decode_wave<Int8Kind<D, QBF16, kInt8PageGroup, true, Pair>, false>(a);
 }
 
 template <int D, bool BF16>
@@ -1842,6 +1954,31 @@ hipError_t launch_pair(DecodeKernel k, const DecodeArgs& a, int head_dim, hipStr
   return head_dim == 128 ? launch_merge<128>(a, s) : launch_merge<64>(a, s);
 }
 
+// The one-token INT8 grid kernel for a head size, q type and scale format:
+// head size 128 with a group that fits the pair tile takes two pages per
+// softmax update (measured: batched step 126 -> 122 us back to back, 32K
+// 112 -> 105 us); head size 64 keeps one (its smaller pages gained nothing:
+// the small-head configuration measured 22.2 -> 22.5 us).
+constexpr int kPairMaxGroup = 8;
+template <bool Static, int D, bool B>
+DecodeKernel int8_kernel(bool pair) {
+  if constexpr (Static)
+    return pair ? decode_int8_static_kernel<D, B, true> : decode_int8_static_kernel<D, B, false>;
+  else
+    return pair ? decode_int8_kernel<D, B, true> : decode_int8_kernel<D, B, false>;
+}
+template <bool Static>
+DecodeKernel pick_int8(int head_dim, int group, bool q_bf16) {
+  const bool pair = group <= kPairMaxGroup;
+  if (head_dim == 128)
+    return q_bf16 ? int8_kernel<Static, 128, true>(pair) : int8_kernel<Static, 128, false>(pair);
+  if constexpr (Static)
+    return q_bf16 ? decode_int8_static_kernel<64, true, false>
+                  : decode_int8_static_kernel<64, false, false>;
+  else
+    return q_bf16 ? decode_int8_kernel<64, true, false> : decode_int8_kernel<64, false, false>;
+}
+
 }  // namespace
 
 hipError_t launch_decode_int8(const DecodeArgs& a, int head_dim, bool q_bf16, hipStream_t s) {
@@ -1852,9 +1989,7 @@ hipError_t launch_decode_int8(const DecodeArgs& a, int head_dim, bool q_bf16, hi
                                                      : decode_int8_unit_kernel<64, false>);
     return launch_unit(k, a, head_dim, s);
   }
-  const DecodeKernel k =
-      head_dim == 128 ? (q_bf16 ? decode_int8_kernel<128, true> : decode_int8_kernel<128, false>)
-                      : (q_bf16 ? decode_int8_kernel<64, true> : decode_int8_kernel<64, false>);
+  const DecodeKernel k = pick_int8<false>(head_dim, a.group, q_bf16);
   return launch_pair(k, a, head_dim, s);
 }
 
@@ -1896,10 +2031,7 @@ hipError_t launch_decode_int8_static(const DecodeArgs& a, int head_dim, bool q_b
                                                      : decode_int8_static_unit_kernel<64, false>);
     return launch_unit(k, a, head_dim, s);
   }
-  const DecodeKernel k =
-      head_dim == 128
-          ? (q_bf16 ? decode_int8_static_kernel<128, true> : decode_int8_static_kernel<128, false>)
-          : (q_bf16 ? decode_int8_static_kernel<64, true> : decode_int8_static_kernel<64, false>);
+  const DecodeKernel k = pick_int8<true>(head_dim, a.group, q_bf16);
   return launch_pair(k, a, head_dim, s);
 }
 
