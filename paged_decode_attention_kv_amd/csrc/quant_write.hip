@@ -297,11 +297,14 @@ struct Rows {
 // (nt >= 1): lane (head hh, token r, i) gets elements EPL*i .. EPL*i + EPL-1
 // of token r's rows of KV head h0 + hh; past the call's end the last token,
 // and past the last head the last head, are loaded again.
-template <int D, int EPL, bool Vec>
+// (QPW = 2: the wave's lane groups of HPW / 2 heads each take one of two
+// quads, q and t0 being those of the lane's quad)
+template <int D, int EPL, bool Vec, int QPW = 1>
 __device__ __forceinline__ Rows<EPL> load_rows(const WriteArgs& a, const Quad& q, int64_t t0,
                                                int h0, int lane) {
   constexpr int NV = EPL / 8, LPT = D / EPL, LPH = kQuad * LPT;
-  const int hh = lane / LPH, r = lane % LPH / LPT, i = lane % LPT;
+  constexpr int HQ = heads_per_wave(D, EPL) / QPW;  // heads per quad
+  const int hh = lane / LPH % HQ, r = lane % LPH / LPT, i = lane % LPT;
   const int h = h0 + hh;
   const int hl = h < a.num_kv_heads ? h : a.num_kv_heads - 1;
   const int64_t t = t0 + (r < q.nt ? r : q.nt - 1);
@@ -367,19 +370,23 @@ __device__ __forceinline__ uint64_t codes_static_div(const u4_t& w, float s) {
 // group words (one dimension of the four tokens) and every lane stores
 // EPL / 4 whole words; otherwise each token's V elements are stored one by
 // one.
-template <int D, int EPL, int F, bool BF16>
+// QPW = 2: two quads at once, the lane groups of the first HPW / 2 heads on
+// q's first quad and the others on its second (q is the lane's own quad).
+template <int D, int EPL, int F, bool BF16, int QPW = 1>
 __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q,
                                            const Rows<EPL>& in, int h0, u4_t* s_elems,
                                            int lane) {
   constexpr int NV = EPL / 8;       // vectors of eight elements per lane
   constexpr int LPT = D / EPL;      // lanes per token row
   constexpr int LPH = kQuad * LPT;  // lanes per head
+  constexpr int HQ = heads_per_wave(D, EPL) / QPW;  // heads per quad
   constexpr int E = F == kBits16 ? 2 : 1;  // bytes per stored element
   constexpr bool Scales = F == kInt8Sym;
   static_assert(NV * 8 * E <= 16, "a lane's V elements fit its 16 LDS bytes");
   using L = HeadLayout<D, E, Scales>;
   using Packed = typename std::conditional<E == 2, u4_t, uint64_t>::type;  // eight elements
-  const int hh = lane / LPH, r = lane % LPH / LPT, i = lane % LPT;
+  const int hg = lane / LPH;  // the lane group of one head and one quad
+  const int hh = hg % HQ, r = lane % LPH / LPT, i = lane % LPT;
   const int h = h0 + hh;
   const bool hvalid = h < a.num_kv_heads;
   const int32_t my_slot = r == 0 ? q.slot[0] : r == 1 ? q.slot[1] : r == 2 ? q.slot[2] : q.slot[3];
@@ -435,7 +442,7 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q,
   // whole V group of this lane's head: all four tokens stored (uniform over
   // the head's lanes)
   const uint64_t stored = __ballot(ok);
-  const uint64_t head_lanes = LPH == 64 ? ~0ull : ((1ull << LPH) - 1) << (LPH * hh);
+  const uint64_t head_lanes = LPH == 64 ? ~0ull : ((1ull << LPH) - 1) << (LPH * hg);
   const bool whole = q.nt == kQuad && (stored & head_lanes) == head_lanes &&
                      q.slot[0] % 4 == 0 && q.slot[1] == q.slot[0] + 1 &&
                      q.slot[2] == q.slot[0] + 2 && q.slot[3] == q.slot[0] + 3;
@@ -474,7 +481,7 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q,
     // head (one element of each token per word): it reads from each token's
     // lane (hh, j, i) the word that holds those dimensions' elements and
     // gathers them with byte selects
-    const uint32_t* ew = reinterpret_cast<const uint32_t*>(s_elems + LPH * hh + i);
+    const uint32_t* ew = reinterpret_cast<const uint32_t*>(s_elems + LPH * hg + i);
     uint32_t d[kQuad];
     if constexpr (E == 1 && NV == 2) {
       // dims 16i + 4r .. 16i + 4r + 3: word r of each token's 16 codes; a
@@ -530,9 +537,14 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q,
 // groups) and 16 * EPL / D KV heads. The rows of all its spans are loaded
 // before the first is quantized and stored, so a wave keeps kSpans times the
 // bytes in flight; a span across two runs of slots takes a second round.
-template <int D, int F, bool BF16, bool Vec, int kSpans, int EPL>
+// QPW = 2 (two quads per wave, kSpans = 2): the wave's first HPW / 2 heads'
+// lane groups take span 0 and the others span 1, side by side in one round,
+// so that the 16-element form serves a head count that fills only half a
+// wave (two KV heads at D = 64, an odd count at D = 128).
+template <int D, int F, bool BF16, bool Vec, int kSpans, int EPL, int QPW = 1>
 __global__ __launch_bounds__(64 * kWriteWaves) void write_kernel(WriteArgs a) {
-  constexpr int HPW = heads_per_wave(D, EPL);  // KV heads per wave
+  constexpr int HPW = heads_per_wave(D, EPL) / QPW;  // KV heads per wave
+  static_assert(QPW == 1 || kSpans == 2, "two quads: the wave's two spans side by side");
   __shared__ u4_t s_elems[kWriteWaves][64];  // a lane's V elements
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -546,6 +558,39 @@ __global__ __launch_bounds__(64 * kWriteWaves) void write_kernel(WriteArgs a) {
   const int h0 = static_cast<int>(w - g * hgroups) * HPW;
   Span sp[kSpans];
   load_spans<kSpans>(a, g * kSpans, lane, sp);
+  if constexpr (QPW == 2) {
+    constexpr int LPH = kQuad * D / EPL;
+    const bool second = lane >= LPH * HPW;  // the lane's quad: span 1
+    // a quad with nothing to store for the lane: span 0's tokens (valid
+    // rows to load), no slots
+    auto idle = [](Quad q) {
+#pragma unroll
+      for (int j = 0; j < kQuad; ++j) q.slot[j] = -1;
+      return q;
+    };
+    auto pick = [&](const Quad& q0, int64_t t0, const Quad& q1, int64_t t1, Quad& q,
+                    int64_t& t) {
+      t = second ? t1 : t0;
+      q.nt = second ? q1.nt : q0.nt;
+#pragma unroll
+      for (int j = 0; j < kQuad; ++j) q.slot[j] = second ? q1.slot[j] : q0.slot[j];
+    };
+    const Quad a0 = quad_of<0>(sp[0]);
+    const bool has1 = sp[1].n > 0;
+    Quad q;
+    int64_t t;
+    pick(a0, sp[0].t0, has1 ? quad_of<0>(sp[1]) : idle(a0), has1 ? sp[1].t0 : sp[0].t0, q, t);
+    const Rows<EPL> in = load_rows<D, EPL, Vec, 2>(a, q, t, h0, lane);
+    write_quad<D, EPL, F, BF16, 2>(a, q, in, h0, s_elems[wv], lane);
+    const bool more0 = sp[0].n > kQuad, more1 = sp[1].n > kQuad;
+    if (more0 || more1) {  // a span across two runs of slots: its second round
+      pick(more0 ? quad_of<1>(sp[0]) : idle(a0), more0 ? sp[0].t0 + kQuad : sp[0].t0,
+           more1 ? quad_of<1>(sp[1]) : idle(a0), more1 ? sp[1].t0 + kQuad : sp[0].t0, q, t);
+      const Rows<EPL> in1 = load_rows<D, EPL, Vec, 2>(a, q, t, h0, lane);
+      write_quad<D, EPL, F, BF16, 2>(a, q, in1, h0, s_elems[wv], lane);
+    }
+    return;
+  }
   Rows<EPL> in[kSpans];
 #pragma unroll
   for (int p = 0; p < kSpans; ++p)
@@ -563,9 +608,10 @@ __global__ __launch_bounds__(64 * kWriteWaves) void write_kernel(WriteArgs a) {
     }
 }
 
-// Waves of a call at `spans` spans per wave and `epl` elements per lane.
-int64_t write_waves(const WriteArgs& a, int head_dim, int spans, int epl) {
-  const int hpw = heads_per_wave(head_dim, epl);
+// Waves of a call at `spans` spans per wave and `epl` elements per lane
+// (qpw = 2: the two spans side by side, half the heads per wave).
+int64_t write_waves(const WriteArgs& a, int head_dim, int spans, int epl, int qpw = 1) {
+  const int hpw = heads_per_wave(head_dim, epl) / qpw;
   const int64_t quads = (a.num_tokens + kQuad - 1) / kQuad;
   return (quads + spans - 1) / spans * ((a.num_kv_heads + hpw - 1) / hpw);
 }
@@ -580,16 +626,16 @@ bool vec_rows(const WriteArgs& a, int bytes) {
          (reinterpret_cast<uintptr_t>(a.v) % bytes) == 0;
 }
 
-template <int D, int F, bool BF16, int S, int EPL>
+template <int D, int F, bool BF16, int S, int EPL, int QPW = 1>
 hipError_t launch_spans(const WriteArgs& a, hipStream_t s) {
-  const int64_t waves = write_waves(a, D, S, EPL);
+  const int64_t waves = write_waves(a, D, S, EPL, QPW);
   const dim3 grid(static_cast<unsigned>((waves + kWriteWaves - 1) / kWriteWaves)),
       block(64 * kWriteWaves);
   // lanes load 16 bytes of a row
   if (vec_rows(a, 16))
-    hipLaunchKernelGGL((write_kernel<D, F, BF16, true, S, EPL>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((write_kernel<D, F, BF16, true, S, EPL, QPW>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((write_kernel<D, F, BF16, false, S, EPL>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((write_kernel<D, F, BF16, false, S, EPL, QPW>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -604,8 +650,10 @@ hipError_t launch_epl(const WriteArgs& a, hipStream_t s) {
 template <int D, int F, bool BF16>
 hipError_t launch_dim(const WriteArgs& a, hipStream_t s) {
   if constexpr (F != kBits16) {
-    if (a.num_kv_heads % heads_per_wave(D, kWideEpl) == 0)
-      return launch_epl<D, F, BF16, kWideEpl>(a, s);
+    constexpr int hpw = heads_per_wave(D, kWideEpl);
+    if (a.num_kv_heads % hpw == 0) return launch_epl<D, F, BF16, kWideEpl>(a, s);
+    // heads that fill half a wave: two quads per wave
+    if (a.num_kv_heads % (hpw / 2) == 0) return launch_spans<D, F, BF16, 2, kWideEpl, 2>(a, s);
   }
   return launch_epl<D, F, BF16, 8>(a, s);
 }

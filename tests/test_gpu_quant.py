@@ -217,14 +217,17 @@ def _mixed_slots(rng, num_blocks, runs=18):
 
 @pytest.mark.parametrize("kind", ["int8", "static", "16bit"])
 @pytest.mark.parametrize("d,hkv,runs", [(64, 2, 18), (64, 3, 18), (128, 2, 18),
-                                        (64, 3, 3000), (128, 2, 3000)])
+                                        (64, 3, 3000), (128, 2, 3000), (64, 2, 3000),
+                                        (64, 6, 400), (128, 1, 400), (128, 3, 3000)])
 def test_write_spans_mixed_runs(P, kind, d, hkv, runs):
     """Slot runs of every length and page offset, reversed runs, padding and
-    out-of-range slots, token count not a multiple of four (and, at D = 64,
-    an odd number of KV heads for the two-heads-per-wave INT8 writer): the
-    whole pool equals the oracle's writes of the tokens with valid slots.
-    3,000 runs (about 36K tokens) make a call large enough for the INT8
-    writers' several spans per wave; 18 runs keep one."""
+    out-of-range slots, token count not a multiple of four, and every lane
+    map of the INT8 writers: whole waves of heads (D = 128 with an even head
+    count), two quads of four tokens side by side in a wave (two or six heads
+    at D = 64, one or three at D = 128) and eight elements per lane (three
+    heads at D = 64): the whole pool equals the oracle's writes of the tokens
+    with valid slots. 3,000 runs (about 36K tokens) make a call large enough
+    for several spans per wave; 18 runs keep one."""
     rng = np.random.default_rng(30 + d + hkv + runs)
     nb = 64 if runs <= 32 else 4 * runs
     slots = _mixed_slots(rng, nb, runs)
