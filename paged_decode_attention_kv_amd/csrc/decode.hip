@@ -251,6 +251,57 @@ __device__ __forceinline__ float load_q_scaled(const DecodeArgs& a, bool hvalid,
   return __builtin_amdgcn_ldexpf(a.scale_log2, -kq);
 }
 
+// q for the integer matrix instructions of the page-pair kernels: the lane's
+// 16 dims of each 64-dim chunk i (chunk(2i), chunk(2i + 1)) as integers
+// qi = rint(q * 2^kq) with max|qi| of the head in [2^21, 2^22], in base 256
+// with signed digits: qi = 2^16 a + 2^8 b + c (a, b, c in [-128, 127]; the
+// bytes of qi + 0x808080 are a + 128, b + 128, c + 128), digit p of chunk i
+// one byte per dim in qp[i][p]. The products with the codes and their sums
+// over the chunks are then exact in int32; rounding q costs at most 2^-22 of
+// the head's largest element per element. Returns the factor that turns
+// 2^16 A + 2^8 B + C into base-2 logits.
+typedef int i4_t __attribute__((ext_vector_type(4)));
+template <int NI, bool QBF16, typename ChunkFn>
+__device__ __forceinline__ float load_q_pieces(const DecodeArgs& a, bool hvalid, ChunkFn chunk,
+                                               i4_t (*qp)[3]) {
+  u4_t raw[2 * NI];
+#pragma unroll
+  for (int j = 0; j < 2 * NI; ++j) raw[j] = chunk(j);
+  float qv[NI * 16];
+  float qmax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2 * NI; ++j)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const uint16_t bits = static_cast<uint16_t>(raw[j][r / 2] >> (16 * (r % 2)));
+      const float x = hvalid ? bits16_to_f32<QBF16>(bits) : 0.f;
+      qv[j * 8 + r] = x;
+      qmax = fmaxf(qmax, fabsf(x));
+    }
+  qmax = col_max(qmax);
+  const int kq = qmax > 0.f ? 22 - __builtin_amdgcn_frexp_expf(qmax) : 0;
+  const float f = __builtin_amdgcn_ldexpf(1.0f, kq);
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t u[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        u[e] = static_cast<uint32_t>(static_cast<int>(rintf(qv[i * 16 + 4 * w + e] * f))) +
+               0x808080u;
+      // byte k of the four values into one word, offset removed (xor 0x80)
+      auto digit = [&u](uint32_t lo_sel, uint32_t hi_sel) {
+        return (__builtin_amdgcn_perm(u[1], u[0], lo_sel) |
+                __builtin_amdgcn_perm(u[3], u[2], hi_sel)) ^ 0x80808080u;
+      };
+      qp[i][0][w] = static_cast<int>(digit(0x0c0c0602u, 0x06020c0cu));  // a
+      qp[i][1][w] = static_cast<int>(digit(0x0c0c0501u, 0x05010c0cu));  // b
+      qp[i][2][w] = static_cast<int>(digit(0x0c0c0400u, 0x04000c0cu));  // c
+    }
+  return __builtin_amdgcn_ldexpf(a.scale_log2, -kq);
+}
+
 // ---------------------------------------------------------------------------
 // INT8 pages
 // ---------------------------------------------------------------------------
@@ -546,17 +597,40 @@ __device__ __forceinline__ void static_page_step(const Pg& pg, const h8_t* qf,
 // b's V those of columns 8-15, into one accumulator whose two column halves
 // share the running max and add up when the segment ends (fold_pair).
 // La, Lb: the pages' limits (a missing page gets its first token: masked).
+// QK of a page on the integer matrix cores: the codes as they were loaded
+// (K fragment i = the lane's 16 codes of chunk i) against the three q pieces,
+// three exact int32 sums per logit.
+template <int D, class Pg>
+__device__ __forceinline__ void int8_qk_int(const Pg& pg, const i4_t (*qp)[3], i4_t (&acc)[3]) {
+#pragma unroll
+  for (int p = 0; p < 3; ++p) acc[p] = i4_t{0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i)
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      acc[p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4_t, pg.k[i]), qp[i][p],
+                                                     acc[p], 0, 0, 0);
+}
+
 template <int D, bool Static, class Pg>
-__device__ __forceinline__ void int8_pair_step(const Pg& pa, const Pg& pb, const h8_t* qf,
+__device__ __forceinline__ void int8_pair_step(const Pg& pa, const Pg& pb, const i4_t (*qp)[3],
                                                float qscale, int tok_a, int La, int Lb,
                                                SoftmaxState<D / 16>& st) {
   constexpr int ND = D / 16;
   const bool hi = (threadIdx.x & 8) != 0;
-  const f4_t sa = int8_qk<D>(pa, qf);
-  const f4_t sb = int8_qk<D>(pb, qf);
+  i4_t ia[3], ib[3];
+  int8_qk_int<D>(pa, qp, ia);
+  int8_qk_int<D>(pb, qp, ib);
+  // the lane's page, then 2^16 A + 2^8 B + C (B and C combined exactly in
+  // int32, then one fp32 rounding each for the conversion and the fma)
   f4_t s;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) s[r] = hi ? sb[r] : sa[r];
+  for (int r = 0; r < 4; ++r) {
+    const int A = hi ? ib[0][r] : ia[0][r];
+    const int B = hi ? ib[1][r] : ia[1][r];
+    const int C = hi ? ib[2][r] : ia[2][r];
+    s[r] = fmaf(static_cast<float>(A), 65536.f, static_cast<float>(B * 256 + C));
+  }
   const bool tail = tok_a + 2 * kBlockSize > min(La, Lb);
   const int L = hi ? Lb : La;
   const int tok0 = tail ? lane_token(tok_a + (hi ? kBlockSize : 0)) : 0;
@@ -606,19 +680,21 @@ struct Int8Kind {
   static constexpr int kCodeBytes = 32 * D;            // a head's K and V codes
   static constexpr int kScaleBytes = Static ? 0 : 64;  // a head's scale records
   using Page = typename std::conditional<Static, StaticPage<D>, Int8Page<D>>::type;
-  h8_t qf[D / 32];
+  h8_t qf[D / 32];     // fp16 q fragments (one page per update)
+  i4_t qp[D / 64][3];  // integer q pieces (pair kinds)
   float qscale;
 
   // q of head i16 from the unit's rows in LDS ([G][D] 16-bit values)
   __device__ __forceinline__ void load_q(const DecodeArgs& a, const uint16_t* q_rows, int i16,
                                          int kb, bool hvalid) {
     const uint16_t* row = q_rows + (hvalid ? i16 : 0) * D;
-    qscale = load_q_scaled<D / 32, QBF16>(
-        a, hvalid,
-        [row, kb](int j) {
-          return *reinterpret_cast<const u4_t*>(row + 64 * (j / 2) + 16 * kb + 8 * (j % 2));
-        },
-        qf);
+    auto chunk = [row, kb](int j) {
+      return *reinterpret_cast<const u4_t*>(row + 64 * (j / 2) + 16 * kb + 8 * (j % 2));
+    };
+    if constexpr (Pair)
+      qscale = load_q_pieces<D / 64, QBF16>(a, hvalid, chunk, qp);
+    else
+      qscale = load_q_scaled<D / 32, QBF16>(a, hvalid, chunk, qf);
   }
   static __device__ __forceinline__ void load(Page& pg, HeadRef h, bool live, int i16, int kb) {
     if constexpr (Static)
@@ -637,7 +713,7 @@ struct Int8Kind {
   // two consecutive pages of one segment (pair kinds)
   __device__ __forceinline__ void step_pair(const Page& pa, const Page& pb, int tok_a, int La,
                                             int Lb, SoftmaxState<D / 16>& st) const {
-    int8_pair_step<D, Static>(pa, pb, qf, qscale, tok_a, La, Lb, st);
+    int8_pair_step<D, Static>(pa, pb, qp, qscale, tok_a, La, Lb, st);
   }
   // One page against the first nt of NT query tiles (tile c: q fragments
   // kd[c], state st[c], column limit Lc[c]), two tiles at a time: every K and
