@@ -332,13 +332,18 @@ def main():
                      "head_dim": pwl.head_dim, "dtype": pwl.kv_dtype}
             for key in ("int8", "fp16", "static"):
                 st = setup(pwl, key, None)
-                _, dms, _ = run(pwl, st, max(10, args.steps), args.warmup, "decode")
+                sms, dms, _ = run(pwl, st, max(10, args.steps), args.warmup, "decode")
                 b = decode_bytes(pwl, key)
+                # decode_us: one call between its own pair of events (a
+                # latency, with the events' own cost); step_us: calls back to
+                # back, host-timed between synchronizations like the headline
                 entry[key] = {
                     "decode_us": round(dms * 1e3, 2),
                     "tokens_per_s": round(pwl.num_seqs / (dms * 1e-3), 1),
                     "gbs": round(b / (dms * 1e-3) / 1e9, 1),
-                    "hbm_frac": round(b / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                    "hbm_frac": round(b / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "step_us": round(sms * 1e3, 2),
+                    "step_gbs": round(b / (sms * 1e-3) / 1e9, 1)}
                 del st
                 torch.cuda.empty_cache()
             entry["int8_over_fp16"] = round(entry["int8"]["tokens_per_s"] /

@@ -127,3 +127,16 @@ def test_pair_fused_append_static(P, g):
     _say(f"  max abs diff {d:.3e}")
     assert d <= MAX_ABS_TOL
     assert torch.equal(out, _gpu_static_decode(P, wl, pool, ks, vs))
+
+
+@pytest.mark.parametrize("fmt_name", ["int8", "static"])
+def test_pair_many_short_units_several_passes(P, fmt_name):
+    """2,000 sequences of 0 to 40 tokens (one to three pages, most counts odd):
+    a wave's run of about a dozen pages crosses many units, so a pass reaches
+    its segment limit and the wave takes several passes, each segment padded
+    to whole pairs."""
+    rng = np.random.default_rng(901)
+    lens = rng.integers(0, 41, 2000).tolist()
+    wl = _wl("pair-many", 902, lens, 4)
+    _say(f"pair decode {fmt_name}: 2,000 short sequences, {sum(lens)} tokens")
+    _check_decode(P, wl, fmt_name)
