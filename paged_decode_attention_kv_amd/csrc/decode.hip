@@ -642,16 +642,22 @@ __device__ __forceinline__ void int8_pair_step(const Pg& pa, const Pg& pb, const
         token_scales_w(hi ? pb.ks : pa.ks, hi ? pb.vs : pa.vs, tail, tok0, L);
     int8_probs<true>(s, ts, qscale, tail, tok0, L, st, ph, pl);
   }
-  const h4_t zero = {};
-  const h4_t pha = hi ? zero : ph, pla = hi ? zero : pl;
-  const h4_t phb = hi ? ph : zero, plb = hi ? pl : zero;
+  // PV over both pages in one 16x16x32 instruction per dim block and part:
+  // the lane's eight K-slots hold its four tokens of page a, then the same
+  // four of page b, in V and in P alike (P zero for the other page's half)
+  const u2_t z2 = {0u, 0u};
+  const u2_t ph2 = __builtin_bit_cast(u2_t, ph), pl2 = __builtin_bit_cast(u2_t, pl);
+  const u2_t pha = hi ? z2 : ph2, pla = hi ? z2 : pl2;
+  const u2_t phb = hi ? ph2 : z2, plb = hi ? pl2 : z2;
+  const h8_t p_hi = __builtin_bit_cast(h8_t, u4_t{pha.x, pha.y, phb.x, phb.y});
+  const h8_t p_lo = __builtin_bit_cast(h8_t, u4_t{pla.x, pla.y, plb.x, plb.y});
 #pragma unroll
   for (int k = 0; k < ND; ++k) {
-    const h4_t va = v_frag(pa, k), vb = v_frag(pb, k);
-    st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pha, st.acc[k], 0, 0, 0);
-    st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pla, st.acc[k], 0, 0, 0);
-    st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(vb, phb, st.acc[k], 0, 0, 0);
-    st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(vb, plb, st.acc[k], 0, 0, 0);
+    const u2_t va = __builtin_bit_cast(u2_t, v_frag(pa, k));
+    const u2_t vb = __builtin_bit_cast(u2_t, v_frag(pb, k));
+    const h8_t v8 = __builtin_bit_cast(h8_t, u4_t{va.x, va.y, vb.x, vb.y});
+    st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v8, p_hi, st.acc[k], 0, 0, 0);
+    st.acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(v8, p_lo, st.acc[k], 0, 0, 0);
   }
 }
 
