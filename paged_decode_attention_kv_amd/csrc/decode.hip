@@ -1277,7 +1277,13 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   int s_unit = 0, s_p = 0, s_start = 0, s_n = 0, s_L = 0, s_whole = 0, s_last = 0;
   int ns = 0, items = 0, real = 0;
   while (true) {
-    const int n = min(min(cu.np - cu.p, x1 - (x + real)), kMaxPagesPerWave - items);
+    // a segment is never cut by the end of a pass: its unit would come back
+    // in the next pass of this wave, whose partial takes the same slot. One
+    // that does not fit whole starts the next pass (the first one always
+    // fits: at most P <= kMaxPagesPerWave pages, padded to an even count)
+    const int want = min(cu.np - cu.p, x1 - (x + real));
+    if (ns > 0 && items + (kPair ? want + (want & 1) : want) > kMaxPagesPerWave) break;
+    const int n = min(want, kMaxPagesPerWave - items);
     const int u = cu.b * vh + cu.g;
     if (cu.p == 0 && lane == 0) {
       // this wave holds the unit's first item: record which waves cover it
