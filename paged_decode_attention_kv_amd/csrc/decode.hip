@@ -194,7 +194,7 @@ __device__ __forceinline__ float row_partner8(float x) {
 template <bool Pair = false, int ND>
 __device__ __forceinline__ void raise_max(SoftmaxState<ND>& st, float zmax) {
   zmax = col_max(zmax);
-  if constexpr (Pair) zmax = __builtin_amdgcn_fmed3f(zmax, row_partner8(zmax), INFINITY);
+  if constexpr (Pair) zmax = max_fin(zmax, row_partner8(zmax));
   if (__any(zmax > st.m + kTau)) {
     const float m_new = fmaxf(st.m, zmax);
     const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);  // 0 on the first token
@@ -256,14 +256,19 @@ __device__ __forceinline__ float load_q_scaled(const DecodeArgs& a, bool hvalid,
 // qi = rint(q * 2^kq) with max|qi| of the head in [2^21, 2^22], in base 256
 // with signed digits: qi = 2^16 a + 2^8 b + c (a, b, c in [-128, 127]; the
 // bytes of qi + 0x808080 are a + 128, b + 128, c + 128), digit p of chunk i
-// one byte per dim in qp[i][p]. The products with the codes and their sums
-// over the chunks are then exact in int32; rounding q costs at most 2^-22 of
-// the head's largest element per element. Returns the factor that turns
-// 2^16 A + 2^8 B + C into base-2 logits.
+// one byte per dim.
+// The lanes of MFMA columns 0-7 keep the digits in qa (page a of a pair) and
+// zeros in qb, those of columns 8-15 the reverse, so that one chain of matrix
+// instructions over both pages leaves page a's sums in columns 0-7 and page
+// b's in columns 8-15. Products and sums are exact in int32; rounding q costs
+// at most 2^-22 of the head's largest element per element. (Two digits, 2^-14
+// of the largest element, measured up to 0.2 off the exact attention on rows
+// whose q has outlier channels: the small elements keep too few bits.)
+// Returns the factor that turns 2^16 A + 2^8 B + C into base-2 logits.
 typedef int i4_t __attribute__((ext_vector_type(4)));
 template <int NI, bool QBF16, typename ChunkFn>
 __device__ __forceinline__ float load_q_pieces(const DecodeArgs& a, bool hvalid, ChunkFn chunk,
-                                               i4_t (*qp)[3]) {
+                                               i4_t (*qa)[3], i4_t (*qb)[3]) {
   u4_t raw[2 * NI];
 #pragma unroll
   for (int j = 0; j < 2 * NI; ++j) raw[j] = chunk(j);
@@ -281,6 +286,7 @@ __device__ __forceinline__ float load_q_pieces(const DecodeArgs& a, bool hvalid,
   qmax = col_max(qmax);
   const int kq = qmax > 0.f ? 22 - __builtin_amdgcn_frexp_expf(qmax) : 0;
   const float f = __builtin_amdgcn_ldexpf(1.0f, kq);
+  const bool hi = (lane_id() & 8) != 0;
 #pragma unroll
   for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -292,12 +298,18 @@ __device__ __forceinline__ float load_q_pieces(const DecodeArgs& a, bool hvalid,
                0x808080u;
       // byte k of the four values into one word, offset removed (xor 0x80)
       auto digit = [&u](uint32_t lo_sel, uint32_t hi_sel) {
-        return (__builtin_amdgcn_perm(u[1], u[0], lo_sel) |
-                __builtin_amdgcn_perm(u[3], u[2], hi_sel)) ^ 0x80808080u;
+        return static_cast<int>((__builtin_amdgcn_perm(u[1], u[0], lo_sel) |
+                                 __builtin_amdgcn_perm(u[3], u[2], hi_sel)) ^
+                                0x80808080u);
       };
-      qp[i][0][w] = static_cast<int>(digit(0x0c0c0602u, 0x06020c0cu));  // a
-      qp[i][1][w] = static_cast<int>(digit(0x0c0c0501u, 0x05010c0cu));  // b
-      qp[i][2][w] = static_cast<int>(digit(0x0c0c0400u, 0x04000c0cu));  // c
+      const int d[3] = {digit(0x0c0c0602u, 0x06020c0cu),   // a
+                        digit(0x0c0c0501u, 0x05010c0cu),   // b
+                        digit(0x0c0c0400u, 0x04000c0cu)};  // c
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        qa[i][p][w] = hi ? 0 : d[p];
+        qb[i][p][w] = hi ? d[p] : 0;
+      }
     }
   return __builtin_amdgcn_ldexpf(a.scale_log2, -kq);
 }
@@ -591,46 +603,51 @@ __device__ __forceinline__ void static_page_step(const Pg& pg, const h8_t* qf,
 // Two consecutive pages a, b of one segment against one query tile for a
 // group of at most 8 heads: the tile's 16 MFMA columns hold the heads twice,
 // columns 0-7 (lanes with i16 < 8) for page a and 8-15 for page b, so one
-// softmax update covers 32 tokens. QK runs per page with the same q
-// fragments and each lane keeps its page's logits; in PV, page a's V meets
+// softmax update covers 32 tokens. In QK, page a's codes meet q in columns
+// 0-7 only and page b's in columns 8-15 (zeros in the other half), so one
+// chain of matrix instructions leaves each lane its own page's logits; in
+// PV, page a's V meets
 // the probabilities of the columns 0-7 only (zeros in the others) and page
 // b's V those of columns 8-15, into one accumulator whose two column halves
 // share the running max and add up when the segment ends (fold_pair).
 // La, Lb: the pages' limits (a missing page gets its first token: masked).
-// QK of a page on the integer matrix cores: the codes as they were loaded
-// (K fragment i = the lane's 16 codes of chunk i) against the three q pieces,
-// three exact int32 sums per logit.
+// QK of a page pair on the integer matrix cores: the codes as they were
+// loaded (K fragment i = the lane's 16 codes of chunk i) against the three q
+// digits, page a's against qa and page b's against qb into the same three
+// exact int32 sums per logit.
 template <int D, class Pg>
-__device__ __forceinline__ void int8_qk_int(const Pg& pg, const i4_t (*qp)[3], i4_t (&acc)[3]) {
+__device__ __forceinline__ void int8_pair_qk(const Pg& pa, const Pg& pb, const i4_t (*qa)[3],
+                                             const i4_t (*qb)[3], i4_t (&acc)[3]) {
 #pragma unroll
   for (int p = 0; p < 3; ++p) acc[p] = i4_t{0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < D / 64; ++i)
 #pragma unroll
     for (int p = 0; p < 3; ++p)
-      acc[p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4_t, pg.k[i]), qp[i][p],
+      acc[p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4_t, pa.k[i]), qa[i][p],
+                                                     acc[p], 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i)
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      acc[p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i4_t, pb.k[i]), qb[i][p],
                                                      acc[p], 0, 0, 0);
 }
-
 template <int D, bool Static, class Pg>
-__device__ __forceinline__ void int8_pair_step(const Pg& pa, const Pg& pb, const i4_t (*qp)[3],
-                                               float qscale, int tok_a, int La, int Lb,
-                                               SoftmaxState<D / 16>& st) {
+__device__ __forceinline__ void int8_pair_step(const Pg& pa, const Pg& pb, const i4_t (*qa)[3],
+                                               const i4_t (*qb)[3], float qscale, int tok_a,
+                                               int La, int Lb, SoftmaxState<D / 16>& st) {
   constexpr int ND = D / 16;
   const bool hi = (threadIdx.x & 8) != 0;
-  i4_t ia[3], ib[3];
-  int8_qk_int<D>(pa, qp, ia);
-  int8_qk_int<D>(pb, qp, ib);
-  // the lane's page, then 2^16 A + 2^8 B + C (B and C combined exactly in
-  // int32, then one fp32 rounding each for the conversion and the fma)
+  i4_t acc[3];
+  int8_pair_qk<D>(pa, pb, qa, qb, acc);
+  // 2^16 A + 2^8 B + C (B and C combined exactly in int32, then one fp32
+  // rounding each for the conversion and the fma)
   f4_t s;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int A = hi ? ib[0][r] : ia[0][r];
-    const int B = hi ? ib[1][r] : ia[1][r];
-    const int C = hi ? ib[2][r] : ia[2][r];
-    s[r] = fmaf(static_cast<float>(A), 65536.f, static_cast<float>(B * 256 + C));
-  }
+  for (int r = 0; r < 4; ++r)
+    s[r] = fmaf(static_cast<float>(acc[0][r]), 65536.f,
+                static_cast<float>(acc[1][r] * 256 + acc[2][r]));
   const bool tail = tok_a + 2 * kBlockSize > min(La, Lb);
   const int L = hi ? Lb : La;
   const int tok0 = tail ? lane_token(tok_a + (hi ? kBlockSize : 0)) : 0;
@@ -686,8 +703,8 @@ struct Int8Kind {
   static constexpr int kCodeBytes = 32 * D;            // a head's K and V codes
   static constexpr int kScaleBytes = Static ? 0 : 64;  // a head's scale records
   using Page = typename std::conditional<Static, StaticPage<D>, Int8Page<D>>::type;
-  h8_t qf[D / 32];     // fp16 q fragments (one page per update)
-  i4_t qp[D / 64][3];  // integer q pieces (pair kinds)
+  h8_t qf[D / 32];                   // fp16 q fragments (one page per update)
+  i4_t qa[D / 64][3], qb[D / 64][3];  // integer q digits for pages a, b (pair kinds)
   float qscale;
 
   // q of head i16 from the unit's rows in LDS ([G][D] 16-bit values)
@@ -698,7 +715,7 @@ struct Int8Kind {
       return *reinterpret_cast<const u4_t*>(row + 64 * (j / 2) + 16 * kb + 8 * (j % 2));
     };
     if constexpr (Pair)
-      qscale = load_q_pieces<D / 64, QBF16>(a, hvalid, chunk, qp);
+      qscale = load_q_pieces<D / 64, QBF16>(a, hvalid, chunk, qa, qb);
     else
       qscale = load_q_scaled<D / 32, QBF16>(a, hvalid, chunk, qf);
   }
@@ -719,7 +736,7 @@ struct Int8Kind {
   // two consecutive pages of one segment (pair kinds)
   __device__ __forceinline__ void step_pair(const Page& pa, const Page& pb, int tok_a, int La,
                                             int Lb, SoftmaxState<D / 16>& st) const {
-    int8_pair_step<D, Static>(pa, pb, qp, qscale, tok_a, La, Lb, st);
+    int8_pair_step<D, Static>(pa, pb, qa, qb, qscale, tok_a, La, Lb, st);
   }
   // One page against the first nt of NT query tiles (tile c: q fragments
   // kd[c], state st[c], column limit Lc[c]), two tiles at a time: every K and

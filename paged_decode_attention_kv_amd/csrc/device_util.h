@@ -85,14 +85,22 @@ __device__ __forceinline__ float wave_sum(float x) {
 // 16-lane rows, pairs every lane with its partner.
 __device__ __forceinline__ float max_nc(float a, float b) { return a > b ? a : b; }
 
-// (col_max takes the larger of two with one median-of-three against +inf)
+// The larger of two values that are at most the largest finite float (-inf
+// included), as one median-of-three against that bound. (Against +inf the
+// compiler turns the median into a maximum and first quiets both operands,
+// two more instructions, as the operands of a lane swap are not known to be
+// canonical.)
+constexpr float kMaxFinite = 3.40282347e38f;
+__device__ __forceinline__ float max_fin(float a, float b) {
+  return __builtin_amdgcn_fmed3f(a, b, kMaxFinite);
+}
 __device__ __forceinline__ float col_max(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  x = __builtin_amdgcn_fmed3f(__uint_as_float(h[0]), __uint_as_float(h[1]), INFINITY);
+  x = max_fin(__uint_as_float(h[0]), __uint_as_float(h[1]));
   const uint32_t v = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return __builtin_amdgcn_fmed3f(__uint_as_float(r[0]), __uint_as_float(r[1]), INFINITY);
+  return max_fin(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float col_sum(float x) {
   const uint32_t u = __float_as_uint(x);

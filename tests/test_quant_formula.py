@@ -7,7 +7,11 @@ and scales (quant_write.hip), against IEEE binary32 division:
   within one ulp; all FP16 and BF16 maxima for the scale step;
 * static-scale format (tests/native/static_formula.c): every FP16 and BF16
   input, infinities and NaNs included, against powers of two, all-ones
-  significands and seeded random scales across the writer's window.
+  significands and seeded random scales across the writer's window;
+* integer q of the page-pair decode kernels (tests/native/q_digits.c, for
+  decode.hip's load_q_pieces): the power-of-two scaling bound for every FP16
+  and BF16 head maximum, the three signed base-256 digits of every scaled value
+  as the kernel's byte permutes extract them, and int32 room for the sums.
 
 The kernels' own results are compared with the oracle by the GPU tests; these
 pin the argument that makes them equal for inputs the GPU tests cannot
@@ -78,3 +82,15 @@ def test_static_division_free_codes(static_checker, fmt, seed):
     print(r.stdout)
     assert r.returncode == 0, r.stdout + r.stderr
     assert r.stdout.strip().endswith(", 0 mismatches")
+
+
+@pytest.fixture(scope="module")
+def digit_checker(tmp_path_factory):
+    return _compile(tmp_path_factory, "q_digits")
+
+
+def test_pair_kernel_q_digits(digit_checker):
+    r = subprocess.run([digit_checker], capture_output=True, text=True, timeout=120)
+    print(r.stdout)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.strip() == "checked 33618818, failed 0"
