@@ -480,15 +480,17 @@ template <bool Pair = false, int ND>
 __device__ __forceinline__ void int8_probs(const f4_t& s, const TokenScales& ts, float qscale,
                                            bool tail, int tok0, int Lc, SoftmaxState<ND>& st,
                                            h4_t& ph, h4_t& pl) {
-  // (the fp16 scale factors enter as mixed-precision fma operands, and the
-  // mask is one compare against the lane's count of attendable tokens)
-  const int lim = tail ? Lc - tok0 : 4;
+  // (the fp16 scale factors enter as mixed-precision fma operands; only a
+  // tail page pays the mask, one compare per logit against the lane's count
+  // of attendable tokens)
   float z[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float zj =
-        fmaf(s[j] * qscale, static_cast<float>(ts.sk[j]), static_cast<float>(ts.e[j]));
-    z[j] = j < lim ? zj : -INFINITY;
+  for (int j = 0; j < 4; ++j)
+    z[j] = fmaf(s[j] * qscale, static_cast<float>(ts.sk[j]), static_cast<float>(ts.e[j]));
+  if (tail) {
+    const int lim = Lc - tok0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z[j] = j < lim ? z[j] : -INFINITY;
   }
   raise_max<Pair>(st, fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
   float x[4], p[4];
@@ -567,10 +569,14 @@ __device__ __forceinline__ void load_static_page(StaticPage<D>& pg, HeadRef h, b
 template <bool Pair = false, int ND>
 __device__ __forceinline__ void static_probs(const f4_t& s, float qscale, bool tail, int tok0,
                                              int Lc, SoftmaxState<ND>& st, h4_t& ph, h4_t& pl) {
-  const int lim = tail ? Lc - tok0 : 4;  // the lane's attendable tokens
   float z[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) z[j] = j < lim ? s[j] * qscale : -INFINITY;
+  for (int j = 0; j < 4; ++j) z[j] = s[j] * qscale;
+  if (tail) {
+    const int lim = Lc - tok0;  // the lane's attendable tokens
+#pragma unroll
+    for (int j = 0; j < 4; ++j) z[j] = j < lim ? z[j] : -INFINITY;
+  }
   raise_max<Pair>(st, fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
   float x[4];
 #pragma unroll
@@ -648,7 +654,8 @@ __device__ __forceinline__ void int8_pair_step(const Pg& pa, const Pg& pb, const
   for (int r = 0; r < 4; ++r)
     s[r] = fmaf(static_cast<float>(acc[0][r]), 65536.f,
                 static_cast<float>(acc[1][r] * 256 + acc[2][r]));
-  const bool tail = tok_a + 2 * kBlockSize > min(La, Lb);
+  // (wave-uniform: a scalar branch)
+  const bool tail = __builtin_amdgcn_readfirstlane(tok_a + 2 * kBlockSize > min(La, Lb));
   const int L = hi ? Lb : La;
   const int tok0 = tail ? lane_token(tok_a + (hi ? kBlockSize : 0)) : 0;
   h4_t ph, pl;
