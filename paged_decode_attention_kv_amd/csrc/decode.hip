@@ -14,7 +14,7 @@
 // The work of one call is the list of (sequence, KV head, page) items, in
 // that order: KV head g of sequence b owns the items of its pages
 // 0..ceil(L_b/16)-1 (a "unit"). Every wave of the grid takes an equal,
-// contiguous run of P items (P = max(4, ceil(total / waves))), so all waves
+// contiguous run of P items (P = max(2, ceil(total / waves))), so all waves
 // stream the same number of pages whatever the spread of context lengths, and
 // they run independently (LDS is private to each wave; no barrier). Each wave
 // derives the total and its start from the context lengths itself (a prefix

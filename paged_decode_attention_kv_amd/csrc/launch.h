@@ -14,7 +14,7 @@ namespace pdakv {
 constexpr int kBlockSize = 16;        // tokens per page
 constexpr int kMaxGroup = 16;         // query heads per KV head (one MFMA N tile)
 constexpr int kWaves = 4;             // waves per decode workgroup
-constexpr int kMinPagesPerWave = 4;   // decode: fewest pages a busy wave gets
+constexpr int kMinPagesPerWave = 2;   // decode: fewest pages a busy wave gets (one pair)
 constexpr int kInt8WavesPerSimd = 2;  // INT8 decode occupancy
 constexpr int kInt8PageGroup = 2;     // pages per register buffer
 constexpr int k16WavesPerSimd = 2;    // 16-bit decode occupancy

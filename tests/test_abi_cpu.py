@@ -109,6 +109,9 @@ def test_page_bytes_agree_with_oracle(P):
                 assert P.pdakv_page_bytes(fmt, 16, hkv, d) == oracle.page_bytes(fmt, 16, hkv, d)
 
 
+MIN_PPW = 2  # fewest pages a decode wave is given (one page pair)
+
+
 @pytest.mark.parametrize("B,hkv,L", [(1, 8, 256), (1, 8, 2048), (64, 8, 8193), (8, 8, 32768),
                                      (32, 2, 4104), (8, 8, 8192), (3, 1, 0), (1, 32, 1),
                                      (256, 8, 131072)])
@@ -118,11 +121,11 @@ def test_decode_plan_is_consistent(P, B, hkv, L):
     for fmt in (P.KV_INT8_SYM, P.KV_16BIT, P.KV_INT8_STATIC):
         waves, ppw = P.pdakv_decode_plan(fmt, B, hkv, L)
         assert waves >= 4 and waves % 4 == 0
-        assert 4 <= ppw <= 128 and ppw == max(4, -(-items // waves))
+        assert MIN_PPW <= ppw <= 128 and ppw == max(MIN_PPW, -(-items // waves))
         # one resident round unless the items need more than 128 per wave;
-        # never more waves than 4-page shares (rounded to whole workgroups)
+        # never more waves than MIN_PPW-page shares (rounded to whole workgroups)
         assert waves <= max(4, -(-max(resident[fmt], -(-items // 128)) // 4) * 4)
-        assert waves <= max(4, -(-(-(-items // 4)) // 4) * 4)
+        assert waves <= max(4, -(-(-(-items // MIN_PPW)) // 4) * 4)
 
 
 @pytest.mark.parametrize("B,hkv,L", [(1, 8, 2048), (64, 8, 8193), (8, 8, 32768), (3, 1, 1),
@@ -292,10 +295,10 @@ def test_multi_validation(P, fn, change, status):
 
 def _plan_waves(waves_per_simd, B, heads, L):
     """The decode grid's wave count (256 CUs x 4 SIMDs resident per wave per
-    SIMD; at most 128 and at least 4 items per wave; a multiple of 4)."""
+    SIMD; at most 128 and at least MIN_PPW items per wave; a multiple of 4)."""
     items = B * heads * -(-L // 16)
     v = max(256 * 4 * waves_per_simd, -(-items // 128))
-    v = max(min(v, -(-items // 4)), 1)
+    v = max(min(v, -(-items // MIN_PPW)), 1)
     return -(-v // 4) * 4
 
 
