@@ -49,6 +49,14 @@
 //    P = 2^(s + e - m) * f never leave the fp16 range whatever the scales.
 //    With static scales the K scale is part of the logit factor and the V
 //    scale multiplies the output.
+//  * Page pairs (one-token calls, groups of at most 8 heads, head size 128):
+//    the 16 columns hold the group twice, columns 0-7 for the first page of
+//    a pair and 8-15 for the second, so one softmax update covers 32 tokens.
+//    QK runs on the integer matrix instructions with the codes as loaded and
+//    q in three signed base-256 digits (exact int32 sums), each page meeting
+//    q in its own half of the columns; PV takes both pages in one 16x16x32
+//    instruction per dimension block and part, and the two column halves
+//    are added when the segment ends.
 // A segment that covers a whole unit writes the output rows directly;
 // otherwise it writes a partial (max, sum, accumulator) into the slot
 // wave + unit (unique: along the item order both indexes only grow and one of
