@@ -151,7 +151,7 @@ int pdakv_capabilities(uint32_t* flags_out);
 /* Launch plan of the decode calls for these sizes. The work of a call is the
  * list of (sequence, KV head, page) items; the kernel splits the items of
  * the actual context lengths evenly over *num_waves 64-lane waves (at least
- * 4 items each, a unit that spans several waves is merged afterwards).
+ * 2 items each, a unit that spans several waves is merged afterwards).
  * *max_pages_per_wave is the share when every sequence is at
  * max_context_len (<= 128). kv_format is one of the PDAKV_KV_* formats.
  * Either output pointer may be NULL. Returns
