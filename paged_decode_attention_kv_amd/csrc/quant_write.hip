@@ -226,13 +226,17 @@ __device__ __forceinline__ uint64_t codes_token(const u4_t& w, float s, float re
 // [2^-64, 2^64] and r = fl(1/s), equal to clamp(rint(fl32(x / s)), -127,
 // 127) without a division: q0 = x r is within an ulp of x / s, the residual
 // x - q0 s is exact in an fma, and q0 + residual * r rounds to fl32(x / s)
-// (Markstein's theorem for a correctly rounded reciprocal; also checked
-// against IEEE division for every FP16 and BF16 x over scales across the
-// window). Values are first clamped to +-128 s, which keeps every finite
-// value's code and keeps x r finite: an infinity then saturates to +-127 as
-// the division would, and a NaN (which the clamp turns into -128 s) gives
-// -127, the code the division-based rule gives it too. The clamped quotient
-// plus 1.5 * 2^23 rounds to nearest even, and its low byte is the code.
+// (Markstein's theorem for a correctly rounded reciprocal). q0 is first
+// clamped to +-128 (one median of three): inside the range nothing changes,
+// beyond it q1 stays at or past +-128 and saturates to +-127 as the division
+// does, an infinity (x r infinite, or a finite bf16 x whose x r overflows)
+// gives +-127, and a NaN gives -127, the code the division-based rule gives
+// it too (the hardware's median of three takes the smaller bound for a quiet
+// NaN; the product and the fmas quiet any NaN). The clamped quotient plus
+// 1.5 * 2^23 rounds to nearest even, and its low byte is the code. (Checked
+// against IEEE division for every FP16 and BF16 x, infinities and NaNs
+// included, over scales across the window. FP16 values enter the products
+// as mixed-precision operands, without a conversion of their own.)
 __host__ __device__ __forceinline__ bool static_window(float s) {
   return s >= 0x1p-64f && s <= 0x1p64f;
 }
@@ -240,15 +244,13 @@ __host__ __device__ __forceinline__ bool static_window(float s) {
 template <bool BF16>
 __device__ __forceinline__ uint64_t codes_static(const u4_t& w, float s, float r) {
   constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
-  const float lim = 128.0f * s;
   uint32_t f[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    float x = bits16_to_f32<BF16>(static_cast<uint16_t>(w[e / 2] >> (16 * (e % 2))));
-    x = fminf(fmaxf(x, -lim), lim);
-    const float q0 = fmaf(x, r, 0.0f);
+    const float x = bits16_to_f32<BF16>(static_cast<uint16_t>(w[e / 2] >> (16 * (e % 2))));
+    const float q0 = __builtin_amdgcn_fmed3f(fmaf(x, r, 0.0f), -128.0f, 128.0f);
     const float q1 = fmaf(fmaf(-q0, s, x), r, q0);
-    f[e] = __float_as_uint(fminf(fmaxf(q1, -127.0f), 127.0f) + kMagic);
+    f[e] = __float_as_uint(__builtin_amdgcn_fmed3f(q1, -127.0f, 127.0f) + kMagic);
   }
   auto pack = [](uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     return __builtin_amdgcn_perm(b, a, 0x0c0c0400u) | __builtin_amdgcn_perm(d, c, 0x04000c0cu);
