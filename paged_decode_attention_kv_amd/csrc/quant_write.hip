@@ -185,34 +185,28 @@ __device__ __forceinline__ bool row_scale_token(float a, uint16_t& bits) {
 // Codes of the eight FP16 or BF16 values in w for a per-token scale s (an
 // FP16 value with |x| <= 127 s), equal to clamp(rint(fl32(x / s)), -127, 127)
 // but without a division; recip = the hardware reciprocal of s (within one
-// ulp), kinf = recip * (1 + 2^-15). Why these are the same codes:
+// ulp). Why these are the same codes:
 // * q = x / s is a ratio of two integers of at most 11 bits times a power of
-//   two, so it is exactly a half-integer (a tie) or at least 2^-13 away from
-//   every half-integer; |q| <= 127, so no clamp is needed.
-// * t = fma(x, recip, 1.5 * 2^23) rounds x * recip (within 127.5 * 2^-23 of
-//   q) to an integer c held in t's low mantissa bits: c = rint(q) except at
-//   ties, where it is one of the two neighbours.
-// * e = x - c s is exact in an fma, and e * kinf lies strictly inside
-//   (-0.5, 0.5) unless q is a tie, where it is just beyond +-0.5; clamped to
-//   [-0.5, 0.5] it is q - c at a tie and below 0.5 in magnitude otherwise.
-// * t + that rounds to nearest even at the integer spacing of t: c, or at a
-//   tie the even one of c and c +- 1 (t's parity is c's, 1.5 * 2^23 being
-//   even). The low byte of its bits is then the two's-complement code.
+//   two, so fl32(q) is q itself or q lies at least about 2^-36 |q| away from
+//   every rounding boundary of fp32; |q| <= 127, so no clamp is needed.
+// * q0 = x * recip is within a few ulps of q, so e = x - q0 s is exact in an
+//   fma and q0 + e * recip (one more fma) is within about 2^-45 |q| of q:
+//   rounded once, it is fl32(q) (one Markstein step).
+// * fl32(q) + 1.5 * 2^23 rounds to the nearest integer, ties to even, as
+//   rint does; the low byte of its bits is the two's-complement code.
 // (Checked against IEEE division for every FP16 and BF16 x and FP16 s, with
-// the reciprocal anywhere within one ulp.)
+// the reciprocal anywhere within one ulp; four VALU instructions per
+// element, x entering the two fmas that read it as an FP16 operand.)
 template <bool BF16>
-__device__ __forceinline__ uint64_t codes_token(const u4_t& w, float s, float recip,
-                                                float kinf) {
+__device__ __forceinline__ uint64_t codes_token(const u4_t& w, float s, float recip) {
   constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
   uint32_t f[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float x = bits16_to_f32<BF16>(static_cast<uint16_t>(w[e / 2] >> (16 * (e % 2))));
-    const float t = fmaf(x, recip, kMagic);
-    const float c = t - kMagic;
-    const float err = fmaf(-c, s, x);
-    const float tie = fminf(fmaxf(err * kinf, -0.5f), 0.5f);
-    f[e] = __float_as_uint(t + tie);
+    const float q0 = fmaf(x, recip, 0.0f);
+    const float q1 = fmaf(fmaf(-q0, s, x), recip, q0);
+    f[e] = __float_as_uint(q1 + kMagic);
   }
   // low bytes of f[0..3] and f[4..7] into two words (byte-select 0x0c: zero)
   auto pack = [](uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
@@ -420,11 +414,10 @@ __device__ __forceinline__ void write_quad(const WriteArgs& a, const Quad& q,
     }
     const float sk = f16_bits_to_f32(skb), sv = f16_bits_to_f32(svb);
     const float rk = __builtin_amdgcn_rcpf(sk), rv = __builtin_amdgcn_rcpf(sv);
-    constexpr float kInflate = 1.000030517578125f;  // 1 + 2^-15
 #pragma unroll
     for (int c = 0; c < NV; ++c) {
-      kc[c] = codes_token<BF16>(in.k[c], sk, rk, rk * kInflate);
-      vc[c] = codes_token<BF16>(in.v[c], sv, rv, rv * kInflate);
+      kc[c] = codes_token<BF16>(in.k[c], sk, rk);
+      vc[c] = codes_token<BF16>(in.v[c], sv, rv);
     }
   } else if constexpr (F == kInt8Static) {
     // (scales inside [2^-64, 2^64]; the reciprocals are fl(1/s), from the host)

@@ -4,10 +4,10 @@
  *    a), fl(1/127), q0) for every finite FP16 and BF16 magnitude a;
  *  - the code step: for FP16 scales s (every `stride`-th positive finite
  *    pattern, starting at `first`), every FP16 or BF16 x with |x| <= 127 s
- *    and a reciprocal anywhere within one ulp of 1/s:
- *      t = fma(x, r, 1.5 * 2^23); c = t - 1.5 * 2^23; e = fma(-c, s, x);
- *      w = clamp(e * fl(r * (1 + 2^-15)), -0.5, 0.5)
- *    the low byte of the bits of t + w is clamp(rint(x / s), -127, 127).
+ *    and a reciprocal r anywhere within one ulp of 1/s:
+ *      q0 = fl(x r); q1 = fma(fma(-q0, s, x), r, q0)
+ *    the low byte of the bits of q1 + 1.5 * 2^23 is
+ *    clamp(rint(fl32(x / s)), -127, 127).
  * Usage: quant_formula f16|bf16 stride first. Prints the counts; exit
  * status 1 on any mismatch. Built with -ffp-contract=off so that every
  * product and sum rounds where it is written. */
@@ -71,13 +71,11 @@ int main(int argc, char** argv) {
       const float q = fminf(fmaxf(rintf(x / s), -127.0f), 127.0f);
       const uint8_t want = (uint8_t)(int8_t)q;
       for (int k = 0; k < 3; ++k) {
-        const float r = rs[k], rinf = r * 1.000030517578125f;
-        const float t = fmaf(x, r, magic);
-        const float c = t - magic;
-        const float e = fmaf(-c, s, x);
-        const float w = fminf(fmaxf(e * rinf, -0.5f), 0.5f);
+        const float r = rs[k];
+        const float q0 = x * r;
+        const float q1 = fmaf(fmaf(-q0, s, x), r, q0);
         ++codes;
-        if ((uint8_t)(bits_of(t + w) & 0xff) != want) ++cbad;
+        if ((uint8_t)(bits_of(q1 + magic) & 0xff) != want) ++cbad;
       }
     }
   }
