@@ -79,10 +79,6 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Max / sum over the four lanes l, l^16, l^32, l^48 (same column of a 16x16
-// MFMA tile), with the gfx950 row-swap instructions (VALU only, no LDS round
-// trip): swapping a value with itself across 32-lane halves, then across
-// 16-lane rows, pairs every lane with its partner.
 __device__ __forceinline__ float max_nc(float a, float b) { return a > b ? a : b; }
 
 // The larger of two values that are at most the largest finite float (-inf
@@ -94,6 +90,11 @@ constexpr float kMaxFinite = 3.40282347e38f;
 __device__ __forceinline__ float max_fin(float a, float b) {
   return __builtin_amdgcn_fmed3f(a, b, kMaxFinite);
 }
+
+// Max / sum over the four lanes l, l^16, l^32, l^48 (same column of a 16x16
+// MFMA tile), with the gfx950 row-swap instructions (VALU only, no LDS round
+// trip): swapping a value with itself across 32-lane halves, then across
+// 16-lane rows, pairs every lane with its partner.
 __device__ __forceinline__ float col_max(float x) {
   const uint32_t u = __float_as_uint(x);
   const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
