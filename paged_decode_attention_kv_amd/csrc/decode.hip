@@ -704,6 +704,27 @@ __device__ __forceinline__ void fold_pair(SoftmaxState<ND>& st) {
   st.l += row_partner8(st.l);
 }
 
+// Fused append: the lane's D / 64 elements (dims lane * D / 64 + e) of the
+// newest token's K and V rows of sequence b, KV head g (16-bit patterns).
+template <int D>
+struct NewRows {
+  uint16_t k[D / 64], v[D / 64];
+};
+template <int D>
+__device__ __forceinline__ NewRows<D> load_new_rows(const DecodeArgs& a, int b, int g, int lane) {
+  constexpr int EPL = D / 64;
+  const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
+  const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
+  NewRows<D> r;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int64_t d = lane * EPL + e;
+    r.k[e] = kn[b * a.kn_st + g * a.kn_sh + d * a.kn_sd];
+    r.v[e] = vn[b * a.vn_st + g * a.vn_sh + d * a.vn_sd];
+  }
+  return r;
+}
+
 // The INT8 page formats as seen by the decode loop: per-token FP16 scales in
 // the page, or (Static) codes only with the layer's two scalar scales.
 template <int D_, bool QBF16, int G_ = 1, bool Static = false, bool Pair = false>
@@ -817,30 +838,26 @@ struct Int8Kind {
     return 64 * (k / 4) + 16 * kb + 4 * j + (k % 4);
   }
 
-  // Fused append, first half: quantize the newest token's K and V rows of
-  // (b, g) with the quantize-on-write rule into nt ([D] K codes, [D] V codes,
-  // K scale, V scale) for patch() and store_new(). False when a scale would
-  // exceed FP16 or a row holds a NaN or an infinity (flagged; the slot is
-  // then left as it was, as the separate write leaves it).
-  static __device__ __forceinline__ bool prepare_new(const DecodeArgs& a, int b, int g,
-                                                     uint8_t* nt, int lane) {
+  // Fused append, first half: quantize the newest token's K and V rows
+  // (the lane's elements r, loaded by load_new_rows) with the
+  // quantize-on-write rule into nt ([D] K codes, [D] V codes, K scale, V
+  // scale) for patch() and store_new(). False when a scale would exceed FP16
+  // or a row holds a NaN or an infinity (flagged; the slot is then left as it
+  // was, as the separate write leaves it).
+  static __device__ __forceinline__ bool quant_new(const DecodeArgs& a, const NewRows<D>& r,
+                                                   uint8_t* nt, int lane) {
     constexpr int EPL = D / 64;
     float xk[EPL], xv[EPL];
     // row maxima as 16-bit magnitude patterns (sign bit cleared): FP16 and
     // BF16 magnitudes order like unsigned integers, with a NaN above the
     // infinity, so a NaN or an infinity reaches the scale check
     uint32_t mk = 0, mv = 0;
-    const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
-    const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      const int64_t d = lane * EPL + e;
-      const uint16_t kbits = kn[b * a.kn_st + g * a.kn_sh + d * a.kn_sd];
-      const uint16_t vbits = vn[b * a.vn_st + g * a.vn_sh + d * a.vn_sd];
-      xk[e] = bits16_to_f32<QBF16>(kbits);
-      xv[e] = bits16_to_f32<QBF16>(vbits);
-      mk = max(mk, static_cast<uint32_t>(kbits & 0x7FFFu));
-      mv = max(mv, static_cast<uint32_t>(vbits & 0x7FFFu));
+      xk[e] = bits16_to_f32<QBF16>(r.k[e]);
+      xv[e] = bits16_to_f32<QBF16>(r.v[e]);
+      mk = max(mk, static_cast<uint32_t>(r.k[e] & 0x7FFFu));
+      mv = max(mv, static_cast<uint32_t>(r.v[e] & 0x7FFFu));
     }
     if constexpr (Static) {
       // the layer's scales: nothing can overflow
@@ -872,6 +889,10 @@ struct Int8Kind {
       *reinterpret_cast<uint16_t*>(nt + 2 * D + 2) = svb;
     }
     return true;
+  }
+  static __device__ __forceinline__ bool prepare_new(const DecodeArgs& a, int b, int g,
+                                                     uint8_t* nt, int lane) {
+    return quant_new(a, load_new_rows<D>(a, b, g, lane), nt, lane);
   }
 
   // Fused append, second half (after the page loop): store the token from nt
@@ -1102,21 +1123,24 @@ struct F16Kind {
     return 32 * (k / 2) + 8 * kb + 2 * j + (k % 2);
   }
 
-  // Fused append, first half: the newest token's K and V rows of (b, g)
-  // into nt ([D] K, [D] V, 16-bit) for patch() and store_new().
-  static __device__ __forceinline__ bool prepare_new(const DecodeArgs& a, int b, int g,
-                                                     uint8_t* nt, int lane) {
+  // Fused append, first half: the newest token's K and V rows (the lane's
+  // elements r, loaded by load_new_rows) into nt ([D] K, [D] V, 16-bit) for
+  // patch() and store_new().
+  static __device__ __forceinline__ bool quant_new(const DecodeArgs&, const NewRows<D>& r,
+                                                   uint8_t* nt, int lane) {
     constexpr int EPL = D / 64;
-    const uint16_t* kn = static_cast<const uint16_t*>(a.k_new);
-    const uint16_t* vn = static_cast<const uint16_t*>(a.v_new);
     uint16_t* nt16 = reinterpret_cast<uint16_t*>(nt);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      const int64_t d = lane * EPL + e;
-      nt16[d] = kn[b * a.kn_st + g * a.kn_sh + d * a.kn_sd];
-      nt16[D + d] = vn[b * a.vn_st + g * a.vn_sh + d * a.vn_sd];
+      const int d = lane * EPL + e;
+      nt16[d] = r.k[e];
+      nt16[D + d] = r.v[e];
     }
     return true;
+  }
+  static __device__ __forceinline__ bool prepare_new(const DecodeArgs& a, int b, int g,
+                                                     uint8_t* nt, int lane) {
+    return quant_new(a, load_new_rows<D>(a, b, g, lane), nt, lane);
   }
 
   // Fused append, second half (after the page loop): store the token from nt
@@ -1475,18 +1499,37 @@ __device__ __forceinline__ int run_pass(const DecodeArgs& a, K& kind, Cursor& cu
   // patches it into the page as loaded and stores it into the page (nobody
   // else reads that slot during the call)
   // (its stores wait until after the page loop, so that the loop's waits
-  // count page loads only)
+  // count page loads only). The first such unit's new rows are requested
+  // before q is read from LDS and quantized after, so that their round trip
+  // overlaps q's preparation instead of delaying it (one-token calls: c_n is
+  // the group, whatever the segment).
+  NewRows<D> first_rows{};
+  int first_end = -1;
+  if (!Multi && a.append) {
+    const uint64_t ends = __ballot(lane < ns && s_last != 0);
+    if (ends) {
+      first_end = __builtin_ctzll(ends);
+      const int u = readlane(s_unit, first_end);
+      first_rows = load_new_rows<D>(a, u / hkv, u % hkv, lane);
+    }
+    // (a compiler barrier: keeps these loads here rather than next to their
+    // use; it waits for nothing)
+    asm volatile("" ::: "memory");
+  }
+  if constexpr (!Multi) kind.load_q(a, lds.q, K::col_head(i16), kb, K::col_head(i16) < c_n);
   if (!Multi && a.append) {
     for (int s = 0; s < ns; ++s) {
       if (!readlane(s_last, s)) continue;
       const int u = readlane(s_unit, s);
-      const bool ok = K::prepare_new(a, u / hkv, u % hkv, lds.nt + s * new_token_bytes(D), lane);
+      uint8_t* nt = lds.nt + s * new_token_bytes(D);
+      const bool ok = s == first_end ? K::quant_new(a, first_rows, nt, lane)
+                                     : K::prepare_new(a, u / hkv, u % hkv, nt, lane);
       if (lane == s) s_patch = ok;
     }
   }
   enter(0);
   softmax_init(st);
-  kind.load_q(a, lds.q, K::col_head(i16), kb, K::col_head(i16) < c_n);
+  if constexpr (Multi) kind.load_q(a, lds.q, K::col_head(i16), kb, K::col_head(i16) < c_n);
   for (int i = 0;; i += 2 * G) {
     if (!consume(ga, ba, i)) break;
     __builtin_amdgcn_sched_barrier(0);

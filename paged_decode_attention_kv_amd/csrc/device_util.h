@@ -67,10 +67,24 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Maximum over the 64 lanes, in every lane, on the VALU alone: rotations by
+// 8, 4, 2 and 1 lanes inside each row of 16 (DPP), then the row-swap
+// instructions across rows and across the two halves (a lane shuffle would
+// take six round trips through LDS).
+template <int Ctrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), Ctrl, 0xF, 0xF, false));
+}
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), o)));
-  return x;
+  x = max(x, dpp_u32<0x128>(x));  // row_ror:8
+  x = max(x, dpp_u32<0x124>(x));  // row_ror:4
+  x = max(x, dpp_u32<0x122>(x));  // row_ror:2
+  x = max(x, dpp_u32<0x121>(x));  // row_ror:1
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = max(r[0], r[1]);
+  const auto h = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max(h[0], h[1]);
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
