@@ -313,7 +313,7 @@ def main():
         del st
         torch.cuda.empty_cache()
     waves, ppw = P.pdakv_decode_plan(P.KV_INT8_SYM, wl.num_seqs, wl.num_kv_heads,
-                                     wl.max_context_len)
+                                     wl.head_dim, wl.max_context_len)
     i8 = res["int8"]
     dec_b = decode_bytes(wl, "int8")
     call_b = dec_b + append_bytes(wl, "int8")

@@ -148,24 +148,29 @@ size_t pdakv_page_bytes(int kv_format, int block_size, int num_kv_heads, int hea
  * device, PDAKV_ERR_INVALID_ARG for a NULL flags_out. */
 int pdakv_capabilities(uint32_t* flags_out);
 
-/* Launch plan of the decode calls for these sizes. The work of a call is the
- * list of (sequence, KV head, page) items; the kernel splits the items of
- * the actual context lengths evenly over *num_waves 64-lane waves (at least
- * 2 items each, a unit that spans several waves is merged afterwards).
- * *max_pages_per_wave is the share when every sequence is at
- * max_context_len (<= 128). kv_format is one of the PDAKV_KV_* formats.
- * Either output pointer may be NULL. Returns
- * PDAKV_ERR_INVALID_ARG for a bad format or negative sizes and
- * PDAKV_ERR_UNSUPPORTED above 2^30 items. Host arithmetic only. */
-int pdakv_decode_plan(int kv_format, int num_seqs, int num_kv_heads, int max_context_len,
-                      int* num_waves, int* max_pages_per_wave);
+/* Launch plan of the one-token decode calls for these sizes. The work of a
+ * call is the list of (sequence, KV head, page) items; the kernel splits the
+ * items of the actual context lengths evenly over *num_waves 64-lane waves
+ * (at least 2 items each, a unit that spans several waves is merged
+ * afterwards): one resident round of waves, one per SIMD where a KV head's
+ * block of a page holds 4 KB or more (INT8 pages at head_dim 128, 16-bit
+ * pages) and that round holds every item at <= 128 each, else two (more
+ * rounds only beyond 128 items per wave). *max_pages_per_wave is the share
+ * when every sequence is at max_context_len (<= 128). kv_format is one of
+ * the PDAKV_KV_* formats.
+ * Either output pointer may be NULL. Returns PDAKV_ERR_INVALID_ARG for a bad
+ * format or negative sizes and PDAKV_ERR_UNSUPPORTED for a head_dim other
+ * than 64 or 128 or above 2^30 items. Host arithmetic only. */
+int pdakv_decode_plan(int kv_format, int num_seqs, int num_kv_heads, int head_dim,
+                      int max_context_len, int* num_waves, int* max_pages_per_wave);
 
 /* Device workspace the decode calls need for these sizes (0 when
  * max_context_len or num_seqs is 0). The same value serves every decode
  * entry point. Layout: float partials
  * [num_waves + num_seqs * num_kv_heads][num_q_heads / num_kv_heads][head_dim + 2]
- * (num_waves from the INT8 plan; the region padded to a multiple of 16
- * bytes), then int32 [num_seqs * num_kv_heads][2] merge records. */
+ * (num_waves: the plan at two waves per SIMD, which no decode plan exceeds;
+ * the region padded to a multiple of 16 bytes), then int32
+ * [num_seqs * num_kv_heads][2] merge records. */
 size_t pdakv_decode_workspace_bytes(int num_seqs, int num_q_heads, int num_kv_heads,
                                     int head_dim, int max_context_len);
 

@@ -43,7 +43,7 @@ _SIGS = {
     "pdakv_status_string": (ctypes.c_char_p, [_c_int]),
     "pdakv_page_bytes": (ctypes.c_size_t, [_c_int, _c_int, _c_int, _c_int]),
     "pdakv_capabilities": (_c_int, [ctypes.POINTER(ctypes.c_uint32)]),
-    "pdakv_decode_plan": (_c_int, [_c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_int),
+    "pdakv_decode_plan": (_c_int, [_c_int, _c_int, _c_int, _c_int, _c_int, ctypes.POINTER(_c_int),
                                    ctypes.POINTER(_c_int)]),
     "pdakv_decode_workspace_bytes": (ctypes.c_size_t, [_c_int] * 5),
     "paged_attn_decode_workspace_bytes": (ctypes.c_size_t, [_c_int] * 4),
@@ -215,11 +215,13 @@ def pdakv_capabilities() -> int:
     return int(flags.value)
 
 
-def pdakv_decode_plan(kv_format: int, num_seqs: int, num_kv_heads: int, max_context_len: int):
-    """Returns (num_waves, max_pages_per_wave) of the decode launch."""
+def pdakv_decode_plan(kv_format: int, num_seqs: int, num_kv_heads: int, head_dim: int,
+                      max_context_len: int):
+    """Returns (num_waves, max_pages_per_wave) of the one-token decode launch."""
     waves, pages = _c_int(0), _c_int(0)
     _check("pdakv_decode_plan", _lib.pdakv_decode_plan(kv_format, num_seqs, num_kv_heads,
-                                                       max_context_len, ctypes.byref(waves),
+                                                       head_dim, max_context_len,
+                                                       ctypes.byref(waves),
                                                        ctypes.byref(pages)))
     return waves.value, pages.value
 

@@ -38,8 +38,24 @@ int device_cus() {
 int64_t resident_waves(int waves_per_simd) {
   return int64_t{device_cus()} * pdakv::kSimdsPerCU * waves_per_simd;
 }
-int format_waves_per_simd(int kv_format) {
+// Waves per SIMD the one-token kernel of a format can hold (its registers).
+int kernel_waves_per_simd(int kv_format) {
   return kv_format == PDAKV_KV_16BIT ? pdakv::k16WavesPerSimd : pdakv::kInt8WavesPerSimd;
+}
+// Waves per SIMD a one-token plan of `items` items fills. Each wave keeps
+// two page groups in flight; where one KV head's block of a page holds at
+// least kOneWaveBlockBytes (INT8 pages at head size 128, 16-bit pages) and
+// one wave per SIMD can hold every item (<= kMaxPagesPerWave each), that
+// round keeps enough bytes in flight and streams twice the pages per start
+// and per partial, which measured faster at 8K and 32K contexts than two;
+// smaller blocks (INT8 at head size 64) and larger calls take the kernel's
+// occupancy (a full round, never a mix of SIMDs with one and two waves).
+int format_waves_per_simd(int kv_format, int head_dim, int64_t items) {
+  const int elem_bytes = kv_format == PDAKV_KV_16BIT ? 2 : 1;
+  if (pdakv::kBlockSize * 2 * head_dim * elem_bytes >= pdakv::kOneWaveBlockBytes &&
+      items <= resident_waves(1) * pdakv::kMaxPagesPerWave)
+    return 1;
+  return kernel_waves_per_simd(kv_format);
 }
 
 bool known_format(int f) {
@@ -92,9 +108,10 @@ int merge_waves(int num_seqs, int num_kv_heads, int max_context_len, int64_t wav
 // Waves per SIMD of the kernel a decode call launches, which its plan fills:
 // the one-token kernels' occupancy per format, or that of the several-token
 // kernel for units of unit_tiles tiles.
-int launch_waves_per_simd(int kv_format, bool multi, int unit_tiles) {
+int launch_waves_per_simd(int kv_format, bool multi, int unit_tiles, int head_dim,
+                          int64_t items) {
   return multi ? pdakv::wide_waves_per_simd(kv_format, unit_tiles)
-               : format_waves_per_simd(kv_format);
+               : format_waves_per_simd(kv_format, head_dim, items);
 }
 
 // Query columns of a call: T query tokens x G query heads per KV head, in
@@ -102,9 +119,9 @@ int launch_waves_per_simd(int kv_format, bool multi, int unit_tiles) {
 // to unit_tiles tiles, whose pages are streamed once for all of them: all
 // the tiles of a KV head up to kMaxUnitTiles, else units of that many.
 // waves_per_simd: the most that any decode kernel these columns can run in
-// has (every format; for one query token the one-token and the several-token
-// kernels), so that a workspace sized with it holds the partial slots of
-// every plan.
+// holds (every format; for one query token the one-token and the
+// several-token kernels), an upper bound of every launch plan, so that a
+// workspace sized with it holds the partial slots of every plan.
 struct Columns {
   int cols, unit_tiles, units_per_head, slot_cols, waves_per_simd;
 };
@@ -117,16 +134,18 @@ Columns columns(int num_q_heads, int num_kv_heads, int num_query_tokens) {
   c.slot_cols = std::min(c.cols, 16 * c.unit_tiles);
   c.waves_per_simd = 0;
   for (int f : {PDAKV_KV_INT8_SYM, PDAKV_KV_INT8_STATIC, PDAKV_KV_16BIT}) {
-    c.waves_per_simd = std::max(c.waves_per_simd, launch_waves_per_simd(f, true, c.unit_tiles));
+    c.waves_per_simd =
+        std::max(c.waves_per_simd, pdakv::wide_waves_per_simd(f, c.unit_tiles));
     if (num_query_tokens == 1)
-      c.waves_per_simd = std::max(c.waves_per_simd, launch_waves_per_simd(f, false, 1));
+      c.waves_per_simd = std::max(c.waves_per_simd, kernel_waves_per_simd(f));
   }
   return c;
 }
 
 // Partial results region of the decode workspace (a multiple of 16 bytes):
-// [waves + units][C][D + 2] floats, C = columns per unit. The INT8 plan has
-// the most waves; its slots serve the other formats too.
+// [waves + units][C][D + 2] floats, C = columns per unit, with the waves of
+// a plan at the most waves per SIMD any kernel for these columns holds (no
+// launch plans more), so one workspace serves every format and head size.
 size_t partials_bytes(int num_seqs, int num_query_tokens, int num_q_heads, int num_kv_heads,
                       int head_dim, int max_context_len) {
   const Columns c = columns(num_q_heads, num_kv_heads, num_query_tokens);
@@ -302,7 +321,8 @@ int decode_common(int fmt, Scales sc, const Rows& r, const AppendRows* app,
   a.out_mul = fmt == PDAKV_KV_INT8_STATIC ? sc.v : 1.f;
   a.k_scale = sc.k;
   a.v_scale = sc.v;
-  const int wps = launch_waves_per_simd(fmt, multi, cols.unit_tiles);
+  const int wps = launch_waves_per_simd(fmt, multi, cols.unit_tiles, head_dim,
+                                        item_bound(num_seqs, a.vheads, max_context_len));
   a.num_waves = static_cast<int>(plan_waves(wps, num_seqs, a.vheads, max_context_len));
   a.merge_waves = merge_waves(num_seqs, a.vheads, max_context_len, a.num_waves);
   {
@@ -534,14 +554,17 @@ int pdakv_capabilities(uint32_t* flags_out) {
   return PDAKV_OK;
 }
 
-int pdakv_decode_plan(int kv_format, int num_seqs, int num_kv_heads, int max_context_len,
-                      int* num_waves, int* max_pages_per_wave) {
+int pdakv_decode_plan(int kv_format, int num_seqs, int num_kv_heads, int head_dim,
+                      int max_context_len, int* num_waves, int* max_pages_per_wave) {
   if (!known_format(kv_format)) return PDAKV_ERR_INVALID_ARG;
   if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0) return PDAKV_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return PDAKV_ERR_UNSUPPORTED;
   if (item_bound(num_seqs, num_kv_heads, max_context_len) > kMaxItems)
     return PDAKV_ERR_UNSUPPORTED;
-  const int64_t v = plan_waves(format_waves_per_simd(kv_format), num_seqs, num_kv_heads,
-                               max_context_len);
+  const int64_t v = plan_waves(
+      format_waves_per_simd(kv_format, head_dim,
+                            item_bound(num_seqs, num_kv_heads, max_context_len)),
+      num_seqs, num_kv_heads, max_context_len);
   const int64_t p = std::max<int64_t>(
       pdakv::kMinPagesPerWave, ceil_div(item_bound(num_seqs, num_kv_heads, max_context_len), v));
   if (num_waves) *num_waves = static_cast<int>(v);

@@ -19,6 +19,8 @@ constexpr int kInt8WavesPerSimd = 2;  // INT8 decode occupancy
 constexpr int kInt8PageGroup = 2;     // pages per register buffer
 constexpr int k16WavesPerSimd = 2;    // 16-bit decode occupancy
 constexpr int k16PageGroup = 2;
+constexpr int kOneWaveBlockBytes = 4096;  // one-token plans: one wave per SIMD from
+                                          // this KV-head page-block size up
 constexpr int kSimdsPerCU = 4;
 constexpr int kDefaultCUs = 256;      // MI355X compute units (when no device answers)
 constexpr int kMaxMergeWaves = 8;              // merge: waves per (sequence, q head)

@@ -115,17 +115,22 @@ MIN_PPW = 2  # fewest pages a decode wave is given (one page pair)
 @pytest.mark.parametrize("B,hkv,L", [(1, 8, 256), (1, 8, 2048), (64, 8, 8193), (8, 8, 32768),
                                      (32, 2, 4104), (8, 8, 8192), (3, 1, 0), (1, 32, 1),
                                      (256, 8, 131072)])
-def test_decode_plan_is_consistent(P, B, hkv, L):
+@pytest.mark.parametrize("D", [64, 128])
+def test_decode_plan_is_consistent(P, B, hkv, L, D):
     items = B * hkv * -(-L // 16)
-    resident = {P.KV_INT8_SYM: 2048, P.KV_16BIT: 2048, P.KV_INT8_STATIC: 2048}
     for fmt in (P.KV_INT8_SYM, P.KV_16BIT, P.KV_INT8_STATIC):
-        waves, ppw = P.pdakv_decode_plan(fmt, B, hkv, L)
+        # one wave per SIMD (1,024 on 256 CUs) where a KV head's page block
+        # holds 4 KB or more and that round holds the items at <= 128 each,
+        # else two
+        block = 16 * 2 * D * (2 if fmt == P.KV_16BIT else 1)
+        resident = 1024 if block >= 4096 and items <= 1024 * 128 else 2048
+        waves, ppw = P.pdakv_decode_plan(fmt, B, hkv, D, L)
         assert waves >= 4 and waves % 4 == 0
         assert MIN_PPW <= ppw <= 128 and ppw == max(MIN_PPW, -(-items // waves))
         # one resident round unless the items need more than 128 per wave;
         # never more waves than MIN_PPW-page shares (rounded to whole workgroups)
-        assert waves <= max(4, -(-max(resident[fmt], -(-items // 128)) // 4) * 4)
-        assert waves <= max(4, -(-(-(-items // MIN_PPW)) // 4) * 4)
+        want = min(max(resident, -(-items // 128)), -(-items // MIN_PPW))
+        assert waves == max(4, -(-max(want, 1) // 4) * 4)
 
 
 @pytest.mark.parametrize("B,hkv,L", [(1, 8, 2048), (64, 8, 8193), (8, 8, 32768), (3, 1, 1),
@@ -135,19 +140,23 @@ def test_workspace_holds_every_plan(P, B, hkv, L):
     plan, whichever format a call then decodes: it is sized with the most
     waves any of them plans (a workspace sized for fewer waves than a launch
     uses would be written past its end)."""
-    wmax = max(P.pdakv_decode_plan(f, B, hkv, L)[0]
+    wmax = max(P.pdakv_decode_plan(f, B, hkv, 128, L)[0]
                for f in (P.KV_INT8_SYM, P.KV_16BIT, P.KV_INT8_STATIC))
     ws = P.pdakv_decode_workspace_bytes(B, 4 * hkv, hkv, 128, L)
     partials = -(-(wmax + B * hkv) * 4 * 130 * 4 // 16) * 16
-    assert ws == (0 if L == 0 else partials + B * hkv * 8)
+    # sized for two waves per SIMD (the kernels' occupancy), which no plan exceeds
+    full = -(-(_plan_waves(2, B, hkv, L) + B * hkv) * 4 * 130 * 4 // 16) * 16
+    assert ws == (0 if L == 0 else full + B * hkv * 8)
+    assert ws == 0 or ws >= partials + B * hkv * 8
 
 
 def test_decode_plan_rejects_bad_arguments(P):
-    assert P._lib.pdakv_decode_plan(7, 1, 8, 16, None, None) == P.ERR_INVALID_ARG
-    assert P._lib.pdakv_decode_plan(P.KV_INT8_SYM, -1, 8, 16, None, None) == P.ERR_INVALID_ARG
-    assert P._lib.pdakv_decode_plan(P.KV_INT8_SYM, 1, 0, 16, None, None) == P.ERR_INVALID_ARG
+    assert P._lib.pdakv_decode_plan(7, 1, 8, 128, 16, None, None) == P.ERR_INVALID_ARG
+    assert P._lib.pdakv_decode_plan(P.KV_INT8_SYM, -1, 8, 128, 16, None, None) == P.ERR_INVALID_ARG
+    assert P._lib.pdakv_decode_plan(P.KV_INT8_SYM, 1, 0, 128, 16, None, None) == P.ERR_INVALID_ARG
+    assert P._lib.pdakv_decode_plan(P.KV_INT8_SYM, 1, 8, 96, 16, None, None) == P.ERR_UNSUPPORTED
     # more than 2^30 (sequence, KV head, page) items
-    assert (P._lib.pdakv_decode_plan(P.KV_INT8_SYM, 4096, 64, 1 << 17, None, None) ==
+    assert (P._lib.pdakv_decode_plan(P.KV_INT8_SYM, 4096, 64, 128, 1 << 17, None, None) ==
             P.ERR_UNSUPPORTED)
 
 
@@ -320,8 +329,8 @@ def test_multi_workspace_formula(P, B, T, hq, hkv, L):
     per_unit = min(tiles, 4)
     vh = hkv * -(-tiles // per_unit)
     waves = _plan_waves(2 if per_unit <= 2 else 1, B, vh, L)
-    if per_unit == 1:
-        assert waves == P.pdakv_decode_plan(P.KV_INT8_SYM, B, vh, L)[0]
+    if per_unit == 1:  # the one-token plan never has more waves
+        assert waves >= P.pdakv_decode_plan(P.KV_INT8_SYM, B, vh, 128, L)[0]
     partials = -(-(waves + B * vh) * min(cols, 16 * per_unit) * 130 * 4 // 16) * 16
     assert P.pdakv_decode_multi_workspace_bytes(B, T, hq, hkv, 128, L) == partials + B * vh * 8
     if T == 1:

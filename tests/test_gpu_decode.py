@@ -101,13 +101,17 @@ def test_edge_shapes(P, case, fmt_name):
 
 @pytest.mark.parametrize("fmt_name", ["int8", "16bit"])
 def test_long_single_sequence_many_partials(P, fmt_name):
-    """One 40000-token sequence on one KV head: the split gives every wave
-    the fewest pages it can have (two), so over a thousand partials meet in
-    the merge (several rounds of its LDS slots)."""
+    """One 40000-token sequence on one KV head (head size 64): the INT8 split
+    gives every wave the fewest pages it can have (two), so over a thousand
+    partials meet in the merge (several rounds of its LDS slots); the 16-bit
+    plan (one wave per SIMD for its 4 KB page blocks) gives 834."""
     fmt = P.KV_INT8_SYM if fmt_name == "int8" else P.KV_16BIT
     wl = build("long1", 77, [("prefill", [40000])], 16, 1, 64, "bf16", "logmag", shuffle=True)
-    waves, ppw = P.pdakv_decode_plan(fmt, 1, 1, 40000)
-    assert ppw == 2 and 2500 // ppw > 1024
+    waves, ppw = P.pdakv_decode_plan(fmt, 1, 1, 64, 40000)
+    if fmt_name == "int8":
+        assert ppw == 2 and 2500 // ppw > 1024
+    else:
+        assert ppw == 3 and -(-2500 // ppw) == 834
     _say(f"long single sequence {fmt_name}: {waves} waves")
     pool, _ = gpu_pool(P, wl, fmt)
     out = gpu_decode(P, wl, pool, fmt)

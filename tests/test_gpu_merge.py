@@ -90,7 +90,8 @@ def test_wave_shares_near_the_pass_limit(P, fmt_name):
     wl = build("pass-limit", 903, [("prefill", lens)], 8, 8, 128, "f16", "outlier",
                shuffle=True, spare_blocks=3)
     fmt = P.KV_INT8_SYM if fmt_name == "int8" else P.KV_16BIT
-    waves, ppw = P.pdakv_decode_plan(fmt, wl.num_seqs, wl.num_kv_heads, wl.max_context_len)
+    waves, ppw = P.pdakv_decode_plan(fmt, wl.num_seqs, wl.num_kv_heads, wl.head_dim,
+                                     wl.max_context_len)
     _say(f"pass limit {fmt_name}: {waves} waves, up to {ppw} pages each")
     assert ppw == 128
     pool, _ = gpu_pool(P, wl, fmt)
